@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent-sparse-attention layer on one MI355X.
+
+Default workload: single-request decode at 1M tokens (32 query heads / 4 KV
+heads, d = 128, bf16 K/V from a 65536-centre Gaussian mixture; latent dim 64,
+3-level tree of branching 64, beam 16, k = 2048).  One step is one decode
+layer: lsa_select (group latent, top-down descent, causal fill) followed by
+lsa_attend (sparse attention), with the cluster tree already built and
+resident in HBM, as the pages describe the index (precomputed, then
+maintained).  The index build (projection, k-means levels) is timed in the
+same run and reported under "breakdown".
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on; the CPU baseline is the oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def select_bytes(w, m, counts, cand_leaves):
+    """Algorithmic bytes one lsa_select launch moves for m rows."""
+    G = w.h_q // w.h_kv
+    qb = 2 if w.dtype == "bf16" else 4
+    rows = w.b + (w.L - 1) * w.beam * w.b            # centroid rows scored per group
+    per_group = (G * w.d * qb                          # the group's query heads
+                 + w.d * w.r * 4                       # W_lat of the head
+                 + rows * w.r * 4                      # centroid rows
+                 + rows * 4                            # their member counts
+                 + cand_leaves * 8                     # leaf CSR offsets of candidate leaves
+                 + w.k * 4 + 8)                        # sel row, count, cutoff
+    return m * w.h_kv * per_group + int(counts.sum()) * 4   # gathered member ids
+
+
+def attend_bytes(w, m, counts):
+    G = w.h_q // w.h_kv
+    eb = 2 if w.dtype == "bf16" else 4
+    return (m * w.h_q * w.d * eb * 2                   # Q in, out
+            + m * w.h_q * 4                            # lse
+            + m * w.h_kv * 4                           # counts
+            + int(counts.sum()) * (4 + 2 * w.d * eb))  # sel ids + gathered K and V rows
+
+
+def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s):
+    """The oracle (as it is) on the host: select + attend of one decode layer on
+    the GPU-built index, repeated for about budget_s seconds."""
+    import numpy as np
+    import torch
+    import oracle
+    views = lsa.index_views(index, desc)
+    L = desc.L
+    oix = oracle.Index(desc.n, desc.h_kv, desc.r, desc.b, L,
+                       torch.cat([views["C"][l].reshape(-1) for l in range(1, L + 1)]).cpu().numpy(),
+                       torch.cat([views["cnt"][l].reshape(-1).long() for l in range(1, L + 1)]).cpu().numpy(),
+                       views["leaf_off"].long().cpu().numpy(), views["perm"].cpu().numpy())
+    Kh = K.float().cpu().numpy()
+    Vh = V.float().cpu().numpy()
+    Qh = Q.float().cpu().numpy()
+    Wh = W.cpu().numpy()
+    ph = pos.cpu().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref = oracle.select(Qh, ph, oix, Wh, w.beam, w.k)
+        oracle.attend(Qh, Kh, Vh, ref["sel"], ref["count"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and reps >= 3) or reps >= 100000:
+            break
+    return dict(value=el / reps * 1e6, unit="us/layer", cores=oracle.threads(), kind="oracle",
+                sample=f"{reps} decode layers (select + attend of 1 query row x {w.h_q} heads over the "
+                       f"{desc.n}-key index built on the GPU), identical inputs, {el:.1f} s total")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_1m")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import hierarchical_key_indexing_amd as lsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lsa.lib()
+    w = synth.WORKLOADS[args.workload]
+    log("generate", w.name)
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    pos = w.positions().to(dev)
+    Q = synth.make_queries(w, K, pos)
+    torch.cuda.synchronize()
+
+    # ---- index build (projection + k-means levels), timed with events
+    log("build")
+    desc = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L)
+    index = torch.empty(desc.bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(lsa.build_workspace_bytes(w.n, w.h_kv, w.d, w.r, w.b, w.L), dtype=torch.uint8, device=dev)
+    lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=ws)
+    torch.cuda.synchronize()
+    nb = 3
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for _ in range(nb):
+        lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=ws)
+    b1.record()
+    torch.cuda.synchronize()
+    build_ms = b0.elapsed_time(b1) / nb
+    del ws
+
+    m = pos.shape[0]
+    sel = torch.empty((m, w.h_kv, w.k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((m, w.h_kv), dtype=torch.int32, device=dev)
+    cut = torch.empty((m, w.h_kv), dtype=torch.float32, device=dev)
+    out = torch.empty_like(Q)
+    lse = torch.empty((m, w.h_q), dtype=torch.float32, device=dev)
+    nws = lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k)
+    aws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def do_select():
+        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, cutoff=cut)
+
+    def do_attend():
+        lsa.attend(Q, K, V, sel, cnt, out=out, lse=lse, ws=aws)
+
+    do_select(); do_attend()
+    torch.cuda.synchronize()
+
+    use_graph = not args.no_graph
+    if use_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                do_select(); do_attend()
+            torch.cuda.current_stream().wait_stream(s)
+            g_sel, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_sel):
+                do_select()
+            with torch.cuda.graph(g_att):
+                do_attend()
+            run_sel, run_att = g_sel.replay, g_att.replay
+            # the graphs must reproduce the eager result
+            ref = (sel.clone(), cnt.clone(), out.clone())
+            sel.zero_(); out.zero_()
+            run_sel(); run_att()
+            torch.cuda.synchronize()
+            assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1]) and torch.equal(out, ref[2])
+        except Exception as e:      # graph capture unavailable: time eager launches
+            log("graph capture failed, timing eager launches:", repr(e))
+            use_graph = False
+    if not use_graph:
+        run_sel, run_att = do_select, do_attend
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        run_sel(); run_att()
+    torch.cuda.synchronize()
+    K_ = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_)]
+    log("timed", K_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(K_):
+        ev[s_][0].record()
+        run_sel()
+        ev[s_][1].record()
+        run_att()
+        ev[s_][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K_
+    sel_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    counts = cnt.cpu().numpy()
+    cand_leaves = w.beam * w.b
+    sb = select_bytes(w, m, counts, cand_leaves)
+    ab = attend_bytes(w, m, counts)
+    kernels = {"lsa_select": (sel_us, sb), "lsa_attend": (att_us, ab)}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dus, dbytes = kernels[dom]
+    achieved = dbytes / (dus * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": dom,
+                "kernel_us": round(dus, 3), "algorithmic_bytes": int(dbytes)}
+
+    breakdown = {"select_us": round(sel_us, 3), "attend_us": round(att_us, 3),
+                 "select_GBps": round(sb / (sel_us * 1e-6) / 1e9, 2),
+                 "attend_GBps": round(ab / (att_us * 1e-6) / 1e9, 2),
+                 "build_ms": round(build_ms, 3), "graph": use_graph,
+                 "mean_sel_count": float(counts.mean()),
+                 "index_bytes": int(desc.bytes), "kv_bytes": int(2 * K.numel() * K.element_size())}
+
+    # ---- secondary: last-chunk prefill on the same cache (4096 queries)
+    if not args.no_prefill and w.mode == "decode" and w.n >= 4096:
+        wp = synth.WORKLOADS.get("prefill_1m") if w.name == "decode_1m" else w.replace(m=4096, mode="chunk")
+        ppos = torch.arange(w.n - 4096, w.n, dtype=torch.int32, device=dev)
+        Qp = synth.make_queries(wp, K, ppos)
+        mp = 4096
+        psel = torch.empty((mp, w.h_kv, w.k), dtype=torch.int32, device=dev)
+        pcnt = torch.empty((mp, w.h_kv), dtype=torch.int32, device=dev)
+        pout = torch.empty_like(Qp)
+        pws_n = lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, w.k)
+        pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
+        def pstep():
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False)
+            lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
+        for _ in range(2):
+            pstep()
+        torch.cuda.synchronize()
+        npre = 5
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(npre):
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False)
+        e[1].record()
+        for _ in range(npre):
+            lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
+        e[2].record()
+        torch.cuda.synchronize()
+        ps = e[0].elapsed_time(e[1]) / npre
+        pa = e[1].elapsed_time(e[2]) / npre
+        pc = pcnt.cpu().numpy()
+        breakdown["prefill_1m"] = {
+            "queries_per_s": round(mp / ((ps + pa) * 1e-3), 1), "select_ms": round(ps, 4), "attend_ms": round(pa, 4),
+            "select_share": round(ps / (ps + pa), 4),
+            "attend_GBps_algorithmic": round(attend_bytes(w, mp, pc) / (pa * 1e-3) / 1e9, 2),
+            "attend_tflops": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pa * 1e-3) / 1e12, 3)}
+        del Qp, psel, pcnt, pout, pws
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline")
+        cpu = cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, args.cpu_seconds)
+
+    res = {
+        "metric": "µs/layer decode and queries/s last-chunk prefill at 1M/10M ctx; % HBM/MFMA peak",
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/layer",
+        "n_gpus": 1, "steps": K_, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "r": w.r, "b": w.b,
+                   "L": w.L, "beam": w.beam, "k": w.k, "query_rows": m,
+                   "step": "lsa_select + lsa_attend, index resident",
+                   "indexer_arith": "f64 accumulate", "attention_arith": "f32 accumulate"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

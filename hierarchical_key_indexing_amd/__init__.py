@@ -1,0 +1,214 @@
+"""Latent sparse attention (LSA) layer for MI355X: Python binding of liblsa.so.
+
+A thin ctypes layer over the C ABI declared in include/lsa.h.  Every step of
+the layer runs in the HIP library; this module only allocates outputs with
+torch (device memory) and passes pointers and the current stream.
+
+    index, desc = build_index(K, W, b, L, iters)      # lsa_build_index
+    sel, count, cutoff = select(Q, q_pos, index, desc, W, beam, k)   # lsa_select
+    out, lse = attend(Q, K, V, sel, count)            # lsa_attend
+
+Importing works without a GPU; calling a device entry point without the built
+library raises (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from ._build import LIB as _LIB_PATH
+
+LSA_OK, LSA_EINVAL, LSA_EUNSUPPORTED, LSA_ENOSPC, LSA_EHIP = 0, -1, -2, -3, -4
+LSA_F32, LSA_BF16 = 0, 1
+MAX_LEVELS = 6
+
+EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
+           "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
+           "lsa_attend"]
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("h_kv", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("b", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("nodes", ctypes.c_int64 * (MAX_LEVELS + 1)),
+                ("centroid_off", ctypes.c_int64 * (MAX_LEVELS + 1)),
+                ("count_off", ctypes.c_int64 * (MAX_LEVELS + 1)),
+                ("leaf_off_off", ctypes.c_int64), ("perm_off", ctypes.c_int64), ("bytes", ctypes.c_int64)]
+
+
+class LSAError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {lib().lsa_strerror(code).decode()} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load liblsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library {_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m hierarchical_key_indexing_amd._build")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        D = ctypes.POINTER(IndexDesc)
+        L.lsa_abi_version.restype = i32
+        L.lsa_strerror.argtypes = [i32]
+        L.lsa_strerror.restype = ctypes.c_char_p
+        L.lsa_index_layout.argtypes = [i64, i32, i32, i32, i32, D]
+        L.lsa_build_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_build_index.argtypes = [P, i32, i64, i32, i32, P, i32, i32, i32, i32, P, i64, P, i64, D, P]
+        L.lsa_select_workspace_bytes.argtypes = [i64, i32, D, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, P, P, P, P, i64, P]
+        L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_attend.argtypes = [P, P, P, i32, i64, i32, i32, i64, i32, P, P, i32, ctypes.c_float,
+                                 P, P, P, i64, P]
+        for name in EXPORTS:
+            if name not in ("lsa_abi_version", "lsa_strerror"):
+                getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != LSA_OK:
+        raise LSAError(rc, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LSA_F32
+    if t.dtype == torch.bfloat16:
+        return LSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ layout
+def index_layout(n: int, h_kv: int, r: int, b: int, L: int) -> IndexDesc:
+    d = IndexDesc()
+    _check(lib().lsa_index_layout(n, h_kv, r, b, L, ctypes.byref(d)), "lsa_index_layout")
+    return d
+
+
+def build_workspace_bytes(n: int, h_kv: int, d: int, r: int, b: int, L: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_build_workspace_bytes(n, h_kv, d, r, b, L, ctypes.byref(v)), "lsa_build_workspace_bytes")
+    return v.value
+
+
+def select_workspace_bytes(m: int, h_q: int, desc: IndexDesc, beam: int, k: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_select_workspace_bytes(m, h_q, ctypes.byref(desc), beam, k, ctypes.byref(v)),
+           "lsa_select_workspace_bytes")
+    return v.value
+
+
+def attend_workspace_bytes(m: int, h_q: int, h_kv: int, d: int, k: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_attend_workspace_bytes(m, h_q, h_kv, d, k, ctypes.byref(v)), "lsa_attend_workspace_bytes")
+    return v.value
+
+
+def index_views(index: torch.Tensor, desc: IndexDesc) -> dict:
+    """Typed views of the arrays inside index memory (no copy)."""
+    h, r, L, n = desc.h_kv, desc.r, desc.L, desc.n
+    out = {"C": {}, "cnt": {}}
+    for l in range(1, L + 1):
+        nodes = desc.nodes[l]
+        o = desc.centroid_off[l]
+        out["C"][l] = index[o:o + h * nodes * r * 4].view(torch.float32).view(h, nodes, r)
+        o = desc.count_off[l]
+        out["cnt"][l] = index[o:o + h * nodes * 4].view(torch.int32).view(h, nodes)
+    nl = desc.nodes[L]
+    o = desc.leaf_off_off
+    out["leaf_off"] = index[o:o + h * (nl + 1) * 4].view(torch.int32).view(h, nl + 1)
+    o = desc.perm_off
+    out["perm"] = index[o:o + h * n * 4].view(torch.int32).view(h, n)
+    return out
+
+
+# ------------------------------------------------------------------ entry points
+def build_index(K: torch.Tensor, W: torch.Tensor, b: int, L: int, iters: int = 5,
+                index: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """K [h_kv, n, d] (f32/bf16), W [h_kv, d, r] f32 -> (index uint8 tensor, IndexDesc)."""
+    _need(K, "K"); _need(W, "W")
+    h, n, d = K.shape
+    r = W.shape[2]
+    if W.dtype != torch.float32 or tuple(W.shape) != (h, d, r):
+        raise ValueError("W must be float32 [h_kv, d, r]")
+    desc = index_layout(n, h, r, b, L)
+    if index is None:
+        index = torch.empty(desc.bytes, dtype=torch.uint8, device=K.device)
+    nws = build_workspace_bytes(n, h, d, r, b, L)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=K.device)
+    out = IndexDesc()
+    _check(lib().lsa_build_index(_ptr(K), _dtype_code(K), n, h, d, _ptr(W), r, b, L, iters, _ptr(index),
+                                 index.numel(), _ptr(ws), ws.numel(), ctypes.byref(out), _stream(stream)),
+           "lsa_build_index")
+    return index, out
+
+
+def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: IndexDesc, W: torch.Tensor,
+           beam: int, k: int, sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
+           cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, stream=None):
+    """Q [m, h_q, d], q_pos int32 [m] -> (sel int32 [m, h_kv, k], count int32 [m, h_kv], cutoff f32 [m, h_kv])."""
+    _need(Q, "Q"); _need(q_pos, "q_pos"); _need(W, "W")
+    m, h_q, d = Q.shape
+    h = desc.h_kv
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((m, h, k), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
+    if cutoff is None and want_cutoff:
+        cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    _check(lib().lsa_select(_ptr(Q), _dtype_code(Q), m, h_q, d, _ptr(q_pos), ctypes.byref(desc), _ptr(index),
+                            _ptr(W), beam, k, _ptr(sel), _ptr(sel_count), _ptr(cutoff), None, 0, _stream(stream)),
+           "lsa_select")
+    return sel, sel_count, cutoff
+
+
+def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel: torch.Tensor, sel_count: torch.Tensor,
+           scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           want_lse: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
+    """-> (out [m, h_q, d] in Q's dtype, lse f32 [m, h_q])."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (sel, "sel"), (sel_count, "sel_count")):
+        _need(t, nm)
+    m, h_q, d = Q.shape
+    h_kv, n, _ = K.shape
+    k = sel.shape[2]
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((m, h_q), dtype=torch.float32, device=Q.device)
+    nws = attend_workspace_bytes(m, h_q, h_kv, d, k)
+    if ws is None and nws > 0:
+        ws = torch.empty(nws, dtype=torch.uint8, device=Q.device)
+    _check(lib().lsa_attend(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), m, h_q, h_kv, n, d, _ptr(sel),
+                            _ptr(sel_count), k, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(stream)),
+           "lsa_attend")
+    return out, lse

@@ -1,0 +1,201 @@
+// Sparse attention over the selected keys (gfx950).
+//
+// Each query attends to k selected keys instead of all n ("Latent Sparse
+// Attention Breaks Through the Million-Token Context Bottleneck",
+// kongchang.com, section "The Accuracy-Efficiency Dilemma of Sparse
+// Attention"); attention is computed over the retrieved keys ("Latent sparse
+// attention", bdtechtalks.com, section "How latent sparse attention works").
+//
+// The G query heads that share a KV head share one selected set, so one
+// workgroup serves all G heads of a (row, KV head) pair and reads each
+// gathered K/V row once.  The set is cut into `nsplit` slices (split-K) to
+// fill the chip when there are few rows; slices keep a running max and sum
+// (online softmax, base 2) and a merge kernel combines them by log-sum-exp.
+#include "common.h"
+#include "internal.h"
+
+namespace lsa {
+
+constexpr int kTK = 32;   // keys per tile
+
+struct AttendArgs {
+    const void *Q, *K, *V;
+    int64_t m;
+    int h_q, h_kv;
+    int64_t n;
+    int d;
+    const int32_t *sel, *sel_count;
+    int k;
+    float scale_log2;     // scale * log2(e)
+    int nsplit;
+    void *out;
+    float *lse;
+    float *part;          // [m][h_q][nsplit][d + 2] when nsplit > 1
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
+    extern __shared__ float smem[];
+    const int d = A.d;
+    const int G = A.h_q / A.h_kv;
+    const int dp = d + 1;
+    float *qs = smem;                    // [G][d]
+    float *Ks = qs + G * d;              // [kTK][d + 1]
+    float *Vs = Ks + kTK * dp;           // [kTK][d]
+    float *Sc = Vs + kTK * d;            // [G][kTK]
+    __shared__ int32_t ids[kTK];
+
+    const int64_t row = blockIdx.y;      // i * h_kv + g
+    const int64_t i = row / A.h_kv;
+    const int g = (int)(row % A.h_kv);
+    const int split = blockIdx.x;
+    const int cnt = A.sel_count[row];
+    const int per = (cnt + A.nsplit - 1) / A.nsplit;
+    const int s0 = min(cnt, split * per), s1 = min(cnt, s0 + per);
+    const T *Q = (const T *)A.Q;
+    const T *Kg = (const T *)A.K + (size_t)g * A.n * d;
+    const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
+    const int32_t *S = A.sel + (size_t)row * A.k;
+
+    for (int e = threadIdx.x; e < G * d; e += blockDim.x)
+        qs[e] = to_float(Q[((size_t)i * A.h_q + (size_t)g * G) * d + e]) * A.scale_log2;
+
+    constexpr int MAXE = 16;             // G * d <= 4096 elements over 256 threads
+    const int ne = (G * d + blockDim.x - 1) / blockDim.x;
+    float acc[MAXE], mrun[MAXE], lrun[MAXE];
+#pragma unroll
+    for (int q = 0; q < MAXE; ++q) { acc[q] = 0.0f; mrun[q] = -INFINITY; lrun[q] = 0.0f; }
+
+    for (int kb = s0; kb < s1; kb += kTK) {
+        const int nk = min(kTK, s1 - kb);
+        __syncthreads();
+        if (threadIdx.x < nk) ids[threadIdx.x] = S[kb + threadIdx.x];
+        __syncthreads();
+        for (int e = threadIdx.x; e < nk * d; e += blockDim.x) {
+            const int kk = e / d, t = e % d;
+            const size_t off = (size_t)ids[kk] * d + t;
+            Ks[kk * dp + t] = to_float(Kg[off]);
+            Vs[kk * d + t] = to_float(Vg[off]);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < G * nk; e += blockDim.x) {
+            const int h = e / nk, kk = e % nk;
+            const float *qh = qs + h * d;
+            const float *kr = Ks + kk * dp;
+            float s = 0.0f;
+            for (int t = 0; t < d; ++t) s = fmaf(qh[t], kr[t], s);
+            Sc[h * kTK + kk] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < MAXE; ++q) {
+            if (q >= ne) break;
+            const int e = threadIdx.x + q * blockDim.x;
+            if (e >= G * d) break;
+            const int h = e / d, t = e % d;
+            const float *sc = Sc + h * kTK;
+            float mt = -INFINITY;
+            for (int kk = 0; kk < nk; ++kk) mt = fmaxf(mt, sc[kk]);
+            const float mnew = fmaxf(mrun[q], mt);
+            const float alpha = exp2f(mrun[q] - mnew);
+            float a = acc[q] * alpha, ls = 0.0f;
+            for (int kk = 0; kk < nk; ++kk) {
+                const float p = exp2f(sc[kk] - mnew);
+                ls += p;
+                a = fmaf(p, Vs[kk * d + t], a);
+            }
+            acc[q] = a;
+            lrun[q] = lrun[q] * alpha + ls;
+            mrun[q] = mnew;
+        }
+    }
+    const float ln2 = 0.69314718055994531f;
+#pragma unroll
+    for (int q = 0; q < MAXE; ++q) {
+        if (q >= ne) break;
+        const int e = threadIdx.x + q * blockDim.x;
+        if (e >= G * d) break;
+        const int h = e / d, t = e % d;
+        const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
+        if (A.nsplit == 1) {
+            const float o = (lrun[q] > 0.0f) ? acc[q] / lrun[q] : 0.0f;
+            ((T *)A.out)[oh * d + t] = from_float<T>(o);
+            if (t == 0 && A.lse) A.lse[oh] = (lrun[q] > 0.0f) ? (mrun[q] + log2f(lrun[q])) * ln2 : -INFINITY;
+        } else {
+            float *pp = A.part + (oh * A.nsplit + split) * (size_t)(d + 2);
+            pp[t] = acc[q];
+            if (t == 0) { pp[d] = mrun[q]; pp[d + 1] = lrun[q]; }
+        }
+    }
+}
+
+// Combine split-K slices: M = max m_s, l = sum l_s 2^(m_s - M),
+// o = sum o_s 2^(m_s - M) / l.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attend_merge(AttendArgs A) {
+    const int d = A.d;
+    const int64_t oh = blockIdx.x;                  // i * h_q + h
+    const float *pp = A.part + (size_t)oh * A.nsplit * (d + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, pp[(size_t)s * (d + 2) + d]);
+    float l = 0.0f;
+    for (int s = 0; s < A.nsplit; ++s) {
+        const float ms = pp[(size_t)s * (d + 2) + d];
+        if (ms > -INFINITY) l += pp[(size_t)s * (d + 2) + d + 1] * exp2f(ms - M);
+    }
+    for (int t = threadIdx.x; t < d; t += blockDim.x) {
+        float o = 0.0f;
+        for (int s = 0; s < A.nsplit; ++s) {
+            const float ms = pp[(size_t)s * (d + 2) + d];
+            if (ms > -INFINITY) o += pp[(size_t)s * (d + 2) + t] * exp2f(ms - M);
+        }
+        ((T *)A.out)[(size_t)oh * d + t] = from_float<T>(l > 0.0f ? o / l : 0.0f);
+    }
+    if (threadIdx.x == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+int attend_nsplit(int64_t m, int h_kv, int k) {
+    const int64_t groups = m * h_kv;
+    int64_t want = (512 + groups - 1) / groups;
+    const int64_t cap = (k + 127) / 128;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    if (want > 64) want = 64;
+    return (int)want;
+}
+
+int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k) {
+    const int ns = attend_nsplit(m, h_kv, k);
+    if (ns == 1) return 0;
+    return (int64_t)m * h_q * ns * (d + 2) * (int64_t)sizeof(float);
+}
+
+hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int64_t n,
+                  int d, const int32_t *sel, const int32_t *sel_count, int k, float scale, void *out, float *lse,
+                  void *ws, hipStream_t st) {
+    AttendArgs A{};
+    A.Q = Q; A.K = K; A.V = V; A.m = m; A.h_q = h_q; A.h_kv = h_kv; A.n = n; A.d = d;
+    A.sel = sel; A.sel_count = sel_count; A.k = k;
+    A.scale_log2 = scale * 1.4426950408889634f;
+    A.nsplit = attend_nsplit(m, h_kv, k);
+    A.out = out; A.lse = lse; A.part = (float *)ws;
+    const int G = h_q / h_kv;
+    const size_t shm = sizeof(float) * ((size_t)G * d + (size_t)kTK * (d + 1) + (size_t)kTK * d + (size_t)G * kTK);
+    const dim3 grid((unsigned)A.nsplit, (unsigned)(m * h_kv));
+    if (shm > 65536) {
+        hipError_t e = dtype == 0
+            ? hipFuncSetAttribute((const void *)k_attend<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm)
+            : hipFuncSetAttribute((const void *)k_attend<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+    }
+    if (dtype == 0) {
+        hipLaunchKernelGGL(k_attend<float>, grid, dim3(256), shm, st, A);
+        if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<float>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
+    } else {
+        hipLaunchKernelGGL(k_attend<bf16_t>, grid, dim3(256), shm, st, A);
+        if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<bf16_t>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lsa

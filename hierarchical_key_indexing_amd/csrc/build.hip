@@ -1,0 +1,447 @@
+// Index build: latent projection and top-down k-means tree (gfx950).
+//
+// Method: keys are projected into a learned latent space and grouped by a
+// tree whose root holds every key and whose levels split clusters further,
+// like hierarchical k-means ("Latent Sparse Attention Breaks Through the
+// Million-Token Context Bottleneck", kongchang.com, section "How LSA Sidesteps
+// Per-Key Scoring with Hierarchical Clustering"); each cluster is a centroid
+// stored with references to its keys ("Latent sparse attention",
+// bdtechtalks.com, section "How latent sparse attention works").
+//
+// Work layout.  Per level, the keys sit in `perm` grouped by their parent
+// node, ascending within a parent.  A parent's range is cut into pieces of
+// kPiece positions (one workgroup each), so every piece belongs to exactly one
+// parent and can stage that parent's child centroids in LDS.  One Lloyd round
+// is: assign (nearest child, plus the key's stable rank among the piece's keys
+// with the same child), a per-parent prefix over pieces, a scatter that
+// regroups the keys by child in ascending position, and a fixed-order mean.
+// Distances, projection sums and means are accumulated in double in ascending
+// dimension / key order with no fused multiply-add where a product is
+// inexact, so the tree does not depend on scheduling.
+#include "common.h"
+#include "internal.h"
+
+namespace lsa {
+
+constexpr int kPiece = 256;   // keys per piece = threads per assign workgroup
+
+struct Piece { int32_t u, start, len; };
+
+// ---------------------------------------------------------------- projection
+// z[g][j][c] = fl32(sum_i K[g][j][i] * W[g][i][c]), i ascending.  Each product
+// of a bf16/fp32 key element with an fp32 weight is exact in double, so a
+// fused multiply-add rounds exactly like a multiply followed by an add.
+template <typename T>
+__global__ __launch_bounds__(256) void k_project(const T *__restrict__ K, const float *__restrict__ W,
+                                                 float *__restrict__ Z, int64_t n, int d, int r) {
+    constexpr int KT = 32;    // keys per workgroup
+    constexpr int IC = 64;    // input dimensions staged per pass
+    __shared__ float Ws[IC * 64];
+    __shared__ float Ks[KT * IC];
+    const int g = blockIdx.y;
+    const int64_t key0 = (int64_t)blockIdx.x * KT;
+    const int c = threadIdx.x & 63;
+    const int q = threadIdx.x >> 6;            // 0..3
+    const T *Kg = K + (size_t)g * n * d;
+    const float *Wg = W + (size_t)g * d * r;
+    double acc[KT / 4];
+#pragma unroll
+    for (int t = 0; t < KT / 4; ++t) acc[t] = 0.0;
+    for (int i0 = 0; i0 < d; i0 += IC) {
+        const int ic = min(IC, d - i0);
+        for (int idx = threadIdx.x; idx < ic * r; idx += blockDim.x)
+            Ws[(idx / r) * 64 + (idx % r)] = Wg[(size_t)(i0 + idx / r) * r + (idx % r)];
+        for (int idx = threadIdx.x; idx < KT * ic; idx += blockDim.x) {
+            const int kk = idx / ic, ii = idx % ic;
+            const int64_t j = key0 + kk;
+            Ks[kk * IC + ii] = (j < n) ? to_float(Kg[(size_t)j * d + i0 + ii]) : 0.0f;
+        }
+        __syncthreads();
+        if (c < r) {
+            for (int ii = 0; ii < ic; ++ii) {
+                const double w = (double)Ws[ii * 64 + c];
+#pragma unroll
+                for (int t = 0; t < KT / 4; ++t)
+                    acc[t] = fma((double)Ks[(q + 4 * t) * IC + ii], w, acc[t]);
+            }
+        }
+        __syncthreads();
+    }
+    if (c < r) {
+#pragma unroll
+        for (int t = 0; t < KT / 4; ++t) {
+            const int64_t j = key0 + q + 4 * t;
+            if (j < n) Z[((size_t)g * n + j) * r + c] = (float)acc[t];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- level setup
+__global__ void k_iota(int32_t *perm, int64_t n, int h) {
+    const int64_t tot = n * h;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x)
+        perm[i] = (int32_t)(i % n);
+}
+
+__global__ void k_root_off(int32_t *off, int64_t n, int h) {
+    for (int g = threadIdx.x; g < h; g += blockDim.x) { off[2 * g] = 0; off[2 * g + 1] = (int32_t)n; }
+}
+
+// pieces per parent: np[g][u] = ceil(m_u / kPiece)
+__global__ void k_piece_count(const int32_t *__restrict__ off_prev, int32_t *__restrict__ np, int64_t S, int h) {
+    const int64_t tot = S * h;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t g = i / S, u = i % S;
+        const int32_t *o = off_prev + g * (S + 1);
+        const int32_t m = o[u + 1] - o[u];
+        np[i] = (m + kPiece - 1) / kPiece;
+    }
+}
+
+// exclusive scan of np per head (one workgroup of 1024 threads per head)
+__global__ __launch_bounds__(1024) void k_scan_heads(const int32_t *__restrict__ in, int32_t *__restrict__ out,
+                                                     int32_t *__restrict__ total, int64_t S) {
+    __shared__ int scratch[17];
+    const int g = blockIdx.x;
+    const int32_t *a = in + (size_t)g * S;
+    int32_t *o = out + (size_t)g * S;
+    const int64_t chunk = (S + blockDim.x - 1) / blockDim.x;
+    const int64_t s = threadIdx.x * chunk, e = min(S, s + chunk);
+    int local = 0;
+    for (int64_t i = s; i < e; ++i) local += a[i];
+    int tot;
+    int run = block_excl_scan(local, scratch, &tot);
+    for (int64_t i = s; i < e; ++i) { const int v = a[i]; o[i] = run; run += v; }
+    if (threadIdx.x == 0) total[g] = tot;
+}
+
+__global__ void k_piece_fill(const int32_t *__restrict__ pbase, const int32_t *__restrict__ np,
+                             const int32_t *__restrict__ off_prev, const int32_t *__restrict__ total,
+                             Piece *__restrict__ pieces, int64_t S, int64_t NPmax) {
+    const int g = blockIdx.y;
+    const int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (p >= total[g]) return;
+    const int32_t *pb = pbase + (size_t)g * S;
+    // largest u with pb[u] <= p
+    int64_t lo = 0, hi = S;   // invariant: pb[lo] <= p, answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (pb[mid] <= p) lo = mid; else hi = mid;
+    }
+    const int64_t u = lo;
+    const int32_t *o = off_prev + (size_t)g * (S + 1);
+    const int32_t m = o[u + 1] - o[u];
+    const int32_t t = (int32_t)(p - pb[u]);
+    Piece pc;
+    pc.u = (int32_t)u;
+    pc.start = o[u] + t * kPiece;
+    pc.len = min(kPiece, m - t * kPiece);
+    pieces[(size_t)g * NPmax + p] = pc;
+    (void)np;
+}
+
+// Child seeds: child c < a = min(b, m) of parent u starts at the member of
+// rank floor(c*m/a); the other children are zero and stay empty.
+__global__ void k_init(const int32_t *__restrict__ off_prev, const int32_t *__restrict__ perm_prev,
+                       const float *__restrict__ Z, float *__restrict__ C, int64_t S, int b, int r, int64_t n, int h) {
+    const int64_t tot = (int64_t)h * S * b;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t g = i / (S * b);
+        const int64_t v = i % (S * b);
+        const int64_t u = v / b;
+        const int c = (int)(v % b);
+        const int32_t *o = off_prev + g * (S + 1);
+        const int64_t m = o[u + 1] - o[u];
+        const int a = (int)min((int64_t)b, m);
+        float *dst = C + (size_t)i * r;
+        if (c < a) {
+            const int32_t j = perm_prev[g * n + o[u] + ((int64_t)c * m) / a];
+            const float *src = Z + ((size_t)g * n + j) * r;
+            for (int x = 0; x < r; ++x) dst[x] = src[x];
+        } else {
+            for (int x = 0; x < r; ++x) dst[x] = 0.0f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- Lloyd round
+// Squared Euclidean distance in double, dimensions ascending; the difference
+// of two floats and its square are each rounded once, then added.
+LSA_DEV double sq_dist(const float *z, const float *cs, int r) {
+#pragma clang fp contract(off)
+    double dist = 0.0;
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+        if (x < r) {
+            const double diff = (double)z[x] - (double)cs[x];
+            const double sq = diff * diff;
+            dist = dist + sq;
+        }
+    }
+    return dist;
+}
+
+__global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pieces, const int32_t *__restrict__ total,
+                                                   const int32_t *__restrict__ off_prev,
+                                                   const int32_t *__restrict__ perm_prev, const float *__restrict__ Z,
+                                                   const float *__restrict__ C, uint8_t *__restrict__ child,
+                                                   uint8_t *__restrict__ lrank, int32_t *__restrict__ hist, int64_t S,
+                                                   int64_t NPmax, int b, int r, int64_t n) {
+    __shared__ float Cs[64 * 65];
+    __shared__ int wcnt[kPiece / kWave][64];
+    const int g = blockIdx.y;
+    const int64_t p = blockIdx.x;
+    if (p >= total[g]) return;
+    const Piece pc = pieces[(size_t)g * NPmax + p];
+    const int32_t *o = off_prev + (size_t)g * (S + 1);
+    const int64_t m = o[pc.u + 1] - o[pc.u];
+    const int a = (int)min((int64_t)b, m);
+    const float *Cu = C + ((size_t)g * S * b + (size_t)pc.u * b) * r;
+    for (int idx = threadIdx.x; idx < a * r; idx += blockDim.x) Cs[(idx / r) * 65 + idx % r] = Cu[idx];
+    for (int idx = threadIdx.x; idx < (kPiece / kWave) * 64; idx += blockDim.x) (&wcnt[0][0])[idx] = 0;
+    __syncthreads();
+
+    const bool valid = threadIdx.x < pc.len;
+    const int64_t posn = (int64_t)pc.start + threadIdx.x;
+    int best = 0;
+    if (valid) {
+        const int32_t j = perm_prev[(size_t)g * n + posn];
+        const float *zr = Z + ((size_t)g * n + j) * r;
+        float z[64];
+#pragma unroll
+        for (int x = 0; x < 64; ++x) z[x] = (x < r) ? zr[x] : 0.0f;
+        double bestd = 0.0;
+        for (int c = 0; c < a; ++c) {
+            const double dist = sq_dist(z, Cs + c * 65, r);
+            if (c == 0 || dist < bestd) { bestd = dist; best = c; }
+        }
+    }
+    // stable rank among this wave's lanes with the same child (6-bit match)
+    uint64_t eq = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+        const bool on = (best >> bit) & 1;
+        const uint64_t bb = __ballot(valid && on);
+        eq &= on ? bb : ~bb;
+    }
+    const int w = threadIdx.x / kWave;
+    const int rw = __popcll(eq & lanemask_lt());
+    if (valid && rw == 0) wcnt[w][best] = __popcll(eq);
+    __syncthreads();
+    if (valid) {
+        int rank = rw;
+        for (int w2 = 0; w2 < w; ++w2) rank += wcnt[w2][best];
+        child[(size_t)g * n + posn] = (uint8_t)best;
+        lrank[(size_t)g * n + posn] = (uint8_t)rank;
+    }
+    if (threadIdx.x < b) {
+        int s = 0;
+        for (int w2 = 0; w2 < kPiece / kWave; ++w2) s += wcnt[w2][threadIdx.x];
+        hist[((size_t)g * NPmax + p) * b + threadIdx.x] = s;
+    }
+}
+
+// One wave per parent, lane = child: prefix of the child histograms over the
+// parent's pieces, child counts, and child offsets into the regrouped perm.
+__global__ __launch_bounds__(256) void k_seg_prefix(const int32_t *__restrict__ pbase, const int32_t *__restrict__ np,
+                                                    const int32_t *__restrict__ hist, int32_t *__restrict__ pref,
+                                                    const int32_t *__restrict__ off_prev, int32_t *__restrict__ off_new,
+                                                    int32_t *__restrict__ cnt, int64_t S, int64_t NPmax, int b,
+                                                    int64_t n) {
+    const int g = blockIdx.y;
+    const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (u >= S) return;
+    const int c = lane_id();
+    const int32_t base = pbase[(size_t)g * S + u];
+    const int32_t cntp = np[(size_t)g * S + u];
+    const bool act = c < b;
+    const size_t row0 = ((size_t)g * NPmax + base) * b + c;
+    int run = 0;
+    int q = 0;
+    for (; q + 8 <= cntp; q += 8) {
+        int hv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) hv[t] = act ? hist[row0 + (size_t)(q + t) * b] : 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (act) pref[row0 + (size_t)(q + t) * b] = run;
+            run += hv[t];
+        }
+    }
+    for (; q < cntp; ++q) {
+        const int hv = act ? hist[row0 + (size_t)q * b] : 0;
+        if (act) pref[row0 + (size_t)q * b] = run;
+        run += hv;
+    }
+    const int incl = wave_incl_scan_add(act ? run : 0);
+    const int ex = incl - (act ? run : 0);
+    const int64_t nodes = S * b;
+    if (act) {
+        cnt[(size_t)g * nodes + u * b + c] = run;
+        off_new[(size_t)g * (nodes + 1) + u * b + c] = off_prev[(size_t)g * (S + 1) + u] + ex;
+    }
+    if (u == S - 1 && c == 0) off_new[(size_t)g * (nodes + 1) + nodes] = (int32_t)n;
+}
+
+__global__ __launch_bounds__(kPiece) void k_scatter(const Piece *__restrict__ pieces, const int32_t *__restrict__ total,
+                                                    const uint8_t *__restrict__ child, const uint8_t *__restrict__ lrank,
+                                                    const int32_t *__restrict__ pref, const int32_t *__restrict__ off_new,
+                                                    const int32_t *__restrict__ perm_prev, int32_t *__restrict__ perm_new,
+                                                    int64_t S, int64_t NPmax, int b, int64_t n) {
+    const int g = blockIdx.y;
+    const int64_t p = blockIdx.x;
+    if (p >= total[g]) return;
+    const Piece pc = pieces[(size_t)g * NPmax + p];
+    if (threadIdx.x >= pc.len) return;
+    const int64_t posn = (int64_t)pc.start + threadIdx.x;
+    const int c = child[(size_t)g * n + posn];
+    const int64_t nodes = S * b;
+    const int64_t dest = (int64_t)off_new[(size_t)g * (nodes + 1) + (int64_t)pc.u * b + c] +
+                         pref[((size_t)g * NPmax + p) * b + c] + lrank[(size_t)g * n + posn];
+    perm_new[(size_t)g * n + dest] = perm_prev[(size_t)g * n + posn];
+}
+
+// Centroid = fl32(sum of member latents / count), members in ascending key
+// order, double accumulation; one wave per node (lane = latent dimension).
+// A node without members keeps its centroid.  In parent mode a wave walks all
+// children of one parent, which keeps the wave count small on deep levels.
+LSA_DEV void mean_node(const int32_t *__restrict__ perm, const float *__restrict__ Zg, float *__restrict__ Cv,
+                       int32_t s, int32_t cntv, int r) {
+    const int x = lane_id();
+    double acc = 0.0;
+    int t = 0;
+    for (; t + 8 <= cntv; t += 8) {
+        float zv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int32_t j = perm[s + t + q];
+            zv[q] = (x < r) ? Zg[(size_t)j * r + x] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc = acc + (double)zv[q];
+    }
+    for (; t < cntv; ++t) {
+        const int32_t j = perm[s + t];
+        acc = acc + (double)((x < r) ? Zg[(size_t)j * r + x] : 0.0f);
+    }
+    if (x < r) Cv[x] = (float)(acc / (double)cntv);
+}
+
+__global__ __launch_bounds__(256) void k_mean(const int32_t *__restrict__ off_new, const int32_t *__restrict__ cnt,
+                                              const int32_t *__restrict__ perm_new, const float *__restrict__ Z,
+                                              float *__restrict__ C, int64_t S, int b, int r, int64_t n, int parent_mode) {
+    const int g = blockIdx.y;
+    const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t nodes = S * b;
+    const int32_t *o = off_new + (size_t)g * (nodes + 1);
+    const int32_t *cn = cnt + (size_t)g * nodes;
+    const int32_t *pm = perm_new + (size_t)g * n;
+    const float *Zg = Z + (size_t)g * n * r;
+    float *Cg = C + (size_t)g * nodes * r;
+    if (parent_mode) {
+        if (wv >= S) return;
+        for (int c = 0; c < b; ++c) {
+            const int64_t v = wv * b + c;
+            const int32_t cv = cn[v];
+            if (cv > 0) mean_node(pm, Zg, Cg + (size_t)v * r, o[v], cv, r);
+        }
+    } else {
+        if (wv >= nodes) return;
+        const int32_t cv = cn[wv];
+        if (cv > 0) mean_node(pm, Zg, Cg + (size_t)wv * r, o[wv], cv, r);
+    }
+}
+
+// ---------------------------------------------------------------- host driver
+static inline int64_t ipow64(int64_t b, int e) { int64_t v = 1; while (e-- > 0) v *= b; return v; }
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BuildWs {
+    float *Z;
+    int32_t *permA, *permB, *offA, *offB, *np, *pbase, *total, *hist, *pref;
+    uint8_t *child, *lrank;
+    Piece *pieces;
+    size_t bytes;
+};
+
+static BuildWs carve_build_ws(char *base, int64_t n, int h, int r, int b, int L) {
+    const int64_t Smax = ipow64(b, L - 1);
+    const int64_t NPmax = (n + kPiece - 1) / kPiece + Smax;
+    size_t cur = 0;
+    BuildWs w{};
+    auto take = [&](size_t bytes) { char *p = base ? base + cur : nullptr; cur = align256(cur + bytes); return p; };
+    w.Z = (float *)take(sizeof(float) * (size_t)h * n * r);
+    w.permA = (int32_t *)take(sizeof(int32_t) * (size_t)h * n);
+    w.permB = (int32_t *)take(sizeof(int32_t) * (size_t)h * n);
+    w.offA = (int32_t *)take(sizeof(int32_t) * (size_t)h * (Smax + 1));
+    w.offB = (int32_t *)take(sizeof(int32_t) * (size_t)h * (Smax + 1));
+    w.np = (int32_t *)take(sizeof(int32_t) * (size_t)h * Smax);
+    w.pbase = (int32_t *)take(sizeof(int32_t) * (size_t)h * Smax);
+    w.total = (int32_t *)take(sizeof(int32_t) * (size_t)h);
+    w.pieces = (Piece *)take(sizeof(Piece) * (size_t)h * NPmax);
+    w.hist = (int32_t *)take(sizeof(int32_t) * (size_t)h * NPmax * b);
+    w.pref = (int32_t *)take(sizeof(int32_t) * (size_t)h * NPmax * b);
+    w.child = (uint8_t *)take((size_t)h * n);
+    w.lrank = (uint8_t *)take((size_t)h * n);
+    w.bytes = cur;
+    return w;
+}
+
+int64_t build_workspace_bytes(int64_t n, int h, int r, int b, int L) {
+    return (int64_t)carve_build_ws(nullptr, n, h, r, b, L).bytes;
+}
+
+static inline unsigned grid1(int64_t tot, int bs) {
+    int64_t g = (tot + bs - 1) / bs;
+    if (g > (1 << 20)) g = 1 << 20;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,
+                       int iters, char *index, const int64_t *centroid_off, const int64_t *count_off,
+                       int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st) {
+    BuildWs w = carve_build_ws((char *)ws, n, h, r, b, L);
+    const dim3 pg((unsigned)((n + 31) / 32), (unsigned)h);
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_project<float>, pg, dim3(256), 0, st, (const float *)K, W, w.Z, n, d, r);
+    else
+        hipLaunchKernelGGL(k_project<bf16_t>, pg, dim3(256), 0, st, (const bf16_t *)K, W, w.Z, n, d, r);
+    hipLaunchKernelGGL(k_iota, dim3(grid1(n * h, 256)), dim3(256), 0, st, w.permA, n, h);
+    hipLaunchKernelGGL(k_root_off, dim3(1), dim3(64), 0, st, w.offA, n, h);
+    int32_t *prev_perm = w.permA, *prev_off = w.offA;
+    int32_t *idx_perm = (int32_t *)(index + perm_off);
+    int32_t *idx_leaf = (int32_t *)(index + leaf_off_off);
+    for (int l = 1; l <= L; ++l) {
+        const int64_t S = ipow64(b, l - 1);
+        const int64_t nodes = S * b;
+        const int64_t NPmax = (n + kPiece - 1) / kPiece + S;
+        int32_t *next_perm = (l == L) ? idx_perm : (prev_perm == w.permA ? w.permB : w.permA);
+        int32_t *next_off = (l == L) ? idx_leaf : (prev_off == w.offA ? w.offB : w.offA);
+        float *C = (float *)(index + centroid_off[l]);
+        int32_t *cnt = (int32_t *)(index + count_off[l]);
+        hipLaunchKernelGGL(k_piece_count, dim3(grid1(S * h, 256)), dim3(256), 0, st, prev_off, w.np, S, h);
+        hipLaunchKernelGGL(k_scan_heads, dim3(h), dim3(1024), 0, st, w.np, w.pbase, w.total, S);
+        hipLaunchKernelGGL(k_piece_fill, dim3((unsigned)((NPmax + 255) / 256), (unsigned)h), dim3(256), 0, st, w.pbase,
+                           w.np, prev_off, w.total, w.pieces, S, NPmax);
+        hipLaunchKernelGGL(k_init, dim3(grid1(nodes * h, 256)), dim3(256), 0, st, prev_off, prev_perm, w.Z, C, S, b, r, n,
+                           h);
+        const bool parent_mode = S * h >= 1024;
+        const int64_t mean_waves = parent_mode ? S : nodes;
+        for (int t = 0; t < iters; ++t) {
+            hipLaunchKernelGGL(k_assign, dim3((unsigned)NPmax, (unsigned)h), dim3(kPiece), 0, st, w.pieces, w.total,
+                               prev_off, prev_perm, w.Z, C, w.child, w.lrank, w.hist, S, NPmax, b, r, n);
+            hipLaunchKernelGGL(k_seg_prefix, dim3((unsigned)((S + 3) / 4), (unsigned)h), dim3(256), 0, st, w.pbase, w.np,
+                               w.hist, w.pref, prev_off, next_off, cnt, S, NPmax, b, n);
+            hipLaunchKernelGGL(k_scatter, dim3((unsigned)NPmax, (unsigned)h), dim3(kPiece), 0, st, w.pieces, w.total,
+                               w.child, w.lrank, w.pref, next_off, prev_perm, next_perm, S, NPmax, b, n);
+            hipLaunchKernelGGL(k_mean, dim3((unsigned)((mean_waves + 3) / 4), (unsigned)h), dim3(256), 0, st, next_off,
+                               cnt, next_perm, w.Z, C, S, b, r, n, parent_mode ? 1 : 0);
+        }
+        prev_perm = next_perm;
+        prev_off = next_off;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,25 @@
+// Host-side entry points of the kernel files, used by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+int64_t build_workspace_bytes(int64_t n, int h, int r, int b, int L);
+hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,
+                       int iters, char *index, const int64_t *centroid_off, const int64_t *count_off,
+                       int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st);
+
+hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
+                       int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
+                       const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
+                       int k, int32_t *sel, int32_t *sel_count, float *sel_cutoff, hipStream_t st);
+
+int attend_nsplit(int64_t m, int h_kv, int k);
+int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k);
+hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int64_t n,
+                  int d, const int32_t *sel, const int32_t *sel_count, int k, float scale, void *out, float *lse,
+                  void *ws, hipStream_t st);
+
+}  // namespace lsa

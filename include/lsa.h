@@ -1,0 +1,201 @@
+/*
+ * lsa.h - C ABI of the latent-sparse-attention (LSA) layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer follows the pages that describe the method:
+ *   - "Latent Sparse Attention Breaks Through the Million-Token Context
+ *     Bottleneck" (kongchang.com), section "How LSA Sidesteps Per-Key Scoring
+ *     with Hierarchical Clustering": keys are mapped into a learned latent
+ *     space and clustered top-down into a tree; a query scores a few clusters
+ *     per level from the root and descends the best branches to the leaves.
+ *   - "Latent sparse attention" (bdtechtalks.com), section "How latent sparse
+ *     attention works": each cluster keeps a centroid and references to its
+ *     keys; a fixed search budget per level; a fixed number of original keys
+ *     is retrieved from the chosen clusters and attention runs over them.
+ *   - kongchang.com, section "The Accuracy-Efficiency Dilemma of Sparse
+ *     Attention": sparse attention lets each query interact with k keys.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named as device buffers are device memory on the current
+ *     HIP device; the caller owns every buffer.  The library allocates no
+ *     memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns; results are
+ *     ready once the stream reaches that point.
+ *   - Arguments are checked on the host before anything is enqueued.  A call
+ *     that returns an error has enqueued nothing, except LSA_EHIP, which
+ *     reports a failed launch (the stream's earlier work is unaffected).
+ *   - Layout: row-major, innermost dimension last, no padding.  "bf16" is
+ *     IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *   - Positions are int32: n <= 2^31 - 1 keys.
+ *   - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define LSA_OK 0
+#define LSA_EINVAL (-1)       /* a shape, size or pointer argument is invalid       */
+#define LSA_EUNSUPPORTED (-2) /* valid, but outside what the kernels implement      */
+#define LSA_ENOSPC (-3)       /* a caller-provided buffer is too small              */
+#define LSA_EHIP (-4)         /* the HIP runtime reported an error on launch        */
+
+/* Element types of Q, K, V and the attention output. */
+#define LSA_F32 0
+#define LSA_BF16 1
+
+#define LSA_MAX_LEVELS 6
+
+/*
+ * Index descriptor: where each array of the tree lives inside one caller-owned
+ * device buffer ("index memory").  Plain data; filled by lsa_index_layout.
+ *
+ * The tree is a complete b-ary tree with L levels below the root (the root
+ * holds all keys; level l has b^l nodes; the children of node v are
+ * v*b + c, c = 0..b-1; nodes may be empty).  For each KV head g:
+ *   centroids of level l : float [h_kv][b^l][r]   at byte offset centroid_off[l]
+ *   member counts level l: int32 [h_kv][b^l]      at byte offset count_off[l]
+ *   leaf CSR offsets     : int32 [h_kv][b^L + 1]  at byte offset leaf_off_off
+ *   leaf members (keys)  : int32 [h_kv][n]        at byte offset perm_off
+ * Leaf v of head g holds keys perm[g][leaf_off[g][v] .. leaf_off[g][v+1]) in
+ * ascending position.  A node with count 0 is empty.  Entries at index 0 of
+ * centroid_off/count_off are unused.
+ */
+typedef struct lsa_index_desc {
+    int64_t n;
+    int32_t h_kv, r, b, L;
+    int64_t nodes[LSA_MAX_LEVELS + 1];
+    int64_t centroid_off[LSA_MAX_LEVELS + 1];
+    int64_t count_off[LSA_MAX_LEVELS + 1];
+    int64_t leaf_off_off;
+    int64_t perm_off;
+    int64_t bytes;
+} lsa_index_desc;
+
+/* Version of this ABI (the value of LSA_ABI_VERSION). */
+#define LSA_ABI_VERSION 1
+int lsa_abi_version(void);
+
+/* Message for a return code (static storage, never NULL). */
+const char *lsa_strerror(int code);
+
+/*
+ * Fill *desc with the layout of an index for n keys, h_kv KV heads, latent
+ * dimension r, branching b and L levels.  Host only; touches no device.
+ * Limits: 1 <= n <= 2^31-1, 1 <= h_kv, 1 <= r <= 64, 2 <= b <= 64,
+ * 1 <= L <= LSA_MAX_LEVELS, b^L <= 2^31 - 2.  Arrays start on 256-byte
+ * boundaries.
+ */
+int lsa_index_layout(int64_t n, int h_kv, int r, int b, int L, lsa_index_desc *desc);
+
+/*
+ * Bytes of device workspace lsa_build_index needs for these sizes (*bytes).
+ */
+int lsa_build_workspace_bytes(int64_t n, int h_kv, int d, int r, int b, int L, int64_t *bytes);
+
+/*
+ * Build the cluster tree of every KV head (kongchang.com, "How LSA Sidesteps
+ * ...": the tree over latent keys is precomputed; bdtechtalks.com, "How latent
+ * sparse attention works": centroid plus key references per cluster).
+ *
+ *   K        device, [h_kv][n][d] of `dtype` (LSA_F32 or LSA_BF16)
+ *   W        device, float [h_kv][d][r]: the latent projection of each KV head
+ *   iters    Lloyd rounds per level (>= 1)
+ *   index    device, desc->bytes bytes, written completely
+ *   ws       device workspace of lsa_build_workspace_bytes bytes
+ *   desc     out (host): the layout, as lsa_index_layout returns it
+ *
+ * Per head: z_j = fl32(K_j . W) (latent keys); for l = 1..L, every node of
+ * level l-1 splits its members into b children by `iters` rounds of k-means:
+ * a = min(b, m) children are seeded with the members of rank floor(c*m/a) in
+ * ascending key order, each round assigns every member to the nearest seeded
+ * child by squared Euclidean distance (ties to the lower child) and replaces
+ * each child's centroid by fl32(mean of its members) (a child without members
+ * keeps its centroid).  The last round's assignment is the partition.
+ * Distances, sums and means are accumulated in double, in ascending dimension
+ * and ascending key order, so the tree is bit-identical across runs.
+ * Limits as lsa_index_layout, plus 1 <= d <= 256.
+ */
+int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const float *W, int r,
+                    int b, int L, int iters, void *index, int64_t index_bytes, void *ws,
+                    int64_t ws_bytes, lsa_index_desc *desc, void *stream);
+
+/*
+ * Bytes of device workspace lsa_select needs (*bytes; currently 0).
+ */
+int lsa_select_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, int beam, int k,
+                               int64_t *bytes);
+
+/*
+ * Select keys for every (query row, KV head) by top-down descent of the tree
+ * (kongchang.com, "How LSA Sidesteps ...": score a few candidate clusters per
+ * level and descend; bdtechtalks.com, "How latent sparse attention works":
+ * fixed budget per level, a fixed number of original keys retrieved;
+ * "The compute bottleneck of sparse attention": causal attention sees only
+ * earlier tokens).
+ *
+ *   Q        device, [m][h_q][d] of `dtype`; query head h uses KV head h / (h_q/h_kv)
+ *   q_pos    device, int32 [m]: position of each query row (decode: n)
+ *   index    device, built by lsa_build_index with *desc
+ *   W        device, float [h_kv][d][r]: the same projection as the keys
+ *   beam     nodes kept per level at levels 1..L-1 (>= 1)
+ *   k        keys retrieved per row and KV head (>= 1)
+ *   sel      device out, int32 [m][h_kv][k]: selected keys in ascending order,
+ *            padded with -1
+ *   sel_count device out, int32 [m][h_kv]: number of selected keys (<= k)
+ *   sel_cutoff device out or NULL, float [m][h_kv]: score of the leaf that
+ *            supplied the k-th key, -inf when fewer than k keys were eligible
+ *
+ * The G = h_q/h_kv query heads of a KV head share one selection, scored with
+ * their mean qbar projected by W: u = fl32(qbar . W_g); a node's score is
+ * fl32(u . centroid).  Level-1 candidates are the root's non-empty children;
+ * at levels 1..L-1 the best min(beam, #candidates) in (score desc, id asc)
+ * order are kept and their non-empty children become the next candidates; all
+ * level-L candidates are candidate leaves.  Leaves are visited in (score desc,
+ * id asc) order, each giving its members in ascending position; keys at
+ * positions > q_pos are skipped; the first k are taken.  Dot products are
+ * accumulated in double in ascending index order.
+ * Limits: h_q % h_kv == 0, 1 <= d <= 256, beam * b <= 4096, k <= 8192.
+ */
+int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
+               const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,
+               int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes,
+               void *stream);
+
+/*
+ * Bytes of device workspace lsa_attend needs (*bytes).
+ */
+int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64_t *bytes);
+
+/*
+ * Softmax attention of every query head over its KV head's selected keys
+ * (kongchang.com, "The Accuracy-Efficiency Dilemma of Sparse Attention": each
+ * query interacts with only k keys).
+ *
+ *   Q        device, [m][h_q][d] of `dtype`
+ *   K, V     device, [h_kv][n][d] of `dtype`
+ *   sel, sel_count  as written by lsa_select (k = row stride of sel)
+ *   scale    score scale; 0 means 1/sqrt(d)
+ *   out      device out, [m][h_q][d] of `dtype` (fp32 accumulation, rounded
+ *            to nearest even for bf16)
+ *   lse      device out or NULL, float [m][h_q]: natural-log sum of exp of the
+ *            scaled scores; -inf for an empty selection (whose out row is 0)
+ *   ws       device workspace of lsa_attend_workspace_bytes bytes
+ * Entries of sel must lie in [0, n).  Limits: h_q % h_kv == 0, h_q/h_kv <= 16,
+ * 8 <= d <= 256 with d % 8 == 0, k <= 8192.
+ */
+int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q,
+               int h_kv, int64_t n, int d, const int32_t *sel, const int32_t *sel_count, int k,
+               float scale, void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports every declared entry point and rejects
+bad arguments on the host (no device work is enqueued by these calls)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_key_indexing_amd as lsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "lsa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = lsa.lib()
+    names = _declared()
+    assert len(names) >= 9
+    for nm in names:
+        assert hasattr(L, nm), nm
+    assert sorted(names) == sorted(lsa.EXPORTS)
+    assert L.lsa_abi_version() == 1
+    assert L.lsa_strerror(-3).decode() == "buffer too small"
+
+
+def test_index_layout_sizes():
+    d = lsa.index_layout(1 << 20, 4, 64, 64, 3)
+    assert list(d.nodes[:4]) == [1, 64, 4096, 262144]
+    assert d.centroid_off[1] == 0
+    for l in range(1, 4):
+        assert d.centroid_off[l] % 256 == 0 and d.count_off[l] % 256 == 0
+    assert d.count_off[1] >= d.centroid_off[3] + 4 * 262144 * 64 * 4
+    assert d.perm_off >= d.leaf_off_off + 4 * (262144 + 1) * 4
+    assert d.bytes >= d.perm_off + 4 * (1 << 20) * 4
+    # the 10M-token tree: 64^4 leaves per head
+    d = lsa.index_layout(10 << 20, 4, 64, 64, 4)
+    assert d.nodes[4] == 64 ** 4
+    assert d.bytes > 4 * 64 ** 4 * 64 * 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 8, 2, 1), lsa.LSA_EINVAL),
+    ((10, 1, 8, 1, 1), lsa.LSA_EINVAL),
+    ((10, 1, 65, 2, 1), lsa.LSA_EUNSUPPORTED),
+    ((10, 1, 8, 65, 1), lsa.LSA_EUNSUPPORTED),
+    ((10, 1, 8, 64, 7), lsa.LSA_EUNSUPPORTED),
+    ((10, 1, 8, 64, 6), lsa.LSA_EUNSUPPORTED),     # 64^6 leaves overflow int32
+    ((10, 0, 8, 2, 1), lsa.LSA_EINVAL),
+])
+def test_index_layout_rejects(args, code):
+    d = lsa.IndexDesc()
+    assert lsa.lib().lsa_index_layout(*args, ctypes.byref(d)) == code
+
+
+def test_entry_points_validate_before_touching_the_device():
+    L = lsa.lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)     # never dereferenced: every call below fails its host checks
+    d = lsa.IndexDesc()
+    # build: iters < 1, small index buffer, small workspace
+    assert L.lsa_build_index(fake, 0, 100, 1, 16, fake, 8, 4, 2, 0, fake, 1 << 30, fake, 1 << 30,
+                             ctypes.byref(d), None) == lsa.LSA_EINVAL
+    assert L.lsa_build_index(fake, 0, 100, 1, 16, fake, 8, 4, 2, 5, fake, 16, fake, 1 << 30,
+                             ctypes.byref(d), None) == lsa.LSA_ENOSPC
+    assert L.lsa_build_index(fake, 0, 100, 1, 16, fake, 8, 4, 2, 5, fake, 1 << 30, fake, 16,
+                             ctypes.byref(d), None) == lsa.LSA_ENOSPC
+    assert L.lsa_build_index(fake, 7, 100, 1, 16, fake, 8, 4, 2, 5, fake, 1 << 30, fake, 1 << 30,
+                             ctypes.byref(d), None) == lsa.LSA_EUNSUPPORTED
+    assert L.lsa_build_index(fake, 0, 100, 1, 300, fake, 8, 4, 2, 5, fake, 1 << 30, fake, 1 << 30,
+                             ctypes.byref(d), None) == lsa.LSA_EUNSUPPORTED
+    # select: descriptor must be one lsa_index_layout produced
+    d = lsa.index_layout(100, 2, 8, 4, 2)
+    bad = lsa.IndexDesc.from_buffer_copy(d)
+    bad.bytes += 1
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 2, 8, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL
+    assert L.lsa_select(fake, 0, 1, 3, 16, fake, ctypes.byref(d), fake, fake, 2, 8, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL          # h_q % h_kv != 0
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2000, 8, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EUNSUPPORTED    # beam * b > 4096
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 9000, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EUNSUPPORTED    # k > 8192
+    assert L.lsa_select(fake, 0, 0, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, fake, fake, None, None, 0,
+                        None) == lsa.LSA_OK              # m = 0: nothing to do
+    # attend
+    f = ctypes.c_float
+    assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 3, 100, 64, fake, fake, 8, f(0), fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL          # h_q % h_kv
+    assert L.lsa_attend(fake, fake, fake, 0, 1, 34, 2, 100, 64, fake, fake, 8, f(0), fake, None, None, 0,
+                        None) == lsa.LSA_EUNSUPPORTED    # G = 17
+    assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 2, 100, 60, fake, fake, 8, f(0), fake, None, None, 0,
+                        None) == lsa.LSA_EUNSUPPORTED    # d % 8
+    assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 2, 100, 64, fake, fake, 8, f(-1), fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL          # negative scale
+    nws = lsa.attend_workspace_bytes(1, 32, 4, 128, 2048)
+    assert nws > 0
+    assert L.lsa_attend(fake, fake, fake, 1, 1, 32, 4, 100, 128, fake, fake, 2048, f(0), fake, None, None, 0,
+                        None) == lsa.LSA_ENOSPC
+    assert lsa.build_workspace_bytes(1 << 20, 4, 128, 64, 64, 3) > 4 * (1 << 20) * 64 * 4

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP library against the CPU oracle on identical seeded inputs.
+
+Index build and selection must match bit for bit (both sides accumulate in
+double in the same order); attention must match within max-abs 1e-4 (fp32
+inputs) or 2e-2 (bf16 inputs)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import (assert_index_equal, assert_same_bits, compact_kv, host_index, np32, replay_node, say)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hierarchical_key_indexing_amd as m
+    m.lib()
+    return m
+
+
+def _wl(name, **kw):
+    return synth.WORKLOADS[name].replace(**kw) if kw else synth.WORKLOADS[name]
+
+
+# small and ragged shapes: (name, overrides)
+SMALL = [
+    ("tiny_4k", {}),
+    ("ragged_bf16_b5", dict(n=1000, h_q=4, h_kv=2, d=64, dtype="bf16", r=16, b=5, L=3, beam=3, k=100,
+                            centres=40, m=7, mode="chunk")),
+    ("wide_b64_sparse", dict(n=777, h_q=3, h_kv=3, d=32, dtype="f32", r=8, b=64, L=2, beam=2, k=50,
+                             centres=30, m=5, mode="chunk")),
+    ("multi_piece_root", dict(n=20000, h_q=16, h_kv=2, d=128, dtype="bf16", r=64, b=64, L=2, beam=8, k=1000,
+                              centres=1024, m=3, mode="decode")),
+    ("odd_r_deep", dict(n=9000, h_q=8, h_kv=1, d=48, dtype="f32", r=24, b=8, L=3, beam=5, k=333,
+                        centres=200, m=9, mode="chunk")),
+    ("n_below_b", dict(n=3, h_q=2, h_kv=1, d=16, dtype="f32", r=4, b=4, L=2, beam=2, k=5, centres=2,
+                       m=4, mode="chunk")),
+    ("single_key", dict(n=1, h_q=1, h_kv=1, d=8, dtype="bf16", r=2, b=2, L=3, beam=1, k=1, centres=1,
+                        m=1, mode="decode")),
+    ("flat_L1", dict(n=5000, h_q=4, h_kv=1, d=64, dtype="bf16", r=32, b=64, L=1, beam=1, k=700,
+                     centres=300, m=6, mode="chunk")),
+]
+
+
+def _inputs(w, dev, m=None):
+    data = synth.make_workload(w, device="cpu", m=m)
+    out = {k: v.to(dev) for k, v in data.items()}
+    out["cpu"] = data
+    return out
+
+
+def _build_both(lsa, w, data):
+    say("build", w.name, w.n, w.h_kv, w.b, w.L)
+    index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    views = lsa.index_views(index, desc)
+    gix = host_index(views, desc)
+    c = data["cpu"]
+    oix = oracle.build_index(np32(c["K"]), c["W"].numpy(), w.b, w.L, w.iters)
+    return index, desc, gix, oix
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_pipeline_matches_oracle(lsa, name, over):
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", **over) if name != "tiny_4k" else _wl("tiny_4k")
+    w = w.replace(name=name)
+    data = _inputs(w, dev)
+    index, desc, gix, oix = _build_both(lsa, w, data)
+    assert_index_equal(gix, oix)
+
+    c = data["cpu"]
+    Qh = np32(c["Q"])
+    pos = c["pos"].numpy()
+    for beam, k in [(w.beam, w.k), (1, 1), (w.b ** max(w.L - 1, 0), min(w.n + 3, 8192))]:
+        say("select", name, beam, k)
+        sel, cnt, cut = lsa.select(data["Q"], data["pos"], index, desc, data["W"], beam, k)
+        torch.cuda.synchronize()
+        ref = oracle.select(Qh, pos, oix, c["W"].numpy(), beam, k)
+        assert_same_bits(cnt.cpu().numpy(), ref["count"], "sel_count")
+        assert_same_bits(sel.cpu().numpy(), ref["sel"], "sel")
+        assert_same_bits(cut.cpu().numpy(), ref["cutoff"], "cutoff")
+        # every selected key precedes (or is) its query
+        s = sel.cpu().numpy()
+        assert np.all((s == -1) | (s <= pos[:, None, None]))
+
+        say("attend", name, beam, k)
+        out, lse = lsa.attend(data["Q"], data["K"], data["V"], sel, cnt)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attend(Qh, np32(c["K"]), np32(c["V"]), ref["sel"], ref["count"])
+        tol = TOL[w.torch_dtype]
+        assert np.max(np.abs(np32(out) - o_ref)) <= tol
+        g = lse.cpu().numpy()
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(g), fin)
+        if fin.any():
+            assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
+
+
+def test_positions_before_every_candidate_give_empty_rows(lsa):
+    """A query whose candidate leaves only hold later keys selects nothing; its
+    attention output is 0 and its lse is -inf."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", n=2000, h_q=2, h_kv=1, d=32, r=8, b=16, L=2, beam=1, k=4, centres=64, m=64, mode="all")
+    K, V = synth.make_kv(w)
+    W = synth.make_w(w)
+    pos = torch.arange(0, 64, dtype=torch.int32)
+    Q = synth.make_queries(w, K, pos)
+    Q[:] = -K[0, 1999].float()      # aims away from early keys' clusters, mostly
+    index, desc = lsa.build_index(K.to(dev), W.to(dev), w.b, w.L, 5)
+    sel, cnt, cut = lsa.select(Q.to(dev), pos.to(dev), index, desc, W.to(dev), 1, 4)
+    out, lse = lsa.attend(Q.to(dev), K.to(dev), V.to(dev), sel, cnt)
+    torch.cuda.synchronize()
+    gix = host_index(lsa.index_views(index, desc), desc)
+    ref = oracle.select(Q.numpy(), pos.numpy(), gix, W.numpy(), 1, 4)
+    assert_same_bits(sel.cpu().numpy(), ref["sel"], "sel")
+    assert_same_bits(cnt.cpu().numpy(), ref["count"], "sel_count")
+    empty = ref["count"][:, 0] == 0
+    assert empty.any() and (~empty).any()
+    o = out.cpu().numpy()
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse.cpu().numpy()[empty]))
+
+
+@pytest.mark.parametrize("G,d,dtype,m,k", [(1, 8, torch.float32, 3, 17), (2, 64, torch.bfloat16, 1, 700),
+                                           (8, 128, torch.bfloat16, 2, 2048), (16, 256, torch.float32, 2, 300),
+                                           (4, 128, torch.float32, 40, 64), (8, 128, torch.bfloat16, 300, 256)])
+def test_attend_random_sets(lsa, G, d, dtype, m, k):
+    """Attention alone on random selections (counts from 0 to k) against the oracle."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(G * 1000 + d)
+    h_kv, n = 2, 3000
+    gen = torch.Generator().manual_seed(d + G)
+    Q = torch.randn(m, G * h_kv, d, generator=gen).to(dtype)
+    K = torch.randn(h_kv, n, d, generator=gen).to(dtype)
+    V = torch.randn(h_kv, n, d, generator=gen).to(dtype)
+    cnt = rng.integers(0, k + 1, size=(m, h_kv)).astype(np.int32)
+    cnt[0, 0] = 0
+    cnt[-1, -1] = k
+    sel = np.full((m, h_kv, k), -1, np.int32)
+    for i in range(m):
+        for g in range(h_kv):
+            sel[i, g, :cnt[i, g]] = np.sort(rng.choice(n, size=cnt[i, g], replace=False))
+    say("attend_random", G, d, dtype, m, k)
+    out, lse = lsa.attend(Q.to(dev), K.to(dev), V.to(dev), torch.from_numpy(sel).to(dev),
+                          torch.from_numpy(cnt).to(dev))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attend(np32(Q), np32(K), np32(V), sel, cnt)
+    assert np.max(np.abs(np32(out) - o_ref)) <= TOL[dtype]
+    g = lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
+
+
+@pytest.mark.parametrize("b,L", [(4, 3), (16, 2), (64, 1)])
+def test_dense_equivalence_on_gpu(lsa, b, L):
+    """beam covering every cluster and k = n: LSA equals dense causal attention."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", n=1500, h_q=8, h_kv=2, d=64, dtype="f32", r=16, b=b, L=L, centres=50, m=12, mode="chunk")
+    data = _inputs(w, dev)
+    index, desc = lsa.build_index(data["K"], data["W"], b, L, 5)
+    sel, cnt, _ = lsa.select(data["Q"], data["pos"], index, desc, data["W"], b ** (L - 1), w.n)
+    out, _ = lsa.attend(data["Q"], data["K"], data["V"], sel, cnt)
+    torch.cuda.synchronize()
+    c = data["cpu"]
+    q = c["Q"].double()[:, :, None, :]
+    G = w.h_q // w.h_kv
+    k = c["K"].double().repeat_interleave(G, 0)[None]
+    v = c["V"].double().repeat_interleave(G, 0)[None]
+    keys = torch.arange(w.n)
+    mask = (keys[None, :] <= c["pos"][:, None].long())[:, None, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)[:, :, 0, :]
+    assert torch.max(torch.abs(out.cpu().double() - ref)).item() <= 1e-4
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL = [("decode_1m", None, 1), ("prefill_1m", 48, 1), ("train_128k", 64, 2), ("decode_10m", None, 0)]
+
+
+@pytest.mark.parametrize("name,sample_rows,replay_depth", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workload(lsa, name, sample_rows, replay_depth):
+    """The workload at its real size, in the launch configuration the benchmark
+    uses: bit-exact tree on sampled nodes (the oracle re-clusters the node from
+    the members the GPU gave its parent), bit-exact selection and attention on
+    sampled rows."""
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[name]
+    say("generate", name)
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    pos = w.positions().to(dev)
+    Q = synth.make_queries(w, K, pos)
+    say("build", name)
+    index, desc = lsa.build_index(K, W, w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    views = lsa.index_views(index, desc)
+    gix = host_index(views, desc)
+    rng = np.random.default_rng(7)
+    # sampled nodes: the root of head 0 when affordable, then random parents per level
+    picks = []
+    if w.n <= (1 << 20) and replay_depth >= 1:
+        picks.append((0, 1, 0))
+    for l in range(2, w.L + 1):
+        g = int(rng.integers(w.h_kv))
+        nz = np.nonzero(gix.cnt(l - 1)[g])[0]
+        for u in rng.choice(nz, size=min(3, len(nz)), replace=False):
+            picks.append((g, l, int(u)))
+    for g, l, u in picks:
+        say("replay", name, g, l, u)
+        replay_node(K, W, gix, g, l, u, w.iters)
+
+    say("select", name)
+    sel, cnt, cut = lsa.select(Q, pos, index, desc, W, w.beam, w.k)
+    say("attend", name)
+    out, lse = lsa.attend(Q, K, V, sel, cnt)
+    torch.cuda.synchronize()
+    # causal and count invariants on every row, on the device
+    s = sel.long()
+    valid = s >= 0
+    assert bool(torch.all(~valid | (s <= pos[:, None, None].long())))
+    assert bool(torch.all(valid.sum(-1) == cnt.long()))
+    assert bool(torch.all((s[..., 1:] > s[..., :-1]) | ~valid[..., 1:]))
+
+    rows = np.arange(w.m) if sample_rows is None else np.sort(rng.choice(w.m, size=sample_rows, replace=False))
+    ridx = torch.from_numpy(rows).to(dev)
+    Qs = np32(Q[ridx])
+    say("oracle select", name, len(rows))
+    ref = oracle.select(Qs, pos[ridx].cpu().numpy(), gix, np32(W), w.beam, w.k)
+    assert_same_bits(cnt[ridx].cpu().numpy(), ref["count"], "sel_count")
+    assert_same_bits(sel[ridx].cpu().numpy(), ref["sel"], "sel")
+    assert_same_bits(cut[ridx].cpu().numpy(), ref["cutoff"], "cutoff")
+    say("oracle attend", name, len(rows))
+    Kc, Vc, sel2 = compact_kv(K, V, ref["sel"], ref["count"])
+    o_ref, lse_ref = oracle.attend(Qs, Kc, Vc, sel2, ref["count"])
+    assert np.max(np.abs(np32(out[ridx]) - o_ref)) <= TOL[w.torch_dtype]
+    fin = np.isfinite(lse_ref)
+    g = lse[ridx].cpu().numpy()
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
+    say("mean sel_count", name, float(cnt.float().mean()))
+    del K, V, index, views
+    torch.cuda.empty_cache()
