@@ -14,8 +14,8 @@
 // into the latent space, each level's candidates are scored with double
 // accumulation, the best `beam` are kept by a bitonic sort of 64-bit
 // (score, id) keys in LDS, and at the leaf level the candidate leaves are
-// ordered, their eligible members counted, prefix-summed and gathered, and the
-// gathered key ids sorted ascending.
+// ordered, their eligible members counted and prefix-summed, and each leaf's
+// taken members written at its prefix offset (retrieval order).
 #include "common.h"
 #include "internal.h"
 
@@ -68,13 +68,12 @@ LSA_DEV int count_le(const int32_t *a, int len, int32_t key) {
     return lo;
 }
 
-template <typename T, int CMAX, int KMAX>
+template <typename T, int CMAX>
 __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
     __shared__ float qbar_s[256];
     __shared__ float u_s[64];
     __shared__ uint64_t keys[CMAX];
     __shared__ int32_t aux[CMAX + 1];
-    __shared__ int32_t selbuf[KMAX];
     __shared__ int scratch[8];
     __shared__ int nc_s;
     __shared__ float cut_s;
@@ -166,6 +165,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
     }
     const int avail = nc_s;
     const int count = min(A.k, avail);
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
     for (int e = threadIdx.x; e < nc; e += blockDim.x) {
         const int p0 = aux[e];
         if (p0 >= count) continue;
@@ -173,15 +173,11 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
         const int take = min(p1 - p0, count - p0);
         const uint32_t v = key_id(keys[e]);
         const int32_t a = lo[v];
-        for (int t = 0; t < take; ++t) selbuf[p0 + t] = pm[a + t];
+        for (int t = 0; t < take; ++t) out[p0 + t] = pm[a + t];
         if (count == A.k && p1 >= A.k) cut_s = key_score(keys[e]);
     }
-    const int N2 = next_pow2(count);
-    for (int e = count + threadIdx.x; e < N2; e += blockDim.x) selbuf[e] = INT32_MAX;
+    for (int t = count + threadIdx.x; t < A.k; t += blockDim.x) out[t] = -1;
     __syncthreads();
-    block_bitonic_sort<int32_t, false>(selbuf, N2);
-    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
-    for (int t = threadIdx.x; t < A.k; t += blockDim.x) out[t] = (t < count) ? selbuf[t] : -1;
     if (threadIdx.x == 0) {
         A.sel_count[(size_t)i * A.h_kv + g] = count;
         if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
@@ -200,13 +196,13 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     const dim3 grid((unsigned)m, (unsigned)h_kv);
     const int cmax = beam * b > b ? beam * b : b;
-    const bool small = cmax <= 1024 && k <= 4096;
+    const bool small = cmax <= 1024;
     if (dtype == 0) {
-        if (small) hipLaunchKernelGGL((k_select<float, 1024, 4096>), grid, dim3(256), 0, st, A);
-        else hipLaunchKernelGGL((k_select<float, 4096, 8192>), grid, dim3(256), 0, st, A);
+        if (small) hipLaunchKernelGGL((k_select<float, 1024>), grid, dim3(256), 0, st, A);
+        else hipLaunchKernelGGL((k_select<float, 4096>), grid, dim3(256), 0, st, A);
     } else {
-        if (small) hipLaunchKernelGGL((k_select<bf16_t, 1024, 4096>), grid, dim3(256), 0, st, A);
-        else hipLaunchKernelGGL((k_select<bf16_t, 4096, 8192>), grid, dim3(256), 0, st, A);
+        if (small) hipLaunchKernelGGL((k_select<bf16_t, 1024>), grid, dim3(256), 0, st, A);
+        else hipLaunchKernelGGL((k_select<bf16_t, 4096>), grid, dim3(256), 0, st, A);
     }
     return hipGetLastError();
 }

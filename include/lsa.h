@@ -146,7 +146,8 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, i
  *   W        device, float [h_kv][d][r]: the same projection as the keys
  *   beam     nodes kept per level at levels 1..L-1 (>= 1)
  *   k        keys retrieved per row and KV head (>= 1)
- *   sel      device out, int32 [m][h_kv][k]: selected keys in ascending order,
+ *   sel      device out, int32 [m][h_kv][k]: selected keys in the order they
+ *            are retrieved (leaf by leaf, ascending position inside a leaf),
  *            padded with -1
  *   sel_count device out, int32 [m][h_kv]: number of selected keys (<= k)
  *   sel_cutoff device out or NULL, float [m][h_kv]: score of the leaf that

@@ -203,8 +203,9 @@ int oracle_build(const float *K, int64_t n, int h_kv, int d, const float *W, int
  *   - leaves are visited in (score desc, id asc) order, each emitting its
  *     members in ascending position; keys at positions > pos are skipped
  *     (a key at the query's own position is visible); the first k are taken;
- *   - sel holds the taken keys in ascending order, padded with -1; cutoff is
- *     the score of the leaf holding the k-th taken key, -inf when fewer than k
+ *   - sel lists the taken keys in the order they were retrieved (leaf order,
+ *     then ascending position inside a leaf), padded with -1; cutoff is the
+ *     score of the leaf holding the k-th taken key, -inf when fewer than k
  *     keys were available.
  * Optional outputs (may be NULL): kept [m][h_kv][L-1][beam] (ids, -1 padded, in
  * rank order), nscored [m][h_kv] (number of centroids scored). */
@@ -216,12 +217,6 @@ static int cand_cmp(const void *pa, const void *pb)
     if (a->s > b->s) return -1;
     if (a->s < b->s) return 1;
     return (a->id < b->id) ? -1 : (a->id > b->id);
-}
-
-static int i32_cmp(const void *pa, const void *pb)
-{
-    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
-    return (a > b) - (a < b);
 }
 
 static float score_row(const float *u, const float *c, int r)
@@ -303,7 +298,6 @@ int oracle_select(const float *Q, int64_t m, int h_q, int d, const int32_t *pos,
                     if (taken == k) cut = F[t].s;
                 }
             }
-            qsort(out, (size_t)taken, sizeof(int32_t), i32_cmp);
             for (int64_t t = taken; t < k; ++t) out[t] = -1;
             sel_count[i * h_kv + g] = (int32_t)taken;
             if (cutoff) cutoff[i * h_kv + g] = cut;

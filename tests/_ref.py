@@ -28,7 +28,7 @@ def brute_select(Q, pos, Cs, cnts, leaf_off, perm, W, G, beam, k):
     """Score every node of every level (no pruning), then apply the per-level
     top-beam rule and the causal fill.  Q: [h_q, d] of one row; Cs/cnts: lists
     indexed by level-1 of [h_kv, b^l, r] / [h_kv, b^l]; returns per KV head
-    (sel sorted, count, cutoff, n_scored)."""
+    (sel in retrieval order, count, cutoff, n_scored)."""
     h_kv = Cs[0].shape[0]
     b = Cs[0].shape[1]
     L = len(Cs)
@@ -55,7 +55,7 @@ def brute_select(Q, pos, Cs, cnts, leaf_off, perm, W, G, beam, k):
                     taken.append(int(j))
                     if len(taken) == k:
                         cut = float(scores[L - 1][v])
-        out.append((sorted(taken), len(taken), cut, nsc))
+        out.append((taken, len(taken), cut, nsc))
     return out
 
 
