@@ -4,8 +4,8 @@
 Default workload: single-request decode at 1M tokens (32 query heads / 4 KV
 heads, d = 128, bf16 K/V from a 65536-centre Gaussian mixture; latent dim 64,
 3-level tree of branching 64, beam 16, k = 2048).  One step is one decode
-layer: lsa_select (group latent, top-down descent, causal fill) followed by
-lsa_attend (sparse attention), with the cluster tree already built and
+layer: lsa_select_attend (group latent, top-down descent, causal fill, then
+sparse attention, in one launch), with the cluster tree already built and
 resident in HBM, as the pages describe the index (precomputed, then
 maintained).  The index build (projection, k-means levels) is timed in the
 same run and reported under "breakdown".
@@ -138,77 +138,83 @@ def main():
     cut = torch.empty((m, w.h_kv), dtype=torch.float32, device=dev)
     out = torch.empty_like(Q)
     lse = torch.empty((m, w.h_q), dtype=torch.float32, device=dev)
-    nws = lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k)
-    aws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    fws = lsa.workspace(lsa.select_attend_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
 
-    def do_select():
-        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, cutoff=cut)
+    def do_step():
+        lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, cutoff=cut,
+                          out=out, lse=lse, ws=fws)
 
-    def do_attend():
-        lsa.attend(Q, K, V, sel, cnt, out=out, lse=lse, ws=aws)
-
-    do_select(); do_attend()
+    do_step()
     torch.cuda.synchronize()
-
     use_graph = not args.no_graph
+    run_step = do_step
     if use_graph:
         try:
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):
-                do_select(); do_attend()
+                do_step()
             torch.cuda.current_stream().wait_stream(s)
-            g_sel, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_sel):
-                do_select()
-            with torch.cuda.graph(g_att):
-                do_attend()
-            run_sel, run_att = g_sel.replay, g_att.replay
-            # the graphs must reproduce the eager result
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                do_step()
+            # replays must reproduce the eager result
             ref = (sel.clone(), cnt.clone(), out.clone())
-            sel.zero_(); out.zero_()
-            run_sel(); run_att()
-            torch.cuda.synchronize()
-            assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1]) and torch.equal(out, ref[2])
+            for _ in range(3):
+                sel.zero_(); out.zero_()
+                graph.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1]) and torch.equal(out, ref[2])
+            run_step = graph.replay
         except Exception as e:      # graph capture unavailable: time eager launches
             log("graph capture failed, timing eager launches:", repr(e))
             use_graph = False
-    if not use_graph:
-        run_sel, run_att = do_select, do_attend
 
     log("warmup", args.warmup)
     for _ in range(args.warmup):
-        run_sel(); run_att()
+        run_step()
     torch.cuda.synchronize()
     K_ = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_)]
     log("timed", K_)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(K_):
         ev[s_][0].record()
-        run_sel()
+        run_step()
         ev[s_][1].record()
-        run_att()
-        ev[s_][2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K_
-    sel_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-    att_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    step_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
     counts = cnt.cpu().numpy()
     cand_leaves = w.beam * w.b
     sb = select_bytes(w, m, counts, cand_leaves)
     ab = attend_bytes(w, m, counts)
-    kernels = {"lsa_select": (sel_us, sb), "lsa_attend": (att_us, ab)}
-    dom = max(kernels, key=lambda k: kernels[k][0])
-    dus, dbytes = kernels[dom]
-    achieved = dbytes / (dus * 1e-6) / 1e9
+    dbytes = sb + ab
+    achieved = dbytes / (step_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": dom,
-                "kernel_us": round(dus, 3), "algorithmic_bytes": int(dbytes)}
+                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "k_decode (lsa_select_attend)",
+                "kernel_us": round(step_us, 3), "algorithmic_bytes": int(dbytes)}
 
-    breakdown = {"select_us": round(sel_us, 3), "attend_us": round(att_us, 3),
+    # the two calls separately (select on the multi-workgroup kernel, then attend)
+    sws = lsa.workspace(lsa.select_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
+    aws = lsa.workspace(lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k), dev)
+    nsep = 50
+    e3 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e3[0].record()
+    for _ in range(nsep):
+        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, cutoff=cut, ws=sws)
+    e3[1].record()
+    for _ in range(nsep):
+        lsa.attend(Q, K, V, sel, cnt, out=out, lse=lse, ws=aws)
+    e3[2].record()
+    torch.cuda.synchronize()
+    sel_us = e3[0].elapsed_time(e3[1]) / nsep * 1e3
+    att_us = e3[1].elapsed_time(e3[2]) / nsep * 1e3
+
+    breakdown = {"fused_step_us": round(step_us, 3),
+                 "select_only_us": round(sel_us, 3), "attend_only_us": round(att_us, 3),
                  "select_GBps": round(sb / (sel_us * 1e-6) / 1e9, 2),
                  "attend_GBps": round(ab / (att_us * 1e-6) / 1e9, 2),
                  "build_ms": round(build_ms, 3), "graph": use_graph,
@@ -227,7 +233,7 @@ def main():
         pws_n = lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, w.k)
         pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
         def pstep():
-            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False)
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=None)
             lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
         for _ in range(2):
             pstep()
@@ -236,7 +242,7 @@ def main():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
         for _ in range(npre):
-            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False)
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=None)
         e[1].record()
         for _ in range(npre):
             lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
@@ -266,7 +272,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "r": w.r, "b": w.b,
                    "L": w.L, "beam": w.beam, "k": w.k, "query_rows": m,
-                   "step": "lsa_select + lsa_attend, index resident",
+                   "step": "lsa_select_attend (select + attend, one launch), index resident",
                    "indexer_arith": "f64 accumulate", "attention_arith": "f32 accumulate"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -27,7 +27,7 @@ MAX_LEVELS = 6
 
 EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
-           "lsa_attend"]
+           "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend"]
 
 
 class IndexDesc(ctypes.Structure):
@@ -64,7 +64,10 @@ def lib():
         L.lsa_index_layout.argtypes = [i64, i32, i32, i32, i32, D]
         L.lsa_build_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_build_index.argtypes = [P, i32, i64, i32, i32, P, i32, i32, i32, i32, P, i64, P, i64, D, P]
-        L.lsa_select_workspace_bytes.argtypes = [i64, i32, D, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select_attend_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select_attend.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, ctypes.c_float,
+                                        P, P, P, P, P, P, i64, P]
         L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, P, P, P, P, i64, P]
         L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_attend.argtypes = [P, P, P, i32, i64, i32, i32, i64, i32, P, P, i32, ctypes.c_float,
@@ -118,11 +121,24 @@ def build_workspace_bytes(n: int, h_kv: int, d: int, r: int, b: int, L: int) -> 
     return v.value
 
 
-def select_workspace_bytes(m: int, h_q: int, desc: IndexDesc, beam: int, k: int) -> int:
+def select_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int) -> int:
     v = ctypes.c_int64()
-    _check(lib().lsa_select_workspace_bytes(m, h_q, ctypes.byref(desc), beam, k, ctypes.byref(v)),
+    _check(lib().lsa_select_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, ctypes.byref(v)),
            "lsa_select_workspace_bytes")
     return v.value
+
+
+def select_attend_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_select_attend_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, ctypes.byref(v)),
+           "lsa_select_attend_workspace_bytes")
+    return v.value
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace (the multi-workgroup kernels need zeroed counters
+    on first use and leave them zeroed)."""
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes > 0 else None
 
 
 def attend_workspace_bytes(m: int, h_q: int, h_kv: int, d: int, k: int) -> int:
@@ -171,10 +187,17 @@ def build_index(K: torch.Tensor, W: torch.Tensor, b: int, L: int, iters: int = 5
     return index, out
 
 
+_NO_WS = object()
+
+
 def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: IndexDesc, W: torch.Tensor,
            beam: int, k: int, sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
-           cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, stream=None):
-    """Q [m, h_q, d], q_pos int32 [m] -> (sel int32 [m, h_kv, k], count int32 [m, h_kv], cutoff f32 [m, h_kv])."""
+           cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, ws=_NO_WS, stream=None):
+    """Q [m, h_q, d], q_pos int32 [m] -> (sel int32 [m, h_kv, k], count int32 [m, h_kv], cutoff f32 [m, h_kv]).
+
+    ws: None runs one workgroup per (row, KV head); a zero-filled workspace of
+    select_workspace_bytes lets small batches use the multi-workgroup kernel
+    (allocated per call when omitted)."""
     _need(Q, "Q"); _need(q_pos, "q_pos"); _need(W, "W")
     m, h_q, d = Q.shape
     h = desc.h_kv
@@ -185,10 +208,45 @@ def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: Inde
         sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
     if cutoff is None and want_cutoff:
         cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    if ws is _NO_WS:
+        ws = workspace(select_workspace_bytes(m, h_q, d, desc, beam, k), dev)
     _check(lib().lsa_select(_ptr(Q), _dtype_code(Q), m, h_q, d, _ptr(q_pos), ctypes.byref(desc), _ptr(index),
-                            _ptr(W), beam, k, _ptr(sel), _ptr(sel_count), _ptr(cutoff), None, 0, _stream(stream)),
+                            _ptr(W), beam, k, _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_select")
     return sel, sel_count, cutoff
+
+
+def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor,
+                  desc: IndexDesc, W: torch.Tensor, beam: int, k: int, scale: float = 0.0,
+                  sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
+                  cutoff: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_cutoff: bool = True, want_lse: bool = True,
+                  ws: Optional[torch.Tensor] = None, stream=None):
+    """lsa_select + lsa_attend (one launch for small batches) -> (sel, count, cutoff, out, lse)."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (q_pos, "q_pos"), (W, "W")):
+        _need(t, nm)
+    m, h_q, d = Q.shape
+    h = desc.h_kv
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((m, h, k), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
+    if cutoff is None and want_cutoff:
+        cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((m, h_q), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(select_attend_workspace_bytes(m, h_q, d, desc, beam, k), dev)
+    _check(lib().lsa_select_attend(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), m, h_q, d, _ptr(q_pos),
+                                   ctypes.byref(desc), _ptr(index), _ptr(W), beam, k, float(scale), _ptr(sel),
+                                   _ptr(sel_count), _ptr(cutoff), _ptr(out), _ptr(lse), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)),
+           "lsa_select_attend")
+    return sel, sel_count, cutoff, out, lse
 
 
 def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel: torch.Tensor, sel_count: torch.Tensor,

@@ -127,9 +127,11 @@ int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const 
                     int64_t ws_bytes, lsa_index_desc *desc, void *stream);
 
 /*
- * Bytes of device workspace lsa_select needs (*bytes; currently 0).
+ * Bytes of device workspace that let lsa_select run its multi-workgroup
+ * kernel for this batch (*bytes; 0 when the batch is too large for it, in
+ * which case every (row, KV head) pair runs in one workgroup).
  */
-int lsa_select_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, int beam, int k,
+int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
                                int64_t *bytes);
 
 /*
@@ -163,6 +165,15 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, i
  * positions > q_pos are skipped; the first k are taken.  Dot products are
  * accumulated in double in ascending index order.
  * Limits: h_q % h_kv == 0, 1 <= d <= 256, beam * b <= 4096, k <= 8192.
+ *
+ * Workspace: ws may be NULL.  When ws holds at least
+ * lsa_select_workspace_bytes bytes (> 0), small batches (m * h_kv * beam up
+ * to the number of compute units, L >= 2, beam <= 32) run on beam
+ * workgroups per (row, KV head) that synchronise through counters in ws.  The
+ * caller zero-fills ws once before its first use; every call leaves the
+ * counters at zero again, so the same ws serves any number of calls.  Calls
+ * that share one ws must not run concurrently.  Both kernels give identical
+ * results.
  */
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
                const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,
@@ -194,6 +205,30 @@ int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64
 int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q,
                int h_kv, int64_t n, int d, const int32_t *sel, const int32_t *sel_count, int k,
                float scale, void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
+
+/*
+ * Bytes of device workspace lsa_select_attend needs (*bytes).
+ */
+int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam,
+                                      int k, int64_t *bytes);
+
+/*
+ * lsa_select followed by lsa_attend on the same rows, in one launch when the
+ * batch is small (the decode case: the beam workgroups of each (row, KV head)
+ * pair also attend over the keys they retrieved and the last one merges the
+ * partial softmax states), else as the two calls in sequence.  Arguments as
+ * in lsa_select and lsa_attend; K and V are the cache the index was built
+ * from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes bytes) must be
+ * zero-filled before its first use and is left reusable; calls sharing one ws
+ * must not run concurrently.  Outputs equal those of the two separate calls
+ * (sel, sel_count and sel_cutoff bit for bit; out and lse within fp32
+ * rounding of the accumulation order).
+ * Limits: those of lsa_select and of lsa_attend.
+ */
+int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
+                      const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W,
+                      int beam, int k, float scale, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
+                      void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

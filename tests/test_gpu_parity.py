@@ -81,14 +81,23 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
     c = data["cpu"]
     Qh = np32(c["Q"])
     pos = c["pos"].numpy()
+    tol = TOL[w.torch_dtype]
     for beam, k in [(w.beam, w.k), (1, 1), (w.b ** max(w.L - 1, 0), min(w.n + 3, 8192))]:
-        say("select", name, beam, k)
-        sel, cnt, cut = lsa.select(data["Q"], data["pos"], index, desc, data["W"], beam, k)
-        torch.cuda.synchronize()
         ref = oracle.select(Qh, pos, oix, c["W"].numpy(), beam, k)
-        assert_same_bits(cnt.cpu().numpy(), ref["count"], "sel_count")
-        assert_same_bits(sel.cpu().numpy(), ref["sel"], "sel")
-        assert_same_bits(cut.cpu().numpy(), ref["cutoff"], "cutoff")
+        o_ref, lse_ref = oracle.attend(Qh, np32(c["K"]), np32(c["V"]), ref["sel"], ref["count"])
+        # one workgroup per (row, KV head), then the multi-workgroup kernel (when it applies)
+        nws = lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k)
+        for label, ws in (("single-wg", None), ("multi-wg", lsa.workspace(nws, dev))):
+            if label == "multi-wg" and ws is None:
+                continue
+            say("select", name, label, beam, k)
+            sel, cnt, cut = lsa.select(data["Q"], data["pos"], index, desc, data["W"], beam, k, ws=ws)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt.cpu().numpy(), ref["count"], f"sel_count ({label})")
+            assert_same_bits(sel.cpu().numpy(), ref["sel"], f"sel ({label})")
+            assert_same_bits(cut.cpu().numpy(), ref["cutoff"], f"cutoff ({label})")
+            if ws is not None:
+                assert int(ws[:w.m * w.h_kv * 16].count_nonzero()) == 0, "group counters not reset"
         # every selected key precedes (or is) its query
         s = sel.cpu().numpy()
         assert np.all((s == -1) | (s <= pos[:, None, None]))
@@ -96,14 +105,29 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
         say("attend", name, beam, k)
         out, lse = lsa.attend(data["Q"], data["K"], data["V"], sel, cnt)
         torch.cuda.synchronize()
-        o_ref, lse_ref = oracle.attend(Qh, np32(c["K"]), np32(c["V"]), ref["sel"], ref["count"])
-        tol = TOL[w.torch_dtype]
-        assert np.max(np.abs(np32(out) - o_ref)) <= tol
-        g = lse.cpu().numpy()
-        fin = np.isfinite(lse_ref)
-        assert np.array_equal(np.isfinite(g), fin)
-        if fin.any():
-            assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
+        _check_attention(out, lse, o_ref, lse_ref, tol)
+
+        say("select_attend", name, beam, k)
+        fws = lsa.workspace(lsa.select_attend_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k), dev)
+        for rep in range(2):     # the workspace is reusable
+            sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(data["Q"], data["K"], data["V"], data["pos"], index,
+                                                             desc, data["W"], beam, k, ws=fws)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt2.cpu().numpy(), ref["count"], "sel_count (fused)")
+            assert_same_bits(sel2.cpu().numpy(), ref["sel"], "sel (fused)")
+            assert_same_bits(cut2.cpu().numpy(), ref["cutoff"], "cutoff (fused)")
+            _check_attention(out2, lse2, o_ref, lse_ref, tol)
+        if lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k) > 0:
+            assert int(fws[:w.m * w.h_kv * 16].count_nonzero()) == 0, "group counters not reset"
+
+
+def _check_attention(out, lse, o_ref, lse_ref, tol):
+    assert np.max(np.abs(np32(out) - o_ref)) <= tol
+    g = lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    if fin.any():
+        assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
 
 
 def test_positions_before_every_candidate_give_empty_rows(lsa):
@@ -223,6 +247,12 @@ def test_full_size_workload(lsa, name, sample_rows, replay_depth):
     say("attend", name)
     out, lse = lsa.attend(Q, K, V, sel, cnt)
     torch.cuda.synchronize()
+    if w.m * w.h_kv <= 256:
+        say("select_attend", name)
+        sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k)
+        torch.cuda.synchronize()
+        assert torch.equal(sel2, sel) and torch.equal(cnt2, cnt) and torch.equal(cut2, cut)
+        assert float((out2.float() - out.float()).abs().max()) <= TOL[w.torch_dtype]
     # causal and count invariants on every row, on the device
     s = sel.long()
     valid = s >= 0
