@@ -71,12 +71,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
         __syncthreads();
         if (threadIdx.x < nk) ids[threadIdx.x] = S[kb + threadIdx.x];
         __syncthreads();
-        for (int e = threadIdx.x; e < nk * d; e += blockDim.x) {
-            const int kk = e / d, t = e % d;
-            const size_t off = (size_t)ids[kk] * d + t;
-            Ks[kk * dp + t] = to_float(Kg[off]);
-            Vs[kk * d + t] = to_float(Vg[off]);
-        }
+        gather_tile<T>(Kg, Vg, ids, nk, d, Ks, dp, Vs);
         __syncthreads();
         for (int e = threadIdx.x; e < G * nk; e += blockDim.x) {
             const int h = e / nk, kk = e % nk;

@@ -105,6 +105,102 @@ LSA_DEV void block_bitonic_sort(K *keys, int N) {
     }
 }
 
+// Copy n floats (n % 4 == 0, src 16-byte aligned) from global memory into LDS
+// rows of `cols` floats (cols % 4 == 0) with row stride `ld`.  Every thread
+// issues up to U 16-byte loads before it stores any of them, so one copy costs
+// about one memory round trip per U * blockDim float4s.
+template <int U>
+LSA_DEV void g2s_rows(float *dst, int ld, const float *__restrict__ src, int n, int cols) {
+    const float4 *s4 = reinterpret_cast<const float4 *>(src);
+    const int n4 = n >> 2;
+    for (int base = 0; base < n4; base += U * (int)blockDim.x) {
+        float4 t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n4) t[u] = s4[e];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n4) {
+                const int f = e * 4, row = f / cols, col = f % cols;
+                float *q = dst + row * ld + col;
+                q[0] = t[u].x; q[1] = t[u].y; q[2] = t[u].z; q[3] = t[u].w;
+            }
+        }
+    }
+}
+
+// Same for arbitrary n and cols (scalar loads, U in flight per thread).
+template <int U, typename S, typename D>
+LSA_DEV void g2s_scalar(D *dst, int ld, const S *__restrict__ src, int n, int cols) {
+    for (int base = 0; base < n; base += U * (int)blockDim.x) {
+        S t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n) t[u] = src[e];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n) dst[(e / cols) * ld + (e % cols)] = (D)t[u];
+        }
+    }
+}
+
+// Gather nk rows of K and V (row ids in LDS) into float LDS tiles, 8 elements
+// per load, every load of a thread issued before the first use.
+template <typename T>
+LSA_DEV void gather_tile(const T *__restrict__ Kg, const T *__restrict__ Vg, const int32_t *ids, int nk, int d,
+                         float *Kt, int dp, float *Vt) {
+    constexpr int U = 4;
+    const int cpr = d / 8;
+    const int nch = nk * cpr;
+    for (int base = 0; base < nch; base += U * (int)blockDim.x) {
+        uint4 kr[U][sizeof(T) == 2 ? 1 : 2], vr[U][sizeof(T) == 2 ? 1 : 2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < nch) {
+                const size_t off = (size_t)ids[e / cpr] * d + (e % cpr) * 8;
+                const uint4 *kp = reinterpret_cast<const uint4 *>(Kg + off);
+                const uint4 *vp = reinterpret_cast<const uint4 *>(Vg + off);
+#pragma unroll
+                for (int h = 0; h < (sizeof(T) == 2 ? 1 : 2); ++h) { kr[u][h] = kp[h]; vr[u][h] = vp[h]; }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < nch) {
+                const int kk = e / cpr, c8 = (e % cpr) * 8;
+                float kv[8], vv[8];
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t kw[4] = {kr[u][0].x, kr[u][0].y, kr[u][0].z, kr[u][0].w};
+                    const uint32_t vw[4] = {vr[u][0].x, vr[u][0].y, vr[u][0].z, vr[u][0].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        kv[2 * q] = __uint_as_float(kw[q] << 16); kv[2 * q + 1] = __uint_as_float(kw[q] & 0xffff0000u);
+                        vv[2 * q] = __uint_as_float(vw[q] << 16); vv[2 * q + 1] = __uint_as_float(vw[q] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        kv[4 * h + 0] = __uint_as_float(kr[u][h].x); kv[4 * h + 1] = __uint_as_float(kr[u][h].y);
+                        kv[4 * h + 2] = __uint_as_float(kr[u][h].z); kv[4 * h + 3] = __uint_as_float(kr[u][h].w);
+                        vv[4 * h + 0] = __uint_as_float(vr[u][h].x); vv[4 * h + 1] = __uint_as_float(vr[u][h].y);
+                        vv[4 * h + 2] = __uint_as_float(vr[u][h].z); vv[4 * h + 3] = __uint_as_float(vr[u][h].w);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) { Kt[kk * dp + c8 + q] = kv[q]; Vt[kk * d + c8 + q] = vv[q]; }
+            }
+        }
+    }
+}
+
 LSA_DEV int next_pow2(int x) {
     int p = 1;
     while (p < x) p <<= 1;

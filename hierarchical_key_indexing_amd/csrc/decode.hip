@@ -121,6 +121,30 @@ LSA_DEV float score_lds(const float *u, const float *row, int r) {
     return (float)s;
 }
 
+// Contiguous global -> LDS copy with U loads in flight per thread.
+template <int U, typename E>
+LSA_DEV void g2s_flat(E *dst, const E *__restrict__ src, int n) {
+    for (int base = 0; base < n; base += U * (int)blockDim.x) {
+        E t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n) t[u] = src[e];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
+            if (e < n) dst[e] = t[u];
+        }
+    }
+}
+
+// b rows of r floats (a node's children) into LDS rows of stride 65.
+LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
+    if ((r & 3) == 0) g2s_rows<4>(Cs, 65, src, b * r, r);
+    else g2s_scalar<16, float, float>(Cs, 65, src, b * r, r);
+}
+
 // All workgroups of a group wait here until `target` arrivals are counted.
 LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
     __syncthreads();
@@ -178,11 +202,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     // ---- level-1 rows (independent of the query), W, the group's queries
     {
         const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
-        for (int e = tid; e < b * r; e += blockDim.x) Cs[(e / r) * 65 + e % r] = C1[e];
         const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
         if (tid < b) ccnt[tid] = cn1[tid];
+        load_rows(Cs, C1, b, r);
         const float *Wg = A.W + (size_t)g * d * r;
-        for (int e = tid; e < d * r; e += blockDim.x) dyn[e] = Wg[e];
+        if (((d * r) & 3) == 0) g2s_rows<8>(dyn, d * r, Wg, d * r, d * r);
+        else g2s_flat<16>(dyn, Wg, d * r);
         for (int t = tid; t < d; t += blockDim.x) {
             float qv[16];
 #pragma unroll
@@ -224,17 +249,16 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         const bool leaf = (l == L);
         if (v >= 0) {
             const float *Cl = (const float *)(A.index + A.centroid_off[l]) + ((size_t)g * A.nodes[l] + (size_t)v * b) * r;
-            for (int e = tid; e < b * r; e += blockDim.x) Cs[(e / r) * 65 + e % r] = Cl[e];
             const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l] + (size_t)v * b;
             if (tid < b) ccnt[tid] = cn[tid];
             if (leaf && tid <= b) clo[tid] = leaf_off[(size_t)v * b + tid];
+            load_rows(Cs, Cl, b, r);
         }
         __syncthreads();
         if (leaf && v >= 0) {
             // stage the node's members (leaves of one node are contiguous)
             const int m0 = clo[0], mn = clo[b] - clo[0];
-            if (mn <= kMemCap)
-                for (int e = tid; e < mn; e += blockDim.x) mem_s[e] = perm[m0 + e];
+            if (mn <= kMemCap) g2s_flat<8>(mem_s, perm + m0, mn);
             __syncthreads();
         }
         if (wv == 0) {
@@ -265,7 +289,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         group_barrier(ctrl, barriers * P, ctrl + 2);
         if (!leaf) {
             const uint64_t *src = A.lists + ((size_t)(l - 2) * (A.m * A.h_kv) + gi) * P * P;
-            for (int e = tid; e < P * P; e += blockDim.x) lk[e] = src[e];
+            g2s_flat<4>(lk, src, P * P);
             if (tid == 0) nz_s = 0;
             __syncthreads();
             for (int e = tid; e < P * P; e += blockDim.x) {
@@ -288,7 +312,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     {
         const uint64_t *srck = A.leaf_keys + (size_t)gi * P * 64;
         const int32_t *srcp = A.leaf_pre + (size_t)gi * P * 64;
-        for (int e = tid; e < P * 64; e += blockDim.x) { lk[e] = srck[e]; lp[e] = srcp[e]; }
+        g2s_flat<8>(lk, srck, P * 64);
+        g2s_flat<8>(lp, srcp, P * 64);
         if (tid < 64) take_s[tid] = 0;
         __syncthreads();
         if (tid == 0) {
@@ -365,31 +390,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             __syncthreads();
             // gather rows, 8 elements per load
-            const int cpr = d / 8;
-            for (int e = tid; e < nk * cpr; e += blockDim.x) {
-                const int kk = e / cpr, c8 = (e % cpr) * 8;
-                const size_t off = (size_t)ids_s[kk] * d + c8;
-                float kv[8], vv[8];
-                if constexpr (sizeof(T) == 2) {
-                    const uint4 kr = *reinterpret_cast<const uint4 *>(Kg + off);
-                    const uint4 vr = *reinterpret_cast<const uint4 *>(Vg + off);
-                    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        kv[2 * q] = __uint_as_float(kw[q] << 16); kv[2 * q + 1] = __uint_as_float(kw[q] & 0xffff0000u);
-                        vv[2 * q] = __uint_as_float(vw[q] << 16); vv[2 * q + 1] = __uint_as_float(vw[q] & 0xffff0000u);
-                    }
-                } else {
-                    const float4 k0 = *reinterpret_cast<const float4 *>(Kg + off);
-                    const float4 k1 = *reinterpret_cast<const float4 *>(Kg + off + 4);
-                    const float4 v0 = *reinterpret_cast<const float4 *>(Vg + off);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(Vg + off + 4);
-                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w; kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
-                    vv[0] = v0.x; vv[1] = v0.y; vv[2] = v0.z; vv[3] = v0.w; vv[4] = v1.x; vv[5] = v1.y; vv[6] = v1.z; vv[7] = v1.w;
-                }
-#pragma unroll
-                for (int q = 0; q < 8; ++q) { Kt[kk * dp + c8 + q] = kv[q]; Vt[kk * d + c8 + q] = vv[q]; }
-            }
+            gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
             __syncthreads();
             for (int e = tid; e < G * kTKD; e += blockDim.x) {
                 const int h = e / kTKD, kk = e % kTKD;
@@ -456,22 +457,42 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     if constexpr (ATTEND) {
         const float *pb = A.part + (size_t)gi * P * (G * d + 2 * G);
         const int stride = G * d + 2 * G;
+        // per-(workgroup, head) weights 2^(m_q - M) and the total sums, in LDS
+        float *wq = dyn;                       // [P][G]
+        float *lq = dyn + kMaxP * 16;          // [P][G]
+        float *Ms = lq + kMaxP * 16;           // [G], then L [G]
+        for (int e = tid; e < P * G; e += blockDim.x) {
+            const int q = e / G, h = e % G;
+            wq[e] = pb[(size_t)q * stride + G * d + h];
+            lq[e] = pb[(size_t)q * stride + G * d + G + h];
+        }
+        __syncthreads();
+        if (tid < G) {
+            float M = -INFINITY;
+            for (int q = 0; q < P; ++q) M = fmaxf(M, wq[q * G + tid]);
+            float l = 0.0f;
+            for (int q = 0; q < P; ++q) {
+                const float mq = wq[q * G + tid];
+                const float w = (mq > -INFINITY) ? exp2f(mq - M) : 0.0f;
+                wq[q * G + tid] = w;
+                l += lq[q * G + tid] * w;
+            }
+            Ms[tid] = M;
+            Ms[16 + tid] = l;
+        }
+        __syncthreads();
         for (int e = tid; e < G * d; e += blockDim.x) {
             const int h = e / d;
-            float M = -INFINITY;
-            for (int q = 0; q < P; ++q) M = fmaxf(M, pb[(size_t)q * stride + G * d + h]);
-            float l = 0.0f, o = 0.0f;
-            for (int q = 0; q < P; ++q) {
-                const float mq = pb[(size_t)q * stride + G * d + h];
-                if (mq > -INFINITY) {
-                    const float w = exp2f(mq - M);
-                    l += pb[(size_t)q * stride + G * d + G + h] * w;
-                    o += pb[(size_t)q * stride + e] * w;
-                }
-            }
+            float t[kMaxP];
+#pragma unroll
+            for (int q = 0; q < kMaxP; ++q) t[q] = (q < P) ? pb[(size_t)q * stride + e] : 0.0f;
+            float o = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kMaxP; ++q) if (q < P) o += t[q] * wq[q * G + h];
+            const float l = Ms[16 + h];
             const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
             ((T *)A.out)[oh * d + (e % d)] = from_float<T>(l > 0.0f ? o / l : 0.0f);
-            if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+            if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (Ms[h] + log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
     }
     if (tid == 0) {

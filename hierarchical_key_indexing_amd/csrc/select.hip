@@ -41,16 +41,23 @@ struct SelectArgs {
 };
 
 // u . row in double, ascending index; fp32 x fp32 products are exact in double.
+// All loads of a row are issued before the first FMA.
 LSA_DEV float score_row(const float *u, const float *__restrict__ row, int r) {
     double s = 0.0;
     if ((r & 3) == 0) {
         const float4 *row4 = reinterpret_cast<const float4 *>(row);
-        for (int x = 0; x < r / 4; ++x) {
-            const float4 v = row4[x];
-            s = fma((double)u[4 * x + 0], (double)v.x, s);
-            s = fma((double)u[4 * x + 1], (double)v.y, s);
-            s = fma((double)u[4 * x + 2], (double)v.z, s);
-            s = fma((double)u[4 * x + 3], (double)v.w, s);
+        float4 v[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+            if (4 * x < r) v[x] = row4[x];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            if (4 * x < r) {
+                s = fma((double)u[4 * x + 0], (double)v[x].x, s);
+                s = fma((double)u[4 * x + 1], (double)v[x].y, s);
+                s = fma((double)u[4 * x + 2], (double)v[x].z, s);
+                s = fma((double)u[4 * x + 3], (double)v[x].w, s);
+            }
         }
     } else {
         for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
