@@ -13,6 +13,7 @@
 // (online softmax, base 2) and a merge kernel combines them by log-sum-exp.
 #include "common.h"
 #include "internal.h"
+#include "mfma_attn.h"
 
 namespace lsa {
 
@@ -124,6 +125,65 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- MFMA path (bf16)
+// Each of the four waves walks its own 32-key steps of the workgroup's slice
+// with the matrix-core step of mfma_attn.h and keeps its own softmax state;
+// the four states are combined at the end.
+template <int D>
+__global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
+    __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * kVTS];
+    __shared__ int32_t ids_w[4][kMT];
+    const int64_t row = blockIdx.y;
+    const int64_t i = row / A.h_kv;
+    const int g = (int)(row % A.h_kv);
+    const int G = A.h_q / A.h_kv;
+    const int split = blockIdx.x;
+    const int cnt = A.sel_count[row];
+    const int per = (cnt + A.nsplit - 1) / A.nsplit;
+    const int s0 = min(cnt, split * per), s1 = min(cnt, s0 + per);
+    const int w = threadIdx.x / kWave, l = lane_id();
+    const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * D;
+    const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * D;
+    const uint16_t *Qb = (const uint16_t *)A.Q + ((size_t)i * A.h_q + (size_t)g * G) * D;
+    const int32_t *S = A.sel + (size_t)row * A.k;
+
+    bf16x8_t qf[D / 32];
+    wave_load_q<D>(qf, Qb, G);
+    WaveAttn<D> st;
+    wave_attn_init<D>(st);
+    const int nsteps = (s1 - s0 + 4 * kMT - 1) / (4 * kMT);
+    for (int t = 0; t < nsteps; ++t) {
+        const int kb = s0 + (4 * t + w) * kMT;
+        const int nk = max(0, min(kMT, s1 - kb));
+        if (l < kMT) ids_w[w][l] = (l < nk) ? S[kb + l] : ((nk > 0) ? S[kb] : 0);
+        __syncthreads();
+        bf16x8_t pf;
+        float alpha;
+        wave_attn_part1<D>(Kg, Vg, ids_w[w], nk, qf, A.scale_log2, vt[w], st, pf, alpha);
+        __syncthreads();
+        wave_attn_part2<D>(vt[w], pf, alpha, st);
+    }
+    __syncthreads();
+    float *scratch = reinterpret_cast<float *>(&vt[0][0]);
+    wave_attn_stash<D>(st, scratch);
+    __syncthreads();
+    const float ln2 = 0.69314718055994531f;
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int h = e / D, dd = e % D;
+        float M, Ls;
+        const float o = wave_attn_combine<D>(scratch, h, dd, M, Ls);
+        const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
+        if (A.nsplit == 1) {
+            ((bf16_t *)A.out)[oh * D + dd] = from_float<bf16_t>(Ls > 0.0f ? o / Ls : 0.0f);
+            if (dd == 0 && A.lse) A.lse[oh] = (Ls > 0.0f) ? (M + log2f(Ls)) * ln2 : -INFINITY;
+        } else {
+            float *pp = A.part + (oh * A.nsplit + split) * (size_t)(D + 2);
+            pp[dd] = o;
+            if (dd == 0) { pp[D] = M; pp[D + 1] = Ls; }
+        }
+    }
+}
+
 // Combine split-K slices: M = max m_s, l = sum l_s 2^(m_s - M),
 // o = sum o_s 2^(m_s - M) / l.
 template <typename T>
@@ -187,7 +247,10 @@ hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_
         hipLaunchKernelGGL(k_attend<float>, grid, dim3(256), shm, st, A);
         if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<float>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
     } else {
-        hipLaunchKernelGGL(k_attend<bf16_t>, grid, dim3(256), shm, st, A);
+        if (d == 128) hipLaunchKernelGGL(k_attend_mfma<128>, grid, dim3(256), 0, st, A);
+        else if (d == 64) hipLaunchKernelGGL(k_attend_mfma<64>, grid, dim3(256), 0, st, A);
+        else if (d == 256) hipLaunchKernelGGL(k_attend_mfma<256>, grid, dim3(256), 0, st, A);
+        else hipLaunchKernelGGL(k_attend<bf16_t>, grid, dim3(256), shm, st, A);
         if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<bf16_t>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
     }
     return hipGetLastError();

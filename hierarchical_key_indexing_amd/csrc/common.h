@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #define LSA_DEV __device__ __forceinline__
 
 namespace lsa {
@@ -11,7 +13,10 @@ namespace lsa {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- element types
-struct bf16_t { uint16_t bits; };
+struct bf16_t {
+    uint16_t bits;
+    LSA_DEV explicit operator float() const { return __uint_as_float(((uint32_t)bits) << 16); }
+};
 
 LSA_DEV float to_float(float x) { return x; }
 LSA_DEV float to_float(bf16_t x) { return __uint_as_float(((uint32_t)x.bits) << 16); }

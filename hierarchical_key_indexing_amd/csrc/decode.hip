@@ -13,25 +13,27 @@
 // latent query and the level-1 ranking itself (identical results), then at
 // each deeper level workgroup p scores the children of the p-th kept node,
 // sorts them within one wave and publishes the sorted list.  After a group
-// barrier every workgroup derives the global ranks by binary search in the P
-// sorted lists (the global top-beam at internal levels; at the leaf level each
-// leaf's count of eligible keys retrieved before it), so no workgroup sorts
-// more than 64 keys.  Workgroup p then writes its own leaves' keys at their
-// retrieval offsets and attends over them; the last workgroup of the group to
-// finish merges the P partial softmax states and resets the group's counters.
+// barrier every workgroup derives global ranks by fixed-step binary searches
+// in the P sorted lists (the global top-beam at internal levels; at the leaf
+// level, how many eligible keys are retrieved before each of its leaves), so
+// no workgroup sorts more than 64 keys.  Workgroup p then writes its own
+// leaves' keys at their retrieval offsets and attends over them (matrix cores
+// for bf16); the last workgroup of the group to finish merges the P partial
+// softmax states and resets the group's counters.
 //
 // Group barriers spin on a device-scope counter in the caller's workspace;
 // the grid is at most one workgroup per compute unit, and every spin is
 // bounded (a flag in the workspace records a timeout).
 #include "common.h"
 #include "internal.h"
+#include "mfma_attn.h"
 
 namespace lsa {
 
-constexpr int kTKD = 64;           // keys per attention tile
 constexpr int kMaxP = 32;          // beam limit of this path
 constexpr int kMemCap = 2048;      // node members staged in LDS
 constexpr int kSpinLimit = 1 << 20;
+constexpr int kTKD = 64;           // keys per tile of the vector attention path
 
 struct DecodeArgs {
     const void *Q, *K, *V;
@@ -54,13 +56,13 @@ struct DecodeArgs {
     float *lse;
     // workspace
     int32_t *ctrl;        // [groups][4]: barrier, arrivals, timeout flag
-    uint64_t *lists;      // [L-2][groups][P][beam]
+    uint64_t *lists;      // [L-2][groups][P][64] sorted child keys of internal levels
     uint64_t *leaf_keys;  // [groups][P][64]
-    int32_t *leaf_pre;    // [groups][P][64]
+    int32_t *leaf_pre;    // [groups][P][64] inclusive prefix of eligible counts
     float *part;          // [groups][P][G*d + 2*G]
 };
 
-// ---------------------------------------------------------------- wave helpers
+// ---------------------------------------------------------------- helpers
 LSA_DEV uint64_t shfl_xor64(uint64_t v, int m) {
     const uint32_t lo = __shfl_xor((unsigned int)(v & 0xffffffffu), m, kWave);
     const uint32_t hi = __shfl_xor((unsigned int)(v >> 32), m, kWave);
@@ -77,8 +79,7 @@ LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) {
             const uint64_t ok = shfl_xor64(key, stride);
             const int op = __shfl_xor(pay, stride, kWave);
             const bool lower = (l & stride) == 0;
-            const bool desc_seg = (l & size) == 0;      // this segment ends descending
-            // lower lane keeps the larger key in a descending segment
+            const bool desc_seg = (l & size) == 0;
             const bool take_other = (lower == desc_seg) ? (ok > key) : (ok < key);
             if (take_other) { key = ok; pay = op; }
         }
@@ -96,14 +97,14 @@ LSA_DEV float wave_sum(float v) {
     return v;
 }
 
-// number of entries > x in a list sorted descending
-LSA_DEV int count_gt_desc(const uint64_t *a, int len, uint64_t x) {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] > x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
+// Number of entries > x in a 64-entry list sorted descending; a fixed number
+// of steps, so searches in different lists overlap.
+LSA_DEV int cnt_gt64(const uint64_t *a, uint64_t x) {
+    int c = 0;
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1) c += (a[c + step - 1] > x) ? step : 0;
+    c += (a[c] > x) ? 1 : 0;
+    return c;
 }
 
 LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
@@ -115,9 +116,15 @@ LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     return lo;
 }
 
+template <int RC>
 LSA_DEV float score_lds(const float *u, const float *row, int r) {
     double s = 0.0;
-    for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
+    if constexpr (RC > 0) {
+#pragma unroll
+        for (int x = 0; x < RC; ++x) s = fma((double)u[x], (double)row[x], s);
+    } else {
+        for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
+    }
     return (float)s;
 }
 
@@ -139,34 +146,35 @@ LSA_DEV void g2s_flat(E *dst, const E *__restrict__ src, int n) {
     }
 }
 
-// b rows of r floats (a node's children) into LDS rows of stride 65.
+// b rows of r floats (one node's children) into LDS rows of stride 65.
 LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
     if ((r & 3) == 0) g2s_rows<4>(Cs, 65, src, b * r, r);
     else g2s_scalar<16, float, float>(Cs, 65, src, b * r, r);
 }
 
 // All workgroups of a group wait here until `target` arrivals are counted.
+// The spin uses relaxed device-scope loads; one acquire fence follows it.
 LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
 }
 
-template <typename T, bool ATTEND>
+template <typename T, bool ATTEND, int RC, int DC>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
-    extern __shared__ float dyn[];                 // W staging, then attention tiles
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
     __shared__ float qbar_s[256];
     __shared__ float u_s[64];
     __shared__ float Cs[64 * 65];
@@ -175,19 +183,22 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t kept_s[kMaxP];
     __shared__ uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
-    __shared__ int32_t take_s[64], toff_s[65];
+    __shared__ int32_t take_s[64], toff_s[65], wpart[4][64];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s, nz_s;
+    __shared__ int32_t ids_w[4][kMT];
     __shared__ float m_run[16], l_run[16], alpha_s[16];
-    __shared__ int32_t ids_s[kTKD];
 
+    constexpr bool kMfma = ATTEND && sizeof(T) == 2 && DC > 0 && DC % 32 == 0;
+    const int r = RC > 0 ? RC : A.r;
+    const int d = DC > 0 ? DC : A.d;
     const int P = A.beam;
     const int p = blockIdx.x;
     const int gi = blockIdx.y;
     const int64_t i = gi / A.h_kv;
     const int g = gi % A.h_kv;
     const int G = A.h_q / A.h_kv;
-    const int d = A.d, r = A.r, b = A.b, L = A.L;
+    const int b = A.b, L = A.L;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wv = tid / kWave;
@@ -198,33 +209,37 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     const int32_t *perm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
     const int32_t *leaf_off = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
     const bool all_eligible = pos >= A.n - 1;
+    const size_t groups = (size_t)A.m * A.h_kv;
 
-    // ---- level-1 rows (independent of the query), W, the group's queries
+    // ---- prologue: level-1 rows and counts, W_g and the group's queries
+    float *Wl = dyn;               // [d][r]
+    float *Ql = dyn + d * r;       // [G][d]
     {
         const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
         const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
         if (tid < b) ccnt[tid] = cn1[tid];
         load_rows(Cs, C1, b, r);
         const float *Wg = A.W + (size_t)g * d * r;
-        if (((d * r) & 3) == 0) g2s_rows<8>(dyn, d * r, Wg, d * r, d * r);
-        else g2s_flat<16>(dyn, Wg, d * r);
-        for (int t = tid; t < d; t += blockDim.x) {
-            float qv[16];
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                qv[h] = (h < G) ? to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]) : 0.0f;
-            double s = 0.0;
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (h < G) s = s + (double)qv[h];
-            qbar_s[t] = (float)(s / (double)G);
-        }
+        if (((d * r) & 3) == 0) g2s_rows<8>(Wl, d * r, Wg, d * r, d * r);
+        else g2s_flat<16>(Wl, Wg, d * r);
+        g2s_scalar<16, T, float>(Ql, G * d, Q + ((size_t)i * A.h_q + (size_t)g * G) * d, G * d, G * d);
         if (tid == 0) { count_s = 0; last_s = 0; }
+    }
+    __syncthreads();
+    for (int t = tid; t < d; t += blockDim.x) {
+        double s = 0.0;
+        for (int h = 0; h < G; ++h) s = s + (double)Ql[h * d + t];
+        qbar_s[t] = (float)(s / (double)G);
     }
     __syncthreads();
     for (int c = tid; c < r; c += blockDim.x) {
         double s = 0.0;
-        for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)dyn[t * r + c], s);
+        if constexpr (DC > 0) {
+#pragma unroll 32
+            for (int t = 0; t < DC; ++t) s = fma((double)qbar_s[t], (double)Wl[t * r + c], s);
+        } else {
+            for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)Wl[t * r + c], s);
+        }
         u_s[c] = (float)s;
     }
     __syncthreads();
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     if (wv == 0) {
         uint64_t key = 0;
         int pay = 0;
-        if (lane < b && ccnt[lane] > 0) key = make_key(score_lds(u_s, Cs + lane * 65, r), (uint32_t)lane);
+        if (lane < b && ccnt[lane] > 0) key = make_key(score_lds<RC>(u_s, Cs + lane * 65, r), (uint32_t)lane);
         const int nz = __popcll(__ballot(key != 0));
         wave_sort_desc(key, pay);
         const int keep = min(P, nz);
@@ -244,8 +259,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     int barriers = 0;
     int64_t v = -1;
     for (int l = 2; l <= L; ++l) {
-        const int keep_prev = keep_s;
-        v = (p < keep_prev) ? kept_s[p] : -1;
+        v = (p < keep_s) ? kept_s[p] : -1;
         const bool leaf = (l == L);
         if (v >= 0) {
             const float *Cl = (const float *)(A.index + A.centroid_off[l]) + ((size_t)g * A.nodes[l] + (size_t)v * b) * r;
@@ -255,17 +269,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             load_rows(Cs, Cl, b, r);
         }
         __syncthreads();
-        if (leaf && v >= 0) {
-            // stage the node's members (leaves of one node are contiguous)
-            const int m0 = clo[0], mn = clo[b] - clo[0];
-            if (mn <= kMemCap) g2s_flat<8>(mem_s, perm + m0, mn);
+        if (leaf && v >= 0 && !all_eligible) {
+            // the node's members (its leaves are contiguous), for the causal counts
+            const int mn = clo[b] - clo[0];
+            if (mn <= kMemCap) g2s_flat<8>(mem_s, perm + clo[0], mn);
             __syncthreads();
         }
         if (wv == 0) {
             uint64_t key = 0;
             int e = 0;
             if (v >= 0 && lane < b && ccnt[lane] > 0) {
-                key = make_key(score_lds(u_s, Cs + lane * 65, r), (uint32_t)(v * b + lane));
+                key = make_key(score_lds<RC>(u_s, Cs + lane * 65, r), (uint32_t)(v * b + lane));
                 if (leaf) {
                     const int a0 = clo[lane], a1 = clo[lane + 1];
                     if (all_eligible) e = a1 - a0;
@@ -276,8 +290,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             wave_sort_desc(key, e);
             if (!leaf) {
-                uint64_t *dst = A.lists + (((size_t)(l - 2) * (A.m * A.h_kv) + gi) * P + p) * P;
-                if (lane < P) dst[lane] = key;
+                A.lists[(((size_t)(l - 2) * groups + gi) * P + p) * 64 + lane] = key;
             } else {
                 const int incl = wave_incl_scan_add(e);
                 const size_t o = ((size_t)gi * P + p) * 64 + lane;
@@ -288,18 +301,19 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         ++barriers;
         group_barrier(ctrl, barriers * P, ctrl + 2);
         if (!leaf) {
-            const uint64_t *src = A.lists + ((size_t)(l - 2) * (A.m * A.h_kv) + gi) * P * P;
-            g2s_flat<4>(lk, src, P * P);
+            g2s_flat<8>(lk, A.lists + ((size_t)(l - 2) * groups + gi) * P * 64, P * 64);
             if (tid == 0) nz_s = 0;
             __syncthreads();
+            if (tid < P) atomicAdd(&nz_s, cnt_gt64(lk + tid * 64, 0ull));
+            // global rank of each list's first P entries
             for (int e = tid; e < P * P; e += blockDim.x) {
-                const uint64_t x = lk[e];
-                if (x == 0) continue;
-                atomicAdd(&nz_s, 1);
                 const int q = e / P, j = e % P;
+                const uint64_t x = lk[q * 64 + j];
+                if (x == 0) continue;
                 int rank = j;
-                for (int q2 = 0; q2 < P; ++q2)
-                    if (q2 != q) rank += count_gt_desc(lk + q2 * P, P, x);
+#pragma unroll
+                for (int q2 = 0; q2 < kMaxP; ++q2)
+                    if (q2 < P && q2 != q) rank += cnt_gt64(lk + q2 * 64, x);
                 if (rank < P) kept_s[rank] = (int32_t)key_id(x);
             }
             __syncthreads();
@@ -310,16 +324,30 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 
     // ---- fill: every workgroup places its own leaves' keys
     {
-        const uint64_t *srck = A.leaf_keys + (size_t)gi * P * 64;
-        const int32_t *srcp = A.leaf_pre + (size_t)gi * P * 64;
-        g2s_flat<8>(lk, srck, P * 64);
-        g2s_flat<8>(lp, srcp, P * 64);
+        g2s_flat<8>(lk, A.leaf_keys + (size_t)gi * P * 64, P * 64);
+        g2s_flat<8>(lp, A.leaf_pre + (size_t)gi * P * 64, P * 64);
         if (tid < 64) take_s[tid] = 0;
         __syncthreads();
         if (tid == 0) {
             int tot = 0;
             for (int q = 0; q < P; ++q) tot += lp[q * 64 + 63];
             count_s = min(A.k, tot);
+        }
+        // eligible keys of other workgroups' leaves retrieved before each own leaf
+        {
+            const uint64_t x = lk[p * 64 + lane];
+            int part = 0;
+            if (x != 0) {
+#pragma unroll
+                for (int u = 0; u < kMaxP / 4; ++u) {
+                    const int q = wv + 4 * u;
+                    if (q < P && q != p) {
+                        const int c = cnt_gt64(lk + q * 64, x);
+                        if (c > 0) part += lp[q * 64 + c - 1];
+                    }
+                }
+            }
+            wpart[wv][lane] = part;
         }
         __syncthreads();
         const int count = count_s;
@@ -329,12 +357,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (x != 0) {
                 const int before = lane > 0 ? lp[p * 64 + lane - 1] : 0;
                 const int e = lp[p * 64 + lane] - before;
-                int wex = before;
-                for (int q = 0; q < P; ++q) {
-                    if (q == p) continue;
-                    const int c = count_gt_desc(lk + q * 64, 64, x);
-                    if (c > 0) wex += lp[q * 64 + c - 1];
-                }
+                const int wex = before + wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
                 const int take = max(0, min(e, count - wex));
                 const int c = (int)(key_id(x) - (uint32_t)(v * b));
                 take_s[c] = take;
@@ -356,111 +379,144 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 
     if constexpr (ATTEND) {
         // ---- attention over this workgroup's own keys
-        const int dp = d + 1;
-        float *qs = dyn;                       // [G][d]
-        float *Kt = qs + G * d;                // [TK][d + 1]
-        float *Vt = Kt + kTKD * dp;            // [TK][d]
-        float *S = Vt + kTKD * d;              // [G][TK]
         if (wv == 0) {
             const int tk = take_s[lane];
             const int incl = wave_incl_scan_add(tk);
             toff_s[lane] = incl - tk;
             if (lane == 63) toff_s[64] = incl;
         }
-        for (int e = tid; e < G * d; e += blockDim.x)
-            qs[e] = to_float(Q[((size_t)i * A.h_q + (size_t)g * G) * d + e]) * A.scale_log2;
-        if (tid < 16) { m_run[tid] = -INFINITY; l_run[tid] = 0.0f; }
         __syncthreads();
         const int own = (v >= 0) ? toff_s[64] : 0;
-        const int ne = (G * d + blockDim.x - 1) / blockDim.x;
-        float acc[16];
+        // key id of own key f: its leaf is the last c with toff_s[c] <= f
+        auto own_id = [&](int f) -> int32_t {
+            int c = 0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-        const T *Kg = (const T *)A.K + (size_t)g * A.n * d;
-        const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
-        const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
-        for (int f0 = 0; f0 < own; f0 += kTKD) {
-            const int nk = min(kTKD, own - f0);
-            if (tid < nk) {
-                const int f = f0 + tid;
-                int lo = 0, hi = 64;                 // last leaf c with toff_s[c] <= f
-                while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (toff_s[mid] <= f) lo = mid; else hi = mid; }
-                const int off = clo[lo] + (f - toff_s[lo]);
-                ids_s[tid] = staged ? mem_s[off - clo[0]] : perm[off];
+            for (int step = 32; step >= 1; step >>= 1) c += (toff_s[c + step] <= f) ? step : 0;
+            return perm[clo[c] + (f - toff_s[c])];
+        };
+        float *pp = A.part + ((size_t)gi * P + p) * (G * d + 2 * G);
+        if constexpr (kMfma) {
+            const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
+            const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * DC;
+            const uint16_t *Qb = (const uint16_t *)A.Q + ((size_t)i * A.h_q + (size_t)g * G) * DC;
+            uint16_t *vt = reinterpret_cast<uint16_t *>(dyn) + (size_t)wv * DC * kVTS;
+            bf16x8_t qf[DC / 32];
+            wave_load_q<DC>(qf, Qb, G);
+            WaveAttn<DC> st;
+            wave_attn_init<DC>(st);
+            const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
+            for (int t = 0; t < nsteps; ++t) {
+                const int fb = (4 * t + wv) * kMT;
+                const int nk = max(0, min(kMT, own - fb));
+                if (lane < kMT) ids_w[wv][lane] = (lane < nk) ? own_id(fb + lane) : 0;
+                __syncthreads();
+                bf16x8_t pf;
+                float alpha;
+                wave_attn_part1<DC>(Kg, Vg, ids_w[wv], nk, qf, A.scale_log2, vt, st, pf, alpha);
+                __syncthreads();
+                wave_attn_part2<DC>(vt, pf, alpha, st);
             }
             __syncthreads();
-            // gather rows, 8 elements per load
-            gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
+            wave_attn_stash<DC>(st, dyn);
             __syncthreads();
-            for (int e = tid; e < G * kTKD; e += blockDim.x) {
-                const int h = e / kTKD, kk = e % kTKD;
-                float s = -INFINITY;
-                if (kk < nk) {
-                    const float *qh = qs + h * d;
-                    const float *kr = Kt + kk * dp;
-                    s = 0.0f;
-                    for (int t = 0; t < d; ++t) s = fmaf(qh[t], kr[t], s);
+            for (int e = tid; e < G * DC; e += blockDim.x) {
+                const int h = e / DC, dd = e % DC;
+                float M, Ls;
+                pp[e] = wave_attn_combine<DC>(dyn, h, dd, M, Ls);
+                if (dd == 0) { pp[G * DC + h] = M; pp[G * DC + G + h] = Ls; }
+            }
+        } else {
+            const int dp = d + 1;
+            float *qs = dyn;                       // [G][d]
+            float *Kt = qs + G * d;                // [TK][d + 1]
+            float *Vt = Kt + kTKD * dp;            // [TK][d]
+            float *S = Vt + kTKD * d;              // [G][TK]
+            int32_t *ids_s = &ids_w[0][0];         // kTKD ids
+            for (int e = tid; e < G * d; e += blockDim.x)
+                qs[e] = to_float(Q[((size_t)i * A.h_q + (size_t)g * G) * d + e]) * A.scale_log2;
+            if (tid < 16) { m_run[tid] = -INFINITY; l_run[tid] = 0.0f; }
+            __syncthreads();
+            const int ne = (G * d + blockDim.x - 1) / blockDim.x;
+            float acc[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+            const T *Kg = (const T *)A.K + (size_t)g * A.n * d;
+            const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
+            for (int f0 = 0; f0 < own; f0 += kTKD) {
+                const int nk = min(kTKD, own - f0);
+                if (tid < nk) ids_s[tid] = own_id(f0 + tid);
+                __syncthreads();
+                gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
+                __syncthreads();
+                for (int e = tid; e < G * kTKD; e += blockDim.x) {
+                    const int h = e / kTKD, kk = e % kTKD;
+                    float s = -INFINITY;
+                    if (kk < nk) {
+                        const float *qh = qs + h * d;
+                        const float *kr = Kt + kk * dp;
+                        s = 0.0f;
+#pragma unroll 8
+                        for (int t = 0; t < d; ++t) s = fmaf(qh[t], kr[t], s);
+                    }
+                    S[h * kTKD + kk] = s;
                 }
-                S[h * kTKD + kk] = s;
-            }
-            __syncthreads();
-            for (int h = wv; h < G; h += blockDim.x / kWave) {
-                const float x = S[h * kTKD + lane];
-                const float mt = wave_max(x);
-                const float mnew = fmaxf(m_run[h], mt);
-                const float pr = (lane < nk) ? exp2f(x - mnew) : 0.0f;
-                S[h * kTKD + lane] = pr;
-                const float ls = wave_sum(pr);
-                if (lane == 0) {
-                    const float al = exp2f(m_run[h] - mnew);
-                    alpha_s[h] = al;
-                    l_run[h] = l_run[h] * al + ls;
-                    m_run[h] = mnew;
+                __syncthreads();
+                for (int h = wv; h < G; h += blockDim.x / kWave) {
+                    const float x = S[h * kTKD + lane];
+                    const float mt = wave_max(x);
+                    const float mnew = fmaxf(m_run[h], mt);
+                    const float pr = (lane < nk) ? exp2f(x - mnew) : 0.0f;
+                    S[h * kTKD + lane] = pr;
+                    const float ls = wave_sum(pr);
+                    if (lane == 0) {
+                        const float al = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mnew);
+                        alpha_s[h] = al;
+                        l_run[h] = l_run[h] * al + ls;
+                        m_run[h] = mnew;
+                    }
                 }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    if (q >= ne) break;
+                    const int e = tid + q * blockDim.x;
+                    if (e >= G * d) break;
+                    const int h = e / d, t = e % d;
+                    const float *ph = S + h * kTKD;
+                    float a = acc[q] * alpha_s[h];
+#pragma unroll 8
+                    for (int kk = 0; kk < nk; ++kk) a = fmaf(ph[kk], Vt[kk * d + t], a);
+                    acc[q] = a;
+                }
+                __syncthreads();
             }
-            __syncthreads();
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 if (q >= ne) break;
                 const int e = tid + q * blockDim.x;
                 if (e >= G * d) break;
-                const int h = e / d, t = e % d;
-                const float *ph = S + h * kTKD;
-                float a = acc[q] * alpha_s[h];
-                for (int kk = 0; kk < nk; ++kk) a = fmaf(ph[kk], Vt[kk * d + t], a);
-                acc[q] = a;
+                pp[e] = acc[q];
             }
-            __syncthreads();
+            if (tid < G) { pp[G * d + tid] = m_run[tid]; pp[G * d + G + tid] = l_run[tid]; }
         }
-        // partial state of this workgroup
-        float *pp = A.part + ((size_t)gi * P + p) * (G * d + 2 * G);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q >= ne) break;
-            const int e = tid + q * blockDim.x;
-            if (e >= G * d) break;
-            pp[e] = acc[q];
-        }
-        if (tid < G) { pp[G * d + tid] = m_run[tid]; pp[G * d + G + tid] = l_run[tid]; }
     }
 
     // ---- arrival; the last workgroup merges and resets the group's counters
     __syncthreads();
     if (tid == 0) {
-        __threadfence();
-        const int old = __hip_atomic_fetch_add(ctrl + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const int old = __hip_atomic_fetch_add(ctrl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_s = (old == P - 1);
-        __threadfence();
+        if (last_s) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!last_s) return;
     if constexpr (ATTEND) {
         const float *pb = A.part + (size_t)gi * P * (G * d + 2 * G);
         const int stride = G * d + 2 * G;
-        // per-(workgroup, head) weights 2^(m_q - M) and the total sums, in LDS
-        float *wq = dyn;                       // [P][G]
-        float *lq = dyn + kMaxP * 16;          // [P][G]
-        float *Ms = lq + kMaxP * 16;           // [G], then L [G]
+        float *wq = dyn;                       // [P][G] weights 2^(m_q - M)
+        float *lq = dyn + kMaxP * 16;          // [P][G] sums
+        float *Ms = lq + kMaxP * 16;           // [G] max, then [G] total
         for (int e = tid; e < P * G; e += blockDim.x) {
             const int q = e / G, h = e % G;
             wq[e] = pb[(size_t)q * stride + G * d + h];
@@ -497,7 +553,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
     if (tid == 0) {
         __hip_atomic_store(ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ctrl + 1, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -511,7 +567,7 @@ static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G,
     DecodeWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
     w.ctrl = (int32_t *)take(sizeof(int32_t) * 4 * (size_t)groups);
-    w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * P);
+    w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * 64);
     w.leaf_keys = (uint64_t *)take(sizeof(uint64_t) * (size_t)groups * P * 64);
     w.leaf_pre = (int32_t *)take(sizeof(int32_t) * (size_t)groups * P * 64);
     w.part = (float *)take(sizeof(float) * (size_t)groups * P * ((size_t)G * d + 2 * G));
@@ -531,10 +587,17 @@ static int device_cus() {
     return cus[dev];
 }
 
-static size_t decode_dyn_bytes(int G, int d, int r) {
-    const size_t att = sizeof(float) * ((size_t)G * d + (size_t)kTKD * (d + 1) + (size_t)kTKD * d + (size_t)G * kTKD);
-    const size_t w = sizeof(float) * (size_t)d * r;
-    return att > w ? att : w;
+static bool fast_shape(int dtype, int d, int r) { return dtype == 1 && d == 128 && r == 64; }
+
+static size_t decode_dyn_bytes(int dtype, int G, int d, int r) {
+    const size_t stage = sizeof(float) * ((size_t)d * r + (size_t)G * d);                 // W, Q staging
+    size_t att;
+    if (fast_shape(dtype, d, r))
+        att = std::max(sizeof(uint16_t) * 4 * (size_t)d * kVTS, sizeof(float) * (4 * (size_t)d * 16 + 128));
+    else
+        att = sizeof(float) * ((size_t)G * d + (size_t)kTKD * (d + 1) + (size_t)kTKD * d + (size_t)G * kTKD);
+    const size_t merge = sizeof(float) * (2 * kMaxP * 16 + 32);
+    return std::max(stage, std::max(att, merge));
 }
 
 constexpr size_t kStaticLds = 56 * 1024;      // upper bound of k_decode's static LDS
@@ -543,7 +606,7 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k) {
     const int G = h_q / h_kv;
     if (L < 2 || b > 64 || r > 64 || beam > kMaxP || beam < 1 || G > 16 || d > 256 || d % 8 != 0) return false;
-    if (decode_dyn_bytes(G, d, r) + kStaticLds > kLdsPerCu) return false;
+    if (decode_dyn_bytes(0, G, d, r) + kStaticLds > kLdsPerCu) return false;
     (void)k;
     const int cus = device_cus();
     return cus > 0 && m * h_kv * beam <= cus;
@@ -551,6 +614,21 @@ bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, in
 
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam) {
     return (int64_t)carve_decode_ws(nullptr, m * h_kv, beam, L, h_q / h_kv, d).bytes;
+}
+
+template <typename T, bool ATT, int RC, int DC>
+static hipError_t launch_decode(const DecodeArgs &A, dim3 grid, size_t shm, hipStream_t st) {
+    static int attr_set[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_decode<T, ATT, RC, DC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsPerCu - kStaticLds));
+        if (e != hipSuccess) return e;
+        attr_set[dev] = 1;
+    }
+    hipLaunchKernelGGL((k_decode<T, ATT, RC, DC>), grid, dim3(256), shm, st, A);
+    return hipGetLastError();
 }
 
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,
@@ -568,30 +646,17 @@ hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_
     const int G = h_q / h_kv;
     DecodeWs w = carve_decode_ws((char *)ws, m * h_kv, beam, L, G, d);
     A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.part = w.part;
-    const size_t shm = decode_dyn_bytes(G, d, r);
+    const size_t shm = decode_dyn_bytes(dtype, G, d, r);
     const dim3 grid((unsigned)beam, (unsigned)(m * h_kv));
-    // allow the largest dynamic LDS this path uses, once per kernel and device
-    static int attr_set[64][4] = {{0}};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    const int which = (dtype == 0 ? 0 : 2) + (attend ? 1 : 0);
-    if (!attr_set[dev][which]) {
-        const void *fn;
-        if (dtype == 0) fn = attend ? (const void *)k_decode<float, true> : (const void *)k_decode<float, false>;
-        else fn = attend ? (const void *)k_decode<bf16_t, true> : (const void *)k_decode<bf16_t, false>;
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kLdsPerCu - kStaticLds));
-        if (e != hipSuccess) return e;
-        attr_set[dev][which] = 1;
+    if (fast_shape(dtype, d, r)) {
+        return attend ? launch_decode<bf16_t, true, 64, 128>(A, grid, shm, st)
+                      : launch_decode<bf16_t, false, 64, 128>(A, grid, shm, st);
     }
-    if (dtype == 0) {
-        if (attend) hipLaunchKernelGGL((k_decode<float, true>), grid, dim3(256), shm, st, A);
-        else hipLaunchKernelGGL((k_decode<float, false>), grid, dim3(256), shm, st, A);
-    } else {
-        if (attend) hipLaunchKernelGGL((k_decode<bf16_t, true>), grid, dim3(256), shm, st, A);
-        else hipLaunchKernelGGL((k_decode<bf16_t, false>), grid, dim3(256), shm, st, A);
-    }
-    return hipGetLastError();
+    if (dtype == 0)
+        return attend ? launch_decode<float, true, 0, 0>(A, grid, shm, st)
+                      : launch_decode<float, false, 0, 0>(A, grid, shm, st);
+    return attend ? launch_decode<bf16_t, true, 0, 0>(A, grid, shm, st)
+                  : launch_decode<bf16_t, false, 0, 0>(A, grid, shm, st);
 }
 
 }  // namespace lsa
