@@ -92,6 +92,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--layers-per-graph", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -146,8 +147,13 @@ def main():
 
     do_step()
     torch.cuda.synchronize()
+    # A model's decode step runs its layers back to back inside one captured
+    # graph; R consecutive layers are captured here and each replay counts as R
+    # steps (R divides the step count).
+    R = args.layers_per_graph if args.steps % args.layers_per_graph == 0 else 1
     use_graph = not args.no_graph
-    run_step = do_step
+    run_block = do_step
+    single_layer_us = None
     if use_graph:
         try:
             s = torch.cuda.Stream()
@@ -155,38 +161,54 @@ def main():
             with torch.cuda.stream(s):
                 do_step()
             torch.cuda.current_stream().wait_stream(s)
-            graph = torch.cuda.CUDAGraph()
+            graph, g1 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
+                for _ in range(R):
+                    do_step()
+            with torch.cuda.graph(g1):
                 do_step()
             # replays must reproduce the eager result
             ref = (sel.clone(), cnt.clone(), out.clone())
-            for _ in range(3):
+            for gr in (graph, g1, graph):
                 sel.zero_(); out.zero_()
-                graph.replay()
+                gr.replay()
                 torch.cuda.synchronize()
                 assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1]) and torch.equal(out, ref[2])
-            run_step = graph.replay
+            run_block = graph.replay
+            for _ in range(10):
+                g1.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(100):
+                g1.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            single_layer_us = e0.elapsed_time(e1) * 10.0
         except Exception as e:      # graph capture unavailable: time eager launches
             log("graph capture failed, timing eager launches:", repr(e))
             use_graph = False
+            R = 1
+    if not use_graph:
+        R = 1
 
     log("warmup", args.warmup)
-    for _ in range(args.warmup):
-        run_step()
+    for _ in range(max(1, args.warmup // R)):
+        run_block()
     torch.cuda.synchronize()
     K_ = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_)]
-    log("timed", K_)
+    nblk = K_ // R
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nblk)]
+    log("timed", K_, "steps in", nblk, "launches of", R)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s_ in range(K_):
+    for s_ in range(nblk):
         ev[s_][0].record()
-        run_step()
+        run_block()
         ev[s_][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K_
-    step_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    step_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3 / R
     counts = cnt.cpu().numpy()
     cand_leaves = w.beam * w.b
     sb = select_bytes(w, m, counts, cand_leaves)
@@ -213,7 +235,8 @@ def main():
     sel_us = e3[0].elapsed_time(e3[1]) / nsep * 1e3
     att_us = e3[1].elapsed_time(e3[2]) / nsep * 1e3
 
-    breakdown = {"fused_step_us": round(step_us, 3),
+    breakdown = {"fused_step_us": round(step_us, 3), "layers_per_graph": R,
+                 "single_layer_graph_us": None if single_layer_us is None else round(single_layer_us, 3),
                  "select_only_us": round(sel_us, 3), "attend_only_us": round(att_us, 3),
                  "select_GBps": round(sb / (sel_us * 1e-6) / 1e9, 2),
                  "attend_GBps": round(ab / (att_us * 1e-6) / 1e9, 2),
@@ -273,6 +296,7 @@ def main():
         "config": {"workload": w.name, "n": w.n, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "r": w.r, "b": w.b,
                    "L": w.L, "beam": w.beam, "k": w.k, "query_rows": m,
                    "step": "lsa_select_attend (select + attend, one launch), index resident",
+                   "timing": "consecutive decode layers captured in one HIP graph, per-layer time",
                    "indexer_arith": "f64 accumulate", "attention_arith": "f32 accumulate"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -107,6 +107,25 @@ LSA_DEV int cnt_gt64(const uint64_t *a, uint64_t x) {
     return c;
 }
 
+// Sum over the first P 64-entry lists of the number of entries > x.  All
+// searches advance one step together, so their LDS reads overlap.
+LSA_DEV int cnt_gt_lists(const uint64_t *lists, int P, uint64_t x) {
+    int c[kMaxP];
+#pragma unroll
+    for (int q = 0; q < kMaxP; ++q) c[q] = 0;
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1) {
+#pragma unroll
+        for (int q = 0; q < kMaxP; ++q)
+            if (q < P) c[q] += (lists[q * 64 + c[q] + step - 1] > x) ? step : 0;
+    }
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxP; ++q)
+        if (q < P) tot += c[q] + ((lists[q * 64 + c[q]] > x) ? 1 : 0);
+    return tot;
+}
+
 LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     int lo = 0, hi = len;
     while (lo < hi) {
@@ -218,11 +237,43 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
         const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
         if (tid < b) ccnt[tid] = cn1[tid];
-        load_rows(Cs, C1, b, r);
         const float *Wg = A.W + (size_t)g * d * r;
-        if (((d * r) & 3) == 0) g2s_rows<8>(Wl, d * r, Wg, d * r, d * r);
-        else g2s_flat<16>(Wl, Wg, d * r);
-        g2s_scalar<16, T, float>(Ql, G * d, Q + ((size_t)i * A.h_q + (size_t)g * G) * d, G * d, G * d);
+        if constexpr (RC == 64 && DC == 128 && sizeof(T) == 2) {
+            // one round of loads: 4 float4 of rows, 8 float4 of W, 1 uint4 of Q per thread
+            const float4 *c4 = reinterpret_cast<const float4 *>(C1);
+            const float4 *w4 = reinterpret_cast<const float4 *>(Wg);
+            const uint4 *q4 = reinterpret_cast<const uint4 *>(Q + ((size_t)i * A.h_q + (size_t)g * G) * DC);
+            float4 cr[4], wr[8];
+            uint4 qr = {0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { const int e = tid + 256 * u; if (e < b * 16) cr[u] = c4[e]; }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) wr[u] = w4[tid + 256 * u];
+            if (tid < G * 16) qr = q4[tid];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = tid + 256 * u;
+                if (e < b * 16) {
+                    float *q = Cs + (e / 16) * 65 + (e % 16) * 4;
+                    q[0] = cr[u].x; q[1] = cr[u].y; q[2] = cr[u].z; q[3] = cr[u].w;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) reinterpret_cast<float4 *>(Wl)[tid + 256 * u] = wr[u];
+            if (tid < G * 16) {
+                const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    Ql[tid * 8 + 2 * j] = __uint_as_float(qw[j] << 16);
+                    Ql[tid * 8 + 2 * j + 1] = __uint_as_float(qw[j] & 0xffff0000u);
+                }
+            }
+        } else {
+            load_rows(Cs, C1, b, r);
+            if (((d * r) & 3) == 0) g2s_rows<8>(Wl, d * r, Wg, d * r, d * r);
+            else g2s_flat<16>(Wl, Wg, d * r);
+            g2s_scalar<16, T, float>(Ql, G * d, Q + ((size_t)i * A.h_q + (size_t)g * G) * d, G * d, G * d);
+        }
         if (tid == 0) { count_s = 0; last_s = 0; }
     }
     __syncthreads();
@@ -269,8 +320,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             load_rows(Cs, Cl, b, r);
         }
         __syncthreads();
-        if (leaf && v >= 0 && !all_eligible) {
-            // the node's members (its leaves are contiguous), for the causal counts
+        if (leaf && v >= 0) {
+            // the node's members (its leaves are contiguous): causal counts,
+            // the keys this workgroup writes and attends over
             const int mn = clo[b] - clo[0];
             if (mn <= kMemCap) g2s_flat<8>(mem_s, perm + clo[0], mn);
             __syncthreads();
@@ -305,16 +357,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (tid == 0) nz_s = 0;
             __syncthreads();
             if (tid < P) atomicAdd(&nz_s, cnt_gt64(lk + tid * 64, 0ull));
-            // global rank of each list's first P entries
+            // global rank of each list's first P entries: the number of keys
+            // above it over all lists (its own list contributes its index)
             for (int e = tid; e < P * P; e += blockDim.x) {
                 const int q = e / P, j = e % P;
                 const uint64_t x = lk[q * 64 + j];
-                if (x == 0) continue;
-                int rank = j;
-#pragma unroll
-                for (int q2 = 0; q2 < kMaxP; ++q2)
-                    if (q2 < P && q2 != q) rank += cnt_gt64(lk + q2 * 64, x);
-                if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                const int rank = cnt_gt_lists(lk, P, x);
+                if (x != 0 && rank < P) kept_s[rank] = (int32_t)key_id(x);
             }
             __syncthreads();
             if (tid == 0) keep_s = min(P, nz_s);
@@ -336,18 +385,28 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         // eligible keys of other workgroups' leaves retrieved before each own leaf
         {
             const uint64_t x = lk[p * 64 + lane];
-            int part = 0;
-            if (x != 0) {
+            constexpr int U = kMaxP / 4;
+            int c[U];
 #pragma unroll
-                for (int u = 0; u < kMaxP / 4; ++u) {
+            for (int u = 0; u < U; ++u) c[u] = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
                     const int q = wv + 4 * u;
-                    if (q < P && q != p) {
-                        const int c = cnt_gt64(lk + q * 64, x);
-                        if (c > 0) part += lp[q * 64 + c - 1];
-                    }
+                    if (q < P) c[u] += (lk[q * 64 + c[u] + step - 1] > x) ? step : 0;
                 }
             }
-            wpart[wv][lane] = part;
+            int part = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = wv + 4 * u;
+                if (q < P && q != p) {
+                    const int cc = c[u] + ((lk[q * 64 + c[u]] > x) ? 1 : 0);
+                    if (cc > 0) part += lp[q * 64 + cc - 1];
+                }
+            }
+            wpart[wv][lane] = (x != 0) ? part : 0;
         }
         __syncthreads();
         const int count = count_s;
@@ -363,7 +422,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 take_s[c] = take;
                 if (take > 0) {
                     const int a0 = clo[c];
-                    for (int t = 0; t < take; ++t) out[wex + t] = perm[a0 + t];
+                    if (clo[b] - clo[0] <= kMemCap)
+                        for (int t = 0; t < take; ++t) out[wex + t] = mem_s[a0 - clo[0] + t];
+                    else
+                        for (int t = 0; t < take; ++t) out[wex + t] = perm[a0 + t];
                 }
                 if (count == A.k && wex < A.k && wex + e >= A.k && A.sel_cutoff)
                     A.sel_cutoff[gi] = key_score(x);
@@ -388,11 +450,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         __syncthreads();
         const int own = (v >= 0) ? toff_s[64] : 0;
         // key id of own key f: its leaf is the last c with toff_s[c] <= f
+        const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
         auto own_id = [&](int f) -> int32_t {
             int c = 0;
 #pragma unroll
             for (int step = 32; step >= 1; step >>= 1) c += (toff_s[c + step] <= f) ? step : 0;
-            return perm[clo[c] + (f - toff_s[c])];
+            const int off = clo[c] + (f - toff_s[c]);
+            return staged ? mem_s[off - clo[0]] : perm[off];
         };
         float *pp = A.part + ((size_t)gi * P + p) * (G * d + 2 * G);
         if constexpr (kMfma) {

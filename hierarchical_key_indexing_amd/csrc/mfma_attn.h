@@ -5,7 +5,8 @@
 // v_mfma_f32_16x16x32_bf16 (A: 16 keys x 32 dims, B: 32 dims x 16 heads, each
 // lane holding 8 consecutive bf16 of one row; D: lane l holds head l % 16 and
 // keys 4*(l/16)..+3).  K fragments come straight from the gathered rows.  The
-// online softmax runs per head column in registers (base 2).  The output is
+// online softmax runs per head column in registers (base 2); the running sum
+// uses the fp32 probabilities, the P V product their bf16 rounding.  The output is
 // accumulated transposed, O^T[dim][head] += V^T P^T, with the 32 keys of the
 // contraction placed in the order each lane already holds its probabilities
 // (slot s < 4: key 4*(l/16) + s, slot s >= 4: key 16 + 4*(l/16) + s - 4), so the
@@ -113,9 +114,8 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const float pr = (sv[s] == -INFINITY) ? 0.0f : exp2f(sv[s] - m_new);
-        const uint16_t pb = bf16_bits_rne(pr);
-        ls += __uint_as_float((uint32_t)pb << 16);
-        pf[s] = __builtin_bit_cast(__bf16, pb);
+        ls += pr;
+        pf[s] = __builtin_bit_cast(__bf16, bf16_bits_rne(pr));
     }
     ls += __shfl_xor(ls, 16, kWave);
     ls += __shfl_xor(ls, 32, kWave);
