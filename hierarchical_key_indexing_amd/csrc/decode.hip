@@ -13,10 +13,10 @@
 // latent query and the level-1 ranking itself (identical results), then at
 // each deeper level workgroup p scores the children of the p-th kept node,
 // sorts them within one wave and publishes the sorted list.  After a group
-// barrier every workgroup derives global ranks by fixed-step binary searches
-// in the P sorted lists (the global top-beam at internal levels; at the leaf
-// level, how many eligible keys are retrieved before each of its leaves), so
-// no workgroup sorts more than 64 keys.  Workgroup p then writes its own
+// barrier every workgroup derives global ranks by counting, with broadcast LDS
+// reads, the published keys above each candidate (the global top-beam at
+// internal levels; at the leaf level, how many eligible keys are retrieved
+// before each of its leaves), so no workgroup sorts more than 64 keys.  Workgroup p then writes its own
 // leaves' keys at their retrieval offsets and attends over them (matrix cores
 // for bf16); the last workgroup of the group to finish merges the P partial
 // softmax states and resets the group's counters.
@@ -97,35 +97,6 @@ LSA_DEV float wave_sum(float v) {
     return v;
 }
 
-// Number of entries > x in a 64-entry list sorted descending; a fixed number
-// of steps, so searches in different lists overlap.
-LSA_DEV int cnt_gt64(const uint64_t *a, uint64_t x) {
-    int c = 0;
-#pragma unroll
-    for (int step = 32; step >= 1; step >>= 1) c += (a[c + step - 1] > x) ? step : 0;
-    c += (a[c] > x) ? 1 : 0;
-    return c;
-}
-
-// Sum over the first P 64-entry lists of the number of entries > x.  All
-// searches advance one step together, so their LDS reads overlap.
-LSA_DEV int cnt_gt_lists(const uint64_t *lists, int P, uint64_t x) {
-    int c[kMaxP];
-#pragma unroll
-    for (int q = 0; q < kMaxP; ++q) c[q] = 0;
-#pragma unroll
-    for (int step = 32; step >= 1; step >>= 1) {
-#pragma unroll
-        for (int q = 0; q < kMaxP; ++q)
-            if (q < P) c[q] += (lists[q * 64 + c[q] + step - 1] > x) ? step : 0;
-    }
-    int tot = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxP; ++q)
-        if (q < P) tot += c[q] + ((lists[q * 64 + c[q]] > x) ? 1 : 0);
-    return tot;
-}
-
 LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     int lo = 0, hi = len;
     while (lo < hi) {
@@ -203,6 +174,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
     __shared__ int32_t take_s[64], toff_s[65], wpart[4][64];
+    __shared__ int32_t le_s[kMaxP * 64];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s, nz_s;
     __shared__ int32_t ids_w[4][kMT];
@@ -353,17 +325,23 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         ++barriers;
         group_barrier(ctrl, barriers * P, ctrl + 2);
         if (!leaf) {
-            g2s_flat<8>(lk, A.lists + ((size_t)(l - 2) * groups + gi) * P * 64, P * 64);
+            // candidates: the first P entries of every list (the global top P
+            // lie among them); a candidate's rank is the number of candidates
+            // above it, counted with broadcast LDS reads
+            const uint64_t *src = A.lists + ((size_t)(l - 2) * groups + gi) * P * 64;
+            const int nc = P * P;
+            for (int e = tid; e < nc; e += blockDim.x) lk[e] = src[(e / P) * 64 + (e % P)];
             if (tid == 0) nz_s = 0;
             __syncthreads();
-            if (tid < P) atomicAdd(&nz_s, cnt_gt64(lk + tid * 64, 0ull));
-            // global rank of each list's first P entries: the number of keys
-            // above it over all lists (its own list contributes its index)
-            for (int e = tid; e < P * P; e += blockDim.x) {
-                const int q = e / P, j = e % P;
-                const uint64_t x = lk[q * 64 + j];
-                const int rank = cnt_gt_lists(lk, P, x);
-                if (x != 0 && rank < P) kept_s[rank] = (int32_t)key_id(x);
+            for (int e = tid; e < nc; e += blockDim.x) {
+                const uint64_t x = lk[e];
+                int rank = 0;
+#pragma unroll 16
+                for (int y = 0; y < nc; ++y) rank += (lk[y] > x) ? 1 : 0;
+                if (x != 0) {
+                    atomicAdd(&nz_s, 1);
+                    if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                }
             }
             __syncthreads();
             if (tid == 0) keep_s = min(P, nz_s);
@@ -382,29 +360,20 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int q = 0; q < P; ++q) tot += lp[q * 64 + 63];
             count_s = min(A.k, tot);
         }
-        // eligible keys of other workgroups' leaves retrieved before each own leaf
+        // eligible keys retrieved before each own leaf: wave w sums, over the
+        // lists q = w, w + 4, ..., the counts of leaves scored above it
+        // (broadcast LDS reads; the own list gives the keys before it)
+        for (int e = tid; e < P * 64; e += blockDim.x) {
+            const int j = e % 64;
+            le_s[e] = lp[e] - (j > 0 ? lp[e - 1] : 0);
+        }
+        __syncthreads();
         {
             const uint64_t x = lk[p * 64 + lane];
-            constexpr int U = kMaxP / 4;
-            int c[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) c[u] = 0;
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int q = wv + 4 * u;
-                    if (q < P) c[u] += (lk[q * 64 + c[u] + step - 1] > x) ? step : 0;
-                }
-            }
             int part = 0;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = wv + 4 * u;
-                if (q < P && q != p) {
-                    const int cc = c[u] + ((lk[q * 64 + c[u]] > x) ? 1 : 0);
-                    if (cc > 0) part += lp[q * 64 + cc - 1];
-                }
+            for (int q = wv; q < P; q += 4) {
+#pragma unroll 16
+                for (int j = 0; j < 64; ++j) part += (lk[q * 64 + j] > x) ? le_s[q * 64 + j] : 0;
             }
             wpart[wv][lane] = (x != 0) ? part : 0;
         }
@@ -414,9 +383,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         if (wv == 0 && v >= 0) {
             const uint64_t x = lk[p * 64 + lane];
             if (x != 0) {
-                const int before = lane > 0 ? lp[p * 64 + lane - 1] : 0;
-                const int e = lp[p * 64 + lane] - before;
-                const int wex = before + wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
+                const int e = le_s[p * 64 + lane];
+                const int wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
                 const int take = max(0, min(e, count - wex));
                 const int c = (int)(key_id(x) - (uint32_t)(v * b));
                 take_s[c] = take;
@@ -664,7 +632,7 @@ static size_t decode_dyn_bytes(int dtype, int G, int d, int r) {
     return std::max(stage, std::max(att, merge));
 }
 
-constexpr size_t kStaticLds = 56 * 1024;      // upper bound of k_decode's static LDS
+constexpr size_t kStaticLds = 64 * 1024;      // upper bound of k_decode's static LDS
 constexpr size_t kLdsPerCu = 160 * 1024;
 
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k) {
