@@ -78,10 +78,13 @@ LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             const uint64_t ok = shfl_xor64(key, stride);
             const int op = __shfl_xor(pay, stride, kWave);
-            const bool lower = (l & stride) == 0;
-            const bool desc_seg = (l & size) == 0;
-            const bool take_other = (lower == desc_seg) ? (ok > key) : (ok < key);
-            if (take_other) { key = ok; pay = op; }
+            // lower lane of a descending segment (or upper lane of an
+            // ascending one) keeps the larger key; branch-free select
+            const unsigned want_gt = ((l & stride) == 0) == ((l & size) == 0);
+            const unsigned gt = ok > key, lt = ok < key;
+            const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
+            key = take ? ok : key;
+            pay = take ? op : pay;
         }
     }
 }
@@ -171,10 +174,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t ccnt[64];
     __shared__ int32_t clo[65];
     __shared__ int32_t kept_s[kMaxP];
-    __shared__ uint64_t lk[kMaxP * 64];
+    __shared__ __attribute__((aligned(16))) uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
     __shared__ int32_t take_s[64], toff_s[65], wpart[4][64];
-    __shared__ int32_t le_s[kMaxP * 64];
+    __shared__ __attribute__((aligned(16))) int32_t le_s[kMaxP * 64];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s, nz_s;
     __shared__ int32_t ids_w[4][kMT];
@@ -333,11 +336,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int e = tid; e < nc; e += blockDim.x) lk[e] = src[(e / P) * 64 + (e % P)];
             if (tid == 0) nz_s = 0;
             __syncthreads();
+            for (int e = nc + tid; e < ((nc + 3) & ~3); e += blockDim.x) lk[e] = 0ull;
+            __syncthreads();
             for (int e = tid; e < nc; e += blockDim.x) {
                 const uint64_t x = lk[e];
                 int rank = 0;
-#pragma unroll 16
-                for (int y = 0; y < nc; ++y) rank += (lk[y] > x) ? 1 : 0;
+                const ulonglong2 *l2 = reinterpret_cast<const ulonglong2 *>(lk);
+#pragma unroll 8
+                for (int y = 0; y < (nc + 3) / 4; ++y) {
+                    const ulonglong2 a = l2[2 * y], c = l2[2 * y + 1];
+                    rank += (int)(a.x > x) + (int)(a.y > x) + (int)(c.x > x) + (int)(c.y > x);
+                }
                 if (x != 0) {
                     atomicAdd(&nz_s, 1);
                     if (rank < P) kept_s[rank] = (int32_t)key_id(x);
@@ -372,8 +381,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const uint64_t x = lk[p * 64 + lane];
             int part = 0;
             for (int q = wv; q < P; q += 4) {
-#pragma unroll 16
-                for (int j = 0; j < 64; ++j) part += (lk[q * 64 + j] > x) ? le_s[q * 64 + j] : 0;
+                const ulonglong2 *l2 = reinterpret_cast<const ulonglong2 *>(lk + q * 64);
+                const int4 *e4 = reinterpret_cast<const int4 *>(le_s + q * 64);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const ulonglong2 a = l2[2 * j], c = l2[2 * j + 1];
+                    const int4 e = e4[j];
+                    part += ((a.x > x) ? e.x : 0) + ((a.y > x) ? e.y : 0) + ((c.x > x) ? e.z : 0) + ((c.y > x) ? e.w : 0);
+                }
             }
             wpart[wv][lane] = (x != 0) ? part : 0;
         }
