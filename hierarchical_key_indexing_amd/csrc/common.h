@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #define LSA_DEV __device__ __forceinline__
+#define LSA_HOST_DEV __host__ __device__
 
 namespace lsa {
 

@@ -59,8 +59,11 @@ struct DecodeArgs {
     uint64_t *lists;      // [L-2][groups][P][64] sorted child keys of internal levels
     uint64_t *leaf_keys;  // [groups][P][64]
     int32_t *leaf_pre;    // [groups][P][64] inclusive prefix of eligible counts
-    float *part;          // [groups][P][G*d + 2*G]
+    float *part;          // [groups][P][part_stride(G, d)]: output, then G maxima, then G sums
 };
+
+// floats per partial state, padded so every state starts 16-byte aligned
+LSA_HOST_DEV inline int part_stride(int G, int d) { return (G * d + 2 * G + 3) & ~3; }
 
 // ---------------------------------------------------------------- helpers
 LSA_DEV uint64_t shfl_xor64(uint64_t v, int m) {
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const int off = clo[c] + (f - toff_s[c]);
             return staged ? mem_s[off - clo[0]] : perm[off];
         };
-        float *pp = A.part + ((size_t)gi * P + p) * (G * d + 2 * G);
+        float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
         if constexpr (kMfma) {
             const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
             const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * DC;
@@ -559,43 +562,43 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __syncthreads();
     if (!last_s) return;
     if constexpr (ATTEND) {
-        const float *pb = A.part + (size_t)gi * P * (G * d + 2 * G);
-        const int stride = G * d + 2 * G;
-        float *wq = dyn;                       // [P][G] weights 2^(m_q - M)
-        float *lq = dyn + kMaxP * 16;          // [P][G] sums
-        float *Ms = lq + kMaxP * 16;           // [G] max, then [G] total
-        for (int e = tid; e < P * G; e += blockDim.x) {
-            const int q = e / G, h = e % G;
-            wq[e] = pb[(size_t)q * stride + G * d + h];
-            lq[e] = pb[(size_t)q * stride + G * d + G + h];
-        }
-        __syncthreads();
-        if (tid < G) {
-            float M = -INFINITY;
-            for (int q = 0; q < P; ++q) M = fmaxf(M, wq[q * G + tid]);
-            float l = 0.0f;
-            for (int q = 0; q < P; ++q) {
-                const float mq = wq[q * G + tid];
-                const float w = (mq > -INFINITY) ? exp2f(mq - M) : 0.0f;
-                wq[q * G + tid] = w;
-                l += lq[q * G + tid] * w;
+        // each thread merges 4 consecutive outputs of one head: every load
+        // (the P partial outputs and each partial's max and sum) is issued
+        // before the first use
+        const int stride = part_stride(G, d);
+        const float *pb = A.part + (size_t)gi * P * stride;
+        for (int c4 = tid; c4 < G * d / 4; c4 += blockDim.x) {
+            const int e = 4 * c4, h = e / d;
+            float4 o[kMaxP];
+            float mq[kMaxP], lq[kMaxP];
+#pragma unroll
+            for (int q = 0; q < kMaxP; ++q) {
+                if (q < P) {
+                    const float *pq = pb + (size_t)q * stride;
+                    o[q] = *reinterpret_cast<const float4 *>(pq + e);
+                    mq[q] = pq[G * d + h];
+                    lq[q] = pq[G * d + G + h];
+                }
             }
-            Ms[tid] = M;
-            Ms[16 + tid] = l;
-        }
-        __syncthreads();
-        for (int e = tid; e < G * d; e += blockDim.x) {
-            const int h = e / d;
-            float t[kMaxP];
+            float M = -INFINITY;
 #pragma unroll
-            for (int q = 0; q < kMaxP; ++q) t[q] = (q < P) ? pb[(size_t)q * stride + e] : 0.0f;
-            float o = 0.0f;
+            for (int q = 0; q < kMaxP; ++q) if (q < P) M = fmaxf(M, mq[q]);
+            float l = 0.0f;
+            float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < kMaxP; ++q) if (q < P) o += t[q] * wq[q * G + h];
-            const float l = Ms[16 + h];
+            for (int q = 0; q < kMaxP; ++q) {
+                if (q < P && mq[q] > -INFINITY) {
+                    const float w = exp2f(mq[q] - M);
+                    l += lq[q] * w;
+                    acc.x += o[q].x * w; acc.y += o[q].y * w; acc.z += o[q].z * w; acc.w += o[q].w * w;
+                }
+            }
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
             const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
-            ((T *)A.out)[oh * d + (e % d)] = from_float<T>(l > 0.0f ? o / l : 0.0f);
-            if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (Ms[h] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+            T *op = (T *)A.out + oh * d + (e % d);
+            op[0] = from_float<T>(acc.x * inv); op[1] = from_float<T>(acc.y * inv);
+            op[2] = from_float<T>(acc.z * inv); op[3] = from_float<T>(acc.w * inv);
+            if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
     }
     if (tid == 0) {
@@ -617,7 +620,7 @@ static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G,
     w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * 64);
     w.leaf_keys = (uint64_t *)take(sizeof(uint64_t) * (size_t)groups * P * 64);
     w.leaf_pre = (int32_t *)take(sizeof(int32_t) * (size_t)groups * P * 64);
-    w.part = (float *)take(sizeof(float) * (size_t)groups * P * ((size_t)G * d + 2 * G));
+    w.part = (float *)take(sizeof(float) * (size_t)groups * P * (size_t)part_stride(G, d));
     w.bytes = cur;
     return w;
 }
