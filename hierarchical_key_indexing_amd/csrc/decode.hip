@@ -363,14 +363,31 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 
     // ---- fill: every workgroup places its own leaves' keys
     {
-        g2s_flat<8>(lk, A.leaf_keys + (size_t)gi * P * 64, P * 64);
-        g2s_flat<8>(lp, A.leaf_pre + (size_t)gi * P * 64, P * 64);
+        {
+            // keys and prefix counts of all P lists in one round of loads
+            const uint64_t *sk = A.leaf_keys + (size_t)gi * P * 64;
+            const int32_t *sp = A.leaf_pre + (size_t)gi * P * 64;
+            constexpr int U = kMaxP * 64 / 256;
+            uint64_t tk[U];
+            int32_t tp[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = tid + 256 * u;
+                if (e < P * 64) { tk[u] = sk[e]; tp[u] = sp[e]; }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = tid + 256 * u;
+                if (e < P * 64) { lk[e] = tk[u]; lp[e] = tp[u]; }
+            }
+        }
         if (tid < 64) take_s[tid] = 0;
         __syncthreads();
-        if (tid == 0) {
-            int tot = 0;
-            for (int q = 0; q < P; ++q) tot += lp[q * 64 + 63];
-            count_s = min(A.k, tot);
+        if (wv == 0) {
+            int tot = (lane < P) ? lp[lane * 64 + 63] : 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+            if (lane == 0) count_s = min(A.k, tot);
         }
         // eligible keys retrieved before each own leaf: wave w sums, over the
         // lists q = w, w + 4, ..., the counts of leaves scored above it
