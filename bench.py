@@ -23,6 +23,34 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SOURCES = ("decode.hip", "mfma_attn.h", "common.h")
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "hierarchical_key_indexing_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(profile, names):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what it
+    reads for a plain copy of known size) from a committed rocprofv3 counter
+    summary; None unless that summary was taken on the current kernel sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", profile)) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if ln.startswith("traffic_record: "):
+            rec = json.loads(ln[len("traffic_record: "):])
+            if rec.get("sources_sha256") == sources_sha256(names):
+                return int(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
 
 
 def log(*a):
@@ -93,6 +121,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--layers-per-graph", type=int, default=8)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy, the reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -108,6 +138,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lsa.lib()
+    if args.calibrate_copy:
+        # 64 Mi floats: 268435456 bytes read and 268435456 bytes written per launch
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     log("generate", w.name)
     K, V = synth.make_kv(w, device=dev)
@@ -216,7 +255,8 @@ def main():
     dbytes = sb + ab
     achieved = dbytes / (step_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "k_decode (lsa_select_attend)",
+                "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": measured_traffic("k_decode_decode_1m.md", DECODE_SOURCES) if w.name == "decode_1m" else None, "kernel": "k_decode (lsa_select_attend)",
                 "kernel_us": round(step_us, 3), "algorithmic_bytes": int(dbytes)}
 
     # the two calls separately (select on the multi-workgroup kernel, then attend)
