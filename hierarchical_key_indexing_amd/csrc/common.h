@@ -13,6 +13,10 @@ namespace lsa {
 
 constexpr int kWave = 64;
 
+// Native 4-float vector: whole-vector loads and stores keep arrays of these in
+// registers (HIP's float4 struct, copied whole, can push an array to scratch).
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------- element types
 struct bf16_t {
     uint16_t bits;
@@ -61,15 +65,72 @@ LSA_DEV uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-template <typename T>
-LSA_DEV T wave_incl_scan_add(T v) {
-    int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        T t = __shfl_up(v, o, kWave);
-        if (l >= o) v += t;
+// Value of lane (l ^ M) for every lane l, without a trip through LDS: DPP quad
+// permutes for M = 1, 2; DPP row shifts (both directions, then a per-lane
+// select) for M = 4, 8; the gfx950 row-swap instructions for M = 16, 32.
+template <int M>
+LSA_DEV uint32_t xor_lane(uint32_t x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4 || M == 8) {
+        const uint32_t from_below = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + M, 0xF, 0xF, false);  // row_shr
+        const uint32_t from_above = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + M, 0xF, 0xF, false);  // row_shl
+        return (lane_id() & M) ? from_below : from_above;
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane_id() & 16) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane_id() & 32) ? r[0] : r[1];
     }
+}
+template <int M>
+LSA_DEV uint64_t xor_lane64(uint64_t v) {
+    return ((uint64_t)xor_lane<M>((uint32_t)(v >> 32)) << 32) | xor_lane<M>((uint32_t)v);
+}
+template <int M>
+LSA_DEV float xor_lane_f(float v) { return __uint_as_float(xor_lane<M>(__float_as_uint(v))); }
+template <int M>
+LSA_DEV int xor_lane_i(int v) { return (int)xor_lane<M>((uint32_t)v); }
+
+LSA_DEV float wave_max_f(float v) {
+    v = fmaxf(v, xor_lane_f<32>(v)); v = fmaxf(v, xor_lane_f<16>(v)); v = fmaxf(v, xor_lane_f<8>(v));
+    v = fmaxf(v, xor_lane_f<4>(v)); v = fmaxf(v, xor_lane_f<2>(v)); v = fmaxf(v, xor_lane_f<1>(v));
     return v;
+}
+LSA_DEV float wave_sum_f(float v) {
+    v += xor_lane_f<32>(v); v += xor_lane_f<16>(v); v += xor_lane_f<8>(v);
+    v += xor_lane_f<4>(v); v += xor_lane_f<2>(v); v += xor_lane_f<1>(v);
+    return v;
+}
+LSA_DEV int wave_sum_i(int v) {
+    v += xor_lane_i<32>(v); v += xor_lane_i<16>(v); v += xor_lane_i<8>(v);
+    v += xor_lane_i<4>(v); v += xor_lane_i<2>(v); v += xor_lane_i<1>(v);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes: scans of the four 16-lane rows with
+// DPP row shifts (a lane with no source adds 0), then each row adds the
+// totals of the rows below it, read from lanes 15, 31 and 47.
+LSA_DEV int wave_incl_scan_add(int v) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        int t;
+        switch (o) {
+            case 1: t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false); break;
+            case 2: t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false); break;
+            case 4: t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false); break;
+            default: t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false); break;
+        }
+        v += t;
+    }
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane_id() >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Exclusive prefix sum over a block; returns the thread's exclusive prefix and
@@ -112,27 +173,27 @@ LSA_DEV void block_bitonic_sort(K *keys, int N) {
 }
 
 // Copy n floats (n % 4 == 0, src 16-byte aligned) from global memory into LDS
-// rows of `cols` floats (cols % 4 == 0) with row stride `ld`.  Every thread
+// rows of `cols` floats (cols % 4 == 0) with row stride `ld` (ld % 4 == 0, dst
+// 16-byte aligned).  Every thread
 // issues up to U 16-byte loads before it stores any of them, so one copy costs
 // about one memory round trip per U * blockDim float4s.
 template <int U>
 LSA_DEV void g2s_rows(float *dst, int ld, const float *__restrict__ src, int n, int cols) {
-    const float4 *s4 = reinterpret_cast<const float4 *>(src);
+    const f4_t *s4 = reinterpret_cast<const f4_t *>(src);
     const int n4 = n >> 2;
     for (int base = 0; base < n4; base += U * (int)blockDim.x) {
-        float4 t[U];
+        f4_t t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
-            if (e < n4) t[u] = s4[e];
+            t[u] = s4[min(e, n4 - 1)];        // clamped: every load stays in bounds
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
             if (e < n4) {
                 const int f = e * 4, row = f / cols, col = f % cols;
-                float *q = dst + row * ld + col;
-                q[0] = t[u].x; q[1] = t[u].y; q[2] = t[u].z; q[3] = t[u].w;
+                *reinterpret_cast<f4_t *>(dst + row * ld + col) = t[u];
             }
         }
     }

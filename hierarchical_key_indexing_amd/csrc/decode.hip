@@ -66,42 +66,27 @@ struct DecodeArgs {
 LSA_HOST_DEV inline int part_stride(int G, int d) { return (G * d + 2 * G + 3) & ~3; }
 
 // ---------------------------------------------------------------- helpers
-LSA_DEV uint64_t shfl_xor64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor((unsigned int)(v & 0xffffffffu), m, kWave);
-    const uint32_t hi = __shfl_xor((unsigned int)(v >> 32), m, kWave);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // Bitonic sort of one 64-bit key (plus payload) per lane, descending by lane.
-LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) {
-    const int l = lane_id();
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint64_t ok = shfl_xor64(key, stride);
-            const int op = __shfl_xor(pay, stride, kWave);
-            // lower lane of a descending segment (or upper lane of an
-            // ascending one) keeps the larger key; branch-free select
-            const unsigned want_gt = ((l & stride) == 0) == ((l & size) == 0);
-            const unsigned gt = ok > key, lt = ok < key;
-            const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
-            key = take ? ok : key;
-            pay = take ? op : pay;
-        }
-    }
+// Every compare-exchange reads the partner lane through DPP / row swaps.
+template <int SIZE, int STRIDE>
+LSA_DEV void sort_stage(uint64_t &key, int &pay, int l) {
+    const uint64_t ok = xor_lane64<STRIDE>(key);
+    const int op = xor_lane_i<STRIDE>(pay);
+    // lower lane of a descending segment (or upper lane of an ascending one)
+    // keeps the larger key; branch-free select
+    const unsigned want_gt = ((l & STRIDE) == 0) == ((l & SIZE) == 0);
+    const unsigned gt = ok > key, lt = ok < key;
+    const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
+    key = take ? ok : key;
+    pay = take ? op : pay;
 }
-
-LSA_DEV float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+template <int SIZE, int STRIDE>
+LSA_DEV void sort_stages(uint64_t &key, int &pay, int l) {
+    sort_stage<SIZE, STRIDE>(key, pay, l);
+    if constexpr (STRIDE > 1) sort_stages<SIZE, STRIDE / 2>(key, pay, l);
+    else if constexpr (SIZE < kWave) sort_stages<SIZE * 2, SIZE>(key, pay, l);
 }
-LSA_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
+LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_stages<2, 1>(key, pay, lane_id()); }
 
 LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     int lo = 0, hi = len;
@@ -115,9 +100,18 @@ LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
 template <int RC>
 LSA_DEV float score_lds(const float *u, const float *row, int r) {
     double s = 0.0;
-    if constexpr (RC > 0) {
+    if constexpr (RC > 0 && RC % 4 == 0) {
+        // 16-byte LDS reads (u is a broadcast); products summed in dimension order
+        const f4_t *u4 = reinterpret_cast<const f4_t *>(u);
+        const f4_t *r4 = reinterpret_cast<const f4_t *>(row);
 #pragma unroll
-        for (int x = 0; x < RC; ++x) s = fma((double)u[x], (double)row[x], s);
+        for (int x = 0; x < RC / 4; ++x) {
+            const f4_t a = u4[x], c = r4[x];
+            s = fma((double)a.x, (double)c.x, s);
+            s = fma((double)a.y, (double)c.y, s);
+            s = fma((double)a.z, (double)c.z, s);
+            s = fma((double)a.w, (double)c.w, s);
+        }
     } else {
         for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
     }
@@ -142,10 +136,14 @@ LSA_DEV void g2s_flat(E *dst, const E *__restrict__ src, int n) {
     }
 }
 
-// b rows of r floats (one node's children) into LDS rows of stride 65.
+// LDS row stride of staged centroid rows: a multiple of 4 (16-byte row reads)
+// whose eight consecutive rows start in eight different 4-bank groups.
+constexpr int kCS = 68;
+
+// b rows of r floats (one node's children) into LDS rows of stride kCS.
 LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
-    if ((r & 3) == 0) g2s_rows<4>(Cs, 65, src, b * r, r);
-    else g2s_scalar<16, float, float>(Cs, 65, src, b * r, r);
+    if ((r & 3) == 0) g2s_rows<4>(Cs, kCS, src, b * r, r);
+    else g2s_scalar<16, float, float>(Cs, kCS, src, b * r, r);
 }
 
 // All workgroups of a group wait here until `target` arrivals are counted.
@@ -172,8 +170,8 @@ template <typename T, bool ATTEND, int RC, int DC>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     __shared__ float qbar_s[256];
-    __shared__ float u_s[64];
-    __shared__ float Cs[64 * 65];
+    __shared__ __attribute__((aligned(16))) float u_s[64];
+    __shared__ __attribute__((aligned(16))) float Cs[64 * kCS];
     __shared__ int32_t ccnt[64];
     __shared__ int32_t clo[65];
     __shared__ int32_t kept_s[kMaxP];
@@ -218,13 +216,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         const float *Wg = A.W + (size_t)g * d * r;
         if constexpr (RC == 64 && DC == 128 && sizeof(T) == 2) {
             // one round of loads: 4 float4 of rows, 8 float4 of W, 1 uint4 of Q per thread
-            const float4 *c4 = reinterpret_cast<const float4 *>(C1);
-            const float4 *w4 = reinterpret_cast<const float4 *>(Wg);
+            const f4_t *c4 = reinterpret_cast<const f4_t *>(C1);
+            const f4_t *w4 = reinterpret_cast<const f4_t *>(Wg);
             const uint4 *q4 = reinterpret_cast<const uint4 *>(Q + ((size_t)i * A.h_q + (size_t)g * G) * DC);
-            float4 cr[4], wr[8];
+            f4_t cr[4], wr[8];
             uint4 qr = {0, 0, 0, 0};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) { const int e = tid + 256 * u; if (e < b * 16) cr[u] = c4[e]; }
+            for (int u = 0; u < 4; ++u) cr[u] = c4[min(tid + 256 * u, b * 16 - 1)];   // clamped: loads stay in bounds
 #pragma unroll
             for (int u = 0; u < 8; ++u) wr[u] = w4[tid + 256 * u];
             if (tid < G * 16) qr = q4[tid];
@@ -232,12 +230,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int u = 0; u < 4; ++u) {
                 const int e = tid + 256 * u;
                 if (e < b * 16) {
-                    float *q = Cs + (e / 16) * 65 + (e % 16) * 4;
-                    q[0] = cr[u].x; q[1] = cr[u].y; q[2] = cr[u].z; q[3] = cr[u].w;
+                    *reinterpret_cast<f4_t *>(Cs + (e / 16) * kCS + (e % 16) * 4) = cr[u];
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) reinterpret_cast<float4 *>(Wl)[tid + 256 * u] = wr[u];
+            for (int u = 0; u < 8; ++u) reinterpret_cast<f4_t *>(Wl)[tid + 256 * u] = wr[u];
             if (tid < G * 16) {
                 const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
 #pragma unroll
@@ -276,7 +273,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     if (wv == 0) {
         uint64_t key = 0;
         int pay = 0;
-        if (lane < b && ccnt[lane] > 0) key = make_key(score_lds<RC>(u_s, Cs + lane * 65, r), (uint32_t)lane);
+        if (lane < b && ccnt[lane] > 0) key = make_key(score_lds<RC>(u_s, Cs + lane * kCS, r), (uint32_t)lane);
         const int nz = __popcll(__ballot(key != 0));
         wave_sort_desc(key, pay);
         const int keep = min(P, nz);
@@ -309,7 +306,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             uint64_t key = 0;
             int e = 0;
             if (v >= 0 && lane < b && ccnt[lane] > 0) {
-                key = make_key(score_lds<RC>(u_s, Cs + lane * 65, r), (uint32_t)(v * b + lane));
+                key = make_key(score_lds<RC>(u_s, Cs + lane * kCS, r), (uint32_t)(v * b + lane));
                 if (leaf) {
                     const int a0 = clo[lane], a1 = clo[lane + 1];
                     if (all_eligible) e = a1 - a0;
@@ -385,8 +382,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         __syncthreads();
         if (wv == 0) {
             int tot = (lane < P) ? lp[lane * 64 + 63] : 0;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+            tot = wave_sum_i(tot);
             if (lane == 0) count_s = min(A.k, tot);
         }
         // eligible keys retrieved before each own leaf: wave w sums, over the
@@ -530,11 +526,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 __syncthreads();
                 for (int h = wv; h < G; h += blockDim.x / kWave) {
                     const float x = S[h * kTKD + lane];
-                    const float mt = wave_max(x);
+                    const float mt = wave_max_f(x);
                     const float mnew = fmaxf(m_run[h], mt);
                     const float pr = (lane < nk) ? exp2f(x - mnew) : 0.0f;
                     S[h * kTKD + lane] = pr;
-                    const float ls = wave_sum(pr);
+                    const float ls = wave_sum_f(pr);
                     if (lane == 0) {
                         const float al = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mnew);
                         alpha_s[h] = al;

@@ -106,8 +106,8 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
             sv[4 * mb + j] = x;
             mt = fmaxf(mt, x);
         }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = fmaxf(mt, xor_lane_f<16>(mt));
+    mt = fmaxf(mt, xor_lane_f<32>(mt));
     const float m_new = fmaxf(st.m, mt);
     alpha = (st.m == -INFINITY) ? 0.0f : exp2f(st.m - m_new);
     float ls = 0.0f;
@@ -117,8 +117,8 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
         ls += pr;
         pf[s] = __builtin_bit_cast(__bf16, bf16_bits_rne(pr));
     }
-    ls += __shfl_xor(ls, 16, kWave);
-    ls += __shfl_xor(ls, 32, kWave);
+    ls += xor_lane_f<16>(ls);
+    ls += xor_lane_f<32>(ls);
     st.l = st.l * alpha + ls;
     st.m = m_new;
 }
