@@ -2,7 +2,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/lsa.h"
+#include "lsa.h"
 #include "internal.h"
 
 namespace {

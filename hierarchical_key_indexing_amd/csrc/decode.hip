@@ -146,22 +146,19 @@ LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
     else g2s_scalar<16, float, float>(Cs, kCS, src, b * r, r);
 }
 
-// All workgroups of a group wait here until `target` arrivals are counted.
-// The spin uses relaxed device-scope loads; one acquire fence follows it.
+// All workgroups of a group wait here until `target` arrivals are counted:
+// a release increment, then acquire polls (bounded; a timeout sets `flag`).
 LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
     __syncthreads();
     if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         int spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
+        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
             if (++spins > kSpinLimit) {
                 __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
 }
@@ -671,6 +668,8 @@ bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, in
     if (L < 2 || b > 64 || r > 64 || beam > kMaxP || beam < 1 || G > 16 || d > 256 || d % 8 != 0) return false;
     if (decode_dyn_bytes(0, G, d, r) + kStaticLds > kLdsPerCu) return false;
     (void)k;
+    // every workgroup of a group must be resident at once (one per compute
+    // unit at this kernel's LDS size)
     const int cus = device_cus();
     return cus > 0 && m * h_kv * beam <= cus;
 }
