@@ -97,6 +97,27 @@ LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     return lo;
 }
 
+// For key x and the descending key lists a + q * stride (q = q0, q0 + dq, ...
+// below nq; len <= LEN entries each): c[i] = number of leading entries of list
+// q0 + i * dq greater than x.  Binary lifting, all lists side by side, so the
+// dependent LDS reads take log2(LEN) + 1 rounds.
+template <int NQ, int LEN>
+LSA_DEV void count_gt_lists(const uint64_t *a, int stride, int q0, int dq, int nq, int len, uint64_t x, int (&c)[NQ]) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) c[i] = 0;
+#pragma unroll
+    for (int s = LEN; s >= 1; s >>= 1) {
+        // branch-free step, all reads issued before the first compare (lists
+        // q >= nq are read but not counted; the caller's array holds
+        // q0 + (NQ - 1) * dq + 1 lists of stride entries)
+        uint64_t v[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) v[i] = a[(q0 + i * dq) * stride + min(c[i] + s, len) - 1];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) c[i] += (q0 + i * dq < nq && c[i] + s <= len && v[i] > x) ? s : 0;
+    }
+}
+
 template <int RC>
 LSA_DEV float score_lds(const float *u, const float *row, int r) {
     double s = 0.0;
@@ -163,7 +184,7 @@ LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
     __syncthreads();
 }
 
-template <typename T, bool ATTEND, int RC, int DC>
+template <typename T, bool ATTEND, int RC, int DC, int PC>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     __shared__ float qbar_s[256];
@@ -175,16 +196,15 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ __attribute__((aligned(16))) uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
     __shared__ int32_t take_s[64], toff_s[65], wpart[4][64];
-    __shared__ __attribute__((aligned(16))) int32_t le_s[kMaxP * 64];
     __shared__ int32_t mem_s[kMemCap];
-    __shared__ int keep_s, count_s, last_s, nz_s;
+    __shared__ int keep_s, count_s, last_s;
     __shared__ int32_t ids_w[4][kMT];
     __shared__ float m_run[16], l_run[16], alpha_s[16];
 
     constexpr bool kMfma = ATTEND && sizeof(T) == 2 && DC > 0 && DC % 32 == 0;
     const int r = RC > 0 ? RC : A.r;
     const int d = DC > 0 ? DC : A.d;
-    const int P = A.beam;
+    const int P = PC > 0 ? PC : A.beam;      // workgroups per group (= beam)
     const int p = blockIdx.x;
     const int gi = blockIdx.y;
     const int64_t i = gi / A.h_kv;
@@ -326,31 +346,29 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         group_barrier(ctrl, barriers * P, ctrl + 2);
         if (!leaf) {
             // candidates: the first P entries of every list (the global top P
-            // lie among them); a candidate's rank is the number of candidates
-            // above it, counted with broadcast LDS reads
+            // lie among them); a candidate's rank is its position in its own
+            // list plus, for every other list, the number of entries above it
             const uint64_t *src = A.lists + ((size_t)(l - 2) * groups + gi) * P * 64;
             const int nc = P * P;
             for (int e = tid; e < nc; e += blockDim.x) lk[e] = src[(e / P) * 64 + (e % P)];
-            if (tid == 0) nz_s = 0;
             __syncthreads();
-            for (int e = nc + tid; e < ((nc + 3) & ~3); e += blockDim.x) lk[e] = 0ull;
-            __syncthreads();
+            int nonzero = 0;
             for (int e = tid; e < nc; e += blockDim.x) {
                 const uint64_t x = lk[e];
-                int rank = 0;
-                const ulonglong2 *l2 = reinterpret_cast<const ulonglong2 *>(lk);
-#pragma unroll 8
-                for (int y = 0; y < (nc + 3) / 4; ++y) {
-                    const ulonglong2 a = l2[2 * y], c = l2[2 * y + 1];
-                    rank += (int)(a.x > x) + (int)(a.y > x) + (int)(c.x > x) + (int)(c.y > x);
-                }
                 if (x != 0) {
-                    atomicAdd(&nz_s, 1);
+                    const int q = e / P;
+                    constexpr int NQ = PC > 0 ? PC : kMaxP;
+                    int c[NQ];
+                    count_gt_lists<NQ, NQ>(lk, P, 0, 1, P, P, x, c);
+                    int rank = e % P;
+#pragma unroll
+                    for (int q2 = 0; q2 < NQ; ++q2) rank += (q2 < P && q2 != q) ? c[q2] : 0;
                     if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                    ++nonzero;
                 }
             }
-            __syncthreads();
-            if (tid == 0) keep_s = min(P, nz_s);
+            const int nz = __syncthreads_count(nonzero);
+            if (tid == 0) keep_s = min(P, nz);
             __syncthreads();
         }
     }
@@ -383,27 +401,23 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (lane == 0) count_s = min(A.k, tot);
         }
         // eligible keys retrieved before each own leaf: wave w sums, over the
-        // lists q = w, w + 4, ..., the counts of leaves scored above it
-        // (broadcast LDS reads; the own list gives the keys before it)
-        for (int e = tid; e < P * 64; e += blockDim.x) {
-            const int j = e % 64;
-            le_s[e] = lp[e] - (j > 0 ? lp[e - 1] : 0);
-        }
-        __syncthreads();
+        // lists q = w, w + 4, ..., the eligible counts of the leaves above it
+        // (a binary search in list q, then its inclusive prefix); the own list
+        // gives the keys before it
         {
             const uint64_t x = lk[p * 64 + lane];
             int part = 0;
-            for (int q = wv; q < P; q += 4) {
-                const ulonglong2 *l2 = reinterpret_cast<const ulonglong2 *>(lk + q * 64);
-                const int4 *e4 = reinterpret_cast<const int4 *>(le_s + q * 64);
+            if (x != 0) {
+                constexpr int NQ = (PC > 0 ? PC : kMaxP) / 4;
+                int c[NQ];
+                count_gt_lists<NQ, 64>(lk, 64, wv, 4, P, 64, x, c);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const ulonglong2 a = l2[2 * j], c = l2[2 * j + 1];
-                    const int4 e = e4[j];
-                    part += ((a.x > x) ? e.x : 0) + ((a.y > x) ? e.y : 0) + ((c.x > x) ? e.z : 0) + ((c.y > x) ? e.w : 0);
+                for (int i = 0; i < NQ; ++i) {
+                    const int q = wv + 4 * i;
+                    part += (q < P && c[i] > 0) ? lp[q * 64 + c[i] - 1] : 0;
                 }
             }
-            wpart[wv][lane] = (x != 0) ? part : 0;
+            wpart[wv][lane] = part;
         }
         __syncthreads();
         const int count = count_s;
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         if (wv == 0 && v >= 0) {
             const uint64_t x = lk[p * 64 + lane];
             if (x != 0) {
-                const int e = le_s[p * 64 + lane];
+                const int e = lp[p * 64 + lane] - (lane > 0 ? lp[p * 64 + lane - 1] : 0);
                 const int wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
                 const int take = max(0, min(e, count - wex));
                 const int c = (int)(key_id(x) - (uint32_t)(v * b));
@@ -678,18 +692,18 @@ int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int b
     return (int64_t)carve_decode_ws(nullptr, m * h_kv, beam, L, h_q / h_kv, d).bytes;
 }
 
-template <typename T, bool ATT, int RC, int DC>
+template <typename T, bool ATT, int RC, int DC, int PC>
 static hipError_t launch_decode(const DecodeArgs &A, dim3 grid, size_t shm, hipStream_t st) {
     static int attr_set[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!attr_set[dev]) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_decode<T, ATT, RC, DC>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_decode<T, ATT, RC, DC, PC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsPerCu - kStaticLds));
         if (e != hipSuccess) return e;
         attr_set[dev] = 1;
     }
-    hipLaunchKernelGGL((k_decode<T, ATT, RC, DC>), grid, dim3(256), shm, st, A);
+    hipLaunchKernelGGL((k_decode<T, ATT, RC, DC, PC>), grid, dim3(256), shm, st, A);
     return hipGetLastError();
 }
 
@@ -710,15 +724,19 @@ hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_
     A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.part = w.part;
     const size_t shm = decode_dyn_bytes(dtype, G, d, r);
     const dim3 grid((unsigned)beam, (unsigned)(m * h_kv));
+    if (fast_shape(dtype, d, r) && beam == 16) {
+        return attend ? launch_decode<bf16_t, true, 64, 128, 16>(A, grid, shm, st)
+                      : launch_decode<bf16_t, false, 64, 128, 16>(A, grid, shm, st);
+    }
     if (fast_shape(dtype, d, r)) {
-        return attend ? launch_decode<bf16_t, true, 64, 128>(A, grid, shm, st)
-                      : launch_decode<bf16_t, false, 64, 128>(A, grid, shm, st);
+        return attend ? launch_decode<bf16_t, true, 64, 128, 0>(A, grid, shm, st)
+                      : launch_decode<bf16_t, false, 64, 128, 0>(A, grid, shm, st);
     }
     if (dtype == 0)
-        return attend ? launch_decode<float, true, 0, 0>(A, grid, shm, st)
-                      : launch_decode<float, false, 0, 0>(A, grid, shm, st);
-    return attend ? launch_decode<bf16_t, true, 0, 0>(A, grid, shm, st)
-                  : launch_decode<bf16_t, false, 0, 0>(A, grid, shm, st);
+        return attend ? launch_decode<float, true, 0, 0, 0>(A, grid, shm, st)
+                      : launch_decode<float, false, 0, 0, 0>(A, grid, shm, st);
+    return attend ? launch_decode<bf16_t, true, 0, 0, 0>(A, grid, shm, st)
+                  : launch_decode<bf16_t, false, 0, 0, 0>(A, grid, shm, st);
 }
 
 }  // namespace lsa
