@@ -346,28 +346,43 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         group_barrier(ctrl, barriers * P, ctrl + 2);
         if (!leaf) {
             // candidates: the first P entries of every list (the global top P
-            // lie among them); a candidate's rank is its position in its own
-            // list plus, for every other list, the number of entries above it
+            // lie among them).  Two merge rounds: the top P of each quartet of
+            // lists, placed at their ranks within the quartet, then the top P
+            // of those merged lists.  A rank is the number of entries above
+            // the key in every list of its round (its own list gives its
+            // position), found by side-by-side binary searches.
+            constexpr int LQ = PC > 0 ? PC : kMaxP;          // list length bound
             const uint64_t *src = A.lists + ((size_t)(l - 2) * groups + gi) * P * 64;
             const int nc = P * P;
+            const int nm = (P + 3) / 4;                       // merged lists
+            uint64_t *m1 = lk + kMaxP * kMaxP;                // [nm][P]
             for (int e = tid; e < nc; e += blockDim.x) lk[e] = src[(e / P) * 64 + (e % P)];
+            for (int e = tid; e < nm * P; e += blockDim.x) m1[e] = 0ull;
             __syncthreads();
             int nonzero = 0;
             for (int e = tid; e < nc; e += blockDim.x) {
                 const uint64_t x = lk[e];
                 if (x != 0) {
-                    const int q = e / P;
-                    constexpr int NQ = PC > 0 ? PC : kMaxP;
-                    int c[NQ];
-                    count_gt_lists<NQ, NQ>(lk, P, 0, 1, P, P, x, c);
-                    int rank = e % P;
-#pragma unroll
-                    for (int q2 = 0; q2 < NQ; ++q2) rank += (q2 < P && q2 != q) ? c[q2] : 0;
-                    if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                    const int quad = (e / P) / 4;
+                    int c[4];
+                    count_gt_lists<4, LQ>(lk, P, 4 * quad, 1, P, P, x, c);
+                    const int rank = c[0] + c[1] + c[2] + c[3];
+                    if (rank < P) m1[quad * P + rank] = x;
                     ++nonzero;
                 }
             }
             const int nz = __syncthreads_count(nonzero);
+            for (int e = tid; e < nm * P; e += blockDim.x) {
+                const uint64_t x = m1[e];
+                if (x != 0) {
+                    int c[LQ / 4];
+                    count_gt_lists<LQ / 4, LQ>(m1, P, 0, 1, nm, P, x, c);
+                    int rank = 0;
+#pragma unroll
+                    for (int q = 0; q < LQ / 4; ++q) rank += c[q];
+                    if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                }
+            }
             if (tid == 0) keep_s = min(P, nz);
             __syncthreads();
         }
