@@ -60,6 +60,15 @@ LSA_DEV float key_score(uint64_t key) { return unorderable((uint32_t)(key >> 32)
 // ---------------------------------------------------------------- wave helpers
 LSA_DEV int lane_id() { return __lane_id(); }
 
+// Orders one wave's LDS accesses across this point (for LDS regions only this
+// wave reads and writes): the lanes of a wave run in lockstep and the LDS
+// serves one wave's operations in issue order, so no workgroup barrier is needed.
+LSA_DEV void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 LSA_DEV uint64_t lanemask_lt() {
     int l = lane_id();
     return l == 0 ? 0ull : (~0ull >> (64 - l));

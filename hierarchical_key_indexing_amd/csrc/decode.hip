@@ -32,6 +32,7 @@ namespace lsa {
 
 constexpr int kMaxP = 32;          // beam limit of this path
 constexpr int kMemCap = 2048;      // node members staged in LDS
+constexpr int kOwnCap = 2048;      // own (selected) keys listed in LDS
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kTKD = 64;           // keys per tile of the vector attention path
 
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t kept_s[kMaxP];
     __shared__ __attribute__((aligned(16))) uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
-    __shared__ int32_t take_s[64], toff_s[65], wpart[4][64];
+    __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64];
+    __shared__ int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s;
     __shared__ int32_t ids_w[4][kMT];
@@ -408,7 +410,6 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 if (e < P * 64) { lk[e] = tk[u]; lp[e] = tp[u]; }
             }
         }
-        if (tid < 64) take_s[tid] = 0;
         __syncthreads();
         if (wv == 0) {
             int tot = (lane < P) ? lp[lane * 64 + 63] : 0;
@@ -437,24 +438,41 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         __syncthreads();
         const int count = count_s;
         int32_t *out = A.sel + (size_t)gi * A.k;
-        if (wv == 0 && v >= 0) {
-            const uint64_t x = lk[p * 64 + lane];
+        if (wv == 0) {
+            // lane j: the j-th own leaf in score order; its first `take` members
+            // go to sel from its retrieval offset wex and to own_s (this
+            // workgroup's keys, in lane order) from its offset toff
+            const uint64_t x = (v >= 0) ? lk[p * 64 + lane] : 0ull;
+            int take = 0, wex = 0, e = 0, a0 = 0;
             if (x != 0) {
-                const int e = lp[p * 64 + lane] - (lane > 0 ? lp[p * 64 + lane - 1] : 0);
-                const int wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
-                const int take = max(0, min(e, count - wex));
-                const int c = (int)(key_id(x) - (uint32_t)(v * b));
-                take_s[c] = take;
-                if (take > 0) {
-                    const int a0 = clo[c];
-                    if (clo[b] - clo[0] <= kMemCap)
-                        for (int t = 0; t < take; ++t) out[wex + t] = mem_s[a0 - clo[0] + t];
-                    else
-                        for (int t = 0; t < take; ++t) out[wex + t] = perm[a0 + t];
-                }
-                if (count == A.k && wex < A.k && wex + e >= A.k && A.sel_cutoff)
-                    A.sel_cutoff[gi] = key_score(x);
+                e = lp[p * 64 + lane] - (lane > 0 ? lp[p * 64 + lane - 1] : 0);
+                wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
+                take = max(0, min(e, count - wex));
+                a0 = clo[(int)(key_id(x) - (uint32_t)(v * b))];
             }
+            const int incl = wave_incl_scan_add(take);
+            toff_s[lane] = incl - take;
+            a0_s[lane] = a0;
+            wex_s[lane] = wex;
+            if (lane == 63) toff_s[64] = incl;
+            if (x != 0 && count == A.k && wex < A.k && wex + e >= A.k && A.sel_cutoff)
+                A.sel_cutoff[gi] = key_score(x);
+        }
+        __syncthreads();
+        // own key f (all threads): its lane j is the last with toff_s[j] <= f
+        const int own = toff_s[64];
+        const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
+        auto own_lane = [&](int f) -> int {
+            int j = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) j += (j + step < 64 && toff_s[j + step] <= f) ? step : 0;
+            return j;
+        };
+        for (int f = tid; f < own; f += blockDim.x) {
+            const int j = own_lane(f), t = f - toff_s[j];
+            const int32_t id = staged ? mem_s[a0_s[j] - clo[0] + t] : perm[a0_s[j] + t];
+            out[wex_s[j] + t] = id;
+            if (ATTEND && own <= kOwnCap) own_s[f] = id;
         }
         for (int t = count + p * blockDim.x + tid; t < A.k; t += P * blockDim.x) out[t] = -1;
         if (p == 0 && tid == 0) {
@@ -466,21 +484,19 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 
     if constexpr (ATTEND) {
         // ---- attention over this workgroup's own keys
-        if (wv == 0) {
-            const int tk = take_s[lane];
-            const int incl = wave_incl_scan_add(tk);
-            toff_s[lane] = incl - tk;
-            if (lane == 63) toff_s[64] = incl;
-        }
+        const int own = toff_s[64];
+        const bool own_fits = own <= kOwnCap;
+        // own_s is padded with key 0 to whole 4 x 32-key steps
+        if (own_fits)
+            for (int f = own + tid; f < ((own + 4 * kMT - 1) / (4 * kMT)) * 4 * kMT; f += blockDim.x) own_s[f] = 0;
         __syncthreads();
-        const int own = (v >= 0) ? toff_s[64] : 0;
-        // key id of own key f: its leaf is the last c with toff_s[c] <= f
+        // key id of own key f without own_s
         const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
         auto own_id = [&](int f) -> int32_t {
-            int c = 0;
+            int j = 0;
 #pragma unroll
-            for (int step = 32; step >= 1; step >>= 1) c += (toff_s[c + step] <= f) ? step : 0;
-            const int off = clo[c] + (f - toff_s[c]);
+            for (int step = 32; step >= 1; step >>= 1) j += (j + step < 64 && toff_s[j + step] <= f) ? step : 0;
+            const int off = a0_s[j] + (f - toff_s[j]);
             return staged ? mem_s[off - clo[0]] : perm[off];
         };
         float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
@@ -497,12 +513,16 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int t = 0; t < nsteps; ++t) {
                 const int fb = (4 * t + wv) * kMT;
                 const int nk = max(0, min(kMT, own - fb));
-                if (lane < kMT) ids_w[wv][lane] = (lane < nk) ? own_id(fb + lane) : 0;
-                __syncthreads();
+                const int32_t *ids = own_s + fb;
+                if (!own_fits) {
+                    if (lane < kMT) ids_w[wv][lane] = (lane < nk) ? own_id(fb + lane) : 0;
+                    wave_sync();
+                    ids = ids_w[wv];
+                }
                 bf16x8_t pf;
                 float alpha;
-                wave_attn_part1<DC>(Kg, Vg, ids_w[wv], nk, qf, A.scale_log2, vt, st, pf, alpha);
-                __syncthreads();
+                wave_attn_part1<DC>(Kg, Vg, ids, nk, qf, A.scale_log2, vt, st, pf, alpha);
+                wave_sync();
                 wave_attn_part2<DC>(vt, pf, alpha, st);
             }
             __syncthreads();

@@ -10,7 +10,9 @@
 // accumulated transposed, O^T[dim][head] += V^T P^T, with the 32 keys of the
 // contraction placed in the order each lane already holds its probabilities
 // (slot s < 4: key 4*(l/16) + s, slot s >= 4: key 16 + 4*(l/16) + s - 4), so the
-// B fragment is the lane's own P values; V^T is staged per wave in LDS.
+// B fragment is the lane's own P values; V^T is staged per wave in LDS: a lane
+// loads one 8-dim chunk of 8 keys' V rows, transposes the 8 x 8 block in
+// registers and writes it as eight 16-byte rows of V^T.
 #pragma once
 
 #include "common.h"
@@ -21,7 +23,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 32;        // keys per wave step
-constexpr int kVTS = kMT + 4;  // V^T row stride in LDS (bf16 elements)
+constexpr int kVTS = kMT + 8;  // V^T row stride in LDS (bf16 elements; 16-byte aligned rows)
 
 LSA_DEV uint16_t bf16_bits_rne(float x) {
     uint32_t u = __float_as_uint(x);
@@ -61,7 +63,7 @@ template <int D>
 LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__restrict__ Vg, const int32_t *ids,
                              int nk, const bf16x8_t (&qf)[D / 32], float scale_log2, uint16_t *vt, WaveAttn<D> &st,
                              bf16x8_t &pf, float &alpha) {
-    constexpr int KS = D / 32, VCH = D / 16;
+    constexpr int KS = D / 32;
     const int l = lane_id(), q = l / 16, c16 = l % 16;
     bf16x8_t kf[2][KS];
 #pragma unroll
@@ -70,21 +72,40 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = *reinterpret_cast<const bf16x8_t *>(Kg + base + 32 * ks);
     }
-    const int kap = l % kMT;
-    uint4 vch[VCH];
-    {
-        const size_t vb = (size_t)ids[kap] * D;
+    // V: unit un = (key block kb = un % 4: keys 8 kb..8 kb + 7, chunk cg = un / 4:
+    // dims 8 cg..8 cg + 7), D / 2 units over the 64 lanes
+    constexpr int NU = D / 2, UPL = (NU + kWave - 1) / kWave;
+    uint4 vv[UPL][8];
 #pragma unroll
-        for (int u = 0; u < VCH; ++u) vch[u] = *reinterpret_cast<const uint4 *>(Vg + vb + 8 * (l / kMT + 2 * u));
+    for (int t = 0; t < UPL; ++t) {
+        const int un = l + kWave * t;
+        if (un < NU) {
+            const int kb = un % 4, cg = un / 4;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                vv[t][j] = *reinterpret_cast<const uint4 *>(Vg + (size_t)ids[8 * kb + j] * D + 8 * cg);
+        }
     }
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-        const int c = l / kMT + 2 * u;
-        const uint32_t w4[4] = {vch[u].x, vch[u].y, vch[u].z, vch[u].w};
+    for (int t = 0; t < UPL; ++t) {
+        const int un = l + kWave * t;
+        if (un < NU) {
+            const int kb = un % 4, cg = un / 4;
+            uint32_t w[8][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            vt[(8 * c + 2 * j) * kVTS + kap] = (uint16_t)(w4[j] & 0xffffu);
-            vt[(8 * c + 2 * j + 1) * kVTS + kap] = (uint16_t)(w4[j] >> 16);
+            for (int j = 0; j < 8; ++j) { w[j][0] = vv[t][j].x; w[j][1] = vv[t][j].y; w[j][2] = vv[t][j].z; w[j][3] = vv[t][j].w; }
+            // row dd = 2 i + h of V^T: dim 8 cg + dd of keys 8 kb + 2 m, 8 kb + 2 m + 1
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t pl[4], ph[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    pl[m] = (w[2 * m][i] & 0xffffu) | (w[2 * m + 1][i] << 16);
+                    ph[m] = (w[2 * m][i] >> 16) | (w[2 * m + 1][i] & 0xffff0000u);
+                }
+                *reinterpret_cast<uint4 *>(vt + (8 * cg + 2 * i) * kVTS + 8 * kb) = uint4{pl[0], pl[1], pl[2], pl[3]};
+                *reinterpret_cast<uint4 *>(vt + (8 * cg + 2 * i + 1) * kVTS + 8 * kb) = uint4{ph[0], ph[1], ph[2], ph[3]};
+            }
         }
     }
     floatx4_t sacc[2];
