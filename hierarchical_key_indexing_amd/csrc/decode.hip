@@ -168,9 +168,22 @@ LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
     else g2s_scalar<16, float, float>(Cs, kCS, src, b * r, r);
 }
 
+// Waits until this wave's global stores have completed (reached the L2): a
+// workgroup barrier alone does not wait for other waves' stores, so before one
+// thread releases data that every wave wrote, each wave waits here first.
+LSA_DEV void wave_stores_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xF70);     // vmcnt(0); expcnt, lgkmcnt not waited on
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // All workgroups of a group wait here until `target` arrivals are counted:
-// a release increment, then acquire polls (bounded; a timeout sets `flag`).
+// one thread releases the workgroup's writes (ALL_WAVES: written by every
+// wave, else by wave 0 only), counts the arrival and polls with acquire loads
+// (bounded; a timeout sets `flag`).
+template <bool ALL_WAVES>
 LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
+    if (ALL_WAVES) wave_stores_done();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -200,7 +213,6 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s;
-    __shared__ int32_t ids_w[4][kMT];
     __shared__ float m_run[16], l_run[16], alpha_s[16];
 
     constexpr bool kMfma = ATTEND && sizeof(T) == 2 && DC > 0 && DC % 32 == 0;
@@ -345,7 +357,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
         }
         ++barriers;
-        group_barrier(ctrl, barriers * P, ctrl + 2);
+        group_barrier<false>(ctrl, barriers * P, ctrl + 2);      // lists: written by wave 0
         if (!leaf) {
             // candidates: the first P entries of every list (the global top P
             // lie among them).  Two merge rounds: the top P of each quartet of
@@ -472,7 +484,6 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const int j = own_lane(f), t = f - toff_s[j];
             const int32_t id = staged ? mem_s[a0_s[j] - clo[0] + t] : perm[a0_s[j] + t];
             out[wex_s[j] + t] = id;
-            if (ATTEND && own <= kOwnCap) own_s[f] = id;
         }
         for (int t = count + p * blockDim.x + tid; t < A.k; t += P * blockDim.x) out[t] = -1;
         if (p == 0 && tid == 0) {
@@ -483,22 +494,16 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
 
     if constexpr (ATTEND) {
-        // ---- attention over this workgroup's own keys
-        const int own = toff_s[64];
-        const bool own_fits = own <= kOwnCap;
-        // own_s is padded with key 0 to whole 4 x 32-key steps
-        if (own_fits)
-            for (int f = own + tid; f < ((own + 4 * kMT - 1) / (4 * kMT)) * 4 * kMT; f += blockDim.x) own_s[f] = 0;
-        __syncthreads();
-        // key id of own key f without own_s
-        const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
-        auto own_id = [&](int f) -> int32_t {
-            int j = 0;
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1) j += (j + step < 64 && toff_s[j + step] <= f) ? step : 0;
-            const int off = a0_s[j] + (f - toff_s[j]);
-            return staged ? mem_s[off - clo[0]] : perm[off];
-        };
+        // ---- attention.  Once every workgroup of the group has written its
+        // keys to sel, workgroup p attends over the retrieval positions
+        // [count * p / P, count * (p + 1) / P), so the gathers are spread
+        // evenly whatever the nodes supplied; ids are staged in own_s in
+        // chunks of up to kOwnCap, padded with key 0 to whole 4 x 32-key steps.
+        ++barriers;
+        group_barrier<true>(ctrl, barriers * P, ctrl + 2);
+        const int cnt_all = count_s;
+        const int lo = (int)(((int64_t)cnt_all * p) / P), hi = (int)(((int64_t)cnt_all * (p + 1)) / P);
+        const int32_t *selg = A.sel + (size_t)gi * A.k;
         float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
         if constexpr (kMfma) {
             const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
@@ -509,23 +514,22 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             wave_load_q<DC>(qf, Qb, G);
             WaveAttn<DC> st;
             wave_attn_init<DC>(st);
-            const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
-            for (int t = 0; t < nsteps; ++t) {
-                const int fb = (4 * t + wv) * kMT;
-                const int nk = max(0, min(kMT, own - fb));
-                const int32_t *ids = own_s + fb;
-                if (!own_fits) {
-                    if (lane < kMT) ids_w[wv][lane] = (lane < nk) ? own_id(fb + lane) : 0;
+            for (int c0 = lo; c0 < hi; c0 += kOwnCap) {
+                const int own = min(kOwnCap, hi - c0);
+                const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
+                for (int f = tid; f < nsteps * 4 * kMT; f += blockDim.x) own_s[f] = (f < own) ? selg[c0 + f] : 0;
+                __syncthreads();
+                for (int t = 0; t < nsteps; ++t) {
+                    const int fb = (4 * t + wv) * kMT;
+                    const int nk = max(0, min(kMT, own - fb));
+                    bf16x8_t pf;
+                    float alpha;
+                    wave_attn_part1<DC>(Kg, Vg, own_s + fb, nk, qf, A.scale_log2, vt, st, pf, alpha);
                     wave_sync();
-                    ids = ids_w[wv];
+                    wave_attn_part2<DC>(vt, pf, alpha, st);
                 }
-                bf16x8_t pf;
-                float alpha;
-                wave_attn_part1<DC>(Kg, Vg, ids, nk, qf, A.scale_log2, vt, st, pf, alpha);
-                wave_sync();
-                wave_attn_part2<DC>(vt, pf, alpha, st);
+                __syncthreads();
             }
-            __syncthreads();
             wave_attn_stash<DC>(st, dyn);
             __syncthreads();
             for (int e = tid; e < G * DC; e += blockDim.x) {
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             float *Kt = qs + G * d;                // [TK][d + 1]
             float *Vt = Kt + kTKD * dp;            // [TK][d]
             float *S = Vt + kTKD * d;              // [G][TK]
-            int32_t *ids_s = &ids_w[0][0];         // kTKD ids
+            int32_t *ids_s = own_s;                // kTKD ids
             for (int e = tid; e < G * d; e += blockDim.x)
                 qs[e] = to_float(Q[((size_t)i * A.h_q + (size_t)g * G) * d + e]) * A.scale_log2;
             if (tid < 16) { m_run[tid] = -INFINITY; l_run[tid] = 0.0f; }
@@ -551,9 +555,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
             const T *Kg = (const T *)A.K + (size_t)g * A.n * d;
             const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
-            for (int f0 = 0; f0 < own; f0 += kTKD) {
-                const int nk = min(kTKD, own - f0);
-                if (tid < nk) ids_s[tid] = own_id(f0 + tid);
+            for (int f0 = lo; f0 < hi; f0 += kTKD) {
+                const int nk = min(kTKD, hi - f0);
+                if (tid < nk) ids_s[tid] = selg[f0 + tid];
                 __syncthreads();
                 gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
                 __syncthreads();
@@ -611,6 +615,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
 
     // ---- arrival; the last workgroup merges and resets the group's counters
+    // (the partial state is written by every wave)
+    wave_stores_done();
     __syncthreads();
     if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
