@@ -168,17 +168,21 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
     wave_attn_stash<D>(st, scratch);
     __syncthreads();
     const float ln2 = 0.69314718055994531f;
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-        const int h = e / D, dd = e % D;
+    for (int e4 = threadIdx.x; e4 < G * D / 4; e4 += blockDim.x) {
+        const int h = e4 / (D / 4), dd = 4 * (e4 % (D / 4));
         float M, Ls;
-        const float o = wave_attn_combine<D>(scratch, h, dd, M, Ls);
+        const floatx4_t o = wave_attn_combine4<D>(scratch, h, dd, M, Ls);
         const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
         if (A.nsplit == 1) {
-            ((bf16_t *)A.out)[oh * D + dd] = from_float<bf16_t>(Ls > 0.0f ? o / Ls : 0.0f);
+            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+            bf16_t *op = (bf16_t *)A.out + oh * D + dd;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) op[j] = from_float<bf16_t>(o[j] * inv);
             if (dd == 0 && A.lse) A.lse[oh] = (Ls > 0.0f) ? (M + log2f(Ls)) * ln2 : -INFINITY;
         } else {
             float *pp = A.part + (oh * A.nsplit + split) * (size_t)(D + 2);
-            pp[dd] = o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp[dd + j] = o[j];
             if (dd == 0) { pp[D] = M; pp[D + 1] = Ls; }
         }
     }

@@ -532,10 +532,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             wave_attn_stash<DC>(st, dyn);
             __syncthreads();
-            for (int e = tid; e < G * DC; e += blockDim.x) {
-                const int h = e / DC, dd = e % DC;
+            for (int e4 = tid; e4 < G * DC / 4; e4 += blockDim.x) {
+                const int h = e4 / (DC / 4), dd = 4 * (e4 % (DC / 4));
                 float M, Ls;
-                pp[e] = wave_attn_combine<DC>(dyn, h, dd, M, Ls);
+                *reinterpret_cast<floatx4_t *>(pp + h * DC + dd) = wave_attn_combine4<DC>(dyn, h, dd, M, Ls);
                 if (dd == 0) { pp[G * DC + h] = M; pp[G * DC + G + h] = Ls; }
             }
         } else {
@@ -632,17 +632,21 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         // before the first use
         const int stride = part_stride(G, d);
         const float *pb = A.part + (size_t)gi * P * stride;
+        float *ml = dyn;                                   // [P][2G]: maxima, sums
+        for (int e = tid; e < P * 2 * G; e += blockDim.x) ml[e] = pb[(size_t)(e / (2 * G)) * stride + G * d + e % (2 * G)];
+        __syncthreads();
         for (int c4 = tid; c4 < G * d / 4; c4 += blockDim.x) {
             const int e = 4 * c4, h = e / d;
             float4 o[kMaxP];
             float mq[kMaxP], lq[kMaxP];
 #pragma unroll
+            for (int q = 0; q < kMaxP; ++q)
+                if (q < P) o[q] = *reinterpret_cast<const float4 *>(pb + (size_t)q * stride + e);
+#pragma unroll
             for (int q = 0; q < kMaxP; ++q) {
                 if (q < P) {
-                    const float *pq = pb + (size_t)q * stride;
-                    o[q] = *reinterpret_cast<const float4 *>(pq + e);
-                    mq[q] = pq[G * d + h];
-                    lq[q] = pq[G * d + G + h];
+                    mq[q] = ml[q * 2 * G + h];
+                    lq[q] = ml[q * 2 * G + G + h];
                 }
             }
             float M = -INFINITY;

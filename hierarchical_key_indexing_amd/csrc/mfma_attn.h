@@ -160,36 +160,41 @@ LSA_DEV void wave_attn_part2(const uint16_t *vt, const bf16x8_t &pf, float alpha
     }
 }
 
-// Write the four waves' states to LDS (scratch: >= 4*D*16 + 128 floats) so
-// that the workgroup can combine them: mo[w][dim][head], mm[w][head], ll[w][head].
+// Write the four waves' states to LDS (scratch: >= 4 * 64 * D / 4 + 128
+// floats) so that the workgroup can combine them: lane l of wave w stores its
+// D / 4 accumulator values contiguously (16-byte writes) at mo[w][l], then the
+// maxima mm[w][head] and sums ll[w][head].
 template <int D>
 LSA_DEV void wave_attn_stash(const WaveAttn<D> &st, float *scratch) {
     const int w = threadIdx.x / kWave, l = lane_id(), q = l / 16, c16 = l % 16;
-    float *mo = scratch, *mm = scratch + 4 * D * 16, *ll = mm + 64;
+    float *mo = scratch + ((size_t)w * kWave + l) * (D / 4);
+    float *mm = scratch + 4 * kWave * (D / 4), *ll = mm + 64;
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mo[((size_t)w * D + 16 * nb + 4 * q + j) * 16 + c16] = st.acc[nb][j];
+    for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<floatx4_t *>(mo + 4 * nb) = st.acc[nb];
     if (q == 0) { mm[w * 16 + c16] = st.m; ll[w * 16 + c16] = st.l; }
 }
 
-// Combined state of head h over the four waves: returns the unnormalised
-// output for dimension dd and, through M and Lsum, the max and the sum.
+// Combined state of head h over the four waves for dimensions dd..dd + 3
+// (dd % 4 == 0): returns the unnormalised outputs and, through M and Lsum, the
+// max and the sum.  Dimension dd of head h sits in lane 16 * ((dd % 16) / 4) + h,
+// accumulator block dd / 16.
 template <int D>
-LSA_DEV float wave_attn_combine(const float *scratch, int h, int dd, float &M, float &Lsum) {
-    const float *mo = scratch, *mm = scratch + 4 * D * 16, *ll = mm + 64;
+LSA_DEV floatx4_t wave_attn_combine4(const float *scratch, int h, int dd, float &M, float &Lsum) {
+    const float *mm = scratch + 4 * kWave * (D / 4), *ll = mm + 64;
+    const int lane = 16 * ((dd % 16) / 4) + h, nb = dd / 16;
     M = -INFINITY;
 #pragma unroll
     for (int x = 0; x < 4; ++x) M = fmaxf(M, mm[x * 16 + h]);
-    float o = 0.0f;
+    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
     Lsum = 0.0f;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const float mx = mm[x * 16 + h];
+        const floatx4_t v = *reinterpret_cast<const floatx4_t *>(scratch + ((size_t)x * kWave + lane) * (D / 4) + 4 * nb);
         if (mx > -INFINITY) {
             const float wgt = exp2f(mx - M);
             Lsum += ll[x * 16 + h] * wgt;
-            o += mo[((size_t)x * D + dd) * 16 + h] * wgt;
+            o += v * wgt;
         }
     }
     return o;
