@@ -111,7 +111,7 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
     *bytes = lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)
-                 ? lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam)
+                 ? lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)
                  : 0;
     return LSA_OK;
 }
@@ -129,7 +129,7 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
     if (m == 0) return LSA_OK;
     if (!Q || !q_pos || !index || !W || !sel || !sel_count) return LSA_EINVAL;
     if (ws && lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k) &&
-        ws_bytes >= lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam)) {
+        ws_bytes >= lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)) {
         hipError_t e = lsa::decode(Q, nullptr, nullptr, dtype, m, h_q, desc->h_kv, d, q_pos, (const char *)index,
                                    desc->n, desc->r, desc->b, desc->L, desc->nodes, desc->centroid_off,
                                    desc->count_off, desc->leaf_off_off, desc->perm_off, W, beam, k, sel, sel_count,
@@ -175,7 +175,7 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
     if (lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k))
-        *bytes = lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam);
+        *bytes = lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k);
     else
         *bytes = lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k);
     return LSA_OK;

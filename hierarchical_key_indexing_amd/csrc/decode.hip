@@ -12,18 +12,22 @@
 // Each group gets P = beam workgroups.  Every workgroup computes the group's
 // latent query and the level-1 ranking itself (identical results), then at
 // each deeper level workgroup p scores the children of the p-th kept node,
-// sorts them within one wave and publishes the sorted list.  After a group
-// barrier every workgroup derives global ranks by counting, with broadcast LDS
-// reads, the published keys above each candidate (the global top-beam at
-// internal levels; at the leaf level, how many eligible keys are retrieved
-// before each of its leaves), so no workgroup sorts more than 64 keys.  Workgroup p then writes its own
-// leaves' keys at their retrieval offsets and attends over them (matrix cores
-// for bf16); the last workgroup of the group to finish merges the P partial
-// softmax states and resets the group's counters.
+// sorts them within one wave and publishes its top P (its whole sorted list at
+// the leaf level, with the running eligible counts).  Every workgroup then
+// derives global ranks from the published lists by side-by-side binary
+// searches (the global top-beam at internal levels; at the leaf level, how
+// many eligible keys are retrieved before each of its leaves), so no
+// workgroup sorts more than 64 keys.  Workgroup p writes its own leaves' keys
+// at their retrieval offsets, and then attends over an even 1/P slice of the
+// retrieval order (matrix cores for bf16); the last workgroup of the group to
+// finish merges the P partial softmax states.
 //
-// Group barriers spin on a device-scope counter in the caller's workspace;
-// the grid is at most one workgroup per compute unit, and every spin is
-// bounded (a flag in the workspace records a timeout).
+// Workgroups exchange data through the caller's workspace without barriers:
+// it starts zeroed, a writer publishes nonzero words with device-scope stores,
+// a reader polls each word it needs until it is nonzero (bounded; a flag in
+// the workspace records a timeout), and the last workgroup zeroes everything
+// again.  The grid is at most one workgroup per compute unit, so every
+// workgroup of a group is resident while the others wait on its words.
 #include "common.h"
 #include "internal.h"
 #include "mfma_attn.h"
@@ -34,6 +38,7 @@ constexpr int kMaxP = 32;          // beam limit of this path
 constexpr int kMemCap = 2048;      // node members staged in LDS
 constexpr int kOwnCap = 2048;      // own (selected) keys listed in LDS
 constexpr int kSpinLimit = 1 << 20;
+constexpr uint64_t kEmpty = 1;     // published "no key" (real keys are >= 2^32)
 constexpr int kTKD = 64;           // keys per tile of the vector attention path
 
 struct DecodeArgs {
@@ -56,10 +61,13 @@ struct DecodeArgs {
     void *out;
     float *lse;
     // workspace
-    int32_t *ctrl;        // [groups][4]: barrier, arrivals, timeout flag
-    uint64_t *lists;      // [L-2][groups][P][64] sorted child keys of internal levels
-    uint64_t *leaf_keys;  // [groups][P][64]
-    int32_t *leaf_pre;    // [groups][P][64] inclusive prefix of eligible counts
+    // Exchange buffers: zero before a launch, published with device-scope
+    // stores of nonzero values, polled by the readers, zeroed again at the end.
+    int32_t *ctrl;        // [groups][4]: -, arrivals, timeout flag, -
+    uint64_t *lists;      // [L-2][groups][P][P] top P child keys per workgroup (kEmpty: none)
+    uint64_t *leaf_keys;  // [groups][P][64] sorted leaf keys (kEmpty: none)
+    int32_t *leaf_pre;    // [groups][P][64] 1 + inclusive prefix of eligible counts
+    int32_t *keys;        // [groups][k] 1 + key id at each retrieval position
     float *part;          // [groups][P][part_stride(G, d)]: output, then G maxima, then G sums
 };
 
@@ -168,6 +176,38 @@ LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
     else g2s_scalar<16, float, float>(Cs, kCS, src, b * r, r);
 }
 
+// Polls the words src[e] (e = threadIdx.x + blockDim.x * u < n) until each is
+// nonzero; every round issues all of the thread's outstanding loads at once.
+// Bounded: after kSpinLimit rounds `flag` records a timeout and words still
+// zero are returned as zero.
+template <int U, typename W>
+LSA_DEV void poll_nonzero(const W *src, int n, W (&out)[U], int32_t *flag) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) out[u] = 0;
+    for (int spins = 0;; ++spins) {
+        bool missing = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = (int)threadIdx.x + (int)blockDim.x * u;
+            if (e < n && out[u] == 0)
+                out[u] = __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) missing |= ((int)threadIdx.x + (int)blockDim.x * u < n) && out[u] == 0;
+        if (!missing) break;
+        if (spins >= kSpinLimit) {
+            __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
+// A polled key id, kept inside [0, n) so that no gather can leave the cache.
+LSA_DEV int32_t clamp_id(int32_t id, int64_t n) { return (int32_t)min<int64_t>(max(id, 0), n - 1); }
+
+template <typename W>
+LSA_DEV void publish(W *dst, W v) { __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
 // Waits until this wave's global stores have completed (reached the L2): a
 // workgroup barrier alone does not wait for other waves' stores, so before one
 // thread releases data that every wave wrote, each wave waits here first.
@@ -175,27 +215,6 @@ LSA_DEV void wave_stores_done() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0xF70);     // vmcnt(0); expcnt, lgkmcnt not waited on
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// All workgroups of a group wait here until `target` arrivals are counted:
-// one thread releases the workgroup's writes (ALL_WAVES: written by every
-// wave, else by wave 0 only), counts the arrival and polls with acquire loads
-// (bounded; a timeout sets `flag`).
-template <bool ALL_WAVES>
-LSA_DEV void group_barrier(int32_t *ctr, int target, int32_t *flag) {
-    if (ALL_WAVES) wave_stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        int spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > kSpinLimit) {
-                __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
 }
 
 template <typename T, bool ATTEND, int RC, int DC, int PC>
@@ -313,7 +332,6 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
     __syncthreads();
 
-    int barriers = 0;
     int64_t v = -1;
     for (int l = 2; l <= L; ++l) {
         v = (p < keep_s) ? kept_s[p] : -1;
@@ -348,16 +366,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             wave_sort_desc(key, e);
             if (!leaf) {
-                A.lists[(((size_t)(l - 2) * groups + gi) * P + p) * 64 + lane] = key;
+                if (lane < P) publish(A.lists + (((size_t)(l - 2) * groups + gi) * P + p) * P + lane, key ? key : kEmpty);
             } else {
                 const int incl = wave_incl_scan_add(e);
                 const size_t o = ((size_t)gi * P + p) * 64 + lane;
-                A.leaf_keys[o] = key;
-                A.leaf_pre[o] = incl;
+                publish(A.leaf_keys + o, key ? key : kEmpty);
+                publish(A.leaf_pre + o, incl + 1);
             }
         }
-        ++barriers;
-        group_barrier<false>(ctrl, barriers * P, ctrl + 2);      // lists: written by wave 0
         if (!leaf) {
             // candidates: the first P entries of every list (the global top P
             // lie among them).  Two merge rounds: the top P of each quartet of
@@ -366,11 +382,19 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             // the key in every list of its round (its own list gives its
             // position), found by side-by-side binary searches.
             constexpr int LQ = PC > 0 ? PC : kMaxP;          // list length bound
-            const uint64_t *src = A.lists + ((size_t)(l - 2) * groups + gi) * P * 64;
+            const uint64_t *src = A.lists + ((size_t)(l - 2) * groups + gi) * P * P;
             const int nc = P * P;
             const int nm = (P + 3) / 4;                       // merged lists
             uint64_t *m1 = lk + kMaxP * kMaxP;                // [nm][P]
-            for (int e = tid; e < nc; e += blockDim.x) lk[e] = src[(e / P) * 64 + (e % P)];
+            {
+                uint64_t w[kMaxP * kMaxP / 256];
+                poll_nonzero(src, nc, w, ctrl + 2);
+#pragma unroll
+                for (int u = 0; u < kMaxP * kMaxP / 256; ++u) {
+                    const int e = tid + 256 * u;
+                    if (e < nc) lk[e] = (w[u] == kEmpty) ? 0ull : w[u];
+                }
+            }
             for (int e = tid; e < nm * P; e += blockDim.x) m1[e] = 0ull;
             __syncthreads();
             int nonzero = 0;
@@ -394,7 +418,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                     int rank = 0;
 #pragma unroll
                     for (int q = 0; q < LQ / 4; ++q) rank += c[q];
-                    if (rank < P) kept_s[rank] = (int32_t)key_id(x);
+                    // (clamped: a node id of this level whatever the buffer held)
+                    if (rank < P) kept_s[rank] = (int32_t)min<int64_t>(key_id(x), A.nodes[l] - 1);
                 }
             }
             if (tid == 0) keep_s = min(P, nz);
@@ -405,28 +430,23 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     // ---- fill: every workgroup places its own leaves' keys
     {
         {
-            // keys and prefix counts of all P lists in one round of loads
-            const uint64_t *sk = A.leaf_keys + (size_t)gi * P * 64;
-            const int32_t *sp = A.leaf_pre + (size_t)gi * P * 64;
+            // keys and prefix counts of all P lists, polled as they are published
             constexpr int U = kMaxP * 64 / 256;
             uint64_t tk[U];
             int32_t tp[U];
+            poll_nonzero(A.leaf_keys + (size_t)gi * P * 64, P * 64, tk, ctrl + 2);
+            poll_nonzero(A.leaf_pre + (size_t)gi * P * 64, P * 64, tp, ctrl + 2);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = tid + 256 * u;
-                if (e < P * 64) { tk[u] = sk[e]; tp[u] = sp[e]; }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = tid + 256 * u;
-                if (e < P * 64) { lk[e] = tk[u]; lp[e] = tp[u]; }
+                if (e < P * 64) { lk[e] = (tk[u] == kEmpty) ? 0ull : tk[u]; lp[e] = max(tp[u] - 1, 0); }
             }
         }
         __syncthreads();
         if (wv == 0) {
             int tot = (lane < P) ? lp[lane * 64 + 63] : 0;
             tot = wave_sum_i(tot);
-            if (lane == 0) count_s = min(A.k, tot);
+            if (lane == 0) count_s = max(0, min(A.k, tot));
         }
         // eligible keys retrieved before each own leaf: wave w sums, over the
         // lists q = w, w + 4, ..., the eligible counts of the leaves above it
@@ -484,6 +504,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const int j = own_lane(f), t = f - toff_s[j];
             const int32_t id = staged ? mem_s[a0_s[j] - clo[0] + t] : perm[a0_s[j] + t];
             out[wex_s[j] + t] = id;
+            if (ATTEND) publish(A.keys + (size_t)gi * A.k + wex_s[j] + t, id + 1);
         }
         for (int t = count + p * blockDim.x + tid; t < A.k; t += P * blockDim.x) out[t] = -1;
         if (p == 0 && tid == 0) {
@@ -494,16 +515,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
 
     if constexpr (ATTEND) {
-        // ---- attention.  Once every workgroup of the group has written its
-        // keys to sel, workgroup p attends over the retrieval positions
-        // [count * p / P, count * (p + 1) / P), so the gathers are spread
-        // evenly whatever the nodes supplied; ids are staged in own_s in
-        // chunks of up to kOwnCap, padded with key 0 to whole 4 x 32-key steps.
-        ++barriers;
-        group_barrier<true>(ctrl, barriers * P, ctrl + 2);
+        // ---- attention.  Workgroup p attends over the retrieval positions
+        // [count * p / P, count * (p + 1) / P), whichever workgroups placed
+        // them, so the gathers are spread evenly whatever the nodes supplied;
+        // their ids are polled from the published keys into own_s in chunks
+        // of up to kOwnCap, padded with key 0 to whole 4 x 32-key steps.
         const int cnt_all = count_s;
         const int lo = (int)(((int64_t)cnt_all * p) / P), hi = (int)(((int64_t)cnt_all * (p + 1)) / P);
-        const int32_t *selg = A.sel + (size_t)gi * A.k;
         float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
         if constexpr (kMfma) {
             const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
@@ -517,7 +535,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             for (int c0 = lo; c0 < hi; c0 += kOwnCap) {
                 const int own = min(kOwnCap, hi - c0);
                 const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
-                for (int f = tid; f < nsteps * 4 * kMT; f += blockDim.x) own_s[f] = (f < own) ? selg[c0 + f] : 0;
+                for (int f0 = 0; f0 < own; f0 += 8 * 256) {
+                    int32_t w[8];
+                    poll_nonzero(A.keys + (size_t)gi * A.k + c0 + f0, own - f0, w, ctrl + 2);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (f0 + tid + 256 * u < own) own_s[f0 + tid + 256 * u] = clamp_id(w[u] - 1, A.n);
+                }
+                for (int f = own + tid; f < nsteps * 4 * kMT; f += blockDim.x) own_s[f] = 0;
                 __syncthreads();
                 for (int t = 0; t < nsteps; ++t) {
                     const int fb = (4 * t + wv) * kMT;
@@ -557,7 +582,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
             for (int f0 = lo; f0 < hi; f0 += kTKD) {
                 const int nk = min(kTKD, hi - f0);
-                if (tid < nk) ids_s[tid] = selg[f0 + tid];
+                {
+                    int32_t w[1];
+                    poll_nonzero(A.keys + (size_t)gi * A.k + f0, nk, w, ctrl + 2);
+                    if (tid < nk) ids_s[tid] = clamp_id(w[0] - 1, A.n);
+                }
                 __syncthreads();
                 gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
                 __syncthreads();
@@ -670,25 +699,41 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
     }
-    if (tid == 0) {
-        __hip_atomic_store(ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ctrl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every workgroup has arrived and the merge has read the partial states,
+    // so no one reads the group's part of the workspace any more: leave all of
+    // it zeroed for the next launch (a launch of another shape lays its
+    // exchange buffers over this one's partial states)
+    __syncthreads();
+    if (ATTEND) {
+        const size_t np = (size_t)P * part_stride(G, d);
+        f4_t *pz = reinterpret_cast<f4_t *>(A.part + (size_t)gi * np);
+        for (size_t e = tid; e < np / 4; e += blockDim.x) pz[e] = f4_t{0.f, 0.f, 0.f, 0.f};
     }
+    for (int e = tid; e < (L - 2) * P * P; e += blockDim.x)
+        publish(A.lists + ((size_t)(e / (P * P)) * groups + gi) * P * P + e % (P * P), (uint64_t)0);
+    for (int e = tid; e < P * 64; e += blockDim.x) {
+        publish(A.leaf_keys + (size_t)gi * P * 64 + e, (uint64_t)0);
+        publish(A.leaf_pre + (size_t)gi * P * 64 + e, 0);
+    }
+    if (ATTEND)
+        for (int e = tid; e < count_s; e += blockDim.x) publish(A.keys + (size_t)gi * A.k + e, 0);
+    if (tid == 0) publish(ctrl + 1, 0);
 }
 
 // ---------------------------------------------------------------- host side
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct DecodeWs { int32_t *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre; float *part; size_t bytes; };
+struct DecodeWs { int32_t *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre, *keys; float *part; size_t bytes; };
 
-static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G, int d) {
+static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G, int d, int k) {
     size_t cur = 0;
     DecodeWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
     w.ctrl = (int32_t *)take(sizeof(int32_t) * 4 * (size_t)groups);
-    w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * 64);
+    w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * P);
     w.leaf_keys = (uint64_t *)take(sizeof(uint64_t) * (size_t)groups * P * 64);
     w.leaf_pre = (int32_t *)take(sizeof(int32_t) * (size_t)groups * P * 64);
+    w.keys = (int32_t *)take(sizeof(int32_t) * (size_t)groups * k);
     w.part = (float *)take(sizeof(float) * (size_t)groups * P * (size_t)part_stride(G, d));
     w.bytes = cur;
     return w;
@@ -733,8 +778,8 @@ bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, in
     return cus > 0 && m * h_kv * beam <= cus;
 }
 
-int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam) {
-    return (int64_t)carve_decode_ws(nullptr, m * h_kv, beam, L, h_q / h_kv, d).bytes;
+int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k) {
+    return (int64_t)carve_decode_ws(nullptr, m * h_kv, beam, L, h_q / h_kv, d, k).bytes;
 }
 
 template <typename T, bool ATT, int RC, int DC, int PC>
@@ -765,8 +810,9 @@ hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     A.scale_log2 = scale * 1.4426950408889634f; A.out = out; A.lse = lse;
     const int G = h_q / h_kv;
-    DecodeWs w = carve_decode_ws((char *)ws, m * h_kv, beam, L, G, d);
-    A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.part = w.part;
+    DecodeWs w = carve_decode_ws((char *)ws, m * h_kv, beam, L, G, d, k);
+    A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.keys = w.keys;
+    A.part = w.part;
     const size_t shm = decode_dyn_bytes(dtype, G, d, r);
     const dim3 grid((unsigned)beam, (unsigned)(m * h_kv));
     if (fast_shape(dtype, d, r) && beam == 16) {
