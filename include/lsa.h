@@ -169,11 +169,12 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * Workspace: ws may be NULL.  When ws holds at least
  * lsa_select_workspace_bytes bytes (> 0), small batches (m * h_kv * beam up
  * to the number of compute units, L >= 2, beam <= 32) run on beam
- * workgroups per (row, KV head) that synchronise through counters in ws.  The
- * caller zero-fills ws once before its first use; every call leaves the
- * counters at zero again, so the same ws serves any number of calls.  Calls
- * that share one ws must not run concurrently.  Both kernels give identical
- * results.
+ * workgroups per (row, KV head) that exchange their partial rankings through
+ * ws (words published into zeroed memory and polled by the readers).  The
+ * caller zero-fills ws once before its first use; every call leaves all of the
+ * bytes it used at zero again, so the same ws serves any number of calls, of
+ * any sizes that fit it.  Calls that share one ws must not run concurrently
+ * (they would read each other's words).  Both kernels give identical results.
  */
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
                const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,
@@ -219,8 +220,11 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
  * partial softmax states), else as the two calls in sequence.  Arguments as
  * in lsa_select and lsa_attend; K and V are the cache the index was built
  * from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes bytes) must be
- * zero-filled before its first use and is left reusable; calls sharing one ws
- * must not run concurrently.  Outputs equal those of the two separate calls
+ * zero-filled before its first use; every call leaves it zeroed again, so it
+ * serves any number of calls of any sizes that fit it; calls sharing one ws
+ * must not run concurrently.  In the one-launch form the workgroups of a
+ * (row, KV head) pair split the attention evenly over the retrieval order.
+ * Outputs equal those of the two separate calls
  * (sel, sel_count and sel_cutoff bit for bit; out and lse within fp32
  * rounding of the accumulation order).
  * Limits: those of lsa_select and of lsa_attend.
