@@ -197,6 +197,7 @@ LSA_DEV void g2s_rows(float *dst, int ld, const float *__restrict__ src, int n, 
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
             t[u] = s4[min(e, n4 - 1)];        // clamped: every load stays in bounds
         }
+        __builtin_amdgcn_sched_barrier(0);     // all loads issued before the first store waits
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
@@ -216,8 +217,9 @@ LSA_DEV void g2s_scalar(D *dst, int ld, const S *__restrict__ src, int n, int co
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
-            if (e < n) t[u] = src[e];
+            t[u] = src[min(e, n - 1)];         // clamped: every load stays in bounds
         }
+        __builtin_amdgcn_sched_barrier(0);     // all loads issued before the first store waits
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;

@@ -156,8 +156,9 @@ LSA_DEV void g2s_flat(E *dst, const E *__restrict__ src, int n) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
-            if (e < n) t[u] = src[e];
+            t[u] = src[min(e, n - 1)];         // clamped: every load stays in bounds
         }
+        __builtin_amdgcn_sched_barrier(0);     // all loads issued before the first store waits
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = base + (int)threadIdx.x + u * (int)blockDim.x;
@@ -166,9 +167,27 @@ LSA_DEV void g2s_flat(E *dst, const E *__restrict__ src, int n) {
     }
 }
 
+// b <= 64 rows of 64 floats into LDS rows of stride kCS: four 16-byte loads per
+// thread, all issued before any store (sources clamped to the b rows; rows at
+// and beyond b receive copies that are never read).
+LSA_DEV void load_rows64(float *Cs, const float *__restrict__ src, int b);
+
 // LDS row stride of staged centroid rows: a multiple of 4 (16-byte row reads)
 // whose eight consecutive rows start in eight different 4-bank groups.
 constexpr int kCS = 68;
+
+LSA_DEV void load_rows64(float *Cs, const float *__restrict__ src, int b) {
+    const f4_t *s4 = reinterpret_cast<const f4_t *>(src);
+    f4_t t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = s4[min((int)threadIdx.x + 256 * u, b * 16 - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = (int)threadIdx.x + 256 * u;
+        *reinterpret_cast<f4_t *>(Cs + (e / 16) * kCS + (e % 16) * 4) = t[u];
+    }
+}
 
 // b rows of r floats (one node's children) into LDS rows of stride kCS.
 LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
@@ -262,7 +281,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     {
         const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
         const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
-        if (tid < b) ccnt[tid] = cn1[tid];
+        const int32_t cnt_r = cn1[min(tid, b - 1)];       // stored after the other loads are issued
         const float *Wg = A.W + (size_t)g * d * r;
         if constexpr (RC == 64 && DC == 128 && sizeof(T) == 2) {
             // one round of loads: 4 float4 of rows, 8 float4 of W, 1 uint4 of Q per thread
@@ -270,18 +289,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const f4_t *w4 = reinterpret_cast<const f4_t *>(Wg);
             const uint4 *q4 = reinterpret_cast<const uint4 *>(Q + ((size_t)i * A.h_q + (size_t)g * G) * DC);
             f4_t cr[4], wr[8];
-            uint4 qr = {0, 0, 0, 0};
+            uint4 qr;
 #pragma unroll
             for (int u = 0; u < 4; ++u) cr[u] = c4[min(tid + 256 * u, b * 16 - 1)];   // clamped: loads stay in bounds
 #pragma unroll
             for (int u = 0; u < 8; ++u) wr[u] = w4[tid + 256 * u];
-            if (tid < G * 16) qr = q4[tid];
+            qr = q4[min(tid, G * 16 - 1)];
+            __builtin_amdgcn_sched_barrier(0);     // all loads issued before the first store waits
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int e = tid + 256 * u;
-                if (e < b * 16) {
-                    *reinterpret_cast<f4_t *>(Cs + (e / 16) * kCS + (e % 16) * 4) = cr[u];
-                }
+                const int e = tid + 256 * u;      // rows at and beyond b get copies that are never read
+                *reinterpret_cast<f4_t *>(Cs + (e / 16) * kCS + (e % 16) * 4) = cr[u];
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) reinterpret_cast<f4_t *>(Wl)[tid + 256 * u] = wr[u];
@@ -299,6 +317,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             else g2s_flat<16>(Wl, Wg, d * r);
             g2s_scalar<16, T, float>(Ql, G * d, Q + ((size_t)i * A.h_q + (size_t)g * G) * d, G * d, G * d);
         }
+        if (tid < b) ccnt[tid] = cnt_r;
         if (tid == 0) { count_s = 0; last_s = 0; }
     }
     __syncthreads();
@@ -339,9 +358,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         if (v >= 0) {
             const float *Cl = (const float *)(A.index + A.centroid_off[l]) + ((size_t)g * A.nodes[l] + (size_t)v * b) * r;
             const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l] + (size_t)v * b;
-            if (tid < b) ccnt[tid] = cn[tid];
-            if (leaf && tid <= b) clo[tid] = leaf_off[(size_t)v * b + tid];
-            load_rows(Cs, Cl, b, r);
+            // counts, leaf offsets and rows in one round of loads (clamped
+            // indices; the LDS stores come after every load is issued)
+            const int32_t cnt_r = cn[min(tid, b - 1)];
+            const int32_t lo_r = leaf ? leaf_off[(size_t)v * b + min(tid, b)] : 0;
+            if constexpr (RC == 64) load_rows64(Cs, Cl, b);
+            else load_rows(Cs, Cl, b, r);
+            if (tid < b) ccnt[tid] = cnt_r;
+            if (leaf && tid <= b) clo[tid] = lo_r;
         }
         __syncthreads();
         if (leaf && v >= 0) {

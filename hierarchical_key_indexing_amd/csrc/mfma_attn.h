@@ -79,17 +79,19 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
 #pragma unroll
     for (int t = 0; t < UPL; ++t) {
         const int un = l + kWave * t;
-        if (un < NU) {
+        if (NU % kWave == 0 || un < NU) {
             const int kb = un % 4, cg = un / 4;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 vv[t][j] = *reinterpret_cast<const uint4 *>(Vg + (size_t)ids[8 * kb + j] * D + 8 * cg);
         }
     }
+    // every K and V load is in flight before the first use of any of them
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < UPL; ++t) {
         const int un = l + kWave * t;
-        if (un < NU) {
+        if (NU % kWave == 0 || un < NU) {
             const int kb = un % 4, cg = un / 4;
             uint32_t w[8][4];
 #pragma unroll
