@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
         float alpha;
         wave_attn_part1<D>(Kg, Vg, ids_w[w], nk, qf, A.scale_log2, vt[w], st, pf, alpha);
         __syncthreads();
-        wave_attn_part2<D>(vt[w], pf, alpha, st);
+        wave_attn_part2<D>(vt[w], pf, alpha, st, t == 0);
     }
     __syncthreads();
     float *scratch = reinterpret_cast<float *>(&vt[0][0]);

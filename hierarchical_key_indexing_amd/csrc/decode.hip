@@ -575,7 +575,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                     float alpha;
                     wave_attn_part1<DC>(Kg, Vg, own_s + fb, nk, qf, A.scale_log2, vt, st, pf, alpha);
                     wave_sync();
-                    wave_attn_part2<DC>(vt, pf, alpha, st);
+                    wave_attn_part2<DC>(vt, pf, alpha, st, c0 == lo && t == 0);
                 }
                 __syncthreads();
             }

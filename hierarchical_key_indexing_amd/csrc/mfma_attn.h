@@ -25,12 +25,6 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr int kMT = 32;        // keys per wave step
 constexpr int kVTS = kMT + 8;  // V^T row stride in LDS (bf16 elements; 16-byte aligned rows)
 
-LSA_DEV uint16_t bf16_bits_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 template <int D>
 struct WaveAttn {
     floatx4_t acc[D / 16];   // O^T blocks: lane holds head l%16, dims 16*nb + 4*(l/16) + j
@@ -102,8 +96,9 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
                 uint32_t pl[4], ph[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    pl[m] = (w[2 * m][i] & 0xffffu) | (w[2 * m + 1][i] << 16);
-                    ph[m] = (w[2 * m][i] >> 16) | (w[2 * m + 1][i] & 0xffff0000u);
+                    // low halves / high halves of keys 2m, 2m + 1 (one byte permute each)
+                    pl[m] = __builtin_amdgcn_perm(w[2 * m + 1][i], w[2 * m][i], 0x05040100u);
+                    ph[m] = __builtin_amdgcn_perm(w[2 * m + 1][i], w[2 * m][i], 0x07060302u);
                 }
                 *reinterpret_cast<uint4 *>(vt + (8 * cg + 2 * i) * kVTS + 8 * kb) = uint4{pl[0], pl[1], pl[2], pl[3]};
                 *reinterpret_cast<uint4 *>(vt + (8 * cg + 2 * i + 1) * kVTS + 8 * kb) = uint4{ph[0], ph[1], ph[2], ph[3]};
@@ -132,13 +127,13 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
     mt = fmaxf(mt, xor_lane_f<16>(mt));
     mt = fmaxf(mt, xor_lane_f<32>(mt));
     const float m_new = fmaxf(st.m, mt);
-    alpha = (st.m == -INFINITY) ? 0.0f : exp2f(st.m - m_new);
+    alpha = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
     float ls = 0.0f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const float pr = (sv[s] == -INFINITY) ? 0.0f : exp2f(sv[s] - m_new);
+        const float pr = (sv[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[s] - m_new);
         ls += pr;
-        pf[s] = __builtin_bit_cast(__bf16, bf16_bits_rne(pr));
+        pf[s] = (__bf16)pr;                      // round to nearest even
     }
     ls += xor_lane_f<16>(ls);
     ls += xor_lane_f<32>(ls);
@@ -148,7 +143,8 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
 
 // Second half: O^T = alpha * O^T + V^T P^T (V^T from this wave's LDS tile).
 template <int D>
-LSA_DEV void wave_attn_part2(const uint16_t *vt, const bf16x8_t &pf, float alpha, WaveAttn<D> &st) {
+LSA_DEV void wave_attn_part2(const uint16_t *vt, const bf16x8_t &pf, float alpha, WaveAttn<D> &st,
+                             bool first = false) {
     const int l = lane_id(), q = l / 16, c16 = l % 16;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
@@ -157,7 +153,7 @@ LSA_DEV void wave_attn_part2(const uint16_t *vt, const bf16x8_t &pf, float alpha
         const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * q);
         const uint4 vv = {lo.x, lo.y, hi.x, hi.y};
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
-        st.acc[nb] = st.acc[nb] * alpha;
+        if (!first) st.acc[nb] = st.acc[nb] * alpha;   // first step: the accumulators are still 0
         st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, st.acc[nb], 0, 0, 0);
     }
 }
@@ -194,7 +190,7 @@ LSA_DEV floatx4_t wave_attn_combine4(const float *scratch, int h, int dd, float 
         const float mx = mm[x * 16 + h];
         const floatx4_t v = *reinterpret_cast<const floatx4_t *>(scratch + ((size_t)x * kWave + lane) * (D / 4) + 4 * nb);
         if (mx > -INFINITY) {
-            const float wgt = exp2f(mx - M);
+            const float wgt = __builtin_amdgcn_exp2f(mx - M);
             Lsum += ll[x * 16 + h] * wgt;
             o += v * wgt;
         }
