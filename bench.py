@@ -12,7 +12,11 @@ its own cache and index: the bench builds --layers distinct layers (48 by
 default: 48 x 6.5 MB touched per step exceeds the 256 MB last-level cache, so
 every layer starts cold in the caches) and replays them in one HIP graph; the
 per-layer time is the replay time over the layers.  The same layer replayed
-eight times (its 6.5 MB then cache-resident) is reported as warm_same_layer_us.  The index build (projection, k-means levels) is timed in the
+eight times (its 6.5 MB then cache-resident) is reported as warm_same_layer_us.
+The breakdown also reports a 4096-row last-chunk prefill on the same cache, a
+decode layer at 10M tokens (decode_10m) and the forward of a training-shaped
+causal layer at 128k tokens (train_128k: build, select and attend of every
+position).  The index build (projection, k-means levels) is timed in the
 same run and reported under "breakdown".
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
@@ -116,6 +120,108 @@ def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s):
                        f"{desc.n}-key index built on the GPU), identical inputs, {el:.1f} s total")
 
 
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def extra_decode(lsa, synth, torch, np, dev, w, reps=25, per_graph=8):
+    """One decode layer at w's size, replayed (its data then cache-resident):
+    per-layer time, index build time, algorithmic bandwidth."""
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    pos = w.positions().to(dev)
+    Q = synth.make_queries(w, K, pos)
+    desc = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L)
+    index = torch.empty(desc.bytes, dtype=torch.uint8, device=dev)
+    bws = torch.empty(lsa.build_workspace_bytes(w.n, w.h_kv, w.d, w.r, w.b, w.L), dtype=torch.uint8, device=dev)
+    e = _events(torch, 2)
+    e[0].record()
+    lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=bws)
+    e[1].record()
+    torch.cuda.synchronize()
+    build_ms = e[0].elapsed_time(e[1])
+    del bws
+    m = pos.shape[0]
+    fws = lsa.workspace(lsa.select_attend_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
+    sel = torch.empty((m, w.h_kv, w.k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((m, w.h_kv), dtype=torch.int32, device=dev)
+    out = torch.empty_like(Q)
+    lse = torch.empty((m, w.h_q), dtype=torch.float32, device=dev)
+
+    def step():
+        lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, out=out, lse=lse,
+                          want_cutoff=False, ws=fws)
+    step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            step()
+    for _ in range(3):
+        g.replay()
+    e = _events(torch, 2)
+    e[0].record()
+    for _ in range(reps):
+        g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    us = e[0].elapsed_time(e[1]) * 1e3 / (reps * per_graph)
+    c = cnt.cpu().numpy()
+    ab = select_bytes(w, m, c, w.beam * w.b) + attend_bytes(w, m, c)
+    return {"us_per_layer_warm": round(us, 3), "build_ms": round(build_ms, 3), "mean_sel_count": float(c.mean()),
+            "algorithmic_bytes": int(ab), "achieved_GBps": round(ab / (us * 1e-6) / 1e9, 2),
+            "index_bytes": int(desc.bytes), "kv_bytes": int(2 * K.numel() * K.element_size()),
+            "timing": f"one layer replayed {per_graph} times per graph, {reps} graphs (cache-resident)"}
+
+
+def extra_train(lsa, synth, torch, np, dev, w, reps=3):
+    """Forward of a training-shaped layer: index build, then select and attend
+    for every position (causal), timed with events."""
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    pos = w.positions().to(dev)
+    Q = synth.make_queries(w, K, pos)
+    m = pos.shape[0]
+    desc = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L)
+    index = torch.empty(desc.bytes, dtype=torch.uint8, device=dev)
+    bws = torch.empty(lsa.build_workspace_bytes(w.n, w.h_kv, w.d, w.r, w.b, w.L), dtype=torch.uint8, device=dev)
+    sel = torch.empty((m, w.h_kv, w.k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((m, w.h_kv), dtype=torch.int32, device=dev)
+    out = torch.empty_like(Q)
+    aws_n = lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k)
+    aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device=dev)
+
+    def fwd(ev=None):
+        if ev: ev[0].record()
+        lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=bws)
+        if ev: ev[1].record()
+        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, want_cutoff=False, ws=None)
+        if ev: ev[2].record()
+        lsa.attend(Q, K, V, sel, cnt, out=out, want_lse=False, ws=aws)
+        if ev: ev[3].record()
+    fwd()
+    torch.cuda.synchronize()
+    evs = [_events(torch, 4) for _ in range(reps)]
+    for ev in evs:
+        fwd(ev)
+    torch.cuda.synchronize()
+    b = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
+    sl = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs]))
+    at = float(np.mean([ev[2].elapsed_time(ev[3]) for ev in evs]))
+    c = cnt.cpu().numpy()
+    tot = b + sl + at
+    return {"forward_ms": round(tot, 3), "build_ms": round(b, 3), "select_ms": round(sl, 3), "attend_ms": round(at, 3),
+            "queries_per_s": round(m / (tot * 1e-3), 1), "mean_sel_count": float(c.mean()),
+            "attend_GBps_algorithmic": round(attend_bytes(w, m, c) / (at * 1e-3) / 1e9, 2),
+            "attend_tflops": round(4.0 * m * w.h_q * float(c.mean()) * w.d / (at * 1e-3) / 1e12, 3),
+            "timing": f"build + select + attend of all {m} positions, mean of {reps} forwards"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +232,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 10M decode and 128k training-layer figures")
     ap.add_argument("--layers", type=int, default=48,
                     help="distinct decode layers (each its own cache, index and query) run in sequence")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -365,6 +472,19 @@ def main():
     if not args.no_cpu:
         log("cpu baseline")
         cpu = cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, args.cpu_seconds)
+
+    # ---- secondary workloads on their own caches: decode at 10M tokens, a
+    # training-shaped causal layer at 128k tokens
+    if not args.no_extra and w.name == "decode_1m":
+        del layers, L0, K, V, W, Q, index, fws, sws, aws, sel, cnt, cut, out, lse
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log("decode_10m")
+        breakdown["decode_10m"] = extra_decode(lsa, synth, torch, np, dev, synth.WORKLOADS["decode_10m"])
+        torch.cuda.empty_cache()
+        log("train_128k")
+        breakdown["train_128k"] = extra_train(lsa, synth, torch, np, dev, synth.WORKLOADS["train_128k"])
+        torch.cuda.empty_cache()
 
     res = {
         "metric": "µs/layer decode and queries/s last-chunk prefill at 1M/10M ctx; % HBM/MFMA peak",
