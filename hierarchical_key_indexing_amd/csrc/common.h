@@ -121,6 +121,85 @@ LSA_DEV int wave_sum_i(int v) {
     return v;
 }
 
+// An opaque copy of v: per-stage lane masks are then recomputed by each stage
+// instead of being kept live (in scalar registers) across the whole network.
+LSA_DEV int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Bitonic sort of one 64-bit key (plus payload) per lane, descending by lane.
+// Every compare-exchange reads the partner lane through DPP / row swaps.
+template <int SIZE, int STRIDE>
+LSA_DEV void sort_stage(uint64_t &key, int &pay, int l0) {
+    const int l = opaque(l0);
+    const uint64_t ok = xor_lane64<STRIDE>(key);
+    const int op = xor_lane_i<STRIDE>(pay);
+    // lower lane of a descending segment (or upper lane of an ascending one)
+    // keeps the larger key; branch-free select
+    const unsigned want_gt = ((l & STRIDE) == 0) == ((l & SIZE) == 0);
+    const unsigned gt = ok > key, lt = ok < key;
+    const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
+    key = take ? ok : key;
+    pay = take ? op : pay;
+}
+template <int SIZE, int STRIDE>
+LSA_DEV void sort_stages(uint64_t &key, int &pay, int l) {
+    sort_stage<SIZE, STRIDE>(key, pay, l);
+    if constexpr (STRIDE > 1) sort_stages<SIZE, STRIDE / 2>(key, pay, l);
+    else if constexpr (SIZE < kWave) sort_stages<SIZE * 2, SIZE>(key, pay, l);
+}
+LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_stages<2, 1>(key, pay, lane_id()); }
+
+// Bitonic sort, descending, of the 1024 64-bit keys of a 256-thread block,
+// four per thread: thread t holds elements 4t..4t+3 before and after.
+// Exchanges between a thread's own elements stay in registers, between the
+// lanes of a wave they go through DPP / row swaps, and only the two strides
+// that cross waves (256, 512) go through LDS (`sk`, 1024 keys).
+template <int SIZE, int S>
+LSA_DEV void bsort_stage(uint64_t (&k)[4], int t0, uint64_t *sk) {
+    const int t = opaque(t0);
+    if constexpr (S < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if ((i & S) == 0) {
+                const bool desc = ((4 * t + i) & SIZE) == 0;   // lower element keeps the larger key
+                const uint64_t a = k[i], b = k[i + S];
+                const bool sw = desc ? (b > a) : (a > b);
+                k[i] = sw ? b : a;
+                k[i + S] = sw ? a : b;
+            }
+        }
+    } else if constexpr (S < 256) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * t + i;
+            const uint64_t o = xor_lane64<S / 4>(k[i]);
+            const bool want_gt = ((e & S) == 0) == ((e & SIZE) == 0);
+            k[i] = (want_gt ? (o > k[i]) : (o < k[i])) ? o : k[i];
+        }
+    } else {
+        __syncthreads();                 // earlier readers of sk are done
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sk[4 * t + i] = k[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * t + i;
+            const uint64_t o = sk[e ^ S];
+            const bool want_gt = ((e & S) == 0) == ((e & SIZE) == 0);
+            k[i] = (want_gt ? (o > k[i]) : (o < k[i])) ? o : k[i];
+        }
+    }
+}
+template <int SIZE, int S>
+LSA_DEV void bsort_stages(uint64_t (&k)[4], int t, uint64_t *sk) {
+    bsort_stage<SIZE, S>(k, t, sk);
+    if constexpr (S > 1) bsort_stages<SIZE, S / 2>(k, t, sk);
+    else if constexpr (SIZE < 1024) bsort_stages<SIZE * 2, SIZE>(k, t, sk);
+}
+LSA_DEV void block_sort1024_desc(uint64_t (&k)[4], uint64_t *sk) { bsort_stages<2, 1>(k, (int)threadIdx.x, sk); }
+
 // Inclusive prefix sum over the 64 lanes: scans of the four 16-lane rows with
 // DPP row shifts (a lane with no source adds 0), then each row adds the
 // totals of the rows below it, read from lanes 15, 31 and 47.

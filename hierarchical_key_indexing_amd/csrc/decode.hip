@@ -75,28 +75,6 @@ struct DecodeArgs {
 LSA_HOST_DEV inline int part_stride(int G, int d) { return (G * d + 2 * G + 3) & ~3; }
 
 // ---------------------------------------------------------------- helpers
-// Bitonic sort of one 64-bit key (plus payload) per lane, descending by lane.
-// Every compare-exchange reads the partner lane through DPP / row swaps.
-template <int SIZE, int STRIDE>
-LSA_DEV void sort_stage(uint64_t &key, int &pay, int l) {
-    const uint64_t ok = xor_lane64<STRIDE>(key);
-    const int op = xor_lane_i<STRIDE>(pay);
-    // lower lane of a descending segment (or upper lane of an ascending one)
-    // keeps the larger key; branch-free select
-    const unsigned want_gt = ((l & STRIDE) == 0) == ((l & SIZE) == 0);
-    const unsigned gt = ok > key, lt = ok < key;
-    const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
-    key = take ? ok : key;
-    pay = take ? op : pay;
-}
-template <int SIZE, int STRIDE>
-LSA_DEV void sort_stages(uint64_t &key, int &pay, int l) {
-    sort_stage<SIZE, STRIDE>(key, pay, l);
-    if constexpr (STRIDE > 1) sort_stages<SIZE, STRIDE / 2>(key, pay, l);
-    else if constexpr (SIZE < kWave) sort_stages<SIZE * 2, SIZE>(key, pay, l);
-}
-LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_stages<2, 1>(key, pay, lane_id()); }
-
 LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
     int lo = 0, hi = len;
     while (lo < hi) {

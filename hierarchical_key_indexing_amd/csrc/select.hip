@@ -191,6 +191,176 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- throughput path
+// Same selection for many rows (prefill, training layers), shaped for
+// throughput: r = 64, b <= 64, beam <= 16, L >= 2, leaf ids below 2^22.
+//   * W_g is staged in LDS and u = fl32(qbar . W_g) computed from there;
+//   * the root's children are scored by one wave and ranked by a wave sort;
+//   * at each deeper level wave w scores the children of kept nodes w, w + 4,
+//     ... (lane c: child c, its row loaded straight into registers), and the
+//     block sorts all beam * b candidates at once (four keys per thread,
+//     DPP exchanges inside a wave, LDS only across waves);
+//   * a candidate leaf's key also carries its slot (kept node j, child c), so
+//     after the sort its eligible count and first member are found in LDS.
+// Scores, order and ties are those of k_select.
+
+// (orderable score) << 32 | (~id, 22 bits) << 10 | slot: orders as make_key for ids < 2^22
+LSA_DEV uint64_t make_key_slot(float score, uint32_t id, int slot) {
+    return ((uint64_t)orderable(score) << 32) | ((uint64_t)(~id & 0x3FFFFFu) << 10) | (uint64_t)slot;
+}
+LSA_DEV uint32_t slot_key_id(uint64_t k) { return ~(uint32_t)(k >> 10) & 0x3FFFFFu; }
+
+// u . row (64 floats) in double, ascending index; the row comes straight from
+// global memory (16 loads issued before the first FMA), u from LDS.
+LSA_DEV float score_row64(const float *u, const float *__restrict__ row) {
+    const f4_t *r4 = reinterpret_cast<const f4_t *>(row);
+    const f4_t *u4 = reinterpret_cast<const f4_t *>(u) + opaque(0);   // u read at each use, not kept live
+    f4_t v[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) v[x] = r4[x];
+    double s = 0.0;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+        const f4_t a = u4[x];
+        s = fma((double)a.x, (double)v[x].x, s);
+        s = fma((double)a.y, (double)v[x].y, s);
+        s = fma((double)a.z, (double)v[x].z, s);
+        s = fma((double)a.w, (double)v[x].w, s);
+    }
+    return (float)s;
+}
+
+constexpr int kFastP = 16;          // beam limit of the throughput path
+constexpr int kFastR = 64;          // latent dimension of the throughput path
+
+template <typename T>
+__global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float dynf[];   // W_g, then keys and leaf tables
+    __shared__ __attribute__((aligned(16))) float qbar_s[256];
+    __shared__ __attribute__((aligned(16))) float u_s[kFastR];
+    __shared__ int32_t kept_s[kFastP];
+    __shared__ int keep_s, scratch[8];
+    __shared__ float cut_s;
+    constexpr int R = kFastR;
+    const int64_t i = blockIdx.x;
+    const int g = blockIdx.y;
+    const int G = A.h_q / A.h_kv, d = A.d, b = A.b, L = A.L, P = A.beam;
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+    const T *Q = (const T *)A.Q;
+    const int32_t pos = A.q_pos[i];
+    const bool all_eligible = pos >= A.n - 1;
+
+    // ---- group latent query
+    float *Wl = dynf;                                   // [d][R]
+    g2s_rows<8>(Wl, d * R, A.W + (size_t)g * d * R, d * R, d * R);
+    for (int t = tid; t < d; t += blockDim.x) {
+        double s = 0.0;
+        for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
+        qbar_s[t] = (float)(s / (double)G);
+    }
+    if (tid == 0) cut_s = -INFINITY;
+    __syncthreads();
+    if (tid < R) {
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)Wl[t * R + tid], s);
+        u_s[tid] = (float)s;
+    }
+    __syncthreads();
+
+    // ---- level 1: the root's non-empty children, best min(beam, #) kept
+    if (wv == 0) {
+        const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * R;
+        const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
+        uint64_t key = 0;
+        int pay = 0;
+        if (lane < b && cn1[lane] > 0) key = make_key(score_row64(u_s, C1 + (size_t)lane * R), (uint32_t)lane);
+        const int nz = __popcll(__ballot(key != 0));
+        wave_sort_desc(key, pay);
+        const int keep = min(P, nz);
+        if (lane < keep) kept_s[lane] = (int32_t)key_id(key);
+        if (lane == 0) keep_s = keep;
+    }
+    __syncthreads();
+
+    // ---- levels 2..L
+    uint64_t *sk = reinterpret_cast<uint64_t *>(dynf);           // 1024 candidate keys
+    int32_t *eli = reinterpret_cast<int32_t *>(sk + 1024);        // [kFastP][64] eligible counts
+    int32_t *lof = eli + kFastP * 64;                             // [kFastP][64] first member offsets
+    const int64_t nleaf = A.nodes[L];
+    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
+    const int32_t *pm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
+    uint64_t k4[4];
+    for (int l = 2; l <= L; ++l) {
+        const bool leaf = l == L;
+        const int keep = keep_s;
+        const float *Cl = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * R;
+        const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
+        for (int j = wv; j < kFastP; j += 4) {
+            uint64_t key = 0;
+            if (j < keep && lane < b) {
+                const int64_t child = (int64_t)kept_s[j] * b + lane;
+                if (cn[child] > 0) {
+                    int e = 1;
+                    if (leaf) {
+                        const int32_t a0 = lo[child], a1 = lo[child + 1];
+                        // members ascend: all are eligible when the last one is
+                        e = (all_eligible || pm[a1 - 1] <= pos) ? a1 - a0 : count_le(pm + a0, a1 - a0, pos);
+                        eli[j * 64 + lane] = e;
+                        lof[j * 64 + lane] = a0;
+                    }
+                    if (e > 0) key = make_key_slot(score_row64(u_s, Cl + (size_t)child * R), (uint32_t)child, j * 64 + lane);
+                }
+            }
+            sk[j * 64 + lane] = key;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) k4[ii] = sk[4 * tid + ii];
+        block_sort1024_desc(k4, sk);
+        if (leaf) break;
+        // the first keep' = min(beam, #non-empty) sorted keys are the kept nodes
+        if (wv == 0) {
+            int c = 0;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int ps = 4 * lane + ii;
+                if (ps < P && k4[ii] != 0) { kept_s[ps] = (int32_t)slot_key_id(k4[ii]); ++c; }
+            }
+            c = wave_sum_i(c);
+            if (lane == 0) keep_s = c;
+        }
+        __syncthreads();
+    }
+
+    // ---- fill: leaves in sorted order, each giving its first eligible members
+    int e4[4], tot = 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
+        tot += e4[ii];
+    }
+    int total;
+    int off = block_excl_scan(tot, scratch, &total);
+    const int count = min(A.k, total);
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        if (e4[ii] > 0 && off < count) {
+            const int take = min(e4[ii], count - off);
+            const int32_t a0 = lof[(int)(k4[ii] & 1023u)];
+            for (int t = 0; t < take; ++t) out[off + t] = pm[a0 + t];
+            if (count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
+        }
+        off += e4[ii];
+    }
+    for (int t = count + tid; t < A.k; t += blockDim.x) out[t] = -1;
+    __syncthreads();
+    if (tid == 0) {
+        A.sel_count[(size_t)i * A.h_kv + g] = count;
+        if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
+    }
+}
+
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
                        int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
@@ -202,6 +372,12 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
     A.leaf_off_off = leaf_off_off; A.perm_off = perm_off; A.W = W; A.beam = beam; A.k = k;
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     const dim3 grid((unsigned)m, (unsigned)h_kv);
+    if (r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= (int64_t)1 << 22) {
+        const size_t shm = std::max(sizeof(float) * (size_t)d * kFastR, sizeof(uint64_t) * 1024 + sizeof(int32_t) * 2 * kFastP * 64);
+        if (dtype == 0) hipLaunchKernelGGL((k_select_fast<float>), grid, dim3(256), shm, st, A);
+        else hipLaunchKernelGGL((k_select_fast<bf16_t>), grid, dim3(256), shm, st, A);
+        return hipGetLastError();
+    }
     const int cmax = beam * b > b ? beam * b : b;
     const bool small = cmax <= 1024;
     if (dtype == 0) {
