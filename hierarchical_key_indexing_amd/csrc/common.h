@@ -221,6 +221,45 @@ LSA_DEV int wave_incl_scan_add(int v) {
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// Weighted radix selection over the 1024 64-bit keys of a 256-thread block
+// (four per thread, zero keys ignored), eight bits per round from the top:
+// returns the key T such that the keys > T weigh less than `want` and the
+// keys >= T weigh at least `want` (0 when all keys together weigh less).
+// `hist` holds 256 ints, `sel` 4.  Every thread gets the result.
+LSA_DEV uint64_t block_radix_select(const uint64_t (&k)[4], const int (&w)[4], int want, int *hist, int *sel) {
+    const int tid = threadIdx.x;
+    uint64_t prefix = 0, mask = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (k[i] != 0 && (k[i] & mask) == prefix && w[i] > 0) atomicAdd(&hist[(int)((k[i] >> shift) & 255u)], w[i]);
+        __syncthreads();
+        // thread t owns digit 255 - t: the weight of the larger digits is an
+        // exclusive scan in thread order
+        const int hv = hist[255 - tid];
+        const int wvv = tid / kWave;
+        const int incl = wave_incl_scan_add(hv);
+        if (lane_id() == kWave - 1) sel[wvv] = incl;
+        __syncthreads();
+        int before = incl - hv;
+        for (int q = 0; q < wvv; ++q) before += sel[q];
+        __syncthreads();
+        if (hv > 0 && before < want && before + hv >= want) { sel[0] = 255 - tid; sel[1] = want - before; }
+        if (tid == 255 && before + hv < want) { sel[0] = -1; }        // all keys weigh less than want
+        __syncthreads();
+        const int dg = sel[0];
+        if (dg < 0) return 0;
+        want = sel[1];
+        prefix |= (uint64_t)dg << shift;
+        mask |= (uint64_t)255 << shift;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+
 // Exclusive prefix sum over a block; returns the thread's exclusive prefix and
 // writes the block total to *total.  `scratch` holds >= blockDim/64 + 1 ints.
 LSA_DEV int block_excl_scan(int v, int *scratch, int *total) {

@@ -239,7 +239,8 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
     __shared__ __attribute__((aligned(16))) float qbar_s[256];
     __shared__ __attribute__((aligned(16))) float u_s[kFastR];
     __shared__ int32_t kept_s[kFastP];
-    __shared__ int keep_s, scratch[8];
+    __shared__ int keep_s, ncol_s, scratch[8], hist_s[256], sel_s[4];
+    __shared__ uint64_t col_s[kFastP];
     __shared__ float cut_s;
     constexpr int R = kFastR;
     const int64_t i = blockIdx.x;
@@ -316,18 +317,27 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
         __syncthreads();
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) k4[ii] = sk[4 * tid + ii];
-        block_sort1024_desc(k4, sk);
-        if (leaf) break;
-        // the first keep' = min(beam, #non-empty) sorted keys are the kept nodes
-        if (wv == 0) {
-            int c = 0;
+        if (leaf) {
+            block_sort1024_desc(k4, sk);
+            break;
+        }
+        // internal level: the beam-th largest key by radix selection, then the
+        // keys at or above it (min(beam, #non-empty) of them) ranked by one wave
+        const int one[4] = {1, 1, 1, 1};
+        const uint64_t thr = block_radix_select(k4, one, P, hist_s, sel_s);
+        if (tid == 0) ncol_s = 0;
+        __syncthreads();
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int ps = 4 * lane + ii;
-                if (ps < P && k4[ii] != 0) { kept_s[ps] = (int32_t)slot_key_id(k4[ii]); ++c; }
-            }
-            c = wave_sum_i(c);
-            if (lane == 0) keep_s = c;
+        for (int ii = 0; ii < 4; ++ii)
+            if (k4[ii] != 0 && k4[ii] >= thr) col_s[atomicAdd(&ncol_s, 1)] = k4[ii];
+        __syncthreads();
+        if (wv == 0) {
+            const int nk = ncol_s;
+            uint64_t key = lane < nk ? col_s[lane] : 0ull;
+            int pay = 0;
+            wave_sort_desc(key, pay);
+            if (lane < nk) kept_s[lane] = (int32_t)slot_key_id(key);
+            if (lane == 0) keep_s = nk;
         }
         __syncthreads();
     }
@@ -343,15 +353,29 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
     int off = block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
     int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+    // the thread's (up to) four leaves: the first 8 members of each are loaded
+    // in one round (clamped indices), longer leaves finish in a loop
+    constexpr int kC = 8;
+    int take[4], a0v[4], offv[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-        if (e4[ii] > 0 && off < count) {
-            const int take = min(e4[ii], count - off);
-            const int32_t a0 = lof[(int)(k4[ii] & 1023u)];
-            for (int t = 0; t < take; ++t) out[off + t] = pm[a0 + t];
-            if (count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
-        }
+        offv[ii] = off;
+        take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
+        a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
+        if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
         off += e4[ii];
+    }
+    int32_t mv[4][kC];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+        for (int t = 0; t < kC; ++t)
+            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
+        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
     }
     for (int t = count + tid; t < A.k; t += blockDim.x) out[t] = -1;
     __syncthreads();
