@@ -151,54 +151,55 @@ LSA_DEV void sort_stages(uint64_t &key, int &pay, int l) {
 }
 LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_stages<2, 1>(key, pay, lane_id()); }
 
-// Bitonic sort, descending, of the 1024 64-bit keys of a 256-thread block,
-// four per thread: thread t holds elements 4t..4t+3 before and after.
-// Exchanges between a thread's own elements stay in registers, between the
-// lanes of a wave they go through DPP / row swaps, and only the two strides
-// that cross waves (256, 512) go through LDS (`sk`, 1024 keys).
-template <int SIZE, int S>
-LSA_DEV void bsort_stage(uint64_t (&k)[4], int t0, uint64_t *sk) {
+// Bitonic sort, descending, of the 256 * KPT 64-bit keys of a 256-thread
+// block, KPT (1, 2 or 4) per thread: thread t holds elements KPT t ..
+// KPT t + KPT - 1 before and after.  Exchanges between a thread's own elements
+// stay in registers, between the lanes of a wave they go through DPP / row
+// swaps, and only strides that cross waves go through LDS (`sk`, 256 * KPT keys).
+template <int KPT, int SIZE, int S>
+LSA_DEV void bsort_stage(uint64_t (&k)[KPT], int t0, uint64_t *sk) {
     const int t = opaque(t0);
-    if constexpr (S < 4) {
+    if constexpr (S < KPT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < KPT; ++i) {
             if ((i & S) == 0) {
-                const bool desc = ((4 * t + i) & SIZE) == 0;   // lower element keeps the larger key
+                const bool desc = ((KPT * t + i) & SIZE) == 0;   // lower element keeps the larger key
                 const uint64_t a = k[i], b = k[i + S];
                 const bool sw = desc ? (b > a) : (a > b);
                 k[i] = sw ? b : a;
                 k[i + S] = sw ? a : b;
             }
         }
-    } else if constexpr (S < 256) {
+    } else if constexpr (S < 64 * KPT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * t + i;
-            const uint64_t o = xor_lane64<S / 4>(k[i]);
+        for (int i = 0; i < KPT; ++i) {
+            const int e = KPT * t + i;
+            const uint64_t o = xor_lane64<S / KPT>(k[i]);
             const bool want_gt = ((e & S) == 0) == ((e & SIZE) == 0);
             k[i] = (want_gt ? (o > k[i]) : (o < k[i])) ? o : k[i];
         }
     } else {
         __syncthreads();                 // earlier readers of sk are done
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sk[4 * t + i] = k[i];
+        for (int i = 0; i < KPT; ++i) sk[KPT * t + i] = k[i];
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * t + i;
+        for (int i = 0; i < KPT; ++i) {
+            const int e = KPT * t + i;
             const uint64_t o = sk[e ^ S];
             const bool want_gt = ((e & S) == 0) == ((e & SIZE) == 0);
             k[i] = (want_gt ? (o > k[i]) : (o < k[i])) ? o : k[i];
         }
     }
 }
-template <int SIZE, int S>
-LSA_DEV void bsort_stages(uint64_t (&k)[4], int t, uint64_t *sk) {
-    bsort_stage<SIZE, S>(k, t, sk);
-    if constexpr (S > 1) bsort_stages<SIZE, S / 2>(k, t, sk);
-    else if constexpr (SIZE < 1024) bsort_stages<SIZE * 2, SIZE>(k, t, sk);
+template <int KPT, int SIZE, int S>
+LSA_DEV void bsort_stages(uint64_t (&k)[KPT], int t, uint64_t *sk) {
+    bsort_stage<KPT, SIZE, S>(k, t, sk);
+    if constexpr (S > 1) bsort_stages<KPT, SIZE, S / 2>(k, t, sk);
+    else if constexpr (SIZE < 256 * KPT) bsort_stages<KPT, SIZE * 2, SIZE>(k, t, sk);
 }
-LSA_DEV void block_sort1024_desc(uint64_t (&k)[4], uint64_t *sk) { bsort_stages<2, 1>(k, (int)threadIdx.x, sk); }
+template <int KPT>
+LSA_DEV void block_sort_desc(uint64_t (&k)[KPT], uint64_t *sk) { bsort_stages<KPT, 2, 1>(k, (int)threadIdx.x, sk); }
 
 // Inclusive prefix sum over the 64 lanes: scans of the four 16-lane rows with
 // DPP row shifts (a lane with no source adds 0), then each row adds the

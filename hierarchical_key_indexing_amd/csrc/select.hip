@@ -230,6 +230,50 @@ LSA_DEV float score_row64(const float *u, const float *__restrict__ row) {
     return (float)s;
 }
 
+// Sorts the 256 * KPT leaf keys in sk (descending) and writes, for each leaf
+// in that order, its first eligible members at its retrieval offset, up to
+// `count` keys (the first 8 members of each of a thread's leaves are loaded in
+// one round; longer leaves finish in a loop).  Sets *cut to the score of the
+// leaf that supplies key k - 1 when count == k.
+template <int KPT>
+LSA_DEV void fill_sorted(uint64_t *sk, const int32_t *eli, const int32_t *lof, const int32_t *__restrict__ pm,
+                         int count, int k, int32_t *out, float *cut, int *scratch) {
+    uint64_t kk[KPT];
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) kk[ii] = sk[KPT * threadIdx.x + ii];
+    block_sort_desc<KPT>(kk, sk);
+    int e[KPT], tot = 0;
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) {
+        e[ii] = (kk[ii] != 0) ? eli[(int)(kk[ii] & 1023u)] : 0;
+        tot += e[ii];
+    }
+    int total;
+    int off = block_excl_scan(tot, scratch, &total);
+    constexpr int kC = 8;
+    int take[KPT], a0v[KPT], offv[KPT];
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) {
+        offv[ii] = off;
+        take[ii] = (e[ii] > 0 && off < count) ? min(e[ii], count - off) : 0;
+        a0v[ii] = take[ii] > 0 ? lof[(int)(kk[ii] & 1023u)] : 0;
+        if (take[ii] > 0 && count == k && off + e[ii] >= k) *cut = key_score(kk[ii]);
+        off += e[ii];
+    }
+    int32_t mv[KPT][kC];
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii)
+#pragma unroll
+        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) {
+#pragma unroll
+        for (int t = 0; t < kC; ++t)
+            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
+        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
+    }
+}
+
 constexpr int kFastP = 16;          // beam limit of the throughput path
 constexpr int kFastR = 64;          // latent dimension of the throughput path
 
@@ -317,10 +361,7 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
         __syncthreads();
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) k4[ii] = sk[4 * tid + ii];
-        if (leaf) {
-            block_sort1024_desc(k4, sk);
-            break;
-        }
+        if (leaf) break;
         // internal level: the beam-th largest key by radix selection, then the
         // keys at or above it (min(beam, #non-empty) of them) ranked by one wave
         const int one[4] = {1, 1, 1, 1};
@@ -342,41 +383,33 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
         __syncthreads();
     }
 
-    // ---- fill: leaves in sorted order, each giving its first eligible members
-    int e4[4], tot = 0;
+    // ---- fill.  The leaf holding retrieval position count - 1 is found by a
+    // radix selection weighted by the eligible counts; only the leaves at or
+    // above it are sorted, then each gives its first eligible members.
+    int w4[4], tot = 0;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-        e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
-        tot += e4[ii];
+        w4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
+        tot += w4[ii];
     }
     int total;
-    int off = block_excl_scan(tot, scratch, &total);
+    (void)block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
-    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
-    // the thread's (up to) four leaves: the first 8 members of each are loaded
-    // in one round (clamped indices), longer leaves finish in a loop
-    constexpr int kC = 8;
-    int take[4], a0v[4], offv[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        offv[ii] = off;
-        take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
-        a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
-        if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
-        off += e4[ii];
-    }
-    int32_t mv[4][kC];
+    const uint64_t thr = count > 0 ? block_radix_select(k4, w4, count, hist_s, sel_s) : ~0ull;
+    if (tid == 0) ncol_s = 0;
+    __syncthreads();
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-#pragma unroll
-        for (int t = 0; t < kC; ++t)
-            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
-        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
-    }
+        if (w4[ii] > 0 && k4[ii] >= thr) sk[atomicAdd(&ncol_s, 1)] = k4[ii];
+    __syncthreads();
+    const int nsel = ncol_s;
+    const int kpt = nsel <= 256 ? 1 : nsel <= 512 ? 2 : 4;
+    for (int e = nsel + tid; e < 256 * kpt; e += blockDim.x) sk[e] = 0ull;
+    __syncthreads();
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+    if (kpt == 1) fill_sorted<1>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
+    else if (kpt == 2) fill_sorted<2>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
+    else fill_sorted<4>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
     for (int t = count + tid; t < A.k; t += blockDim.x) out[t] = -1;
     __syncthreads();
     if (tid == 0) {
