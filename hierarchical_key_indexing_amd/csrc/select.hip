@@ -211,74 +211,36 @@ LSA_DEV uint64_t make_key_slot(float score, uint32_t id, int slot) {
 LSA_DEV uint32_t slot_key_id(uint64_t k) { return ~(uint32_t)(k >> 10) & 0x3FFFFFu; }
 
 // u . row (64 floats) in double, ascending index; the row comes straight from
-// global memory (16 loads issued before the first FMA), u from LDS.
+// global memory in two halves (each half's 8 loads issued before its FMAs),
+// u from LDS.  Halves keep fewer registers live, so more waves stay resident.
 LSA_DEV float score_row64(const float *u, const float *__restrict__ row) {
     const f4_t *r4 = reinterpret_cast<const f4_t *>(row);
     const f4_t *u4 = reinterpret_cast<const f4_t *>(u) + opaque(0);   // u read at each use, not kept live
-    f4_t v[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) v[x] = r4[x];
     double s = 0.0;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-        const f4_t a = u4[x];
-        s = fma((double)a.x, (double)v[x].x, s);
-        s = fma((double)a.y, (double)v[x].y, s);
-        s = fma((double)a.z, (double)v[x].z, s);
-        s = fma((double)a.w, (double)v[x].w, s);
+    for (int h = 0; h < 2; ++h) {
+        f4_t v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = r4[8 * h + x];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const f4_t a = u4[8 * h + x];
+            s = fma((double)a.x, (double)v[x].x, s);
+            s = fma((double)a.y, (double)v[x].y, s);
+            s = fma((double)a.z, (double)v[x].z, s);
+            s = fma((double)a.w, (double)v[x].w, s);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     return (float)s;
 }
 
-// Sorts the 256 * KPT leaf keys in sk (descending) and writes, for each leaf
-// in that order, its first eligible members at its retrieval offset, up to
-// `count` keys (the first 8 members of each of a thread's leaves are loaded in
-// one round; longer leaves finish in a loop).  Sets *cut to the score of the
-// leaf that supplies key k - 1 when count == k.
-template <int KPT>
-LSA_DEV void fill_sorted(uint64_t *sk, const int32_t *eli, const int32_t *lof, const int32_t *__restrict__ pm,
-                         int count, int k, int32_t *out, float *cut, int *scratch) {
-    uint64_t kk[KPT];
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii) kk[ii] = sk[KPT * threadIdx.x + ii];
-    block_sort_desc<KPT>(kk, sk);
-    int e[KPT], tot = 0;
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii) {
-        e[ii] = (kk[ii] != 0) ? eli[(int)(kk[ii] & 1023u)] : 0;
-        tot += e[ii];
-    }
-    int total;
-    int off = block_excl_scan(tot, scratch, &total);
-    constexpr int kC = 8;
-    int take[KPT], a0v[KPT], offv[KPT];
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii) {
-        offv[ii] = off;
-        take[ii] = (e[ii] > 0 && off < count) ? min(e[ii], count - off) : 0;
-        a0v[ii] = take[ii] > 0 ? lof[(int)(kk[ii] & 1023u)] : 0;
-        if (take[ii] > 0 && count == k && off + e[ii] >= k) *cut = key_score(kk[ii]);
-        off += e[ii];
-    }
-    int32_t mv[KPT][kC];
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii)
-#pragma unroll
-        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii) {
-#pragma unroll
-        for (int t = 0; t < kC; ++t)
-            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
-        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
-    }
-}
-
 constexpr int kFastP = 16;          // beam limit of the throughput path
 constexpr int kFastR = 64;          // latent dimension of the throughput path
+constexpr int kWRows = 64;          // rows of W staged at a time (16 KB)
 
 template <typename T>
-__global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
+__global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     extern __shared__ __attribute__((aligned(16))) float dynf[];   // W_g, then keys and leaf tables
     __shared__ __attribute__((aligned(16))) float qbar_s[256];
     __shared__ __attribute__((aligned(16))) float u_s[kFastR];
@@ -295,21 +257,25 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
     const int32_t pos = A.q_pos[i];
     const bool all_eligible = pos >= A.n - 1;
 
-    // ---- group latent query
-    float *Wl = dynf;                                   // [d][R]
-    g2s_rows<8>(Wl, d * R, A.W + (size_t)g * d * R, d * R, d * R);
+    // ---- group latent query.  W_g is staged in LDS 64 input rows (16 KB) at
+    // a time; the sum over the input dimension continues in order across them.
+    float *Wl = dynf;                                   // [64][R]
     for (int t = tid; t < d; t += blockDim.x) {
         double s = 0.0;
         for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
         qbar_s[t] = (float)(s / (double)G);
     }
     if (tid == 0) cut_s = -INFINITY;
-    __syncthreads();
-    if (tid < R) {
-        double s = 0.0;
-        for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)Wl[t * R + tid], s);
-        u_s[tid] = (float)s;
+    double us = 0.0;
+    for (int t0 = 0; t0 < d; t0 += kWRows) {
+        const int nt = min(kWRows, d - t0);
+        g2s_rows<4>(Wl, nt * R, A.W + ((size_t)g * d + t0) * R, nt * R, nt * R);
+        __syncthreads();
+        if (tid < R)
+            for (int t = 0; t < nt; ++t) us = fma((double)qbar_s[t0 + t], (double)Wl[t * R + tid], us);
+        __syncthreads();
     }
+    if (tid < R) u_s[tid] = (float)us;
     __syncthreads();
 
     // ---- level 1: the root's non-empty children, best min(beam, #) kept
@@ -361,7 +327,10 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
         __syncthreads();
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) k4[ii] = sk[4 * tid + ii];
-        if (leaf) break;
+        if (leaf) {
+            block_sort_desc<4>(k4, sk);
+            break;
+        }
         // internal level: the beam-th largest key by radix selection, then the
         // keys at or above it (min(beam, #non-empty) of them) ranked by one wave
         const int one[4] = {1, 1, 1, 1};
@@ -383,33 +352,41 @@ __global__ __launch_bounds__(256, 4) void k_select_fast(SelectArgs A) {
         __syncthreads();
     }
 
-    // ---- fill.  The leaf holding retrieval position count - 1 is found by a
-    // radix selection weighted by the eligible counts; only the leaves at or
-    // above it are sorted, then each gives its first eligible members.
-    int w4[4], tot = 0;
+    // ---- fill: leaves in sorted order, each giving its first eligible members
+    int e4[4], tot = 0;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-        w4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
-        tot += w4[ii];
+        e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
+        tot += e4[ii];
     }
     int total;
-    (void)block_excl_scan(tot, scratch, &total);
+    int off = block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
-    const uint64_t thr = count > 0 ? block_radix_select(k4, w4, count, hist_s, sel_s) : ~0ull;
-    if (tid == 0) ncol_s = 0;
-    __syncthreads();
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+    // the thread's (up to) four leaves: the first 8 members of each are loaded
+    // in one round (clamped indices), longer leaves finish in a loop
+    constexpr int kC = 4;
+    int take[4], a0v[4], offv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        offv[ii] = off;
+        take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
+        a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
+        if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
+        off += e4[ii];
+    }
+    int32_t mv[4][kC];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-        if (w4[ii] > 0 && k4[ii] >= thr) sk[atomicAdd(&ncol_s, 1)] = k4[ii];
-    __syncthreads();
-    const int nsel = ncol_s;
-    const int kpt = nsel <= 256 ? 1 : nsel <= 512 ? 2 : 4;
-    for (int e = nsel + tid; e < 256 * kpt; e += blockDim.x) sk[e] = 0ull;
-    __syncthreads();
-    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
-    if (kpt == 1) fill_sorted<1>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
-    else if (kpt == 2) fill_sorted<2>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
-    else fill_sorted<4>(sk, eli, lof, pm, count, A.k, out, &cut_s, scratch);
+#pragma unroll
+        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+        for (int t = 0; t < kC; ++t)
+            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
+        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
+    }
     for (int t = count + tid; t < A.k; t += blockDim.x) out[t] = -1;
     __syncthreads();
     if (tid == 0) {
@@ -430,7 +407,7 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     const dim3 grid((unsigned)m, (unsigned)h_kv);
     if (r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= (int64_t)1 << 22) {
-        const size_t shm = std::max(sizeof(float) * (size_t)d * kFastR, sizeof(uint64_t) * 1024 + sizeof(int32_t) * 2 * kFastP * 64);
+        const size_t shm = std::max(sizeof(float) * (size_t)kWRows * kFastR, sizeof(uint64_t) * 1024 + sizeof(int32_t) * 2 * kFastP * 64);
         if (dtype == 0) hipLaunchKernelGGL((k_select_fast<float>), grid, dim3(256), shm, st, A);
         else hipLaunchKernelGGL((k_select_fast<bf16_t>), grid, dim3(256), shm, st, A);
         return hipGetLastError();
