@@ -51,7 +51,7 @@ def lib():
         L.oracle_build.argtypes = [P, i64, i32, i32, P, i32, i32, i32, i32, P, P, P, P]
         L.oracle_build.restype = i32
         L.oracle_select.argtypes = [P, i64, i32, i32, P, i64, i32, i32, i32, i32,
-                                    P, P, P, P, P, i32, i32, P, P, P, P, P]
+                                    P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_select.restype = i32
         L.oracle_attend.argtypes = [P, P, P, i64, i32, i32, i64, i32, P, P, i32, dbl, P, P]
         L.oracle_attend.restype = i32
@@ -144,21 +144,22 @@ def build_index(K: np.ndarray, W: np.ndarray, b: int, L: int, T: int = 5) -> Ind
 
 
 def select(Q: np.ndarray, pos: np.ndarray, index: Index, W: np.ndarray, beam: int, k: int,
-           want_kept: bool = False):
-    """Q [m, h_q, d] float32, pos [m] int32.  Returns dict with sel [m, h_kv, k],
+           want_kept: bool = False, n_sink: int = 0, window: int = 0):
+    """Q [m, h_q, d] float32, pos [m] int32.  Returns dict with sel [m, h_kv,
+    k + n_sink + window] (retrieved keys, then sinks, then window, -1 padded),
     count [m, h_kv], cutoff [m, h_kv], nscored [m, h_kv] and optionally kept
     [m, h_kv, L-1, beam]."""
     Q = _c(Q, np.float32); pos = _c(pos, np.int32); W = _c(W, np.float32)
     m, h_q, d = Q.shape
     ix = index
-    sel = np.empty((m, ix.h_kv, k), np.int32)
+    sel = np.empty((m, ix.h_kv, k + n_sink + window), np.int32)
     cnt = np.empty((m, ix.h_kv), np.int32)
     cut = np.empty((m, ix.h_kv), np.float32)
     nsc = np.empty((m, ix.h_kv), np.int64)
     kept = np.empty((m, ix.h_kv, max(ix.L - 1, 1), beam), np.int32) if want_kept else None
     lib().oracle_select(_p(Q), m, h_q, d, _p(pos), ix.n, ix.h_kv, ix.r, ix.b, ix.L,
                         _p(ix.C_all), _p(ix.cnt_all), _p(ix.leaf_off), _p(ix.perm), _p(W),
-                        beam, k, _p(sel), _p(cnt), _p(cut), _p(kept), _p(nsc))
+                        beam, k, n_sink, window, _p(sel), _p(cnt), _p(cut), _p(kept), _p(nsc))
     out = dict(sel=sel, count=cnt, cutoff=cut, nscored=nsc)
     if want_kept:
         out["kept"] = kept

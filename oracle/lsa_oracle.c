@@ -204,9 +204,20 @@ int oracle_build(const float *K, int64_t n, int h_kv, int d, const float *W, int
  *     members in ascending position; keys at positions > pos are skipped
  *     (a key at the query's own position is visible); the first k are taken;
  *   - sel lists the taken keys in the order they were retrieved (leaf order,
- *     then ascending position inside a leaf), padded with -1; cutoff is the
- *     score of the leaf holding the k-th taken key, -inf when fewer than k
- *     keys were available.
+ *     then ascending position inside a leaf); cutoff is the score of the leaf
+ *     holding the k-th taken key, -inf when fewer than k keys were available.
+ *
+ * Sinks and window (bdtechtalks.com, "How latent sparse attention works": the
+ * retrieved keys are joined by a window of recent tokens and a few initial
+ * sink tokens).  Readings: with hi = min(pos, n - 1) the latest key the query
+ * sees, the sinks are the keys [0, min(n_sink, hi + 1)) and the window is the
+ * `window` latest visible keys that are not sinks, [max(n_sink, hi - window +
+ * 1), hi]; retrieval skips both, so it only takes keys in [n_sink, hi -
+ * window] and still takes up to k of them.  The three parts are disjoint and
+ * their union is the attention set.  A row of sel holds k + n_sink + window
+ * entries: the retrieved keys, then the sinks ascending, then the window
+ * ascending, padded with -1; count is the number of entries before the
+ * padding.  n_sink = window = 0 is the plain retrieval above.
  * Optional outputs (may be NULL): kept [m][h_kv][L-1][beam] (ids, -1 padded, in
  * rank order), nscored [m][h_kv] (number of centroids scored). */
 typedef struct { float s; int64_t id; } cand_t;
@@ -229,7 +240,7 @@ static float score_row(const float *u, const float *c, int r)
 int oracle_select(const float *Q, int64_t m, int h_q, int d, const int32_t *pos,
                   int64_t n, int h_kv, int r, int b, int L,
                   const float *C_all, const int64_t *cnt_all, const int64_t *leaf_off,
-                  const int32_t *perm, const float *W, int beam, int k,
+                  const int32_t *perm, const float *W, int beam, int k, int n_sink, int window,
                   int32_t *sel, int32_t *sel_count, float *cutoff,
                   int32_t *kept, int64_t *nscored)
 {
@@ -285,21 +296,29 @@ int oracle_select(const float *Q, int64_t m, int h_q, int d, const int32_t *pos,
                 F = nx;
                 nf = nn;
             }
-            /* fill: leaves in (score desc, id asc) order, members ascending */
-            int32_t *out = sel + (i * h_kv + g) * (int64_t)k;
+            /* fill: leaves in (score desc, id asc) order, members ascending,
+             * only keys in [n_sink, hi - window] */
+            const int64_t row = (int64_t)k + n_sink + window;
+            int32_t *out = sel + (i * h_kv + g) * row;
             const int64_t *lo = leaf_off + (int64_t)g * (nleaf + 1);
             const int32_t *pm = perm + (int64_t)g * n;
+            const int64_t hi = (int64_t)pos[i] < n - 1 ? (int64_t)pos[i] : n - 1;
             int64_t taken = 0;
             float cut = -INFINITY;
             for (int64_t t = 0; t < nf && taken < k; ++t) {
                 for (int64_t p = lo[F[t].id]; p < lo[F[t].id + 1] && taken < k; ++p) {
-                    if (pm[p] > pos[i]) continue;
+                    if (pm[p] < n_sink || pm[p] > hi - window) continue;
                     out[taken++] = pm[p];
                     if (taken == k) cut = F[t].s;
                 }
             }
-            for (int64_t t = taken; t < k; ++t) out[t] = -1;
-            sel_count[i * h_kv + g] = (int32_t)taken;
+            int64_t filled = taken;
+            /* sinks, then the window */
+            for (int64_t j = 0; j < n_sink && j <= hi; ++j) out[filled++] = (int32_t)j;
+            for (int64_t j = (hi - window + 1 > n_sink ? hi - window + 1 : n_sink); j <= hi; ++j)
+                out[filled++] = (int32_t)j;
+            for (int64_t t = filled; t < row; ++t) out[t] = -1;
+            sel_count[i * h_kv + g] = (int32_t)filled;
             if (cutoff) cutoff[i * h_kv + g] = cut;
             if (nscored) nscored[i * h_kv + g] = scored;
             free(F); free(qbar); free(u);

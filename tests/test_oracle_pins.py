@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from _ref import brute_select, check_tree, fl32, node_members, ulp_diff
+from _ref import brute_select, check_tree, fl32, group_latent, node_members, ulp_diff
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -43,7 +43,8 @@ def test_hand_worked_tree_and_selection(oracle_lib):
     for q in g["queries"]:
         ix = trees[q["tree"]]
         Q = np.array(q["q"], np.float32)[None, None]
-        out = oracle.select(Q, np.array([q["pos"]], np.int32), ix, W, q["beam"], q["k"])
+        out = oracle.select(Q, np.array([q["pos"]], np.int32), ix, W, q["beam"], q["k"],
+                            n_sink=q.get("n_sink", 0), window=q.get("window", 0))
         assert list(out["sel"][0, 0]) == q["sel"]
         assert out["count"][0, 0] == q["count"]
         assert out["cutoff"][0, 0] == _frac32(q["cutoff"])
@@ -279,3 +280,73 @@ def test_dense_equivalence(oracle_lib, shape):
     mask = np.broadcast_to((keys[None, :] <= pos[:, None])[:, None, :], (len(pos), w.h_q, w.n)).copy()
     ref = _sdpa_masked(Q, K, V, mask, 1.0 / np.sqrt(w.d))
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- sinks and window
+_LOCAL = [(0, 0), (4, 0), (0, 16), (3, 25), (50, 700), (1, 1)]
+
+
+@pytest.mark.parametrize("n_sink,window", _LOCAL)
+def test_local_keys_filter_the_plain_retrieval_order(oracle_lib, n_sink, window):
+    """With sinks and a window, the retrieved part is the plain retrieval order
+    (no local keys, k = n: the whole walk over the candidate leaves) restricted
+    to [n_sink, hi - window], cut at k; the rest of the row is the sinks, then
+    the window, each ascending; the parts are disjoint."""
+    w, K, V, W, Q, pos = _small_case(b=4, L=3, seed=31, m=8)
+    ix = oracle.build_index(K, W, 4, 3, 5)
+    beam, k = 2, 37
+    walk = oracle.select(Q, pos, ix, W, beam, w.n)
+    out = oracle.select(Q, pos, ix, W, beam, k, n_sink=n_sink, window=window)
+    assert out["sel"].shape[2] == k + n_sink + window
+    for i, p in enumerate(pos):
+        hi = min(int(p), w.n - 1)
+        sinks = list(range(0, min(n_sink, hi + 1)))
+        win = list(range(max(n_sink, hi - window + 1), hi + 1))
+        for g in range(w.h_kv):
+            full = walk["sel"][i, g, :walk["count"][i, g]]
+            ret = [int(j) for j in full if n_sink <= j <= hi - window][:k]
+            c = out["count"][i, g]
+            row = list(out["sel"][i, g])
+            assert c == len(ret) + len(sinks) + len(win)
+            assert row[:c] == ret + sinks + win
+            assert all(x == -1 for x in row[c:])
+            assert len(set(row[:c])) == c
+            # the latest min(window, hi + 1) visible keys are all attended
+            assert set(range(max(0, hi - window + 1), hi + 1)) <= set(row[:c])
+            if len(ret) == k:
+                # the score of the leaf that holds the k-th retrieved key
+                u = group_latent(Q[i], W, g, w.h_q // w.h_kv).astype(np.float64)
+                lo = ix.leaf_off[g]
+                leaf = int(np.searchsorted(lo, np.nonzero(ix.perm[g] == ret[-1])[0][0], side="right") - 1)
+                assert out["cutoff"][i, g] == fl32(ix.C(3)[g][leaf].astype(np.float64) @ u)
+            else:
+                assert np.isneginf(out["cutoff"][i, g])
+
+
+@pytest.mark.parametrize("n_sink,window", [(3, 10), (0, 64), (200, 1)])
+def test_dense_equivalence_with_local_keys(oracle_lib, n_sink, window):
+    """beam covering every cluster and k = n: sinks, window and retrieved keys
+    together are every visible key once, so attention is dense causal."""
+    b, L = 3, 3
+    w, K, V, W, Q, pos = _small_case(b=b, L=L, seed=41, m=8)
+    ix = oracle.build_index(K, W, b, L, 5)
+    out = oracle.select(Q, pos, ix, W, beam=b ** (L - 1), k=w.n, n_sink=n_sink, window=window)
+    o, _ = oracle.attend(Q, K, V, out["sel"], out["count"])
+    keys = np.arange(w.n)
+    mask = np.broadcast_to((keys[None, :] <= pos[:, None])[:, None, :], (len(pos), w.h_q, w.n)).copy()
+    ref = _sdpa_masked(Q, K, V, mask, 1.0 / np.sqrt(w.d))
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_window_covering_the_context_is_dense_whatever_the_index(oracle_lib):
+    """A window at least as long as the visible context leaves nothing to
+    retrieve: any beam and k give dense causal attention."""
+    w, K, V, W, Q, pos = _small_case(b=4, L=2, seed=43, m=6)
+    ix = oracle.build_index(K, W, 4, 2, 5)
+    out = oracle.select(Q, pos, ix, W, beam=1, k=3, n_sink=2, window=w.n)
+    o, _ = oracle.attend(Q, K, V, out["sel"], out["count"])
+    keys = np.arange(w.n)
+    mask = np.broadcast_to((keys[None, :] <= pos[:, None])[:, None, :], (len(pos), w.h_q, w.n)).copy()
+    ref = _sdpa_masked(Q, K, V, mask, 1.0 / np.sqrt(w.d))
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(out["cutoff"]))
