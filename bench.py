@@ -222,6 +222,82 @@ def extra_train(lsa, synth, torch, np, dev, w, reps=3):
             "timing": f"build + select + attend of all {m} positions, mean of {reps} forwards"}
 
 
+LOCAL_SINKS, LOCAL_WINDOW = 4, 512
+
+
+def local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc, reps=4):
+    """The decode layers again with LOCAL_SINKS sink tokens and a LOCAL_WINDOW
+    recent window joined to the retrieved keys: all layers back to back in one
+    HIP graph (per-layer time), plus the 4096-row last chunk of layer 0."""
+    ns, nw = LOCAL_SINKS, LOCAL_WINDOW
+    m = pos.shape[0]
+    row = w.k + ns + nw
+    sel = torch.empty((m, w.h_kv, row), dtype=torch.int32, device=dev)
+    cnt = torch.empty((m, w.h_kv), dtype=torch.int32, device=dev)
+    out = torch.empty_like(layers[0]["Q"])
+    lse = torch.empty((m, w.h_q), dtype=torch.float32, device=dev)
+    ws = lsa.workspace(lsa.select_attend_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k, ns, nw), dev)
+
+    def run():
+        for a in layers:
+            lsa.select_attend(a["Q"], a["K"], a["V"], pos, a["index"], desc, a["W"], w.beam, w.k, sel=sel,
+                              sel_count=cnt, out=out, lse=lse, want_cutoff=False, ws=ws, n_sink=ns, window=nw)
+    run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    e = _events(torch, 2)
+    e[0].record()
+    for _ in range(reps):
+        g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    res = {"n_sink": ns, "window": nw,
+           "decode_us_per_layer": round(e[0].elapsed_time(e[1]) * 1e3 / (reps * len(layers)), 3),
+           "decode_mean_sel_count": float(cnt.float().mean()),
+           "timing": f"{len(layers)} distinct decode layers in one HIP graph, {reps} replays"}
+    del g
+    if w.name == "decode_1m":
+        import synth
+        wp = synth.WORKLOADS["prefill_1m"]
+        a = layers[0]
+        ppos = torch.arange(w.n - 4096, w.n, dtype=torch.int32, device=dev)
+        Qp = synth.make_queries(wp, a["K"], ppos)
+        mp = 4096
+        psel = torch.empty((mp, w.h_kv, row), dtype=torch.int32, device=dev)
+        pcnt = torch.empty((mp, w.h_kv), dtype=torch.int32, device=dev)
+        pout = torch.empty_like(Qp)
+        pws = torch.empty(max(lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, row), 1), dtype=torch.uint8,
+                          device=dev)
+        sel_call = lambda: lsa.select(Qp, ppos, a["index"], desc, a["W"], w.beam, w.k, sel=psel, sel_count=pcnt,
+                                      want_cutoff=False, ws=None, n_sink=ns, window=nw)
+        att_call = lambda: lsa.attend(Qp, a["K"], a["V"], psel, pcnt, out=pout, want_lse=False, ws=pws)
+        for _ in range(2):
+            sel_call(); att_call()
+        torch.cuda.synchronize()
+        npre = 5
+        e = _events(torch, 3)
+        e[0].record()
+        for _ in range(npre):
+            sel_call()
+        e[1].record()
+        for _ in range(npre):
+            att_call()
+        e[2].record()
+        torch.cuda.synchronize()
+        ps, pa = e[0].elapsed_time(e[1]) / npre, e[1].elapsed_time(e[2]) / npre
+        res.update({"prefill_queries_per_s": round(mp / ((ps + pa) * 1e-3), 1), "prefill_select_ms": round(ps, 4),
+                    "prefill_attend_ms": round(pa, 4), "prefill_mean_sel_count": float(pcnt.float().mean())})
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +543,10 @@ def main():
             "attend_GBps_algorithmic": round(attend_bytes(w, mp, pc) / (pa * 1e-3) / 1e9, 2),
             "attend_tflops": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pa * 1e-3) / 1e12, 3)}
         del Qp, psel, pcnt, pout, pws
+
+    if not args.no_extra:
+        log("sinks and window")
+        breakdown["sinks_window"] = local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc)
 
     cpu = None
     if not args.no_cpu:

@@ -64,11 +64,11 @@ def lib():
         L.lsa_index_layout.argtypes = [i64, i32, i32, i32, i32, D]
         L.lsa_build_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_build_index.argtypes = [P, i32, i64, i32, i32, P, i32, i32, i32, i32, P, i64, P, i64, D, P]
-        L.lsa_select_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, ctypes.POINTER(i64)]
-        L.lsa_select_attend_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, ctypes.POINTER(i64)]
-        L.lsa_select_attend.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, ctypes.c_float,
+        L.lsa_select_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select_attend_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_select_attend.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, ctypes.c_float,
                                         P, P, P, P, P, P, i64, P]
-        L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, P, P, P, P, i64, P]
+        L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, P, P, P, P, i64, P]
         L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_attend.argtypes = [P, P, P, i32, i64, i32, i32, i64, i32, P, P, i32, ctypes.c_float,
                                  P, P, P, i64, P]
@@ -108,6 +108,15 @@ def _need(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_out(t: Optional[torch.Tensor], name: str, shape, dtype):
+    """A caller-provided output: device, contiguous, of exactly this shape and dtype."""
+    if t is None:
+        return
+    _need(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 # ------------------------------------------------------------------ layout
 def index_layout(n: int, h_kv: int, r: int, b: int, L: int) -> IndexDesc:
     d = IndexDesc()
@@ -121,16 +130,20 @@ def build_workspace_bytes(n: int, h_kv: int, d: int, r: int, b: int, L: int) -> 
     return v.value
 
 
-def select_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int) -> int:
+def select_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int,
+                           n_sink: int = 0, window: int = 0) -> int:
     v = ctypes.c_int64()
-    _check(lib().lsa_select_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, ctypes.byref(v)),
+    _check(lib().lsa_select_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, n_sink, window,
+                                            ctypes.byref(v)),
            "lsa_select_workspace_bytes")
     return v.value
 
 
-def select_attend_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int) -> int:
+def select_attend_workspace_bytes(m: int, h_q: int, d: int, desc: IndexDesc, beam: int, k: int,
+                                  n_sink: int = 0, window: int = 0) -> int:
     v = ctypes.c_int64()
-    _check(lib().lsa_select_attend_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, ctypes.byref(v)),
+    _check(lib().lsa_select_attend_workspace_bytes(m, h_q, d, ctypes.byref(desc), beam, k, n_sink, window,
+                                                   ctypes.byref(v)),
            "lsa_select_attend_workspace_bytes")
     return v.value
 
@@ -192,8 +205,10 @@ _NO_WS = object()
 
 def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: IndexDesc, W: torch.Tensor,
            beam: int, k: int, sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
-           cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, ws=_NO_WS, stream=None):
-    """Q [m, h_q, d], q_pos int32 [m] -> (sel int32 [m, h_kv, k], count int32 [m, h_kv], cutoff f32 [m, h_kv]).
+           cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, ws=_NO_WS, stream=None,
+           n_sink: int = 0, window: int = 0):
+    """Q [m, h_q, d], q_pos int32 [m] -> (sel int32 [m, h_kv, k + n_sink + window], count int32 [m, h_kv],
+    cutoff f32 [m, h_kv]).  A row of sel: retrieved keys, then the sinks and the window.
 
     ws: None runs one workgroup per (row, KV head); a zero-filled workspace of
     select_workspace_bytes lets small batches use the multi-workgroup kernel
@@ -203,15 +218,18 @@ def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: Inde
     h = desc.h_kv
     dev = Q.device
     if sel is None:
-        sel = torch.empty((m, h, k), dtype=torch.int32, device=dev)
+        sel = torch.empty((m, h, k + n_sink + window), dtype=torch.int32, device=dev)
     if sel_count is None:
         sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
     if cutoff is None and want_cutoff:
         cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    _need_out(sel, "sel", (m, h, k + n_sink + window), torch.int32)
+    _need_out(sel_count, "sel_count", (m, h), torch.int32)
+    _need_out(cutoff, "cutoff", (m, h), torch.float32)
     if ws is _NO_WS:
-        ws = workspace(select_workspace_bytes(m, h_q, d, desc, beam, k), dev)
+        ws = workspace(select_workspace_bytes(m, h_q, d, desc, beam, k, n_sink, window), dev)
     _check(lib().lsa_select(_ptr(Q), _dtype_code(Q), m, h_q, d, _ptr(q_pos), ctypes.byref(desc), _ptr(index),
-                            _ptr(W), beam, k, _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(ws),
+                            _ptr(W), beam, k, n_sink, window, _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_select")
     return sel, sel_count, cutoff
@@ -222,7 +240,7 @@ def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
                   sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
                   cutoff: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                   lse: Optional[torch.Tensor] = None, want_cutoff: bool = True, want_lse: bool = True,
-                  ws: Optional[torch.Tensor] = None, stream=None):
+                  ws: Optional[torch.Tensor] = None, stream=None, n_sink: int = 0, window: int = 0):
     """lsa_select + lsa_attend (one launch for small batches) -> (sel, count, cutoff, out, lse)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (q_pos, "q_pos"), (W, "W")):
         _need(t, nm)
@@ -230,7 +248,7 @@ def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
     h = desc.h_kv
     dev = Q.device
     if sel is None:
-        sel = torch.empty((m, h, k), dtype=torch.int32, device=dev)
+        sel = torch.empty((m, h, k + n_sink + window), dtype=torch.int32, device=dev)
     if sel_count is None:
         sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
     if cutoff is None and want_cutoff:
@@ -239,10 +257,16 @@ def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
         out = torch.empty_like(Q)
     if lse is None and want_lse:
         lse = torch.empty((m, h_q), dtype=torch.float32, device=dev)
+    _need_out(sel, "sel", (m, h, k + n_sink + window), torch.int32)
+    _need_out(sel_count, "sel_count", (m, h), torch.int32)
+    _need_out(cutoff, "cutoff", (m, h), torch.float32)
+    _need_out(out, "out", (m, h_q, d), Q.dtype)
+    _need_out(lse, "lse", (m, h_q), torch.float32)
     if ws is None:
-        ws = workspace(select_attend_workspace_bytes(m, h_q, d, desc, beam, k), dev)
+        ws = workspace(select_attend_workspace_bytes(m, h_q, d, desc, beam, k, n_sink, window), dev)
     _check(lib().lsa_select_attend(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), m, h_q, d, _ptr(q_pos),
-                                   ctypes.byref(desc), _ptr(index), _ptr(W), beam, k, float(scale), _ptr(sel),
+                                   ctypes.byref(desc), _ptr(index), _ptr(W), beam, k, n_sink, window, float(scale),
+                                   _ptr(sel),
                                    _ptr(sel_count), _ptr(cutoff), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_select_attend")
@@ -262,6 +286,11 @@ def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel: torch.Tensor,
         out = torch.empty_like(Q)
     if lse is None and want_lse:
         lse = torch.empty((m, h_q), dtype=torch.float32, device=Q.device)
+    _need_out(sel_count, "sel_count", (m, h_kv), torch.int32)
+    if tuple(sel.shape[:2]) != (m, h_kv):
+        raise ValueError(f"sel must be [m, h_kv, row] = [{m}, {h_kv}, row], got {tuple(sel.shape)}")
+    _need_out(out, "out", (m, h_q, d), Q.dtype)
+    _need_out(lse, "lse", (m, h_q), torch.float32)
     nws = attend_workspace_bytes(m, h_q, h_kv, d, k)
     if ws is None and nws > 0:
         ws = torch.empty(nws, dtype=torch.uint8, device=Q.device)

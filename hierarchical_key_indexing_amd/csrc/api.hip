@@ -29,6 +29,15 @@ inline int check_desc(const lsa_index_desc *desc) {
 
 inline bool dtype_ok(int dtype) { return dtype == LSA_F32 || dtype == LSA_BF16; }
 
+constexpr int kMaxRow = 1 << 24;     // longest row of sel (attention set of one row and KV head)
+
+// sinks and window: EINVAL when negative, EUNSUPPORTED when a row would exceed kMaxRow
+inline int check_local(int k, int n_sink, int window) {
+    if (n_sink < 0 || window < 0) return LSA_EINVAL;
+    if ((int64_t)k + n_sink + window > kMaxRow) return LSA_EUNSUPPORTED;
+    return LSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,11 +114,12 @@ int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const 
 }
 
 int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
-                               int64_t *bytes) {
+                               int n_sink, int window, int64_t *bytes) {
     int rc = check_desc(desc);
     if (rc != LSA_OK) return rc;
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
     *bytes = lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)
                  ? lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)
                  : 0;
@@ -117,12 +127,14 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
 }
 
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
-               const lsa_index_desc *desc, const void *index, const float *W, int beam, int k, int32_t *sel,
-               int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes, void *stream) {
+               const lsa_index_desc *desc, const void *index, const float *W, int beam, int k, int n_sink,
+               int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes,
+               void *stream) {
     int rc = check_desc(desc);
     if (rc != LSA_OK) return rc;
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
     if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
     if (d > 256 || (int64_t)beam * desc->b > 4096 || k > 8192) return LSA_EUNSUPPORTED;
     if (m > INT32_MAX) return LSA_EUNSUPPORTED;
@@ -132,14 +144,15 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
         ws_bytes >= lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)) {
         hipError_t e = lsa::decode(Q, nullptr, nullptr, dtype, m, h_q, desc->h_kv, d, q_pos, (const char *)index,
                                    desc->n, desc->r, desc->b, desc->L, desc->nodes, desc->centroid_off,
-                                   desc->count_off, desc->leaf_off_off, desc->perm_off, W, beam, k, sel, sel_count,
-                                   sel_cutoff, 0.0f, nullptr, nullptr, ws, false, (hipStream_t)stream);
+                                   desc->count_off, desc->leaf_off_off, desc->perm_off, W, beam, k, n_sink, window,
+                                   sel, sel_count, sel_cutoff, 0.0f, nullptr, nullptr, ws, false,
+                                   (hipStream_t)stream);
         return e == hipSuccess ? LSA_OK : LSA_EHIP;
     }
     hipError_t e = lsa::select_keys(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
                                     desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off,
-                                    desc->leaf_off_off, desc->perm_off, W, beam, k, sel, sel_count, sel_cutoff,
-                                    (hipStream_t)stream);
+                                    desc->leaf_off_off, desc->perm_off, W, beam, k, n_sink, window, sel, sel_count,
+                                    sel_cutoff, (hipStream_t)stream);
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
@@ -156,7 +169,7 @@ int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m
     if (m < 0 || h_q < 1 || h_kv < 1 || n < 1 || n > INT32_MAX || d < 1 || k < 1) return LSA_EINVAL;
     if (h_q % h_kv != 0) return LSA_EINVAL;
     if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
-    if (h_q / h_kv > 16 || d < 8 || d > 256 || d % 8 != 0 || k > 8192) return LSA_EUNSUPPORTED;
+    if (h_q / h_kv > 16 || d < 8 || d > 256 || d % 8 != 0 || k > kMaxRow) return LSA_EUNSUPPORTED;
     if (!(scale >= 0.0f) || isinf(scale)) return LSA_EINVAL;
     if (m == 0) return LSA_OK;
     if (!Q || !K || !V || !sel || !sel_count || !out) return LSA_EINVAL;
@@ -169,26 +182,28 @@ int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m
 }
 
 int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
-                                      int64_t *bytes) {
+                                      int n_sink, int window, int64_t *bytes) {
     int rc = check_desc(desc);
     if (rc != LSA_OK) return rc;
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
     if (lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k))
         *bytes = lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k);
     else
-        *bytes = lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k);
+        *bytes = lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k + n_sink + window);
     return LSA_OK;
 }
 
 int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
                       const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W, int beam,
-                      int k, float scale, int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *out, float *lse,
-                      void *ws, int64_t ws_bytes, void *stream) {
+                      int k, int n_sink, int window, float scale, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
+                      void *out, float *lse, void *ws, int64_t ws_bytes, void *stream) {
     int rc = check_desc(desc);
     if (rc != LSA_OK) return rc;
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
     if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
     if (d > 256 || (int64_t)beam * desc->b > 4096 || k > 8192) return LSA_EUNSUPPORTED;
     if (h_q / desc->h_kv > 16 || d < 8 || d % 8 != 0) return LSA_EUNSUPPORTED;
@@ -197,7 +212,7 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
     if (m == 0) return LSA_OK;
     if (!Q || !K || !V || !q_pos || !index || !W || !sel || !sel_count || !out) return LSA_EINVAL;
     int64_t need = 0;
-    rc = lsa_select_attend_workspace_bytes(m, h_q, d, desc, beam, k, &need);
+    rc = lsa_select_attend_workspace_bytes(m, h_q, d, desc, beam, k, n_sink, window, &need);
     if (rc != LSA_OK) return rc;
     if (ws_bytes < need || (!ws && need > 0)) return LSA_ENOSPC;
     if (scale == 0.0f) scale = 1.0f / sqrtf((float)d);
@@ -205,15 +220,16 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
     if (lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)) {
         e = lsa::decode(Q, K, V, dtype, m, h_q, desc->h_kv, d, q_pos, (const char *)index, desc->n, desc->r,
                         desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
-                        desc->perm_off, W, beam, k, sel, sel_count, sel_cutoff, scale, out, lse, ws, true,
-                        (hipStream_t)stream);
+                        desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff, scale, out, lse,
+                        ws, true, (hipStream_t)stream);
     } else {
         e = lsa::select_keys(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
                              desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
-                             desc->perm_off, W, beam, k, sel, sel_count, sel_cutoff, (hipStream_t)stream);
+                             desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff,
+                             (hipStream_t)stream);
         if (e == hipSuccess)
-            e = lsa::attend(Q, K, V, dtype, m, h_q, desc->h_kv, desc->n, d, sel, sel_count, k, scale, out, lse,
-                            ws, (hipStream_t)stream);
+            e = lsa::attend(Q, K, V, dtype, m, h_q, desc->h_kv, desc->n, d, sel, sel_count, k + n_sink + window,
+                            scale, out, lse, ws, (hipStream_t)stream);
     }
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }

@@ -404,4 +404,52 @@ LSA_DEV int next_pow2(int x) {
     return p;
 }
 
+// number of entries <= key in an ascending array
+LSA_DEV int count_le(const int32_t *a, int len, int32_t key) {
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= key) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------- attention set
+// The retrieved keys are joined by a few initial sink tokens and a window of
+// recent tokens ("Latent sparse attention", bdtechtalks.com, section "How
+// latent sparse attention works").  With hi = min(pos, n - 1) the latest key a
+// row sees: sinks are [0, ns), ns = min(n_sink, hi + 1); the window is
+// [wlo, hi], wlo = max(n_sink, hi - window + 1); retrieval only takes keys in
+// [rlo, rhi] = [n_sink, hi - window].  The three parts are disjoint.  A row of
+// sel lists the retrieved keys, then the nloc sinks and window keys ascending.
+struct AttnSet {
+    int32_t rlo, rhi;   // retrieval range (empty when rhi < rlo)
+    int32_t ns, wlo;    // sinks [0, ns); window from wlo
+    int32_t nloc;       // number of sink and window keys
+    bool all;           // every key of the cache is in the retrieval range
+};
+LSA_DEV AttnSet attn_set(int32_t pos, int64_t n, int n_sink, int window) {
+    const int64_t hi = min<int64_t>((int64_t)pos, n - 1);
+    const int64_t wlo = max<int64_t>((int64_t)n_sink, hi - window + 1);
+    AttnSet s;
+    s.rlo = n_sink;
+    s.rhi = (int32_t)max<int64_t>(hi - window, -1);
+    s.ns = (int32_t)max<int64_t>(0, min<int64_t>((int64_t)n_sink, hi + 1));
+    s.wlo = (int32_t)wlo;
+    s.nloc = s.ns + (int32_t)max<int64_t>(0, hi - wlo + 1);
+    s.all = n_sink == 0 && (int64_t)s.rhi >= n - 1;
+    return s;
+}
+// the t-th local key (t < nloc)
+LSA_DEV int32_t local_key(const AttnSet &s, int t) { return t < s.ns ? t : s.wlo + (t - s.ns); }
+// members of an ascending list that lie in the retrieval range: the first of
+// them and their number
+LSA_DEV void in_range(const AttnSet &s, const int32_t *mem, int len, int &first, int &cnt) {
+    if (s.all || len <= 0) { first = 0; cnt = max(len, 0); return; }
+    const int a = (mem[0] >= s.rlo) ? 0 : count_le(mem, len, s.rlo - 1);
+    const int z = (mem[len - 1] <= s.rhi) ? len : count_le(mem, len, s.rhi);
+    first = a;
+    cnt = max(0, z - a);
+}
+
 }  // namespace lsa

@@ -55,6 +55,8 @@ struct DecodeArgs {
     int64_t leaf_off_off, perm_off;
     const float *W;
     int beam, k;
+    int n_sink, window;
+    int row;              // entries per row of sel: k + n_sink + window
     int32_t *sel, *sel_count;
     float *sel_cutoff;
     float scale_log2;
@@ -75,15 +77,6 @@ struct DecodeArgs {
 LSA_HOST_DEV inline int part_stride(int G, int d) { return (G * d + 2 * G + 3) & ~3; }
 
 // ---------------------------------------------------------------- helpers
-LSA_DEV int count_le_i32(const int32_t *a, int len, int32_t key) {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= key) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
 // For key x and the descending key lists a + q * stride (q = q0, q0 + dq, ...
 // below nq; len <= LEN entries each): c[i] = number of leading entries of list
 // q0 + i * dq greater than x.  Binary lifting, all lists side by side, so the
@@ -225,7 +218,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t kept_s[kMaxP];
     __shared__ __attribute__((aligned(16))) uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
-    __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64];
+    __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64], skip_s[64];
     __shared__ int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, last_s;
@@ -246,11 +239,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     const int wv = tid / kWave;
     const T *Q = (const T *)A.Q;
     int32_t *ctrl = A.ctrl + (size_t)gi * 4;
-    const int32_t pos = A.q_pos[i];
+    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     const int64_t nleaf = A.nodes[L];
     const int32_t *perm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
     const int32_t *leaf_off = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
-    const bool all_eligible = pos >= A.n - 1;
     const size_t groups = (size_t)A.m * A.h_kv;
 
     // ---- prologue: level-1 rows and counts, W_g and the group's queries
@@ -359,10 +351,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (v >= 0 && lane < b && ccnt[lane] > 0) {
                 key = make_key(score_lds<RC>(u_s, Cs + lane * kCS, r), (uint32_t)(v * b + lane));
                 if (leaf) {
+                    // members in the retrieval range: the first one and their number
                     const int a0 = clo[lane], a1 = clo[lane + 1];
-                    if (all_eligible) e = a1 - a0;
-                    else if (clo[b] - clo[0] <= kMemCap) e = count_le_i32(mem_s + (a0 - clo[0]), a1 - a0, pos);
-                    else e = count_le_i32(perm + a0, a1 - a0, pos);
+                    int f;
+                    if (clo[b] - clo[0] <= kMemCap) in_range(as, mem_s + (a0 - clo[0]), a1 - a0, f, e);
+                    else in_range(as, perm + a0, a1 - a0, f, e);
+                    skip_s[lane] = f;
                     if (e == 0) key = 0;
                 }
             }
@@ -471,7 +465,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         }
         __syncthreads();
         const int count = count_s;
-        int32_t *out = A.sel + (size_t)gi * A.k;
+        int32_t *out = A.sel + (size_t)gi * A.row;
         if (wv == 0) {
             // lane j: the j-th own leaf in score order; its first `take` members
             // go to sel from its retrieval offset wex and to own_s (this
@@ -482,7 +476,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 e = lp[p * 64 + lane] - (lane > 0 ? lp[p * 64 + lane - 1] : 0);
                 wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
                 take = max(0, min(e, count - wex));
-                a0 = clo[(int)(key_id(x) - (uint32_t)(v * b))];
+                const int c = (int)(key_id(x) - (uint32_t)(v * b));
+                a0 = clo[c] + skip_s[c];
             }
             const int incl = wave_incl_scan_add(take);
             toff_s[lane] = incl - take;
@@ -508,22 +503,27 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             out[wex_s[j] + t] = id;
             if (ATTEND) publish(A.keys + (size_t)gi * A.k + wex_s[j] + t, id + 1);
         }
-        for (int t = count + p * blockDim.x + tid; t < A.k; t += P * blockDim.x) out[t] = -1;
+        // the sinks and the window follow the retrieved keys
+        for (int t = p * blockDim.x + tid; t < as.nloc; t += P * blockDim.x) out[count + t] = local_key(as, t);
+        for (int t = count + as.nloc + p * blockDim.x + tid; t < A.row; t += P * blockDim.x) out[t] = -1;
         if (p == 0 && tid == 0) {
-            A.sel_count[gi] = count;
+            A.sel_count[gi] = count + as.nloc;
             if (count < A.k && A.sel_cutoff) A.sel_cutoff[gi] = -INFINITY;
         }
         __syncthreads();
     }
 
     if constexpr (ATTEND) {
-        // ---- attention.  Workgroup p attends over the retrieval positions
-        // [count * p / P, count * (p + 1) / P), whichever workgroups placed
-        // them, so the gathers are spread evenly whatever the nodes supplied;
-        // their ids are polled from the published keys into own_s in chunks
-        // of up to kOwnCap, padded with key 0 to whole 4 x 32-key steps.
+        // ---- attention.  The row's attention set is the retrieved keys
+        // (positions [0, count)) followed by the sinks and the window;
+        // workgroup p attends over positions [tot * p / P, tot * (p + 1) / P),
+        // whichever workgroups placed them, so the gathers are spread evenly
+        // whatever the nodes supplied.  Retrieved ids are polled from the
+        // published keys, local ones computed, into own_s in chunks of up to
+        // kOwnCap, padded with key 0 to whole 4 x 32-key steps.
         const int cnt_all = count_s;
-        const int lo = (int)(((int64_t)cnt_all * p) / P), hi = (int)(((int64_t)cnt_all * (p + 1)) / P);
+        const int tot = cnt_all + as.nloc;
+        const int lo = (int)(((int64_t)tot * p) / P), hi = (int)(((int64_t)tot * (p + 1)) / P);
         float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
         if constexpr (kMfma) {
             const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
@@ -536,14 +536,16 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             wave_attn_init<DC>(st);
             for (int c0 = lo; c0 < hi; c0 += kOwnCap) {
                 const int own = min(kOwnCap, hi - c0);
+                const int nr = max(0, min(own, cnt_all - c0));     // retrieved entries of the chunk
                 const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
-                for (int f0 = 0; f0 < own; f0 += 8 * 256) {
+                for (int f0 = 0; f0 < nr; f0 += 8 * 256) {
                     int32_t w[8];
-                    poll_nonzero(A.keys + (size_t)gi * A.k + c0 + f0, own - f0, w, ctrl + 2);
+                    poll_nonzero(A.keys + (size_t)gi * A.k + c0 + f0, nr - f0, w, ctrl + 2);
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
-                        if (f0 + tid + 256 * u < own) own_s[f0 + tid + 256 * u] = clamp_id(w[u] - 1, A.n);
+                        if (f0 + tid + 256 * u < nr) own_s[f0 + tid + 256 * u] = clamp_id(w[u] - 1, A.n);
                 }
+                for (int f = nr + tid; f < own; f += blockDim.x) own_s[f] = local_key(as, c0 + f - cnt_all);
                 for (int f = own + tid; f < nsteps * 4 * kMT; f += blockDim.x) own_s[f] = 0;
                 __syncthreads();
                 for (int t = 0; t < nsteps; ++t) {
@@ -584,10 +586,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             const T *Vg = (const T *)A.V + (size_t)g * A.n * d;
             for (int f0 = lo; f0 < hi; f0 += kTKD) {
                 const int nk = min(kTKD, hi - f0);
+                const int nr = max(0, min(nk, cnt_all - f0));      // retrieved entries of the tile
                 {
                     int32_t w[1];
-                    poll_nonzero(A.keys + (size_t)gi * A.k + f0, nk, w, ctrl + 2);
-                    if (tid < nk) ids_s[tid] = clamp_id(w[0] - 1, A.n);
+                    poll_nonzero(A.keys + (size_t)gi * A.k + f0, nr, w, ctrl + 2);
+                    if (tid < nr) ids_s[tid] = clamp_id(w[0] - 1, A.n);
+                    else if (tid < nk) ids_s[tid] = local_key(as, f0 + tid - cnt_all);
                 }
                 __syncthreads();
                 gather_tile<T>(Kg, Vg, ids_s, nk, d, Kt, dp, Vt);
@@ -802,13 +806,14 @@ static hipError_t launch_decode(const DecodeArgs &A, dim3 grid, size_t shm, hipS
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,
                   const int32_t *q_pos, const char *index, int64_t n, int r, int b, int L, const int64_t *nodes,
                   const int64_t *centroid_off, const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off,
-                  const float *W, int beam, int k, int32_t *sel, int32_t *sel_count, float *sel_cutoff, float scale,
-                  void *out, float *lse, void *ws, bool attend, hipStream_t st) {
+                  const float *W, int beam, int k, int n_sink, int window, int32_t *sel, int32_t *sel_count,
+                  float *sel_cutoff, float scale, void *out, float *lse, void *ws, bool attend, hipStream_t st) {
     DecodeArgs A{};
     A.Q = Q; A.K = K; A.V = V; A.m = m; A.h_q = h_q; A.h_kv = h_kv; A.d = d; A.q_pos = q_pos;
     A.index = index; A.n = n; A.r = r; A.b = b; A.L = L;
     for (int l = 0; l <= L; ++l) { A.nodes[l] = nodes[l]; A.centroid_off[l] = centroid_off[l]; A.count_off[l] = count_off[l]; }
     A.leaf_off_off = leaf_off_off; A.perm_off = perm_off; A.W = W; A.beam = beam; A.k = k;
+    A.n_sink = n_sink; A.window = window; A.row = k + n_sink + window;
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     A.scale_log2 = scale * 1.4426950408889634f; A.out = out; A.lse = lse;
     const int G = h_q / h_kv;

@@ -14,7 +14,8 @@ hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const 
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
                        int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
-                       int k, int32_t *sel, int32_t *sel_count, float *sel_cutoff, hipStream_t st);
+                       int k, int n_sink, int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
+                       hipStream_t st);
 
 int attend_nsplit(int64_t m, int h_kv, int k);
 int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k);
@@ -27,7 +28,7 @@ int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int b
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,
                   const int32_t *q_pos, const char *index, int64_t n, int r, int b, int L, const int64_t *nodes,
                   const int64_t *centroid_off, const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off,
-                  const float *W, int beam, int k, int32_t *sel, int32_t *sel_count, float *sel_cutoff, float scale,
-                  void *out, float *lse, void *ws, bool attend, hipStream_t st);
+                  const float *W, int beam, int k, int n_sink, int window, int32_t *sel, int32_t *sel_count,
+                  float *sel_cutoff, float scale, void *out, float *lse, void *ws, bool attend, hipStream_t st);
 
 }  // namespace lsa

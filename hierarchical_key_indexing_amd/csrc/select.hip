@@ -35,6 +35,8 @@ struct SelectArgs {
     int64_t leaf_off_off, perm_off;
     const float *W;
     int beam, k;
+    int n_sink, window;
+    int row;              // entries per row of sel: k + n_sink + window
     int32_t *sel;
     int32_t *sel_count;
     float *sel_cutoff;
@@ -63,16 +65,6 @@ LSA_DEV float score_row(const float *u, const float *__restrict__ row, int r) {
         for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
     }
     return (float)s;
-}
-
-// number of entries <= key in an ascending array
-LSA_DEV int count_le(const int32_t *a, int len, int32_t key) {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= key) lo = mid + 1; else hi = mid;
-    }
-    return lo;
 }
 
 template <typename T, int CMAX>
@@ -151,7 +143,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
     const int64_t nleaf = A.nodes[L];
     const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
     const int32_t *pm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
-    const int32_t pos = A.q_pos[i];
+    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     {
         const int chunk = (nc + blockDim.x - 1) / blockDim.x;
         const int s0 = min(nc, (int)threadIdx.x * chunk), s1 = min(nc, s0 + chunk);
@@ -160,7 +152,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
         for (int e = s0; e < s1; ++e) {
             const uint32_t v = key_id(keys[e]);
             const int32_t a = lo[v], z = lo[v + 1];
-            const int c = count_le(pm + a, z - a, pos);
+            int f, c;
+            in_range(as, pm + a, z - a, f, c);
             el[e - s0] = c;
             local += c;
         }
@@ -172,21 +165,24 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs A) {
     }
     const int avail = nc_s;
     const int count = min(A.k, avail);
-    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.row;
     for (int e = threadIdx.x; e < nc; e += blockDim.x) {
         const int p0 = aux[e];
         if (p0 >= count) continue;
         const int p1 = aux[e + 1];
         const int take = min(p1 - p0, count - p0);
         const uint32_t v = key_id(keys[e]);
-        const int32_t a = lo[v];
+        int f, c;
+        in_range(as, pm + lo[v], lo[v + 1] - lo[v], f, c);
+        const int32_t a = lo[v] + f;
         for (int t = 0; t < take; ++t) out[p0 + t] = pm[a + t];
         if (count == A.k && p1 >= A.k) cut_s = key_score(keys[e]);
     }
-    for (int t = count + threadIdx.x; t < A.k; t += blockDim.x) out[t] = -1;
+    for (int t = threadIdx.x; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
+    for (int t = count + as.nloc + threadIdx.x; t < A.row; t += blockDim.x) out[t] = -1;
     __syncthreads();
     if (threadIdx.x == 0) {
-        A.sel_count[(size_t)i * A.h_kv + g] = count;
+        A.sel_count[(size_t)i * A.h_kv + g] = count + as.nloc;
         if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
     }
 }
@@ -254,8 +250,7 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     const int G = A.h_q / A.h_kv, d = A.d, b = A.b, L = A.L, P = A.beam;
     const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
     const T *Q = (const T *)A.Q;
-    const int32_t pos = A.q_pos[i];
-    const bool all_eligible = pos >= A.n - 1;
+    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
 
     // ---- group latent query.  W_g is staged in LDS 64 input rows (16 KB) at
     // a time; the sum over the input dimension continues in order across them.
@@ -314,10 +309,10 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
                     int e = 1;
                     if (leaf) {
                         const int32_t a0 = lo[child], a1 = lo[child + 1];
-                        // members ascend: all are eligible when the last one is
-                        e = (all_eligible || pm[a1 - 1] <= pos) ? a1 - a0 : count_le(pm + a0, a1 - a0, pos);
+                        int f;
+                        in_range(as, pm + a0, a1 - a0, f, e);
                         eli[j * 64 + lane] = e;
-                        lof[j * 64 + lane] = a0;
+                        lof[j * 64 + lane] = a0 + f;
                     }
                     if (e > 0) key = make_key_slot(score_row64(u_s, Cl + (size_t)child * R), (uint32_t)child, j * 64 + lane);
                 }
@@ -362,7 +357,7 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     int total;
     int off = block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
-    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.k;
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.row;
     // the thread's (up to) four leaves: the first 8 members of each are loaded
     // in one round (clamped indices), longer leaves finish in a loop
     constexpr int kC = 4;
@@ -387,10 +382,11 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
             if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
         for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
     }
-    for (int t = count + tid; t < A.k; t += blockDim.x) out[t] = -1;
+    for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
+    for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
     __syncthreads();
     if (tid == 0) {
-        A.sel_count[(size_t)i * A.h_kv + g] = count;
+        A.sel_count[(size_t)i * A.h_kv + g] = count + as.nloc;
         if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
     }
 }
@@ -398,12 +394,14 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
                        int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
-                       int k, int32_t *sel, int32_t *sel_count, float *sel_cutoff, hipStream_t st) {
+                       int k, int n_sink, int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
+                       hipStream_t st) {
     SelectArgs A{};
     A.Q = Q; A.m = m; A.h_q = h_q; A.h_kv = h_kv; A.d = d; A.q_pos = q_pos; A.index = index; A.n = n;
     A.r = r; A.b = b; A.L = L;
     for (int l = 0; l <= L; ++l) { A.nodes[l] = nodes[l]; A.centroid_off[l] = centroid_off[l]; A.count_off[l] = count_off[l]; }
     A.leaf_off_off = leaf_off_off; A.perm_off = perm_off; A.W = W; A.beam = beam; A.k = k;
+    A.n_sink = n_sink; A.window = window; A.row = k + n_sink + window;
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     const dim3 grid((unsigned)m, (unsigned)h_kv);
     if (r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= (int64_t)1 << 22) {

@@ -132,7 +132,7 @@ int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const 
  * which case every (row, KV head) pair runs in one workgroup).
  */
 int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
-                               int64_t *bytes);
+                               int n_sink, int window, int64_t *bytes);
 
 /*
  * Select keys for every (query row, KV head) by top-down descent of the tree
@@ -148,12 +148,17 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  *   W        device, float [h_kv][d][r]: the same projection as the keys
  *   beam     nodes kept per level at levels 1..L-1 (>= 1)
  *   k        keys retrieved per row and KV head (>= 1)
- *   sel      device out, int32 [m][h_kv][k]: selected keys in the order they
- *            are retrieved (leaf by leaf, ascending position inside a leaf),
+ *   n_sink   initial sink tokens joined to the retrieved keys (>= 0)
+ *   window   recent tokens joined to the retrieved keys (>= 0)
+ *   sel      device out, int32 [m][h_kv][k + n_sink + window]: the attention
+ *            set of each row and KV head: the retrieved keys in the order
+ *            they are retrieved (leaf by leaf, ascending position inside a
+ *            leaf), then the sinks and the window in ascending position,
  *            padded with -1
- *   sel_count device out, int32 [m][h_kv]: number of selected keys (<= k)
+ *   sel_count device out, int32 [m][h_kv]: number of entries before the padding
  *   sel_cutoff device out or NULL, float [m][h_kv]: score of the leaf that
- *            supplied the k-th key, -inf when fewer than k keys were eligible
+ *            supplied the k-th retrieved key, -inf when fewer than k keys
+ *            could be retrieved
  *
  * The G = h_q/h_kv query heads of a KV head share one selection, scored with
  * their mean qbar projected by W: u = fl32(qbar . W_g); a node's score is
@@ -164,7 +169,16 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * id asc) order, each giving its members in ascending position; keys at
  * positions > q_pos are skipped; the first k are taken.  Dot products are
  * accumulated in double in ascending index order.
- * Limits: h_q % h_kv == 0, 1 <= d <= 256, beam * b <= 4096, k <= 8192.
+ *
+ * Sinks and window ("Latent sparse attention", bdtechtalks.com, "How latent
+ * sparse attention works": the retrieved keys are joined by a window of recent
+ * tokens and a few initial sink tokens).  With hi = min(q_pos, n - 1), the
+ * latest key the row sees, the sinks are keys [0, min(n_sink, hi + 1)) and the
+ * window is [max(n_sink, hi - window + 1), hi]; retrieval skips both (it takes
+ * only keys in [n_sink, hi - window], still up to k of them), so the three
+ * parts are disjoint.  n_sink = window = 0 gives the retrieved keys alone.
+ * Limits: h_q % h_kv == 0, 1 <= d <= 256, beam * b <= 4096, k <= 8192,
+ * k + n_sink + window <= 2^24.
  *
  * Workspace: ws may be NULL.  When ws holds at least
  * lsa_select_workspace_bytes bytes (> 0), small batches (m * h_kv * beam up
@@ -178,8 +192,8 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  */
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
                const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,
-               int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes,
-               void *stream);
+               int n_sink, int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws,
+               int64_t ws_bytes, void *stream);
 
 /*
  * Bytes of device workspace lsa_attend needs (*bytes).
@@ -193,7 +207,8 @@ int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64
  *
  *   Q        device, [m][h_q][d] of `dtype`
  *   K, V     device, [h_kv][n][d] of `dtype`
- *   sel, sel_count  as written by lsa_select (k = row stride of sel)
+ *   sel, sel_count  as written by lsa_select (k = row length of sel, which
+ *            is k + n_sink + window of the lsa_select call)
  *   scale    score scale; 0 means 1/sqrt(d)
  *   out      device out, [m][h_q][d] of `dtype` (fp32 accumulation, rounded
  *            to nearest even for bf16)
@@ -201,7 +216,7 @@ int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64
  *            scaled scores; -inf for an empty selection (whose out row is 0)
  *   ws       device workspace of lsa_attend_workspace_bytes bytes
  * Entries of sel must lie in [0, n).  Limits: h_q % h_kv == 0, h_q/h_kv <= 16,
- * 8 <= d <= 256 with d % 8 == 0, k <= 8192.
+ * 8 <= d <= 256 with d % 8 == 0, k <= 2^24.
  */
 int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q,
                int h_kv, int64_t n, int d, const int32_t *sel, const int32_t *sel_count, int k,
@@ -211,7 +226,7 @@ int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m
  * Bytes of device workspace lsa_select_attend needs (*bytes).
  */
 int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam,
-                                      int k, int64_t *bytes);
+                                      int k, int n_sink, int window, int64_t *bytes);
 
 /*
  * lsa_select followed by lsa_attend on the same rows, in one launch when the
@@ -223,7 +238,8 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
  * zero-filled before its first use; every call leaves it zeroed again, so it
  * serves any number of calls of any sizes that fit it; calls sharing one ws
  * must not run concurrently.  In the one-launch form the workgroups of a
- * (row, KV head) pair split the attention evenly over the retrieval order.
+ * (row, KV head) pair split the attention evenly over the attention set
+ * (retrieved keys, then sinks and window).
  * Outputs equal those of the two separate calls
  * (sel, sel_count and sel_cutoff bit for bit; out and lse within fp32
  * rounding of the accumulation order).
@@ -231,8 +247,8 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
  */
 int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
                       const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W,
-                      int beam, int k, float scale, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
-                      void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
+                      int beam, int k, int n_sink, int window, float scale, int32_t *sel, int32_t *sel_count,
+                      float *sel_cutoff, void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

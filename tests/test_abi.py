@@ -79,16 +79,22 @@ def test_entry_points_validate_before_touching_the_device():
     d = lsa.index_layout(100, 2, 8, 4, 2)
     bad = lsa.IndexDesc.from_buffer_copy(d)
     bad.bytes += 1
-    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 2, 8, fake, fake, None, None, 0,
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 2, 8, 0, 0, fake, fake, None, None, 0,
                         None) == lsa.LSA_EINVAL
-    assert L.lsa_select(fake, 0, 1, 3, 16, fake, ctypes.byref(d), fake, fake, 2, 8, fake, fake, None, None, 0,
+    assert L.lsa_select(fake, 0, 1, 3, 16, fake, ctypes.byref(d), fake, fake, 2, 8, 0, 0, fake, fake, None, None, 0,
                         None) == lsa.LSA_EINVAL          # h_q % h_kv != 0
-    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2000, 8, fake, fake, None, None, 0,
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2000, 8, 0, 0, fake, fake, None, None, 0,
                         None) == lsa.LSA_EUNSUPPORTED    # beam * b > 4096
-    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 9000, fake, fake, None, None, 0,
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 9000, 0, 0, fake, fake, None, None, 0,
                         None) == lsa.LSA_EUNSUPPORTED    # k > 8192
-    assert L.lsa_select(fake, 0, 0, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, fake, fake, None, None, 0,
+    assert L.lsa_select(fake, 0, 0, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, 0, 0, fake, fake, None, None, 0,
                         None) == lsa.LSA_OK              # m = 0: nothing to do
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, -1, 0, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL          # negative sink count
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, 0, -5, fake, fake, None, None, 0,
+                        None) == lsa.LSA_EINVAL          # negative window
+    assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, 1 << 23, 1 << 23, fake, fake,
+                        None, None, 0, None) == lsa.LSA_EUNSUPPORTED    # row longer than 2^24
     # attend
     f = ctypes.c_float
     assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 3, 100, 64, fake, fake, 8, f(0), fake, None, None, 0,

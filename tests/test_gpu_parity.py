@@ -154,6 +154,60 @@ def test_workspace_reused_across_shapes(lsa):
             assert torch.equal(a, b_), f"select-only {nm} differs with a reused workspace (beam {bm}, k {k})"
 
 
+LOCAL_CASES = [("tiny_4k", {}), ("ragged_bf16_b5", {}), ("multi_piece_root", {}),
+               ("multi_piece_root", dict(beam=16)), ("odd_r_deep", {}), ("flat_L1", {})]
+LOCAL_SETS = [(4, 16), (0, 300), (7, 0), (50, 100000)]
+
+
+@pytest.mark.parametrize("name,over", LOCAL_CASES, ids=[f"{c[0]}{'_beam16' if c[1] else ''}" for c in LOCAL_CASES])
+def test_sinks_and_window_match_oracle(lsa, name, over):
+    """Sinks and a recent window joined to the retrieved keys: every select
+    path (one workgroup per row, the multi-workgroup kernel, the fused
+    select + attend) gives the oracle's rows bit for bit, and attention over
+    them matches the oracle's."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", **dict(SMALL)[name]) if name != "tiny_4k" else _wl("tiny_4k")
+    w = w.replace(name=name, **over)
+    data = _inputs(w, dev)
+    index, desc, gix, oix = _build_both(lsa, w, data)
+    c = data["cpu"]
+    Qh = np32(c["Q"])
+    pos = c["pos"].numpy()
+    tol = TOL[w.torch_dtype]
+    for n_sink, window in LOCAL_SETS:
+        ref = oracle.select(Qh, pos, gix, c["W"].numpy(), w.beam, w.k, n_sink=n_sink, window=window)
+        o_ref, lse_ref = oracle.attend(Qh, np32(c["K"]), np32(c["V"]), ref["sel"], ref["count"])
+        nws = lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, w.beam, w.k, n_sink, window)
+        for label, ws in (("single-wg", None), ("multi-wg", lsa.workspace(nws, dev))):
+            if label == "multi-wg" and ws is None:
+                continue
+            say("local select", name, over, label, n_sink, window)
+            sel, cnt, cut = lsa.select(data["Q"], data["pos"], index, desc, data["W"], w.beam, w.k, ws=ws,
+                                       n_sink=n_sink, window=window)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt.cpu().numpy(), ref["count"], f"sel_count ({label})")
+            assert_same_bits(sel.cpu().numpy(), ref["sel"], f"sel ({label})")
+            assert_same_bits(cut.cpu().numpy(), ref["cutoff"], f"cutoff ({label})")
+        say("local attend", name, n_sink, window)
+        out, lse = lsa.attend(data["Q"], data["K"], data["V"], sel, cnt)
+        torch.cuda.synchronize()
+        _check_attention(out, lse, o_ref, lse_ref, tol)
+        say("local select_attend", name, n_sink, window)
+        fws = lsa.workspace(lsa.select_attend_workspace_bytes(w.m, w.h_q, w.d, desc, w.beam, w.k, n_sink, window),
+                            dev)
+        for rep in range(2):
+            sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(data["Q"], data["K"], data["V"], data["pos"], index,
+                                                             desc, data["W"], w.beam, w.k, ws=fws,
+                                                             n_sink=n_sink, window=window)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt2.cpu().numpy(), ref["count"], "sel_count (fused)")
+            assert_same_bits(sel2.cpu().numpy(), ref["sel"], "sel (fused)")
+            assert_same_bits(cut2.cpu().numpy(), ref["cutoff"], "cutoff (fused)")
+            _check_attention(out2, lse2, o_ref, lse_ref, tol)
+        if lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, w.beam, w.k) > 0:
+            _assert_exchange_zeroed(fws, w.m * w.h_kv, w.beam, w.h_q // w.h_kv, w.d)
+
+
 def _check_attention(out, lse, o_ref, lse_ref, tol):
     assert np.max(np.abs(np32(out) - o_ref)) <= tol
     g = lse.cpu().numpy()
@@ -240,11 +294,13 @@ def test_dense_equivalence_on_gpu(lsa, b, L):
 
 
 # ------------------------------------------------------------------ full-size workloads
-FULL = [("decode_1m", None, 1), ("prefill_1m", 48, 1), ("train_128k", 64, 2), ("decode_10m", None, 0)]
+FULL = [("decode_1m", None, 1, (0, 0)), ("prefill_1m", 48, 1, (0, 0)), ("train_128k", 64, 2, (0, 0)),
+        ("decode_10m", None, 0, (0, 0)), ("decode_1m", None, 0, (4, 512)), ("prefill_1m", 32, 0, (4, 512))]
 
 
-@pytest.mark.parametrize("name,sample_rows,replay_depth", FULL, ids=[f[0] for f in FULL])
-def test_full_size_workload(lsa, name, sample_rows, replay_depth):
+@pytest.mark.parametrize("name,sample_rows,replay_depth,local", FULL,
+                         ids=[f[0] + ("" if f[3] == (0, 0) else "_sinks%d_window%d" % f[3]) for f in FULL])
+def test_full_size_workload(lsa, name, sample_rows, replay_depth, local):
     """The workload at its real size, in the launch configuration the benchmark
     uses: bit-exact tree on sampled nodes (the oracle re-clusters the node from
     the members the GPU gave its parent), bit-exact selection and attention on
@@ -275,14 +331,16 @@ def test_full_size_workload(lsa, name, sample_rows, replay_depth):
         say("replay", name, g, l, u)
         replay_node(K, W, gix, g, l, u, w.iters)
 
-    say("select", name)
-    sel, cnt, cut = lsa.select(Q, pos, index, desc, W, w.beam, w.k)
+    n_sink, window = local
+    say("select", name, local)
+    sel, cnt, cut = lsa.select(Q, pos, index, desc, W, w.beam, w.k, n_sink=n_sink, window=window)
     say("attend", name)
     out, lse = lsa.attend(Q, K, V, sel, cnt)
     torch.cuda.synchronize()
     if w.m * w.h_kv <= 256:
         say("select_attend", name)
-        sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k)
+        sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k,
+                                                         n_sink=n_sink, window=window)
         torch.cuda.synchronize()
         assert torch.equal(sel2, sel) and torch.equal(cnt2, cnt) and torch.equal(cut2, cut)
         assert float((out2.float() - out.float()).abs().max()) <= TOL[w.torch_dtype]
@@ -299,7 +357,7 @@ def test_full_size_workload(lsa, name, sample_rows, replay_depth):
     ridx = torch.from_numpy(rows).to(dev)
     Qs = np32(Q[ridx])
     say("oracle select", name, len(rows))
-    ref = oracle.select(Qs, pos[ridx].cpu().numpy(), gix, np32(W), w.beam, w.k)
+    ref = oracle.select(Qs, pos[ridx].cpu().numpy(), gix, np32(W), w.beam, w.k, n_sink=n_sink, window=window)
     assert_same_bits(cnt[ridx].cpu().numpy(), ref["count"], "sel_count")
     assert_same_bits(sel[ridx].cpu().numpy(), ref["sel"], "sel")
     assert_same_bits(cut[ridx].cpu().numpy(), ref["cutoff"], "cutoff")
