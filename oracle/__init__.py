@@ -53,6 +53,9 @@ def lib():
         L.oracle_select.argtypes = [P, i64, i32, i32, P, i64, i32, i32, i32, i32,
                                     P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_select.restype = i32
+        L.oracle_select_flat.argtypes = [P, i64, i32, i32, P, i64, i32, i32, i32, i32,
+                                         P, P, P, P, P, i32, i32, i32, P, P, P, P]
+        L.oracle_select_flat.restype = i32
         L.oracle_attend.argtypes = [P, P, P, i64, i32, i32, i64, i32, P, P, i32, dbl, P, P]
         L.oracle_attend.restype = i32
         _lib = L
@@ -164,6 +167,23 @@ def select(Q: np.ndarray, pos: np.ndarray, index: Index, W: np.ndarray, beam: in
     if want_kept:
         out["kept"] = kept
     return out
+
+
+def select_flat(Q: np.ndarray, pos: np.ndarray, index: Index, W: np.ndarray, k: int,
+                n_sink: int = 0, window: int = 0):
+    """Flat search: every non-empty leaf scored.  Same outputs as select()
+    (sel [m, h_kv, k + n_sink + window], count, cutoff, nscored)."""
+    Q = _c(Q, np.float32); pos = _c(pos, np.int32); W = _c(W, np.float32)
+    m, h_q, d = Q.shape
+    ix = index
+    sel = np.empty((m, ix.h_kv, k + n_sink + window), np.int32)
+    cnt = np.empty((m, ix.h_kv), np.int32)
+    cut = np.empty((m, ix.h_kv), np.float32)
+    nsc = np.empty((m, ix.h_kv), np.int64)
+    lib().oracle_select_flat(_p(Q), m, h_q, d, _p(pos), ix.n, ix.h_kv, ix.r, ix.b, ix.L,
+                             _p(ix.C_all), _p(ix.cnt_all), _p(ix.leaf_off), _p(ix.perm), _p(W),
+                             k, n_sink, window, _p(sel), _p(cnt), _p(cut), _p(nsc))
+    return dict(sel=sel, count=cnt, cutoff=cut, nscored=nsc)
 
 
 def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, count: np.ndarray,

@@ -328,6 +328,74 @@ int oracle_select(const float *Q, int64_t m, int h_q, int d, const int32_t *pos,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Flat search (bdtechtalks.com, "How latent sparse attention works": the
+ * query is compared against all cluster centroids; the hierarchical search is
+ * the alternative that follows a few branches per level).  Reading: the
+ * clusters are the leaves of the tree; every non-empty leaf is scored with
+ * score(v) = fl32(u . C_L[v]), the leaves are visited in (score desc, id asc)
+ * order and filled exactly as in oracle_select (retrieval range, k, sinks,
+ * window, cutoff).  No level above the leaves is consulted.  Outputs as in
+ * oracle_select; nscored [m][h_kv] may be NULL. */
+int oracle_select_flat(const float *Q, int64_t m, int h_q, int d, const int32_t *pos,
+                       int64_t n, int h_kv, int r, int b, int L,
+                       const float *C_all, const int64_t *cnt_all, const int64_t *leaf_off,
+                       const int32_t *perm, const float *W, int k, int n_sink, int window,
+                       int32_t *sel, int32_t *sel_count, float *cutoff, int64_t *nscored)
+{
+    int G = h_q / h_kv;
+    int64_t nleaf = ipow(b, L);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int g = 0; g < h_kv; ++g) {
+            float *qbar = (float *)malloc(sizeof(float) * (size_t)d);
+            float *u = (float *)malloc(sizeof(float) * (size_t)r);
+            for (int t = 0; t < d; ++t) {
+                double s = 0.0;
+                for (int h = 0; h < G; ++h) s += (double)Q[(i * h_q + (int64_t)g * G + h) * d + t];
+                qbar[t] = (float)(s / (double)G);
+            }
+            const float *Wg = W + (int64_t)g * d * r;
+            for (int c = 0; c < r; ++c) {
+                double s = 0.0;
+                for (int t = 0; t < d; ++t) s += (double)qbar[t] * (double)Wg[(int64_t)t * r + c];
+                u[c] = (float)s;
+            }
+            const int64_t *cn = cnt_all + oracle_level_base(h_kv, b, L) + (int64_t)g * nleaf;
+            const float *C = C_all + (oracle_level_base(h_kv, b, L) + (int64_t)g * nleaf) * r;
+            cand_t *F = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nleaf > 0 ? nleaf : 1));
+            int64_t nf = 0;
+            for (int64_t v = 0; v < nleaf; ++v)
+                if (cn[v] > 0) { F[nf].id = v; F[nf].s = score_row(u, C + v * r, r); nf++; }
+            qsort(F, (size_t)nf, sizeof(cand_t), cand_cmp);
+            const int64_t row = (int64_t)k + n_sink + window;
+            int32_t *out = sel + (i * h_kv + g) * row;
+            const int64_t *lo = leaf_off + (int64_t)g * (nleaf + 1);
+            const int32_t *pm = perm + (int64_t)g * n;
+            const int64_t hi = (int64_t)pos[i] < n - 1 ? (int64_t)pos[i] : n - 1;
+            int64_t taken = 0;
+            float cut = -INFINITY;
+            for (int64_t t = 0; t < nf && taken < k; ++t) {
+                for (int64_t p = lo[F[t].id]; p < lo[F[t].id + 1] && taken < k; ++p) {
+                    if (pm[p] < n_sink || pm[p] > hi - window) continue;
+                    out[taken++] = pm[p];
+                    if (taken == k) cut = F[t].s;
+                }
+            }
+            int64_t filled = taken;
+            for (int64_t j = 0; j < n_sink && j <= hi; ++j) out[filled++] = (int32_t)j;
+            for (int64_t j = (hi - window + 1 > n_sink ? hi - window + 1 : n_sink); j <= hi; ++j)
+                out[filled++] = (int32_t)j;
+            for (int64_t t = filled; t < row; ++t) out[t] = -1;
+            sel_count[i * h_kv + g] = (int32_t)filled;
+            if (cutoff) cutoff[i * h_kv + g] = cut;
+            if (nscored) nscored[i * h_kv + g] = nf;
+            free(F); free(qbar); free(u);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sparse attention over the selected keys (kongchang.com, "The
  * Accuracy-Efficiency Dilemma ...": each query interacts with k keys instead
  * of all n; bdtechtalks.com, "How latent sparse attention works": attention is

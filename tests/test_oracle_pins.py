@@ -49,6 +49,15 @@ def test_hand_worked_tree_and_selection(oracle_lib):
         assert out["count"][0, 0] == q["count"]
         assert out["cutoff"][0, 0] == _frac32(q["cutoff"])
         assert out["nscored"][0, 0] == q["nscored"]
+    for q in g["flat_queries"]:
+        ix = trees[q["tree"]]
+        Q = np.array(q["q"], np.float32)[None, None]
+        out = oracle.select_flat(Q, np.array([q["pos"]], np.int32), ix, W, q["k"],
+                                 n_sink=q.get("n_sink", 0), window=q.get("window", 0))
+        assert list(out["sel"][0, 0]) == q["sel"]
+        assert out["count"][0, 0] == q["count"]
+        assert out["cutoff"][0, 0] == _frac32(q["cutoff"])
+        assert out["nscored"][0, 0] == q["nscored"]
 
 
 # --------------------------------------------------------------------------- projection
@@ -350,3 +359,53 @@ def test_window_covering_the_context_is_dense_whatever_the_index(oracle_lib):
     ref = _sdpa_masked(Q, K, V, mask, 1.0 / np.sqrt(w.d))
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
     assert np.all(np.isneginf(out["cutoff"]))
+
+
+# --------------------------------------------------------------------------- flat search
+@pytest.mark.parametrize("b,L,k,n_sink,window", [(4, 3, 40, 0, 0), (3, 2, 17, 2, 9), (8, 2, 200, 0, 31),
+                                                 (16, 1, 50, 5, 0), (5, 3, 1, 0, 0), (4, 2, 10000, 3, 3)])
+def test_flat_select_matches_numpy_ranking(oracle_lib, b, L, k, n_sink, window):
+    """Flat search against a numpy ranking of every key by (leaf score desc,
+    leaf id asc, position asc), the leaf scores computed from the leaf
+    centroids with a float64 matmul; then the sinks and the window."""
+    w, K, V, W, Q, pos = _small_case(b=b, L=L, seed=50 + b * 3 + L, m=6)
+    Q[0] = 0.0
+    ix = oracle.build_index(K, W, b, L, 5)
+    out = oracle.select_flat(Q, pos, ix, W, k, n_sink=n_sink, window=window)
+    G = w.h_q // w.h_kv
+    keys = np.arange(w.n)
+    for i, p in enumerate(pos):
+        hi = min(int(p), w.n - 1)
+        for g in range(w.h_kv):
+            u = group_latent(Q[i], W, g, G).astype(np.float64)
+            leaf_score = fl32(ix.C(L)[g].astype(np.float64) @ u)
+            leaf_of = np.empty(w.n, np.int64)
+            lo = ix.leaf_off[g]
+            for v in range(b ** L):
+                leaf_of[ix.perm[g][lo[v]:lo[v + 1]]] = v
+            elig = keys[(keys >= n_sink) & (keys <= hi - window)]
+            order = np.lexsort((elig, leaf_of[elig], -leaf_score[leaf_of[elig]].astype(np.float64)))
+            ret = list(elig[order][:k])
+            local = list(range(0, min(n_sink, hi + 1))) + list(range(max(n_sink, hi - window + 1), hi + 1))
+            c = out["count"][i, g]
+            assert c == len(ret) + len(local)
+            assert list(out["sel"][i, g, :c]) == ret + local
+            assert np.all(out["sel"][i, g, c:] == -1)
+            if len(ret) == k:
+                assert out["cutoff"][i, g] == leaf_score[leaf_of[ret[-1]]]
+            else:
+                assert np.isneginf(out["cutoff"][i, g])
+            assert out["nscored"][i, g] == int(np.count_nonzero(ix.cnt(L)[g]))
+
+
+@pytest.mark.parametrize("b,L", [(4, 3), (3, 2), (16, 1)])
+def test_flat_select_equals_descent_with_every_branch_kept(oracle_lib, b, L):
+    """A beam that keeps every node at every level leaves nothing pruned: the
+    hierarchical search then visits exactly the flat search's leaves."""
+    w, K, V, W, Q, pos = _small_case(b=b, L=L, seed=70 + b, m=8)
+    ix = oracle.build_index(K, W, b, L, 5)
+    for k, ns, nw in [(25, 0, 0), (300, 2, 7)]:
+        f = oracle.select_flat(Q, pos, ix, W, k, n_sink=ns, window=nw)
+        h = oracle.select(Q, pos, ix, W, b ** max(L - 1, 0), k, n_sink=ns, window=nw)
+        assert np.array_equal(f["sel"], h["sel"]) and np.array_equal(f["count"], h["count"])
+        assert np.array_equal(f["cutoff"], h["cutoff"])
