@@ -27,7 +27,8 @@ MAX_LEVELS = 6
 
 EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
-           "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend"]
+           "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend", "lsa_select_flat_workspace_bytes",
+           "lsa_select_flat"]
 
 
 class IndexDesc(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib():
         L.lsa_select_attend.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, ctypes.c_float,
                                         P, P, P, P, P, P, i64, P]
         L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, P, P, P, P, i64, P]
+        L.lsa_select_flat_workspace_bytes.argtypes = [i64, i32, D, ctypes.POINTER(i64)]
+        L.lsa_select_flat.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, P, P, P, P, i64, P]
         L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_attend.argtypes = [P, P, P, i32, i64, i32, i32, i64, i32, P, P, i32, ctypes.c_float,
                                  P, P, P, i64, P]
@@ -232,6 +235,40 @@ def select(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: Inde
                             _ptr(W), beam, k, n_sink, window, _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_select")
+    return sel, sel_count, cutoff
+
+
+def select_flat_workspace_bytes(m: int, h_q: int, desc: IndexDesc) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_select_flat_workspace_bytes(m, h_q, ctypes.byref(desc), ctypes.byref(v)),
+           "lsa_select_flat_workspace_bytes")
+    return v.value
+
+
+def select_flat(Q: torch.Tensor, q_pos: torch.Tensor, index: torch.Tensor, desc: IndexDesc, W: torch.Tensor,
+                k: int, sel: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
+                cutoff: Optional[torch.Tensor] = None, want_cutoff: bool = True, ws: Optional[torch.Tensor] = None,
+                stream=None, n_sink: int = 0, window: int = 0):
+    """Flat search (every leaf scored) -> (sel, count, cutoff) as select()."""
+    _need(Q, "Q"); _need(q_pos, "q_pos"); _need(W, "W")
+    m, h_q, d = Q.shape
+    h = desc.h_kv
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((m, h, k + n_sink + window), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
+    if cutoff is None and want_cutoff:
+        cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    _need_out(sel, "sel", (m, h, k + n_sink + window), torch.int32)
+    _need_out(sel_count, "sel_count", (m, h), torch.int32)
+    _need_out(cutoff, "cutoff", (m, h), torch.float32)
+    if ws is None:
+        ws = torch.empty(max(select_flat_workspace_bytes(m, h_q, desc), 1), dtype=torch.uint8, device=dev)
+    _check(lib().lsa_select_flat(_ptr(Q), _dtype_code(Q), m, h_q, d, _ptr(q_pos), ctypes.byref(desc), _ptr(index),
+                                 _ptr(W), k, n_sink, window, _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(ws),
+                                 ws.numel(), _stream(stream)),
+           "lsa_select_flat")
     return sel, sel_count, cutoff
 
 

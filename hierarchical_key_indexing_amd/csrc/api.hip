@@ -156,6 +156,36 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
+int lsa_select_flat_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, int64_t *bytes) {
+    int rc = check_desc(desc);
+    if (rc != LSA_OK) return rc;
+    if (m < 0 || h_q < 1 || !bytes) return LSA_EINVAL;
+    if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    *bytes = lsa::flat_workspace_bytes(m, desc->h_kv, desc->r, desc->nodes[desc->L]);
+    return LSA_OK;
+}
+
+int lsa_select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
+                    const lsa_index_desc *desc, const void *index, const float *W, int k, int n_sink, int window,
+                    int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != LSA_OK) return rc;
+    if (m < 0 || h_q < 1 || d < 1 || k < 1) return LSA_EINVAL;
+    if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
+    if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
+    if (d > 256 || k > 8192 || m > INT32_MAX) return LSA_EUNSUPPORTED;
+    if (m == 0) return LSA_OK;
+    if (!Q || !q_pos || !index || !W || !sel || !sel_count) return LSA_EINVAL;
+    const int64_t nleaf = desc->nodes[desc->L];
+    if (!ws || lsa::flat_batch_rows(m, desc->h_kv, desc->r, nleaf, ws_bytes) < 1) return LSA_ENOSPC;
+    hipError_t e = lsa::select_flat(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
+                                    nleaf, desc->centroid_off[desc->L], desc->count_off[desc->L],
+                                    desc->leaf_off_off, desc->perm_off, W, k, n_sink, window, sel, sel_count,
+                                    sel_cutoff, ws, ws_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? LSA_OK : LSA_EHIP;
+}
+
 int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64_t *bytes) {
     if (m < 0 || h_q < 1 || h_kv < 1 || d < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % h_kv != 0) return LSA_EINVAL;

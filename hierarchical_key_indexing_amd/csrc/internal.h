@@ -23,6 +23,14 @@ hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_
                   int d, const int32_t *sel, const int32_t *sel_count, int k, float scale, void *out, float *lse,
                   void *ws, hipStream_t st);
 
+int64_t flat_workspace_bytes(int64_t m, int h_kv, int r, int64_t nleaf);
+int64_t flat_batch_rows(int64_t m, int h_kv, int r, int64_t nleaf, int64_t ws_bytes);
+hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
+                       int64_t n, int h_kv, int r, int64_t nleaf, int64_t leaf_c_off, int64_t leaf_cnt_off,
+                       int64_t leaf_off_off, int64_t perm_off, const float *W, int k, int n_sink, int window,
+                       int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes,
+                       hipStream_t st);
+
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k);
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k);
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,

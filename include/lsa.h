@@ -196,6 +196,35 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
                int64_t ws_bytes, void *stream);
 
 /*
+ * Bytes of device workspace lsa_select_flat needs to run m rows in batches of
+ * up to 256 rows (*bytes).  Any workspace of at least the one-row size works;
+ * a smaller one runs the rows in smaller batches.
+ */
+int lsa_select_flat_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, int64_t *bytes);
+
+/*
+ * Flat search ("Latent sparse attention", bdtechtalks.com, "How latent sparse
+ * attention works": the query is compared against all cluster centroids,
+ * the alternative to the hierarchical search that follows a few branches per
+ * level).  The clusters are the leaves of the tree built by lsa_build_index:
+ * every non-empty leaf v is scored with fl32(u . centroid_L[v]) (u as in
+ * lsa_select); the leaves are visited in (score desc, id asc) order and the
+ * keys retrieved from them exactly as lsa_select retrieves keys from its
+ * candidate leaves (retrieval range, k, sinks and window, cutoff).  No level
+ * above the leaves is read.  On a tree with L = 1 both searches coincide.
+ *
+ * Arguments as in lsa_select (no beam).  ws (device, required) holds per row
+ * and KV head the score and eligible count of every leaf, 6 bytes a leaf;
+ * rows run in batches that fit ws_bytes (LSA_ENOSPC below the one-row size).
+ * The work per row is linear in the number of leaves, as the page notes for
+ * flat search.  Limits as lsa_select (beam excepted).
+ */
+int lsa_select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
+                    const lsa_index_desc *desc, const void *index, const float *W, int k, int n_sink,
+                    int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws,
+                    int64_t ws_bytes, void *stream);
+
+/*
  * Bytes of device workspace lsa_attend needs (*bytes).
  */
 int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64_t *bytes);

@@ -95,6 +95,17 @@ def test_entry_points_validate_before_touching_the_device():
                         None) == lsa.LSA_EINVAL          # negative window
     assert L.lsa_select(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 2, 8, 1 << 23, 1 << 23, fake, fake,
                         None, None, 0, None) == lsa.LSA_EUNSUPPORTED    # row longer than 2^24
+    # flat search: workspace required and sized per row
+    one = lsa.select_flat_workspace_bytes(1, 4, d)
+    assert one >= 2 * 4 ** 2 * 6 and lsa.select_flat_workspace_bytes(1000, 4, d) > one
+    assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 8, 0, 0, fake, fake, None, None, 0,
+                             None) == lsa.LSA_ENOSPC      # no workspace
+    assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 8, 0, 0, fake, fake, None, fake,
+                             one - 1, None) == lsa.LSA_ENOSPC
+    assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(d), fake, fake, 9000, 0, 0, fake, fake, None, fake,
+                             one, None) == lsa.LSA_EUNSUPPORTED    # k > 8192
+    assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 8, 0, 0, fake, fake, None, fake,
+                             one, None) == lsa.LSA_EINVAL
     # attend
     f = ctypes.c_float
     assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 3, 100, 64, fake, fake, 8, f(0), fake, None, None, 0,

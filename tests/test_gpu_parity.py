@@ -208,6 +208,60 @@ def test_sinks_and_window_match_oracle(lsa, name, over):
             _assert_exchange_zeroed(fws, w.m * w.h_kv, w.beam, w.h_q // w.h_kv, w.d)
 
 
+FLAT_CASES = ["tiny_4k", "ragged_bf16_b5", "multi_piece_root", "odd_r_deep", "flat_L1", "n_below_b", "single_key"]
+
+
+@pytest.mark.parametrize("name", FLAT_CASES)
+def test_flat_search_matches_oracle(lsa, name):
+    """Flat search (every leaf scored): rows bit for bit equal to the oracle's,
+    with and without sinks and a window, in one batch and in batches forced by
+    a one-row workspace; attention over them matches the oracle's."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", **dict(SMALL)[name]) if name != "tiny_4k" else _wl("tiny_4k")
+    w = w.replace(name=name)
+    data = _inputs(w, dev)
+    index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    gix = host_index(lsa.index_views(index, desc), desc)
+    c = data["cpu"]
+    Qh = np32(c["Q"])
+    pos = c["pos"].numpy()
+    small_ws = lsa.workspace(lsa.select_flat_workspace_bytes(1, w.h_q, desc), dev)
+    for k, n_sink, window in [(w.k, 0, 0), (max(1, w.k // 3), 4, 16), (min(w.n + 5, 8192), 0, 0)]:
+        ref = oracle.select_flat(Qh, pos, gix, c["W"].numpy(), k, n_sink=n_sink, window=window)
+        for label, ws in (("one batch", None), ("one-row batches", small_ws)):
+            say("flat", name, label, k, n_sink, window)
+            sel, cnt, cut = lsa.select_flat(data["Q"], data["pos"], index, desc, data["W"], k, ws=ws,
+                                            n_sink=n_sink, window=window)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt.cpu().numpy(), ref["count"], f"sel_count ({label})")
+            assert_same_bits(sel.cpu().numpy(), ref["sel"], f"sel ({label})")
+            assert_same_bits(cut.cpu().numpy(), ref["cutoff"], f"cutoff ({label})")
+        out, lse = lsa.attend(data["Q"], data["K"], data["V"], sel, cnt)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attend(Qh, np32(c["K"]), np32(c["V"]), ref["sel"], ref["count"])
+        _check_attention(out, lse, o_ref, lse_ref, TOL[w.torch_dtype])
+
+
+def test_flat_search_tied_scores(lsa):
+    """All-zero queries score every leaf 0: the order falls to the leaf ids,
+    and the boundary search has to resolve the ids' bits."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", n=30000, h_q=4, h_kv=1, d=32, dtype="f32", r=8, b=32, L=2, centres=500, m=3, mode="chunk")
+    data = _inputs(w, dev)
+    data["Q"].zero_()
+    data["cpu"]["Q"].zero_()
+    index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    gix = host_index(lsa.index_views(index, desc), desc)
+    ref = oracle.select_flat(np32(data["cpu"]["Q"]), data["cpu"]["pos"].numpy(), gix, data["cpu"]["W"].numpy(), 777)
+    sel, cnt, cut = lsa.select_flat(data["Q"], data["pos"], index, desc, data["W"], 777)
+    torch.cuda.synchronize()
+    assert_same_bits(cnt.cpu().numpy(), ref["count"], "sel_count")
+    assert_same_bits(sel.cpu().numpy(), ref["sel"], "sel")
+    assert_same_bits(cut.cpu().numpy(), ref["cutoff"], "cutoff")
+
+
 def _check_attention(out, lse, o_ref, lse_ref, tol):
     assert np.max(np.abs(np32(out) - o_ref)) <= tol
     g = lse.cpu().numpy()
@@ -371,4 +425,40 @@ def test_full_size_workload(lsa, name, sample_rows, replay_depth, local):
     assert np.max(np.abs(g[fin] - lse_ref[fin])) <= 1e-3
     say("mean sel_count", name, float(cnt.float().mean()))
     del K, V, index, views
+    torch.cuda.empty_cache()
+
+
+FLAT_FULL = [("decode_1m", None), ("prefill_1m", 16)]
+
+
+@pytest.mark.parametrize("name,sample_rows", FLAT_FULL, ids=[f[0] for f in FLAT_FULL])
+def test_flat_search_full_size(lsa, name, sample_rows):
+    """Flat search at the workload's real size (262144 leaves per KV head),
+    every row through the GPU, sampled rows against the oracle bit for bit."""
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[name]
+    say("generate", name)
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    pos = w.positions().to(dev)
+    Q = synth.make_queries(w, K, pos)
+    index, desc = lsa.build_index(K, W, w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    gix = host_index(lsa.index_views(index, desc), desc)
+    say("flat select", name)
+    sel, cnt, cut = lsa.select_flat(Q, pos, index, desc, W, w.k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.arange(w.m) if sample_rows is None else np.sort(rng.choice(w.m, size=sample_rows, replace=False))
+    ridx = torch.from_numpy(rows).to(dev)
+    say("oracle flat", name, len(rows))
+    ref = oracle.select_flat(np32(Q[ridx]), pos[ridx].cpu().numpy(), gix, np32(W), w.k)
+    assert_same_bits(cnt[ridx].cpu().numpy(), ref["count"], "sel_count")
+    assert_same_bits(sel[ridx].cpu().numpy(), ref["sel"], "sel")
+    assert_same_bits(cut[ridx].cpu().numpy(), ref["cutoff"], "cutoff")
+    s = sel.long()
+    valid = s >= 0
+    assert bool(torch.all(~valid | (s <= pos[:, None, None].long())))
+    assert bool(torch.all(valid.sum(-1) == cnt.long()))
+    del K, V, index
     torch.cuda.empty_cache()
