@@ -7,20 +7,29 @@
 // are visited in (score desc, id asc) order and the keys are retrieved exactly
 // as in the top-down selection (retrieval range, k, sinks and window).
 //
-// Three kernels per batch of rows:
-//   k_flat_latent  u = fl32(fl32(mean of the group's query heads) . W_g) per
-//                  (row, KV head);
-//   k_flat_score   1024 leaves x up to 64 rows of one KV head per workgroup:
-//                  a leaf's centroid row is loaded once into registers and
-//                  scored against every row's u (double accumulation in
-//                  ascending index order, two rows at a time), and its members
-//                  in each row's retrieval range are counted; writes the
-//                  orderable score and min(count, k) of every (row, leaf);
-//   k_flat_select  one workgroup per (row, KV head): weighted radix selection
-//                  over the 64-bit keys (score, ~leaf), up to 11 bits a round,
-//                  narrows the boundary to a bucket that fits in LDS together
-//                  with every key above it; those keys are collected, sorted
-//                  and filled in order.
+// Five kernels per batch of rows; a leaf's key is the 64-bit (orderable
+// score, ~leaf id), so keys are distinct and descend in visiting order:
+//   k_flat_latent    u = fl32(fl32(mean of the group's query heads) . W_g) per
+//                    (row, KV head);
+//   k_flat_score     1024 leaves x up to 64 rows of one KV head per workgroup:
+//                    a leaf's centroid row is loaded once into registers and
+//                    scored against every row's u (double accumulation in
+//                    ascending index order, two rows at a time), and its
+//                    members in each row's retrieval range are counted; writes
+//                    the score and min(count, k) of every (row, leaf), and the
+//                    keys of every S-th leaf as a sample;
+//   k_flat_threshold one workgroup per (row, KV head): sorts the sample and
+//                    takes as threshold T the key where the sample's weight
+//                    reaches 8k / S, an estimate of where the full weight
+//                    reaches 8k;
+//   k_flat_collect   4096 leaves of one (row, KV head) per workgroup: every key
+//                    >= T goes to the row's list, with its weight;
+//   k_flat_finish    one workgroup per (row, KV head): when the list weighs at
+//                    least k (so the k-th retrieved key is in it) and fits, it
+//                    is sorted and filled in order; otherwise an exact weighted
+//                    radix selection (up to 11 bits a round) over all leaves
+//                    narrows the boundary to a bucket that fits, and those keys
+//                    are sorted and filled.
 #include <algorithm>
 
 #include "common.h"
@@ -35,6 +44,8 @@ constexpr int kFlatRows = 64;       // rows per scoring workgroup
 constexpr int kFlatList = 16384;    // keys collected per (row, KV head) in LDS
 constexpr int kFlatBins = 2048;     // radix digits of up to 11 bits
 constexpr int64_t kFlatBatch = 256; // rows per batch the workspace query sizes for
+constexpr int kSampleMax = 1024;    // sampled keys per (row, KV head)
+constexpr int kCollect = 4096;      // leaves per collecting workgroup
 
 struct FlatArgs {
     const void *Q;              // the batch's first row
@@ -51,13 +62,22 @@ struct FlatArgs {
     float *U;                   // [mb][h_kv][r]
     uint32_t *sc;               // [mb][h_kv][nleaf] orderable scores
     uint16_t *wt;               // [mb][h_kv][nleaf] min(members in range, k); 0: not a candidate
+    int64_t S;                  // sample stride (0: no sample, every candidate is collected)
+    int ns;                     // sampled leaves (0, S, 2S, ...)
+    uint64_t *smp;              // [mb][h_kv][kSampleMax] sampled keys (0: not a candidate)
+    uint64_t *thr;              // [mb][h_kv] threshold key T
+    int32_t *lcnt, *lwt;        // [mb][h_kv] collected keys and their weight
+    uint64_t *lst;              // [mb][h_kv][kFlatList] collected keys
     int32_t *sel, *sel_count;   // the batch's rows
     float *sel_cutoff;
 };
 
+// W_g is staged in LDS 64 input rows (16 KB) at a time; the sum over the
+// input dimension continues in order across them.
 template <typename T>
 __global__ __launch_bounds__(256) void k_flat_latent(FlatArgs A) {
     __shared__ float qbar_s[256];
+    __shared__ __attribute__((aligned(16))) float w_s[64 * 64];
     const int64_t i = blockIdx.x;
     const int g = blockIdx.y;
     const int G = A.h_q / A.h_kv, d = A.d, r = A.r;
@@ -67,13 +87,18 @@ __global__ __launch_bounds__(256) void k_flat_latent(FlatArgs A) {
         for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
         qbar_s[t] = (float)(s / (double)G);
     }
-    __syncthreads();
-    if ((int)threadIdx.x < r) {
-        const float *Wg = A.W + (size_t)g * d * r;
-        double s = 0.0;
-        for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)Wg[(size_t)t * r + threadIdx.x], s);
-        A.U[((size_t)i * A.h_kv + g) * r + threadIdx.x] = (float)s;
+    const float *Wg = A.W + (size_t)g * d * r;
+    double s = 0.0;
+    for (int t0 = 0; t0 < d; t0 += 64) {
+        const int nt = min(64, d - t0);
+        if (((nt * r) & 3) == 0 && (((size_t)g * d * r + (size_t)t0 * r) & 3) == 0) g2s_rows<4>(w_s, nt * r, Wg + (size_t)t0 * r, nt * r, nt * r);
+        else for (int e = threadIdx.x; e < nt * r; e += blockDim.x) w_s[e] = Wg[(size_t)t0 * r + e];
+        __syncthreads();
+        if ((int)threadIdx.x < r)
+            for (int t = 0; t < nt; ++t) s = fma((double)qbar_s[t0 + t], (double)w_s[t * r + threadIdx.x], s);
+        __syncthreads();
     }
+    if ((int)threadIdx.x < r) A.U[((size_t)i * A.h_kv + g) * r + threadIdx.x] = (float)s;
 }
 
 // u . c in double, ascending index (u from LDS, 64-float padded; c in registers)
@@ -132,8 +157,14 @@ __global__ __launch_bounds__(256) void k_flat_score(FlatArgs A) {
         if (v >= A.nleaf) break;
         const size_t o = ((size_t)i0 * A.h_kv + g) * A.nleaf + v;
         const int c = cn[v];
+        const bool sampled = A.S > 0 && v % A.S == 0;
+        uint64_t *sp = A.smp + ((size_t)i0 * A.h_kv + g) * kSampleMax + (sampled ? v / A.S : 0);
+        const size_t ss = (size_t)A.h_kv * kSampleMax;           // sample stride between rows
         if (c <= 0) {
-            for (int rr = 0; rr < nr; ++rr) A.wt[o + rr * rs] = 0;
+            for (int rr = 0; rr < nr; ++rr) {
+                A.wt[o + rr * rs] = 0;
+                if (sampled) sp[rr * ss] = 0ull;
+            }
             continue;
         }
         const int32_t a0 = lo[v], a1 = lo[v + 1];
@@ -157,34 +188,237 @@ __global__ __launch_bounds__(256) void k_flat_score(FlatArgs A) {
             // two independent accumulation chains
             const double s0 = dot_row<RC>(u_s + rr * 64, cr, r);
             const double s1 = two ? dot_row<RC>(u_s + (rr + 1) * 64, cr, r) : 0.0;
-            A.sc[o + rr * rs] = e0 > 0 ? orderable((float)s0) : 0u;
+            const uint32_t o0 = e0 > 0 ? orderable((float)s0) : 0u, o1 = e1 > 0 ? orderable((float)s1) : 0u;
+            A.sc[o + rr * rs] = o0;
             A.wt[o + rr * rs] = (uint16_t)min(e0, A.k);
+            if (sampled) sp[rr * ss] = e0 > 0 ? ((uint64_t)o0 << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
             if (two) {
-                A.sc[o + (rr + 1) * rs] = e1 > 0 ? orderable((float)s1) : 0u;
+                A.sc[o + (rr + 1) * rs] = o1;
                 A.wt[o + (rr + 1) * rs] = (uint16_t)min(e1, A.k);
+                if (sampled) sp[(rr + 1) * ss] = e1 > 0 ? ((uint64_t)o1 << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
             }
         }
     }
 }
 
-__global__ __launch_bounds__(256) void k_flat_select(FlatArgs A) {
-    extern __shared__ __attribute__((aligned(16))) uint64_t lst[];   // [kFlatList] keys
-    int *hw = reinterpret_cast<int *>(lst + kFlatList);               // [kFlatBins] weight per digit
-    int *hc = hw + kFlatBins;                                          // [kFlatBins] keys per digit
-    __shared__ int scr[8], nlist_s, res_s[4];
-    __shared__ float cut_s;
-    const int64_t gi = blockIdx.x;                 // row * h_kv + KV head, within the batch
+// ---------------------------------------------------------------- threshold
+__global__ __launch_bounds__(256) void k_flat_threshold(FlatArgs A) {
+    __shared__ __attribute__((aligned(16))) uint64_t sk[256 * 4];
+    __shared__ int scr[8];
+    __shared__ uint64_t t_s;
+    const int64_t gi = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (A.S == 0) {                                   // few leaves: collect every candidate
+        if (tid == 0) { A.thr[gi] = 1ull; A.lcnt[gi] = 0; A.lwt[gi] = 0; }
+        return;
+    }
+    // thread t: sorted ranks 4t .. 4t + 3
+    uint64_t kk[4];
+    const uint64_t *sp = A.smp + (size_t)gi * kSampleMax;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = 4 * tid + u;
+        kk[u] = e < A.ns ? sp[e] : 0ull;
+    }
+    block_sort_desc<4>(kk, sk);
+    const uint16_t *wt = A.wt + (size_t)gi * A.nleaf;
+    int w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = kk[u] ? (int)wt[~(uint32_t)kk[u]] : 0;
+    const int local = w[0] + w[1] + w[2] + w[3];
+    int total;
+    int run = block_excl_scan(local, scr, &total);
+    const int target = (int)std::min<int64_t>((8 * (int64_t)A.k + A.S - 1) / A.S, INT32_MAX);
+    if (tid == 0) t_s = 1ull;                         // sample too light: collect every candidate
+    __syncthreads();
+    if (run < target && run + local >= target) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            run += w[u];
+            if (run >= target) { t_s = kk[u]; break; }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) { A.thr[gi] = t_s; A.lcnt[gi] = 0; A.lwt[gi] = 0; }
+}
+
+// ---------------------------------------------------------------- collect
+__global__ __launch_bounds__(256) void k_flat_collect(FlatArgs A) {
+    __shared__ uint64_t lk[kCollect];
+    __shared__ int n_s, w_s, base_s;
+    const int64_t gi = blockIdx.y;
+    const int64_t v0 = (int64_t)blockIdx.x * kCollect;
+    const int tid = threadIdx.x;
+    const uint64_t T = A.thr[gi];
+    const uint32_t *sc = A.sc + (size_t)gi * A.nleaf;
+    const uint16_t *wt = A.wt + (size_t)gi * A.nleaf;
+    if (tid == 0) { n_s = 0; w_s = 0; }
+    __syncthreads();
+    int wloc = 0;
+    auto take = [&](int64_t v, uint32_t s, int w) {
+        const uint64_t key = ((uint64_t)s << 32) | (uint64_t)(~(uint32_t)v);
+        if (w == 0 || key < T) return;
+        lk[atomicAdd(&n_s, 1)] = key;
+        wloc += w;
+    };
+    if ((A.nleaf & 7) == 0) {
+        // two steps of eight leaves per thread; every load issued before use
+        // (clamped indices; the rows start 16-byte aligned)
+        const int64_t nq = A.nleaf / 8, q0 = v0 / 8;
+        uint4 wv[2], s0[2], s1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t q = min(q0 + tid + 256 * u, nq - 1);
+            wv[u] = reinterpret_cast<const uint4 *>(wt)[q];
+            s0[u] = reinterpret_cast<const uint4 *>(sc)[2 * q];
+            s1[u] = reinterpret_cast<const uint4 *>(sc)[2 * q + 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t q = q0 + tid + 256 * u;
+            if (q >= nq) break;
+            const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            const uint32_t ss[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+#pragma unroll
+            for (int x = 0; x < 8; ++x) take(8 * q + x, ss[x], (int)((ww[x >> 1] >> (16 * (x & 1))) & 0xffffu));
+        }
+    } else {
+        for (int64_t v = v0 + tid; v < min<int64_t>(v0 + kCollect, A.nleaf); v += blockDim.x) take(v, sc[v], wt[v]);
+    }
+    atomicAdd(&w_s, wloc);
+    __syncthreads();
+    if (tid == 0) {
+        base_s = n_s > 0 ? atomicAdd(A.lcnt + gi, n_s) : 0;
+        if (w_s > 0) atomicAdd(A.lwt + gi, w_s);
+    }
+    __syncthreads();
+    uint64_t *dst = A.lst + (size_t)gi * kFlatList;
+    for (int e = tid; e < n_s; e += blockDim.x)
+        if (base_s + e < kFlatList) dst[base_s + e] = lk[e];
+}
+
+// ---------------------------------------------------------------- finish
+// Fill the row from the nl descending keys lst[0..nl) (LDS), in rounds of 256
+// ranks, one per thread: a block scan of the weights gives each leaf its
+// offset, and every thread copies its leaf's members (eight loads in flight).
+// Rounds stop once k keys are placed.
+LSA_DEV void fill_rounds(const FlatArgs &A, const uint64_t *lst, int nl, int *scr, float *cut_s) {
+    const int64_t gi = blockIdx.x;
     const int64_t i = gi / A.h_kv;
     const int g = (int)(gi % A.h_kv);
     const int tid = threadIdx.x;
+    const uint16_t *wt = A.wt + (size_t)gi * A.nleaf;
+    const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
+    const int32_t *pm = A.perm + (size_t)g * A.n;
+    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
+    int32_t *out = A.sel + (size_t)gi * A.row;
+    int carry = 0;
+    for (int base = 0; base < nl && carry < A.k; base += blockDim.x) {
+        const int e = base + tid;
+        const uint64_t key = e < nl ? lst[e] : 0ull;
+        const uint32_t v = key ? ~(uint32_t)key : 0u;
+        const int w = key ? (int)wt[v] : 0;
+        const int32_t a0 = lo[v], a1 = lo[v + 1];
+        int tot;
+        const int run = carry + block_excl_scan(w, scr, &tot);
+        if (w > 0 && run < A.k) {
+            const int take = min(w, A.k - run);
+            int f, c;
+            in_range(as, pm + a0, a1 - a0, f, c);
+            const int32_t *src = pm + a0 + f;
+            for (int t0 = 0; t0 < take; t0 += 8) {
+                int32_t x[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) x[t] = src[min(t0 + t, take - 1)];       // clamped: in the leaf
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (t0 + t < take) out[run + t0 + t] = x[t];
+            }
+            if (run + w >= A.k) *cut_s = unorderable((uint32_t)(key >> 32));
+        }
+        carry += tot;
+    }
+    const int count = min(A.k, carry);
+    for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
+    for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
+    __syncthreads();
+    if (tid == 0) {
+        A.sel_count[gi] = count + as.nloc;
+        if (A.sel_cutoff) A.sel_cutoff[gi] = *cut_s;
+    }
+}
+
+// Bitonic sort, descending, of keys[0..N) in LDS (N a power of two) by the
+// block; each thread's eight compare-exchanges of a stage are loaded before
+// any is stored.  Loops rather than unrolled stages keep the code small.
+LSA_DEV void lds_sort_desc(uint64_t *keys, int N) {
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t0 = threadIdx.x; t0 < (N >> 1); t0 += 8 * blockDim.x) {
+                uint64_t a[8], b[8];
+                int lo[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = min(t0 + u * (int)blockDim.x, (N >> 1) - 1);      // clamped: in bounds
+                    lo[u] = 2 * t - (t & (stride - 1));
+                    a[u] = keys[lo[u]];
+                    b[u] = keys[lo[u] + stride];
+                }
+                __builtin_amdgcn_sched_barrier(0);   // every load issued before the first store
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (t0 + u * (int)blockDim.x >= (N >> 1)) break;
+                    const bool desc = (lo[u] & size) == 0;     // segment sorted descending
+                    const bool sw = desc ? (b[u] > a[u]) : (a[u] > b[u]);
+                    if (sw) { keys[lo[u]] = b[u]; keys[lo[u] + stride] = a[u]; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Sort the nl keys of src (global memory or LDS) descending into lst (LDS, at
+// least kFlatList keys; may be src) and fill the row from them.  Up to 1024
+// keys are sorted in registers (four per thread), more in LDS.
+LSA_DEV void sort_and_fill_any(const FlatArgs &A, const uint64_t *src, int nl, uint64_t *lst, int *scr, float *cut_s) {
+    if (nl <= 1024) {
+        uint64_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = 4 * (int)threadIdx.x + u;
+            kk[u] = e < nl ? src[e] : 0ull;
+        }
+        block_sort_desc<4>(kk, lst);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lst[4 * threadIdx.x + u] = kk[u];
+        __syncthreads();
+    } else {
+        const int np2 = next_pow2(nl);
+        if (src != lst)
+            for (int e = threadIdx.x; e < nl; e += blockDim.x) lst[e] = src[e];
+        for (int e = nl + threadIdx.x; e < np2; e += blockDim.x) lst[e] = 0ull;
+        __syncthreads();
+        lds_sort_desc(lst, np2);
+    }
+    fill_rounds(A, lst, nl, scr, cut_s);
+}
+
+// Every key at or above the boundary bucket into lst (LDS), their number to
+// *nlist: exact weighted radix selection over all of the row's leaves.
+LSA_DEV void exact_boundary_list(const FlatArgs &A, uint64_t *lst, int *hw, int *hc, int *scr, int *res_s,
+                                 int *nlist) {
+    const int64_t gi = blockIdx.x;
+    const int tid = threadIdx.x;
+    // ---- exact boundary by weighted radix selection: the top `fixed` bits
+    // `prefix` of the key whose inclusion brings the weight of the keys above
+    // it to k, refined until the keys above the bucket and the bucket itself
+    // fit in LDS (at 64 bits the bucket is one key: the keys are distinct)
     const uint32_t *sc = A.sc + (size_t)gi * A.nleaf;
     const uint16_t *wt = A.wt + (size_t)gi * A.nleaf;
     auto keyof = [&](int64_t v) -> uint64_t { return ((uint64_t)sc[v] << 32) | (uint64_t)(~(uint32_t)v); };
-
-    // ---- boundary: the top `fixed` bits `prefix` of the key whose inclusion
-    // brings the weight of the keys above it to k; refined until the keys above
-    // the bucket and the bucket itself fit in LDS (at 64 bits the bucket is
-    // one key: the keys are distinct)
     uint64_t prefix = 0;
     int fixed = 0, want = A.k, nabove = 0;
     bool take_all = false;
@@ -203,8 +437,8 @@ __global__ __launch_bounds__(256) void k_flat_select(FlatArgs A) {
             atomicAdd(&hc[dg], 1);
         }
         __syncthreads();
-        // thread t owns the digits nb-1-t*per .. nb-t*per-per (descending): the
-        // weight of larger digits is an exclusive scan in thread order
+        // thread t owns the digits nb-1-t*per .. nb-t*per-per (descending):
+        // the weight of larger digits is an exclusive scan in thread order
         const int per = nb / 256;
         int sw = 0, sn = 0;
         for (int q = 0; q < per; ++q) {
@@ -238,68 +472,168 @@ __global__ __launch_bounds__(256) void k_flat_select(FlatArgs A) {
         __syncthreads();
         if (nabove + nbucket <= kFlatList) break;
     }
-
-    // ---- the keys above the bucket and in it (all candidates when their total
-    // weight is below k: fewer than k of them), sorted descending
-    if (tid == 0) { nlist_s = 0; cut_s = -INFINITY; }
+    // the keys above the bucket and in it (all candidates when their total
+    // weight is below k: fewer than k of them)
+    const uint64_t lo_key = take_all ? 1ull : prefix << (64 - fixed);
+    if (tid == 0) *nlist = 0;
     __syncthreads();
     for (int64_t v = tid; v < A.nleaf; v += blockDim.x) {
         if (wt[v] == 0) continue;
         const uint64_t key = keyof(v);
-        if (!take_all && (key >> (64 - fixed)) < prefix) continue;
-        const int at = atomicAdd(&nlist_s, 1);
+        if (key < lo_key) continue;
+        const int at = atomicAdd(nlist, 1);
         if (at < kFlatList) lst[at] = key;
     }
     __syncthreads();
-    const int nl = min(nlist_s, kFlatList);
-    const int np2 = next_pow2(max(nl, 2));
-    for (int e = nl + tid; e < np2; e += blockDim.x) lst[e] = 0ull;
-    __syncthreads();
-    block_bitonic_sort<uint64_t, true>(lst, np2);
+}
 
-    // ---- fill: leaves in order, each giving its members in the retrieval range
-    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
-    const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
-    const int32_t *pm = A.perm + (size_t)g * A.n;
-    const int chunk = (nl + blockDim.x - 1) / blockDim.x;
-    const int e0 = min(nl, tid * chunk), e1 = min(nl, e0 + chunk);
-    int local = 0;
-    for (int e = e0; e < e1; ++e) local += wt[~(uint32_t)lst[e]];
-    int total;
-    int run = block_excl_scan(local, scr, &total);
-    const int count = min(A.k, total);
-    int32_t *out = A.sel + (size_t)gi * A.row;
-    for (int e = e0; e < e1 && run < count; ++e) {
-        const uint32_t v = ~(uint32_t)lst[e];
-        const int w = wt[v];
-        const int take = min(w, count - run);
-        int f, c;
-        in_range(as, pm + lo[v], lo[v + 1] - lo[v], f, c);
-        const int32_t a = lo[v] + f;
-        for (int t = 0; t < take; ++t) out[run + t] = pm[a + t];
-        if (count == A.k && run + w >= A.k) cut_s = unorderable((uint32_t)(lst[e] >> 32));
-        run += w;
-    }
-    for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
-    for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
+// The smallest key B of the nl keys lst[0..nl) (LDS) such that the keys >= B
+// weigh at least k, widened to a bucket of the key's top bits that holds at
+// most 1024 keys (with every key above it) where the bits allow: the keys at
+// or above the returned value include every key retrieval reaches.  1 when the
+// whole list weighs less than k.  Weighted radix selection from the first bit
+// where the list's keys differ, up to 11 bits a round.
+LSA_DEV uint64_t narrow_list(const FlatArgs &A, const uint64_t *lst, int nl, int *hw, int *hc, int *scr, int *res_s,
+                             unsigned long long *red_s) {
+    const int64_t gi = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t *wt = A.wt + (size_t)gi * A.nleaf;
+    if (tid == 0) { red_s[0] = 0ull; red_s[1] = ~0ull; }
     __syncthreads();
-    if (tid == 0) {
-        A.sel_count[gi] = count + as.nloc;
-        if (A.sel_cutoff) A.sel_cutoff[gi] = cut_s;
+    unsigned long long mx = 0ull, mn = ~0ull;
+    for (int e = tid; e < nl; e += blockDim.x) { mx = max(mx, (unsigned long long)lst[e]); mn = min(mn, (unsigned long long)lst[e]); }
+    atomicMax(red_s, mx);
+    atomicMin(red_s + 1, mn);
+    __syncthreads();
+    mx = red_s[0];
+    mn = red_s[1];
+    __syncthreads();
+    if (nl == 0) return 1ull;
+    int fixed = (mx == mn) ? 64 : __clzll((long long)(mx ^ mn));
+    uint64_t prefix = fixed == 0 ? 0ull : (uint64_t)mx >> (64 - fixed);
+    int want = A.k, nabove = 0;
+    bool first = true;
+    while (fixed < 64) {
+        const int D = min(11, 64 - fixed);
+        const int nb = 1 << D, shift = 64 - fixed - D;
+        for (int e = tid; e < nb; e += blockDim.x) { hw[e] = 0; hc[e] = 0; }
+        __syncthreads();
+        for (int e0 = tid; e0 < nl; e0 += 8 * blockDim.x) {
+            uint64_t key[8];
+            int w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + u * (int)blockDim.x;
+                key[u] = e < nl ? lst[e] : 0ull;
+                const bool in = key[u] != 0ull && (fixed == 0 || (key[u] >> (64 - fixed)) == prefix);
+                w[u] = in ? (int)wt[~(uint32_t)key[u]] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (w[u] == 0) continue;
+                const int dg = (int)((key[u] >> shift) & (uint64_t)(nb - 1));
+                atomicAdd(&hw[dg], w[u]);
+                atomicAdd(&hc[dg], 1);
+            }
+        }
+        __syncthreads();
+        // thread t owns digits nb-1-t*per .. (descending), per >= 1
+        const int per = max(1, nb / (int)blockDim.x);
+        int sw = 0, sn = 0;
+        for (int q = 0; q < per; ++q) {
+            const int dg = nb - 1 - (tid * per + q);
+            if (dg >= 0) { sw += hw[dg]; sn += hc[dg]; }
+        }
+        int totw, totn;
+        const int bw = block_excl_scan(sw, scr, &totw);
+        const int bn = block_excl_scan(sn, scr, &totn);
+        if (first && totw < want) return 1ull;                   // the whole list is taken
+        first = false;
+        {
+            int run = bw, runn = bn;
+            for (int q = 0; q < per; ++q) {
+                const int dg = nb - 1 - (tid * per + q);
+                if (dg < 0) break;
+                const int h = hw[dg];
+                if (h > 0 && run < want && run + h >= want) {
+                    res_s[0] = dg; res_s[1] = want - run; res_s[2] = runn; res_s[3] = hc[dg];
+                }
+                run += h;
+                runn += hc[dg];
+            }
+        }
+        __syncthreads();
+        const int dg = res_s[0];
+        want = res_s[1];
+        nabove += res_s[2];
+        const int nbucket = res_s[3];
+        prefix = (prefix << D) | (uint64_t)dg;
+        fixed += D;
+        __syncthreads();
+        if (nabove + nbucket <= 1024) break;
     }
+    return prefix << (64 - fixed);
+}
+
+__global__ __launch_bounds__(256) void k_flat_finish(FlatArgs A) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t lst[];   // [kFlatList] keys
+    int *hw = reinterpret_cast<int *>(lst + kFlatList);               // [kFlatBins] weight per digit
+    int *hc = hw + kFlatBins;                                          // [kFlatBins] keys per digit
+    __shared__ int scr[8], nlist_s, res_s[4];
+    __shared__ unsigned long long red_s[2];
+    __shared__ float cut_s;
+    const int64_t gi = blockIdx.x;                 // row * h_kv + KV head, within the batch
+    const int tid = threadIdx.x;
+    if (tid == 0) cut_s = -INFINITY;
+    const int nl0 = A.lcnt[gi], wl0 = A.lwt[gi];
+    const uint64_t T = A.thr[gi];
+    uint64_t *glst = A.lst + (size_t)gi * kFlatList;
+    // the list holds every key >= T; it holds the k-th retrieved key when it
+    // weighs >= k, or when it holds every candidate (T = 1).  Otherwise the
+    // exact radix selection over every leaf builds it.
+    int nl;
+    if (nl0 <= kFlatList && (wl0 >= A.k || T == 1ull)) {
+        for (int e = tid; e < nl0; e += blockDim.x) lst[e] = glst[e];
+        nl = nl0;
+        __syncthreads();
+    } else {
+        exact_boundary_list(A, lst, hw, hc, scr, res_s, &nlist_s);
+        nl = min(nlist_s, kFlatList);
+    }
+    // keep the keys at or above the list's own boundary (in the row's global
+    // list, any order), then sort them and fill
+    const uint64_t lo_key = narrow_list(A, lst, nl, hw, hc, scr, res_s, red_s);
+    if (tid == 0) nlist_s = 0;
+    __syncthreads();
+    for (int e = tid; e < nl; e += blockDim.x) {
+        const uint64_t key = lst[e];
+        if (key >= lo_key) glst[atomicAdd(&nlist_s, 1)] = key;
+    }
+    __syncthreads();
+    const int nk = nlist_s;
+    __syncthreads();
+    sort_and_fill_any(A, glst, nk, lst, scr, &cut_s);
 }
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct FlatWs { float *U; uint32_t *sc; uint16_t *wt; size_t bytes; };
+struct FlatWs {
+    float *U; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt; uint64_t *lst; size_t bytes;
+};
 
 FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
     size_t cur = 0;
     FlatWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
-    w.U = (float *)take(sizeof(float) * (size_t)mb * h_kv * r);
-    w.sc = (uint32_t *)take(sizeof(uint32_t) * (size_t)mb * h_kv * nleaf);
-    w.wt = (uint16_t *)take(sizeof(uint16_t) * (size_t)mb * h_kv * nleaf);
+    const size_t groups = (size_t)mb * h_kv;
+    w.U = (float *)take(sizeof(float) * groups * r);
+    w.sc = (uint32_t *)take(sizeof(uint32_t) * groups * nleaf);
+    w.wt = (uint16_t *)take(sizeof(uint16_t) * groups * nleaf);
+    w.smp = (uint64_t *)take(sizeof(uint64_t) * groups * kSampleMax);
+    w.thr = (uint64_t *)take(sizeof(uint64_t) * groups);
+    w.lcnt = (int32_t *)take(sizeof(int32_t) * groups);
+    w.lwt = (int32_t *)take(sizeof(int32_t) * groups);
+    w.lst = (uint64_t *)take(sizeof(uint64_t) * groups * kFlatList);
     w.bytes = cur;
     return w;
 }
@@ -328,13 +662,16 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     const size_t shm = sizeof(uint64_t) * kFlatList + sizeof(int) * 2 * kFlatBins;
     if (!attr_set[dev]) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_flat_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipError_t e = hipFuncSetAttribute((const void *)k_flat_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)shm);
         if (e != hipSuccess) return e;
         attr_set[dev] = 1;
     }
     const int row = k + n_sink + window;
     const size_t esz = dtype == 0 ? 4 : 2;
+    // sample stride: none when every candidate fits the list, else at least
+    // 64 and at most kSampleMax samples
+    const int64_t S = nleaf <= kFlatList ? 0 : std::max<int64_t>(64, (nleaf + kSampleMax - 1) / kSampleMax);
     for (int64_t i0 = 0; i0 < m; i0 += mb) {
         const int64_t nb = std::min(mb, m - i0);
         FlatWs w = carve_flat_ws((char *)ws, nb, h_kv, r, nleaf);
@@ -348,16 +685,21 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
         A.perm = (const int32_t *)(index + perm_off);
         A.W = W; A.k = k; A.n_sink = n_sink; A.window = window; A.row = row;
         A.U = w.U; A.sc = w.sc; A.wt = w.wt;
+        A.S = S; A.ns = S > 0 ? (int)((nleaf + S - 1) / S) : 0;
+        A.smp = w.smp; A.thr = w.thr; A.lcnt = w.lcnt; A.lwt = w.lwt; A.lst = w.lst;
         A.sel = sel + (size_t)i0 * h_kv * row;
         A.sel_count = sel_count + (size_t)i0 * h_kv;
         A.sel_cutoff = sel_cutoff ? sel_cutoff + (size_t)i0 * h_kv : nullptr;
+        const unsigned groups = (unsigned)(nb * h_kv);
         if (dtype == 0) hipLaunchKernelGGL(k_flat_latent<float>, dim3((unsigned)nb, (unsigned)h_kv), dim3(256), 0, st, A);
         else hipLaunchKernelGGL(k_flat_latent<bf16_t>, dim3((unsigned)nb, (unsigned)h_kv), dim3(256), 0, st, A);
         const dim3 sgrid((unsigned)((nleaf + kFlatLeaves - 1) / kFlatLeaves), (unsigned)((nb + kFlatRows - 1) / kFlatRows),
                          (unsigned)h_kv);
         if (r == 64) hipLaunchKernelGGL(k_flat_score<64>, sgrid, dim3(256), 0, st, A);
         else hipLaunchKernelGGL(k_flat_score<0>, sgrid, dim3(256), 0, st, A);
-        hipLaunchKernelGGL(k_flat_select, dim3((unsigned)(nb * h_kv)), dim3(256), shm, st, A);
+        hipLaunchKernelGGL(k_flat_threshold, dim3(groups), dim3(256), 0, st, A);
+        hipLaunchKernelGGL(k_flat_collect, dim3((unsigned)((nleaf + kCollect - 1) / kCollect), groups), dim3(256), 0, st, A);
+        hipLaunchKernelGGL(k_flat_finish, dim3(groups), dim3(256), shm, st, A);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

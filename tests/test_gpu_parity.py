@@ -262,6 +262,33 @@ def test_flat_search_tied_scores(lsa):
     assert_same_bits(cut.cpu().numpy(), ref["cutoff"], "cutoff")
 
 
+@pytest.mark.parametrize("zero_q,k", [(False, 100), (False, 8192), (True, 100), (True, 8192)])
+def test_flat_search_large_leaf_table(lsa, zero_q, k):
+    """32768 leaves (more than fit in LDS): the sampled threshold (k = 100),
+    the exact radix fallback (k = 8192: the sample weighs too little), tied
+    scores that leave the order to the leaf ids, and an early row whose
+    candidates weigh less than k."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", n=20000, h_q=4, h_kv=1, d=32, dtype="f32", r=8, b=32, L=3, centres=400, m=5, mode="chunk")
+    data = _inputs(w, dev)
+    data["pos"][0] = 50
+    data["cpu"]["pos"][0] = 50
+    if zero_q:
+        data["Q"].zero_()
+        data["cpu"]["Q"].zero_()
+    index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    assert desc.nodes[desc.L] == 32768
+    gix = host_index(lsa.index_views(index, desc), desc)
+    ref = oracle.select_flat(np32(data["cpu"]["Q"]), data["cpu"]["pos"].numpy(), gix, data["cpu"]["W"].numpy(), k)
+    say("flat large table", zero_q, k)
+    sel, cnt, cut = lsa.select_flat(data["Q"], data["pos"], index, desc, data["W"], k)
+    torch.cuda.synchronize()
+    assert_same_bits(cnt.cpu().numpy(), ref["count"], "sel_count")
+    assert_same_bits(sel.cpu().numpy(), ref["sel"], "sel")
+    assert_same_bits(cut.cpu().numpy(), ref["cutoff"], "cutoff")
+
+
 def _check_attention(out, lse, o_ref, lse_ref, tol):
     assert np.max(np.abs(np32(out) - o_ref)) <= tol
     g = lse.cpu().numpy()
