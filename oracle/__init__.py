@@ -202,3 +202,34 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, count: 
     lib().oracle_attend(_p(Q), _p(K), _p(V), m, h_q, h_kv, n, d, _p(sel), _p(count), k,
                         float(scale), _p(out), _p(lse))
     return out, lse
+
+
+def pca_projection(K: np.ndarray, r: int):
+    """Training-free latent projection ("Latent sparse attention",
+    bdtechtalks.com, "How latent sparse attention works": principal component
+    analysis builds the indexing space without trained projections).
+
+    Per KV head g: C = (1/n) sum_j (k_j - mu)(k_j - mu)^T in float64 (mu the
+    mean key), its eigenvectors by numpy's symmetric eigensolver, the r with
+    the largest eigenvalues as the columns of W_g, largest first.  Each column
+    is signed so that its entry of largest magnitude (the first such) is
+    positive.  K [h, n, d] float32 -> (W [h, d, r] float32, eigenvalues [h, r]
+    float64)."""
+    K = np.asarray(K, dtype=np.float32)
+    h, n, d = K.shape
+    W = np.empty((h, d, r), np.float32)
+    ev = np.empty((h, r), np.float64)
+    for g in range(h):
+        X = K[g].astype(np.float64)
+        Xc = X - X.mean(axis=0)
+        C = (Xc.T @ Xc) / n
+        lam, vec = np.linalg.eigh(C)
+        order = np.argsort(-lam, kind="stable")[:r]
+        V = vec[:, order]
+        for c in range(r):
+            j = int(np.argmax(np.abs(V[:, c])))
+            if V[j, c] < 0:
+                V[:, c] = -V[:, c]
+        W[g] = V.astype(np.float32)
+        ev[g] = lam[order]
+    return W, ev

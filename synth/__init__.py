@@ -136,6 +136,28 @@ def make_queries(w: Workload, K: torch.Tensor, pos: torch.Tensor, seed: Optional
     return Q
 
 
+def make_lowrank_keys(n: int, h: int, d: int, dtype=torch.bfloat16, seed: int = 4000, decay: float = 0.97,
+                      noise: float = 0.05, device="cpu") -> torch.Tensor:
+    """Keys with a decaying spectrum, [h, n, d]: per head, K = (Z * s) R^T + mu
+    + noise * eps with Z, eps ~ N(0, I), s_i = decay^i (distinct principal
+    scales), R a random orthogonal matrix (QR of a Gaussian matrix) and
+    mu ~ N(0, I).  Rounded once to `dtype`."""
+    g = _gen(seed, device)
+    K = torch.empty((h, n, d), dtype=dtype, device=device)
+    sc = decay ** torch.arange(d, dtype=torch.float32, device=device)
+    chunk = 1 << 20
+    for hh in range(h):
+        R, _ = torch.linalg.qr(torch.randn((d, d), generator=g, device=device, dtype=torch.float64))
+        R = R.float()
+        mu = torch.randn((d,), generator=g, device=device)
+        for s0 in range(0, n, chunk):
+            e = min(n, s0 + chunk)
+            Z = torch.randn((e - s0, d), generator=g, device=device) * sc
+            eps = torch.randn((e - s0, d), generator=g, device=device)
+            K[hh, s0:e] = (Z @ R.T + mu + noise * eps).to(dtype)
+    return K
+
+
 def make_workload(w: Workload, device="cpu", m: Optional[int] = None, pos: Optional[torch.Tensor] = None):
     """Everything one pass of the layer needs: K, V, W_lat, Q and query positions."""
     K, V = make_kv(w, device)

@@ -409,3 +409,48 @@ def test_flat_select_equals_descent_with_every_branch_kept(oracle_lib, b, L):
         h = oracle.select(Q, pos, ix, W, b ** max(L - 1, 0), k, n_sink=ns, window=nw)
         assert np.array_equal(f["sel"], h["sel"]) and np.array_equal(f["count"], h["count"])
         assert np.array_equal(f["cutoff"], h["cutoff"])
+
+
+# --------------------------------------------------------------------------- PCA projection
+def test_pca_closed_form_covariance(oracle_lib):
+    """Keys mu +- s_i R_i (i < d) have mean mu and covariance R diag(2 s_i^2 / n) R^T
+    exactly: the projection's columns are R's columns (signed), its eigenvalues
+    2 s_i^2 / n."""
+    rng = np.random.default_rng(5)
+    d, r = 24, 10
+    R, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    s = 2.0 ** (-np.arange(d) / 3.0)
+    mu = rng.standard_normal(d)
+    rows = []
+    for i in range(d):
+        rows += [mu + s[i] * R[:, i], mu - s[i] * R[:, i]]
+    K = np.array(rows, np.float32)[None]                      # [1, 2d, d]
+    W, ev = oracle.pca_projection(K, r)
+    n = 2 * d
+    np.testing.assert_allclose(ev[0], 2 * s[:r] ** 2 / n, rtol=2e-5)
+    for c in range(r):
+        v = R[:, c] * np.sign(R[np.argmax(np.abs(R[:, c])), c])
+        np.testing.assert_allclose(W[0][:, c], v, atol=3e-5)
+
+
+def test_pca_matches_sklearn_and_is_orthonormal(oracle_lib):
+    from sklearn.decomposition import PCA
+    K = synth.make_lowrank_keys(3000, 2, 32, dtype=torch.float32, seed=11).numpy()
+    r = 12
+    W, ev = oracle.pca_projection(K, r)
+    for g in range(2):
+        p = PCA(n_components=r, svd_solver="full").fit(K[g].astype(np.float64))
+        comp = p.components_                                   # rows, any sign
+        for c in range(r):
+            assert abs(abs(float(comp[c] @ W[g][:, c].astype(np.float64))) - 1.0) < 1e-6
+            j = int(np.argmax(np.abs(W[g][:, c])))
+            assert W[g][j, c] > 0
+        # sklearn divides by n - 1
+        np.testing.assert_allclose(ev[g] * 3000 / 2999, p.explained_variance_, rtol=1e-9)
+        np.testing.assert_allclose(W[g].T.astype(np.float64) @ W[g].astype(np.float64), np.eye(r), atol=1e-6)
+        assert np.all(np.diff(ev[g]) < 0)
+        X = K[g].astype(np.float64)
+        Xc = X - X.mean(0)
+        C = Xc.T @ Xc / 3000
+        resid = C @ W[g].astype(np.float64) - W[g].astype(np.float64) * ev[g][None, :]
+        assert np.abs(resid).max() < 1e-6 * ev[g][0]
