@@ -28,7 +28,7 @@ MAX_LEVELS = 6
 EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
            "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend", "lsa_select_flat_workspace_bytes",
-           "lsa_select_flat"]
+           "lsa_select_flat", "lsa_pca_workspace_bytes", "lsa_pca_projection"]
 
 
 class IndexDesc(ctypes.Structure):
@@ -72,6 +72,8 @@ def lib():
         L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, P, P, P, P, i64, P]
         L.lsa_select_flat_workspace_bytes.argtypes = [i64, i32, D, ctypes.POINTER(i64)]
         L.lsa_select_flat.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, P, P, P, P, i64, P]
+        L.lsa_pca_workspace_bytes.argtypes = [i64, i32, i32, ctypes.POINTER(i64)]
+        L.lsa_pca_projection.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, i64, P]
         L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_attend.argtypes = [P, P, P, i32, i64, i32, i32, i64, i32, P, P, i32, ctypes.c_float,
                                  P, P, P, i64, P]
@@ -336,3 +338,26 @@ def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel: torch.Tensor,
                             0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_attend")
     return out, lse
+
+
+def pca_workspace_bytes(n: int, h_kv: int, d: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_pca_workspace_bytes(n, h_kv, d, ctypes.byref(v)), "lsa_pca_workspace_bytes")
+    return v.value
+
+
+def pca_projection(K: torch.Tensor, r: int, W: Optional[torch.Tensor] = None, want_eigenvalues: bool = True,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """K [h_kv, n, d] (f32/bf16) -> (W f32 [h_kv, d, r], eigenvalues f64 [h_kv, r] or None)."""
+    _need(K, "K")
+    h, n, d = K.shape
+    if W is None:
+        W = torch.empty((h, d, r), dtype=torch.float32, device=K.device)
+    _need_out(W, "W", (h, d, r), torch.float32)
+    ev = torch.empty((h, r), dtype=torch.float64, device=K.device) if want_eigenvalues else None
+    if ws is None:
+        ws = torch.empty(pca_workspace_bytes(n, h, d), dtype=torch.uint8, device=K.device)
+    _check(lib().lsa_pca_projection(_ptr(K), _dtype_code(K), n, h, d, r, _ptr(W), _ptr(ev), _ptr(ws), ws.numel(),
+                                    _stream(stream)),
+           "lsa_pca_projection")
+    return W, ev

@@ -186,6 +186,24 @@ int lsa_select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const i
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
+int lsa_pca_workspace_bytes(int64_t n, int h_kv, int d, int64_t *bytes) {
+    if (n < 1 || h_kv < 1 || d < 2 || !bytes) return LSA_EINVAL;
+    if (d > 128) return LSA_EUNSUPPORTED;
+    *bytes = lsa::pca_workspace_bytes(n, h_kv);
+    return LSA_OK;
+}
+
+int lsa_pca_projection(const void *K, int dtype, int64_t n, int h_kv, int d, int r, float *W, double *eigenvalues,
+                       void *ws, int64_t ws_bytes, void *stream) {
+    if (n < 1 || n > INT32_MAX || h_kv < 1 || d < 2 || r < 1 || r > d) return LSA_EINVAL;
+    if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
+    if (d > 128) return LSA_EUNSUPPORTED;
+    if (!K || !W) return LSA_EINVAL;
+    if (!ws || ws_bytes < lsa::pca_workspace_bytes(n, h_kv)) return LSA_ENOSPC;
+    hipError_t e = lsa::pca_projection(K, dtype, n, h_kv, d, r, W, eigenvalues, ws, (hipStream_t)stream);
+    return e == hipSuccess ? LSA_OK : LSA_EHIP;
+}
+
 int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64_t *bytes) {
     if (m < 0 || h_q < 1 || h_kv < 1 || d < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % h_kv != 0) return LSA_EINVAL;

@@ -110,6 +110,15 @@ LSA_DEV float wave_max_f(float v) {
     v = fmaxf(v, xor_lane_f<4>(v)); v = fmaxf(v, xor_lane_f<2>(v)); v = fmaxf(v, xor_lane_f<1>(v));
     return v;
 }
+LSA_DEV double wave_max_d(double v) {
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<1>((uint64_t)__double_as_longlong(v))));
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<2>((uint64_t)__double_as_longlong(v))));
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<4>((uint64_t)__double_as_longlong(v))));
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<8>((uint64_t)__double_as_longlong(v))));
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<16>((uint64_t)__double_as_longlong(v))));
+    v = fmax(v, __longlong_as_double((long long)xor_lane64<32>((uint64_t)__double_as_longlong(v))));
+    return v;
+}
 LSA_DEV float wave_sum_f(float v) {
     v += xor_lane_f<32>(v); v += xor_lane_f<16>(v); v += xor_lane_f<8>(v);
     v += xor_lane_f<4>(v); v += xor_lane_f<2>(v); v += xor_lane_f<1>(v);

@@ -31,6 +31,10 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
                        int32_t *sel, int32_t *sel_count, float *sel_cutoff, void *ws, int64_t ws_bytes,
                        hipStream_t st);
 
+int64_t pca_workspace_bytes(int64_t n, int h);
+hipError_t pca_projection(const void *K, int dtype, int64_t n, int h, int d, int r, float *W, double *evals, void *ws,
+                          hipStream_t st);
+
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k);
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k);
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,

@@ -225,6 +225,37 @@ int lsa_select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const i
                     int64_t ws_bytes, void *stream);
 
 /*
+ * Bytes of device workspace lsa_pca_projection needs for n keys of h_kv KV
+ * heads (*bytes): about 128 KB per 8192 keys and head.
+ */
+int lsa_pca_workspace_bytes(int64_t n, int h_kv, int d, int64_t *bytes);
+
+/*
+ * Training-free latent projection ("Latent sparse attention", bdtechtalks.com,
+ * "How latent sparse attention works": principal component analysis builds
+ * the indexing space without trained projection matrices).  Per KV head g:
+ *   mu = mean of the n keys, C = (1/n) sum_j (k_j - mu)(k_j - mu)^T (double),
+ *   W[g] = the eigenvectors of C with the r largest eigenvalues, largest
+ *   first, each signed so that its entry of largest magnitude (the first such)
+ *   is positive, rounded to fp32.
+ * The result is a W for lsa_build_index / lsa_select (centring does not
+ * change which clusters a query selects: it shifts every centroid's score by
+ * the same amount).
+ *
+ *   K         device, [h_kv][n][d] of `dtype`
+ *   W         device out, float [h_kv][d][r]
+ *   eigenvalues device out or NULL, double [h_kv][r]
+ *   ws        device workspace of lsa_pca_workspace_bytes bytes
+ * Sums are taken in a fixed order (results are deterministic); the
+ * eigenvectors come from cyclic Jacobi rotations run to convergence, so they
+ * agree with any other symmetric eigensolver to within the conditioning of
+ * the eigenproblem (close eigenvalues give ill-determined eigenvectors).
+ * Limits: 2 <= d <= 128, 1 <= r <= d, 1 <= n <= 2^31 - 1.
+ */
+int lsa_pca_projection(const void *K, int dtype, int64_t n, int h_kv, int d, int r, float *W,
+                       double *eigenvalues, void *ws, int64_t ws_bytes, void *stream);
+
+/*
  * Bytes of device workspace lsa_attend needs (*bytes).
  */
 int lsa_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k, int64_t *bytes);

@@ -106,6 +106,11 @@ def test_entry_points_validate_before_touching_the_device():
                              one, None) == lsa.LSA_EUNSUPPORTED    # k > 8192
     assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 8, 0, 0, fake, fake, None, fake,
                              one, None) == lsa.LSA_EINVAL
+    # PCA projection
+    assert L.lsa_pca_projection(fake, 0, 100, 2, 129, 8, fake, None, fake, 1 << 40, None) == lsa.LSA_EUNSUPPORTED
+    assert L.lsa_pca_projection(fake, 0, 100, 2, 64, 65, fake, None, fake, 1 << 40, None) == lsa.LSA_EINVAL
+    assert L.lsa_pca_projection(fake, 0, 100, 2, 64, 8, fake, None, fake, 16, None) == lsa.LSA_ENOSPC
+    assert lsa.pca_workspace_bytes(1 << 20, 4, 128) >= 4 * 128 * 128 * 8 * 128
     # attend
     f = ctypes.c_float
     assert L.lsa_attend(fake, fake, fake, 0, 1, 4, 3, 100, 64, fake, fake, 8, f(0), fake, None, None, 0,
