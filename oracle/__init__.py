@@ -233,3 +233,70 @@ def pca_projection(K: np.ndarray, r: int):
         W[g] = V.astype(np.float32)
         ev[g] = lam[order]
     return W, ev
+
+
+def index_insert(index: Index, K_new: np.ndarray, W: np.ndarray) -> Index:
+    """Incremental insertion of keys appended to the cache ("Latent Sparse
+    Attention Breaks Through the Million-Token Context Bottleneck",
+    kongchang.com, "How LSA Sidesteps Per-Key Scoring with Hierarchical
+    Clustering": the key index is precomputed and updated).
+
+    K_new [h, m, d] float32 are the keys at positions n .. n + m - 1.  Readings:
+      - each new key's latent z = fl32(k . W_g) descends from the root to the
+        nearest non-empty child at every level (squared Euclidean distance in
+        double, dimensions ascending, each difference and square rounded once;
+        ties to the smaller child), against the centroids as they were before
+        the batch;
+      - every node on a path then takes its new keys: with c its old count and
+        S the double sum of their latents (keys ascending),
+        centroid = fl32((c * centroid + S) / (c + #new)), count = c + #new
+        (one new key: the online k-means update);
+      - a leaf's members are its old members followed by its new keys
+        (ascending positions).
+    Returns the tree over n + m keys."""
+    ix = index
+    K_new = np.ascontiguousarray(K_new, np.float32)
+    W = np.ascontiguousarray(W, np.float32)
+    h, m, d = K_new.shape
+    n, r, b, L = ix.n, ix.r, ix.b, ix.L
+    Cs = [ix.C(l).copy() for l in range(1, L + 1)]
+    cnts = [ix.cnt(l).copy() for l in range(1, L + 1)]
+    nleaf = b ** L
+    leaf_off = np.zeros((h, nleaf + 1), np.int64)
+    perm = np.zeros((h, n + m), np.int32)
+    for g in range(h):
+        Z = project(K_new[g], W[g]).astype(np.float64)          # [m, r], exact fp32 values
+        paths = np.zeros((m, L), np.int64)
+        for j in range(m):
+            u = 0
+            for l in range(L):
+                ch = u * b + np.arange(b)
+                cand = ch[ix.cnt(l + 1)[g][ch] > 0]
+                Cc = ix.C(l + 1)[g][cand].astype(np.float64)   # centroids before the batch
+                dist = np.zeros(len(cand))
+                for i in range(r):
+                    t = Z[j, i] - Cc[:, i]
+                    dist = dist + t * t
+                u = int(cand[int(np.argmin(dist))])
+                paths[j, l] = u
+        for l in range(L):
+            for v in np.unique(paths[:, l]):
+                js = np.nonzero(paths[:, l] == v)[0]
+                S = np.zeros(r)
+                for j in js:
+                    S = S + Z[j]
+                c_old = float(ix.cnt(l + 1)[g][v])
+                c0 = ix.C(l + 1)[g][v].astype(np.float64)
+                Cs[l][g][v] = ((c_old * c0 + S) / (c_old + len(js))).astype(np.float32)
+                cnts[l][g][v] = int(c_old) + len(js)
+        lo = ix.leaf_off[g]
+        pos = 0
+        for v in range(nleaf):
+            old = ix.perm[g][lo[v]:lo[v + 1]]
+            new = n + np.nonzero(paths[:, L - 1] == v)[0]
+            leaf_off[g, v] = pos
+            perm[g, pos:pos + len(old)] = old
+            perm[g, pos + len(old):pos + len(old) + len(new)] = new
+            pos += len(old) + len(new)
+        leaf_off[g, nleaf] = pos
+    return Index.from_levels(n + m, h, r, b, L, Cs, cnts, leaf_off, perm)

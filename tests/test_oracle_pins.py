@@ -49,6 +49,16 @@ def test_hand_worked_tree_and_selection(oracle_lib):
         assert out["count"][0, 0] == q["count"]
         assert out["cutoff"][0, 0] == _frac32(q["cutoff"])
         assert out["nscored"][0, 0] == q["nscored"]
+    for q in g["insertions"]:
+        ix = trees[q["tree"]]
+        out = oracle.index_insert(ix, np.array(q["keys"], np.float32)[None], W)
+        assert out.n == ix.n + len(q["keys"])
+        assert np.array_equal(out.cnt(1)[0], q["level1_counts"])
+        assert np.array_equal(out.cnt(2)[0], q["level2_counts"])
+        assert np.array_equal(out.C(1)[0], np.array([[_frac32(x) for x in row] for row in q["level1_centroids"]]))
+        assert np.array_equal(out.C(2)[0], np.array([[_frac32(x) for x in row] for row in q["level2_centroids"]]))
+        lo = out.leaf_off[0]
+        assert [list(out.perm[0][lo[v]:lo[v + 1]]) for v in range(len(lo) - 1)] == q["leaf_members"]
     for q in g["flat_queries"]:
         ix = trees[q["tree"]]
         Q = np.array(q["q"], np.float32)[None, None]
@@ -454,3 +464,60 @@ def test_pca_matches_sklearn_and_is_orthonormal(oracle_lib):
         C = Xc.T @ Xc / 3000
         resid = C @ W[g].astype(np.float64) - W[g].astype(np.float64) * ev[g][None, :]
         assert np.abs(resid).max() < 1e-6 * ev[g][0]
+
+
+# --------------------------------------------------------------------------- incremental insertion
+@pytest.mark.parametrize("b,L,m", [(4, 3, 1), (4, 3, 37), (8, 2, 200), (3, 2, 5), (16, 1, 50)])
+def test_insert_invariants_and_descent(oracle_lib, b, L, m):
+    """After inserting m keys: the tree is a valid tree over n + m keys, every
+    old key keeps its leaf, every node's count grows by the new keys below it,
+    each new key sits in the leaf a greedy nearest-non-empty-child descent
+    (numpy distances, pre-batch centroids) reaches, and every centroid stays
+    within float32 rounding of its members' mean when the tree's centroids
+    were exact means."""
+    n = 500
+    w, K, V, W, Q, pos = _small_case(b=b, L=L, seed=80 + b + m, n=n + m, m=3)
+    ix = oracle.build_index(K[:, :n], W, b, L, 5)
+    out = oracle.index_insert(ix, K[:, n:], W)
+    Zs = [oracle.project(K[g], W[g]) for g in range(w.h_kv)]
+    Cs = [out.C(l) for l in range(1, L + 1)]
+    cnts = [out.cnt(l) for l in range(1, L + 1)]
+    # structure (the centroid check is loose: a running mean from rounded centroids)
+    check_tree(Zs, Cs, cnts, out.leaf_off, out.perm, b, L, ulps=64)
+    for g in range(w.h_kv):
+        leaf_old = np.empty(n, np.int64)
+        for v in range(b ** L):
+            leaf_old[ix.perm[g][ix.leaf_off[g][v]:ix.leaf_off[g][v + 1]]] = v
+        leaf_new = np.empty(n + m, np.int64)
+        for v in range(b ** L):
+            leaf_new[out.perm[g][out.leaf_off[g][v]:out.leaf_off[g][v + 1]]] = v
+        assert np.array_equal(leaf_new[:n], leaf_old)
+        for j in range(m):
+            z = Zs[g][n + j].astype(np.float64)
+            u = 0
+            for l in range(1, L + 1):
+                ch = u * b + np.arange(b)
+                ch = ch[ix.cnt(l)[g][ch] > 0]
+                dist = ((ix.C(l)[g][ch].astype(np.float64) - z) ** 2).sum(axis=1)
+                u = int(ch[np.argmin(dist)])
+            assert leaf_new[n + j] == u
+        for l in range(1, L + 1):
+            added = np.zeros(b ** l, np.int64)
+            for j in range(m):
+                added[leaf_new[n + j] // b ** (L - l)] += 1
+            assert np.array_equal(out.cnt(l)[g], ix.cnt(l)[g] + added)
+
+
+def test_insert_then_dense_select_sees_new_keys(oracle_lib):
+    """Every key, old or new, is reachable after insertion: beam over every
+    cluster and k = n + m give dense causal attention over the grown cache."""
+    b, L, n, m = 3, 3, 400, 60
+    w, K, V, W, Q, pos = _small_case(b=b, L=L, seed=91, n=n + m, m=6)
+    ix = oracle.build_index(K[:, :n], W, b, L, 5)
+    out = oracle.index_insert(ix, K[:, n:], W)
+    sel = oracle.select(Q, pos, out, W, beam=b ** (L - 1), k=n + m)
+    o, _ = oracle.attend(Q, K, V, sel["sel"], sel["count"])
+    keys = np.arange(n + m)
+    mask = np.broadcast_to((keys[None, :] <= pos[:, None])[:, None, :], (len(pos), w.h_q, n + m)).copy()
+    ref = _sdpa_masked(Q, K, V, mask, 1.0 / np.sqrt(w.d))
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
