@@ -28,7 +28,8 @@ MAX_LEVELS = 6
 EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
            "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend", "lsa_select_flat_workspace_bytes",
-           "lsa_select_flat", "lsa_pca_workspace_bytes", "lsa_pca_projection"]
+           "lsa_select_flat", "lsa_pca_workspace_bytes", "lsa_pca_projection",
+           "lsa_index_insert_workspace_bytes", "lsa_index_insert"]
 
 
 class IndexDesc(ctypes.Structure):
@@ -72,6 +73,8 @@ def lib():
         L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, P, P, P, P, i64, P]
         L.lsa_select_flat_workspace_bytes.argtypes = [i64, i32, D, ctypes.POINTER(i64)]
         L.lsa_select_flat.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, P, P, P, P, i64, P]
+        L.lsa_index_insert_workspace_bytes.argtypes = [i64, D, ctypes.POINTER(i64)]
+        L.lsa_index_insert.argtypes = [P, i32, i64, i32, P, D, P, i64, P, i64, P]
         L.lsa_pca_workspace_bytes.argtypes = [i64, i32, i32, ctypes.POINTER(i64)]
         L.lsa_pca_projection.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, i64, P]
         L.lsa_attend_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64)]
@@ -361,3 +364,28 @@ def pca_projection(K: torch.Tensor, r: int, W: Optional[torch.Tensor] = None, wa
                                     _stream(stream)),
            "lsa_pca_projection")
     return W, ev
+
+
+def index_insert_workspace_bytes(m: int, desc: IndexDesc) -> int:
+    v = ctypes.c_int64()
+    _check(lib().lsa_index_insert_workspace_bytes(m, ctypes.byref(desc), ctypes.byref(v)),
+           "lsa_index_insert_workspace_bytes")
+    return v.value
+
+
+def index_insert(K_new: torch.Tensor, W: torch.Tensor, index: torch.Tensor, desc: IndexDesc,
+                 ws: Optional[torch.Tensor] = None, stream=None) -> IndexDesc:
+    """Insert the keys K_new [h_kv, m, d] (positions desc.n ..) into `index` in
+    place; `index` must hold the layout for desc.n + m keys.  Returns the new
+    descriptor (desc itself is left unchanged)."""
+    _need(K_new, "K_new"); _need(W, "W"); _need(index, "index")
+    h, m, d = K_new.shape
+    if h != desc.h_kv:
+        raise ValueError("K_new must have one row block per KV head of the index")
+    out = IndexDesc.from_buffer_copy(desc)
+    if ws is None:
+        ws = torch.empty(index_insert_workspace_bytes(m, desc), dtype=torch.uint8, device=K_new.device)
+    _check(lib().lsa_index_insert(_ptr(K_new), _dtype_code(K_new), m, d, _ptr(W), ctypes.byref(out), _ptr(index),
+                                  index.numel(), _ptr(ws), ws.numel(), _stream(stream)),
+           "lsa_index_insert")
+    return out

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "liblsa.so")
-SOURCES = ["api.hip", "build.hip", "select.hip", "attend.hip", "decode.hip", "flat.hip", "pca.hip"]
+SOURCES = ["api.hip", "build.hip", "select.hip", "attend.hip", "decode.hip", "flat.hip", "pca.hip", "insert.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions stay off (hand-written or compiler-made)
@@ -31,7 +31,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(LIBDIR, s.replace(".hip", ".o"))
         objs.append(obj)
         jobs.append((src, obj))
-    with ThreadPoolExecutor(max_workers=min(7, len(jobs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda j: _compile(*j), jobs))
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)

@@ -113,6 +113,39 @@ int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const 
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
+int lsa_index_insert_workspace_bytes(int64_t m, const lsa_index_desc *desc, int64_t *bytes) {
+    int rc = check_desc(desc);
+    if (rc != LSA_OK) return rc;
+    if (m < 1 || !bytes) return LSA_EINVAL;
+    if (m > 4096) return LSA_EUNSUPPORTED;
+    *bytes = lsa::insert_workspace_bytes(m, desc->n, desc->h_kv, desc->r, desc->L, desc->nodes[desc->L]);
+    return LSA_OK;
+}
+
+int lsa_index_insert(const void *K_new, int dtype, int64_t m, int d, const float *W, lsa_index_desc *desc,
+                     void *index, int64_t index_bytes, void *ws, int64_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != LSA_OK) return rc;
+    if (m < 1 || d < 1) return LSA_EINVAL;
+    if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
+    if (m > 4096 || d > 256) return LSA_EUNSUPPORTED;
+    if (desc->n + m > INT32_MAX) return LSA_EUNSUPPORTED;
+    if (!K_new || !W || !index) return LSA_EINVAL;
+    lsa_index_desc grown;
+    rc = lsa_index_layout(desc->n + m, desc->h_kv, desc->r, desc->b, desc->L, &grown);
+    if (rc != LSA_OK) return rc;
+    if (grown.perm_off != desc->perm_off || grown.leaf_off_off != desc->leaf_off_off) return LSA_EINVAL;
+    if (index_bytes < grown.bytes) return LSA_ENOSPC;
+    const int64_t need = lsa::insert_workspace_bytes(m, desc->n, desc->h_kv, desc->r, desc->L, desc->nodes[desc->L]);
+    if (!ws || ws_bytes < need) return LSA_ENOSPC;
+    hipError_t e = lsa::index_insert(K_new, dtype, m, d, W, (char *)index, desc->n, desc->h_kv, desc->r, desc->b,
+                                     desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
+                                     desc->perm_off, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return LSA_EHIP;
+    *desc = grown;
+    return LSA_OK;
+}
+
 int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
                                int n_sink, int window, int64_t *bytes) {
     int rc = check_desc(desc);

@@ -165,22 +165,6 @@ __global__ void k_init(const int32_t *__restrict__ off_prev, const int32_t *__re
 }
 
 // ---------------------------------------------------------------- Lloyd round
-// Squared Euclidean distance in double, dimensions ascending; the difference
-// of two floats and its square are each rounded once, then added.
-LSA_DEV double sq_dist(const float *z, const float *cs, int r) {
-#pragma clang fp contract(off)
-    double dist = 0.0;
-#pragma unroll
-    for (int x = 0; x < 64; ++x) {
-        if (x < r) {
-            const double diff = (double)z[x] - (double)cs[x];
-            const double sq = diff * diff;
-            dist = dist + sq;
-        }
-    }
-    return dist;
-}
-
 __global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pieces, const int32_t *__restrict__ total,
                                                    const int32_t *__restrict__ off_prev,
                                                    const int32_t *__restrict__ perm_prev, const float *__restrict__ Z,
@@ -396,6 +380,16 @@ static inline unsigned grid1(int64_t tot, int bs) {
     if (g > (1 << 20)) g = 1 << 20;
     if (g < 1) g = 1;
     return (unsigned)g;
+}
+
+hipError_t project_keys(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, float *Z,
+                        hipStream_t st) {
+    const dim3 pg((unsigned)((n + 31) / 32), (unsigned)h);
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_project<float>, pg, dim3(256), 0, st, (const float *)K, W, Z, n, d, r);
+    else
+        hipLaunchKernelGGL(k_project<bf16_t>, pg, dim3(256), 0, st, (const bf16_t *)K, W, Z, n, d, r);
+    return hipGetLastError();
 }
 
 hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,

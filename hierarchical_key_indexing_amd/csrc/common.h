@@ -413,6 +413,22 @@ LSA_DEV int next_pow2(int x) {
     return p;
 }
 
+// Squared Euclidean distance in double, dimensions ascending (r <= 64); the
+// difference of two floats and its square are each rounded once, then added.
+LSA_DEV double sq_dist(const float *z, const float *cs, int r) {
+#pragma clang fp contract(off)
+    double dist = 0.0;
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+        if (x < r) {
+            const double diff = (double)z[x] - (double)cs[x];
+            const double sq = diff * diff;
+            dist = dist + sq;
+        }
+    }
+    return dist;
+}
+
 // number of entries <= key in an ascending array
 LSA_DEV int count_le(const int32_t *a, int len, int32_t key) {
     int lo = 0, hi = len;

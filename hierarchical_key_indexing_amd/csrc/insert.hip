@@ -1,0 +1,209 @@
+// Incremental insertion of appended keys into the cluster tree (gfx950).
+//
+// The key index is precomputed and then updated as the context grows ("Latent
+// Sparse Attention Breaks Through the Million-Token Context Bottleneck",
+// kongchang.com, section "How LSA Sidesteps Per-Key Scoring with Hierarchical
+// Clustering").  A batch of m keys (positions n .. n + m - 1) is inserted:
+//   * each key's latent (the build's projection) descends from the root to the
+//     nearest non-empty child at every level (squared distance in double,
+//     ties to the smaller child) against the centroids before the batch;
+//   * every node on a path takes its new keys: c its old count and S the
+//     double sum of their latents (keys ascending),
+//     centroid = fl32((c * centroid + S) / (c + #new)), count = c + #new;
+//   * each leaf's member list becomes its old members followed by its new
+//     keys, and the member array's per-head stride grows from n to n + m.
+//
+// Kernels, in stream order:
+//   k_ins_copy     the member array and leaf offsets to the workspace;
+//   (projection)   z for the new keys, as in the build;
+//   k_ins_descend  one wave per new key, lane c scoring child c of the node;
+//   k_ins_update   one workgroup per (level, head): the batch's (node, key)
+//                  pairs sorted, each node's run summed in key order and its
+//                  centroid and count rewritten;
+//   k_ins_perm     one thread per leaf: new offset = old offset + new keys in
+//                  earlier leaves (binary search in the sorted leaf run), old
+//                  members then new keys written in place.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace lsa {
+
+namespace {
+
+constexpr int kInsMax = 4096;      // keys per batch (the update kernel sorts them in LDS)
+
+struct InsArgs {
+    int64_t m, n;                  // new keys, old keys
+    int h, r, b, L;
+    int64_t nleaf;
+    char *index;
+    int64_t nodes[8], centroid_off[8], count_off[8];
+    int64_t leaf_off_off, perm_off;
+    const float *Z;                // [h][m][r] latents of the new keys
+    int32_t *path;                 // [h][m][L] node of each new key per level
+    uint64_t *slist;               // [h][kInsMax] (leaf << 32 | key) sorted, level L
+    int32_t *perm_old;             // [h][n]
+    int32_t *lo_old;               // [h][nleaf + 1]
+};
+
+__global__ __launch_bounds__(256) void k_ins_copy(InsArgs A) {
+    const int g = blockIdx.y;
+    const int32_t *perm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
+    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nleaf + 1);
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.n + A.nleaf + 1;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        if (e < A.n) A.perm_old[(size_t)g * A.n + e] = perm[e];
+        else A.lo_old[(size_t)g * (A.nleaf + 1) + (e - A.n)] = lo[e - A.n];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
+    __shared__ float z_s[4][64];
+    const int g = blockIdx.y, wv = threadIdx.x / kWave, lane = lane_id();
+    const int64_t j = (int64_t)blockIdx.x * 4 + wv;
+    if (j >= A.m) return;                                   // whole waves only
+    const int r = A.r, b = A.b;
+    if (lane < r) z_s[wv][lane] = A.Z[((size_t)g * A.m + j) * r + lane];
+    wave_sync();
+    int64_t u = 0;
+    for (int l = 1; l <= A.L; ++l) {
+        const float *C = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
+        const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
+        const int64_t child = u * b + lane;
+        const bool ok = lane < b && cn[min<int64_t>(child, A.nodes[l] - 1)] > 0;
+        // distances are >= 0, so their bit patterns order like the values
+        uint64_t key = ok ? (uint64_t)__double_as_longlong(sq_dist(z_s[wv], C + (size_t)child * r, r)) : ~0ull;
+        int best = lane;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            uint64_t ok2;
+            int ob;
+            switch (s) {
+                case 1: ok2 = xor_lane64<1>(key); ob = xor_lane_i<1>(best); break;
+                case 2: ok2 = xor_lane64<2>(key); ob = xor_lane_i<2>(best); break;
+                case 4: ok2 = xor_lane64<4>(key); ob = xor_lane_i<4>(best); break;
+                case 8: ok2 = xor_lane64<8>(key); ob = xor_lane_i<8>(best); break;
+                case 16: ok2 = xor_lane64<16>(key); ob = xor_lane_i<16>(best); break;
+                default: ok2 = xor_lane64<32>(key); ob = xor_lane_i<32>(best); break;
+            }
+            if (ok2 < key || (ok2 == key && ob < best)) { key = ok2; best = ob; }
+        }
+        u = u * b + best;
+        if (lane == 0) A.path[((size_t)g * A.m + j) * A.L + (l - 1)] = (int32_t)u;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_ins_update(InsArgs A) {
+#pragma clang fp contract(off)
+    __shared__ uint64_t ks[kInsMax];
+    __shared__ int nseg_s;
+    __shared__ int seg_s[kInsMax];
+    const int l = blockIdx.x + 1, g = blockIdx.y, t = threadIdx.x;
+    const int m = (int)A.m, r = A.r;
+    const int N = next_pow2(max(m, 2));
+    for (int e = t; e < N; e += blockDim.x)
+        ks[e] = e < m ? ((uint64_t)(uint32_t)A.path[((size_t)g * m + e) * A.L + (l - 1)] << 32) | (uint32_t)e : ~0ull;
+    if (t == 0) nseg_s = 0;
+    __syncthreads();
+    block_bitonic_sort<uint64_t, false>(ks, N);
+    // runs of equal nodes (keys ascending inside a run)
+    for (int e = t; e < m; e += blockDim.x)
+        if (e == 0 || (ks[e] >> 32) != (ks[e - 1] >> 32)) seg_s[atomicAdd(&nseg_s, 1)] = e;
+    if (l == A.L)
+        for (int e = t; e < m; e += blockDim.x) A.slist[(size_t)g * kInsMax + e] = ks[e];
+    __syncthreads();
+    float *C = (float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
+    int32_t *cn = (int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
+    for (int q = t; q < nseg_s; q += blockDim.x) {
+        const int e0 = seg_s[q];
+        const uint32_t v = (uint32_t)(ks[e0] >> 32);
+        int e1 = e0 + 1;
+        while (e1 < m && (uint32_t)(ks[e1] >> 32) == v) ++e1;
+        const int c0 = cn[v];
+        const double cd = (double)c0, cnew = (double)(c0 + (e1 - e0));
+        for (int x = 0; x < r; ++x) {
+            double S = 0.0;
+            for (int e = e0; e < e1; ++e) S = S + (double)A.Z[((size_t)g * m + (uint32_t)ks[e]) * r + x];
+            const double num = cd * (double)C[(size_t)v * r + x] + S;
+            C[(size_t)v * r + x] = (float)(num / cnew);
+        }
+        cn[v] = c0 + (e1 - e0);
+    }
+}
+
+// number of sorted leaf-run entries with leaf < v
+LSA_DEV int leaf_lower(const uint64_t *sl, int m, uint32_t v) {
+    int lo = 0, hi = m;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((uint32_t)(sl[mid] >> 32) < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void k_ins_perm(InsArgs A) {
+    const int g = blockIdx.y;
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v > A.nleaf) return;
+    const int m = (int)A.m;
+    const int64_t nn = A.n + A.m;
+    int32_t *lo_new = (int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nleaf + 1);
+    int32_t *perm_new = (int32_t *)(A.index + A.perm_off) + (size_t)g * nn;
+    if (v == A.nleaf) { lo_new[v] = (int32_t)nn; return; }
+    const uint64_t *sl = A.slist + (size_t)g * kInsMax;
+    const int lb = leaf_lower(sl, m, (uint32_t)v), ub = leaf_lower(sl, m, (uint32_t)v + 1);
+    const int32_t *lo = A.lo_old + (size_t)g * (A.nleaf + 1);
+    const int32_t a0 = lo[v], a1 = lo[v + 1];
+    const int64_t o = (int64_t)a0 + lb;
+    lo_new[v] = (int32_t)o;
+    const int32_t *po = A.perm_old + (size_t)g * A.n;
+    for (int32_t t = 0; t < a1 - a0; ++t) perm_new[o + t] = po[a0 + t];
+    for (int t = 0; t < ub - lb; ++t) perm_new[o + (a1 - a0) + t] = (int32_t)(A.n + (uint32_t)sl[lb + t]);
+}
+
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct InsWs { float *Z; int32_t *path; uint64_t *slist; int32_t *perm_old, *lo_old; size_t bytes; };
+
+InsWs carve_ins_ws(char *base, int64_t m, int64_t n, int h, int r, int L, int64_t nleaf) {
+    size_t cur = 0;
+    InsWs w{};
+    auto take = [&](size_t b) { char *p = base ? base + cur : nullptr; cur = a256(cur + b); return p; };
+    w.Z = (float *)take(sizeof(float) * (size_t)h * m * r);
+    w.path = (int32_t *)take(sizeof(int32_t) * (size_t)h * m * L);
+    w.slist = (uint64_t *)take(sizeof(uint64_t) * (size_t)h * kInsMax);
+    w.perm_old = (int32_t *)take(sizeof(int32_t) * (size_t)h * n);
+    w.lo_old = (int32_t *)take(sizeof(int32_t) * (size_t)h * (nleaf + 1));
+    w.bytes = cur;
+    return w;
+}
+
+}  // namespace
+
+int64_t insert_workspace_bytes(int64_t m, int64_t n, int h, int r, int L, int64_t nleaf) {
+    return (int64_t)carve_ins_ws(nullptr, m, n, h, r, L, nleaf).bytes;
+}
+
+hipError_t index_insert(const void *K_new, int dtype, int64_t m, int d, const float *W, char *index, int64_t n, int h,
+                        int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
+                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st) {
+    InsArgs A{};
+    A.m = m; A.n = n; A.h = h; A.r = r; A.b = b; A.L = L; A.nleaf = nodes[L]; A.index = index;
+    for (int l = 0; l <= L; ++l) { A.nodes[l] = nodes[l]; A.centroid_off[l] = centroid_off[l]; A.count_off[l] = count_off[l]; }
+    A.leaf_off_off = leaf_off_off; A.perm_off = perm_off;
+    InsWs w = carve_ins_ws((char *)ws, m, n, h, r, L, A.nleaf);
+    A.Z = w.Z; A.path = w.path; A.slist = w.slist; A.perm_old = w.perm_old; A.lo_old = w.lo_old;
+    const int64_t ncopy = n + A.nleaf + 1;
+    hipLaunchKernelGGL(k_ins_copy, dim3((unsigned)std::min<int64_t>((ncopy + 255) / 256, 4096), (unsigned)h), dim3(256),
+                       0, st, A);
+    hipError_t e = project_keys(K_new, dtype, m, h, d, W, r, w.Z, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ins_descend, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_ins_update, dim3((unsigned)L, (unsigned)h), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_ins_perm, dim3((unsigned)((A.nleaf + 1 + 255) / 256), (unsigned)h), dim3(256), 0, st, A);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -127,6 +127,40 @@ int lsa_build_index(const void *K, int dtype, int64_t n, int h_kv, int d, const 
                     int64_t ws_bytes, lsa_index_desc *desc, void *stream);
 
 /*
+ * Bytes of device workspace lsa_index_insert needs to insert m keys into the
+ * index described by *desc (*bytes).
+ */
+int lsa_index_insert_workspace_bytes(int64_t m, const lsa_index_desc *desc, int64_t *bytes);
+
+/*
+ * Insert m keys appended to the cache into a built index, in place
+ * (kongchang.com, "How LSA Sidesteps Per-Key Scoring with Hierarchical
+ * Clustering": the key index is precomputed and updated).
+ *
+ *   K_new     device, [h_kv][m][d] of `dtype`: the keys at positions
+ *             desc->n .. desc->n + m - 1
+ *   W         device, float [h_kv][d][r]: the index's projection
+ *   desc      in: the index over n keys; out (on success): over n + m keys
+ *   index     device, the index; index_bytes must hold the layout for n + m
+ *             keys (lsa_index_layout(n + m, ...).bytes: only the member array
+ *             grows, every other array keeps its offset)
+ *   ws        device workspace of lsa_index_insert_workspace_bytes bytes
+ * The batch is inserted at once: each new key's latent fl32(k . W_g)
+ * descends from the root to the nearest non-empty child at every level
+ * (squared distance in double, ties to the smaller child) against the
+ * centroids as they were before the batch; then every node on a path, with c
+ * its old count and S the double sum of its new keys' latents (keys
+ * ascending), gets centroid fl32((c * centroid + S) / (c + #new)) and count
+ * c + #new; each leaf lists its old members, then its new keys.  One key per
+ * batch is the online k-means update.  Results are deterministic.
+ * Limits: 1 <= m <= 4096 (insert longer appends in several batches),
+ * n + m <= 2^31 - 1, d <= 256.
+ */
+int lsa_index_insert(const void *K_new, int dtype, int64_t m, int d, const float *W,
+                     lsa_index_desc *desc, void *index, int64_t index_bytes, void *ws, int64_t ws_bytes,
+                     void *stream);
+
+/*
  * Bytes of device workspace that let lsa_select run its multi-workgroup
  * kernel for this batch (*bytes; 0 when the batch is too large for it, in
  * which case every (row, KV head) pair runs in one workgroup).

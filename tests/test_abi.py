@@ -106,6 +106,18 @@ def test_entry_points_validate_before_touching_the_device():
                              one, None) == lsa.LSA_EUNSUPPORTED    # k > 8192
     assert L.lsa_select_flat(fake, 0, 1, 4, 16, fake, ctypes.byref(bad), fake, fake, 8, 0, 0, fake, fake, None, fake,
                              one, None) == lsa.LSA_EINVAL
+    # insertion: batch size, capacity and workspace checked on the host
+    di = lsa.index_layout(100, 2, 8, 4, 2)
+    assert L.lsa_index_insert(fake, 0, 0, 16, fake, ctypes.byref(di), fake, 1 << 30, fake, 1 << 30,
+                              None) == lsa.LSA_EINVAL
+    assert L.lsa_index_insert(fake, 0, 5000, 16, fake, ctypes.byref(di), fake, 1 << 30, fake, 1 << 30,
+                              None) == lsa.LSA_EUNSUPPORTED
+    assert lsa.index_layout(300, 2, 8, 4, 2).bytes > di.bytes
+    assert L.lsa_index_insert(fake, 0, 200, 16, fake, ctypes.byref(di), fake, di.bytes, fake, 1 << 30,
+                              None) == lsa.LSA_ENOSPC          # no room for 300 keys
+    assert L.lsa_index_insert(fake, 0, 3, 16, fake, ctypes.byref(di), fake, 1 << 30, fake, 8,
+                              None) == lsa.LSA_ENOSPC          # workspace too small
+    assert di.n == 100                                          # unchanged on error
     # PCA projection
     assert L.lsa_pca_projection(fake, 0, 100, 2, 129, 8, fake, None, fake, 1 << 40, None) == lsa.LSA_EUNSUPPORTED
     assert L.lsa_pca_projection(fake, 0, 100, 2, 64, 65, fake, None, fake, 1 << 40, None) == lsa.LSA_EINVAL

@@ -513,3 +513,70 @@ def test_pca_projection_matches_oracle(lsa, n, h, d, r, dtype):
     for g in range(h):
         Wd = Wg[g].astype(np.float64)
         assert np.abs(Wd.T @ Wd - np.eye(r)).max() < 1e-5
+
+
+INSERT_CASES = [("tiny_4k", [1, 7]), ("ragged_bf16_b5", [300]), ("odd_r_deep", [64, 1, 250]), ("flat_L1", [33]),
+                ("multi_piece_root", [4096])]
+
+
+@pytest.mark.parametrize("name,batches", INSERT_CASES, ids=[c[0] for c in INSERT_CASES])
+def test_index_insert_matches_oracle(lsa, name, batches):
+    """Keys appended in batches and inserted in place: after every batch the
+    tree equals the oracle's insertion into the same tree bit for bit, and a
+    selection over the grown index equals the oracle's."""
+    dev = torch.device("cuda:0")
+    w0 = _wl("tiny_4k", **dict(SMALL)[name]) if name != "tiny_4k" else _wl("tiny_4k")
+    total = sum(batches)
+    w = w0.replace(name=name, n=w0.n + total)
+    K, V = synth.make_kv(w)
+    W = synth.make_w(w)
+    n = w0.n
+    Kd, Wd = K.to(dev), W.to(dev)
+    cap = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L).bytes
+    index = torch.zeros(cap, dtype=torch.uint8, device=dev)
+    index, desc = lsa.build_index(Kd[:, :n].contiguous(), Wd, w.b, w.L, w.iters, index=index)
+    torch.cuda.synchronize()
+    ref = host_index(lsa.index_views(index, desc), desc)
+    for mb in batches:
+        say("insert", name, desc.n, mb)
+        Knew = K[:, desc.n:desc.n + mb].contiguous()
+        desc = lsa.index_insert(Knew.to(dev), Wd, index, desc)
+        torch.cuda.synchronize()
+        ref = oracle.index_insert(ref, np32(Knew), W.numpy())
+        assert desc.n == ref.n
+        assert_index_equal(host_index(lsa.index_views(index, desc), desc), ref)
+    # select over the grown cache (decode rows at the end, chunk rows spread)
+    pos = torch.tensor(sorted(np.random.default_rng(3).choice(desc.n + 1, size=6, replace=False)), dtype=torch.int32)
+    Q = synth.make_queries(w, K, pos)
+    sel, cnt, cut = lsa.select(Q.to(dev), pos.to(dev), index, desc, Wd, w.beam, w.k)
+    torch.cuda.synchronize()
+    o = oracle.select(np32(Q), pos.numpy(), ref, W.numpy(), w.beam, w.k)
+    assert_same_bits(sel.cpu().numpy(), o["sel"], "sel after insertion")
+    assert_same_bits(cnt.cpu().numpy(), o["count"], "sel_count after insertion")
+
+
+def test_index_insert_full_size_decode(lsa):
+    """The 1M-key decode index grown by 64 appended keys (one batch), then by
+    one more: every array equals the oracle's insertion into the GPU-built
+    tree."""
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["decode_1m"]
+    n0 = w.n - 65
+    K, V = synth.make_kv(w, device=dev)
+    W = synth.make_w(w, device=dev)
+    cap = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L).bytes
+    index = torch.zeros(cap, dtype=torch.uint8, device=dev)
+    say("build", n0)
+    index, desc = lsa.build_index(K[:, :n0].contiguous(), W, w.b, w.L, w.iters, index=index)
+    torch.cuda.synchronize()
+    ref = host_index(lsa.index_views(index, desc), desc)
+    for mb in (64, 1):
+        say("insert", desc.n, mb)
+        Knew = K[:, desc.n:desc.n + mb].contiguous()
+        desc = lsa.index_insert(Knew, W, index, desc)
+        torch.cuda.synchronize()
+        ref = oracle.index_insert(ref, np32(Knew), np32(W))
+        assert_index_equal(host_index(lsa.index_views(index, desc), desc), ref)
+    assert desc.n == w.n
+    del K, V, index
+    torch.cuda.empty_cache()
