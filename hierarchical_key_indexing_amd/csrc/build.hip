@@ -382,16 +382,6 @@ static inline unsigned grid1(int64_t tot, int bs) {
     return (unsigned)g;
 }
 
-hipError_t project_keys(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, float *Z,
-                        hipStream_t st) {
-    const dim3 pg((unsigned)((n + 31) / 32), (unsigned)h);
-    if (dtype == 0)
-        hipLaunchKernelGGL(k_project<float>, pg, dim3(256), 0, st, (const float *)K, W, Z, n, d, r);
-    else
-        hipLaunchKernelGGL(k_project<bf16_t>, pg, dim3(256), 0, st, (const bf16_t *)K, W, Z, n, d, r);
-    return hipGetLastError();
-}
-
 hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,
                        int iters, char *index, const int64_t *centroid_off, const int64_t *count_off,
                        int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st) {

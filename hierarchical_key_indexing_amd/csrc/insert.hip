@@ -15,11 +15,13 @@
 //
 // Kernels, in stream order:
 //   k_ins_copy     the member array and leaf offsets to the workspace;
-//   (projection)   z for the new keys, as in the build;
-//   k_ins_descend  one wave per new key, lane c scoring child c of the node;
+//   k_ins_descend  one wave per new key: its latent (lane c: dimension c,
+//                  summed as the build's projection does), then lane c scores
+//                  child c of the node at every level;
 //   k_ins_update   one workgroup per (level, head): the batch's (node, key)
-//                  pairs sorted, each node's run summed in key order and its
-//                  centroid and count rewritten;
+//                  pairs sorted, each node's run (one wave, a lane per
+//                  dimension) summed in key order and its centroid and count
+//                  rewritten;
 //   k_ins_perm     one thread per leaf: new offset = old offset + new keys in
 //                  earlier leaves (binary search in the sorted leaf run), old
 //                  members then new keys written in place.
@@ -41,7 +43,10 @@ struct InsArgs {
     char *index;
     int64_t nodes[8], centroid_off[8], count_off[8];
     int64_t leaf_off_off, perm_off;
-    const float *Z;                // [h][m][r] latents of the new keys
+    const void *K;                 // [h][m][d] the new keys
+    int d, dtype;
+    const float *W;                // [h][d][r]
+    float *Z;                      // [h][m][r] latents of the new keys
     int32_t *path;                 // [h][m][L] node of each new key per level
     uint64_t *slist;               // [h][kInsMax] (leaf << 32 | key) sorted, level L
     int32_t *perm_old;             // [h][n]
@@ -59,22 +64,55 @@ __global__ __launch_bounds__(256) void k_ins_copy(InsArgs A) {
     }
 }
 
+template <typename T>
 __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
     __shared__ float z_s[4][64];
+    __shared__ float k_s[4][256];
     const int g = blockIdx.y, wv = threadIdx.x / kWave, lane = lane_id();
     const int64_t j = (int64_t)blockIdx.x * 4 + wv;
     if (j >= A.m) return;                                   // whole waves only
-    const int r = A.r, b = A.b;
-    if (lane < r) z_s[wv][lane] = A.Z[((size_t)g * A.m + j) * r + lane];
+    const int r = A.r, b = A.b, d = A.d;
+    // the latent, as the build projects keys: lane c sums k_i * W[i][c] in
+    // double over i ascending (each product exact), rounded once
+    const T *kr = (const T *)A.K + ((size_t)g * A.m + j) * d;
+    for (int i = lane; i < d; i += kWave) k_s[wv][i] = to_float(kr[i]);
+    wave_sync();
+    if (lane < r) {
+        const float *Wg = A.W + (size_t)g * d * r + lane;
+        double acc = 0.0;
+        for (int i0 = 0; i0 < d; i0 += 64) {
+            float wv64[64];
+#pragma unroll
+            for (int u = 0; u < 64; ++u) wv64[u] = Wg[(size_t)min(i0 + u, d - 1) * r];    // clamped
+#pragma unroll
+            for (int u = 0; u < 64; ++u)
+                if (i0 + u < d) acc = fma((double)k_s[wv][i0 + u], (double)wv64[u], acc);
+        }
+        z_s[wv][lane] = (float)acc;
+        A.Z[((size_t)g * A.m + j) * r + lane] = (float)acc;
+    }
     wave_sync();
     int64_t u = 0;
     for (int l = 1; l <= A.L; ++l) {
         const float *C = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
         const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
-        const int64_t child = u * b + lane;
-        const bool ok = lane < b && cn[min<int64_t>(child, A.nodes[l] - 1)] > 0;
+        const int64_t child = min<int64_t>(u * b + lane, A.nodes[l] - 1);      // clamped: in bounds
+        const bool ok = lane < b && cn[child] > 0;
+        // the child's row in registers first (16-byte loads when r = 64)
+        float row[64];
+        if (r == 64) {
+            const f4_t *c4 = reinterpret_cast<const f4_t *>(C + (size_t)child * 64);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const f4_t t4 = c4[x];
+                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < 64; ++x) row[x] = x < r ? C[(size_t)child * r + x] : 0.0f;
+        }
         // distances are >= 0, so their bit patterns order like the values
-        uint64_t key = ok ? (uint64_t)__double_as_longlong(sq_dist(z_s[wv], C + (size_t)child * r, r)) : ~0ull;
+        uint64_t key = ok ? (uint64_t)__double_as_longlong(sq_dist(z_s[wv], row, r)) : ~0ull;
         int best = lane;
 #pragma unroll
         for (int s = 1; s < kWave; s <<= 1) {
@@ -116,20 +154,23 @@ __global__ __launch_bounds__(256) void k_ins_update(InsArgs A) {
     __syncthreads();
     float *C = (float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
     int32_t *cn = (int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
-    for (int q = t; q < nseg_s; q += blockDim.x) {
+    // one wave per run (node), lane x: dimension x
+    const int wv = t / kWave, lane = lane_id();
+    for (int q = wv; q < nseg_s; q += blockDim.x / kWave) {
         const int e0 = seg_s[q];
         const uint32_t v = (uint32_t)(ks[e0] >> 32);
         int e1 = e0 + 1;
         while (e1 < m && (uint32_t)(ks[e1] >> 32) == v) ++e1;
         const int c0 = cn[v];
         const double cd = (double)c0, cnew = (double)(c0 + (e1 - e0));
-        for (int x = 0; x < r; ++x) {
+        if (lane < r) {
             double S = 0.0;
-            for (int e = e0; e < e1; ++e) S = S + (double)A.Z[((size_t)g * m + (uint32_t)ks[e]) * r + x];
-            const double num = cd * (double)C[(size_t)v * r + x] + S;
-            C[(size_t)v * r + x] = (float)(num / cnew);
+            for (int e = e0; e < e1; ++e) S = S + (double)A.Z[((size_t)g * m + (uint32_t)ks[e]) * r + lane];
+            const double num = cd * (double)C[(size_t)v * r + lane] + S;
+            C[(size_t)v * r + lane] = (float)(num / cnew);
         }
-        cn[v] = c0 + (e1 - e0);
+        wave_sync();
+        if (lane == 0) cn[v] = c0 + (e1 - e0);
     }
 }
 
@@ -194,13 +235,13 @@ hipError_t index_insert(const void *K_new, int dtype, int64_t m, int d, const fl
     for (int l = 0; l <= L; ++l) { A.nodes[l] = nodes[l]; A.centroid_off[l] = centroid_off[l]; A.count_off[l] = count_off[l]; }
     A.leaf_off_off = leaf_off_off; A.perm_off = perm_off;
     InsWs w = carve_ins_ws((char *)ws, m, n, h, r, L, A.nleaf);
+    A.K = K_new; A.d = d; A.dtype = dtype; A.W = W;
     A.Z = w.Z; A.path = w.path; A.slist = w.slist; A.perm_old = w.perm_old; A.lo_old = w.lo_old;
     const int64_t ncopy = n + A.nleaf + 1;
     hipLaunchKernelGGL(k_ins_copy, dim3((unsigned)std::min<int64_t>((ncopy + 255) / 256, 4096), (unsigned)h), dim3(256),
                        0, st, A);
-    hipError_t e = project_keys(K_new, dtype, m, h, d, W, r, w.Z, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ins_descend, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
+    if (dtype == 0) hipLaunchKernelGGL(k_ins_descend<float>, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
+    else hipLaunchKernelGGL(k_ins_descend<bf16_t>, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_ins_update, dim3((unsigned)L, (unsigned)h), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_ins_perm, dim3((unsigned)((A.nleaf + 1 + 255) / 256), (unsigned)h), dim3(256), 0, st, A);
     return hipGetLastError();

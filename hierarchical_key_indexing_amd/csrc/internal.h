@@ -11,10 +11,6 @@ hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const 
                        int iters, char *index, const int64_t *centroid_off, const int64_t *count_off,
                        int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st);
 
-// z_j = fl32(K_j . W_g) for n keys of h heads (the build's projection)
-hipError_t project_keys(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, float *Z,
-                        hipStream_t st);
-
 int64_t insert_workspace_bytes(int64_t m, int64_t n, int h, int r, int L, int64_t nleaf);
 hipError_t index_insert(const void *K_new, int dtype, int64_t m, int d, const float *W, char *index, int64_t n, int h,
                         int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
