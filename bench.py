@@ -298,6 +298,125 @@ def local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc, reps=4):
     return res
 
 
+def flat_figures(lsa, torch, np, dev, w, layer, pos, desc, reps=20):
+    """Flat search (every leaf scored) on layer 0's index: one decode layer
+    (flat select, then attend) replayed in a HIP graph, and the 4096-row last
+    chunk (flat select, then attend) timed with events."""
+    a = layer
+    m = pos.shape[0]
+    nleaf = int(desc.nodes[desc.L])
+    sel = torch.empty((m, w.h_kv, w.k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((m, w.h_kv), dtype=torch.int32, device=dev)
+    out = torch.empty_like(a["Q"])
+    fws = torch.empty(lsa.select_flat_workspace_bytes(m, w.h_q, desc), dtype=torch.uint8, device=dev)
+    aws = lsa.workspace(lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k), dev)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        lsa.select_flat(a["Q"], pos, a["index"], desc, a["W"], w.k, sel=sel, sel_count=cnt, want_cutoff=False, ws=fws)
+        if ev: ev[1].record()
+        lsa.attend(a["Q"], a["K"], a["V"], sel, cnt, out=out, want_lse=False, ws=aws)
+        if ev: ev[2].record()
+    step()
+    torch.cuda.synchronize()
+    evs = [_events(torch, 3) for _ in range(reps)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    fs = float(np.median([ev[0].elapsed_time(ev[1]) for ev in evs])) * 1e3
+    fa = float(np.median([ev[1].elapsed_time(ev[2]) for ev in evs])) * 1e3
+    c = cnt.cpu().numpy()
+    # scoring reads every leaf's centroid row, count and offsets once per KV head
+    score_bytes = w.h_kv * nleaf * (w.r * 4 + 4 + 8)
+    res = {"decode_select_us": round(fs, 3), "decode_attend_us": round(fa, 3), "decode_us_per_layer": round(fs + fa, 3),
+           "leaves_scored_per_head": nleaf, "decode_mean_sel_count": float(c.mean()),
+           "decode_select_GBps_leaf_table": round(score_bytes / (fs * 1e-6) / 1e9, 2),
+           "timing": f"median of {reps} eager calls (events), one decode layer"}
+    if w.name == "decode_1m":
+        import synth
+        wp = synth.WORKLOADS["prefill_1m"]
+        ppos = torch.arange(w.n - 4096, w.n, dtype=torch.int32, device=dev)
+        Qp = synth.make_queries(wp, a["K"], ppos)
+        mp = 4096
+        psel = torch.empty((mp, w.h_kv, w.k), dtype=torch.int32, device=dev)
+        pcnt = torch.empty((mp, w.h_kv), dtype=torch.int32, device=dev)
+        pout = torch.empty_like(Qp)
+        pfws = torch.empty(lsa.select_flat_workspace_bytes(mp, w.h_q, desc), dtype=torch.uint8, device=dev)
+        pws = torch.empty(max(lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, w.k), 1), dtype=torch.uint8,
+                          device=dev)
+        sel_call = lambda: lsa.select_flat(Qp, ppos, a["index"], desc, a["W"], w.k, sel=psel, sel_count=pcnt,
+                                           want_cutoff=False, ws=pfws)
+        att_call = lambda: lsa.attend(Qp, a["K"], a["V"], psel, pcnt, out=pout, want_lse=False, ws=pws)
+        sel_call(); att_call()
+        torch.cuda.synchronize()
+        npre = 2
+        e = _events(torch, 3)
+        e[0].record()
+        for _ in range(npre):
+            sel_call()
+        e[1].record()
+        for _ in range(npre):
+            att_call()
+        e[2].record()
+        torch.cuda.synchronize()
+        ps, pa = e[0].elapsed_time(e[1]) / npre, e[1].elapsed_time(e[2]) / npre
+        fma = mp * w.h_kv * float(nleaf) * w.r
+        res.update({"prefill_queries_per_s": round(mp / ((ps + pa) * 1e-3), 1), "prefill_select_ms": round(ps, 3),
+                    "prefill_attend_ms": round(pa, 3),
+                    "prefill_select_f64_TFLOPs": round(2 * fma / (ps * 1e-3) / 1e12, 3),
+                    "prefill_workspace_bytes": int(pfws.numel())})
+    return res
+
+
+def insert_figures(lsa, torch, np, dev, w, layer, reps=5):
+    """Incremental insertion into the decode index: keys appended at the end of
+    a cache of w.n - 64 keys, one key and a batch of 64, each timed with events
+    on a fresh copy of the index (the copy is outside the timed region)."""
+    K, W = layer["K"], layer["W"]
+    n0 = w.n - 64
+    cap = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L).bytes
+    base = torch.zeros(cap, dtype=torch.uint8, device=dev)
+    base, desc0 = lsa.build_index(K[:, :n0].contiguous(), W, w.b, w.L, w.iters, index=base)
+    work = torch.empty_like(base)
+    res = {}
+    for m in (1, 64):
+        Knew = K[:, n0:n0 + m].contiguous()
+        ws = torch.empty(lsa.index_insert_workspace_bytes(m, desc0), dtype=torch.uint8, device=dev)
+        ts = []
+        for _ in range(reps + 1):
+            work.copy_(base)
+            e = _events(torch, 2)
+            e[0].record()
+            lsa.index_insert(Knew, W, work, desc0, ws=ws)
+            e[1].record()
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]) * 1e3)
+        res[f"insert_{m}_us"] = round(float(np.median(ts[1:])), 3)
+    # the rewrite of the leaf offsets and member lists moves every member once
+    res["member_bytes_moved_per_call"] = int(2 * 4 * w.h_kv * (w.n + desc0.nodes[desc0.L]))
+    res["timing"] = f"median of {reps} calls on a fresh copy of the {n0}-key index"
+    return res
+
+
+def pca_figures(lsa, torch, np, dev, w, layer, reps=3):
+    """PCA projection of layer 0's keys (n x h_kv x d), events around the call."""
+    K = layer["K"]
+    ws = torch.empty(lsa.pca_workspace_bytes(w.n, w.h_kv, w.d), dtype=torch.uint8, device=dev)
+    lsa.pca_projection(K, w.r, ws=ws)
+    torch.cuda.synchronize()
+    e = _events(torch, 2)
+    e[0].record()
+    for _ in range(reps):
+        lsa.pca_projection(K, w.r, ws=ws)
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / reps
+    fma = w.h_kv * w.n * 128.0 * 128.0                      # the Gram matrices (padded to 128 x 128)
+    return {"pca_ms": round(ms, 3), "gram_f64_TFLOPs_whole_call": round(2 * fma / (ms * 1e-3) / 1e12, 3),
+            "keys": w.n, "heads": w.h_kv, "d": w.d, "r": w.r,
+            "timing": f"mean of {reps} calls (mean, Gram, reduction, Jacobi eigensolver)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -547,6 +666,12 @@ def main():
     if not args.no_extra:
         log("sinks and window")
         breakdown["sinks_window"] = local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc)
+        log("flat search")
+        breakdown["flat_search"] = flat_figures(lsa, torch, np, dev, w, layers[0], pos, desc)
+        log("insertion")
+        breakdown["index_insert"] = insert_figures(lsa, torch, np, dev, w, layers[0])
+        log("pca")
+        breakdown["pca_projection"] = pca_figures(lsa, torch, np, dev, w, layers[0])
 
     cpu = None
     if not args.no_cpu:
