@@ -195,12 +195,13 @@ def extra_train(lsa, synth, torch, np, dev, w, reps=3):
     out = torch.empty_like(Q)
     aws_n = lsa.attend_workspace_bytes(m, w.h_q, w.h_kv, w.d, w.k)
     aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device=dev)
+    sws = lsa.workspace(lsa.select_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
 
     def fwd(ev=None):
         if ev: ev[0].record()
         lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=bws)
         if ev: ev[1].record()
-        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, want_cutoff=False, ws=None)
+        lsa.select(Q, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, want_cutoff=False, ws=sws)
         if ev: ev[2].record()
         lsa.attend(Q, K, V, sel, cnt, out=out, want_lse=False, ws=aws)
         if ev: ev[3].record()
@@ -276,8 +277,9 @@ def local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc, reps=4):
         pout = torch.empty_like(Qp)
         pws = torch.empty(max(lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, row), 1), dtype=torch.uint8,
                           device=dev)
+        sws = lsa.workspace(lsa.select_workspace_bytes(mp, w.h_q, w.d, desc, w.beam, w.k, ns, nw), dev)
         sel_call = lambda: lsa.select(Qp, ppos, a["index"], desc, a["W"], w.beam, w.k, sel=psel, sel_count=pcnt,
-                                      want_cutoff=False, ws=None, n_sink=ns, window=nw)
+                                      want_cutoff=False, ws=sws, n_sink=ns, window=nw)
         att_call = lambda: lsa.attend(Qp, a["K"], a["V"], psel, pcnt, out=pout, want_lse=False, ws=pws)
         for _ in range(2):
             sel_call(); att_call()
@@ -637,8 +639,9 @@ def main():
         pout = torch.empty_like(Qp)
         pws_n = lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, w.k)
         pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
+        psws = lsa.workspace(lsa.select_workspace_bytes(mp, w.h_q, w.d, desc, w.beam, w.k), dev)
         def pstep():
-            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=None)
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=psws)
             lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
         for _ in range(2):
             pstep()
@@ -647,7 +650,7 @@ def main():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
         for _ in range(npre):
-            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=None)
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=psws)
         e[1].record()
         for _ in range(npre):
             lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
@@ -661,7 +664,7 @@ def main():
             "select_share": round(ps / (ps + pa), 4),
             "attend_GBps_algorithmic": round(attend_bytes(w, mp, pc) / (pa * 1e-3) / 1e9, 2),
             "attend_tflops": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pa * 1e-3) / 1e12, 3)}
-        del Qp, psel, pcnt, pout, pws
+        del Qp, psel, pcnt, pout, pws, psws
 
     if not args.no_extra:
         log("sinks and window")

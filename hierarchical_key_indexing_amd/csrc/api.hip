@@ -153,9 +153,12 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
     if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1 || !bytes) return LSA_EINVAL;
     if (h_q % desc->h_kv != 0) return LSA_EINVAL;
     if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
-    *bytes = lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)
-                 ? lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)
-                 : 0;
+    if (lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k))
+        *bytes = lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k);
+    else if (lsa::nm_shape_ok(desc->r, desc->b, desc->L, beam, d, desc->nodes))
+        *bytes = lsa::nm_workspace_bytes(m, desc->h_kv, desc->L, desc->nodes);
+    else
+        *bytes = 0;
     return LSA_OK;
 }
 
@@ -185,7 +188,7 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
     hipError_t e = lsa::select_keys(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
                                     desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off,
                                     desc->leaf_off_off, desc->perm_off, W, beam, k, n_sink, window, sel, sel_count,
-                                    sel_cutoff, (hipStream_t)stream);
+                                    sel_cutoff, ws, ws ? ws_bytes : 0, (hipStream_t)stream);
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
@@ -306,7 +309,7 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
     } else {
         e = lsa::select_keys(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
                              desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
-                             desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff,
+                             desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff, nullptr, 0,
                              (hipStream_t)stream);
         if (e == hipSuccess)
             e = lsa::attend(Q, K, V, dtype, m, h_q, desc->h_kv, desc->n, d, sel, sel_count, k + n_sink + window,

@@ -20,7 +20,9 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
                        int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
                        int k, int n_sink, int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
-                       hipStream_t st);
+                       void *ws, int64_t ws_bytes, hipStream_t st);
+bool nm_shape_ok(int r, int b, int L, int beam, int d, const int64_t *nodes);
+int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes);
 
 int attend_nsplit(int64_t m, int h_kv, int k);
 int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k);

@@ -16,6 +16,8 @@
 // (score, id) keys in LDS, and at the leaf level the candidate leaves are
 // ordered, their eligible members counted and prefix-summed, and each leaf's
 // taken members written at its prefix offset (retrieval order).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -235,6 +237,52 @@ constexpr int kFastP = 16;          // beam limit of the throughput path
 constexpr int kFastR = 64;          // latent dimension of the throughput path
 constexpr int kWRows = 64;          // rows of W staged at a time (16 KB)
 
+// u = fl32(qbar . W_g) of row i, KV head g, into u_s.  W_g is staged in LDS
+// (Wl, kWRows x kFastR floats) 64 input rows at a time; the sum over the
+// input dimension continues in order across them.
+template <typename T>
+LSA_DEV void fast_latent(const SelectArgs &A, int64_t i, int g, float *Wl, float *qbar_s, float *u_s) {
+    constexpr int R = kFastR;
+    const int tid = threadIdx.x, G = A.h_q / A.h_kv, d = A.d;
+    const T *Q = (const T *)A.Q;
+    for (int t = tid; t < d; t += blockDim.x) {
+        double s = 0.0;
+        for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
+        qbar_s[t] = (float)(s / (double)G);
+    }
+    double us = 0.0;
+    for (int t0 = 0; t0 < d; t0 += kWRows) {
+        const int nt = min(kWRows, d - t0);
+        g2s_rows<4>(Wl, nt * R, A.W + ((size_t)g * d + t0) * R, nt * R, nt * R);
+        __syncthreads();
+        if (tid < R)
+            for (int t = 0; t < nt; ++t) us = fma((double)qbar_s[t0 + t], (double)Wl[t * R + tid], us);
+        __syncthreads();
+    }
+    if (tid < R) u_s[tid] = (float)us;
+    __syncthreads();
+}
+
+// Level 1: the root's non-empty children scored and ranked by wave 0; the
+// best min(beam, #) go to kept_s, their number to *keep_s.
+LSA_DEV void fast_level1(const SelectArgs &A, int g, const float *u_s, int32_t *kept_s, int *keep_s) {
+    constexpr int R = kFastR;
+    const int lane = lane_id();
+    if (threadIdx.x / kWave == 0) {
+        const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * R;
+        const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
+        uint64_t key = 0;
+        int pay = 0;
+        if (lane < A.b && cn1[lane] > 0) key = make_key(score_row64(u_s, C1 + (size_t)lane * R), (uint32_t)lane);
+        const int nz = __popcll(__ballot(key != 0));
+        wave_sort_desc(key, pay);
+        const int keep = min(A.beam, nz);
+        if (lane < keep) kept_s[lane] = (int32_t)key_id(key);
+        if (lane == 0) *keep_s = keep;
+    }
+    __syncthreads();
+}
+
 template <typename T>
 __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     extern __shared__ __attribute__((aligned(16))) float dynf[];   // W_g, then keys and leaf tables
@@ -252,41 +300,11 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     const T *Q = (const T *)A.Q;
     const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
 
-    // ---- group latent query.  W_g is staged in LDS 64 input rows (16 KB) at
-    // a time; the sum over the input dimension continues in order across them.
+    // ---- group latent query, then level 1
     float *Wl = dynf;                                   // [64][R]
-    for (int t = tid; t < d; t += blockDim.x) {
-        double s = 0.0;
-        for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
-        qbar_s[t] = (float)(s / (double)G);
-    }
     if (tid == 0) cut_s = -INFINITY;
-    double us = 0.0;
-    for (int t0 = 0; t0 < d; t0 += kWRows) {
-        const int nt = min(kWRows, d - t0);
-        g2s_rows<4>(Wl, nt * R, A.W + ((size_t)g * d + t0) * R, nt * R, nt * R);
-        __syncthreads();
-        if (tid < R)
-            for (int t = 0; t < nt; ++t) us = fma((double)qbar_s[t0 + t], (double)Wl[t * R + tid], us);
-        __syncthreads();
-    }
-    if (tid < R) u_s[tid] = (float)us;
-    __syncthreads();
-
-    // ---- level 1: the root's non-empty children, best min(beam, #) kept
-    if (wv == 0) {
-        const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * R;
-        const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
-        uint64_t key = 0;
-        int pay = 0;
-        if (lane < b && cn1[lane] > 0) key = make_key(score_row64(u_s, C1 + (size_t)lane * R), (uint32_t)lane);
-        const int nz = __popcll(__ballot(key != 0));
-        wave_sort_desc(key, pay);
-        const int keep = min(P, nz);
-        if (lane < keep) kept_s[lane] = (int32_t)key_id(key);
-        if (lane == 0) keep_s = keep;
-    }
-    __syncthreads();
+    fast_latent<T>(A, i, g, Wl, qbar_s, u_s);
+    fast_level1(A, g, u_s, kept_s, &keep_s);
 
     // ---- levels 2..L
     uint64_t *sk = reinterpret_cast<uint64_t *>(dynf);           // 1024 candidate keys
@@ -391,11 +409,424 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- node-major path
+// For many rows the kernel above reads, per (row, KV head), the b children of
+// each of its `beam` kept nodes at every level: 256 KB per row at the leaf
+// level of the 1M workloads, mostly from HBM, although different rows keep
+// the same nodes.  Here levels 2..L are scored node by node: the (row, kept
+// node) pairs are grouped by node, and a wave loads a node's children rows
+// once into registers and scores them against every row that kept it.  The
+// keys (with their slots), eligible counts and first members are those of
+// k_select_fast, so the rows it writes are identical.
+//   k_nm_top     per (row, KV head): u and level 1, as k_select_fast;
+//   k_nm_zero, k_nm_count, k_nm_scan, k_nm_fill: the pairs grouped by node;
+//   k_nm_score   64 pairs per workgroup, 16 per wave: the wave keeps the
+//                children rows of its current node in registers (lane c:
+//                child c) and writes each pair's 64 candidate keys (at the
+//                leaf level also eligible counts and first members);
+//   k_nm_keep    internal levels, per (row, KV head): the top `beam` by a
+//                weighted radix selection and a one-wave sort;
+//   k_nm_finish  leaf level, per (row, KV head): block sort and fill.
+
+struct NmArgs {
+    SelectArgs S;
+    int64_t row0;                  // first row of the batch
+    int64_t groups;                // rows of the batch x h_kv; group = (row - row0) * h_kv + g
+    int level;                     // the level being scored (2..L)
+    float *U;                      // [groups][64]
+    int32_t *kept;                 // [groups][kFastP] node ids at level - 1
+    int32_t *keep;                 // [groups]
+    uint64_t *keys;                // [groups][kFastP * 64]
+    int32_t *eli, *lof;            // [groups][kFastP * 64] (leaf level)
+    int32_t *ncnt, *noff, *fptr;   // [h_kv * nodes(level - 1) + 1]
+    int32_t *pairs;                // [groups * kFastP]: group * kFastP + slot, grouped by node
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_nm_top(NmArgs N) {
+    __shared__ __attribute__((aligned(16))) float Wl[kWRows * kFastR];
+    __shared__ __attribute__((aligned(16))) float qbar_s[256];
+    __shared__ __attribute__((aligned(16))) float u_s[kFastR];
+    __shared__ int32_t kept_s[kFastP];
+    __shared__ int keep_s;
+    const SelectArgs &A = N.S;
+    const int64_t i = N.row0 + blockIdx.x;
+    const int g = blockIdx.y;
+    const int64_t grp = (int64_t)blockIdx.x * A.h_kv + g;
+    fast_latent<T>(A, i, g, Wl, qbar_s, u_s);
+    fast_level1(A, g, u_s, kept_s, &keep_s);
+    const int tid = threadIdx.x;
+    if (tid < kFastR) N.U[grp * kFastR + tid] = u_s[tid];
+    if (tid < kFastP) N.kept[grp * kFastP + tid] = tid < keep_s ? kept_s[tid] : 0;
+    if (tid == 0) N.keep[grp] = keep_s;
+}
+
+__global__ __launch_bounds__(256) void k_nm_zero(NmArgs N, int64_t count) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x)
+        N.ncnt[e] = 0;
+}
+
+constexpr int kNmChunk = 2048;      // pair entries per counting workgroup
+constexpr int kNmBins = 16384;      // (head, node) counters held in LDS (larger tables go straight to memory)
+
+// the (head, node) bin of pair entry e, or -1 when the slot is empty
+LSA_DEV int64_t nm_bin(const NmArgs &N, int64_t e) {
+    if (e >= N.groups * kFastP) return -1;
+    const int64_t grp = e / kFastP;
+    const int j = (int)(e % kFastP);
+    if (j >= N.keep[grp]) return -1;
+    return (int64_t)(grp % N.S.h_kv) * N.S.nodes[N.level - 1] + N.kept[grp * kFastP + j];
+}
+
+// counts per (head, node): each workgroup takes kNmChunk entries, counts them
+// in LDS and adds its nonzero counters to memory
+__global__ __launch_bounds__(256) void k_nm_count(NmArgs N, int64_t nbins) {
+    extern __shared__ int h_s[];            // nbins counters when nbins <= kNmBins
+    const int64_t e0 = (int64_t)blockIdx.x * kNmChunk;
+    if (nbins > kNmBins) {
+        for (int u = threadIdx.x; u < kNmChunk; u += blockDim.x) {
+            const int64_t bin = nm_bin(N, e0 + u);
+            if (bin >= 0) atomicAdd(N.ncnt + bin, 1);
+        }
+        return;
+    }
+    for (int u = threadIdx.x; u < nbins; u += blockDim.x) h_s[u] = 0;
+    __syncthreads();
+    for (int u = threadIdx.x; u < kNmChunk; u += blockDim.x) {
+        const int64_t bin = nm_bin(N, e0 + u);
+        if (bin >= 0) atomicAdd(&h_s[bin], 1);
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < nbins; u += blockDim.x)
+        if (h_s[u] > 0) atomicAdd(N.ncnt + u, h_s[u]);
+}
+
+// exclusive scan of ncnt[0..count) into noff and fptr, total at noff[count]
+__global__ __launch_bounds__(256) void k_nm_scan(NmArgs N, int64_t count) {
+    __shared__ int scr[8];
+    int carry = 0;
+    for (int64_t base = 0; base < count; base += 256 * 8) {
+        int v[8], s = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
+            v[u] = e < count ? N.ncnt[e] : 0;
+            s += v[u];
+        }
+        int tot;
+        int run = carry + block_excl_scan(s, scr, &tot);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
+            if (e < count) { N.noff[e] = run; N.fptr[e] = run; }
+            run += v[u];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) N.noff[count] = carry;
+}
+
+// pair entries grouped by (head, node): each workgroup ranks its entries per
+// bin in LDS, reserves one run per nonzero bin, then writes them
+__global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
+    extern __shared__ int h_s[];            // nbins run offsets when nbins <= kNmBins
+    constexpr int U = kNmChunk / 256;
+    const int64_t e0 = (int64_t)blockIdx.x * kNmChunk;
+    if (nbins > kNmBins) {
+        for (int u = threadIdx.x; u < kNmChunk; u += blockDim.x) {
+            const int64_t bin = nm_bin(N, e0 + u);
+            if (bin >= 0) N.pairs[atomicAdd(N.fptr + bin, 1)] = (int32_t)(e0 + u);
+        }
+        return;
+    }
+    for (int u = threadIdx.x; u < nbins; u += blockDim.x) h_s[u] = 0;
+    __syncthreads();
+    int64_t bin[U];
+    int rk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        bin[u] = nm_bin(N, e0 + threadIdx.x + 256 * u);
+        rk[u] = bin[u] >= 0 ? atomicAdd(&h_s[bin[u]], 1) : 0;
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < nbins; u += blockDim.x)
+        if (h_s[u] > 0) h_s[u] = atomicAdd(N.fptr + u, h_s[u]);          // this workgroup's run
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (bin[u] >= 0) N.pairs[h_s[bin[u]] + rk[u]] = (int32_t)(e0 + threadIdx.x + 256 * u);
+}
+
+__global__ __launch_bounds__(256) void k_nm_score(NmArgs N) {
+    __shared__ __attribute__((aligned(16))) float u_s[4][kFastR];
+    constexpr int R = kFastR;
+    const SelectArgs &A = N.S;
+    const int l = N.level, b = A.b;
+    const bool leaf = l == A.L;
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int64_t nodes_prev = A.nodes[l - 1];
+    const int64_t npairs = N.noff[(size_t)A.h_kv * nodes_prev];
+    const float *Cl = (const float *)(A.index + A.centroid_off[l]);
+    const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]);
+    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off);
+    const int32_t *pm = (const int32_t *)(A.index + A.perm_off);
+    __shared__ int32_t pe_s[4][16], pv_s[4][16], pp_s[4][16];
+    int64_t cur = -1;                                  // (head, node) whose children are in registers
+    float row[R];
+    int c_cnt = 0, c_a0 = 0, c_a1 = 0, c_first = 0, c_last = 0;
+    int64_t child = 0;
+    const int64_t p0 = (int64_t)blockIdx.x * 64 + wv * 16;
+    const int np = (int)max<int64_t>(0, min<int64_t>(16, npairs - p0));
+    if (np == 0) return;                               // wave-local: the kernel has no block barrier
+    // the wave's pairs up front: entry, node and query position (lanes 0..15),
+    // and every pair's u (lane x: component x), all loads issued together
+    if (lane < 16) {
+        const int e = N.pairs[p0 + min(lane, np - 1)];
+        const int64_t grp = e / kFastP;
+        pe_s[wv][lane] = e;
+        pv_s[wv][lane] = N.kept[grp * kFastP + e % kFastP];
+        pp_s[wv][lane] = A.q_pos[N.row0 + grp / A.h_kv];
+    }
+    wave_sync();
+    float uq[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) uq[q] = N.U[(size_t)(pe_s[wv][min(q, np - 1)] / kFastP) * R + lane];
+    for (int q = 0; q < np; ++q) {
+        const int e = pe_s[wv][q];
+        const int64_t grp = e / kFastP;
+        const int j = e % kFastP;
+        const int g = (int)(grp % A.h_kv);
+        const int64_t v = pv_s[wv][q];
+        const int64_t hv = (int64_t)g * nodes_prev + v;
+        if (hv != cur) {
+            // the node's children (lane c: child c) into registers
+            cur = hv;
+            child = v * b + min(lane, b - 1);
+            const size_t gc = (size_t)g * A.nodes[l] + child;
+            const f4_t *c4 = reinterpret_cast<const f4_t *>(Cl + gc * R);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const f4_t t4 = c4[x];
+                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
+            }
+            c_cnt = lane < b ? cn[gc] : 0;
+            if (leaf) {
+                const int32_t *lg = lo + (size_t)g * (A.nodes[l] + 1);
+                c_a0 = lg[child];
+                c_a1 = lg[child + 1];
+                const int32_t *pg = pm + (size_t)g * A.n;
+                c_first = c_cnt > 0 ? pg[c_a0] : 0;
+                c_last = c_cnt > 0 ? pg[c_a1 - 1] : 0;
+            }
+        }
+        float uv = uq[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) uv = (q == x) ? uq[x] : uv;
+        u_s[wv][lane] = uv;
+        wave_sync();
+        uint64_t key = 0;
+        int e_c = 0, f_c = 0;
+        if (c_cnt > 0) {
+            int ok = 1;
+            if (leaf) {
+                const AttnSet as = attn_set(pp_s[wv][q], A.n, A.n_sink, A.window);
+                if (as.all || (c_first >= as.rlo && c_last <= as.rhi)) { e_c = c_a1 - c_a0; f_c = 0; }
+                else if (c_last < as.rlo || c_first > as.rhi) { e_c = 0; }
+                else in_range(as, pm + (size_t)g * A.n + c_a0, c_a1 - c_a0, f_c, e_c);
+                ok = e_c > 0;
+            }
+            if (ok) {
+                const f4_t *u4 = reinterpret_cast<const f4_t *>(u_s[wv]);
+                double sc = 0.0;
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const f4_t a = u4[x];
+                    sc = fma((double)a.x, (double)row[4 * x + 0], sc);
+                    sc = fma((double)a.y, (double)row[4 * x + 1], sc);
+                    sc = fma((double)a.z, (double)row[4 * x + 2], sc);
+                    sc = fma((double)a.w, (double)row[4 * x + 3], sc);
+                }
+                key = make_key_slot((float)sc, (uint32_t)(v * b + lane), j * 64 + lane);
+            }
+        }
+        const size_t o = (size_t)grp * (kFastP * 64) + j * 64 + lane;
+        N.keys[o] = key;
+        if (leaf) { N.eli[o] = e_c; N.lof[o] = c_a0 + f_c; }
+        wave_sync();
+    }
+}
+
+// this group's candidates, four per thread (slots beyond keep are empty)
+LSA_DEV void nm_load_keys(const NmArgs &N, int64_t grp, uint64_t (&k4)[4]) {
+    const int keep = N.keep[grp];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int e = 4 * (int)threadIdx.x + ii;
+        k4[ii] = (e / 64 < keep) ? N.keys[(size_t)grp * (kFastP * 64) + e] : 0ull;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_nm_keep(NmArgs N) {
+    __shared__ int hist_s[256], sel_s[4], ncol_s;
+    __shared__ uint64_t col_s[kFastP];
+    const int64_t grp = blockIdx.x;
+    const int P = N.S.beam;
+    uint64_t k4[4];
+    nm_load_keys(N, grp, k4);
+    const int one[4] = {1, 1, 1, 1};
+    const uint64_t thr = block_radix_select(k4, one, P, hist_s, sel_s);
+    if (threadIdx.x == 0) ncol_s = 0;
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+        if (k4[ii] != 0 && k4[ii] >= thr) col_s[atomicAdd(&ncol_s, 1)] = k4[ii];
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const int lane = lane_id(), nk = ncol_s;
+        uint64_t key = lane < nk ? col_s[lane] : 0ull;
+        int pay = 0;
+        wave_sort_desc(key, pay);
+        if (lane < kFastP) N.kept[grp * kFastP + lane] = lane < nk ? (int32_t)slot_key_id(key) : 0;
+        if (lane == 0) N.keep[grp] = nk;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
+    __shared__ __attribute__((aligned(16))) uint64_t sk[1024];
+    __shared__ int scratch[8];
+    __shared__ float cut_s;
+    const SelectArgs &A = N.S;
+    const int64_t grp = blockIdx.x;
+    const int64_t i = N.row0 + grp / A.h_kv;
+    const int g = (int)(grp % A.h_kv);
+    const int tid = threadIdx.x;
+    if (tid == 0) cut_s = -INFINITY;
+    uint64_t k4[4];
+    nm_load_keys(N, grp, k4);
+    block_sort_desc<4>(k4, sk);
+    const int32_t *eli = N.eli + (size_t)grp * (kFastP * 64);
+    const int32_t *lof = N.lof + (size_t)grp * (kFastP * 64);
+    const int32_t *pm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
+    int e4[4], tot = 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
+        tot += e4[ii];
+    }
+    int total;
+    int off = block_excl_scan(tot, scratch, &total);
+    const int count = min(A.k, total);
+    int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.row;
+    int take[4], a0v[4], offv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        offv[ii] = off;
+        take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
+        a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
+        if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
+        off += e4[ii];
+    }
+    constexpr int kC = 4;
+    int32_t mv[4][kC];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+        for (int t = 0; t < kC; ++t)
+            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
+        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
+    }
+    const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
+    for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
+    for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
+    __syncthreads();
+    if (tid == 0) {
+        A.sel_count[(size_t)i * A.h_kv + g] = count + as.nloc;
+        if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
+    }
+}
+
+static inline size_t nm_a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct NmWs { float *U; int32_t *kept, *keep; uint64_t *keys; int32_t *eli, *lof, *ncnt, *noff, *fptr, *pairs; size_t bytes; };
+
+static NmWs carve_nm_ws(char *base, int64_t groups, int h_kv, int64_t max_nodes) {
+    size_t cur = 0;
+    NmWs w{};
+    auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = nm_a256(cur + n); return p; };
+    w.U = (float *)take(sizeof(float) * groups * kFastR);
+    w.kept = (int32_t *)take(sizeof(int32_t) * groups * kFastP);
+    w.keep = (int32_t *)take(sizeof(int32_t) * groups);
+    w.keys = (uint64_t *)take(sizeof(uint64_t) * groups * kFastP * 64);
+    w.eli = (int32_t *)take(sizeof(int32_t) * groups * kFastP * 64);
+    w.lof = (int32_t *)take(sizeof(int32_t) * groups * kFastP * 64);
+    w.ncnt = (int32_t *)take(sizeof(int32_t) * (h_kv * max_nodes + 1));
+    w.noff = (int32_t *)take(sizeof(int32_t) * (h_kv * max_nodes + 1));
+    w.fptr = (int32_t *)take(sizeof(int32_t) * (h_kv * max_nodes + 1));
+    w.pairs = (int32_t *)take(sizeof(int32_t) * groups * kFastP);
+    w.bytes = cur;
+    return w;
+}
+
+constexpr int64_t kNmRows = 4096;   // rows per batch the workspace query sizes for
+
+// the node-major path applies to the throughput kernel's shapes
+bool nm_shape_ok(int r, int b, int L, int beam, int d, const int64_t *nodes) {
+    return r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= ((int64_t)1 << 22);
+}
+
+int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes) {
+    return (int64_t)carve_nm_ws(nullptr, std::max<int64_t>(1, std::min(m, kNmRows)) * h_kv, h_kv, nodes[L - 1]).bytes;
+}
+
+static int64_t nm_batch_rows(int64_t m, int h_kv, int L, const int64_t *nodes, int64_t ws_bytes) {
+    int64_t mb = std::min(m, kNmRows);
+    while (mb > 0 && (int64_t)carve_nm_ws(nullptr, mb * h_kv, h_kv, nodes[L - 1]).bytes > ws_bytes) mb >>= 1;
+    return mb;
+}
+
+static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws_bytes, hipStream_t st) {
+    const int64_t mb = nm_batch_rows(A.m, A.h_kv, A.L, A.nodes, ws_bytes);
+    if (mb < 1) return hipErrorInvalidValue;
+    for (int64_t r0 = 0; r0 < A.m; r0 += mb) {
+        const int64_t nb = std::min(mb, A.m - r0);
+        const int64_t groups = nb * A.h_kv;
+        NmWs w = carve_nm_ws((char *)ws, groups, A.h_kv, A.nodes[A.L - 1]);
+        NmArgs N{};
+        N.S = A; N.row0 = r0; N.groups = groups;
+        N.U = w.U; N.kept = w.kept; N.keep = w.keep; N.keys = w.keys; N.eli = w.eli; N.lof = w.lof;
+        N.ncnt = w.ncnt; N.noff = w.noff; N.fptr = w.fptr; N.pairs = w.pairs;
+        const dim3 tg((unsigned)nb, (unsigned)A.h_kv);
+        if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
+        else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
+        for (int l = 2; l <= A.L; ++l) {
+            N.level = l;
+            const int64_t cnt = (int64_t)A.h_kv * A.nodes[l - 1];
+            const unsigned cg = (unsigned)((groups * kFastP + kNmChunk - 1) / kNmChunk);
+            hipLaunchKernelGGL(k_nm_zero, dim3((unsigned)std::min<int64_t>((cnt + 255) / 256, 1024)), dim3(256), 0, st, N,
+                               cnt);
+            const size_t hb = cnt <= kNmBins ? (size_t)cnt * sizeof(int) : 0;
+            hipLaunchKernelGGL(k_nm_count, dim3(cg), dim3(256), hb, st, N, cnt);
+            hipLaunchKernelGGL(k_nm_scan, dim3(1), dim3(256), 0, st, N, cnt);
+            hipLaunchKernelGGL(k_nm_fill, dim3(cg), dim3(256), hb, st, N, cnt);
+            hipLaunchKernelGGL(k_nm_score, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
+            if (l < A.L) hipLaunchKernelGGL(k_nm_keep, dim3((unsigned)groups), dim3(256), 0, st, N);
+            else hipLaunchKernelGGL(k_nm_finish, dim3((unsigned)groups), dim3(256), 0, st, N);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
                        int64_t n, int h_kv, int r, int b, int L, const int64_t *nodes, const int64_t *centroid_off,
                        const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off, const float *W, int beam,
                        int k, int n_sink, int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff,
-                       hipStream_t st) {
+                       void *ws, int64_t ws_bytes, hipStream_t st) {
     SelectArgs A{};
     A.Q = Q; A.m = m; A.h_q = h_q; A.h_kv = h_kv; A.d = d; A.q_pos = q_pos; A.index = index; A.n = n;
     A.r = r; A.b = b; A.L = L;
@@ -404,6 +835,8 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
     A.n_sink = n_sink; A.window = window; A.row = k + n_sink + window;
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     const dim3 grid((unsigned)m, (unsigned)h_kv);
+    if (ws && nm_shape_ok(r, b, L, beam, d, nodes) && nm_batch_rows(m, h_kv, L, nodes, ws_bytes) >= 1)
+        return select_nm(A, dtype, ws, ws_bytes, st);
     if (r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= (int64_t)1 << 22) {
         const size_t shm = std::max(sizeof(float) * (size_t)kWRows * kFastR, sizeof(uint64_t) * 1024 + sizeof(int32_t) * 2 * kFastP * 64);
         if (dtype == 0) hipLaunchKernelGGL((k_select_fast<float>), grid, dim3(256), shm, st, A);

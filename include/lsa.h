@@ -162,8 +162,10 @@ int lsa_index_insert(const void *K_new, int dtype, int64_t m, int d, const float
 
 /*
  * Bytes of device workspace that let lsa_select run its multi-workgroup
- * kernel for this batch (*bytes; 0 when the batch is too large for it, in
- * which case every (row, KV head) pair runs in one workgroup).
+ * paths for this batch (*bytes): the decode kernel for small batches; for
+ * larger ones with r = 64, b <= 64, beam <= 16, L >= 2 and leaf ids below
+ * 2^22, the node-major path, sized for batches of up to 4096 rows; 0 when
+ * neither applies (then every (row, KV head) pair runs in one workgroup).
  */
 int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
                                int n_sink, int window, int64_t *bytes);
@@ -222,7 +224,12 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * caller zero-fills ws once before its first use; every call leaves all of the
  * bytes it used at zero again, so the same ws serves any number of calls, of
  * any sizes that fit it.  Calls that share one ws must not run concurrently
- * (they would read each other's words).  Both kernels give identical results.
+ * (they would read each other's words).  Larger batches of the shapes named
+ * at lsa_select_workspace_bytes score levels 2..L node by node: the (row,
+ * kept node) pairs are grouped by node in ws, and each kept node's children
+ * are read once per group of rows that kept it instead of once per row; rows
+ * run in batches that fit ws (no zero-filling needed).  Every path gives
+ * identical results.
  */
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
                const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,

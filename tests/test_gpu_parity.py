@@ -580,3 +580,43 @@ def test_index_insert_full_size_decode(lsa):
     assert desc.n == w.n
     del K, V, index
     torch.cuda.empty_cache()
+
+
+NM_CASES = [("nm_b64_L2", dict(n=20000, h_q=16, h_kv=2, d=128, dtype="bf16", r=64, b=64, L=2, beam=8, k=1000,
+                               centres=1024, m=600, mode="chunk")),
+            ("nm_b16_L3", dict(n=30000, h_q=8, h_kv=4, d=64, dtype="f32", r=64, b=16, L=3, beam=16, k=700,
+                               centres=900, m=500, mode="chunk")),
+            ("nm_b32_L3_all", dict(n=6000, h_q=4, h_kv=1, d=128, dtype="bf16", r=64, b=32, L=3, beam=5, k=300,
+                                   centres=300, m=6000, mode="all"))]
+
+
+@pytest.mark.parametrize("name,over", NM_CASES, ids=[c[0] for c in NM_CASES])
+def test_node_major_select_matches_oracle(lsa, name, over):
+    """Batches too large for the decode kernel, with a workspace: levels 2..L
+    scored node by node.  Rows equal the oracle's and the one-workgroup
+    kernel's bit for bit, with and without sinks and a window, in one batch and
+    in one-row batches."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", **over).replace(name=name)
+    data = _inputs(w, dev)
+    index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
+    torch.cuda.synchronize()
+    gix = host_index(lsa.index_views(index, desc), desc)
+    c = data["cpu"]
+    nws = lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, w.beam, w.k)
+    assert nws > 0
+    one_row = lsa.workspace(lsa.select_workspace_bytes(1, w.h_q, w.d, desc, w.beam, w.k), dev)
+    for n_sink, window in [(0, 0), (4, 64)]:
+        ref = oracle.select(np32(c["Q"]), c["pos"].numpy(), gix, c["W"].numpy(), w.beam, w.k,
+                            n_sink=n_sink, window=window)
+        runs = [("one-workgroup", None), ("node-major", lsa.workspace(nws, dev))]
+        if name != "nm_b32_L3_all":
+            runs.append(("node-major one-row batches", one_row))
+        for label, ws in runs:
+            say("nm select", name, label, n_sink, window)
+            sel, cnt, cut = lsa.select(data["Q"], data["pos"], index, desc, data["W"], w.beam, w.k, ws=ws,
+                                       n_sink=n_sink, window=window)
+            torch.cuda.synchronize()
+            assert_same_bits(cnt.cpu().numpy(), ref["count"], f"sel_count ({label})")
+            assert_same_bits(sel.cpu().numpy(), ref["sel"], f"sel ({label})")
+            assert_same_bits(cut.cpu().numpy(), ref["cutoff"], f"cutoff ({label})")
