@@ -34,6 +34,16 @@ struct AttendArgs {
     float *part;          // [m][h_q][nsplit][d + 2] when nsplit > 1
 };
 
+// The (row, KV head) group i * h_kv + g a workgroup serves.  Workgroups are
+// taken head-major (all rows of KV head 0, then head 1, ...), so the
+// workgroups resident at one time gather from one head's K/V region and the
+// shared last-level cache holds a larger part of it than when the heads of
+// every row are interleaved.
+LSA_DEV int64_t attend_group(const AttendArgs &A) {
+    const int64_t y = blockIdx.y;
+    return (y % A.m) * A.h_kv + y / A.m;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     extern __shared__ float smem[];
@@ -46,7 +56,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     float *Sc = Vs + kTK * d;            // [G][kTK]
     __shared__ int32_t ids[kTK];
 
-    const int64_t row = blockIdx.y;      // i * h_kv + g
+    const int64_t row = attend_group(A);     // i * h_kv + g
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int split = blockIdx.x;
@@ -133,7 +143,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * kVTS];
     __shared__ int32_t ids_w[4][kMT];
-    const int64_t row = blockIdx.y;
+    const int64_t row = attend_group(A);
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int G = A.h_q / A.h_kv;
