@@ -144,8 +144,11 @@ __global__ void k_piece_fill(const int32_t *__restrict__ pbase, const int32_t *_
 // rank floor(c*m/a); the other children are zero and stay empty.
 __global__ void k_init(const int32_t *__restrict__ off_prev, const int32_t *__restrict__ perm_prev,
                        const float *__restrict__ Z, float *__restrict__ C, int64_t S, int b, int r, int64_t n, int h) {
-    const int64_t tot = (int64_t)h * S * b;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x) {
+    // one thread per (node, latent dimension)
+    const int64_t tot = (int64_t)h * S * b * r;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < tot; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e / r;
+        const int x = (int)(e % r);
         const int64_t g = i / (S * b);
         const int64_t v = i % (S * b);
         const int64_t u = v / b;
@@ -153,25 +156,51 @@ __global__ void k_init(const int32_t *__restrict__ off_prev, const int32_t *__re
         const int32_t *o = off_prev + g * (S + 1);
         const int64_t m = o[u + 1] - o[u];
         const int a = (int)min((int64_t)b, m);
-        float *dst = C + (size_t)i * r;
+        float val = 0.0f;
         if (c < a) {
             const int32_t j = perm_prev[g * n + o[u] + ((int64_t)c * m) / a];
-            const float *src = Z + ((size_t)g * n + j) * r;
-            for (int x = 0; x < r; ++x) dst[x] = src[x];
-        } else {
-            for (int x = 0; x < r; ++x) dst[x] = 0.0f;
+            val = Z[((size_t)g * n + j) * r + x];
         }
+        C[(size_t)i * r + x] = val;
     }
 }
 
 // ---------------------------------------------------------------- Lloyd round
+// Squared distances of z to two centroids: per dimension, in ascending order,
+// diff = z - c, then diff * diff and the running sum as separate roundings
+// (no fused multiply-add); the same arithmetic as widening each float when
+// it is used.
+LSA_DEV void sq_dist2(const double (&z)[64], const double *c0, const double *c1, int r, double &d0, double &d1) {
+#pragma clang fp contract(off)
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int x = 0; x < 64; x += 2) {
+        if (x < r) {
+            const double2 a = *reinterpret_cast<const double2 *>(c0 + x);
+            const double2 b = *reinterpret_cast<const double2 *>(c1 + x);
+            const double e0 = z[x] - a.x, e1 = z[x] - b.x;
+            const double q0 = e0 * e0, q1 = e1 * e1;
+            s0 = s0 + q0;
+            s1 = s1 + q1;
+            if (x + 1 < r) {                 // (LDS entries at and beyond r are never written)
+                const double f0 = z[x + 1] - a.y, f1 = z[x + 1] - b.y;
+                const double p0 = f0 * f0, p1 = f1 * f1;
+                s0 = s0 + p0;
+                s1 = s1 + p1;
+            }
+        }
+    }
+    d0 = s0;
+    d1 = s1;
+}
+
 __global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pieces, const int32_t *__restrict__ total,
                                                    const int32_t *__restrict__ off_prev,
                                                    const int32_t *__restrict__ perm_prev, const float *__restrict__ Z,
                                                    const float *__restrict__ C, uint8_t *__restrict__ child,
                                                    uint8_t *__restrict__ lrank, int32_t *__restrict__ hist, int64_t S,
                                                    int64_t NPmax, int b, int r, int64_t n) {
-    __shared__ float Cs[64 * 65];
+    __shared__ __attribute__((aligned(16))) double Cs[64 * 64];     // child centroids, widened once
     __shared__ int wcnt[kPiece / kWave][64];
     const int g = blockIdx.y;
     const int64_t p = blockIdx.x;
@@ -181,7 +210,7 @@ __global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pie
     const int64_t m = o[pc.u + 1] - o[pc.u];
     const int a = (int)min((int64_t)b, m);
     const float *Cu = C + ((size_t)g * S * b + (size_t)pc.u * b) * r;
-    for (int idx = threadIdx.x; idx < a * r; idx += blockDim.x) Cs[(idx / r) * 65 + idx % r] = Cu[idx];
+    for (int idx = threadIdx.x; idx < a * r; idx += blockDim.x) Cs[(idx / r) * 64 + idx % r] = (double)Cu[idx];
     for (int idx = threadIdx.x; idx < (kPiece / kWave) * 64; idx += blockDim.x) (&wcnt[0][0])[idx] = 0;
     __syncthreads();
 
@@ -191,13 +220,22 @@ __global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pie
     if (valid) {
         const int32_t j = perm_prev[(size_t)g * n + posn];
         const float *zr = Z + ((size_t)g * n + j) * r;
-        float z[64];
+        double z[64];
 #pragma unroll
-        for (int x = 0; x < 64; ++x) z[x] = (x < r) ? zr[x] : 0.0f;
+        for (int x = 0; x < 64; ++x) z[x] = (x < r) ? (double)zr[x] : 0.0;
         double bestd = 0.0;
-        for (int c = 0; c < a; ++c) {
-            const double dist = sq_dist(z, Cs + c * 65, r);
-            if (c == 0 || dist < bestd) { bestd = dist; best = c; }
+        int c = 0;
+        // two children per step (independent chains), compared in child order
+        for (; c + 2 <= a; c += 2) {
+            double d0, d1;
+            sq_dist2(z, Cs + c * 64, Cs + (c + 1) * 64, r, d0, d1);
+            if (c == 0 || d0 < bestd) { bestd = d0; best = c; }
+            if (d1 < bestd) { bestd = d1; best = c + 1; }
+        }
+        if (c < a) {
+            double d0, d1;
+            sq_dist2(z, Cs + c * 64, Cs + c * 64, r, d0, d1);
+            if (c == 0 || d0 < bestd) { bestd = d0; best = c; }
         }
     }
     // stable rank among this wave's lanes with the same child (6-bit match)
@@ -242,12 +280,12 @@ __global__ __launch_bounds__(256) void k_seg_prefix(const int32_t *__restrict__ 
     const size_t row0 = ((size_t)g * NPmax + base) * b + c;
     int run = 0;
     int q = 0;
-    for (; q + 8 <= cntp; q += 8) {
-        int hv[8];
+    for (; q + 32 <= cntp; q += 32) {
+        int hv[32];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) hv[t] = act ? hist[row0 + (size_t)(q + t) * b] : 0;
+        for (int t = 0; t < 32; ++t) hv[t] = act ? hist[row0 + (size_t)(q + t) * b] : 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 32; ++t) {
             if (act) pref[row0 + (size_t)(q + t) * b] = run;
             run += hv[t];
         }
@@ -286,54 +324,145 @@ __global__ __launch_bounds__(kPiece) void k_scatter(const Piece *__restrict__ pi
 }
 
 // Centroid = fl32(sum of member latents / count), members in ascending key
-// order, double accumulation; one wave per node (lane = latent dimension).
-// A node without members keeps its centroid.  In parent mode a wave walks all
-// children of one parent, which keeps the wave count small on deep levels.
-LSA_DEV void mean_node(const int32_t *__restrict__ perm, const float *__restrict__ Zg, float *__restrict__ Cv,
-                       int32_t s, int32_t cntv, int r) {
+// order, double accumulation, lane = latent dimension.  A node without
+// members keeps its centroid.
+//
+// mean_span: one wave walks the consecutive nodes v0 .. v0+nv-1 (one node, or
+// all children of one parent), whose members are contiguous in perm.  Members
+// come 64 at a time: one coalesced load of their perm entries, then 64 row
+// loads in flight, staged in the wave's LDS slice `zs` (lane x keeps column
+// x, so only the lane itself reads back what it wrote) and added in a rolled
+// loop.  Node boundaries (at most 65) are held one per lane and read with
+// readlane, so crossing one costs no load.
+LSA_DEV void mean_span(const int32_t *__restrict__ o, const int32_t *__restrict__ pm, const float *__restrict__ Zg,
+                       float *__restrict__ Cg, int64_t v0, int nv, int r, float *zs) {
     const int x = lane_id();
+    const int32_t t_begin = o[v0];
+    const int32_t t_end = o[v0 + nv];
+    // lane c: start of node v0 + c (lane nv and above: the end of the span)
+    const int32_t ol = (x < nv) ? o[v0 + x] : t_end;
+    int cur = 0;                                         // node being summed (relative to v0)
+    int32_t start = t_begin;
+    int32_t end = __builtin_amdgcn_readlane(ol, min(1, 63));
+    if (nv == 1) end = t_end;
     double acc = 0.0;
-    int t = 0;
-    for (; t + 8 <= cntv; t += 8) {
-        float zv[8];
+    auto finish = [&]() {
+        if (end > start && x < r) Cg[(size_t)(v0 + cur) * r + x] = (float)(acc / (double)(end - start));
+        acc = 0.0;
+        ++cur;
+        start = end;
+        end = (cur + 1 < nv) ? __builtin_amdgcn_readlane(ol, cur + 1) : t_end;
+    };
+    while (cur < nv && end == start) finish();          // leading empty nodes
+    for (int32_t t0 = t_begin; t0 < t_end; t0 += 64) {
+        const int nb = min(64, t_end - t0);
+        const int32_t jl = (x < nb) ? pm[t0 + x] : 0;
+        float zv[64];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int32_t j = perm[s + t + q];
-            zv[q] = (x < r) ? Zg[(size_t)j * r + x] : 0.0f;
+        for (int q = 0; q < 64; ++q) {
+            const int32_t j = __builtin_amdgcn_readlane(jl, q);
+            zv[q] = (q < nb && x < r) ? Zg[(size_t)j * r + x] : 0.0f;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc = acc + (double)zv[q];
+        for (int q = 0; q < 64; ++q) zs[q * 64 + x] = zv[q];
+        for (int q = 0; q < nb; ++q) {
+            acc = acc + (double)zs[q * 64 + x];
+            if (t0 + q + 1 == end) {
+                finish();
+                while (cur < nv && end == start) finish();   // empty nodes in between
+            }
+        }
     }
-    for (; t < cntv; ++t) {
-        const int32_t j = perm[s + t];
-        acc = acc + (double)((x < r) ? Zg[(size_t)j * r + x] : 0.0f);
-    }
-    if (x < r) Cv[x] = (float)(acc / (double)cntv);
 }
 
+// Waves over spans: parent mode, one wave per parent (its b children);
+// otherwise one wave per node.
 __global__ __launch_bounds__(256) void k_mean(const int32_t *__restrict__ off_new, const int32_t *__restrict__ cnt,
                                               const int32_t *__restrict__ perm_new, const float *__restrict__ Z,
                                               float *__restrict__ C, int64_t S, int b, int r, int64_t n, int parent_mode) {
+    __shared__ float zs[4][64 * 64];
     const int g = blockIdx.y;
     const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int64_t nodes = S * b;
     const int32_t *o = off_new + (size_t)g * (nodes + 1);
-    const int32_t *cn = cnt + (size_t)g * nodes;
     const int32_t *pm = perm_new + (size_t)g * n;
     const float *Zg = Z + (size_t)g * n * r;
     float *Cg = C + (size_t)g * nodes * r;
+    (void)cnt;
     if (parent_mode) {
         if (wv >= S) return;
-        for (int c = 0; c < b; ++c) {
-            const int64_t v = wv * b + c;
-            const int32_t cv = cn[v];
-            if (cv > 0) mean_node(pm, Zg, Cg + (size_t)v * r, o[v], cv, r);
-        }
+        mean_span(o, pm, Zg, Cg, wv * b, b, r, zs[threadIdx.x / kWave]);
     } else {
         if (wv >= nodes) return;
-        const int32_t cv = cn[wv];
-        if (cv > 0) mean_node(pm, Zg, Cg + (size_t)wv * r, o[wv], cv, r);
+        mean_span(o, pm, Zg, Cg, wv, 1, r, zs[threadIdx.x / kWave]);
     }
+}
+
+// One workgroup per node, for levels whose nodes hold thousands of members.
+// Waves 1..3 gather 192 member rows a round (perm entries fetched one round
+// ahead) into LDS; wave 0 adds the previous round's rows in member order
+// while the next round's loads are in flight.
+constexpr int kMeanRound = 3 * 64;
+
+__global__ __launch_bounds__(256) void k_mean_wg(const int32_t *__restrict__ off_new, const int32_t *__restrict__ cnt,
+                                                 const int32_t *__restrict__ perm_new, const float *__restrict__ Z,
+                                                 float *__restrict__ C, int64_t nodes, int r, int64_t n) {
+    __shared__ float buf[kMeanRound * 64];
+    const int g = blockIdx.y;
+    const int64_t v = blockIdx.x;
+    const int32_t cv = cnt[(size_t)g * nodes + v];
+    if (cv <= 0) return;
+    const int32_t s0 = off_new[(size_t)g * (nodes + 1) + v];
+    const int32_t *pm = perm_new + (size_t)g * n + s0;
+    const float *Zg = Z + (size_t)g * n * r;
+    const int w = threadIdx.x / kWave, x = lane_id();
+    const int rounds = (cv + kMeanRound - 1) / kMeanRound;
+    float zr[64];
+    auto perm_of = [&](int k) -> int32_t {
+        const int e = k * kMeanRound + (w - 1) * 64 + x;
+        return (w > 0 && e < cv) ? pm[e] : 0;
+    };
+    auto load_rows = [&](int k, int32_t jl) {
+        const int nb = min(64, cv - (k * kMeanRound + (w - 1) * 64));
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            const int32_t j = __builtin_amdgcn_readlane(jl, q);
+            zr[q] = (q < nb && x < r) ? Zg[(size_t)j * r + x] : 0.0f;
+        }
+    };
+    int32_t jnext = 0;
+    if (w > 0) {
+        const int32_t j0 = perm_of(0);
+        jnext = perm_of(1);
+        load_rows(0, j0);
+    }
+    double acc = 0.0;
+    for (int k = 0; k < rounds; ++k) {
+        if (w > 0) {
+#pragma unroll
+            for (int q = 0; q < 64; ++q) buf[((w - 1) * 64 + q) * 64 + x] = zr[q];
+        }
+        __syncthreads();
+        if (w > 0 && k + 1 < rounds) {
+            const int32_t jl = jnext;
+            jnext = perm_of(k + 2);
+            load_rows(k + 1, jl);
+        }
+        if (w == 0) {
+            const int nb = min(kMeanRound, cv - k * kMeanRound);
+            int q = 0;
+            for (; q + 8 <= nb; q += 8) {
+                float t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = buf[(q + u) * 64 + x];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc = acc + (double)t[u];
+            }
+            for (; q < nb; ++q) acc = acc + (double)buf[q * 64 + x];
+        }
+        __syncthreads();
+    }
+    if (w == 0 && x < r) C[((size_t)g * nodes + v) * r + x] = (float)(acc / (double)cv);
 }
 
 // ---------------------------------------------------------------- host driver
@@ -408,10 +537,11 @@ hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const 
         hipLaunchKernelGGL(k_scan_heads, dim3(h), dim3(1024), 0, st, w.np, w.pbase, w.total, S);
         hipLaunchKernelGGL(k_piece_fill, dim3((unsigned)((NPmax + 255) / 256), (unsigned)h), dim3(256), 0, st, w.pbase,
                            w.np, prev_off, w.total, w.pieces, S, NPmax);
-        hipLaunchKernelGGL(k_init, dim3(grid1(nodes * h, 256)), dim3(256), 0, st, prev_off, prev_perm, w.Z, C, S, b, r, n,
-                           h);
+        hipLaunchKernelGGL(k_init, dim3(grid1(nodes * h * r, 256)), dim3(256), 0, st, prev_off, prev_perm, w.Z, C, S, b,
+                           r, n, h);
         const bool parent_mode = S * h >= 1024;
         const int64_t mean_waves = parent_mode ? S : nodes;
+        const bool wg_mean = n >= 2048 * nodes;        // thousands of members per node
         for (int t = 0; t < iters; ++t) {
             hipLaunchKernelGGL(k_assign, dim3((unsigned)NPmax, (unsigned)h), dim3(kPiece), 0, st, w.pieces, w.total,
                                prev_off, prev_perm, w.Z, C, w.child, w.lrank, w.hist, S, NPmax, b, r, n);
@@ -419,8 +549,12 @@ hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const 
                                w.hist, w.pref, prev_off, next_off, cnt, S, NPmax, b, n);
             hipLaunchKernelGGL(k_scatter, dim3((unsigned)NPmax, (unsigned)h), dim3(kPiece), 0, st, w.pieces, w.total,
                                w.child, w.lrank, w.pref, next_off, prev_perm, next_perm, S, NPmax, b, n);
-            hipLaunchKernelGGL(k_mean, dim3((unsigned)((mean_waves + 3) / 4), (unsigned)h), dim3(256), 0, st, next_off,
-                               cnt, next_perm, w.Z, C, S, b, r, n, parent_mode ? 1 : 0);
+            if (wg_mean)
+                hipLaunchKernelGGL(k_mean_wg, dim3((unsigned)nodes, (unsigned)h), dim3(256), 0, st, next_off, cnt,
+                                   next_perm, w.Z, C, nodes, r, n);
+            else
+                hipLaunchKernelGGL(k_mean, dim3((unsigned)((mean_waves + 3) / 4), (unsigned)h), dim3(256), 0, st,
+                                   next_off, cnt, next_perm, w.Z, C, S, b, r, n, parent_mode ? 1 : 0);
         }
         prev_perm = next_perm;
         prev_off = next_off;

@@ -48,6 +48,10 @@ SMALL = [
                         m=1, mode="decode")),
     ("flat_L1", dict(n=5000, h_q=4, h_kv=1, d=64, dtype="bf16", r=32, b=64, L=1, beam=1, k=700,
                      centres=300, m=6, mode="chunk")),
+    # level 1 over 2048 members per node (one workgroup per node for the mean),
+    # level 3 with 4 x 256 parents (one wave per parent), odd latent dimension
+    ("big_nodes_odd_r", dict(n=40000, h_q=8, h_kv=4, d=48, dtype="f32", r=33, b=16, L=3, beam=4, k=500,
+                             centres=500, m=4, mode="chunk")),
 ]
 
 
