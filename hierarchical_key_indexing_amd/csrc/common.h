@@ -63,6 +63,14 @@ LSA_DEV int lane_id() { return __lane_id(); }
 // Orders one wave's LDS accesses across this point (for LDS regions only this
 // wave reads and writes): the lanes of a wave run in lockstep and the LDS
 // serves one wave's operations in issue order, so no workgroup barrier is needed.
+// Workgroup barrier that orders LDS traffic only: each wave waits for its own
+// LDS operations, then for the other waves; its global loads may stay in
+// flight (a __syncthreads fence would wait for them too).  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+LSA_DEV void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 LSA_DEV void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -76,18 +84,21 @@ LSA_DEV uint64_t lanemask_lt() {
 
 // Value of lane (l ^ M) for every lane l, without a trip through LDS: DPP quad
 // permutes for M = 1, 2; DPP row shifts (both directions, then a per-lane
-// select) for M = 4, 8; the gfx950 row-swap instructions for M = 16, 32.
+// select) for M = 4; a DPP row rotate by 8 for M = 8; the gfx950 row-swap
+// instructions for M = 16, 32.
 template <int M>
 LSA_DEV uint32_t xor_lane(uint32_t x) {
     static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
     if constexpr (M == 1) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
     } else if constexpr (M == 2) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    } else if constexpr (M == 4 || M == 8) {
-        const uint32_t from_below = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + M, 0xF, 0xF, false);  // row_shr
-        const uint32_t from_above = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + M, 0xF, 0xF, false);  // row_shl
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4) {
+        const uint32_t from_below = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+        const uint32_t from_above = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x104, 0xF, 0xF, false);  // row_shl:4
         return (lane_id() & M) ? from_below : from_above;
+    } else if constexpr (M == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
     } else if constexpr (M == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
         return (lane_id() & 16) ? r[0] : r[1];
@@ -137,28 +148,67 @@ LSA_DEV int opaque(int v) {
     return v;
 }
 
+// Value of lane (l ^ M) for the masks of the wave sort network: M = 2^k (see
+// xor_lane) or M = 2^k - 1, a reversal inside blocks of 2^k lanes (DPP quad
+// permute, half-row and row mirrors, then row swaps for 31 and 63).
+template <int M>
+LSA_DEV uint32_t partner_lane(uint32_t x) {
+    if constexpr (M == 3) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
+    } else if constexpr (M == 7) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    } else if constexpr (M == 15) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false);  // row_mirror
+    } else if constexpr (M == 31) {
+        return xor_lane<16>(partner_lane<15>(x));
+    } else if constexpr (M == 63) {
+        return xor_lane<32>(xor_lane<16>(partner_lane<15>(x)));
+    } else {
+        return xor_lane<M>(x);
+    }
+}
+
 // Bitonic sort of one 64-bit key (plus payload) per lane, descending by lane.
-// Every compare-exchange reads the partner lane through DPP / row swaps.
-template <int SIZE, int STRIDE>
-LSA_DEV void sort_stage(uint64_t &key, int &pay, int l0) {
-    const int l = opaque(l0);
-    const uint64_t ok = xor_lane64<STRIDE>(key);
-    const int op = xor_lane_i<STRIDE>(pay);
-    // lower lane of a descending segment (or upper lane of an ascending one)
-    // keeps the larger key; branch-free select
-    const unsigned want_gt = ((l & STRIDE) == 0) == ((l & SIZE) == 0);
-    const unsigned gt = ok > key, lt = ok < key;
-    const unsigned take = (want_gt & gt) | ((want_gt ^ 1u) & lt);
-    key = take ? ok : key;
+// Each merge phase of block size SIZE starts by comparing lane l with lane
+// l ^ (SIZE - 1) (the two sorted halves read against each other in reverse)
+// and continues with half-cleaners l ^ S, S = SIZE/4 .. 1; in every step the
+// lane whose H bit is clear keeps the larger key, so the direction of each
+// step is a fixed lane mask.  Every partner value comes through DPP / row
+// swaps, never through LDS.
+// lanes whose bit H is set (H a power of two below 64)
+template <int H>
+constexpr uint64_t upper_lanes() {
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l)
+        if (l & H) m |= (uint64_t)1 << l;
+    return m;
+}
+template <int M, int H>
+LSA_DEV void sort_cx(uint64_t &key, int &pay, int lane) {
+    (void)lane;
+    const uint64_t o = ((uint64_t)partner_lane<M>((uint32_t)(key >> 32)) << 32) | partner_lane<M>((uint32_t)key);
+    const int op = (int)partner_lane<M>((uint32_t)pay);
+    // the exchange decision as lane masks: lower lanes take a larger partner,
+    // upper lanes a smaller one (the whole wave is active here)
+    constexpr uint64_t up = upper_lanes<H>();
+    const uint64_t gt = __builtin_amdgcn_ballot_w64(o > key);
+    const uint64_t lt = __builtin_amdgcn_ballot_w64(o < key);
+    const bool take = __builtin_amdgcn_inverse_ballot_w64((gt & ~up) | (lt & up));
+    key = take ? o : key;
     pay = take ? op : pay;
 }
-template <int SIZE, int STRIDE>
-LSA_DEV void sort_stages(uint64_t &key, int &pay, int l) {
-    sort_stage<SIZE, STRIDE>(key, pay, l);
-    if constexpr (STRIDE > 1) sort_stages<SIZE, STRIDE / 2>(key, pay, l);
-    else if constexpr (SIZE < kWave) sort_stages<SIZE * 2, SIZE>(key, pay, l);
+template <int S>
+LSA_DEV void sort_half_cleaners(uint64_t &key, int &pay, int lane) {
+    sort_cx<S, S>(key, pay, lane);
+    if constexpr (S > 1) sort_half_cleaners<S / 2>(key, pay, lane);
 }
-LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_stages<2, 1>(key, pay, lane_id()); }
+template <int SIZE>
+LSA_DEV void sort_phase(uint64_t &key, int &pay, int lane) {
+    sort_cx<SIZE - 1, SIZE / 2>(key, pay, lane);
+    if constexpr (SIZE >= 4) sort_half_cleaners<SIZE / 4>(key, pay, lane);
+    if constexpr (SIZE < kWave) sort_phase<SIZE * 2>(key, pay, lane);
+}
+LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_phase<2>(key, pay, lane_id()); }
 
 // Bitonic sort, descending, of the 256 * KPT 64-bit keys of a 256-thread
 // block, KPT (1, 2 or 4) per thread: thread t holds elements KPT t ..

@@ -245,7 +245,17 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     const int32_t *leaf_off = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
     const size_t groups = (size_t)A.m * A.h_kv;
 
-    // ---- prologue: level-1 rows and counts, W_g and the group's queries
+    // ---- prologue: level-1 rows and counts, W_g and the group's queries.
+    // With r = 64, L >= 3 and b <= 4 P, wave w of workgroup p also owns
+    // level-1 node vw = p + P w (every level-1 node has one owner) and loads
+    // its children's rows (16 KB, coalesced: lane l holds float4 l + 64 x)
+    // and counts (lane c: child c) into registers behind the other loads, so
+    // level 2 needs no load after level 1.
+    constexpr bool kPreShape = RC == 64 && DC == 128 && sizeof(T) == 2;
+    const bool pre = kPreShape && L >= 3 && b <= 4 * P;
+    const int vw = p + P * wv;
+    f4_t rw[16];
+    int32_t rcnt = 0;
     float *Wl = dyn;               // [d][r]
     float *Ql = dyn + d * r;       // [G][d]
     {
@@ -289,14 +299,28 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         }
         if (tid < b) ccnt[tid] = cnt_r;
         if (tid == 0) { count_s = 0; last_s = 0; }
+        // (issued after the stores above, so no wait there covers them: they
+        // land while the latent query is computed)
+        // Unconditional loads (a wave that owns no node reads the start of
+        // the index instead), so that no branch pulls a use of them forward.
+        if constexpr (kPreShape) {
+            const bool own = pre && vw < b;
+            const size_t n0 = own ? (size_t)g * A.nodes[2] + (size_t)vw * b : 0;
+            const char *cb = own ? A.index + A.centroid_off[2] : A.index;
+            const char *nb = own ? A.index + A.count_off[2] : A.index;
+            const f4_t *r4 = reinterpret_cast<const f4_t *>((const float *)cb + n0 * 64);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) rw[x] = r4[min(lane + 64 * x, b * 16 - 1)];   // (clamped to the b rows)
+            rcnt = ((const int32_t *)nb)[n0 + (own ? min(lane, b - 1) : 0)];
+        }
     }
-    __syncthreads();
+    lds_barrier();                 // (the level-2 rows stay in flight)
     for (int t = tid; t < d; t += blockDim.x) {
         double s = 0.0;
         for (int h = 0; h < G; ++h) s = s + (double)Ql[h * d + t];
         qbar_s[t] = (float)(s / (double)G);
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = tid; c < r; c += blockDim.x) {
         double s = 0.0;
         if constexpr (DC > 0) {
@@ -307,9 +331,40 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         }
         u_s[c] = (float)s;
     }
-    __syncthreads();
+    lds_barrier();
     // ---- level 1 (every workgroup of the group computes the same ranking)
-    if (wv == 0) {
+    if (pre) {
+        // every wave scores the level-1 nodes itself; the owner of a kept node
+        // (rank below P among the nonzero keys) scores, sorts and publishes its
+        // children as list number `rank`, which is the list the workgroup of
+        // that rank would publish after loading them; lists from keep to P-1
+        // are published empty by the workgroup of that index
+        uint64_t k1 = 0;
+        if (lane < b && ccnt[lane] > 0) k1 = make_key(score_lds<RC>(u_s, Cs + lane * kCS, r), (uint32_t)lane);
+        const int keep = min(P, __popcll(__ballot(k1 != 0)));
+        if (vw < b) {
+            const uint64_t kw = ((uint64_t)__builtin_amdgcn_readlane((int)(k1 >> 32), vw) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k1, vw);
+            const int rank = __popcll(__ballot(k1 > kw));
+            if (kw != 0 && rank < P) {
+                // the rows to this wave's LDS slice (the W / Q staging area,
+                // free once u is known), row c at stride kCS; lane c scores row c
+                float *Rs = dyn + (size_t)wv * 64 * kCS;
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int e = lane + 64 * x;
+                    *reinterpret_cast<f4_t *>(Rs + (e / 16) * kCS + (e % 16) * 4) = rw[x];
+                }
+                wave_sync();
+                uint64_t key = 0;
+                int e = 0;
+                if (lane < b && rcnt > 0) key = make_key(score_lds<RC>(u_s, Rs + lane * kCS, r), (uint32_t)(vw * b + lane));
+                wave_sort_desc(key, e);
+                if (lane < P) publish(A.lists + ((size_t)gi * P + rank) * P + lane, key ? key : kEmpty);
+            }
+        }
+        if (wv == 0 && p >= keep && lane < P) publish(A.lists + ((size_t)gi * P + p) * P + lane, kEmpty);
+    } else if (wv == 0) {
         uint64_t key = 0;
         int pay = 0;
         if (lane < b && ccnt[lane] > 0) key = make_key(score_lds<RC>(u_s, Cs + lane * kCS, r), (uint32_t)lane);
@@ -323,8 +378,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 
     int64_t v = -1;
     for (int l = 2; l <= L; ++l) {
-        v = (p < keep_s) ? kept_s[p] : -1;
         const bool leaf = (l == L);
+        if (!(pre && l == 2)) {
+        v = (p < keep_s) ? kept_s[p] : -1;
         if (v >= 0) {
             const float *Cl = (const float *)(A.index + A.centroid_off[l]) + ((size_t)g * A.nodes[l] + (size_t)v * b) * r;
             const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l] + (size_t)v * b;
@@ -370,6 +426,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 publish(A.leaf_pre + o, incl + 1);
             }
         }
+        }   // level l scored by this workgroup
         if (!leaf) {
             // candidates: the first P entries of every list (the global top P
             // lie among them).  Two merge rounds: the top P of each quartet of
@@ -767,7 +824,9 @@ static size_t decode_dyn_bytes(int dtype, int G, int d, int r) {
     else
         att = sizeof(float) * ((size_t)G * d + (size_t)kTKD * (d + 1) + (size_t)kTKD * d + (size_t)G * kTKD);
     const size_t merge = sizeof(float) * (2 * kMaxP * 16 + 32);
-    return std::max(stage, std::max(att, merge));
+    // fast shape: four waves' level-2 node blocks (64 rows at stride kCS)
+    const size_t pre = fast_shape(dtype, d, r) ? sizeof(float) * 4 * 64 * (size_t)kCS : 0;
+    return std::max(std::max(stage, pre), std::max(att, merge));
 }
 
 constexpr size_t kStaticLds = 64 * 1024;      // upper bound of k_decode's static LDS

@@ -52,6 +52,10 @@ SMALL = [
     # level 3 with 4 x 256 parents (one wave per parent), odd latent dimension
     ("big_nodes_odd_r", dict(n=40000, h_q=8, h_kv=4, d=48, dtype="f32", r=33, b=16, L=3, beam=4, k=500,
                              centres=500, m=4, mode="chunk")),
+    # bf16, d = 128, r = 64 and b <= 4 beam with a level between the first and the
+    # leaves: the decode kernel takes level 2 from rows loaded before level 1
+    ("pre_level2_b16", dict(n=30000, h_q=16, h_kv=2, d=128, dtype="bf16", r=64, b=16, L=3, beam=4, k=700,
+                            centres=500, m=3, mode="decode")),
 ]
 
 
