@@ -215,29 +215,60 @@ LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_phase<2>(key, pay, l
 // KPT t + KPT - 1 before and after.  Exchanges between a thread's own elements
 // stay in registers, between the lanes of a wave they go through DPP / row
 // swaps, and only strides that cross waves go through LDS (`sk`, 256 * KPT keys).
+// Lanes of this wave whose element e = KPT t + i lies in an ascending block
+// of the merge of size SIZE ((e & SIZE) != 0), as a lane mask: a fixed mask
+// while SIZE / KPT < 64, else one bit of the wave index (the same for every
+// lane), and none at the last merge.
+template <int KPT, int SIZE>
+LSA_DEV uint64_t bsort_ascending_lanes(int t0) {
+    if constexpr (SIZE / KPT < 64) {
+        return upper_lanes<SIZE / KPT>();
+    } else if constexpr (SIZE < 256 * KPT) {
+        const int w = __builtin_amdgcn_readfirstlane(t0 >> 6);
+        return (w & (SIZE / KPT / 64)) ? ~0ull : 0ull;
+    } else {
+        return 0ull;
+    }
+}
+
 template <int KPT, int SIZE, int S>
 LSA_DEV void bsort_stage(uint64_t (&k)[KPT], int t0, uint64_t *sk) {
-    const int t = opaque(t0);
     if constexpr (S < KPT) {
+        // partners inside the thread: element i against i + S; the lower
+        // element keeps the larger key in a descending block
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             if ((i & S) == 0) {
-                const bool desc = ((KPT * t + i) & SIZE) == 0;   // lower element keeps the larger key
                 const uint64_t a = k[i], b = k[i + S];
-                const bool sw = desc ? (b > a) : (a > b);
+                bool sw;
+                if constexpr (SIZE < KPT) {
+                    sw = ((i & SIZE) == 0) ? (b > a) : (a > b);
+                } else {
+                    const uint64_t asc = bsort_ascending_lanes<KPT, SIZE>(t0);
+                    const uint64_t gt = __builtin_amdgcn_ballot_w64(b > a);
+                    const uint64_t lt = __builtin_amdgcn_ballot_w64(a > b);
+                    sw = __builtin_amdgcn_inverse_ballot_w64((gt & ~asc) | (lt & asc));
+                }
                 k[i] = sw ? b : a;
                 k[i + S] = sw ? a : b;
             }
         }
     } else if constexpr (S < 64 * KPT) {
+        // partners in other lanes of the wave (DPP / row swaps): a lane keeps
+        // the larger key when it is the lower of the pair in a descending
+        // block or the upper one in an ascending block
+        constexpr uint64_t upper = upper_lanes<S / KPT>();
+        const uint64_t want_gt = ~(upper ^ bsort_ascending_lanes<KPT, SIZE>(t0));
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int e = KPT * t + i;
             const uint64_t o = xor_lane64<S / KPT>(k[i]);
-            const bool want_gt = ((e & S) == 0) == ((e & SIZE) == 0);
-            k[i] = (want_gt ? (o > k[i]) : (o < k[i])) ? o : k[i];
+            const uint64_t gt = __builtin_amdgcn_ballot_w64(o > k[i]);
+            const uint64_t lt = __builtin_amdgcn_ballot_w64(o < k[i]);
+            const bool take = __builtin_amdgcn_inverse_ballot_w64((gt & want_gt) | (lt & ~want_gt));
+            k[i] = take ? o : k[i];
         }
     } else {
+        const int t = opaque(t0);
         __syncthreads();                 // earlier readers of sk are done
 #pragma unroll
         for (int i = 0; i < KPT; ++i) sk[KPT * t + i] = k[i];

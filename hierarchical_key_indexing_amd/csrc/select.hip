@@ -656,13 +656,128 @@ __global__ __launch_bounds__(256) void k_nm_score(NmArgs N) {
     }
 }
 
-// this group's candidates, four per thread (slots beyond keep are empty)
-LSA_DEV void nm_load_keys(const NmArgs &N, int64_t grp, uint64_t (&k4)[4]) {
-    const int keep = N.keep[grp];
+// b <= 32: each wave takes its 16 pairs two at a time, lanes 0..31 the first
+// and lanes 32..63 the second (lane = child in its half), with the same
+// arithmetic as k_nm_score.  Slots j * 64 + 32 .. j * 64 + 63 are not
+// written; the readers use the packed order (nm_slot).
+__global__ __launch_bounds__(256) void k_nm_score_packed(NmArgs N) {
+    __shared__ __attribute__((aligned(16))) float u_s[4][2][kFastR];
+    __shared__ int32_t pe_s[4][16], pv_s[4][16], pp_s[4][16];
+    constexpr int R = kFastR;
+    const SelectArgs &A = N.S;
+    const int l = N.level, b = A.b;
+    const bool leaf = l == A.L;
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int hf = lane >> 5, c = lane & 31;
+    const int64_t nodes_prev = A.nodes[l - 1];
+    const int64_t npairs = N.noff[(size_t)A.h_kv * nodes_prev];
+    const float *Cl = (const float *)(A.index + A.centroid_off[l]);
+    const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]);
+    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off);
+    const int32_t *pm = (const int32_t *)(A.index + A.perm_off);
+    const int64_t p0 = (int64_t)blockIdx.x * 64 + wv * 16;
+    const int np = (int)max<int64_t>(0, min<int64_t>(16, npairs - p0));
+    if (np == 0) return;                               // wave-local: the kernel has no block barrier
+    if (lane < 16) {
+        const int e = N.pairs[p0 + min(lane, np - 1)];
+        const int64_t grp = e / kFastP;
+        pe_s[wv][lane] = e;
+        pv_s[wv][lane] = N.kept[grp * kFastP + e % kFastP];
+        pp_s[wv][lane] = A.q_pos[N.row0 + grp / A.h_kv];
+    }
+    wave_sync();
+    float uq[16];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const int e = 4 * (int)threadIdx.x + ii;
-        k4[ii] = (e / 64 < keep) ? N.keys[(size_t)grp * (kFastP * 64) + e] : 0ull;
+    for (int q = 0; q < 16; ++q) uq[q] = N.U[(size_t)(pe_s[wv][min(q, np - 1)] / kFastP) * R + lane];
+    int64_t cur = -1;                                  // this half's (head, node) whose children are in registers
+    float row[R];
+    int c_cnt = 0, c_a0 = 0, c_a1 = 0, c_first = 0, c_last = 0;
+    for (int q0 = 0; q0 < np; q0 += 2) {
+        const int q = min(q0 + hf, np - 1);
+        const bool act = q0 + hf < np;
+        const int e = pe_s[wv][q];
+        const int64_t grp = e / kFastP;
+        const int j = e % kFastP;
+        const int g = (int)(grp % A.h_kv);
+        const int64_t v = pv_s[wv][q];
+        const int64_t hv = (int64_t)g * nodes_prev + v;
+        if (act && hv != cur) {
+            cur = hv;
+            const int64_t child = v * b + min(c, b - 1);
+            const size_t gc = (size_t)g * A.nodes[l] + child;
+            const f4_t *c4 = reinterpret_cast<const f4_t *>(Cl + gc * R);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const f4_t t4 = c4[x];
+                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
+            }
+            c_cnt = c < b ? cn[gc] : 0;
+            if (leaf) {
+                const int32_t *lg = lo + (size_t)g * (A.nodes[l] + 1);
+                c_a0 = lg[child];
+                c_a1 = lg[child + 1];
+                const int32_t *pg = pm + (size_t)g * A.n;
+                c_first = c_cnt > 0 ? pg[c_a0] : 0;
+                c_last = c_cnt > 0 ? pg[c_a1 - 1] : 0;
+            }
+        }
+        // u of both pairs (lane x: component x)
+        float ua = uq[0], ub = uq[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) {
+            ua = (q0 == x) ? uq[x] : ua;
+            ub = (min(q0 + 1, np - 1) == x) ? uq[x] : ub;
+        }
+        u_s[wv][0][lane] = ua;
+        u_s[wv][1][lane] = ub;
+        wave_sync();
+        uint64_t key = 0;
+        int e_c = 0, f_c = 0;
+        if (act && c_cnt > 0) {
+            int ok = 1;
+            if (leaf) {
+                const AttnSet as = attn_set(pp_s[wv][q], A.n, A.n_sink, A.window);
+                if (as.all || (c_first >= as.rlo && c_last <= as.rhi)) { e_c = c_a1 - c_a0; f_c = 0; }
+                else if (c_last < as.rlo || c_first > as.rhi) { e_c = 0; }
+                else in_range(as, pm + (size_t)g * A.n + c_a0, c_a1 - c_a0, f_c, e_c);
+                ok = e_c > 0;
+            }
+            if (ok) {
+                const f4_t *u4 = reinterpret_cast<const f4_t *>(u_s[wv][hf]);
+                double sc = 0.0;
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const f4_t a = u4[x];
+                    sc = fma((double)a.x, (double)row[4 * x + 0], sc);
+                    sc = fma((double)a.y, (double)row[4 * x + 1], sc);
+                    sc = fma((double)a.z, (double)row[4 * x + 2], sc);
+                    sc = fma((double)a.w, (double)row[4 * x + 3], sc);
+                }
+                key = make_key_slot((float)sc, (uint32_t)(v * b + c), j * 64 + c);
+            }
+        }
+        if (act) {
+            const size_t o = (size_t)grp * (kFastP * 64) + j * 64 + c;
+            N.keys[o] = key;
+            if (leaf) { N.eli[o] = e_c; N.lof[o] = c_a0 + f_c; }
+        }
+        wave_sync();
+    }
+}
+
+// Candidate e of a group in slot order: slot e, or with b <= 32 (packed) the
+// e-th of the slots j * 64 + c, c < 32.
+LSA_DEV int nm_slot(int e, bool packed) { return packed ? (e >> 5) * 64 + (e & 31) : e; }
+
+// this group's candidates, KPT per thread (slots beyond keep are empty)
+template <int KPT>
+LSA_DEV void nm_load_keys(const NmArgs &N, int64_t grp, uint64_t (&k)[KPT], bool packed) {
+    const int keep = N.keep[grp];
+    const int per = packed ? 32 : 64, tot = kFastP * per;
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) {
+        const int e = KPT * (int)threadIdx.x + ii;
+        k[ii] = (e < tot && e / per < keep) ? N.keys[(size_t)grp * (kFastP * 64) + nm_slot(e, packed)] : 0ull;
     }
 }
 
@@ -672,7 +787,7 @@ __global__ __launch_bounds__(256) void k_nm_keep(NmArgs N) {
     const int64_t grp = blockIdx.x;
     const int P = N.S.beam;
     uint64_t k4[4];
-    nm_load_keys(N, grp, k4);
+    nm_load_keys<4>(N, grp, k4, N.S.b <= 32);
     const int one[4] = {1, 1, 1, 1};
     const uint64_t thr = block_radix_select(k4, one, P, hist_s, sel_s);
     if (threadIdx.x == 0) ncol_s = 0;
@@ -691,6 +806,8 @@ __global__ __launch_bounds__(256) void k_nm_keep(NmArgs N) {
     }
 }
 
+// KPT = 4: 1024 candidate slots; KPT = 2: the 512 packed slots of b <= 32
+template <int KPT>
 __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     __shared__ __attribute__((aligned(16))) uint64_t sk[1024];
     __shared__ int scratch[8];
@@ -701,15 +818,15 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     const int g = (int)(grp % A.h_kv);
     const int tid = threadIdx.x;
     if (tid == 0) cut_s = -INFINITY;
-    uint64_t k4[4];
-    nm_load_keys(N, grp, k4);
-    block_sort_desc<4>(k4, sk);
+    uint64_t k4[KPT];
+    nm_load_keys<KPT>(N, grp, k4, KPT == 2);
+    block_sort_desc<KPT>(k4, sk);
     const int32_t *eli = N.eli + (size_t)grp * (kFastP * 64);
     const int32_t *lof = N.lof + (size_t)grp * (kFastP * 64);
     const int32_t *pm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
-    int e4[4], tot = 0;
+    int e4[KPT], tot = 0;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < KPT; ++ii) {
         e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
         tot += e4[ii];
     }
@@ -717,9 +834,9 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     int off = block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
     int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.row;
-    int take[4], a0v[4], offv[4];
+    int take[KPT], a0v[KPT], offv[KPT];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < KPT; ++ii) {
         offv[ii] = off;
         take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
         a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
@@ -727,13 +844,13 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
         off += e4[ii];
     }
     constexpr int kC = 4;
-    int32_t mv[4][kC];
+    int32_t mv[KPT][kC];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < KPT; ++ii)
 #pragma unroll
         for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < KPT; ++ii) {
 #pragma unroll
         for (int t = 0; t < kC; ++t)
             if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
@@ -812,9 +929,12 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
             hipLaunchKernelGGL(k_nm_count, dim3(cg), dim3(256), hb, st, N, cnt);
             hipLaunchKernelGGL(k_nm_scan, dim3(1), dim3(256), 0, st, N, cnt);
             hipLaunchKernelGGL(k_nm_fill, dim3(cg), dim3(256), hb, st, N, cnt);
-            hipLaunchKernelGGL(k_nm_score, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
+            const bool packed = A.b <= 32;
+            if (packed) hipLaunchKernelGGL(k_nm_score_packed, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
+            else hipLaunchKernelGGL(k_nm_score, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
             if (l < A.L) hipLaunchKernelGGL(k_nm_keep, dim3((unsigned)groups), dim3(256), 0, st, N);
-            else hipLaunchKernelGGL(k_nm_finish, dim3((unsigned)groups), dim3(256), 0, st, N);
+            else if (packed) hipLaunchKernelGGL(k_nm_finish<2>, dim3((unsigned)groups), dim3(256), 0, st, N);
+            else hipLaunchKernelGGL(k_nm_finish<4>, dim3((unsigned)groups), dim3(256), 0, st, N);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

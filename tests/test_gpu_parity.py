@@ -423,6 +423,17 @@ def test_full_size_workload(lsa, name, sample_rows, replay_depth, local):
     n_sink, window = local
     say("select", name, local)
     sel, cnt, cut = lsa.select(Q, pos, index, desc, W, w.beam, w.k, n_sink=n_sink, window=window)
+    # with a workspace (the launch the benchmark times: the decode kernel for
+    # one row, node-major batches for the prefill chunk and the training
+    # layer) every row equals the one-workgroup result bit for bit
+    nws = lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, w.beam, w.k, n_sink, window)
+    if nws > 0:
+        say("select with workspace", name, nws)
+        sws = lsa.workspace(nws, dev)
+        selw, cntw, cutw = lsa.select(Q, pos, index, desc, W, w.beam, w.k, n_sink=n_sink, window=window, ws=sws)
+        torch.cuda.synchronize()
+        assert torch.equal(cntw, cnt) and torch.equal(cutw, cut) and torch.equal(selw, sel)
+        del selw, cntw, cutw, sws
     say("attend", name)
     out, lse = lsa.attend(Q, K, V, sel, cnt)
     torch.cuda.synchronize()
