@@ -139,10 +139,12 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
 // Each of the four waves walks its own 32-key steps of the workgroup's slice
 // with the matrix-core step of mfma_attn.h and keeps its own softmax state;
 // the four states are combined at the end.
+constexpr int kIdsCap = 2048;       // selected ids of a slice staged in LDS at a time
+
 template <int D>
-__global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
+__global__ __launch_bounds__(256, 2) void k_attend_mfma(AttendArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * kVTS];
-    __shared__ int32_t ids_w[4][kMT];
+    __shared__ int32_t ids_s[kIdsCap + 4 * kMT];
     const int64_t row = attend_group(A);
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
@@ -161,17 +163,48 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs A) {
     wave_load_q<D>(qf, Qb, G);
     WaveAttn<D> st;
     wave_attn_init<D>(st);
-    const int nsteps = (s1 - s0 + 4 * kMT - 1) / (4 * kMT);
-    for (int t = 0; t < nsteps; ++t) {
-        const int kb = s0 + (4 * t + w) * kMT;
-        const int nk = max(0, min(kMT, s1 - kb));
-        if (l < kMT) ids_w[w][l] = (l < nk) ? S[kb + l] : ((nk > 0) ? S[kb] : 0);
+    bool first = true;
+    // The slice's ids come to LDS kIdsCap at a time (padded with the chunk's
+    // first id to whole 4 x 32-key steps); wave w takes steps w, w + 4, ...
+    // of the chunk and keeps the next step's K/V loads in flight while it
+    // computes the current one.  Only the wave itself reads its V^T tile.
+    for (int c0 = s0; c0 < s1; c0 += kIdsCap) {
+        const int own = min(kIdsCap, s1 - c0);
+        const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
+        for (int f = threadIdx.x; f < nsteps * 4 * kMT; f += blockDim.x) ids_s[f] = S[c0 + (f < own ? f : 0)];
         __syncthreads();
-        bf16x8_t pf;
-        float alpha;
-        wave_attn_part1<D>(Kg, Vg, ids_w[w], nk, qf, A.scale_log2, vt[w], st, pf, alpha);
-        __syncthreads();
-        wave_attn_part2<D>(vt[w], pf, alpha, st, t == 0);
+        WaveRows<D> ra, rb;
+        int t = 0;
+        if (nsteps > 0) wave_attn_load<D>(Kg, Vg, ids_s + w * kMT, ra);
+        while (t < nsteps) {
+            // step t in ra, step t + 1 loading into rb (then the roles swap)
+            if (t + 1 < nsteps) wave_attn_load<D>(Kg, Vg, ids_s + (4 * (t + 1) + w) * kMT, rb);
+            {
+                const int nk = max(0, min(kMT, own - (4 * t + w) * kMT));
+                bf16x8_t pf;
+                float alpha;
+                wave_attn_compute<D>(ra, nk, qf, A.scale_log2, vt[w], st, pf, alpha);
+                wave_sync();
+                wave_attn_part2<D>(vt[w], pf, alpha, st, first);
+                wave_sync();
+                first = false;
+            }
+            ++t;
+            if (t >= nsteps) break;
+            if (t + 1 < nsteps) wave_attn_load<D>(Kg, Vg, ids_s + (4 * (t + 1) + w) * kMT, ra);
+            {
+                const int nk = max(0, min(kMT, own - (4 * t + w) * kMT));
+                bf16x8_t pf;
+                float alpha;
+                wave_attn_compute<D>(rb, nk, qf, A.scale_log2, vt[w], st, pf, alpha);
+                wave_sync();
+                wave_attn_part2<D>(vt[w], pf, alpha, st, first);
+                wave_sync();
+                first = false;
+            }
+            ++t;
+        }
+        __syncthreads();                 // ids_s is rewritten by the next chunk
     }
     __syncthreads();
     float *scratch = reinterpret_cast<float *>(&vt[0][0]);

@@ -50,26 +50,29 @@ LSA_DEV void wave_load_q(bf16x8_t (&qf)[D / 32], const uint16_t *Qg, int G) {
     }
 }
 
-// First half of a step: loads, V^T staging, scores and the softmax update.
-// ids: the wave's 32 key ids (LDS); keys >= nk are masked.  Returns the P
-// fragment and the rescale factor; the caller synchronises LDS before part 2.
+// The gathered rows of one step: K fragments (A operand of S^T) and the V
+// units this lane transposes.
 template <int D>
-LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__restrict__ Vg, const int32_t *ids,
-                             int nk, const bf16x8_t (&qf)[D / 32], float scale_log2, uint16_t *vt, WaveAttn<D> &st,
-                             bf16x8_t &pf, float &alpha) {
-    constexpr int KS = D / 32;
-    const int l = lane_id(), q = l / 16, c16 = l % 16;
+struct WaveRows {
+    static constexpr int KS = D / 32, NU = D / 2, UPL = (NU + kWave - 1) / kWave;
     bf16x8_t kf[2][KS];
+    uint4 vv[UPL][8];
+};
+
+// Issue the loads of one step.  ids: the wave's 32 key ids (LDS).
+template <int D>
+LSA_DEV void wave_attn_load(const uint16_t *__restrict__ Kg, const uint16_t *__restrict__ Vg, const int32_t *ids,
+                            WaveRows<D> &rw) {
+    constexpr int KS = WaveRows<D>::KS, NU = WaveRows<D>::NU, UPL = WaveRows<D>::UPL;
+    const int l = lane_id(), q = l / 16, c16 = l % 16;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const size_t base = (size_t)ids[16 * mb + c16] * D + 8 * q;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = *reinterpret_cast<const bf16x8_t *>(Kg + base + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) rw.kf[mb][ks] = *reinterpret_cast<const bf16x8_t *>(Kg + base + 32 * ks);
     }
     // V: unit un = (key block kb = un % 4: keys 8 kb..8 kb + 7, chunk cg = un / 4:
     // dims 8 cg..8 cg + 7), D / 2 units over the 64 lanes
-    constexpr int NU = D / 2, UPL = (NU + kWave - 1) / kWave;
-    uint4 vv[UPL][8];
 #pragma unroll
     for (int t = 0; t < UPL; ++t) {
         const int un = l + kWave * t;
@@ -77,11 +80,21 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
             const int kb = un % 4, cg = un / 4;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                vv[t][j] = *reinterpret_cast<const uint4 *>(Vg + (size_t)ids[8 * kb + j] * D + 8 * cg);
+                rw.vv[t][j] = *reinterpret_cast<const uint4 *>(Vg + (size_t)ids[8 * kb + j] * D + 8 * cg);
         }
     }
-    // every K and V load is in flight before the first use of any of them
-    __builtin_amdgcn_sched_barrier(0);
+}
+
+// First half of a step on loaded rows: V^T staging, scores and the softmax
+// update; keys >= nk are masked.  Returns the P fragment and the rescale
+// factor; the caller orders the wave's LDS accesses before part 2.
+template <int D>
+LSA_DEV void wave_attn_compute(const WaveRows<D> &rw, int nk, const bf16x8_t (&qf)[D / 32], float scale_log2,
+                               uint16_t *vt, WaveAttn<D> &st, bf16x8_t &pf, float &alpha) {
+    constexpr int KS = WaveRows<D>::KS, NU = WaveRows<D>::NU, UPL = WaveRows<D>::UPL;
+    const int l = lane_id(), q = l / 16;
+    const auto &kf = rw.kf;
+    const auto &vv = rw.vv;
 #pragma unroll
     for (int t = 0; t < UPL; ++t) {
         const int un = l + kWave * t;
@@ -139,6 +152,18 @@ LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__
     ls += xor_lane_f<32>(ls);
     st.l = st.l * alpha + ls;
     st.m = m_new;
+}
+
+// Loads and first half of a step together (every K and V load is in flight
+// before the first use of any of them).
+template <int D>
+LSA_DEV void wave_attn_part1(const uint16_t *__restrict__ Kg, const uint16_t *__restrict__ Vg, const int32_t *ids,
+                             int nk, const bf16x8_t (&qf)[D / 32], float scale_log2, uint16_t *vt, WaveAttn<D> &st,
+                             bf16x8_t &pf, float &alpha) {
+    WaveRows<D> rw;
+    wave_attn_load<D>(Kg, Vg, ids, rw);
+    __builtin_amdgcn_sched_barrier(0);
+    wave_attn_compute<D>(rw, nk, qf, scale_log2, vt, st, pf, alpha);
 }
 
 // Second half: O^T = alpha * O^T + V^T P^T (V^T from this wave's LDS tile).
