@@ -442,23 +442,59 @@ struct NmArgs {
     int32_t *pairs;                // [groups * kFastP]: group * kFastP + slot, grouped by node
 };
 
+// kTopRows rows of one KV head per workgroup: W_g is staged once for them,
+// thread (rr, c) continues u[c] of row rr across the staged chunks (the same
+// order as fast_latent), and wave rr scores and ranks row rr's level 1.
+constexpr int kTopRows = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_nm_top(NmArgs N) {
     __shared__ __attribute__((aligned(16))) float Wl[kWRows * kFastR];
-    __shared__ __attribute__((aligned(16))) float qbar_s[256];
-    __shared__ __attribute__((aligned(16))) float u_s[kFastR];
-    __shared__ int32_t kept_s[kFastP];
-    __shared__ int keep_s;
+    __shared__ __attribute__((aligned(16))) float qbar_s[kTopRows][256];
+    __shared__ __attribute__((aligned(16))) float u_s[kTopRows][kFastR];
+    constexpr int R = kFastR;
     const SelectArgs &A = N.S;
-    const int64_t i = N.row0 + blockIdx.x;
     const int g = blockIdx.y;
-    const int64_t grp = (int64_t)blockIdx.x * A.h_kv + g;
-    fast_latent<T>(A, i, g, Wl, qbar_s, u_s);
-    fast_level1(A, g, u_s, kept_s, &keep_s);
-    const int tid = threadIdx.x;
-    if (tid < kFastR) N.U[grp * kFastR + tid] = u_s[tid];
-    if (tid < kFastP) N.kept[grp * kFastP + tid] = tid < keep_s ? kept_s[tid] : 0;
-    if (tid == 0) N.keep[grp] = keep_s;
+    const int64_t rb = (int64_t)blockIdx.x * kTopRows;                 // first row, relative to the batch
+    const int nr = (int)min<int64_t>(kTopRows, N.groups / A.h_kv - rb);
+    const int tid = threadIdx.x, G = A.h_q / A.h_kv, d = A.d;
+    const T *Q = (const T *)A.Q;
+    for (int e = tid; e < kTopRows * d; e += blockDim.x) {
+        const int rr = e / d, t = e % d;
+        float val = 0.0f;
+        if (rr < nr) {
+            const int64_t i = N.row0 + rb + rr;
+            double s = 0.0;
+            for (int h = 0; h < G; ++h) s = s + (double)to_float(Q[((size_t)i * A.h_q + (size_t)g * G + h) * d + t]);
+            val = (float)(s / (double)G);
+        }
+        qbar_s[rr][t] = val;
+    }
+    const int rr = tid / kWave, lane = tid % kWave;
+    double us = 0.0;
+    for (int t0 = 0; t0 < d; t0 += kWRows) {
+        const int nt = min(kWRows, d - t0);
+        __syncthreads();                 // qbar_s written / the previous chunk read
+        g2s_rows<4>(Wl, nt * R, A.W + ((size_t)g * d + t0) * R, nt * R, nt * R);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) us = fma((double)qbar_s[rr][t0 + t], (double)Wl[t * R + lane], us);
+    }
+    u_s[rr][lane] = (float)us;
+    wave_sync();
+    if (rr < nr) {
+        const int64_t grp = (rb + rr) * A.h_kv + g;
+        const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * R;
+        const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
+        uint64_t key = 0;
+        int pay = 0;
+        if (lane < A.b && cn1[lane] > 0) key = make_key(score_row64(u_s[rr], C1 + (size_t)lane * R), (uint32_t)lane);
+        const int nz = __popcll(__ballot(key != 0));
+        wave_sort_desc(key, pay);
+        const int keep = min(A.beam, nz);
+        N.U[grp * R + lane] = u_s[rr][lane];
+        if (lane < kFastP) N.kept[grp * kFastP + lane] = lane < keep ? (int32_t)key_id(key) : 0;
+        if (lane == 0) N.keep[grp] = keep;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_nm_zero(NmArgs N, int64_t count) {
@@ -916,7 +952,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         N.S = A; N.row0 = r0; N.groups = groups;
         N.U = w.U; N.kept = w.kept; N.keep = w.keep; N.keys = w.keys; N.eli = w.eli; N.lof = w.lof;
         N.ncnt = w.ncnt; N.noff = w.noff; N.fptr = w.fptr; N.pairs = w.pairs;
-        const dim3 tg((unsigned)nb, (unsigned)A.h_kv);
+        const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
         if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
         else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
         for (int l = 2; l <= A.L; ++l) {
