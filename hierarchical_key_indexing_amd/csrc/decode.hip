@@ -99,22 +99,24 @@ LSA_DEV void count_gt_lists(const uint64_t *a, int stride, int q0, int dq, int n
 }
 
 template <int RC>
-LSA_DEV float score_lds(const float *u, const float *row, int r) {
+LSA_DEV float score_lds(const double *u, const float *row, int r) {
     double s = 0.0;
     if constexpr (RC > 0 && RC % 4 == 0) {
-        // 16-byte LDS reads (u is a broadcast); products summed in dimension order
-        const f4_t *u4 = reinterpret_cast<const f4_t *>(u);
+        // 16-byte LDS reads (u, already widened, is a broadcast); products
+        // summed in dimension order
+        const double2 *u2 = reinterpret_cast<const double2 *>(u);
         const f4_t *r4 = reinterpret_cast<const f4_t *>(row);
 #pragma unroll
         for (int x = 0; x < RC / 4; ++x) {
-            const f4_t a = u4[x], c = r4[x];
-            s = fma((double)a.x, (double)c.x, s);
-            s = fma((double)a.y, (double)c.y, s);
-            s = fma((double)a.z, (double)c.z, s);
-            s = fma((double)a.w, (double)c.w, s);
+            const double2 a = u2[2 * x], b2 = u2[2 * x + 1];
+            const f4_t c = r4[x];
+            s = fma(a.x, (double)c.x, s);
+            s = fma(a.y, (double)c.y, s);
+            s = fma(b2.x, (double)c.z, s);
+            s = fma(b2.y, (double)c.w, s);
         }
     } else {
-        for (int x = 0; x < r; ++x) s = fma((double)u[x], (double)row[x], s);
+        for (int x = 0; x < r; ++x) s = fma(u[x], (double)row[x], s);
     }
     return (float)s;
 }
@@ -210,8 +212,8 @@ LSA_DEV void wave_stores_done() {
 template <typename T, bool ATTEND, int RC, int DC, int PC>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     extern __shared__ __attribute__((aligned(16))) float dyn[];
-    __shared__ float qbar_s[256];
-    __shared__ __attribute__((aligned(16))) float u_s[64];
+    __shared__ double qbar_s[256];                            // fl32(mean), widened
+    __shared__ __attribute__((aligned(16))) double u_s[64];   // fl32(u), widened
     __shared__ __attribute__((aligned(16))) float Cs[64 * kCS];
     __shared__ int32_t ccnt[64];
     __shared__ int32_t clo[65];
@@ -256,8 +258,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     const int vw = p + P * wv;
     f4_t rw[16];
     int32_t rcnt = 0;
-    float *Wl = dyn;               // [d][r]
-    float *Ql = dyn + d * r;       // [G][d]
+    // W_g staged widened to double in the bf16, d = 128, r = 64 kernel (no
+    // conversion in the u chain), as float otherwise
+    float *Wl = dyn;                                      // [d][r] float
+    double *Wd = reinterpret_cast<double *>(dyn);         // [d][r] double (kPreShape)
+    float *Ql = kPreShape ? dyn + 2 * d * r : dyn + d * r;   // [G][d]
     {
         const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
         const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
@@ -282,7 +287,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 *reinterpret_cast<f4_t *>(Cs + (e / 16) * kCS + (e % 16) * 4) = cr[u];
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) reinterpret_cast<f4_t *>(Wl)[tid + 256 * u] = wr[u];
+            for (int u = 0; u < 8; ++u) {
+                double2 *w2 = reinterpret_cast<double2 *>(Wd + 4 * (tid + 256 * u));
+                w2[0] = double2{(double)wr[u].x, (double)wr[u].y};
+                w2[1] = double2{(double)wr[u].z, (double)wr[u].w};
+            }
             if (tid < G * 16) {
                 const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
 #pragma unroll
@@ -318,18 +327,21 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     for (int t = tid; t < d; t += blockDim.x) {
         double s = 0.0;
         for (int h = 0; h < G; ++h) s = s + (double)Ql[h * d + t];
-        qbar_s[t] = (float)(s / (double)G);
+        qbar_s[t] = (double)(float)(s / (double)G);
     }
     lds_barrier();
     for (int c = tid; c < r; c += blockDim.x) {
         double s = 0.0;
         if constexpr (DC > 0) {
 #pragma unroll 32
-            for (int t = 0; t < DC; ++t) s = fma((double)qbar_s[t], (double)Wl[t * r + c], s);
+            for (int t = 0; t < DC; ++t) {
+                if constexpr (kPreShape) s = fma(qbar_s[t], Wd[t * r + c], s);
+                else s = fma(qbar_s[t], (double)Wl[t * r + c], s);
+            }
         } else {
-            for (int t = 0; t < d; ++t) s = fma((double)qbar_s[t], (double)Wl[t * r + c], s);
+            for (int t = 0; t < d; ++t) s = fma(qbar_s[t], (double)Wl[t * r + c], s);
         }
-        u_s[c] = (float)s;
+        u_s[c] = (double)(float)s;
     }
     lds_barrier();
     // ---- level 1 (every workgroup of the group computes the same ranking)
@@ -817,7 +829,9 @@ static int device_cus() {
 static bool fast_shape(int dtype, int d, int r) { return dtype == 1 && d == 128 && r == 64; }
 
 static size_t decode_dyn_bytes(int dtype, int G, int d, int r) {
-    const size_t stage = sizeof(float) * ((size_t)d * r + (size_t)G * d);                 // W, Q staging
+    // W (double in the fast shape), Q staging
+    const size_t stage = (fast_shape(dtype, d, r) ? sizeof(double) : sizeof(float)) * (size_t)d * r +
+                         sizeof(float) * (size_t)G * d;
     size_t att;
     if (fast_shape(dtype, d, r))
         att = std::max(sizeof(uint16_t) * 4 * (size_t)d * kVTS, sizeof(float) * (4 * (size_t)d * 16 + 128));
