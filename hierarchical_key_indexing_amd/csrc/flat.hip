@@ -123,6 +123,34 @@ LSA_DEV double dot_row(const float *u, const float (&c)[64], int r) {
     return s;
 }
 
+// u . c for four rows at once (u widened in LDS, rows at stride 64; c in
+// registers, each element widened once for the four rows): four independent
+// chains, each in ascending index order
+LSA_DEV void dot4_wide(const double *u, const float (&c)[64], double (&s)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = 0.0;
+#pragma unroll
+    for (int x0 = 0; x0 < 64; x0 += 4) {
+        double2 a[4][2];                 // 4 dimensions of the four rows, loaded together
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) a[q][h] = *reinterpret_cast<const double2 *>(u + q * 64 + x0 + 2 * h);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const double c0 = (double)c[x0 + 2 * h], c1 = (double)c[x0 + 2 * h + 1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s[q] = fma(a[q][h].x, c0, s[q]);
+                s[q] = fma(a[q][h].y, c1, s[q]);
+            }
+        }
+        // the step's products are summed here and its loaded values die: the
+        // next step's LDS reads stay after this point
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]) : : "memory");
+    }
+}
+
 // members of a leaf (ascending, pm[0..len), first and last given) in [rlo, rhi]
 LSA_DEV int members_in(const int32_t *pm, int len, int32_t first, int32_t last, int32_t rlo, int32_t rhi) {
     if (first >= rlo && last <= rhi) return len;
@@ -131,16 +159,25 @@ LSA_DEV int members_in(const int32_t *pm, int len, int32_t first, int32_t last, 
 }
 
 template <int RC>
-__global__ __launch_bounds__(256) void k_flat_score(FlatArgs A) {
-    __shared__ __attribute__((aligned(16))) float u_s[kFlatRows * 64];
+__global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
+    // r = 64: u widened to double (rows beyond nr zero); otherwise float
+    constexpr bool kWide = RC == 64;
+    __shared__ __attribute__((aligned(16))) float u_raw[kWide ? kFlatRows * 64 * 2 : kFlatRows * 64];
+    float *u_s = u_raw;
+    double *u_d = reinterpret_cast<double *>(u_raw);
     __shared__ int32_t rlo_s[kFlatRows], rhi_s[kFlatRows];
     const int64_t v0 = (int64_t)blockIdx.x * kFlatLeaves;
     const int64_t i0 = (int64_t)blockIdx.y * kFlatRows;
     const int g = blockIdx.z;
     const int r = RC > 0 ? RC : A.r;
     const int nr = (int)min<int64_t>(kFlatRows, A.mb - i0);
-    for (int e = threadIdx.x; e < nr * r; e += blockDim.x)
-        u_s[(e / r) * 64 + e % r] = A.U[((size_t)(i0 + e / r) * A.h_kv + g) * r + e % r];
+    if constexpr (kWide) {
+        for (int e = threadIdx.x; e < kFlatRows * 64; e += blockDim.x)
+            u_d[e] = e / 64 < nr ? (double)A.U[((size_t)(i0 + e / 64) * A.h_kv + g) * 64 + e % 64] : 0.0;
+    } else {
+        for (int e = threadIdx.x; e < nr * r; e += blockDim.x)
+            u_s[(e / r) * 64 + e % r] = A.U[((size_t)(i0 + e / r) * A.h_kv + g) * r + e % r];
+    }
     if ((int)threadIdx.x < nr) {
         const AttnSet as = attn_set(A.q_pos[i0 + threadIdx.x], A.n, A.n_sink, A.window);
         rlo_s[threadIdx.x] = as.rlo;
@@ -152,6 +189,7 @@ __global__ __launch_bounds__(256) void k_flat_score(FlatArgs A) {
     const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
     const int32_t *pm = A.perm + (size_t)g * A.n;
     const size_t rs = (size_t)A.h_kv * A.nleaf;              // stride between rows
+#pragma unroll 1
     for (int j = 0; j < kFlatLeaves / 256; ++j) {
         const int64_t v = v0 + j * 256 + threadIdx.x;
         if (v >= A.nleaf) break;
@@ -169,6 +207,39 @@ __global__ __launch_bounds__(256) void k_flat_score(FlatArgs A) {
         }
         const int32_t a0 = lo[v], a1 = lo[v + 1];
         const int32_t first = pm[a0], last = pm[a1 - 1];
+        if constexpr (kWide) {
+            float cw[64];
+            const f4_t *c4 = reinterpret_cast<const f4_t *>(Cg + (size_t)v * 64);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const f4_t t = c4[x];
+                cw[4 * x] = t.x; cw[4 * x + 1] = t.y; cw[4 * x + 2] = t.z; cw[4 * x + 3] = t.w;
+            }
+#pragma unroll 1
+            for (int rr = 0; rr < nr; rr += 4) {
+                // (the row stays float: widening it once for every row step would
+                // need 128 registers)
+#pragma unroll
+                for (int x = 0; x < 64; ++x) asm volatile("" : "+v"(cw[x]));
+                int eq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    eq[q] = rr + q < nr ? members_in(pm + a0, a1 - a0, first, last, rlo_s[rr + q], rhi_s[rr + q]) : 0;
+                double sq[4];
+                dot4_wide(u_d + rr * 64, cw, sq);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (rr + q < nr) {
+                        const int e = eq[q];
+                        const uint32_t oq = e > 0 ? orderable((float)sq[q]) : 0u;
+                        A.sc[o + (rr + q) * rs] = oq;
+                        A.wt[o + (rr + q) * rs] = (uint16_t)min(e, A.k);
+                        if (sampled) sp[(rr + q) * ss] = e > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
+                    }
+                }
+            }
+            continue;
+        }
         float cr[64];
         if constexpr (RC == 64) {
             const f4_t *c4 = reinterpret_cast<const f4_t *>(Cg + (size_t)v * 64);
