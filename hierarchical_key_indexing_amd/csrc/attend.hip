@@ -11,6 +11,8 @@
 // gathered K/V row once.  The set is cut into `nsplit` slices (split-K) to
 // fill the chip when there are few rows; slices keep a running max and sum
 // (online softmax, base 2) and a merge kernel combines them by log-sum-exp.
+// In the matrix-core kernel each wave keeps the next 32-key step's gathers in
+// flight while it computes the current one.
 #include "common.h"
 #include "internal.h"
 #include "mfma_attn.h"

@@ -418,15 +418,19 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
 // once into registers and scores them against every row that kept it.  The
 // keys (with their slots), eligible counts and first members are those of
 // k_select_fast, so the rows it writes are identical.
-//   k_nm_top     per (row, KV head): u and level 1, as k_select_fast;
+//   k_nm_top     u and level 1 as k_select_fast, four rows of one KV head per
+//                workgroup;
 //   k_nm_zero, k_nm_count, k_nm_scan, k_nm_fill: the pairs grouped by node;
 //   k_nm_score   64 pairs per workgroup, 16 per wave: the wave keeps the
 //                children rows of its current node in registers (lane c:
 //                child c) and writes each pair's 64 candidate keys (at the
 //                leaf level also eligible counts and first members);
+//                k_nm_score_packed, for b <= 32, scores two pairs per wave
+//                step and the readers take the packed slots (nm_slot);
 //   k_nm_keep    internal levels, per (row, KV head): the top `beam` by a
 //                weighted radix selection and a one-wave sort;
-//   k_nm_finish  leaf level, per (row, KV head): block sort and fill.
+//   k_nm_finish  leaf level, per (row, KV head): block sort (1024 slots, or
+//                the 512 packed ones) and fill.
 
 struct NmArgs {
     SelectArgs S;
