@@ -36,15 +36,12 @@ struct AttendArgs {
     float *part;          // [m][h_q][nsplit][d + 2] when nsplit > 1
 };
 
-// The (row, KV head) group i * h_kv + g a workgroup serves.  Workgroups are
-// taken head-major (all rows of KV head 0, then head 1, ...), so the
-// workgroups resident at one time gather from one head's K/V region and the
-// shared last-level cache holds a larger part of it than when the heads of
-// every row are interleaved.
-LSA_DEV int64_t attend_group(const AttendArgs &A) {
-    const int64_t y = blockIdx.y;
-    return (y % A.m) * A.h_kv + y / A.m;
-}
+// The (row, KV head) group of head-major index y (all rows of KV head 0,
+// then head 1, ...): the workgroups resident at one time then gather from
+// one head's K/V region, and the shared last-level cache holds a larger part
+// of it than when the heads of every row are interleaved.
+LSA_DEV int64_t attend_row(const AttendArgs &A, int64_t y) { return (y % A.m) * A.h_kv + y / A.m; }
+
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
@@ -58,7 +55,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     float *Sc = Vs + kTK * d;            // [G][kTK]
     __shared__ int32_t ids[kTK];
 
-    const int64_t row = attend_group(A);     // i * h_kv + g
+    const int64_t row = attend_row(A, blockIdx.y);     // i * h_kv + g
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int split = blockIdx.x;
@@ -142,94 +139,168 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
 // with the matrix-core step of mfma_attn.h and keeps its own softmax state;
 // the four states are combined at the end.
 constexpr int kIdsCap = 2048;       // selected ids of a slice staged in LDS at a time
+constexpr int kWaveMax = 1024;      // sets this short are attended by one wave each
+constexpr int kIdsW = kIdsCap / 4;  // ids staged per wave in that mode
 
+
+// Output of one group from a normalised-later state: o / l in the input
+// dtype (or the partial state of split `split`), lse on request.
+LSA_DEV void attend_write(const AttendArgs &A, int64_t i, int g, int h, int dd, const floatx4_t &o, float M, float Ls,
+                          int split, int D) {
+    const size_t oh = (size_t)i * A.h_q + (size_t)g * (A.h_q / A.h_kv) + h;
+    if (A.nsplit == 1) {
+        const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+        bf16_t *op = (bf16_t *)A.out + oh * D + dd;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) op[j] = from_float<bf16_t>(o[j] * inv);
+        if (dd == 0 && A.lse) A.lse[oh] = (Ls > 0.0f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+    } else {
+        float *pp = A.part + (oh * A.nsplit + split) * (size_t)(D + 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pp[dd + j] = o[j];
+        if (dd == 0) { pp[D] = M; pp[D + 1] = Ls; }
+    }
+}
+
+// One wave's steps over ids[0, own) (LDS), the next step's gathers in flight
+// while the current one is computed; steps step0, step0 + stride, ...
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attend_mfma(AttendArgs A) {
-    __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * kVTS];
-    __shared__ int32_t ids_s[kIdsCap + 4 * kMT];
-    const int64_t row = attend_group(A);
+LSA_DEV void attend_steps(const uint16_t *Kg, const uint16_t *Vg, const int32_t *ids, int own, int step0, int stride,
+                          const bf16x8_t (&qf)[D / 32], float scale_log2, uint16_t *vt, WaveAttn<D> &st,
+                          bool &first) {
+    const int nsteps = (own + kMT - 1) / kMT;
+    if (step0 >= nsteps) return;
+    WaveRows<D> ra, rb;
+    int t = step0;
+    wave_attn_load<D>(Kg, Vg, ids + t * kMT, ra);
+    while (t < nsteps) {
+        // step t in ra, the next one loading into rb (then the roles swap)
+        if (t + stride < nsteps) wave_attn_load<D>(Kg, Vg, ids + (t + stride) * kMT, rb);
+        {
+            bf16x8_t pf;
+            float alpha;
+            wave_attn_compute<D>(ra, max(0, min(kMT, own - t * kMT)), qf, scale_log2, vt, st, pf, alpha);
+            wave_sync();
+            wave_attn_part2<D>(vt, pf, alpha, st, first);
+            wave_sync();
+            first = false;
+        }
+        t += stride;
+        if (t >= nsteps) break;
+        if (t + stride < nsteps) wave_attn_load<D>(Kg, Vg, ids + (t + stride) * kMT, ra);
+        {
+            bf16x8_t pf;
+            float alpha;
+            wave_attn_compute<D>(rb, max(0, min(kMT, own - t * kMT)), qf, scale_log2, vt, st, pf, alpha);
+            wave_sync();
+            wave_attn_part2<D>(vt, pf, alpha, st, first);
+            wave_sync();
+            first = false;
+        }
+        t += stride;
+    }
+}
+
+// All four waves on one group's slice `split`: ids staged kIdsCap at a time,
+// wave w takes steps w, w + 4, ...; the four states are combined in LDS.
+template <int D>
+LSA_DEV void attend_group_coop(const AttendArgs &A, int64_t row, int split, uint16_t (*vt)[D * kVTS],
+                               int32_t *ids_s) {
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int G = A.h_q / A.h_kv;
-    const int split = blockIdx.x;
     const int cnt = A.sel_count[row];
     const int per = (cnt + A.nsplit - 1) / A.nsplit;
     const int s0 = min(cnt, split * per), s1 = min(cnt, s0 + per);
-    const int w = threadIdx.x / kWave, l = lane_id();
+    const int w = threadIdx.x / kWave;
     const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * D;
     const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * D;
     const uint16_t *Qb = (const uint16_t *)A.Q + ((size_t)i * A.h_q + (size_t)g * G) * D;
     const int32_t *S = A.sel + (size_t)row * A.k;
-
     bf16x8_t qf[D / 32];
     wave_load_q<D>(qf, Qb, G);
     WaveAttn<D> st;
     wave_attn_init<D>(st);
     bool first = true;
-    // The slice's ids come to LDS kIdsCap at a time (padded with the chunk's
-    // first id to whole 4 x 32-key steps); wave w takes steps w, w + 4, ...
-    // of the chunk and keeps the next step's K/V loads in flight while it
-    // computes the current one.  Only the wave itself reads its V^T tile.
+    // (ids padded with the chunk's first id to whole 4 x 32-key steps)
     for (int c0 = s0; c0 < s1; c0 += kIdsCap) {
         const int own = min(kIdsCap, s1 - c0);
         const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
         for (int f = threadIdx.x; f < nsteps * 4 * kMT; f += blockDim.x) ids_s[f] = S[c0 + (f < own ? f : 0)];
         __syncthreads();
-        WaveRows<D> ra, rb;
-        int t = 0;
-        if (nsteps > 0) wave_attn_load<D>(Kg, Vg, ids_s + w * kMT, ra);
-        while (t < nsteps) {
-            // step t in ra, step t + 1 loading into rb (then the roles swap)
-            if (t + 1 < nsteps) wave_attn_load<D>(Kg, Vg, ids_s + (4 * (t + 1) + w) * kMT, rb);
-            {
-                const int nk = max(0, min(kMT, own - (4 * t + w) * kMT));
-                bf16x8_t pf;
-                float alpha;
-                wave_attn_compute<D>(ra, nk, qf, A.scale_log2, vt[w], st, pf, alpha);
-                wave_sync();
-                wave_attn_part2<D>(vt[w], pf, alpha, st, first);
-                wave_sync();
-                first = false;
-            }
-            ++t;
-            if (t >= nsteps) break;
-            if (t + 1 < nsteps) wave_attn_load<D>(Kg, Vg, ids_s + (4 * (t + 1) + w) * kMT, ra);
-            {
-                const int nk = max(0, min(kMT, own - (4 * t + w) * kMT));
-                bf16x8_t pf;
-                float alpha;
-                wave_attn_compute<D>(rb, nk, qf, A.scale_log2, vt[w], st, pf, alpha);
-                wave_sync();
-                wave_attn_part2<D>(vt[w], pf, alpha, st, first);
-                wave_sync();
-                first = false;
-            }
-            ++t;
-        }
+        attend_steps<D>(Kg, Vg, ids_s, own, w, 4, qf, A.scale_log2, vt[w], st, first);
         __syncthreads();                 // ids_s is rewritten by the next chunk
     }
     __syncthreads();
     float *scratch = reinterpret_cast<float *>(&vt[0][0]);
     wave_attn_stash<D>(st, scratch);
     __syncthreads();
-    const float ln2 = 0.69314718055994531f;
     for (int e4 = threadIdx.x; e4 < G * D / 4; e4 += blockDim.x) {
         const int h = e4 / (D / 4), dd = 4 * (e4 % (D / 4));
         float M, Ls;
         const floatx4_t o = wave_attn_combine4<D>(scratch, h, dd, M, Ls);
-        const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
-        if (A.nsplit == 1) {
-            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-            bf16_t *op = (bf16_t *)A.out + oh * D + dd;
+        attend_write(A, i, g, h, dd, o, M, Ls, split, D);
+    }
+}
+
+// One wave on one whole group (nsplit == 1), ids staged kIdsW at a time in
+// the wave's own part of ids_s; the wave writes the outputs itself.
+template <int D>
+LSA_DEV void attend_group_wave(const AttendArgs &A, int64_t row, uint16_t *vt, int32_t *ids_w) {
+    const int l = lane_id();
+    const int64_t i = row / A.h_kv;
+    const int g = (int)(row % A.h_kv);
+    const int G = A.h_q / A.h_kv;
+    const int cnt = A.sel_count[row];
+    const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * D;
+    const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * D;
+    const uint16_t *Qb = (const uint16_t *)A.Q + ((size_t)i * A.h_q + (size_t)g * G) * D;
+    const int32_t *S = A.sel + (size_t)row * A.k;
+    bf16x8_t qf[D / 32];
+    wave_load_q<D>(qf, Qb, G);
+    WaveAttn<D> st;
+    wave_attn_init<D>(st);
+    bool first = true;
+    for (int c0 = 0; c0 < cnt; c0 += kIdsW) {
+        const int own = min(kIdsW, cnt - c0);
+        const int nsteps = (own + kMT - 1) / kMT;
+        for (int f = l; f < nsteps * kMT; f += kWave) ids_w[f] = S[c0 + (f < own ? f : 0)];
+        wave_sync();
+        attend_steps<D>(Kg, Vg, ids_w, own, 0, 1, qf, A.scale_log2, vt, st, first);
+        wave_sync();
+    }
+    // lane l holds head l % 16, dimensions 16 nb + 4 (l / 16) + j
+    const int h = l % 16, q = l / 16;
+    if (h < G) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) op[j] = from_float<bf16_t>(o[j] * inv);
-            if (dd == 0 && A.lse) A.lse[oh] = (Ls > 0.0f) ? (M + log2f(Ls)) * ln2 : -INFINITY;
-        } else {
-            float *pp = A.part + (oh * A.nsplit + split) * (size_t)(D + 2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[dd + j] = o[j];
-            if (dd == 0) { pp[D] = M; pp[D + 1] = Ls; }
-        }
+        for (int nb = 0; nb < D / 16; ++nb) attend_write(A, i, g, h, 16 * nb + 4 * q, st.acc[nb], st.m, st.l, 0, D);
+    }
+}
+
+// nsplit > 1: one group's slice per workgroup (grid nsplit x groups).
+// nsplit == 1: four consecutive head-major groups per workgroup; when all
+// four sets are short (<= kWaveMax keys) each wave attends one of them alone,
+// otherwise the four waves take the groups one after another together.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attend_mfma(AttendArgs A) {
+    __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * kVTS];
+    __shared__ int32_t ids_s[kIdsCap];
+    if (A.nsplit > 1) {
+        attend_group_coop<D>(A, attend_row(A, blockIdx.y), blockIdx.x, vt, ids_s);
+        return;
+    }
+    const int64_t y0 = (int64_t)blockIdx.x * 4;
+    const int ny = (int)min<int64_t>(4, A.m * A.h_kv - y0);
+    int cmax = 0;
+    for (int q = 0; q < ny; ++q) cmax = max(cmax, A.sel_count[attend_row(A, y0 + q)]);
+    if (cmax <= kWaveMax) {
+        const int w = threadIdx.x / kWave;
+        if (w < ny) attend_group_wave<D>(A, attend_row(A, y0 + w), vt[w], ids_s + w * kIdsW);
+        return;
+    }
+    for (int q = 0; q < ny; ++q) {
+        attend_group_coop<D>(A, attend_row(A, y0 + q), 0, vt, ids_s);
+        __syncthreads();                 // vt (the combine scratch) and ids_s are reused by the next group
     }
 }
 
@@ -296,9 +367,10 @@ hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_
         hipLaunchKernelGGL(k_attend<float>, grid, dim3(256), shm, st, A);
         if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<float>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
     } else {
-        if (d == 128) hipLaunchKernelGGL(k_attend_mfma<128>, grid, dim3(256), 0, st, A);
-        else if (d == 64) hipLaunchKernelGGL(k_attend_mfma<64>, grid, dim3(256), 0, st, A);
-        else if (d == 256) hipLaunchKernelGGL(k_attend_mfma<256>, grid, dim3(256), 0, st, A);
+        const dim3 mgrid = A.nsplit > 1 ? grid : dim3((unsigned)((m * h_kv + 3) / 4));
+        if (d == 128) hipLaunchKernelGGL(k_attend_mfma<128>, mgrid, dim3(256), 0, st, A);
+        else if (d == 64) hipLaunchKernelGGL(k_attend_mfma<64>, mgrid, dim3(256), 0, st, A);
+        else if (d == 256) hipLaunchKernelGGL(k_attend_mfma<256>, mgrid, dim3(256), 0, st, A);
         else hipLaunchKernelGGL(k_attend<bf16_t>, grid, dim3(256), shm, st, A);
         if (A.nsplit > 1) hipLaunchKernelGGL(k_attend_merge<bf16_t>, dim3((unsigned)(m * h_q)), dim3(128), 0, st, A);
     }
