@@ -166,6 +166,37 @@ __global__ void k_init(const int32_t *__restrict__ off_prev, const int32_t *__re
 }
 
 // ---------------------------------------------------------------- Lloyd round
+// Squared distances of z to four centroids (four independent chains), the
+// same arithmetic as sq_dist2.
+LSA_DEV void sq_dist4(const double (&z)[64], const double *c0, int r, double (&d)[4]) {
+#pragma clang fp contract(off)
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int x = 0; x < 64; x += 2) {
+        if (x < r) {
+            double2 a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = *reinterpret_cast<const double2 *>(c0 + q * 64 + x);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double e = z[x] - a[q].x;
+                const double p = e * e;
+                s[q] = s[q] + p;
+            }
+            if (x + 1 < r) {                 // (LDS entries at and beyond r are never written)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const double e = z[x + 1] - a[q].y;
+                    const double p = e * e;
+                    s[q] = s[q] + p;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = s[q];
+}
+
 // Squared distances of z to two centroids: per dimension, in ascending order,
 // diff = z - c, then diff * diff and the running sum as separate roundings
 // (no fused multiply-add); the same arithmetic as widening each float when
@@ -225,7 +256,15 @@ __global__ __launch_bounds__(kPiece) void k_assign(const Piece *__restrict__ pie
         for (int x = 0; x < 64; ++x) z[x] = (x < r) ? (double)zr[x] : 0.0;
         double bestd = 0.0;
         int c = 0;
-        // two children per step (independent chains), compared in child order
+        // four, then two children per step (independent chains), compared in
+        // child order
+        for (; c + 4 <= a; c += 4) {
+            double dq[4];
+            sq_dist4(z, Cs + c * 64, r, dq);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if ((c + q == 0) || dq[q] < bestd) { bestd = dq[q]; best = c + q; }
+        }
         for (; c + 2 <= a; c += 2) {
             double d0, d1;
             sq_dist2(z, Cs + c * 64, Cs + (c + 1) * 64, r, d0, d1);
