@@ -14,7 +14,8 @@
 //   k_flat_score     1024 leaves x up to 64 rows of one KV head per workgroup:
 //                    a leaf's centroid row is loaded once into registers and
 //                    scored against every row's u (double accumulation in
-//                    ascending index order, two rows at a time), and its
+//                    ascending index order, four rows at a time, u read
+//                    widened through scalar loads), and its
 //                    members in each row's retrieval range are counted; writes
 //                    the score and min(count, k) of every (row, leaf), and the
 //                    keys of every S-th leaf as a sample;
@@ -60,6 +61,7 @@ struct FlatArgs {
     const float *W;
     int k, n_sink, window, row;
     float *U;                   // [mb][h_kv][r]
+    double *Ud;                 // [mb][h_kv][r]: U widened (read by the scoring through scalar loads)
     uint32_t *sc;               // [mb][h_kv][nleaf] orderable scores
     uint16_t *wt;               // [mb][h_kv][nleaf] min(members in range, k); 0: not a candidate
     int64_t S;                  // sample stride (0: no sample, every candidate is collected)
@@ -98,7 +100,10 @@ __global__ __launch_bounds__(256) void k_flat_latent(FlatArgs A) {
             for (int t = 0; t < nt; ++t) s = fma((double)qbar_s[t0 + t], (double)w_s[t * r + threadIdx.x], s);
         __syncthreads();
     }
-    if ((int)threadIdx.x < r) A.U[((size_t)i * A.h_kv + g) * r + threadIdx.x] = (float)s;
+    if ((int)threadIdx.x < r) {
+        A.U[((size_t)i * A.h_kv + g) * r + threadIdx.x] = (float)s;
+        A.Ud[((size_t)i * A.h_kv + g) * r + threadIdx.x] = (double)(float)s;
+    }
 }
 
 // u . c in double, ascending index (u from LDS, 64-float padded; c in registers)
@@ -123,31 +128,29 @@ LSA_DEV double dot_row(const float *u, const float (&c)[64], int r) {
     return s;
 }
 
-// u . c for four rows at once (u widened in LDS, rows at stride 64; c in
-// registers, each element widened once for the four rows): four independent
-// chains, each in ascending index order
-LSA_DEV void dot4_wide(const double *u, const float (&c)[64], double (&s)[4]) {
+// u . c for four rows at once, u read from memory through uniform addresses
+// (scalar loads: every lane uses the same value, as one operand of the fp64
+// FMA), c in registers widened once per step: four independent chains, each
+// in ascending index order.
+typedef __attribute__((address_space(4))) const double const_f64;   // read-only, scalar-loadable
+
+LSA_DEV const_f64 *as_const(const double *p) { return (const_f64 *)(uintptr_t)p; }
+
+LSA_DEV void dot4_uniform(const_f64 *u0, const_f64 *u1, const_f64 *u2, const_f64 *u3, const float (&c)[64],
+                          double (&s)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) s[q] = 0.0;
 #pragma unroll
-    for (int x0 = 0; x0 < 64; x0 += 4) {
-        double2 a[4][2];                 // 4 dimensions of the four rows, loaded together
+    for (int x0 = 0; x0 < 64; x0 += 8) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) a[q][h] = *reinterpret_cast<const double2 *>(u + q * 64 + x0 + 2 * h);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const double c0 = (double)c[x0 + 2 * h], c1 = (double)c[x0 + 2 * h + 1];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s[q] = fma(a[q][h].x, c0, s[q]);
-                s[q] = fma(a[q][h].y, c1, s[q]);
-            }
+        for (int x = x0; x < x0 + 8; ++x) {
+            const double cx = (double)c[x];
+            s[0] = fma(u0[x], cx, s[0]);
+            s[1] = fma(u1[x], cx, s[1]);
+            s[2] = fma(u2[x], cx, s[2]);
+            s[3] = fma(u3[x], cx, s[3]);
         }
-        // the step's products are summed here and its loaded values die: the
-        // next step's LDS reads stay after this point
-        asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]) : : "memory");
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
     }
 }
 
@@ -160,21 +163,16 @@ LSA_DEV int members_in(const int32_t *pm, int len, int32_t first, int32_t last, 
 
 template <int RC>
 __global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
-    // r = 64: u widened to double (rows beyond nr zero); otherwise float
+    // r = 64: u read widened from memory (A.Ud); otherwise staged as float in LDS
     constexpr bool kWide = RC == 64;
-    __shared__ __attribute__((aligned(16))) float u_raw[kWide ? kFlatRows * 64 * 2 : kFlatRows * 64];
-    float *u_s = u_raw;
-    double *u_d = reinterpret_cast<double *>(u_raw);
+    __shared__ __attribute__((aligned(16))) float u_s[kWide ? 4 : kFlatRows * 64];
     __shared__ int32_t rlo_s[kFlatRows], rhi_s[kFlatRows];
     const int64_t v0 = (int64_t)blockIdx.x * kFlatLeaves;
     const int64_t i0 = (int64_t)blockIdx.y * kFlatRows;
     const int g = blockIdx.z;
     const int r = RC > 0 ? RC : A.r;
     const int nr = (int)min<int64_t>(kFlatRows, A.mb - i0);
-    if constexpr (kWide) {
-        for (int e = threadIdx.x; e < kFlatRows * 64; e += blockDim.x)
-            u_d[e] = e / 64 < nr ? (double)A.U[((size_t)(i0 + e / 64) * A.h_kv + g) * 64 + e % 64] : 0.0;
-    } else {
+    if constexpr (!kWide) {
         for (int e = threadIdx.x; e < nr * r; e += blockDim.x)
             u_s[(e / r) * 64 + e % r] = A.U[((size_t)(i0 + e / r) * A.h_kv + g) * r + e % r];
     }
@@ -217,8 +215,8 @@ __global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
             }
 #pragma unroll 1
             for (int rr = 0; rr < nr; rr += 4) {
-                // (the row stays float: widening it once for every row step would
-                // need 128 registers)
+                // (the row stays float and is widened at each use: widened once
+                // it would take 128 registers and cost occupancy)
 #pragma unroll
                 for (int x = 0; x < 64; ++x) asm volatile("" : "+v"(cw[x]));
                 int eq[4];
@@ -226,7 +224,11 @@ __global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
                 for (int q = 0; q < 4; ++q)
                     eq[q] = rr + q < nr ? members_in(pm + a0, a1 - a0, first, last, rlo_s[rr + q], rhi_s[rr + q]) : 0;
                 double sq[4];
-                dot4_wide(u_d + rr * 64, cw, sq);
+                const double *ub = A.Ud + ((size_t)i0 * A.h_kv + g) * 64;
+                const size_t us = (size_t)A.h_kv * 64;       // between rows (rows past nr repeat the last)
+                dot4_uniform(as_const(ub + (size_t)min(rr, nr - 1) * us), as_const(ub + (size_t)min(rr + 1, nr - 1) * us),
+                             as_const(ub + (size_t)min(rr + 2, nr - 1) * us),
+                             as_const(ub + (size_t)min(rr + 3, nr - 1) * us), cw, sq);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (rr + q < nr) {
@@ -689,7 +691,7 @@ __global__ __launch_bounds__(256) void k_flat_finish(FlatArgs A) {
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct FlatWs {
-    float *U; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt; uint64_t *lst; size_t bytes;
+    float *U; double *Ud; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt; uint64_t *lst; size_t bytes;
 };
 
 FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
@@ -698,6 +700,7 @@ FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
     const size_t groups = (size_t)mb * h_kv;
     w.U = (float *)take(sizeof(float) * groups * r);
+    w.Ud = (double *)take(sizeof(double) * groups * r);
     w.sc = (uint32_t *)take(sizeof(uint32_t) * groups * nleaf);
     w.wt = (uint16_t *)take(sizeof(uint16_t) * groups * nleaf);
     w.smp = (uint64_t *)take(sizeof(uint64_t) * groups * kSampleMax);
@@ -755,7 +758,7 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
         A.leaf_off = (const int32_t *)(index + leaf_off_off);
         A.perm = (const int32_t *)(index + perm_off);
         A.W = W; A.k = k; A.n_sink = n_sink; A.window = window; A.row = row;
-        A.U = w.U; A.sc = w.sc; A.wt = w.wt;
+        A.U = w.U; A.Ud = w.Ud; A.sc = w.sc; A.wt = w.wt;
         A.S = S; A.ns = S > 0 ? (int)((nleaf + S - 1) / S) : 0;
         A.smp = w.smp; A.thr = w.thr; A.lcnt = w.lcnt; A.lwt = w.lwt; A.lst = w.lst;
         A.sel = sel + (size_t)i0 * h_kv * row;
