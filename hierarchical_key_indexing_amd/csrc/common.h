@@ -141,8 +141,8 @@ LSA_DEV int wave_sum_i(int v) {
     return v;
 }
 
-// An opaque copy of v: per-stage lane masks are then recomputed by each stage
-// instead of being kept live (in scalar registers) across the whole network.
+// An opaque copy of v: values derived from it are recomputed where they are
+// used instead of being hoisted and kept live in registers.
 LSA_DEV int opaque(int v) {
     asm volatile("" : "+v"(v));
     return v;
