@@ -162,19 +162,29 @@ def test_workspace_reused_across_shapes(lsa):
             assert torch.equal(a, b_), f"select-only {nm} differs with a reused workspace (beam {bm}, k {k})"
 
 
+# shapes run at their own beam only (their full beam exceeds the selection limits)
+BEAM_ONLY = {
+    # bf16, d = 128, r = 64, b = 32, L = 3: the decode kernel's waves own
+    # level-1 nodes p + beam w; with beam 16 waves 2 and 3 own none
+    "owned_b32": dict(n=40000, h_q=16, h_kv=2, d=128, dtype="bf16", r=64, b=32, L=3, beam=16, k=1500,
+                      centres=800, m=3, mode="decode"),
+}
 LOCAL_CASES = [("tiny_4k", {}), ("ragged_bf16_b5", {}), ("multi_piece_root", {}),
-               ("multi_piece_root", dict(beam=16)), ("odd_r_deep", {}), ("flat_L1", {})]
+               ("multi_piece_root", dict(beam=16)), ("odd_r_deep", {}), ("flat_L1", {}),
+               ("owned_b32", {}), ("owned_b32", dict(beam=8))]
 LOCAL_SETS = [(4, 16), (0, 300), (7, 0), (50, 100000)]
 
 
-@pytest.mark.parametrize("name,over", LOCAL_CASES, ids=[f"{c[0]}{'_beam16' if c[1] else ''}" for c in LOCAL_CASES])
+@pytest.mark.parametrize("name,over", LOCAL_CASES,
+                         ids=[c[0] + "".join(f"_{k}{v}" for k, v in c[1].items()) for c in LOCAL_CASES])
 def test_sinks_and_window_match_oracle(lsa, name, over):
     """Sinks and a recent window joined to the retrieved keys: every select
     path (one workgroup per row, the multi-workgroup kernel, the fused
     select + attend) gives the oracle's rows bit for bit, and attention over
     them matches the oracle's."""
     dev = torch.device("cuda:0")
-    w = _wl("tiny_4k", **dict(SMALL)[name]) if name != "tiny_4k" else _wl("tiny_4k")
+    shapes = {**dict(SMALL), **BEAM_ONLY}
+    w = _wl("tiny_4k", **shapes[name]) if name != "tiny_4k" else _wl("tiny_4k")
     w = w.replace(name=name, **over)
     data = _inputs(w, dev)
     index, desc, gix, oix = _build_both(lsa, w, data)
