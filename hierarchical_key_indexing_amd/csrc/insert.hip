@@ -14,7 +14,8 @@
 //     keys, and the member array's per-head stride grows from n to n + m.
 //
 // Kernels, in stream order:
-//   k_ins_copy     the member array and leaf offsets to the workspace;
+//   k_ins_copy     the member array and leaf offsets to the workspace (16-byte
+//                  copies of the contiguous [h][n] and [h][leaves + 1] arrays);
 //   k_ins_descend  one wave per new key: its latent (lane c: dimension c,
 //                  summed as the build's projection does), then lane c scores
 //                  child c of the node at every level;
@@ -22,9 +23,14 @@
 //                  pairs sorted, each node's run (one wave, a lane per
 //                  dimension) summed in key order and its centroid and count
 //                  rewritten;
-//   k_ins_perm     one thread per leaf: new offset = old offset + new keys in
-//                  earlier leaves (binary search in the sorted leaf run), old
-//                  members then new keys written in place.
+//   k_ins_offsets  one thread per leaf: new offset = old offset + new keys in
+//                  earlier leaves (binary search in the sorted leaf run); and
+//                  the new position of every sorted new key (the end of its
+//                  leaf in the old list plus the new keys before it);
+//   k_ins_gather   one thread per slot of the new member list: the new key
+//                  placed there, or the old member shifted by the number of
+//                  new keys before the slot (binary search over the new keys'
+//                  positions in LDS), coalesced reads and writes.
 #include <algorithm>
 
 #include "common.h"
@@ -51,17 +57,24 @@ struct InsArgs {
     uint64_t *slist;               // [h][kInsMax] (leaf << 32 | key) sorted, level L
     int32_t *perm_old;             // [h][n]
     int32_t *lo_old;               // [h][nleaf + 1]
+    int32_t *qpos, *qid;           // [h][kInsMax] new position and key id of each sorted new key
 };
 
+// Flat copy of `count` ints from src to dst (both 16-byte aligned): 16-byte
+// moves, then the tail.
+LSA_DEV void copy_ints(int32_t *__restrict__ dst, const int32_t *__restrict__ src, int64_t count, int64_t t0,
+                       int64_t stride) {
+    const int64_t n4 = count / 4;
+    const int4 *s4 = reinterpret_cast<const int4 *>(src);
+    int4 *d4 = reinterpret_cast<int4 *>(dst);
+    for (int64_t e = t0; e < n4; e += stride) d4[e] = s4[e];
+    for (int64_t e = 4 * n4 + t0; e < count; e += stride) dst[e] = src[e];
+}
+
 __global__ __launch_bounds__(256) void k_ins_copy(InsArgs A) {
-    const int g = blockIdx.y;
-    const int32_t *perm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
-    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nleaf + 1);
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.n + A.nleaf + 1;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        if (e < A.n) A.perm_old[(size_t)g * A.n + e] = perm[e];
-        else A.lo_old[(size_t)g * (A.nleaf + 1) + (e - A.n)] = lo[e - A.n];
-    }
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+    copy_ints(A.perm_old, (const int32_t *)(A.index + A.perm_off), (int64_t)A.h * A.n, t0, stride);
+    copy_ints(A.lo_old, (const int32_t *)(A.index + A.leaf_off_off), (int64_t)A.h * (A.nleaf + 1), t0, stride);
 }
 
 template <typename T>
@@ -184,29 +197,55 @@ LSA_DEV int leaf_lower(const uint64_t *sl, int m, uint32_t v) {
     return lo;
 }
 
-__global__ __launch_bounds__(256) void k_ins_perm(InsArgs A) {
+__global__ __launch_bounds__(256) void k_ins_offsets(InsArgs A) {
     const int g = blockIdx.y;
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (v > A.nleaf) return;
     const int m = (int)A.m;
     const int64_t nn = A.n + A.m;
-    int32_t *lo_new = (int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nleaf + 1);
-    int32_t *perm_new = (int32_t *)(A.index + A.perm_off) + (size_t)g * nn;
-    if (v == A.nleaf) { lo_new[v] = (int32_t)nn; return; }
     const uint64_t *sl = A.slist + (size_t)g * kInsMax;
-    const int lb = leaf_lower(sl, m, (uint32_t)v), ub = leaf_lower(sl, m, (uint32_t)v + 1);
     const int32_t *lo = A.lo_old + (size_t)g * (A.nleaf + 1);
-    const int32_t a0 = lo[v], a1 = lo[v + 1];
-    const int64_t o = (int64_t)a0 + lb;
-    lo_new[v] = (int32_t)o;
-    const int32_t *po = A.perm_old + (size_t)g * A.n;
-    for (int32_t t = 0; t < a1 - a0; ++t) perm_new[o + t] = po[a0 + t];
-    for (int t = 0; t < ub - lb; ++t) perm_new[o + (a1 - a0) + t] = (int32_t)(A.n + (uint32_t)sl[lb + t]);
+    if (v < m) {
+        // sorted new key v: after its leaf's old members and the new keys before it
+        const uint32_t leaf = (uint32_t)(sl[v] >> 32);
+        A.qpos[(size_t)g * kInsMax + v] = lo[leaf + 1] + (int32_t)v;
+        A.qid[(size_t)g * kInsMax + v] = (int32_t)(A.n + (uint32_t)sl[v]);
+    }
+    if (v > A.nleaf) return;
+    int32_t *lo_new = (int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nleaf + 1);
+    lo_new[v] = v == A.nleaf ? (int32_t)nn : lo[v] + leaf_lower(sl, m, (uint32_t)v);
+}
+
+constexpr int kInsStage = 1024;    // new-key positions staged in LDS by every gather workgroup (up to)
+
+__global__ __launch_bounds__(256) void k_ins_gather(InsArgs A) {
+    __shared__ int32_t q_s[kInsStage];
+    const int g = blockIdx.y;
+    const int m = (int)A.m;
+    const int64_t nn = A.n + A.m;
+    const int32_t *qp = A.qpos + (size_t)g * kInsMax;
+    const bool staged = m <= kInsStage;
+    if (staged) {
+        for (int e = threadIdx.x; e < m; e += blockDim.x) q_s[e] = qp[e];
+        __syncthreads();
+    }
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= nn) return;
+    // c = number of new keys placed before slot j (larger batches search the
+    // positions in memory, where they stay cached)
+    const int32_t *q = staged ? q_s : qp;
+    int lo = 0, hi = m;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (q[mid] < j) lo = mid + 1; else hi = mid;
+    }
+    int32_t *perm_new = (int32_t *)(A.index + A.perm_off) + (size_t)g * nn;
+    perm_new[j] = (lo < m && q[lo] == j) ? A.qid[(size_t)g * kInsMax + lo]
+                                           : A.perm_old[(size_t)g * A.n + (j - lo)];
 }
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct InsWs { float *Z; int32_t *path; uint64_t *slist; int32_t *perm_old, *lo_old; size_t bytes; };
+struct InsWs { float *Z; int32_t *path; uint64_t *slist; int32_t *perm_old, *lo_old, *qpos, *qid; size_t bytes; };
 
 InsWs carve_ins_ws(char *base, int64_t m, int64_t n, int h, int r, int L, int64_t nleaf) {
     size_t cur = 0;
@@ -217,6 +256,8 @@ InsWs carve_ins_ws(char *base, int64_t m, int64_t n, int h, int r, int L, int64_
     w.slist = (uint64_t *)take(sizeof(uint64_t) * (size_t)h * kInsMax);
     w.perm_old = (int32_t *)take(sizeof(int32_t) * (size_t)h * n);
     w.lo_old = (int32_t *)take(sizeof(int32_t) * (size_t)h * (nleaf + 1));
+    w.qpos = (int32_t *)take(sizeof(int32_t) * (size_t)h * kInsMax);
+    w.qid = (int32_t *)take(sizeof(int32_t) * (size_t)h * kInsMax);
     w.bytes = cur;
     return w;
 }
@@ -237,13 +278,15 @@ hipError_t index_insert(const void *K_new, int dtype, int64_t m, int d, const fl
     InsWs w = carve_ins_ws((char *)ws, m, n, h, r, L, A.nleaf);
     A.K = K_new; A.d = d; A.dtype = dtype; A.W = W;
     A.Z = w.Z; A.path = w.path; A.slist = w.slist; A.perm_old = w.perm_old; A.lo_old = w.lo_old;
-    const int64_t ncopy = n + A.nleaf + 1;
-    hipLaunchKernelGGL(k_ins_copy, dim3((unsigned)std::min<int64_t>((ncopy + 255) / 256, 4096), (unsigned)h), dim3(256),
-                       0, st, A);
+    A.qpos = w.qpos; A.qid = w.qid;
+    const int64_t ncopy4 = ((int64_t)h * (n + A.nleaf + 1) + 3) / 4;
+    hipLaunchKernelGGL(k_ins_copy, dim3((unsigned)std::min<int64_t>((ncopy4 + 255) / 256, 8192)), dim3(256), 0, st, A);
     if (dtype == 0) hipLaunchKernelGGL(k_ins_descend<float>, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
     else hipLaunchKernelGGL(k_ins_descend<bf16_t>, dim3((unsigned)((m + 3) / 4), (unsigned)h), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_ins_update, dim3((unsigned)L, (unsigned)h), dim3(256), 0, st, A);
-    hipLaunchKernelGGL(k_ins_perm, dim3((unsigned)((A.nleaf + 1 + 255) / 256), (unsigned)h), dim3(256), 0, st, A);
+    const int64_t noff = std::max<int64_t>(A.nleaf + 1, m);
+    hipLaunchKernelGGL(k_ins_offsets, dim3((unsigned)((noff + 255) / 256), (unsigned)h), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_ins_gather, dim3((unsigned)((n + m + 255) / 256), (unsigned)h), dim3(256), 0, st, A);
     return hipGetLastError();
 }
 
