@@ -420,13 +420,14 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
 // k_select_fast, so the rows it writes are identical.
 //   k_nm_top     u and level 1 as k_select_fast, four rows of one KV head per
 //                workgroup;
-//   k_nm_zero, k_nm_count, k_nm_scan, k_nm_fill: the pairs grouped by node;
-//   k_nm_score   64 pairs per workgroup, 16 per wave: the wave keeps the
-//                children rows of its current node in registers (lane c:
-//                child c) and writes each pair's 64 candidate keys (at the
-//                leaf level also eligible counts and first members);
-//                k_nm_score_packed, for b <= 32, scores two pairs per wave
-//                step and the readers take the packed slots (nm_slot);
+//   k_nm_zero, k_nm_count, k_nm_scan, k_nm_fill: the pairs grouped by node
+//                (each entry with its node);
+//   k_nm_score_mfma  64 pairs per workgroup, 16 per wave: the wave's pairs
+//                times the children of their node on the fp64 matrix cores,
+//                each pair's candidate keys written to its slots (64 per
+//                kept node; with b <= 32 the first 32 of them, the packed
+//                slots of nm_slot), at the leaf level with eligible counts
+//                and first members;
 //   k_nm_keep    internal levels, per (row, KV head): the top `beam` by a
 //                weighted radix selection and a one-wave sort;
 //   k_nm_finish  leaf level, per (row, KV head): block sort (1024 slots, or
@@ -444,6 +445,7 @@ struct NmArgs {
     int32_t *eli, *lof;            // [groups][kFastP * 64] (leaf level)
     int32_t *ncnt, *noff, *fptr;   // [h_kv * nodes(level - 1) + 1]
     int32_t *pairs;                // [groups * kFastP]: group * kFastP + slot, grouped by node
+    int32_t *pnode;                // [groups * kFastP]: the node of each entry of pairs
 };
 
 // kTopRows rows of one KV head per workgroup: W_g is staged once for them,
@@ -575,7 +577,11 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
     if (nbins > kNmBins) {
         for (int u = threadIdx.x; u < kNmChunk; u += blockDim.x) {
             const int64_t bin = nm_bin(N, e0 + u);
-            if (bin >= 0) N.pairs[atomicAdd(N.fptr + bin, 1)] = (int32_t)(e0 + u);
+            if (bin >= 0) {
+                const int32_t at = atomicAdd(N.fptr + bin, 1);
+                N.pairs[at] = (int32_t)(e0 + u);
+                N.pnode[at] = (int32_t)(bin % N.S.nodes[N.level - 1]);
+            }
         }
         return;
     }
@@ -594,214 +600,209 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (bin[u] >= 0) N.pairs[h_s[bin[u]] + rk[u]] = (int32_t)(e0 + threadIdx.x + 256 * u);
+        if (bin[u] >= 0) {
+            const int32_t at = h_s[bin[u]] + rk[u];
+            N.pairs[at] = (int32_t)(e0 + threadIdx.x + 256 * u);
+            N.pnode[at] = (int32_t)(bin[u] % N.S.nodes[N.level - 1]);
+        }
 }
 
-__global__ __launch_bounds__(256) void k_nm_score(NmArgs N) {
-    __shared__ __attribute__((aligned(16))) float u_s[4][kFastR];
+// Members of a leaf held in registers by the scorer (longer leaves are
+// searched in memory).
+constexpr int kNmMemReg = 8;
+
+// fp64 MFMA: v_mfma_f64_16x16x4_f64 accumulates D[i][j] += A[i][k] * B[k][j]
+// over k = 0..3 in order, each step rounded as a separate fma would be, so a
+// chain over dims 4 * blk + k (blk ascending) gives the sequential double sum
+// of the exact float products bit for bit.  Lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; element e of lane l is D[l / 16 + 4 e][l % 16].
+typedef double d4_t __attribute__((ext_vector_type(4)));
+
+// 4 x 4 transpose across the four 16-lane rows of a wave: on return lane
+// (row r, column c) holds in x[t] what lane (row t, column c) held in x[r].
+LSA_DEV void transpose_rows4(f4_t &v) {
+    int x0 = __float_as_int(v.x), x1 = __float_as_int(v.y), x2 = __float_as_int(v.z), x3 = __float_as_int(v.w);
+    const auto p = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+    x0 = p[0]; x2 = p[1]; x1 = q[0]; x3 = q[1];
+    const auto r = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+    const auto t = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
+    v.x = __int_as_float(r[0]); v.y = __int_as_float(r[1]); v.z = __int_as_float(t[0]); v.w = __int_as_float(t[1]);
+}
+
+// A 64-float row spread over the 16-lane column c: lane (row k, column c)
+// loads the quads q0 + k (q0 = 0, 4, 8, 12: four 16-byte loads, the four
+// lanes of a column reading 64 contiguous bytes), and after the transposes
+// element t of load q0 / 4 is dim 4 (q0 + t) + k, the MFMA operand for block
+// q0 + t.
+LSA_DEV void load_row_mfma(const float *row, int k, f4_t (&v)[4]) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const f4_t *>(row + 16 * h + 4 * k);
+}
+
+// The wave's 16 pairs are the 16 rows of the product (lane (k, c): u of pair
+// c at dims 4 blk + k, widened once), a node's children are its columns, 16
+// at a time (lane (k, c): child 16 cb + c).  Runs of pairs that share a
+// (head, node) take that node's children; rows outside the run are computed
+// and dropped.  Each lane then owns the scores of four pairs (k + 4 e)
+// against one child and writes their keys, and at the leaf level eligible
+// counts and first members.  At the leaf level a run's member ranges and
+// first members are loaded with lane = child and shared through LDS; the
+// next block's rows are loaded while a block is multiplied.
+__global__ __launch_bounds__(256) void k_nm_score_mfma(NmArgs N) {
+    __shared__ int32_t pe_s[4][16], pv_s[4][16], pp_s[4][16];
+    constexpr int kInfo = 3 + kNmMemReg;              // a0, len, last, first members
+    __shared__ int32_t info_s[4][kInfo][64];
     constexpr int R = kFastR;
     const SelectArgs &A = N.S;
     const int l = N.level, b = A.b;
     const bool leaf = l == A.L;
     const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int col = lane & 15, kk = lane >> 4;
+    const int ncb = b <= 32 ? 2 : 4;                   // 16-child column blocks written (packed slots when b <= 32)
+    const int nvb = (b + 15) / 16;                     // blocks that hold children
     const int64_t nodes_prev = A.nodes[l - 1];
     const int64_t npairs = N.noff[(size_t)A.h_kv * nodes_prev];
     const float *Cl = (const float *)(A.index + A.centroid_off[l]);
     const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]);
-    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off);
-    const int32_t *pm = (const int32_t *)(A.index + A.perm_off);
-    __shared__ int32_t pe_s[4][16], pv_s[4][16], pp_s[4][16];
-    int64_t cur = -1;                                  // (head, node) whose children are in registers
-    float row[R];
-    int c_cnt = 0, c_a0 = 0, c_a1 = 0, c_first = 0, c_last = 0;
-    int64_t child = 0;
-    const int64_t p0 = (int64_t)blockIdx.x * 64 + wv * 16;
-    const int np = (int)max<int64_t>(0, min<int64_t>(16, npairs - p0));
-    if (np == 0) return;                               // wave-local: the kernel has no block barrier
-    // the wave's pairs up front: entry, node and query position (lanes 0..15),
-    // and every pair's u (lane x: component x), all loads issued together
-    if (lane < 16) {
-        const int e = N.pairs[p0 + min(lane, np - 1)];
-        const int64_t grp = e / kFastP;
-        pe_s[wv][lane] = e;
-        pv_s[wv][lane] = N.kept[grp * kFastP + e % kFastP];
-        pp_s[wv][lane] = A.q_pos[N.row0 + grp / A.h_kv];
-    }
-    wave_sync();
-    float uq[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) uq[q] = N.U[(size_t)(pe_s[wv][min(q, np - 1)] / kFastP) * R + lane];
-    for (int q = 0; q < np; ++q) {
-        const int e = pe_s[wv][q];
-        const int64_t grp = e / kFastP;
-        const int j = e % kFastP;
-        const int g = (int)(grp % A.h_kv);
-        const int64_t v = pv_s[wv][q];
-        const int64_t hv = (int64_t)g * nodes_prev + v;
-        if (hv != cur) {
-            // the node's children (lane c: child c) into registers
-            cur = hv;
-            child = v * b + min(lane, b - 1);
-            const size_t gc = (size_t)g * A.nodes[l] + child;
-            const f4_t *c4 = reinterpret_cast<const f4_t *>(Cl + gc * R);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const f4_t t4 = c4[x];
-                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
-            }
-            c_cnt = lane < b ? cn[gc] : 0;
-            if (leaf) {
-                const int32_t *lg = lo + (size_t)g * (A.nodes[l] + 1);
-                c_a0 = lg[child];
-                c_a1 = lg[child + 1];
-                const int32_t *pg = pm + (size_t)g * A.n;
-                c_first = c_cnt > 0 ? pg[c_a0] : 0;
-                c_last = c_cnt > 0 ? pg[c_a1 - 1] : 0;
-            }
-        }
-        float uv = uq[0];
-#pragma unroll
-        for (int x = 1; x < 16; ++x) uv = (q == x) ? uq[x] : uv;
-        u_s[wv][lane] = uv;
-        wave_sync();
-        uint64_t key = 0;
-        int e_c = 0, f_c = 0;
-        if (c_cnt > 0) {
-            int ok = 1;
-            if (leaf) {
-                const AttnSet as = attn_set(pp_s[wv][q], A.n, A.n_sink, A.window);
-                if (as.all || (c_first >= as.rlo && c_last <= as.rhi)) { e_c = c_a1 - c_a0; f_c = 0; }
-                else if (c_last < as.rlo || c_first > as.rhi) { e_c = 0; }
-                else in_range(as, pm + (size_t)g * A.n + c_a0, c_a1 - c_a0, f_c, e_c);
-                ok = e_c > 0;
-            }
-            if (ok) {
-                const f4_t *u4 = reinterpret_cast<const f4_t *>(u_s[wv]);
-                double sc = 0.0;
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const f4_t a = u4[x];
-                    sc = fma((double)a.x, (double)row[4 * x + 0], sc);
-                    sc = fma((double)a.y, (double)row[4 * x + 1], sc);
-                    sc = fma((double)a.z, (double)row[4 * x + 2], sc);
-                    sc = fma((double)a.w, (double)row[4 * x + 3], sc);
-                }
-                key = make_key_slot((float)sc, (uint32_t)(v * b + lane), j * 64 + lane);
-            }
-        }
-        const size_t o = (size_t)grp * (kFastP * 64) + j * 64 + lane;
-        N.keys[o] = key;
-        if (leaf) { N.eli[o] = e_c; N.lof[o] = c_a0 + f_c; }
-        wave_sync();
-    }
-}
-
-// b <= 32: each wave takes its 16 pairs two at a time, lanes 0..31 the first
-// and lanes 32..63 the second (lane = child in its half), with the same
-// arithmetic as k_nm_score.  Slots j * 64 + 32 .. j * 64 + 63 are not
-// written; the readers use the packed order (nm_slot).
-__global__ __launch_bounds__(256) void k_nm_score_packed(NmArgs N) {
-    __shared__ __attribute__((aligned(16))) float u_s[4][2][kFastR];
-    __shared__ int32_t pe_s[4][16], pv_s[4][16], pp_s[4][16];
-    constexpr int R = kFastR;
-    const SelectArgs &A = N.S;
-    const int l = N.level, b = A.b;
-    const bool leaf = l == A.L;
-    const int wv = threadIdx.x / kWave, lane = lane_id();
-    const int hf = lane >> 5, c = lane & 31;
-    const int64_t nodes_prev = A.nodes[l - 1];
-    const int64_t npairs = N.noff[(size_t)A.h_kv * nodes_prev];
-    const float *Cl = (const float *)(A.index + A.centroid_off[l]);
-    const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]);
-    const int32_t *lo = (const int32_t *)(A.index + A.leaf_off_off);
     const int32_t *pm = (const int32_t *)(A.index + A.perm_off);
     const int64_t p0 = (int64_t)blockIdx.x * 64 + wv * 16;
     const int np = (int)max<int64_t>(0, min<int64_t>(16, npairs - p0));
     if (np == 0) return;                               // wave-local: the kernel has no block barrier
     if (lane < 16) {
-        const int e = N.pairs[p0 + min(lane, np - 1)];
-        const int64_t grp = e / kFastP;
+        const int64_t at = p0 + min(lane, np - 1);
+        const int e = N.pairs[at];
         pe_s[wv][lane] = e;
-        pv_s[wv][lane] = N.kept[grp * kFastP + e % kFastP];
-        pp_s[wv][lane] = A.q_pos[N.row0 + grp / A.h_kv];
+        pv_s[wv][lane] = N.pnode[at];
+        pp_s[wv][lane] = A.q_pos[N.row0 + (e / kFastP) / A.h_kv];
     }
     wave_sync();
-    float uq[16];
+    // runs of one (head, node): pair q starts one when it differs from pair q - 1
+    bool head = lane == 0;
+    if (lane > 0 && lane < np) {
+        const int e1 = pe_s[wv][lane], e0 = pe_s[wv][lane - 1];
+        head = pv_s[wv][lane] != pv_s[wv][lane - 1] || (e1 / kFastP) % A.h_kv != (e0 / kFastP) % A.h_kv;
+    }
+    uint64_t starts = __ballot(head) & ~1ull;          // the first run starts at pair 0
+    int s = 0;
+    int g = (int)((__builtin_amdgcn_readfirstlane(pe_s[wv][0]) / kFastP) % A.h_kv);
+    int64_t v = __builtin_amdgcn_readfirstlane(pv_s[wv][0]);
+    // A operand: pair col (rows past np repeat the last pair)
+    double ua[16];
+    {
+        f4_t t[4];
+        load_row_mfma(N.U + (size_t)(pe_s[wv][min(col, np - 1)] / kFastP) * R, kk, t);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) uq[q] = N.U[(size_t)(pe_s[wv][min(q, np - 1)] / kFastP) * R + lane];
-    int64_t cur = -1;                                  // this half's (head, node) whose children are in registers
-    float row[R];
-    int c_cnt = 0, c_a0 = 0, c_a1 = 0, c_first = 0, c_last = 0;
-    for (int q0 = 0; q0 < np; q0 += 2) {
-        const int q = min(q0 + hf, np - 1);
-        const bool act = q0 + hf < np;
-        const int e = pe_s[wv][q];
-        const int64_t grp = e / kFastP;
-        const int j = e % kFastP;
-        const int g = (int)(grp % A.h_kv);
-        const int64_t v = pv_s[wv][q];
-        const int64_t hv = (int64_t)g * nodes_prev + v;
-        if (act && hv != cur) {
-            cur = hv;
-            const int64_t child = v * b + min(c, b - 1);
-            const size_t gc = (size_t)g * A.nodes[l] + child;
-            const f4_t *c4 = reinterpret_cast<const f4_t *>(Cl + gc * R);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const f4_t t4 = c4[x];
-                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
-            }
-            c_cnt = c < b ? cn[gc] : 0;
-            if (leaf) {
-                const int32_t *lg = lo + (size_t)g * (A.nodes[l] + 1);
-                c_a0 = lg[child];
-                c_a1 = lg[child + 1];
-                const int32_t *pg = pm + (size_t)g * A.n;
-                c_first = c_cnt > 0 ? pg[c_a0] : 0;
-                c_last = c_cnt > 0 ? pg[c_a1 - 1] : 0;
-            }
+        for (int h = 0; h < 4; ++h) {
+            transpose_rows4(t[h]);
+            ua[4 * h] = (double)t[h].x; ua[4 * h + 1] = (double)t[h].y;
+            ua[4 * h + 2] = (double)t[h].z; ua[4 * h + 3] = (double)t[h].w;
         }
-        // u of both pairs (lane x: component x)
-        float ua = uq[0], ub = uq[0];
+    }
+    while (true) {
+        const int e_end = starts ? __builtin_ctzll(starts) : np;
+        const size_t gc0 = (size_t)g * A.nodes[l] + (size_t)v * b;      // the node's first child
+        // block 0's children rows and counts (the next block's are loaded while
+        // this one is multiplied)
+        f4_t cur[4];
+        load_row_mfma(Cl + (gc0 + min(col, b - 1)) * R, kk, cur);
+        int cnt_cur = col < b ? cn[gc0 + col] : 0;
+        if (leaf) {
+            // lane c: child c's member range and first members (clamped into the
+            // head's member array: an empty leaf may start at n)
+            const int32_t *pg = pm + (size_t)g * A.n;
+            const int32_t *lg = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (A.nodes[l] + 1) + (size_t)v * b;
+            const int c = min(lane, b - 1);
+            const int a0 = lg[c], len = lane < b ? lg[c + 1] - a0 : 0;
+            int32_t mem[kNmMemReg];
 #pragma unroll
-        for (int x = 1; x < 16; ++x) {
-            ua = (q0 == x) ? uq[x] : ua;
-            ub = (min(q0 + 1, np - 1) == x) ? uq[x] : ub;
+            for (int t = 0; t < kNmMemReg; ++t) mem[t] = pg[min<int64_t>(a0 + max(0, min(t, len - 1)), A.n - 1)];
+            const int32_t last = len > kNmMemReg ? pg[a0 + len - 1] : mem[kNmMemReg - 1];
+            wave_sync();                               // the previous run's readers are done
+            info_s[wv][0][lane] = a0;
+            info_s[wv][1][lane] = len;
+            info_s[wv][2][lane] = last;
+#pragma unroll
+            for (int t = 0; t < kNmMemReg; ++t) info_s[wv][3 + t][lane] = mem[t];
+            wave_sync();
         }
-        u_s[wv][0][lane] = ua;
-        u_s[wv][1][lane] = ub;
-        wave_sync();
-        uint64_t key = 0;
-        int e_c = 0, f_c = 0;
-        if (act && c_cnt > 0) {
-            int ok = 1;
-            if (leaf) {
-                const AttnSet as = attn_set(pp_s[wv][q], A.n, A.n_sink, A.window);
-                if (as.all || (c_first >= as.rlo && c_last <= as.rhi)) { e_c = c_a1 - c_a0; f_c = 0; }
-                else if (c_last < as.rlo || c_first > as.rhi) { e_c = 0; }
-                else in_range(as, pm + (size_t)g * A.n + c_a0, c_a1 - c_a0, f_c, e_c);
-                ok = e_c > 0;
+#pragma unroll 1
+        for (int cb = 0; cb < ncb; ++cb) {
+            const int c = 16 * cb + col;               // child index inside the node
+            const bool more = cb + 1 < nvb;
+            f4_t nxt[4];
+            int cnt_nxt = 0;
+            if (more) {
+                load_row_mfma(Cl + (gc0 + min(c + 16, b - 1)) * R, kk, nxt);
+                cnt_nxt = c + 16 < b ? cn[gc0 + c + 16] : 0;
             }
-            if (ok) {
-                const f4_t *u4 = reinterpret_cast<const f4_t *>(u_s[wv][hf]);
-                double sc = 0.0;
+            d4_t acc = {0.0, 0.0, 0.0, 0.0};
+            const int c_cnt = cb < nvb ? cnt_cur : 0;
+            if (cb < nvb) {
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const f4_t a = u4[x];
-                    sc = fma((double)a.x, (double)row[4 * x + 0], sc);
-                    sc = fma((double)a.y, (double)row[4 * x + 1], sc);
-                    sc = fma((double)a.z, (double)row[4 * x + 2], sc);
-                    sc = fma((double)a.w, (double)row[4 * x + 3], sc);
+                for (int h = 0; h < 4; ++h) {
+                    f4_t t = cur[h];
+                    transpose_rows4(t);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h], (double)t.x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 1], (double)t.y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 2], (double)t.z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 3], (double)t.w, acc, 0, 0, 0);
                 }
-                key = make_key_slot((float)sc, (uint32_t)(v * b + c), j * 64 + c);
+            }
+            int c_a0 = 0, c_len = 0, c_last = 0;
+            int32_t mem[kNmMemReg];
+            if (leaf) {
+                const int ci = min(c, 63);
+                c_a0 = info_s[wv][0][ci];
+                c_len = c_cnt > 0 ? info_s[wv][1][ci] : 0;
+                c_last = info_s[wv][2][ci];
+#pragma unroll
+                for (int t = 0; t < kNmMemReg; ++t) mem[t] = info_s[wv][3 + t][ci];
+            }
+#pragma unroll 1
+            for (int e = 0; e < 4; ++e) {
+                const int q = kk + 4 * e;
+                if (q < s || q >= e_end) continue;
+                const double sc = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
+                const int pe_e = pe_s[wv][q];
+                int ec = c_len, fc = 0;
+                if (leaf && c_len > 0) {
+                    const AttnSet as = attn_set(pp_s[wv][q], A.n, A.n_sink, A.window);
+                    const int32_t first = mem[0];
+                    if (as.all || (first >= as.rlo && c_last <= as.rhi)) {
+                    } else if (c_last < as.rlo || first > as.rhi) {
+                        ec = 0;
+                    } else if (c_len <= kNmMemReg) {
+                        int a = 0, z = 0;
+#pragma unroll
+                        for (int u = 0; u < kNmMemReg; ++u) {
+                            a += (u < c_len && mem[u] < as.rlo) ? 1 : 0;
+                            z += (u < c_len && mem[u] <= as.rhi) ? 1 : 0;
+                        }
+                        fc = a;
+                        ec = max(0, z - a);
+                    } else {
+                        in_range(as, pm + (size_t)g * A.n + c_a0, c_len, fc, ec);
+                    }
+                }
+                const bool ok = c_cnt > 0 && (!leaf || ec > 0);
+                const int j = pe_e % kFastP;
+                const uint64_t key = ok ? make_key_slot((float)sc, (uint32_t)(v * b + c), j * 64 + c) : 0ull;
+                const size_t o = (size_t)(pe_e / kFastP) * (kFastP * 64) + j * 64 + c;
+                N.keys[o] = key;
+                if (leaf) { N.eli[o] = ok ? ec : 0; N.lof[o] = c_a0 + (ok ? fc : 0); }
+            }
+            if (more) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) cur[h] = nxt[h];
+                cnt_cur = cnt_nxt;
             }
         }
-        if (act) {
-            const size_t o = (size_t)grp * (kFastP * 64) + j * 64 + c;
-            N.keys[o] = key;
-            if (leaf) { N.eli[o] = e_c; N.lof[o] = c_a0 + f_c; }
-        }
-        wave_sync();
+        if (!starts) break;
+        s = __builtin_ctzll(starts);
+        starts &= starts - 1;
+        g = (int)((__builtin_amdgcn_readfirstlane(pe_s[wv][s]) / kFastP) % A.h_kv);
+        v = __builtin_amdgcn_readfirstlane(pv_s[wv][s]);
     }
 }
 
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
 
 static inline size_t nm_a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct NmWs { float *U; int32_t *kept, *keep; uint64_t *keys; int32_t *eli, *lof, *ncnt, *noff, *fptr, *pairs; size_t bytes; };
+struct NmWs { float *U; int32_t *kept, *keep; uint64_t *keys; int32_t *eli, *lof, *ncnt, *noff, *fptr, *pairs, *pnode; size_t bytes; };
 
 static NmWs carve_nm_ws(char *base, int64_t groups, int h_kv, int64_t max_nodes) {
     size_t cur = 0;
@@ -924,6 +925,7 @@ static NmWs carve_nm_ws(char *base, int64_t groups, int h_kv, int64_t max_nodes)
     w.noff = (int32_t *)take(sizeof(int32_t) * (h_kv * max_nodes + 1));
     w.fptr = (int32_t *)take(sizeof(int32_t) * (h_kv * max_nodes + 1));
     w.pairs = (int32_t *)take(sizeof(int32_t) * groups * kFastP);
+    w.pnode = (int32_t *)take(sizeof(int32_t) * groups * kFastP);
     w.bytes = cur;
     return w;
 }
@@ -955,7 +957,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         NmArgs N{};
         N.S = A; N.row0 = r0; N.groups = groups;
         N.U = w.U; N.kept = w.kept; N.keep = w.keep; N.keys = w.keys; N.eli = w.eli; N.lof = w.lof;
-        N.ncnt = w.ncnt; N.noff = w.noff; N.fptr = w.fptr; N.pairs = w.pairs;
+        N.ncnt = w.ncnt; N.noff = w.noff; N.fptr = w.fptr; N.pairs = w.pairs; N.pnode = w.pnode;
         const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
         if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
         else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
@@ -970,8 +972,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
             hipLaunchKernelGGL(k_nm_scan, dim3(1), dim3(256), 0, st, N, cnt);
             hipLaunchKernelGGL(k_nm_fill, dim3(cg), dim3(256), hb, st, N, cnt);
             const bool packed = A.b <= 32;
-            if (packed) hipLaunchKernelGGL(k_nm_score_packed, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
-            else hipLaunchKernelGGL(k_nm_score, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
+            hipLaunchKernelGGL(k_nm_score_mfma, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
             if (l < A.L) hipLaunchKernelGGL(k_nm_keep, dim3((unsigned)groups), dim3(256), 0, st, N);
             else if (packed) hipLaunchKernelGGL(k_nm_finish<2>, dim3((unsigned)groups), dim3(256), 0, st, N);
             else hipLaunchKernelGGL(k_nm_finish<4>, dim3((unsigned)groups), dim3(256), 0, st, N);
