@@ -219,6 +219,7 @@ int lsa_select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, const i
                                     nleaf, desc->centroid_off[desc->L], desc->count_off[desc->L],
                                     desc->leaf_off_off, desc->perm_off, W, k, n_sink, window, sel, sel_count,
                                     sel_cutoff, ws, ws_bytes, (hipStream_t)stream);
+    if (e == hipSuccess) e = lsa::ws_clear_polled(ws, ws_bytes, (hipStream_t)stream);
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
@@ -262,6 +263,7 @@ int lsa_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m
     if (scale == 0.0f) scale = 1.0f / sqrtf((float)d);
     hipError_t e = lsa::attend(Q, K, V, dtype, m, h_q, h_kv, n, d, sel, sel_count, k, scale, out, lse, ws,
                                (hipStream_t)stream);
+    if (e == hipSuccess && need > 0) e = lsa::ws_clear_polled(ws, ws_bytes, (hipStream_t)stream);
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }
 
@@ -314,6 +316,8 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
         if (e == hipSuccess)
             e = lsa::attend(Q, K, V, dtype, m, h_q, desc->h_kv, desc->n, d, sel, sel_count, k + n_sink + window,
                             scale, out, lse, ws, (hipStream_t)stream);
+        // the attention's partial states sit where a later one-launch call polls
+        if (e == hipSuccess) e = lsa::ws_clear_polled(ws, ws_bytes, (hipStream_t)stream);
     }
     return e == hipSuccess ? LSA_OK : LSA_EHIP;
 }

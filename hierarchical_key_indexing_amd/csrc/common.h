@@ -558,4 +558,61 @@ LSA_DEV void in_range(const AttnSet &s, const int32_t *mem, int len, int &first,
     cnt = max(0, z - a);
 }
 
+// fp64 MFMA: v_mfma_f64_16x16x4_f64 accumulates D[i][j] += A[i][k] * B[k][j]
+// over k = 0..3 in order, each step rounded as a separate fma would be, so a
+// chain over dims 4 * blk + k (blk ascending) gives the sequential double sum
+// of the exact float products bit for bit.  Lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; element e of lane l is D[l / 16 + 4 e][l % 16].
+typedef double d4_t __attribute__((ext_vector_type(4)));
+
+// 4 x 4 transpose across the four 16-lane rows of a wave: on return lane
+// (row r, column c) holds in x[t] what lane (row t, column c) held in x[r].
+LSA_DEV void transpose_rows4(f4_t &v) {
+    int x0 = __float_as_int(v.x), x1 = __float_as_int(v.y), x2 = __float_as_int(v.z), x3 = __float_as_int(v.w);
+    const auto p = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+    x0 = p[0]; x2 = p[1]; x1 = q[0]; x3 = q[1];
+    const auto r = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+    const auto t = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
+    v.x = __int_as_float(r[0]); v.y = __int_as_float(r[1]); v.z = __int_as_float(t[0]); v.w = __int_as_float(t[1]);
+}
+
+// A 64-float row spread over the 16-lane column c: lane (row k, column c)
+// loads the quads q0 + k (q0 = 0, 4, 8, 12: four 16-byte loads, the four
+// lanes of a column reading 64 contiguous bytes), and after the transposes
+// element t of load q0 / 4 is dim 4 (q0 + t) + k, the MFMA operand for block
+// q0 + t.
+LSA_DEV void load_row_mfma(const float *row, int k, f4_t (&v)[4]) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const f4_t *>(row + 16 * h + 4 * k);
+}
+
+
+// The A operand of a 64-dim row (load_row_mfma layout) widened once: ua[blk]
+// is dim 4 blk + k of the lane's row.
+LSA_DEV void widen_row_mfma(f4_t (&v)[4], double (&ua)[16]) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        transpose_rows4(v[h]);
+        ua[4 * h] = (double)v[h].x; ua[4 * h + 1] = (double)v[h].y;
+        ua[4 * h + 2] = (double)v[h].z; ua[4 * h + 3] = (double)v[h].w;
+    }
+}
+
+// D = A B over 64 dims: A the rows' operand (widen_row_mfma), B the columns'
+// rows in load_row_mfma layout (transposed here, widened per use).
+LSA_DEV d4_t mfma_dot64(const double (&ua)[16], const f4_t (&rows)[4]) {
+    d4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        f4_t t = rows[h];
+        transpose_rows4(t);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h], (double)t.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 1], (double)t.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 2], (double)t.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 3], (double)t.w, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 }  // namespace lsa

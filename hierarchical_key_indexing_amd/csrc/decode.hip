@@ -31,6 +31,7 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma_attn.h"
+#include "lsa.h"
 
 namespace lsa {
 
@@ -504,7 +505,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = tid + 256 * u;
-                if (e < P * 64) { lk[e] = (tk[u] == kEmpty) ? 0ull : tk[u]; lp[e] = max(tp[u] - 1, 0); }
+                // prefixes clamped to [0, k]: exact for published lists (only
+                // offsets below k place keys) and bounded sums whatever the
+                // buffer held, so every offset below stays in [0, k)
+                if (e < P * 64) { lk[e] = (tk[u] == kEmpty) ? 0ull : tk[u]; lp[e] = min(max(tp[u] - 1, 0), A.k); }
             }
         }
         __syncthreads();
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 e = lp[p * 64 + lane] - (lane > 0 ? lp[p * 64 + lane - 1] : 0);
                 wex = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
                 take = max(0, min(e, count - wex));
-                const int c = (int)(key_id(x) - (uint32_t)(v * b));
+                const int c = min(max((int)(key_id(x) - (uint32_t)(v * b)), 0), b - 1);
                 a0 = clo[c] + skip_s[c];
             }
             const int incl = wave_incl_scan_add(take);
@@ -859,6 +863,17 @@ bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, in
 
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k) {
     return (int64_t)carve_decode_ws(nullptr, m * h_kv, beam, L, h_q / h_kv, d, k).bytes;
+}
+
+// An upper bound on the bytes from the start of a workspace that this path
+// polls (everything before the partial softmax states), over every batch it
+// accepts: groups * beam <= compute units, beam <= kMaxP, L <= LSA_MAX_LEVELS,
+// k <= 8192.
+int64_t decode_polled_bytes_bound() {
+    const int64_t c = std::max(device_cus(), 1);
+    const int64_t ctrl = sizeof(int32_t) * 4 * c, lists = sizeof(uint64_t) * (LSA_MAX_LEVELS - 2) * c * kMaxP;
+    const int64_t leaf = (sizeof(uint64_t) + sizeof(int32_t)) * c * 64, keys = sizeof(int32_t) * c * 8192;
+    return ctrl + lists + leaf + keys + 5 * 256;
 }
 
 template <typename T, bool ATT, int RC, int DC, int PC>

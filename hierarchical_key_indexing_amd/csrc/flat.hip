@@ -274,6 +274,93 @@ __global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
     }
 }
 
+// r = 64 and at least kFlatMfmaRows rows: the same outputs from the fp64
+// matrix cores.  Wave w takes rows 16 w .. 16 w + 15 of the tile (the
+// product's rows: u widened once) against the workgroup's leaves, 16 at a
+// time (the columns: lane (k, c) leaf c); the next 16 leaves' rows and member
+// ranges are loaded while a block is multiplied.  Lane (k, c) then owns rows
+// k + 4 e against leaf c.
+constexpr int kFlatMfmaRows = 16;
+
+__global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
+    __shared__ int32_t rlo_s[kFlatRows], rhi_s[kFlatRows];
+    const int64_t v0 = (int64_t)blockIdx.x * kFlatLeaves;
+    const int64_t i0 = (int64_t)blockIdx.y * kFlatRows;
+    const int g = blockIdx.z;
+    const int nr = (int)min<int64_t>(kFlatRows, A.mb - i0);
+    if ((int)threadIdx.x < nr) {
+        const AttnSet as = attn_set(A.q_pos[i0 + threadIdx.x], A.n, A.n_sink, A.window);
+        rlo_s[threadIdx.x] = as.rlo;
+        rhi_s[threadIdx.x] = as.rhi;
+    }
+    __syncthreads();
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int col = lane & 15, kk = lane >> 4;
+    const int rb = 16 * wv;                                  // the wave's first row in the tile
+    if (rb >= nr) return;                                    // wave-local from here: no block barrier
+    const float *Cg = A.C + (size_t)g * A.nleaf * 64;
+    const int32_t *cn = A.cnt + (size_t)g * A.nleaf;
+    const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
+    const int32_t *pm = A.perm + (size_t)g * A.n;
+    const size_t rs = (size_t)A.h_kv * A.nleaf;              // stride between rows
+    const size_t ss = (size_t)A.h_kv * kSampleMax;           // sample stride between rows
+    double ua[16];
+    {
+        f4_t t[4];
+        load_row_mfma(A.U + ((size_t)(i0 + min(rb + col, nr - 1)) * A.h_kv + g) * 64, kk, t);
+        widen_row_mfma(t, ua);
+    }
+    int rlo[4], rhi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int rr = min(rb + kk + 4 * e, nr - 1);
+        rlo[e] = rlo_s[rr];
+        rhi[e] = rhi_s[rr];
+    }
+    const int64_t vend = min<int64_t>(v0 + kFlatLeaves, A.nleaf);
+    // block 0's leaves (clamped ids: in bounds; leaves past the end are not written)
+    f4_t cur[4];
+    int64_t vc = min<int64_t>(v0 + col, A.nleaf - 1);
+    load_row_mfma(Cg + (size_t)vc * 64, kk, cur);
+    int c_cur = cn[vc], a0_cur = lo[vc], a1_cur = lo[vc + 1];
+#pragma unroll 1
+    for (int64_t vb = v0; vb < vend; vb += 16) {
+        const bool more = vb + 16 < vend;
+        f4_t nxt[4];
+        int c_nxt = 0, a0_nxt = 0, a1_nxt = 0;
+        if (more) {
+            const int64_t vn = min<int64_t>(vb + 16 + col, A.nleaf - 1);
+            load_row_mfma(Cg + (size_t)vn * 64, kk, nxt);
+            c_nxt = cn[vn]; a0_nxt = lo[vn]; a1_nxt = lo[vn + 1];
+        }
+        const int64_t v = vb + col;
+        const int c = c_cur, a0 = a0_cur, a1 = a1_cur;
+        const int32_t first = c > 0 ? pm[a0] : 0, last = c > 0 ? pm[a1 - 1] : 0;
+        const d4_t acc = mfma_dot64(ua, cur);
+        if (v < vend) {
+            const bool sampled = A.S > 0 && v % A.S == 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = rb + kk + 4 * e;
+                if (rr >= nr) continue;
+                const int eq = c > 0 ? members_in(pm + a0, a1 - a0, first, last, rlo[e], rhi[e]) : 0;
+                const uint32_t oq = eq > 0 ? orderable((float)acc[e]) : 0u;
+                const size_t o = ((size_t)(i0 + rr) * A.h_kv + g) * A.nleaf + v;
+                A.sc[o] = oq;
+                A.wt[o] = (uint16_t)min(eq, A.k);
+                if (sampled)
+                    A.smp[((size_t)(i0 + rr) * A.h_kv + g) * kSampleMax + v / A.S] =
+                        eq > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) cur[h] = nxt[h];
+            c_cur = c_nxt; a0_cur = a0_nxt; a1_cur = a1_nxt;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- threshold
 __global__ __launch_bounds__(256) void k_flat_threshold(FlatArgs A) {
     __shared__ __attribute__((aligned(16))) uint64_t sk[256 * 4];
@@ -769,7 +856,8 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
         else hipLaunchKernelGGL(k_flat_latent<bf16_t>, dim3((unsigned)nb, (unsigned)h_kv), dim3(256), 0, st, A);
         const dim3 sgrid((unsigned)((nleaf + kFlatLeaves - 1) / kFlatLeaves), (unsigned)((nb + kFlatRows - 1) / kFlatRows),
                          (unsigned)h_kv);
-        if (r == 64) hipLaunchKernelGGL(k_flat_score<64>, sgrid, dim3(256), 0, st, A);
+        if (r == 64 && nb >= kFlatMfmaRows) hipLaunchKernelGGL(k_flat_score_mfma, sgrid, dim3(256), 0, st, A);
+        else if (r == 64) hipLaunchKernelGGL(k_flat_score<64>, sgrid, dim3(256), 0, st, A);
         else hipLaunchKernelGGL(k_flat_score<0>, sgrid, dim3(256), 0, st, A);
         hipLaunchKernelGGL(k_flat_threshold, dim3(groups), dim3(256), 0, st, A);
         hipLaunchKernelGGL(k_flat_collect, dim3((unsigned)((nleaf + kCollect - 1) / kCollect), groups), dim3(256), 0, st, A);

@@ -44,6 +44,8 @@ hipError_t pca_projection(const void *K, int dtype, int64_t n, int h, int d, int
 
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k);
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k);
+int64_t decode_polled_bytes_bound();
+hipError_t ws_clear_polled(void *ws, int64_t ws_bytes, hipStream_t st);
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,
                   const int32_t *q_pos, const char *index, int64_t n, int r, int b, int L, const int64_t *nodes,
                   const int64_t *centroid_off, const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off,

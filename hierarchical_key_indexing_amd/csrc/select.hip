@@ -611,35 +611,6 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
 // searched in memory).
 constexpr int kNmMemReg = 8;
 
-// fp64 MFMA: v_mfma_f64_16x16x4_f64 accumulates D[i][j] += A[i][k] * B[k][j]
-// over k = 0..3 in order, each step rounded as a separate fma would be, so a
-// chain over dims 4 * blk + k (blk ascending) gives the sequential double sum
-// of the exact float products bit for bit.  Lane l supplies A[l % 16][l / 16]
-// and B[l / 16][l % 16]; element e of lane l is D[l / 16 + 4 e][l % 16].
-typedef double d4_t __attribute__((ext_vector_type(4)));
-
-// 4 x 4 transpose across the four 16-lane rows of a wave: on return lane
-// (row r, column c) holds in x[t] what lane (row t, column c) held in x[r].
-LSA_DEV void transpose_rows4(f4_t &v) {
-    int x0 = __float_as_int(v.x), x1 = __float_as_int(v.y), x2 = __float_as_int(v.z), x3 = __float_as_int(v.w);
-    const auto p = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
-    const auto q = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
-    x0 = p[0]; x2 = p[1]; x1 = q[0]; x3 = q[1];
-    const auto r = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
-    const auto t = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
-    v.x = __int_as_float(r[0]); v.y = __int_as_float(r[1]); v.z = __int_as_float(t[0]); v.w = __int_as_float(t[1]);
-}
-
-// A 64-float row spread over the 16-lane column c: lane (row k, column c)
-// loads the quads q0 + k (q0 = 0, 4, 8, 12: four 16-byte loads, the four
-// lanes of a column reading 64 contiguous bytes), and after the transposes
-// element t of load q0 / 4 is dim 4 (q0 + t) + k, the MFMA operand for block
-// q0 + t.
-LSA_DEV void load_row_mfma(const float *row, int k, f4_t (&v)[4]) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const f4_t *>(row + 16 * h + 4 * k);
-}
-
 // The wave's 16 pairs are the 16 rows of the product (lane (k, c): u of pair
 // c at dims 4 blk + k, widened once), a node's children are its columns, 16
 // at a time (lane (k, c): child 16 cb + c).  Runs of pairs that share a
@@ -692,12 +663,7 @@ __global__ __launch_bounds__(256) void k_nm_score_mfma(NmArgs N) {
     {
         f4_t t[4];
         load_row_mfma(N.U + (size_t)(pe_s[wv][min(col, np - 1)] / kFastP) * R, kk, t);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            transpose_rows4(t[h]);
-            ua[4 * h] = (double)t[h].x; ua[4 * h + 1] = (double)t[h].y;
-            ua[4 * h + 2] = (double)t[h].z; ua[4 * h + 3] = (double)t[h].w;
-        }
+        widen_row_mfma(t, ua);
     }
     while (true) {
         const int e_end = starts ? __builtin_ctzll(starts) : np;
@@ -736,19 +702,8 @@ __global__ __launch_bounds__(256) void k_nm_score_mfma(NmArgs N) {
                 load_row_mfma(Cl + (gc0 + min(c + 16, b - 1)) * R, kk, nxt);
                 cnt_nxt = c + 16 < b ? cn[gc0 + c + 16] : 0;
             }
-            d4_t acc = {0.0, 0.0, 0.0, 0.0};
             const int c_cnt = cb < nvb ? cnt_cur : 0;
-            if (cb < nvb) {
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    f4_t t = cur[h];
-                    transpose_rows4(t);
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h], (double)t.x, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 1], (double)t.y, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 2], (double)t.z, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[4 * h + 3], (double)t.w, acc, 0, 0, 0);
-                }
-            }
+            const d4_t acc = cb < nvb ? mfma_dot64(ua, cur) : d4_t{0.0, 0.0, 0.0, 0.0};
             int c_a0 = 0, c_len = 0, c_last = 0;
             int32_t mem[kNmMemReg];
             if (leaf) {
@@ -907,6 +862,11 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     }
 }
 
+__global__ __launch_bounds__(256) void k_ws_zero16(int4 *p, int64_t count) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x)
+        p[e] = int4{0, 0, 0, 0};
+}
+
 static inline size_t nm_a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct NmWs { float *U; int32_t *kept, *keep; uint64_t *keys; int32_t *eli, *lof, *ncnt, *noff, *fptr, *pairs, *pnode; size_t bytes; };
@@ -980,7 +940,18 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+    return ws_clear_polled(ws, ws_bytes, st);
+}
+
+// A workspace may serve a later small batch, whose workgroups poll words at
+// its start that must read zero: clear that part again after a path that
+// wrote there (a fill kernel, so the call stays capturable in a graph).
+hipError_t ws_clear_polled(void *ws, int64_t ws_bytes, hipStream_t st) {
+    const int64_t z = std::min<int64_t>(ws_bytes, decode_polled_bytes_bound()) / 16;
+    if (!ws || z < 1) return hipSuccess;
+    hipLaunchKernelGGL(k_ws_zero16, dim3((unsigned)std::min<int64_t>((z + 255) / 256, 4096)), dim3(256), 0, st,
+                       (int4 *)ws, z);
+    return hipGetLastError();
 }
 
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,

@@ -221,15 +221,16 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * to the number of compute units, L >= 2, beam <= 32) run on beam
  * workgroups per (row, KV head) that exchange their partial rankings through
  * ws (words published into zeroed memory and polled by the readers).  The
- * caller zero-fills ws once before its first use; every call leaves all of the
- * bytes it used at zero again, so the same ws serves any number of calls, of
- * any sizes that fit it.  Calls that share one ws must not run concurrently
- * (they would read each other's words).  Larger batches of the shapes named
- * at lsa_select_workspace_bytes score levels 2..L node by node: the (row,
- * kept node) pairs are grouped by node in ws, and each kept node's children
- * are read once per group of rows that kept it instead of once per row; rows
- * run in batches that fit ws (no zero-filling needed).  Every path gives
- * identical results.
+ * caller zero-fills ws once before its first use.  Every call of lsa_select,
+ * lsa_select_attend, lsa_select_flat and lsa_attend leaves the bytes at the
+ * start of its ws that such workgroups poll zeroed again, so one ws serves
+ * any number of calls of these functions, of any sizes that fit it.  Calls
+ * that share one ws must not run concurrently (they would read each other's
+ * words).  Larger batches of the shapes named at lsa_select_workspace_bytes
+ * score levels 2..L node by node: the (row, kept node) pairs are grouped by
+ * node in ws, and each kept node's children are read once per group of rows
+ * that kept it instead of once per row; rows run in batches that fit ws.
+ * Every path gives identical results.
  */
 int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos,
                const lsa_index_desc *desc, const void *index, const float *W, int beam, int k,
@@ -336,9 +337,10 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
  * partial softmax states), else as the two calls in sequence.  Arguments as
  * in lsa_select and lsa_attend; K and V are the cache the index was built
  * from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes bytes) must be
- * zero-filled before its first use; every call leaves it zeroed again, so it
- * serves any number of calls of any sizes that fit it; calls sharing one ws
- * must not run concurrently.  In the one-launch form the workgroups of a
+ * zero-filled before its first use; every call leaves the part that the
+ * one-launch form polls zeroed again (see lsa_select), so it serves any
+ * number of calls of any sizes that fit it; calls sharing one ws must not run
+ * concurrently.  In the one-launch form the workgroups of a
  * (row, KV head) pair split the attention evenly over the attention set
  * (retrieved keys, then sinks and window).
  * Outputs equal those of the two separate calls

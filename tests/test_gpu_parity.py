@@ -56,7 +56,16 @@ SMALL = [
     # leaves: the decode kernel takes level 2 from rows loaded before level 1
     ("pre_level2_b16", dict(n=30000, h_q=16, h_kv=2, d=128, dtype="bf16", r=64, b=16, L=3, beam=4, k=700,
                             centres=500, m=3, mode="decode")),
+    # r = 64 with 16 or more rows: flat scoring on the matrix cores, a ragged
+    # last wave (37 = 2 x 16 + 5 rows), every leaf in the list (4096 leaves)
+    ("flat_mfma_rows", dict(n=20000, h_q=8, h_kv=2, d=128, dtype="bf16", r=64, b=64, L=2, beam=8, k=1000,
+                            centres=800, m=37, mode="chunk")),
 ]
+
+# flat search only (b^L above the top-down search's limits): r = 64 with 21
+# rows over 262144 mostly empty leaves, the sampled threshold path
+FLAT_ONLY = {"flat_mfma_sampled": dict(n=20000, h_q=8, h_kv=2, d=128, dtype="bf16", r=64, b=64, L=3, beam=4,
+                                       k=600, centres=800, m=21, mode="chunk")}
 
 
 def _inputs(w, dev, m=None):
@@ -105,7 +114,16 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
             assert_same_bits(sel.cpu().numpy(), ref["sel"], f"sel ({label})")
             assert_same_bits(cut.cpu().numpy(), ref["cutoff"], f"cutoff ({label})")
             if ws is not None:
-                _assert_exchange_zeroed(ws, w.m * w.h_kv, beam, w.h_q // w.h_kv, w.d)
+                cus = torch.cuda.get_device_properties(0).multi_processor_count
+                if w.m * w.h_kv * beam <= cus:          # the multi-workgroup kernel ran
+                    _assert_exchange_zeroed(ws, w.m * w.h_kv, beam, w.h_q // w.h_kv, w.d)
+                # whichever path ran, a one-row call on the same workspace follows
+                say("select", name, "one row after", label, beam, k)
+                s1, c1, u1 = lsa.select(data["Q"][:1], data["pos"][:1], index, desc, data["W"], beam, k, ws=ws)
+                torch.cuda.synchronize()
+                assert_same_bits(c1.cpu().numpy(), ref["count"][:1], "sel_count (one row after)")
+                assert_same_bits(s1.cpu().numpy(), ref["sel"][:1], "sel (one row after)")
+                assert_same_bits(u1.cpu().numpy(), ref["cutoff"][:1], "cutoff (one row after)")
         # every selected key precedes (or is) its query
         s = sel.cpu().numpy()
         assert np.all((s == -1) | (s <= pos[:, None, None]))
@@ -125,8 +143,18 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
             assert_same_bits(sel2.cpu().numpy(), ref["sel"], "sel (fused)")
             assert_same_bits(cut2.cpu().numpy(), ref["cutoff"], "cutoff (fused)")
             _check_attention(out2, lse2, o_ref, lse_ref, tol)
-        if lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k) > 0:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        if lsa.select_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k) > 0 and w.m * w.h_kv * beam <= cus:
             _assert_exchange_zeroed(fws, w.m * w.h_kv, beam, w.h_q // w.h_kv, w.d)
+        # a one-row call on the same workspace follows whichever path ran
+        say("select_attend", name, "one row after", beam, k)
+        sel3, cnt3, cut3, out3, lse3 = lsa.select_attend(data["Q"][:1], data["K"], data["V"], data["pos"][:1], index,
+                                                         desc, data["W"], beam, k, ws=fws)
+        torch.cuda.synchronize()
+        assert_same_bits(cnt3.cpu().numpy(), ref["count"][:1], "sel_count (fused, one row after)")
+        assert_same_bits(sel3.cpu().numpy(), ref["sel"][:1], "sel (fused, one row after)")
+        assert_same_bits(cut3.cpu().numpy(), ref["cutoff"][:1], "cutoff (fused, one row after)")
+        _check_attention(out3, lse3, o_ref[:1], lse_ref[:1], tol)
 
 
 def _assert_exchange_zeroed(ws, groups, beam, G, d):
@@ -226,7 +254,8 @@ def test_sinks_and_window_match_oracle(lsa, name, over):
             _assert_exchange_zeroed(fws, w.m * w.h_kv, w.beam, w.h_q // w.h_kv, w.d)
 
 
-FLAT_CASES = ["tiny_4k", "ragged_bf16_b5", "multi_piece_root", "odd_r_deep", "flat_L1", "n_below_b", "single_key"]
+FLAT_CASES = ["tiny_4k", "ragged_bf16_b5", "multi_piece_root", "odd_r_deep", "flat_L1", "n_below_b", "single_key",
+              "flat_mfma_rows", "flat_mfma_sampled"]
 
 
 @pytest.mark.parametrize("name", FLAT_CASES)
@@ -235,8 +264,8 @@ def test_flat_search_matches_oracle(lsa, name):
     with and without sinks and a window, in one batch and in batches forced by
     a one-row workspace; attention over them matches the oracle's."""
     dev = torch.device("cuda:0")
-    w = _wl("tiny_4k", **dict(SMALL)[name]) if name != "tiny_4k" else _wl("tiny_4k")
-    w = w.replace(name=name)
+    over = FLAT_ONLY[name] if name in FLAT_ONLY else dict(SMALL)[name] if name != "tiny_4k" else {}
+    w = _wl("tiny_4k", **over).replace(name=name)
     data = _inputs(w, dev)
     index, desc = lsa.build_index(data["K"], data["W"], w.b, w.L, w.iters)
     torch.cuda.synchronize()
