@@ -134,7 +134,9 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
         _check_attention(out, lse, o_ref, lse_ref, tol)
 
         say("select_attend", name, beam, k)
-        fws = lsa.workspace(lsa.select_attend_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k), dev)
+        # (sized for this batch and for the one-row call that follows)
+        fws = lsa.workspace(max(lsa.select_attend_workspace_bytes(w.m, w.h_q, w.d, desc, beam, k),
+                                lsa.select_attend_workspace_bytes(1, w.h_q, w.d, desc, beam, k)), dev)
         for rep in range(2):     # the workspace is reusable
             sel2, cnt2, cut2, out2, lse2 = lsa.select_attend(data["Q"], data["K"], data["V"], data["pos"], index,
                                                              desc, data["W"], beam, k, ws=fws)
