@@ -77,6 +77,21 @@ __global__ __launch_bounds__(256) void k_ins_copy(InsArgs A) {
     copy_ints(A.lo_old, (const int32_t *)(A.index + A.leaf_off_off), (int64_t)A.h * (A.nleaf + 1), t0, stride);
 }
 
+// the rows of a node's children (lane c: child c; 16-byte loads when r = 64)
+LSA_DEV void ins_child_row(const float *C, int64_t child, int r, float (&row)[64]) {
+    if (r == 64) {
+        const f4_t *c4 = reinterpret_cast<const f4_t *>(C + (size_t)child * 64);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const f4_t t4 = c4[x];
+            row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < 64; ++x) row[x] = x < r ? C[(size_t)child * r + x] : 0.0f;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
     __shared__ float z_s[4][64];
@@ -85,21 +100,34 @@ __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
     const int64_t j = (int64_t)blockIdx.x * 4 + wv;
     if (j >= A.m) return;                                   // whole waves only
     const int r = A.r, b = A.b, d = A.d;
+    // Every load that does not depend on the key's path is issued first: the
+    // level-1 children (the root's, the same for every key), the key and W.
+    const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * r;
+    const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
+    const int64_t child1 = min<int64_t>(lane, A.nodes[1] - 1);      // clamped: in bounds
+    float row[64];
+    ins_child_row(C1, child1, r, row);
+    const int cnt1 = cn1[child1];
     // the latent, as the build projects keys: lane c sums k_i * W[i][c] in
-    // double over i ascending (each product exact), rounded once
+    // double over i ascending (each product exact), rounded once.  W's first
+    // 128 input rows are loaded before the key (clamped: in bounds).
+    const float *Wg = A.W + (size_t)g * d * r + min(lane, r - 1);
+    float wl[128];
+#pragma unroll
+    for (int u = 0; u < 128; ++u) wl[u] = Wg[(size_t)min(u, d - 1) * r];
     const T *kr = (const T *)A.K + ((size_t)g * A.m + j) * d;
     for (int i = lane; i < d; i += kWave) k_s[wv][i] = to_float(kr[i]);
     wave_sync();
     if (lane < r) {
-        const float *Wg = A.W + (size_t)g * d * r + lane;
         double acc = 0.0;
-        for (int i0 = 0; i0 < d; i0 += 64) {
-            float wv64[64];
+        for (int i0 = 0; i0 < d; i0 += 128) {
+            if (i0 > 0) {
 #pragma unroll
-            for (int u = 0; u < 64; ++u) wv64[u] = Wg[(size_t)min(i0 + u, d - 1) * r];    // clamped
+                for (int u = 0; u < 128; ++u) wl[u] = Wg[(size_t)min(i0 + u, d - 1) * r];
+            }
 #pragma unroll
-            for (int u = 0; u < 64; ++u)
-                if (i0 + u < d) acc = fma((double)k_s[wv][i0 + u], (double)wv64[u], acc);
+            for (int u = 0; u < 128; ++u)
+                if (i0 + u < d) acc = fma((double)k_s[wv][i0 + u], (double)wl[u], acc);
         }
         z_s[wv][lane] = (float)acc;
         A.Z[((size_t)g * A.m + j) * r + lane] = (float)acc;
@@ -110,20 +138,12 @@ __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
         const float *C = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
         const int32_t *cn = (const int32_t *)(A.index + A.count_off[l]) + (size_t)g * A.nodes[l];
         const int64_t child = min<int64_t>(u * b + lane, A.nodes[l] - 1);      // clamped: in bounds
-        const bool ok = lane < b && cn[child] > 0;
-        // the child's row in registers first (16-byte loads when r = 64)
-        float row[64];
-        if (r == 64) {
-            const f4_t *c4 = reinterpret_cast<const f4_t *>(C + (size_t)child * 64);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const f4_t t4 = c4[x];
-                row[4 * x] = t4.x; row[4 * x + 1] = t4.y; row[4 * x + 2] = t4.z; row[4 * x + 3] = t4.w;
-            }
-        } else {
-#pragma unroll
-            for (int x = 0; x < 64; ++x) row[x] = x < r ? C[(size_t)child * r + x] : 0.0f;
+        int cnt = cnt1;
+        if (l > 1) {
+            ins_child_row(C, child, r, row);
+            cnt = cn[child];
         }
+        const bool ok = lane < b && cnt > 0;
         // distances are >= 0, so their bit patterns order like the values
         uint64_t key = ok ? (uint64_t)__double_as_longlong(sq_dist(z_s[wv], row, r)) : ~0ull;
         int best = lane;
