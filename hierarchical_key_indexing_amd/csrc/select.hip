@@ -208,6 +208,31 @@ LSA_DEV uint64_t make_key_slot(float score, uint32_t id, int slot) {
 }
 LSA_DEV uint32_t slot_key_id(uint64_t k) { return ~(uint32_t)(k >> 10) & 0x3FFFFFu; }
 
+// The members of the thread's leaves to sel: leaf ii's first take[ii]
+// members (from pm[a0v[ii]]) go to out[offv[ii] ..].  Rounds of RND members
+// per leaf, every load of a round issued before its stores (clamped
+// indices): a long leaf costs one round trip per RND members, not one per
+// member.
+template <int KPT, int RND>
+LSA_DEV void fill_members(const int32_t *__restrict__ pm, int32_t *__restrict__ out, const int (&take)[KPT],
+                          const int (&a0v)[KPT], const int (&offv)[KPT]) {
+    int mx = 0;
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii) mx = max(mx, take[ii]);
+    for (int t0 = 0; t0 < mx; t0 += RND) {
+        int32_t x[KPT][RND];
+#pragma unroll
+        for (int ii = 0; ii < KPT; ++ii)
+#pragma unroll
+            for (int t = 0; t < RND; ++t) x[ii][t] = pm[take[ii] > 0 ? a0v[ii] + min(t0 + t, take[ii] - 1) : 0];
+#pragma unroll
+        for (int ii = 0; ii < KPT; ++ii)
+#pragma unroll
+            for (int t = 0; t < RND; ++t)
+                if (t0 + t < take[ii]) out[offv[ii] + t0 + t] = x[ii][t];
+    }
+}
+
 // u . row (64 floats) in double, ascending index; the row comes straight from
 // global memory in two halves (each half's 8 loads issued before its FMAs),
 // u from LDS.  Halves keep fewer registers live, so more waves stay resident.
@@ -376,7 +401,7 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
     int off = block_excl_scan(tot, scratch, &total);
     const int count = min(A.k, total);
     int32_t *out = A.sel + ((size_t)i * A.h_kv + g) * A.row;
-    // the thread's (up to) four leaves: the first 8 members of each are loaded
+    // the thread's (up to) four leaves: the first 4 members of each are loaded
     // in one round (clamped indices), longer leaves finish in a loop
     constexpr int kC = 4;
     int take[4], a0v[4], offv[4];
@@ -839,19 +864,7 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
         if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
         off += e4[ii];
     }
-    constexpr int kC = 4;
-    int32_t mv[KPT][kC];
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii)
-#pragma unroll
-        for (int t = 0; t < kC; ++t) mv[ii][t] = take[ii] > 0 ? pm[a0v[ii] + min(t, take[ii] - 1)] : 0;
-#pragma unroll
-    for (int ii = 0; ii < KPT; ++ii) {
-#pragma unroll
-        for (int t = 0; t < kC; ++t)
-            if (t < take[ii]) out[offv[ii] + t] = mv[ii][t];
-        for (int t = kC; t < take[ii]; ++t) out[offv[ii] + t] = pm[a0v[ii] + t];
-    }
+    fill_members<KPT, 8>(pm, out, take, a0v, offv);
     const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
     for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
