@@ -314,9 +314,12 @@ LSA_DEV int wave_incl_scan_add(int v) {
 
 // Weighted radix selection over the 1024 64-bit keys of a 256-thread block
 // (four per thread, zero keys ignored), eight bits per round from the top:
-// returns the key T such that the keys > T weigh less than `want` and the
-// keys >= T weigh at least `want` (0 when all keys together weigh less).
-// `hist` holds 256 ints, `sel` 4.  Every thread gets the result.
+// returns a T such that the keys >= T weigh at least `want` and, without the
+// smallest of them, less than `want` (0 when all keys together weigh less).
+// The rounds stop once the digit that holds the boundary is taken whole; T
+// is then that digit's lower bound rather than the boundary key, and the keys
+// >= T are the same.  `hist` holds 256 ints, `sel` 4.  Every thread gets the
+// result.
 LSA_DEV uint64_t block_radix_select(const uint64_t (&k)[4], const int (&w)[4], int want, int *hist, int *sel) {
     const int tid = threadIdx.x;
     uint64_t prefix = 0, mask = 0;
@@ -337,7 +340,7 @@ LSA_DEV uint64_t block_radix_select(const uint64_t (&k)[4], const int (&w)[4], i
         int before = incl - hv;
         for (int q = 0; q < wvv; ++q) before += sel[q];
         __syncthreads();
-        if (hv > 0 && before < want && before + hv >= want) { sel[0] = 255 - tid; sel[1] = want - before; }
+        if (hv > 0 && before < want && before + hv >= want) { sel[0] = 255 - tid; sel[1] = want - before; sel[2] = hv; }
         if (tid == 255 && before + hv < want) { sel[0] = -1; }        // all keys weigh less than want
         __syncthreads();
         const int dg = sel[0];
@@ -345,7 +348,11 @@ LSA_DEV uint64_t block_radix_select(const uint64_t (&k)[4], const int (&w)[4], i
         want = sel[1];
         prefix |= (uint64_t)dg << shift;
         mask |= (uint64_t)255 << shift;
+        // the whole digit is taken: its lower bound already separates the
+        // same set of keys as the boundary key would
+        const bool whole = sel[2] == want;
         __syncthreads();
+        if (whole) break;
     }
     return prefix;
 }
