@@ -22,10 +22,14 @@ import torch
 from ._build import LIB as _LIB_PATH
 
 LSA_OK, LSA_EINVAL, LSA_EUNSUPPORTED, LSA_ENOSPC, LSA_EHIP = 0, -1, -2, -3, -4
+LSA_EDEVICE, LSA_ESCRATCH = -5, -6
+LSA_STATUS_WAIT_TIMEOUT = 1
 LSA_F32, LSA_BF16 = 0, 1
 MAX_LEVELS = 6
+ABI_VERSION = 2
 
-EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_build_workspace_bytes",
+EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_index_export", "lsa_index_import",
+           "lsa_workspace_status", "lsa_build_workspace_bytes",
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
            "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend", "lsa_select_flat_workspace_bytes",
            "lsa_select_flat", "lsa_pca_workspace_bytes", "lsa_pca_projection",
@@ -64,6 +68,9 @@ def lib():
         L.lsa_strerror.argtypes = [i32]
         L.lsa_strerror.restype = ctypes.c_char_p
         L.lsa_index_layout.argtypes = [i64, i32, i32, i32, i32, D]
+        L.lsa_index_export.argtypes = [D, P, P, i64, P]
+        L.lsa_index_import.argtypes = [D, P, i64, P, i64, P]
+        L.lsa_workspace_status.argtypes = [P, i64, ctypes.POINTER(ctypes.c_int32), P]
         L.lsa_build_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_build_index.argtypes = [P, i32, i64, i32, i32, P, i32, i32, i32, i32, P, i64, P, i64, D, P]
         L.lsa_select_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, i32, i32, ctypes.POINTER(i64)]
@@ -186,6 +193,48 @@ def index_views(index: torch.Tensor, desc: IndexDesc) -> dict:
     return out
 
 
+def index_export(index: torch.Tensor, desc: IndexDesc, stream=None) -> torch.Tensor:
+    """Copy index memory to a host uint8 tensor of desc.bytes bytes (lsa_index_export)."""
+    _need(index, "index")
+    host = torch.empty(desc.bytes, dtype=torch.uint8)
+    _check(lib().lsa_index_export(ctypes.byref(desc), _ptr(index), ctypes.c_void_p(host.data_ptr()), host.numel(),
+                                  _stream(stream)),
+           "lsa_index_export")
+    return host
+
+
+def index_import(host, desc: IndexDesc, device, index: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Load host index memory (uint8, desc's layout; checked on the host first)
+    into a device tensor (lsa_index_import)."""
+    host = torch.as_tensor(host)
+    if host.dtype != torch.uint8 or host.device.type != "cpu" or not host.is_contiguous():
+        raise ValueError("host index memory must be a contiguous uint8 host buffer")
+    if index is None:
+        index = torch.empty(desc.bytes, dtype=torch.uint8, device=device)
+    _need(index, "index")
+    _check(lib().lsa_index_import(ctypes.byref(desc), ctypes.c_void_p(host.data_ptr()), host.numel(), _ptr(index),
+                                  index.numel(), _stream(stream)),
+           "lsa_index_import")
+    return index
+
+
+def workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """Read and clear a workspace's status word (LSA_STATUS_* bits; lsa_workspace_status)."""
+    _need(ws, "ws")
+    v = ctypes.c_int32()
+    _check(lib().lsa_workspace_status(_ptr(ws), ws.numel(), ctypes.byref(v), _stream(stream)), "lsa_workspace_status")
+    return v.value
+
+
+def _need_kv(K: torch.Tensor, V: torch.Tensor, Q: torch.Tensor, h_kv: int, n: Optional[int]):
+    """K and V: the same [h_kv, n, d] shape and Q's dtype."""
+    d = Q.shape[2]
+    want = (h_kv, K.shape[1] if n is None else n, d)
+    for t, nm in ((K, "K"), (V, "V")):
+        if tuple(t.shape) != want or t.dtype != Q.dtype:
+            raise ValueError(f"{nm} must be {Q.dtype} of shape {want}, got {t.dtype} {tuple(t.shape)}")
+
+
 # ------------------------------------------------------------------ entry points
 def build_index(K: torch.Tensor, W: torch.Tensor, b: int, L: int, iters: int = 5,
                 index: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
@@ -288,6 +337,7 @@ def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
         _need(t, nm)
     m, h_q, d = Q.shape
     h = desc.h_kv
+    _need_kv(K, V, Q, h, desc.n)
     dev = Q.device
     if sel is None:
         sel = torch.empty((m, h, k + n_sink + window), dtype=torch.int32, device=dev)
@@ -323,6 +373,7 @@ def attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel: torch.Tensor,
         _need(t, nm)
     m, h_q, d = Q.shape
     h_kv, n, _ = K.shape
+    _need_kv(K, V, Q, h_kv, None)
     k = sel.shape[2]
     if out is None:
         out = torch.empty_like(Q)

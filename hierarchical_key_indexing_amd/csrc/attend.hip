@@ -42,6 +42,12 @@ struct AttendArgs {
 // of it than when the heads of every row are interleaved.
 LSA_DEV int64_t attend_row(const AttendArgs &A, int64_t y) { return (y % A.m) * A.h_kv + y / A.m; }
 
+// A group's count and its selected ids as read from the caller's arrays, kept
+// in range ([0, row length] and [0, n)) so that no gather leaves the cache
+// whatever those arrays hold; in-range inputs pass unchanged.
+LSA_DEV int attend_count(const AttendArgs &A, int64_t row) { return min(max(A.sel_count[row], 0), A.k); }
+LSA_DEV int32_t attend_id(const AttendArgs &A, int32_t id) { return (int32_t)min<int64_t>(max(id, 0), A.n - 1); }
+
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int split = blockIdx.x;
-    const int cnt = A.sel_count[row];
+    const int cnt = attend_count(A, row);
     const int per = (cnt + A.nsplit - 1) / A.nsplit;
     const int s0 = min(cnt, split * per), s1 = min(cnt, s0 + per);
     const T *Q = (const T *)A.Q;
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs A) {
     for (int kb = s0; kb < s1; kb += kTK) {
         const int nk = min(kTK, s1 - kb);
         __syncthreads();
-        if (threadIdx.x < nk) ids[threadIdx.x] = S[kb + threadIdx.x];
+        if (threadIdx.x < nk) ids[threadIdx.x] = attend_id(A, S[kb + threadIdx.x]);
         __syncthreads();
         gather_tile<T>(Kg, Vg, ids, nk, d, Ks, dp, Vs);
         __syncthreads();
@@ -209,7 +215,7 @@ LSA_DEV void attend_group_coop(const AttendArgs &A, int64_t row, int split, uint
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int G = A.h_q / A.h_kv;
-    const int cnt = A.sel_count[row];
+    const int cnt = attend_count(A, row);
     const int per = (cnt + A.nsplit - 1) / A.nsplit;
     const int s0 = min(cnt, split * per), s1 = min(cnt, s0 + per);
     const int w = threadIdx.x / kWave;
@@ -226,7 +232,7 @@ LSA_DEV void attend_group_coop(const AttendArgs &A, int64_t row, int split, uint
     for (int c0 = s0; c0 < s1; c0 += kIdsCap) {
         const int own = min(kIdsCap, s1 - c0);
         const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
-        for (int f = threadIdx.x; f < nsteps * 4 * kMT; f += blockDim.x) ids_s[f] = S[c0 + (f < own ? f : 0)];
+        for (int f = threadIdx.x; f < nsteps * 4 * kMT; f += blockDim.x) ids_s[f] = attend_id(A, S[c0 + (f < own ? f : 0)]);
         __syncthreads();
         attend_steps<D>(Kg, Vg, ids_s, own, w, 4, qf, A.scale_log2, vt[w], st, first);
         __syncthreads();                 // ids_s is rewritten by the next chunk
@@ -251,7 +257,7 @@ LSA_DEV void attend_group_wave(const AttendArgs &A, int64_t row, uint16_t *vt, i
     const int64_t i = row / A.h_kv;
     const int g = (int)(row % A.h_kv);
     const int G = A.h_q / A.h_kv;
-    const int cnt = A.sel_count[row];
+    const int cnt = attend_count(A, row);
     const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * D;
     const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * D;
     const uint16_t *Qb = (const uint16_t *)A.Q + ((size_t)i * A.h_q + (size_t)g * G) * D;
@@ -264,7 +270,7 @@ LSA_DEV void attend_group_wave(const AttendArgs &A, int64_t row, uint16_t *vt, i
     for (int c0 = 0; c0 < cnt; c0 += kIdsW) {
         const int own = min(kIdsW, cnt - c0);
         const int nsteps = (own + kMT - 1) / kMT;
-        for (int f = l; f < nsteps * kMT; f += kWave) ids_w[f] = S[c0 + (f < own ? f : 0)];
+        for (int f = l; f < nsteps * kMT; f += kWave) ids_w[f] = attend_id(A, S[c0 + (f < own ? f : 0)]);
         wave_sync();
         attend_steps<D>(Kg, Vg, ids_w, own, 0, 1, qf, A.scale_log2, vt, st, first);
         wave_sync();
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mfma(AttendArgs A) {
     const int64_t y0 = (int64_t)blockIdx.x * 4;
     const int ny = (int)min<int64_t>(4, A.m * A.h_kv - y0);
     int cmax = 0;
-    for (int q = 0; q < ny; ++q) cmax = max(cmax, A.sel_count[attend_row(A, y0 + q)]);
+    for (int q = 0; q < ny; ++q) cmax = max(cmax, attend_count(A, attend_row(A, y0 + q)));
     if (cmax <= kWaveMax) {
         const int w = threadIdx.x / kWave;
         if (w < ny) attend_group_wave<D>(A, attend_row(A, y0 + w), vt[w], ids_s + w * kIdsW);
@@ -339,10 +345,12 @@ int attend_nsplit(int64_t m, int h_kv, int k) {
     return (int)want;
 }
 
+// Split partial states sit after the workspace's reserved prefix, which this
+// path never writes.
 int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k) {
     const int ns = attend_nsplit(m, h_kv, k);
     if (ns == 1) return 0;
-    return (int64_t)m * h_q * ns * (d + 2) * (int64_t)sizeof(float);
+    return ws_reserved_bytes() + (int64_t)m * h_q * ns * (d + 2) * (int64_t)sizeof(float);
 }
 
 hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int64_t n,
@@ -353,7 +361,8 @@ hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_
     A.sel = sel; A.sel_count = sel_count; A.k = k;
     A.scale_log2 = scale * 1.4426950408889634f;
     A.nsplit = attend_nsplit(m, h_kv, k);
-    A.out = out; A.lse = lse; A.part = (float *)ws;
+    A.out = out; A.lse = lse;
+    A.part = A.nsplit > 1 ? (float *)((char *)ws + ws_reserved_bytes()) : nullptr;
     const int G = h_q / h_kv;
     const size_t shm = sizeof(float) * ((size_t)G * d + (size_t)kTK * (d + 1) + (size_t)kTK * d + (size_t)G * kTK);
     const dim3 grid((unsigned)A.nsplit, (unsigned)(m * h_kv));

@@ -24,14 +24,21 @@
 //
 // Workgroups exchange data through the caller's workspace without barriers:
 // it starts zeroed, a writer publishes nonzero words with device-scope stores,
-// a reader polls each word it needs until it is nonzero (bounded; a flag in
-// the workspace records a timeout), and the last workgroup zeroes everything
-// again.  The grid is at most one workgroup per compute unit, so every
-// workgroup of a group is resident while the others wait on its words.
+// a reader polls each word it needs until it is nonzero (bounded; a flag of
+// the group records a timeout), and the last workgroup zeroes everything
+// again.  It also moves a timeout flag into the status word at the start of
+// the workspace, which the host reads (lsa_workspace_status, or after every
+// call in debug mode).  The grid is at most one workgroup per compute unit,
+// so every workgroup of a group is resident while the others wait on its
+// words.  No other path of the library writes the part of a workspace that
+// these workgroups poll (ws_reserved_bytes), so a stale word can only be one
+// this kernel left, and it leaves none.
 #include "common.h"
 #include "internal.h"
 #include "mfma_attn.h"
 #include "lsa.h"
+
+#include <atomic>
 
 namespace lsa {
 
@@ -64,6 +71,7 @@ struct DecodeArgs {
     void *out;
     float *lse;
     // workspace
+    int32_t *status;      // the workspace's status word (kStatusWaitTimeout bit)
     // Exchange buffers: zero before a launch, published with device-scope
     // stores of nonzero values, polled by the readers, zeroed again at the end.
     int32_t *ctrl;        // [groups][4]: -, arrivals, timeout flag, -
@@ -796,18 +804,33 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
     if (ATTEND)
         for (int e = tid; e < count_s; e += blockDim.x) publish(A.keys + (size_t)gi * A.k + e, 0);
-    if (tid == 0) publish(ctrl + 1, 0);
+    if (tid == 0) {
+        // a bounded wait of this group gave up (its results may be wrong):
+        // report it in the status word, which stays set until the host reads
+        // it, and clear the group's flag so that no later launch reads it as
+        // a published word
+        if (__hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            __hip_atomic_fetch_or(A.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            publish(ctrl + 2, 0);
+        }
+        publish(ctrl + 1, 0);
+    }
 }
 
 // ---------------------------------------------------------------- host side
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct DecodeWs { int32_t *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre, *keys; float *part; size_t bytes; };
+struct DecodeWs {
+    int32_t *status, *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre, *keys; float *part; size_t bytes;
+};
 
+// Workspace layout: the status word (kWsHeader bytes), then the exchange
+// buffers, then the partial softmax states.
 static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G, int d, int k) {
     size_t cur = 0;
     DecodeWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
+    w.status = (int32_t *)take(kWsHeader);
     w.ctrl = (int32_t *)take(sizeof(int32_t) * 4 * (size_t)groups);
     w.lists = (uint64_t *)take(sizeof(uint64_t) * (size_t)(L > 2 ? L - 2 : 1) * groups * P * P);
     w.leaf_keys = (uint64_t *)take(sizeof(uint64_t) * (size_t)groups * P * 64);
@@ -818,16 +841,17 @@ static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G,
     return w;
 }
 
-static int device_cus() {
-    static int cus[64] = {0};
+int device_cus() {
+    // per device, filled on first use (concurrent first uses store the same value)
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cus[dev] == 0) {
-        int c = 0;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cus[dev] = c;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return c;
 }
 
 static bool fast_shape(int dtype, int d, int r) { return dtype == 1 && d == 128 && r == 64; }
@@ -866,26 +890,31 @@ int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int b
 }
 
 // An upper bound on the bytes from the start of a workspace that this path
-// polls (everything before the partial softmax states), over every batch it
-// accepts: groups * beam <= compute units, beam <= kMaxP, L <= LSA_MAX_LEVELS,
-// k <= 8192.
+// polls (the status word and everything before the partial softmax states),
+// over every batch it accepts: groups * beam <= compute units, beam <= kMaxP,
+// L <= LSA_MAX_LEVELS, k <= 8192.
 int64_t decode_polled_bytes_bound() {
     const int64_t c = std::max(device_cus(), 1);
     const int64_t ctrl = sizeof(int32_t) * 4 * c, lists = sizeof(uint64_t) * (LSA_MAX_LEVELS - 2) * c * kMaxP;
     const int64_t leaf = (sizeof(uint64_t) + sizeof(int32_t)) * c * 64, keys = sizeof(int32_t) * c * 8192;
-    return ctrl + lists + leaf + keys + 5 * 256;
+    return kWsHeader + ctrl + lists + leaf + keys + 5 * 256;
 }
+
+// The other paths place their buffers after this many bytes of a workspace,
+// so that they never write a word the decode kernel polls.
+int64_t ws_reserved_bytes() { return (int64_t)a256((size_t)decode_polled_bytes_bound()); }
 
 template <typename T, bool ATT, int RC, int DC, int PC>
 static hipError_t launch_decode(const DecodeArgs &A, dim3 grid, size_t shm, hipStream_t st) {
-    static int attr_set[64] = {0};
+    // the attribute is set once per device (setting it twice is harmless)
+    static std::atomic<int> attr_set[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void *)k_decode<T, ATT, RC, DC, PC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsPerCu - kStaticLds));
         if (e != hipSuccess) return e;
-        attr_set[dev] = 1;
+        attr_set[dev].store(1, std::memory_order_release);
     }
     hipLaunchKernelGGL((k_decode<T, ATT, RC, DC, PC>), grid, dim3(256), shm, st, A);
     return hipGetLastError();
@@ -906,7 +935,7 @@ hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_
     A.scale_log2 = scale * 1.4426950408889634f; A.out = out; A.lse = lse;
     const int G = h_q / h_kv;
     DecodeWs w = carve_decode_ws((char *)ws, m * h_kv, beam, L, G, d, k);
-    A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.keys = w.keys;
+    A.status = w.status; A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.keys = w.keys;
     A.part = w.part;
     const size_t shm = decode_dyn_bytes(dtype, G, d, r);
     const dim3 grid((unsigned)beam, (unsigned)(m * h_kv));

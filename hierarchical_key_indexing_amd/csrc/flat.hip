@@ -32,6 +32,7 @@
 //                    narrows the boundary to a bucket that fits, and those keys
 //                    are sorted and filled.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "internal.h"
@@ -781,8 +782,9 @@ struct FlatWs {
     float *U; double *Ud; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt; uint64_t *lst; size_t bytes;
 };
 
+// (after the workspace's reserved prefix, which this path never writes)
 FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
-    size_t cur = 0;
+    size_t cur = (size_t)ws_reserved_bytes();
     FlatWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
     const size_t groups = (size_t)mb * h_kv;
@@ -818,15 +820,16 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
                        hipStream_t st) {
     const int64_t mb = flat_batch_rows(m, h_kv, r, nleaf, ws_bytes);
     if (mb < 1) return hipErrorInvalidValue;
-    static int attr_set[64] = {0};
+    // the attribute is set once per device (setting it twice is harmless)
+    static std::atomic<int> attr_set[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     const size_t shm = sizeof(uint64_t) * kFlatList + sizeof(int) * 2 * kFlatBins;
-    if (!attr_set[dev]) {
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void *)k_flat_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)shm);
         if (e != hipSuccess) return e;
-        attr_set[dev] = 1;
+        attr_set[dev].store(1, std::memory_order_release);
     }
     const int row = k + n_sink + window;
     const size_t esz = dtype == 0 ? 4 : 2;

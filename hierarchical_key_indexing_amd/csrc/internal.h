@@ -4,7 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lsa.h"
+
 namespace lsa {
+
+// Every workspace starts with a header whose first int32 is the status word
+// (LSA_STATUS_* bits set by kernels, read and cleared by the host).
+constexpr int kWsHeader = 256;
+constexpr int32_t kStatusWaitTimeout = LSA_STATUS_WAIT_TIMEOUT;
+
+int device_cus();
 
 int64_t build_workspace_bytes(int64_t n, int h, int r, int b, int L);
 hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,
@@ -45,7 +54,7 @@ hipError_t pca_projection(const void *K, int dtype, int64_t n, int h, int d, int
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k);
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k);
 int64_t decode_polled_bytes_bound();
-hipError_t ws_clear_polled(void *ws, int64_t ws_bytes, hipStream_t st);
+int64_t ws_reserved_bytes();
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,
                   const int32_t *q_pos, const char *index, int64_t n, int r, int b, int L, const int64_t *nodes,
                   const int64_t *centroid_off, const int64_t *count_off, int64_t leaf_off_off, int64_t perm_off,

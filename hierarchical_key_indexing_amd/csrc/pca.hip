@@ -23,6 +23,7 @@
 //                 one (at most 40), then the r leading eigenvectors are
 //                 ranked, signed and rounded to fp32.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "internal.h"
@@ -325,14 +326,15 @@ hipError_t pca_projection(const void *K, int dtype, int64_t n, int h, int d, int
     hipLaunchKernelGGL(k_pca_reduce, dim3(kPcaD * kPcaD / 256, (unsigned)h), dim3(256), 0, st, A);
     const int m = d + (d & 1);
     const size_t shm = sizeof(double) * (size_t)m * (m + 1);
-    static int attr_set[64] = {0};
+    // the attribute is set once per device (setting it twice is harmless)
+    static std::atomic<int> attr_set[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void *)k_pca_jacobi, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(sizeof(double) * kPcaD * (kPcaD + 1)));
         if (e != hipSuccess) return e;
-        attr_set[dev] = 1;
+        attr_set[dev].store(1, std::memory_order_release);
     }
     hipLaunchKernelGGL(k_pca_jacobi, dim3((unsigned)h), dim3(256), shm, st, A);
     return hipGetLastError();

@@ -875,17 +875,13 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_ws_zero16(int4 *p, int64_t count) {
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x)
-        p[e] = int4{0, 0, 0, 0};
-}
-
 static inline size_t nm_a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct NmWs { float *U; int32_t *kept, *keep; uint64_t *keys; int32_t *eli, *lof, *ncnt, *noff, *fptr, *pairs, *pnode; size_t bytes; };
 
+// (after the workspace's reserved prefix, which this path never writes)
 static NmWs carve_nm_ws(char *base, int64_t groups, int h_kv, int64_t max_nodes) {
-    size_t cur = 0;
+    size_t cur = (size_t)ws_reserved_bytes();
     NmWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = nm_a256(cur + n); return p; };
     w.U = (float *)take(sizeof(float) * groups * kFastR);
@@ -953,18 +949,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return ws_clear_polled(ws, ws_bytes, st);
-}
-
-// A workspace may serve a later small batch, whose workgroups poll words at
-// its start that must read zero: clear that part again after a path that
-// wrote there (a fill kernel, so the call stays capturable in a graph).
-hipError_t ws_clear_polled(void *ws, int64_t ws_bytes, hipStream_t st) {
-    const int64_t z = std::min<int64_t>(ws_bytes, decode_polled_bytes_bound()) / 16;
-    if (!ws || z < 1) return hipSuccess;
-    hipLaunchKernelGGL(k_ws_zero16, dim3((unsigned)std::min<int64_t>((z + 255) / 256, 4096)), dim3(256), 0, st,
-                       (int4 *)ws, z);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,

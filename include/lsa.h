@@ -29,6 +29,21 @@
  *     IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
  *   - Positions are int32: n <= 2^31 - 1 keys.
  *   - Results are deterministic: the same inputs give the same bytes.
+ *   - Failures on the device.  The only kernels that wait on other
+ *     workgroups (the multi-workgroup select of lsa_select and
+ *     lsa_select_attend) bound every wait; a wait that gives up sets
+ *     LSA_STATUS_WAIT_TIMEOUT in the status word of the call's workspace
+ *     (its results may then be wrong), which lsa_workspace_status reads.
+ *   - Debug mode: with the environment variable LSA_DEBUG set to a value
+ *     other than "0" when the library is first used, every entry point also
+ *     checks on the host, before enqueueing, the index it reads (as
+ *     lsa_index_import does) and the sel / sel_count it reads (entries in
+ *     range); and after enqueueing it waits for the stream, returns LSA_EHIP
+ *     for a failed kernel, LSA_EDEVICE when a multi-workgroup select set the
+ *     workspace's status word (it is cleared) or when a select call wrote an
+ *     entry out of range.
+ *     Debug mode synchronises and copies to the host: it is for finding
+ *     faults, not for timing, and not for use under stream capture.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -45,6 +60,11 @@ extern "C" {
 #define LSA_EUNSUPPORTED (-2) /* valid, but outside what the kernels implement      */
 #define LSA_ENOSPC (-3)       /* a caller-provided buffer is too small              */
 #define LSA_EHIP (-4)         /* the HIP runtime reported an error on launch        */
+#define LSA_EDEVICE (-5)      /* a kernel reported a failure (debug mode, lsa_workspace_status) */
+#define LSA_ESCRATCH (-6)     /* the call needs more than the fixed scratch of lsa_select_attend_noalloc */
+
+/* Bits of a workspace's status word (lsa_workspace_status). */
+#define LSA_STATUS_WAIT_TIMEOUT 1 /* a bounded wait between workgroups gave up */
 
 /* Element types of Q, K, V and the attention output. */
 #define LSA_F32 0
@@ -79,7 +99,7 @@ typedef struct lsa_index_desc {
 } lsa_index_desc;
 
 /* Version of this ABI (the value of LSA_ABI_VERSION). */
-#define LSA_ABI_VERSION 1
+#define LSA_ABI_VERSION 2
 int lsa_abi_version(void);
 
 /* Message for a return code (static storage, never NULL). */
@@ -93,6 +113,54 @@ const char *lsa_strerror(int code);
  * boundaries.
  */
 int lsa_index_layout(int64_t n, int h_kv, int r, int b, int L, lsa_index_desc *desc);
+
+/*
+ * Copy an index to host memory (kongchang.com, "How LSA Sidesteps Per-Key
+ * Scoring with Hierarchical Clustering": the tree over the keys is
+ * precomputed, so it can be stored and loaded like the KV cache).
+ *
+ *   desc      the index's descriptor (as lsa_index_layout returns it)
+ *   index     device, desc->bytes bytes
+ *   host_dst  host, dst_bytes >= desc->bytes: receives the index memory byte
+ *             for byte, in the layout *desc describes (bytes between arrays
+ *             are unspecified)
+ * Synchronous: the copy is enqueued on `stream` after its earlier work and
+ * the call returns once it is complete.  Errors: LSA_EINVAL (descriptor,
+ * NULL pointer), LSA_ENOSPC (dst_bytes too small), LSA_EHIP (copy failed).
+ */
+int lsa_index_export(const lsa_index_desc *desc, const void *index, void *host_dst, int64_t dst_bytes,
+                     void *stream);
+
+/*
+ * Load an index from host memory into index memory (the inverse of
+ * lsa_index_export).  host_src holds src_bytes >= desc->bytes bytes in the
+ * layout *desc describes: written by lsa_index_export, or assembled by any
+ * other implementation of the same tree (same arrays, same meaning).  Before
+ * anything is copied the contents are checked on the host, and an index that
+ * fails a check returns LSA_EINVAL with `index` untouched.  Per KV head:
+ *   - leaf offsets start at 0, never decrease and end at n;
+ *   - a leaf's count equals its offset difference, an internal node's count
+ *     the sum of its children's counts;
+ *   - the members are a permutation of 0..n-1, strictly ascending inside
+ *     each leaf;
+ *   - the centroid of every non-empty node is finite.
+ * These are what the select kernels rely on to stay inside their buffers.
+ *   index     device, index_bytes >= desc->bytes
+ * Synchronous, like lsa_index_export.  Errors: LSA_EINVAL, LSA_ENOSPC,
+ * LSA_EHIP.
+ */
+int lsa_index_import(const lsa_index_desc *desc, const void *host_src, int64_t src_bytes, void *index,
+                     int64_t index_bytes, void *stream);
+
+/*
+ * Read and clear the status word of a zero-filled workspace used by
+ * lsa_select or lsa_select_attend (*status: the LSA_STATUS_* bits that every
+ * call since the last read set, 0 when all went well; only their
+ * multi-workgroup form sets any).  Synchronous: waits for `stream` first, so
+ * it sees every call enqueued on that stream before it.  Errors: LSA_EINVAL
+ * (NULL ws or status, ws_bytes < 256), LSA_EHIP.
+ */
+int lsa_workspace_status(void *ws, int64_t ws_bytes, int32_t *status, void *stream);
 
 /*
  * Bytes of device workspace lsa_build_index needs for these sizes (*bytes).
@@ -221,12 +289,13 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * to the number of compute units, L >= 2, beam <= 32) run on beam
  * workgroups per (row, KV head) that exchange their partial rankings through
  * ws (words published into zeroed memory and polled by the readers).  The
- * caller zero-fills ws once before its first use.  Every call of lsa_select,
- * lsa_select_attend, lsa_select_flat and lsa_attend leaves the bytes at the
- * start of its ws that such workgroups poll zeroed again, so one ws serves
- * any number of calls of these functions, of any sizes that fit it.  Calls
- * that share one ws must not run concurrently (they would read each other's
- * words).  Larger batches of the shapes named at lsa_select_workspace_bytes
+ * caller zero-fills ws once before its first use.  Those workgroups poll only
+ * a prefix of ws that no other path of lsa_select, lsa_select_attend,
+ * lsa_select_flat or lsa_attend writes (their buffers start after it), and
+ * they leave it zeroed, so one ws serves any number of calls of these
+ * functions, of any sizes that fit it.  The first int32 of ws is its status
+ * word (lsa_workspace_status).  Calls that share one ws must not run
+ * concurrently (they would read each other's words).  Larger batches of the shapes named at lsa_select_workspace_bytes
  * score levels 2..L node by node: the (row, kept node) pairs are grouped by
  * node in ws, and each kept node's children are read once per group of rows
  * that kept it instead of once per row; rows run in batches that fit ws.
@@ -337,8 +406,8 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
  * partial softmax states), else as the two calls in sequence.  Arguments as
  * in lsa_select and lsa_attend; K and V are the cache the index was built
  * from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes bytes) must be
- * zero-filled before its first use; every call leaves the part that the
- * one-launch form polls zeroed again (see lsa_select), so it serves any
+ * zero-filled before its first use; the one-launch form leaves the part it
+ * polls zeroed and no other path writes it (see lsa_select), so ws serves any
  * number of calls of any sizes that fit it; calls sharing one ws must not run
  * concurrently.  In the one-launch form the workgroups of a
  * (row, KV head) pair split the attention evenly over the attention set

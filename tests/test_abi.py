@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for nm in names:
         assert hasattr(L, nm), nm
     assert sorted(names) == sorted(lsa.EXPORTS)
-    assert L.lsa_abi_version() == 1
+    assert L.lsa_abi_version() == lsa.ABI_VERSION == 2
     assert L.lsa_strerror(-3).decode() == "buffer too small"
 
 
@@ -138,3 +138,97 @@ def test_entry_points_validate_before_touching_the_device():
     assert L.lsa_attend(fake, fake, fake, 1, 1, 32, 4, 100, 128, fake, fake, 2048, f(0), fake, None, None, 0,
                         None) == lsa.LSA_ENOSPC
     assert lsa.build_workspace_bytes(1 << 20, 4, 128, 64, 64, 3) > 4 * (1 << 20) * 64 * 4
+
+
+def _small_oracle_tree():
+    import numpy as np
+    import oracle
+    import synth
+    w = synth.WORKLOADS["tiny_4k"].replace(n=600, b=4, L=3, r=8, d=16, centres=20)
+    data = synth.make_workload(w, device="cpu")
+    K = data["K"].float().numpy()
+    oix = oracle.build_index(K, data["W"].numpy(), w.b, w.L, w.iters)
+    desc = lsa.index_layout(w.n, w.h_kv, w.r, w.b, w.L)
+    return oix, desc
+
+
+def _corruptions(desc, oix):
+    """(name, function that damages a copy of host index memory)."""
+    import numpy as np
+    from _index_bytes import view
+    L = desc.L
+    cL = oix.cnt(L)[0]
+    big = int(np.argmax(cL))                       # a leaf with >= 2 members
+    assert cL[big] >= 2
+    nonempty = int(np.nonzero(oix.cnt(1)[0])[0][0])
+
+    def first_off(buf):
+        view(buf, desc, "leaf_off")[0, 0] = 1
+
+    def last_off(buf):
+        view(buf, desc, "leaf_off")[0, -1] -= 1
+
+    def leaf_count(buf):
+        view(buf, desc, "cnt", L)[0, big] += 1
+
+    def inner_count(buf):
+        view(buf, desc, "cnt", 1)[0, nonempty] += 1
+
+    def duplicate_member(buf):
+        p = view(buf, desc, "perm")
+        s = int(view(buf, desc, "leaf_off")[0, big])
+        p[0, s + 1] = p[0, s]
+
+    def unsorted_leaf(buf):
+        p = view(buf, desc, "perm")
+        s = int(view(buf, desc, "leaf_off")[0, big])
+        p[0, s], p[0, s + 1] = p[0, s + 1], p[0, s]
+
+    def member_out_of_range(buf):
+        p = view(buf, desc, "perm")
+        s = int(view(buf, desc, "leaf_off")[0, big])
+        p[0, s] = desc.n
+
+    def negative_member(buf):
+        view(buf, desc, "perm")[0, 0] = -1
+
+    def nan_centroid(buf):
+        view(buf, desc, "C", 1)[0, nonempty, 3] = np.nan
+
+    def decreasing_offsets(buf):
+        lo = view(buf, desc, "leaf_off")
+        lo[0, big + 1] = lo[0, big] - 1
+
+    return [first_off, last_off, leaf_count, inner_count, duplicate_member, unsorted_leaf,
+            member_out_of_range, negative_member, nan_centroid, decreasing_offsets]
+
+
+def test_index_import_rejects_an_inconsistent_tree_before_any_copy():
+    """lsa_index_import checks the tree on the host and returns EINVAL without
+    touching the device (the destination pointer below is never dereferenced)."""
+    oix, desc = _small_oracle_tree()
+    from _index_bytes import oracle_index_bytes
+    L = lsa.lib()
+    fake = ctypes.c_void_p(0x1000)
+    good = oracle_index_bytes(oix, desc)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    assert L.lsa_index_import(ctypes.byref(desc), ptr(good), good.size - 1, fake, desc.bytes,
+                              None) == lsa.LSA_ENOSPC
+    assert L.lsa_index_import(ctypes.byref(desc), ptr(good), good.size, fake, desc.bytes - 1,
+                              None) == lsa.LSA_ENOSPC
+    assert L.lsa_index_import(ctypes.byref(desc), None, good.size, fake, desc.bytes, None) == lsa.LSA_EINVAL
+    assert L.lsa_index_export(ctypes.byref(desc), fake, ptr(good), good.size - 1, None) == lsa.LSA_ENOSPC
+    for damage in _corruptions(desc, oix):
+        buf = good.copy()
+        damage(buf)
+        assert L.lsa_index_import(ctypes.byref(desc), ptr(buf), buf.size, fake, desc.bytes,
+                                  None) == lsa.LSA_EINVAL, damage.__name__
+
+
+def test_workspace_status_rejects_bad_arguments():
+    L = lsa.lib()
+    v = ctypes.c_int32()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.lsa_workspace_status(fake, 255, ctypes.byref(v), None) == lsa.LSA_EINVAL
+    assert L.lsa_workspace_status(fake, 4096, None, None) == lsa.LSA_EINVAL
+    assert L.lsa_strerror(lsa.LSA_EDEVICE).decode().startswith("a kernel reported")
