@@ -33,7 +33,7 @@ EXPORTS = ["lsa_abi_version", "lsa_strerror", "lsa_index_layout", "lsa_index_exp
            "lsa_build_index", "lsa_select_workspace_bytes", "lsa_select", "lsa_attend_workspace_bytes",
            "lsa_attend", "lsa_select_attend_workspace_bytes", "lsa_select_attend", "lsa_select_flat_workspace_bytes",
            "lsa_select_flat", "lsa_pca_workspace_bytes", "lsa_pca_projection",
-           "lsa_index_insert_workspace_bytes", "lsa_index_insert"]
+           "lsa_index_insert_workspace_bytes", "lsa_index_insert", "lsa_select_attend_noalloc"]
 
 
 class IndexDesc(ctypes.Structure):
@@ -77,6 +77,8 @@ def lib():
         L.lsa_select_attend_workspace_bytes.argtypes = [i64, i32, i32, D, i32, i32, i32, i32, ctypes.POINTER(i64)]
         L.lsa_select_attend.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, ctypes.c_float,
                                         P, P, P, P, P, P, i64, P]
+        L.lsa_select_attend_noalloc.argtypes = [P, P, P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32,
+                                                ctypes.c_float, P, P, P, P, P, P]
         L.lsa_select.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, i32, P, P, P, P, i64, P]
         L.lsa_select_flat_workspace_bytes.argtypes = [i64, i32, D, ctypes.POINTER(i64)]
         L.lsa_select_flat.argtypes = [P, i32, i64, i32, i32, P, D, P, P, i32, i32, i32, P, P, P, P, i64, P]
@@ -218,11 +220,14 @@ def index_import(host, desc: IndexDesc, device, index: Optional[torch.Tensor] = 
     return index
 
 
-def workspace_status(ws: torch.Tensor, stream=None) -> int:
-    """Read and clear a workspace's status word (LSA_STATUS_* bits; lsa_workspace_status)."""
-    _need(ws, "ws")
+def workspace_status(ws: Optional[torch.Tensor], stream=None) -> int:
+    """Read and clear a workspace's status word (LSA_STATUS_* bits;
+    lsa_workspace_status); ws None reads the no-alloc entry point's scratch."""
+    if ws is not None:
+        _need(ws, "ws")
     v = ctypes.c_int32()
-    _check(lib().lsa_workspace_status(_ptr(ws), ws.numel(), ctypes.byref(v), _stream(stream)), "lsa_workspace_status")
+    _check(lib().lsa_workspace_status(_ptr(ws), 0 if ws is None else ws.numel(), ctypes.byref(v), _stream(stream)),
+           "lsa_workspace_status")
     return v.value
 
 
@@ -362,6 +367,45 @@ def select_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
                                    _ptr(sel_count), _ptr(cutoff), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)),
            "lsa_select_attend")
+    return sel, sel_count, cutoff, out, lse
+
+
+def select_attend_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor,
+                          index: torch.Tensor, desc: IndexDesc, W: torch.Tensor, beam: int, k: int,
+                          scale: float = 0.0, sel: Optional[torch.Tensor] = None,
+                          sel_count: Optional[torch.Tensor] = None, cutoff: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          want_cutoff: bool = True, want_lse: bool = True, stream=None, n_sink: int = 0,
+                          window: int = 0):
+    """lsa_select_attend_noalloc: the one-launch select + attend on the
+    library's fixed scratch (no workspace).  Pass every output to make the
+    call allocate nothing at all.  -> (sel, count, cutoff, out, lse)"""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (q_pos, "q_pos"), (W, "W")):
+        _need(t, nm)
+    m, h_q, d = Q.shape
+    h = desc.h_kv
+    _need_kv(K, V, Q, h, desc.n)
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((m, h, k + n_sink + window), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((m, h), dtype=torch.int32, device=dev)
+    if cutoff is None and want_cutoff:
+        cutoff = torch.empty((m, h), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((m, h_q), dtype=torch.float32, device=dev)
+    _need_out(sel, "sel", (m, h, k + n_sink + window), torch.int32)
+    _need_out(sel_count, "sel_count", (m, h), torch.int32)
+    _need_out(cutoff, "cutoff", (m, h), torch.float32)
+    _need_out(out, "out", (m, h_q, d), Q.dtype)
+    _need_out(lse, "lse", (m, h_q), torch.float32)
+    _check(lib().lsa_select_attend_noalloc(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), m, h_q, d, _ptr(q_pos),
+                                           ctypes.byref(desc), _ptr(index), _ptr(W), beam, k, n_sink, window,
+                                           float(scale), _ptr(sel), _ptr(sel_count), _ptr(cutoff), _ptr(out),
+                                           _ptr(lse), _stream(stream)),
+           "lsa_select_attend_noalloc")
     return sel, sel_count, cutoff, out, lse
 
 

@@ -243,8 +243,15 @@ int lsa_index_import(const lsa_index_desc *desc, const void *host_src, int64_t s
 }
 
 int lsa_workspace_status(void *ws, int64_t ws_bytes, int32_t *status, void *stream) {
-    if (!status || !ws || ws_bytes < lsa::kWsHeader) return LSA_EINVAL;
-    return read_status(ws, status, (hipStream_t)stream);
+    if (!status) return LSA_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (!ws) {
+        // the scratch of lsa_select_attend_noalloc on the current device
+        if (lsa::scratch_ptr(&ws, st) != hipSuccess) return LSA_EHIP;
+    } else if (ws_bytes < lsa::kWsHeader) {
+        return LSA_EINVAL;
+    }
+    return read_status(ws, status, st);
 }
 
 int lsa_build_workspace_bytes(int64_t n, int h_kv, int d, int r, int b, int L, int64_t *bytes) {
@@ -488,6 +495,39 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
     }
     return finish_select(e, one_launch ? ws : nullptr, sel, sel_count, m * desc->h_kv, k + n_sink + window, desc->n,
                          st);
+}
+
+int lsa_select_attend_noalloc(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
+                              const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W,
+                              int beam, int k, int n_sink, int window, float scale, int32_t *sel, int32_t *sel_count,
+                              float *sel_cutoff, void *out, float *lse, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != LSA_OK) return rc;
+    if (m < 0 || h_q < 1 || d < 1 || beam < 1 || k < 1) return LSA_EINVAL;
+    if (h_q % desc->h_kv != 0) return LSA_EINVAL;
+    if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
+    if (!dtype_ok(dtype)) return LSA_EUNSUPPORTED;
+    if (d > 256 || (int64_t)beam * desc->b > 4096 || k > 8192) return LSA_EUNSUPPORTED;
+    if (h_q / desc->h_kv > 16 || d < 8 || d % 8 != 0) return LSA_EUNSUPPORTED;
+    if (!(scale >= 0.0f) || isinf(scale)) return LSA_EINVAL;
+    if (m > INT32_MAX) return LSA_EUNSUPPORTED;
+    if (m == 0) return LSA_OK;
+    if (!Q || !K || !V || !q_pos || !index || !W || !sel || !sel_count || !out) return LSA_EINVAL;
+    if (!lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)) return LSA_EUNSUPPORTED;
+    if (lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k) > lsa::scratch_bytes())
+        return LSA_ESCRATCH;
+    if (scale == 0.0f) scale = 1.0f / sqrtf((float)d);
+    hipStream_t st = (hipStream_t)stream;
+    void *ws = nullptr;
+    hipError_t e = lsa::scratch_ptr(&ws, st);
+    if (e == hipSuccess)
+        e = lsa::decode(Q, K, V, dtype, m, h_q, desc->h_kv, d, q_pos, (const char *)index, desc->n, desc->r,
+                        desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
+                        desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff, scale, out, lse,
+                        ws, true, st);
+    // (debug mode: the stream is synchronised and the status word read, with
+    // no host-side copies of the index or of sel)
+    return finish(e, ws, st);
 }
 
 }  // extern "C"

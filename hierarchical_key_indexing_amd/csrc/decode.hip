@@ -39,6 +39,7 @@
 #include "lsa.h"
 
 #include <atomic>
+#include <mutex>
 
 namespace lsa {
 
@@ -918,6 +919,43 @@ static hipError_t launch_decode(const DecodeArgs &A, dim3 grid, size_t shm, hipS
     }
     hipLaunchKernelGGL((k_decode<T, ATT, RC, DC, PC>), grid, dim3(256), shm, st, A);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The workspace of lsa_select_attend_noalloc, for callers that cannot
+// allocate: one copy per device, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory, so host code only
+// ever uses the address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = (int64_t)4 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void k_scratch_clear(int4 *p, int64_t count) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x)
+        p[e] = int4{0, 0, 0, 0};
+}
+
+int64_t scratch_bytes() { return kScratchBytes; }
+
+// This device's copy of the scratch.  Set up once per device, with that
+// device current: its address is taken, and it is cleared on `st` (the decode
+// kernel needs the words it polls zero on entry, and leaves them zero).
+hipError_t scratch_ptr(void **out, hipStream_t st) {
+    static std::mutex mu;
+    static void *dev_ptr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(k_scratch_clear, dim3(256), dim3(256), 0, st, (int4 *)ptr, kScratchBytes / 16);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        dev_ptr[dev] = ptr;
+    }
+    *out = dev_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int d,

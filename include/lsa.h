@@ -18,7 +18,9 @@
  * Conventions shared by every entry point
  *   - All pointers named as device buffers are device memory on the current
  *     HIP device; the caller owns every buffer.  The library allocates no
- *     memory and keeps no state between calls.
+ *     memory and keeps no state between calls, except the fixed scratch of
+ *     lsa_select_attend_noalloc (4 MiB per device that calls it, kept until
+ *     the process ends).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on that stream and returns; results are
  *     ready once the stream reaches that point.
@@ -156,9 +158,10 @@ int lsa_index_import(const lsa_index_desc *desc, const void *host_src, int64_t s
  * Read and clear the status word of a zero-filled workspace used by
  * lsa_select or lsa_select_attend (*status: the LSA_STATUS_* bits that every
  * call since the last read set, 0 when all went well; only their
- * multi-workgroup form sets any).  Synchronous: waits for `stream` first, so
- * it sees every call enqueued on that stream before it.  Errors: LSA_EINVAL
- * (NULL ws or status, ws_bytes < 256), LSA_EHIP.
+ * multi-workgroup form sets any).  With ws = NULL it reads the scratch of
+ * lsa_select_attend_noalloc on the current device.  Synchronous: waits for
+ * `stream` first, so it sees every call enqueued on that stream before it.
+ * Errors: LSA_EINVAL (NULL status, ws_bytes < 256 with ws non-NULL), LSA_EHIP.
  */
 int lsa_workspace_status(void *ws, int64_t ws_bytes, int32_t *status, void *stream);
 
@@ -421,6 +424,29 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
                       const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W,
                       int beam, int k, int n_sink, int window, float scale, int32_t *sel, int32_t *sel_count,
                       float *sel_cutoff, void *out, float *lse, void *ws, int64_t ws_bytes, void *stream);
+
+/*
+ * lsa_select_attend in its one-launch form with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing
+ * and calls no allocating routine: its workspace is a fixed 4 MiB array of
+ * device memory inside the library (one copy per device, set up and cleared
+ * on the first call on that device, held until the process ends).
+ *
+ * Arguments, results and limits as lsa_select_attend, minus ws and ws_bytes.
+ * Errors as lsa_select_attend, plus: LSA_EUNSUPPORTED when the batch does not
+ * take the one-launch form (m * h_kv * beam above the number of compute
+ * units, L < 2, beam > 32, h_q/h_kv > 16); LSA_ESCRATCH when its workspace
+ * (lsa_select_attend_workspace_bytes for the same arguments) exceeds 4 MiB.
+ * The array is shared by every call on a device and keeps the last call's
+ * contents (the call leaves every word it polls zero): calls that overlap on
+ * one device, from any stream or thread, race and give wrong results.  Its
+ * status word is read with lsa_workspace_status(NULL, ...).
+ */
+int lsa_select_attend_noalloc(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
+                              const int32_t *q_pos, const lsa_index_desc *desc, const void *index, const float *W,
+                              int beam, int k, int n_sink, int window, float scale, int32_t *sel, int32_t *sel_count,
+                              float *sel_cutoff, void *out, float *lse, void *stream);
 
 #ifdef __cplusplus
 }
