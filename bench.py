@@ -197,7 +197,11 @@ def extra_train(lsa, synth, torch, np, dev, w, reps=3):
     aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device=dev)
     sws = lsa.workspace(lsa.select_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
 
+    fws = lsa.workspace(lsa.select_attend_workspace_bytes(m, w.h_q, w.d, desc, w.beam, w.k), dev)
+
     def fwd(ev=None):
+        # build, then select and attend as two calls, then as one fused call
+        # (node-major selection and attention)
         if ev: ev[0].record()
         lsa.build_index(K, W, w.b, w.L, w.iters, index=index, ws=bws)
         if ev: ev[1].record()
@@ -205,22 +209,28 @@ def extra_train(lsa, synth, torch, np, dev, w, reps=3):
         if ev: ev[2].record()
         lsa.attend(Q, K, V, sel, cnt, out=out, want_lse=False, ws=aws)
         if ev: ev[3].record()
+        lsa.select_attend(Q, K, V, pos, index, desc, W, w.beam, w.k, sel=sel, sel_count=cnt, out=out,
+                          want_cutoff=False, want_lse=False, ws=fws)
+        if ev: ev[4].record()
     fwd()
     torch.cuda.synchronize()
-    evs = [_events(torch, 4) for _ in range(reps)]
+    evs = [_events(torch, 5) for _ in range(reps)]
     for ev in evs:
         fwd(ev)
     torch.cuda.synchronize()
     b = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
     sl = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs]))
     at = float(np.mean([ev[2].elapsed_time(ev[3]) for ev in evs]))
+    fu = float(np.mean([ev[3].elapsed_time(ev[4]) for ev in evs]))
     c = cnt.cpu().numpy()
-    tot = b + sl + at
-    return {"forward_ms": round(tot, 3), "build_ms": round(b, 3), "select_ms": round(sl, 3), "attend_ms": round(at, 3),
+    tot = b + fu
+    return {"forward_ms": round(tot, 3), "build_ms": round(b, 3), "select_attend_ms": round(fu, 3),
             "queries_per_s": round(m / (tot * 1e-3), 1), "mean_sel_count": float(c.mean()),
-            "attend_GBps_algorithmic": round(attend_bytes(w, m, c) / (at * 1e-3) / 1e9, 2),
-            "attend_tflops": round(4.0 * m * w.h_q * float(c.mean()) * w.d / (at * 1e-3) / 1e12, 3),
-            "timing": f"build + select + attend of all {m} positions, mean of {reps} forwards"}
+            "two_calls": {"select_ms": round(sl, 3), "attend_ms": round(at, 3), "forward_ms": round(b + sl + at, 3),
+                          "attend_GBps_algorithmic": round(attend_bytes(w, m, c) / (at * 1e-3) / 1e9, 2),
+                          "attend_tflops": round(4.0 * m * w.h_q * float(c.mean()) * w.d / (at * 1e-3) / 1e12, 3)},
+            "timing": f"build + fused select_attend of all {m} positions (node-major selection and attention), "
+                      f"mean of {reps} forwards; two_calls: lsa_select then lsa_attend on the same inputs"}
 
 
 LOCAL_SINKS, LOCAL_WINDOW = 4, 512
@@ -640,14 +650,18 @@ def main():
         pws_n = lsa.attend_workspace_bytes(mp, w.h_q, w.h_kv, w.d, w.k)
         pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
         psws = lsa.workspace(lsa.select_workspace_bytes(mp, w.h_q, w.d, desc, w.beam, w.k), dev)
+        pfws = lsa.workspace(lsa.select_attend_workspace_bytes(mp, w.h_q, w.d, desc, w.beam, w.k), dev)
         def pstep():
-            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=psws)
-            lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
+            # the chunk step: one fused call (node-major selection and attention)
+            lsa.select_attend(Qp, K, V, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, out=pout,
+                              want_cutoff=False, want_lse=False, ws=pfws)
         for _ in range(2):
             pstep()
+            lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=psws)
+            lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
         torch.cuda.synchronize()
         npre = 5
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
         for _ in range(npre):
             lsa.select(Qp, ppos, index, desc, W, w.beam, w.k, sel=psel, sel_count=pcnt, want_cutoff=False, ws=psws)
@@ -655,9 +669,13 @@ def main():
         for _ in range(npre):
             lsa.attend(Qp, K, V, psel, pcnt, out=pout, want_lse=False, ws=pws)
         e[2].record()
+        for _ in range(npre):
+            pstep()
+        e[3].record()
         torch.cuda.synchronize()
         ps = e[0].elapsed_time(e[1]) / npre
         pa = e[1].elapsed_time(e[2]) / npre
+        pf = e[2].elapsed_time(e[3]) / npre
         pc = pcnt.cpu().numpy()
         # the same chunk step (select + attend) replayed from a HIP graph, so
         # the gaps between its kernel launches are not counted; every replay
@@ -687,14 +705,19 @@ def main():
             except Exception as ex:     # capture unavailable: the eager figures stand
                 log("prefill graph timing skipped:", repr(ex))
         breakdown["prefill_1m"] = {
-            "queries_per_s": round(mp / ((ps + pa) * 1e-3), 1), "select_ms": round(ps, 4), "attend_ms": round(pa, 4),
-            "select_share": round(ps / (ps + pa), 4),
-            "attend_GBps_algorithmic": round(attend_bytes(w, mp, pc) / (pa * 1e-3) / 1e9, 2),
-            "attend_tflops": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pa * 1e-3) / 1e12, 3),
+            "queries_per_s": round(mp / (pf * 1e-3), 1), "select_attend_ms": round(pf, 4),
+            "mean_sel_count": float(pc.mean()),
+            "attend_tflops_algorithmic_fused": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pf * 1e-3) / 1e12, 3),
             "graph_ms_per_chunk": None if pg_ms is None else round(pg_ms, 4),
             "queries_per_s_graph": None if pg_ms is None else round(mp / (pg_ms * 1e-3), 1),
-            "timing": "select and attend: events around 5 eager calls each; graph: 5 replays of the captured step"}
-        del Qp, psel, pcnt, pout, pws, psws
+            "two_calls": {"queries_per_s": round(mp / ((ps + pa) * 1e-3), 1), "select_ms": round(ps, 4),
+                          "attend_ms": round(pa, 4), "select_share": round(ps / (ps + pa), 4),
+                          "attend_GBps_algorithmic": round(attend_bytes(w, mp, pc) / (pa * 1e-3) / 1e9, 2),
+                          "attend_tflops": round(4.0 * mp * w.h_q * float(pc.mean()) * w.d / (pa * 1e-3) / 1e12, 3)},
+            "timing": "chunk step = one fused select_attend (node-major selection and attention): events around 5 "
+                      "eager calls; graph: 5 replays of the captured step; two_calls: lsa_select then lsa_attend, "
+                      "5 eager calls each"}
+        del Qp, psel, pcnt, pout, pws, psws, pfws
 
     if not args.no_extra:
         log("sinks and window")

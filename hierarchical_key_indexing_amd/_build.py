@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "liblsa.so")
-SOURCES = ["api.hip", "build.hip", "select.hip", "attend.hip", "decode.hip", "flat.hip", "pca.hip", "insert.hip"]
+SOURCES = ["api.hip", "build.hip", "select.hip", "attend.hip", "nm_attend.hip", "decode.hip", "flat.hip", "pca.hip",
+           "insert.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions stay off (hand-written or compiler-made)

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "lsa.h"
@@ -32,6 +33,14 @@ inline int check_desc(const lsa_index_desc *desc) {
 }
 
 inline bool dtype_ok(int dtype) { return dtype == LSA_F32 || dtype == LSA_BF16; }
+
+// lsa_select_attend's node-major form (selection grouped by kept node, each
+// node's keys attended once per tile of rows) applies to these shapes with
+// bf16 inputs
+inline bool nm_attend_shape(int d, int h_q, const lsa_index_desc *desc, int beam, int n_sink, int window) {
+    return lsa::nm_shape_ok(desc->r, desc->b, desc->L, beam, d, desc->nodes) &&
+           lsa::nma_shape_ok(LSA_BF16, d, h_q / desc->h_kv, n_sink, window);
+}
 
 // ---------------------------------------------------------------- index check
 // The tree held in host memory `h` in the layout D: the properties every
@@ -450,6 +459,10 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
     if ((rc = check_local(k, n_sink, window)) != LSA_OK) return rc;
     if (lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k))
         *bytes = lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k);
+    else if (nm_attend_shape(d, h_q, desc, beam, n_sink, window))
+        // sized for the node-major form (bf16 inputs); fp32 inputs need less
+        *bytes = std::max(lsa::nm_attend_workspace_bytes(m, h_q, desc->h_kv, desc->L, desc->nodes),
+                          lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k + n_sink + window));
     else
         *bytes = lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k + n_sink + window);
     return LSA_OK;
@@ -471,9 +484,11 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
     if (m > INT32_MAX) return LSA_EUNSUPPORTED;
     if (m == 0) return LSA_OK;
     if (!Q || !K || !V || !q_pos || !index || !W || !sel || !sel_count || !out) return LSA_EINVAL;
-    int64_t need = 0;
-    rc = lsa_select_attend_workspace_bytes(m, h_q, d, desc, beam, k, n_sink, window, &need);
-    if (rc != LSA_OK) return rc;
+    // (the node-major form runs when its batches fit ws; below that size the
+    // two-step form needs only the attention's workspace)
+    const int64_t need = lsa::decode_path_ok(m, h_q, desc->h_kv, d, desc->r, desc->b, desc->L, beam, k)
+                             ? lsa::decode_workspace_bytes(m, h_q, desc->h_kv, d, desc->L, beam, k)
+                             : lsa::attend_workspace_bytes(m, h_q, desc->h_kv, d, k + n_sink + window);
     if (ws_bytes < need || (!ws && need > 0)) return LSA_ENOSPC;
     if (scale == 0.0f) scale = 1.0f / sqrtf((float)d);
     hipStream_t st = (hipStream_t)stream;
@@ -485,6 +500,13 @@ int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, in
                         desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,
                         desc->perm_off, W, beam, k, n_sink, window, sel, sel_count, sel_cutoff, scale, out, lse,
                         ws, true, st);
+    } else if (ws && lsa::nma_shape_ok(dtype, d, h_q / desc->h_kv, n_sink, window) &&
+               lsa::nm_shape_ok(desc->r, desc->b, desc->L, beam, d, desc->nodes) &&
+               lsa::nm_attend_fits(m, h_q, desc->h_kv, desc->L, desc->nodes, ws_bytes)) {
+        e = lsa::select_attend_nm(Q, K, V, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv,
+                                  desc->r, desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off,
+                                  desc->leaf_off_off, desc->perm_off, W, beam, k, n_sink, window, sel, sel_count,
+                                  sel_cutoff, scale, out, lse, ws, ws_bytes, st);
     } else {
         e = lsa::select_keys(Q, dtype, m, h_q, d, q_pos, (const char *)index, desc->n, desc->h_kv, desc->r,
                              desc->b, desc->L, desc->nodes, desc->centroid_off, desc->count_off, desc->leaf_off_off,

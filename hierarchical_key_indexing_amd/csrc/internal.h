@@ -33,6 +33,37 @@ hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, cons
 bool nm_shape_ok(int r, int b, int L, int beam, int d, const int64_t *nodes);
 int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes);
 
+// node-major attention (nm_attend.hip), run after each batch of node-major
+// selection when select and attention are called together
+struct NmaWs { uint64_t *amask; int32_t *abound, *toff, *tbin; char *pinf; float *part; size_t bytes; };
+struct NmaBatch {
+    const void *Q, *K, *V;
+    const int32_t *q_pos;
+    int64_t row0, groups;
+    int h_q, h_kv;
+    int64_t n;
+    int b;
+    int64_t nodes_prev, nleaf;
+    const int32_t *leaf_off, *perm;
+    int n_sink, window;
+    const int32_t *pairs, *noff, *keep;
+    NmaWs ws;
+    float scale;
+    void *out;
+    float *lse;
+};
+bool nma_shape_ok(int dtype, int d, int G, int n_sink, int window);
+NmaWs carve_nma_ws(char *base, int64_t groups, int G, int64_t nbins);
+hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st);
+int64_t nm_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int L, const int64_t *nodes);
+bool nm_attend_fits(int64_t m, int h_q, int h_kv, int L, const int64_t *nodes, int64_t ws_bytes);
+hipError_t select_attend_nm(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
+                            const int32_t *q_pos, const char *index, int64_t n, int h_kv, int r, int b, int L,
+                            const int64_t *nodes, const int64_t *centroid_off, const int64_t *count_off,
+                            int64_t leaf_off_off, int64_t perm_off, const float *W, int beam, int k, int n_sink,
+                            int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff, float scale, void *out,
+                            float *lse, void *ws, int64_t ws_bytes, hipStream_t st);
+
 int attend_nsplit(int64_t m, int h_kv, int k);
 int64_t attend_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int k);
 hipError_t attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int h_kv, int64_t n,

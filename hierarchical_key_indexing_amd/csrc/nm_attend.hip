@@ -1,0 +1,557 @@
+// Node-major sparse attention for many query rows (gfx950, bf16 K/V, d = 128).
+//
+// Attention runs over the keys each query retrieved ("Latent sparse
+// attention", bdtechtalks.com, section "How latent sparse attention works"),
+// and those keys come from the leaves of a few kept clusters ("Latent Sparse
+// Attention Breaks Through the Million-Token Context Bottleneck",
+// kongchang.com, section "How LSA Sidesteps Per-Key Scoring with Hierarchical
+// Clustering").  Many rows keep the same cluster, so instead of gathering each
+// (row, KV head) group's keys on its own, the work is taken cluster by
+// cluster: the (row, kept level-(L-1) node) pairs that node-major selection
+// grouped by node are cut into tiles of up to 128 / G pairs; a workgroup
+// stages the node's keys and values in LDS once, 64 keys at a time, and its
+// four waves compute the scores and the P V products of every (pair, query
+// head) column of the tile on the matrix cores (v_mfma_f32_16x16x32_bf16, 32
+// columns per wave).  A column only sees the keys its row retrieved from that
+// node: the children whose leaves it took (a 64-bit mask from the selection's
+// finish), inside its retrieval range, and for the one leaf taken in part,
+// up to the last key taken.  Each column writes an unnormalised partial state
+// (output, base-2 max, sum); a merge kernel combines a group's states by
+// log-sum-exp.  Prefill, which computes in bulk, is where this pays (same
+// page, section "The Accuracy-Efficiency Dilemma of Sparse Attention").
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+#include "mfma_attn.h"
+
+namespace lsa {
+
+constexpr int kNmaP = 16;       // kept-node slots per group (the throughput path's beam limit)
+constexpr int kNmaD = 128;      // head dimension of this path
+constexpr int kNmaKC = 64;      // keys staged per step
+constexpr int kNmaCols = 128;   // (pair, head) columns per tile: 32 per wave
+constexpr int kKst = kNmaD + 8; // K tile row stride (bf16)
+constexpr int kVst = kNmaKC + 8;// V^T tile row stride (bf16)
+constexpr float kLazy = 8.0f;   // log2 headroom of the lazily moved running max
+
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // 16 bytes held in registers
+
+struct NmaArgs {
+    const uint16_t *Q, *K, *V;  // bf16: Q [m][h_q][128], K/V [h_kv][n][128]
+    const int32_t *q_pos;
+    int64_t row0, groups;       // the batch: rows row0.., groups = rows x h_kv
+    int h_q, h_kv, G;
+    int64_t n;
+    int b;
+    int64_t nodes_prev, nleaf;  // nodes at level L-1 and L
+    const int32_t *leaf_off;    // [h_kv][nleaf + 1]
+    const int32_t *perm;        // [h_kv][n]
+    int n_sink, window;
+    const int32_t *pairs;       // group * kNmaP + slot, grouped by (head, node) bin
+    const int32_t *noff;        // [nbins + 1]: the bins' runs in pairs
+    const int32_t *keep;        // [groups]
+    const uint64_t *amask;      // [groups][kNmaP]
+    const int32_t *abound;      // [groups][2]
+    int64_t nbins;
+    int T;                      // pairs per tile (128 / G)
+    int32_t *toff;              // [nbins + 1]: tiles before each bin
+    int32_t *tbin;              // [tiles]: the bin of each tile
+    u32x4_t *pinf;              // [pairs][2]: pair records in bin order (k_nma_pairs)
+    float *part;                // [groups][kNmaP][G][128 + 2]
+    float scale_log2;
+    uint16_t *out;              // bf16 [m][h_q][128]
+    float *lse;                 // [m][h_q] or NULL
+};
+
+// tiles per bin, exclusive scan (one workgroup; total at toff[nbins])
+__global__ __launch_bounds__(256) void k_nma_scan(NmaArgs A) {
+    __shared__ int scr[8];
+    int carry = 0;
+    for (int64_t base = 0; base < A.nbins; base += 256 * 8) {
+        int v[8], s = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
+            v[u] = e < A.nbins ? (A.noff[e + 1] - A.noff[e] + A.T - 1) / A.T : 0;
+            s += v[u];
+        }
+        int tot;
+        int run = carry + block_excl_scan(s, scr, &tot);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
+            if (e < A.nbins) A.toff[e] = run;
+            run += v[u];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) A.toff[A.nbins] = carry;
+}
+
+__global__ __launch_bounds__(256) void k_nma_map(NmaArgs A) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.nbins; e += (int64_t)gridDim.x * blockDim.x)
+        for (int t = A.toff[e]; t < A.toff[e + 1]; ++t) A.tbin[t] = (int32_t)e;
+}
+
+// Tiles [t0, t1) of workgroup `bid` of `nwg` (a multiple of 8): the tile
+// list, ordered by node, is cut into nwg contiguous ranges, and neighbouring
+// ranges run on one XCD (workgroup i runs on XCD i % 8), so the tiles of one
+// node that follow each other are served by that XCD's L2.
+LSA_DEV void nma_range(int64_t bid, int64_t nwg, int64_t total, int64_t &t0, int64_t &t1) {
+    const int64_t r = (bid % 8) * (nwg / 8) + bid / 8;
+    const int64_t per = (total + nwg - 1) / nwg;
+    t0 = min(total, r * per);
+    t1 = min(total, t0 + per);
+}
+
+// The child of the node whose leaf holds member position `at` (lof: the
+// node's b + 1 leaf offsets; empty leaves share the next leaf's offset).
+LSA_DEV int nma_child(const int32_t *lof, int b, int64_t at) {
+    int c = 0;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+        if (c + s < b && lof[c + s] <= at) c += s;
+    return c;
+}
+
+// A large node's members, one step at a time: threads < 64 read the members
+// at positions t0.. and their children (64 past the node's end, whose id
+// repeats the last member so that every gather stays inside the cache).
+LSA_DEV void nma_load_ids(const int32_t *pm, const int32_t *lof_s, int b, int64_t t0, int64_t hi, int32_t *ids,
+                          int32_t *cid) {
+    const int tid = threadIdx.x;
+    if (tid < kNmaKC) {
+        const int64_t at = t0 + tid;
+        const bool in = at < hi;
+        ids[tid] = pm[in ? at : hi - 1];
+        cid[tid] = in ? nma_child(lof_s, b, at) : 64;
+    }
+}
+
+// K: thread = (key tid / 4, 32-dim part tid % 4), four 16-byte loads into
+// registers; stored as rows of kKst bf16.
+LSA_DEV void nma_load_k(const uint16_t *__restrict__ Kg, const int32_t *ids, u32x4_t (&kr)[4]) {
+    const int tid = threadIdx.x;
+    const size_t kb = (size_t)ids[tid / 4] * kNmaD + 32 * (tid % 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kr[u] = *reinterpret_cast<const u32x4_t *>(Kg + kb + 8 * u);
+}
+
+LSA_DEV void nma_store_k(uint16_t *Ks, const u32x4_t (&kr)[4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(Ks + (tid / 4) * kKst + 32 * (tid % 4) + 8 * u) = kr[u];
+}
+
+// V: thread = (4-key block tid % 16, 8-dim chunk tid / 16), four 16-byte
+// loads into registers.
+LSA_DEV void nma_load_v(const uint16_t *__restrict__ Vg, const int32_t *ids, u32x4_t (&vr)[4]) {
+    const int tid = threadIdx.x;
+    const int vkq = tid % 16, vcg = tid / 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        vr[j] = *reinterpret_cast<const u32x4_t *>(Vg + (size_t)ids[4 * vkq + j] * kNmaD + 8 * vcg);
+}
+
+// V transposed into V^T: a thread's 4 keys x 8 dims become rows 8 vcg + dd
+// over keys 4 vkq .. + 3 (8 bytes a row; one byte permute per pair of keys).
+LSA_DEV void nma_store_v(uint16_t *Vt, const u32x4_t (&vr)[4]) {
+    const int tid = threadIdx.x;
+    const int vkq = tid % 16, vcg = tid / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // dword i of each key holds dims 8 vcg + 2 i (low half) and + 2 i + 1 (high half)
+        const uint32_t a0 = __builtin_amdgcn_perm(vr[1][i], vr[0][i], 0x05040100u);
+        const uint32_t a1 = __builtin_amdgcn_perm(vr[3][i], vr[2][i], 0x05040100u);
+        const uint32_t b0 = __builtin_amdgcn_perm(vr[1][i], vr[0][i], 0x07060302u);
+        const uint32_t b1 = __builtin_amdgcn_perm(vr[3][i], vr[2][i], 0x07060302u);
+        *reinterpret_cast<uint2 *>(Vt + (8 * vcg + 2 * i) * kVst + 4 * vkq) = uint2{a0, a1};
+        *reinterpret_cast<uint2 *>(Vt + (8 * vcg + 2 * i + 1) * kVst + 4 * vkq) = uint2{b0, b1};
+    }
+}
+
+constexpr int kNmaIds = 1024;   // members of a node staged in LDS (larger nodes: step by step)
+
+// Pair records, in bin order, 32 bytes each (two u32x4): taken-children mask
+// (low, high), entry (group * kNmaP + slot), retrieval range low; range
+// high, child of the leaf taken in part (-1: none), its last taken key, 0.
+// A tile reads its pairs' records in one coalesced load.
+__global__ __launch_bounds__(256) void k_nma_pairs(NmaArgs A) {
+    const int64_t npairs = A.noff[A.nbins];
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < npairs; p += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t e = A.pairs[p];
+        const int64_t grp = e / kNmaP;
+        const int j = e % kNmaP;
+        const AttnSet as = attn_set(A.q_pos[A.row0 + grp / A.h_kv], A.n, A.n_sink, A.window);
+        const uint64_t mask = A.amask[e];
+        const int32_t bs = A.abound[grp * 2];
+        const int32_t bc = (bs >= 0 && (bs >> 6) == j) ? (bs & 63) : -1;
+        A.pinf[2 * p] = u32x4_t{(uint32_t)mask, (uint32_t)(mask >> 32), (uint32_t)e, (uint32_t)as.rlo};
+        A.pinf[2 * p + 1] = u32x4_t{(uint32_t)as.rhi, (uint32_t)bc, (uint32_t)A.abound[grp * 2 + 1], 0u};
+    }
+}
+
+// The keys of the current step that each pair of the tile attends: one
+// ballot per pair (lane = key), wave w taking pairs w, w + 4, ...
+LSA_DEV void nma_pair_masks(int np, const int32_t *ids, const int32_t *chs, const u32x4_t (*pi)[2], uint64_t *pch) {
+    const int lane = lane_id();
+    const int id = ids[lane], c = chs[lane];
+    for (int p = threadIdx.x / kWave; p < np; p += 4) {
+        const u32x4_t r0 = pi[p][0], r1 = pi[p][1];
+        const uint64_t mask = (uint64_t)r0.x | ((uint64_t)r0.y << 32);
+        const int rlo = (int)r0.w, rhi = (int)r1.x, bc = (int)r1.y, plast = (int)r1.z;
+        const bool inc = c < 64 && ((mask >> (c & 63)) & 1ull) && id >= rlo && id <= rhi && !(c == bc && id > plast);
+        const uint64_t word = __ballot(inc);
+        if (lane == 0) pch[p] = word;
+    }
+}
+
+// Tile t: its (head, node) bin, first pair and number of pairs.
+LSA_DEV void nma_tile_desc(const NmaArgs &A, int64_t t, int32_t &bin, int64_t &pb, int &np) {
+    bin = A.tbin[t];
+    pb = A.noff[bin] + (t - A.toff[bin]) * (int64_t)A.T;
+    np = (int)min<int64_t>(A.T, A.noff[bin + 1] - pb);
+}
+
+// Stage node `bin`: its leaf offsets, then (when they fit) its members and
+// their children, padded to whole steps; returns the member range.  Ends
+// with the members visible to the workgroup.
+LSA_DEV void nma_stage_node(const NmaArgs &A, int32_t bin, int32_t *lof_s, int32_t *mid_s, int32_t *mch_s,
+                            int32_t &lo, int32_t &hi, bool &fits) {
+    const int tid = threadIdx.x, b = A.b;
+    const int g = (int)(bin / A.nodes_prev);
+    const int64_t v = bin % A.nodes_prev;
+    if (tid <= b) lof_s[tid] = A.leaf_off[(size_t)g * (A.nleaf + 1) + (size_t)v * b + tid];
+    __syncthreads();
+    lo = lof_s[0];
+    hi = lof_s[b];
+    const int span = (int)min<int64_t>((int64_t)(hi - lo + kNmaKC - 1) / kNmaKC * kNmaKC, (int64_t)kNmaIds + 1);
+    fits = span <= kNmaIds;
+    if (fits && hi > lo) {
+        const int32_t *pm = A.perm + (size_t)g * A.n;
+        for (int x = tid; x < span; x += blockDim.x) {
+            const int64_t at = (int64_t)lo + x;
+            mid_s[x] = pm[at < hi ? at : hi - 1];
+            mch_s[x] = at < hi ? nma_child(lof_s, b, at) : 64;
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kNmaKC * kKst];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[kNmaD * kVst];
+    __shared__ __attribute__((aligned(16))) int32_t mid_s[kNmaIds];    // the node's members (padded to whole steps)
+    __shared__ __attribute__((aligned(16))) int32_t mch_s[kNmaIds];    // and their children
+    __shared__ __attribute__((aligned(16))) int32_t win_s[2][kNmaKC];  // a large node's step members
+    __shared__ __attribute__((aligned(16))) int32_t wch_s[2][kNmaKC];
+    __shared__ int32_t lof_s[65];
+    __shared__ u32x4_t pi_s[2][kNmaCols][2];                           // pair records: this tile's, the next one's
+    __shared__ uint64_t pch_s[kNmaCols];
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int c16 = lane % 16, q = lane / 16;
+    const int G = A.G, b = A.b;
+    int64_t t0, t1;
+    nma_range(blockIdx.x, gridDim.x, A.toff[A.nbins], t0, t1);
+    if (t0 >= t1) return;                         // (uniform in the workgroup)
+
+    // the first tile: its pair records, its node and its first step's rows
+    int32_t bin;
+    int64_t pb;
+    int np;
+    nma_tile_desc(A, t0, bin, pb, np);
+    if (tid < np) { pi_s[0][tid][0] = A.pinf[2 * (pb + tid)]; pi_s[0][tid][1] = A.pinf[2 * (pb + tid) + 1]; }
+    int32_t lo, hi;
+    bool fits;
+    nma_stage_node(A, bin, lof_s, mid_s, mch_s, lo, hi, fits);
+    u32x4_t kr[4], vr[4];
+    {
+        const int g = (int)(bin / A.nodes_prev);
+        const uint16_t *Kg = A.K + (size_t)g * A.n * kNmaD, *Vg = A.V + (size_t)g * A.n * kNmaD;
+        if (!fits && hi > lo) {
+            nma_load_ids(A.perm + (size_t)g * A.n, lof_s, b, lo, hi, win_s[0], wch_s[0]);
+            __syncthreads();
+        }
+        if (hi > lo) {
+            nma_load_k(Kg, fits ? mid_s : win_s[0], kr);
+            nma_load_v(Vg, fits ? mid_s : win_s[0], vr);
+        }
+    }
+    int pbuf = 0;
+    for (int64_t t = t0; t < t1; ++t) {
+        // here: pi_s[pbuf] holds this tile's records, node `bin` is staged and
+        // kr / vr hold (or are loading) this tile's first step
+        const int g = (int)(bin / A.nodes_prev);
+        const int32_t *pm = A.perm + (size_t)g * A.n;
+        const uint16_t *Kg = A.K + (size_t)g * A.n * kNmaD, *Vg = A.V + (size_t)g * A.n * kNmaD;
+        const bool has_next = t + 1 < t1;
+        int32_t nbin = 0;
+        int64_t npb = 0;
+        int nnp = 0;
+        if (has_next) nma_tile_desc(A, t + 1, nbin, npb, nnp);
+        const bool next_same = has_next && nbin == bin && fits;
+        // the next tile's records, in flight during this tile
+        u32x4_t pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
+        if (has_next && tid < nnp) { pn0 = A.pinf[2 * (npb + tid)]; pn1 = A.pinf[2 * (npb + tid) + 1]; }
+        // this lane's two columns (32 w + 16 cb + c16): (pair, head) and the
+        // query fragments (zero past the tile)
+        bf16x8_t qf[2][4];
+        int pcol[2], hh[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int col = 32 * w + 16 * cb + c16;
+            const bool ok = col < np * G;
+            pcol[cb] = ok ? col / G : 0;
+            hh[cb] = ok ? col % G : 0;
+            const int32_t e = (int32_t)pi_s[pbuf][pcol[cb]][0].z;
+            const int64_t i = A.row0 + (e / kNmaP) / A.h_kv;
+            const uint16_t *Qr = A.Q + ((size_t)i * A.h_q + (size_t)g * G + hh[cb]) * kNmaD;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qf[cb][ks] = ok ? *reinterpret_cast<const bf16x8_t *>(Qr + 32 * ks + 8 * q) : bf16x8_t{};
+        }
+        const bool wave_on = 32 * w < np * G;     // (uniform in the wave)
+        floatx4_t acc[2][8];
+        float m_run[2], l_run[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) acc[cb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            m_run[cb] = -INFINITY;
+            l_run[cb] = 0.0f;
+        }
+        int wb = 0;
+        for (int64_t c0 = lo; c0 < hi; c0 += kNmaKC, wb ^= 1) {
+            const int32_t *ids = fits ? mid_s + (c0 - lo) : win_s[wb];
+            const int32_t *chs = fits ? mch_s + (c0 - lo) : wch_s[wb];
+            __syncthreads();                      // the previous step's tiles are read
+            nma_store_k(Ks, kr);
+            nma_store_v(Vt, vr);
+            nma_pair_masks(np, ids, chs, pi_s[pbuf], pch_s);
+            const bool more = c0 + kNmaKC < hi;
+            if (more && !fits) nma_load_ids(pm, lof_s, b, c0 + kNmaKC, hi, win_s[wb ^ 1], wch_s[wb ^ 1]);
+            __syncthreads();
+            // rows in flight while this step is computed: the next step's, or
+            // after the last one the next tile's first (same node); otherwise
+            // this step's again, unused (one unconditional load site, so the
+            // loads stay in flight across the compute)
+            const int32_t *nids = more ? (fits ? mid_s + (c0 + kNmaKC - lo) : win_s[wb ^ 1]) : next_same ? mid_s : ids;
+            nma_load_k(Kg, nids, kr);
+            nma_load_v(Vg, nids, vr);
+            if (!wave_on) continue;
+            // S^T = K Q^T for 64 keys (4 blocks of 16) x 2 column blocks
+            floatx4_t sacc[2][4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                bf16x8_t kf[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    kf[ks] = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * mb + c16) * kKst + 32 * ks + 8 * q);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    sacc[cb][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        sacc[cb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[cb][ks], sacc[cb][mb], 0, 0, 0);
+                }
+            }
+            // Online softmax in base 2 over raw scores (scale folded into the
+            // exponent).  The running max moves only when a column's step max
+            // exceeds it by more than kLazy, so probabilities stay below
+            // 2^kLazy and most steps rescale nothing.
+            bf16x8_t pf[2][2];
+            float alpha[2];
+            bool grow = false;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                // keys 16 mb + 4 q + j of this lane that the column's pair attends
+                const uint64_t word = pch_s[pcol[cb]] >> (4 * q);
+                float sv[16];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = ((word >> (16 * mb + j)) & 1ull) ? sacc[cb][mb][j] : -INFINITY;
+                        sv[4 * mb + j] = x;
+                        mt = fmaxf(mt, x);
+                    }
+                mt = fmaxf(mt, xor_lane_f<16>(mt));
+                mt = fmaxf(mt, xor_lane_f<32>(mt));
+                const float ms = mt * A.scale_log2;                 // (scale > 0: order kept)
+                const bool up = ms > m_run[cb] + kLazy;             // (false while the column is empty)
+                const float m_new = up ? ms : m_run[cb];
+                alpha[cb] = up ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;   // (0 when m_run = -inf)
+                grow |= up;
+                const float mb_ = m_new == -INFINITY ? 0.0f : m_new;   // exp2(-inf - mb_) = 0 for masked keys
+                float ls = 0.0f;
+                // P fragments of the two 32-key PV steps: step s, slot e < 4 is key
+                // 32 s + 4 q + e, slot e >= 4 is key 32 s + 16 + 4 q + e - 4
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = sv[4 * (2 * s + e / 4) + e % 4];
+                        const float pr = __builtin_amdgcn_exp2f(fmaf(x, A.scale_log2, -mb_));
+                        ls += pr;
+                        pf[cb][s][e] = (__bf16)pr;
+                    }
+                ls += xor_lane_f<16>(ls);
+                ls += xor_lane_f<32>(ls);
+                l_run[cb] = l_run[cb] * alpha[cb] + ls;
+                m_run[cb] = m_new;
+            }
+            // O^T += V^T P^T (V^T fragments shared by both column blocks); the
+            // accumulators are rescaled only when some column's max moved
+            if (__any(grow)) {
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) acc[cb][nb] = acc[cb][nb] * alpha[cb];
+            }
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint16_t *vrow = Vt + (16 * nb + c16) * kVst + 32 * s;
+                    const uint2 vlo = *reinterpret_cast<const uint2 *>(vrow + 4 * q);
+                    const uint2 vhi = *reinterpret_cast<const uint2 *>(vrow + 16 + 4 * q);
+                    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, uint4{vlo.x, vlo.y, vhi.x, vhi.y});
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[cb][s], acc[cb][nb], 0, 0, 0);
+                }
+            }
+        }
+        // partial states: unnormalised outputs, base-2 max and sum per column
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int col = 32 * w + 16 * cb + c16;
+            if (col >= np * G) continue;
+            const int32_t e = (int32_t)pi_s[pbuf][pcol[cb]][0].z;
+            float *pp = A.part + ((size_t)e * G + hh[cb]) * (kNmaD + 2);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<floatx4_t *>(pp + 16 * nb + 4 * q) = acc[cb][nb];
+            if (q == 0) { pp[kNmaD] = m_run[cb]; pp[kNmaD + 1] = l_run[cb]; }
+        }
+        if (!has_next) break;
+        // the next tile: its records into the other buffer; a new node is
+        // staged (and its first step loaded) once every wave is past this one
+        if (tid < nnp) { pi_s[pbuf ^ 1][tid][0] = pn0; pi_s[pbuf ^ 1][tid][1] = pn1; }
+        __syncthreads();
+        if (!next_same) {
+            nma_stage_node(A, nbin, lof_s, mid_s, mch_s, lo, hi, fits);
+            const int gn = (int)(nbin / A.nodes_prev);
+            const uint16_t *Kn = A.K + (size_t)gn * A.n * kNmaD, *Vn = A.V + (size_t)gn * A.n * kNmaD;
+            if (!fits && hi > lo) {
+                nma_load_ids(A.perm + (size_t)gn * A.n, lof_s, b, lo, hi, win_s[0], wch_s[0]);
+                __syncthreads();
+            }
+            if (hi > lo) {
+                nma_load_k(Kn, fits ? mid_s : win_s[0], kr);
+                nma_load_v(Vn, fits ? mid_s : win_s[0], vr);
+            }
+        }
+        bin = nbin;
+        pb = npb;
+        np = nnp;
+        pbuf ^= 1;
+    }
+}
+
+// One workgroup per group: M = max m_j, l = sum l_j 2^(m_j - M),
+// o = sum o_j 2^(m_j - M) / l over the group's kept nodes j.
+__global__ __launch_bounds__(256) void k_nma_merge(NmaArgs A) {
+    __shared__ float ml_s[kNmaP][2][16];
+    const int64_t grp = blockIdx.x;
+    const int64_t i = A.row0 + grp / A.h_kv;
+    const int g = (int)(grp % A.h_kv);
+    const int G = A.G, P = A.keep[grp];
+    const float *pb = A.part + (size_t)grp * kNmaP * G * (kNmaD + 2);
+    for (int e = threadIdx.x; e < P * G; e += blockDim.x) {
+        const float *pp = pb + (size_t)e * (kNmaD + 2);
+        ml_s[e / G][0][e % G] = pp[kNmaD];
+        ml_s[e / G][1][e % G] = pp[kNmaD + 1];
+    }
+    __syncthreads();
+    for (int c4 = threadIdx.x; c4 < G * kNmaD / 4; c4 += blockDim.x) {
+        const int h = c4 / (kNmaD / 4), dd = 4 * (c4 % (kNmaD / 4));
+        float M = -INFINITY;
+        for (int j = 0; j < P; ++j) M = fmaxf(M, ml_s[j][0][h]);
+        float l = 0.0f;
+        floatx4_t o = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < P; ++j) {
+            const float mj = ml_s[j][0][h];
+            if (mj == -INFINITY) continue;
+            const float wgt = __builtin_amdgcn_exp2f(mj - M);
+            l += ml_s[j][1][h] * wgt;
+            const float *pp = pb + ((size_t)j * G + h) * (kNmaD + 2) + dd;
+            o += floatx4_t{pp[0], pp[1], pp[2], pp[3]} * wgt;
+        }
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
+        uint16_t *op = A.out + oh * kNmaD + dd;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) op[x] = from_float<bf16_t>(o[x] * inv).bits;
+        if (dd == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+bool nma_shape_ok(int dtype, int d, int G, int n_sink, int window) {
+    return dtype == 1 && d == kNmaD && G >= 1 && G <= 16 && n_sink == 0 && window == 0;
+}
+
+static inline size_t nma_a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int64_t nma_tiles_bound(int64_t groups, int G, int64_t nbins) {
+    const int T = kNmaCols / G;
+    const int64_t pairs = groups * kNmaP;
+    return ((pairs / T + std::min(nbins, pairs) + 8) + 7) / 8 * 8;
+}
+
+// Buffers of the node-major attention for one batch, carved from `base`
+// (NULL: sizes only): taken-leaf masks, boundaries, tile offsets and map,
+// partial states.
+NmaWs carve_nma_ws(char *base, int64_t groups, int G, int64_t nbins) {
+    size_t cur = 0;
+    NmaWs w{};
+    auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = nma_a256(cur + n); return p; };
+    w.amask = (uint64_t *)take(sizeof(uint64_t) * groups * kNmaP);
+    w.abound = (int32_t *)take(sizeof(int32_t) * groups * 2);
+    w.toff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
+    w.tbin = (int32_t *)take(sizeof(int32_t) * nma_tiles_bound(groups, G, nbins));
+    w.pinf = take(32 * (size_t)groups * kNmaP);
+    w.part = (float *)take(sizeof(float) * groups * kNmaP * G * (kNmaD + 2));
+    w.bytes = cur;
+    return w;
+}
+
+hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
+    NmaArgs A{};
+    A.Q = (const uint16_t *)B.Q; A.K = (const uint16_t *)B.K; A.V = (const uint16_t *)B.V; A.q_pos = B.q_pos;
+    A.row0 = B.row0; A.groups = B.groups; A.h_q = B.h_q; A.h_kv = B.h_kv; A.G = B.h_q / B.h_kv;
+    A.n = B.n; A.b = B.b; A.nodes_prev = B.nodes_prev; A.nleaf = B.nleaf;
+    A.leaf_off = B.leaf_off; A.perm = B.perm; A.n_sink = B.n_sink; A.window = B.window;
+    A.pairs = B.pairs; A.noff = B.noff; A.keep = B.keep; A.amask = B.ws.amask; A.abound = B.ws.abound;
+    A.nbins = (int64_t)B.h_kv * B.nodes_prev;
+    A.T = kNmaCols / A.G;
+    A.toff = B.ws.toff; A.tbin = B.ws.tbin; A.pinf = (u32x4_t *)B.ws.pinf; A.part = B.ws.part;
+    A.scale_log2 = B.scale * 1.4426950408889634f;
+    A.out = (uint16_t *)B.out; A.lse = B.lse;
+    // two resident workgroups per compute unit, each walking its range of tiles
+    const int cus = std::max(device_cus(), 8);
+    const int64_t nwg = std::min<int64_t>(nma_tiles_bound(B.groups, A.G, A.nbins), (int64_t)(cus * 2 + 7) / 8 * 8);
+    hipLaunchKernelGGL(k_nma_scan, dim3(1), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_nma_map, dim3((unsigned)std::min<int64_t>((A.nbins + 255) / 256, 4096)), dim3(256), 0, st,
+                       A);
+    hipLaunchKernelGGL(k_nma_pairs, dim3((unsigned)std::min<int64_t>((B.groups * kNmaP + 255) / 256, 8192)),
+                       dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_nma_merge, dim3((unsigned)B.groups), dim3(256), 0, st, A);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

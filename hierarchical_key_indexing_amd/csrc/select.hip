@@ -471,6 +471,10 @@ struct NmArgs {
     int32_t *ncnt, *noff, *fptr;   // [h_kv * nodes(level - 1) + 1]
     int32_t *pairs;                // [groups * kFastP]: group * kFastP + slot, grouped by node
     int32_t *pnode;                // [groups * kFastP]: the node of each entry of pairs
+    // taken leaves, for the node-major attention (NULL when none follows):
+    uint64_t *amask;               // [groups][kFastP]: bit c = child c of kept node j gave keys
+    int32_t *abound;               // [groups][2]: slot j * 64 + c of the leaf taken in part (-1: none)
+                                   // and the last key taken from it
 };
 
 // kTopRows rows of one KV head per workgroup: W_g is staged once for them,
@@ -833,12 +837,15 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     __shared__ __attribute__((aligned(16))) uint64_t sk[1024];
     __shared__ int scratch[8];
     __shared__ float cut_s;
+    __shared__ unsigned long long msk_s[kFastP];
+    __shared__ int32_t bnd_s[2];
     const SelectArgs &A = N.S;
     const int64_t grp = blockIdx.x;
     const int64_t i = N.row0 + grp / A.h_kv;
     const int g = (int)(grp % A.h_kv);
     const int tid = threadIdx.x;
-    if (tid == 0) cut_s = -INFINITY;
+    if (tid == 0) { cut_s = -INFINITY; bnd_s[0] = -1; bnd_s[1] = 0; }
+    if (tid < kFastP) msk_s[tid] = 0ull;
     uint64_t k4[KPT];
     nm_load_keys<KPT>(N, grp, k4, KPT == 2);
     block_sort_desc<KPT>(k4, sk);
@@ -864,6 +871,17 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
         if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
         off += e4[ii];
     }
+    if (N.amask) {
+        // the taken leaves per kept node, and the one leaf (if any) whose
+        // eligible members are taken only in part: its last taken key
+#pragma unroll
+        for (int ii = 0; ii < KPT; ++ii) {
+            if (take[ii] <= 0) continue;
+            const int slot = (int)(k4[ii] & 1023u);
+            atomicOr(&msk_s[slot >> 6], 1ull << (slot & 63));
+            if (take[ii] < e4[ii]) { bnd_s[0] = slot; bnd_s[1] = pm[a0v[ii] + take[ii] - 1]; }
+        }
+    }
     fill_members<KPT, 8>(pm, out, take, a0v, offv);
     const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
@@ -872,6 +890,10 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     if (tid == 0) {
         A.sel_count[(size_t)i * A.h_kv + g] = count + as.nloc;
         if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
+    }
+    if (N.amask) {
+        if (tid < kFastP) N.amask[grp * kFastP + tid] = msk_s[tid];
+        if (tid < 2) N.abound[grp * 2 + tid] = bnd_s[tid];
     }
 }
 
@@ -906,18 +928,34 @@ bool nm_shape_ok(int r, int b, int L, int beam, int d, const int64_t *nodes) {
     return r == kFastR && b <= 64 && beam <= kFastP && L >= 2 && d <= 256 && nodes[L] <= ((int64_t)1 << 22);
 }
 
-int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes) {
-    return (int64_t)carve_nm_ws(nullptr, std::max<int64_t>(1, std::min(m, kNmRows)) * h_kv, h_kv, nodes[L - 1]).bytes;
+// Workspace bytes of one batch: the selection's buffers, then (G > 0) those
+// of the node-major attention that follows it.
+static int64_t nm_batch_bytes(int64_t groups, int h_kv, int L, const int64_t *nodes, int G) {
+    const int64_t sel = (int64_t)carve_nm_ws(nullptr, groups, h_kv, nodes[L - 1]).bytes;
+    return G > 0 ? sel + (int64_t)carve_nma_ws(nullptr, groups, G, (int64_t)h_kv * nodes[L - 1]).bytes : sel;
 }
 
-static int64_t nm_batch_rows(int64_t m, int h_kv, int L, const int64_t *nodes, int64_t ws_bytes) {
+int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes) {
+    return nm_batch_bytes(std::max<int64_t>(1, std::min(m, kNmRows)) * h_kv, h_kv, L, nodes, 0);
+}
+
+int64_t nm_attend_workspace_bytes(int64_t m, int h_q, int h_kv, int L, const int64_t *nodes) {
+    return nm_batch_bytes(std::max<int64_t>(1, std::min(m, kNmRows)) * h_kv, h_kv, L, nodes, h_q / h_kv);
+}
+
+static int64_t nm_batch_rows(int64_t m, int h_kv, int L, const int64_t *nodes, int64_t ws_bytes, int G = 0) {
     int64_t mb = std::min(m, kNmRows);
-    while (mb > 0 && (int64_t)carve_nm_ws(nullptr, mb * h_kv, h_kv, nodes[L - 1]).bytes > ws_bytes) mb >>= 1;
+    while (mb > 0 && nm_batch_bytes(mb * h_kv, h_kv, L, nodes, G) > ws_bytes) mb >>= 1;
     return mb;
 }
 
-static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws_bytes, hipStream_t st) {
-    const int64_t mb = nm_batch_rows(A.m, A.h_kv, A.L, A.nodes, ws_bytes);
+// What the node-major attention after each batch needs besides the selection.
+struct NmAttendReq { const void *K, *V; float scale; void *out; float *lse; };
+
+static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws_bytes, hipStream_t st,
+                            const NmAttendReq *att = nullptr) {
+    const int G = att ? A.h_q / A.h_kv : 0;
+    const int64_t mb = nm_batch_rows(A.m, A.h_kv, A.L, A.nodes, ws_bytes, G);
     if (mb < 1) return hipErrorInvalidValue;
     for (int64_t r0 = 0; r0 < A.m; r0 += mb) {
         const int64_t nb = std::min(mb, A.m - r0);
@@ -927,6 +965,12 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         N.S = A; N.row0 = r0; N.groups = groups;
         N.U = w.U; N.kept = w.kept; N.keep = w.keep; N.keys = w.keys; N.eli = w.eli; N.lof = w.lof;
         N.ncnt = w.ncnt; N.noff = w.noff; N.fptr = w.fptr; N.pairs = w.pairs; N.pnode = w.pnode;
+        NmaWs aw{};
+        if (att) {
+            aw = carve_nma_ws((char *)ws + w.bytes, groups, G, (int64_t)A.h_kv * A.nodes[A.L - 1]);
+            N.amask = aw.amask;
+            N.abound = aw.abound;
+        }
         const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
         if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
         else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
@@ -948,8 +992,45 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (att) {
+            // the leaf level's pairs (grouped by kept level-(L-1) node) and the
+            // finish's taken-leaf masks drive the attention of this batch
+            NmaBatch B{};
+            B.Q = A.Q; B.K = att->K; B.V = att->V; B.q_pos = A.q_pos; B.row0 = r0; B.groups = groups;
+            B.h_q = A.h_q; B.h_kv = A.h_kv; B.n = A.n; B.b = A.b;
+            B.nodes_prev = A.nodes[A.L - 1]; B.nleaf = A.nodes[A.L];
+            B.leaf_off = (const int32_t *)(A.index + A.leaf_off_off);
+            B.perm = (const int32_t *)(A.index + A.perm_off);
+            B.n_sink = A.n_sink; B.window = A.window;
+            B.pairs = w.pairs; B.noff = w.noff; B.keep = w.keep;
+            B.ws = aw; B.scale = att->scale; B.out = att->out; B.lse = att->lse;
+            if ((e = nm_attend_batch(B, st)) != hipSuccess) return e;
+        }
     }
     return hipSuccess;
+}
+
+hipError_t select_attend_nm(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
+                            const int32_t *q_pos, const char *index, int64_t n, int h_kv, int r, int b, int L,
+                            const int64_t *nodes, const int64_t *centroid_off, const int64_t *count_off,
+                            int64_t leaf_off_off, int64_t perm_off, const float *W, int beam, int k, int n_sink,
+                            int window, int32_t *sel, int32_t *sel_count, float *sel_cutoff, float scale, void *out,
+                            float *lse, void *ws, int64_t ws_bytes, hipStream_t st) {
+    SelectArgs A{};
+    A.Q = Q; A.m = m; A.h_q = h_q; A.h_kv = h_kv; A.d = d; A.q_pos = q_pos; A.index = index; A.n = n;
+    A.r = r; A.b = b; A.L = L;
+    for (int l = 0; l <= L; ++l) { A.nodes[l] = nodes[l]; A.centroid_off[l] = centroid_off[l]; A.count_off[l] = count_off[l]; }
+    A.leaf_off_off = leaf_off_off; A.perm_off = perm_off; A.W = W; A.beam = beam; A.k = k;
+    A.n_sink = n_sink; A.window = window; A.row = k + n_sink + window;
+    A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
+    const NmAttendReq att{K, V, scale, out, lse};
+    return select_nm(A, dtype, ws, ws_bytes, st, &att);
+}
+
+// The node-major attention runs when the shapes allow and a batch of at least
+// one row fits the workspace.
+bool nm_attend_fits(int64_t m, int h_q, int h_kv, int L, const int64_t *nodes, int64_t ws_bytes) {
+    return nm_batch_rows(m, h_kv, L, nodes, ws_bytes, h_q / h_kv) >= 1;
 }
 
 hipError_t select_keys(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_t *q_pos, const char *index,
