@@ -31,6 +31,12 @@ import os
 import sys
 import time
 
+# The oracle's idle OpenMP workers sleep instead of spinning, so that its CPU
+# time over its wall time is the parallelism it actually uses (read when the
+# oracle's OpenMP runtime starts).
+os.environ.setdefault("OMP_WAIT_POLICY", "PASSIVE")
+
+FLUSH_BYTES = 512 << 20       # write that evicts the L2s and the last-level cache
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 LAYER_SEED_STRIDE = 10007
@@ -90,9 +96,24 @@ def attend_bytes(w, m, counts):
             + int(counts.sum()) * (4 + 2 * w.d * eb))  # sel ids + gathered K and V rows
 
 
-def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s):
+def host_cpu():
+    """The host's CPU model and logical CPU count."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s, prefill=None):
     """The oracle (as it is) on the host: select + attend of one decode layer on
-    the GPU-built index, repeated for about budget_s seconds."""
+    the GPU-built index, repeated for about budget_s seconds; with `prefill`
+    (query rows, positions) also select + attend of those rows.  `cores` is the
+    parallelism the oracle actually reached: its CPU time over its wall time."""
     import numpy as np
     import torch
     import oracle
@@ -107,7 +128,7 @@ def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s):
     Qh = Q.float().cpu().numpy()
     Wh = W.cpu().numpy()
     ph = pos.cpu().numpy()
-    reps, t0 = 0, time.perf_counter()
+    reps, t0, c0 = 0, time.perf_counter(), os.times()
     while True:
         ref = oracle.select(Qh, ph, oix, Wh, w.beam, w.k)
         oracle.attend(Qh, Kh, Vh, ref["sel"], ref["count"])
@@ -115,9 +136,29 @@ def cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, budget_s):
         el = time.perf_counter() - t0
         if (el >= budget_s and reps >= 3) or reps >= 100000:
             break
-    return dict(value=el / reps * 1e6, unit="us/layer", cores=oracle.threads(), kind="oracle",
-                sample=f"{reps} decode layers (select + attend of 1 query row x {w.h_q} heads over the "
-                       f"{desc.n}-key index built on the GPU), identical inputs, {el:.1f} s total")
+    c1 = os.times()
+    used = ((c1.user - c0.user) + (c1.system - c0.system)) / el
+    model, ncpu = host_cpu()
+    res = dict(value=el / reps * 1e6, unit="us/layer", cores=round(used, 1), kind="oracle",
+               threads_available=oracle.threads(), nproc=ncpu, cpu_model=model,
+               sample=f"{reps} decode layers (select + attend of 1 query row x {w.h_q} heads over the "
+                      f"{desc.n}-key index built on the GPU), identical inputs, {el:.1f} s total; "
+                      f"cores = CPU time / wall time of that loop with idle OpenMP workers sleeping (the select "
+                      f"parallelises over the {w.h_kv} (row, KV head) groups, the attention over the {w.h_q} heads)")
+    if prefill is not None:
+        Qp, pp = prefill
+        Qph, pph = Qp.float().cpu().numpy(), pp.cpu().numpy()
+        t0, c0 = time.perf_counter(), os.times()
+        ref = oracle.select(Qph, pph, oix, Wh, w.beam, w.k)
+        oracle.attend(Qph, Kh, Vh, ref["sel"], ref["count"])
+        el = time.perf_counter() - t0
+        c1 = os.times()
+        res["prefill"] = {"queries_per_s": round(Qph.shape[0] / el, 2), "rows": int(Qph.shape[0]),
+                          "seconds": round(el, 3),
+                          "cores": round(((c1.user - c0.user) + (c1.system - c0.system)) / el, 1),
+                          "sample": f"select + attend of {Qph.shape[0]} rows of the last 4096-position chunk "
+                                    f"(rows spread over the chunk), same index"}
+    return res
 
 
 def _events(torch, n):
@@ -171,12 +212,37 @@ def extra_decode(lsa, synth, torch, np, dev, w, reps=25, per_graph=8):
     e[1].record()
     torch.cuda.synchronize()
     us = e[0].elapsed_time(e[1]) * 1e3 / (reps * per_graph)
+    # cold: the layer after a 512 MiB write (a fill kernel) that evicts the L2
+    # and last-level caches; graph [flush, layer] x R minus graph [flush] x R
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    R = 20
+    gc, gf = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gc):
+        for _ in range(R):
+            flush.fill_(1.0)
+            step()
+    with torch.cuda.graph(gf):
+        for _ in range(R):
+            flush.fill_(1.0)
+    gc.replay(); gf.replay()
+    torch.cuda.synchronize()
+    tc, tf = [], []
+    for _ in range(5):
+        e = _events(torch, 3)
+        e[0].record(); gc.replay(); e[1].record(); gf.replay(); e[2].record()
+        torch.cuda.synchronize()
+        tc.append(e[0].elapsed_time(e[1])); tf.append(e[1].elapsed_time(e[2]))
+    cold_us = (float(np.median(tc)) - float(np.median(tf))) * 1e3 / R
+    del gc, gf, flush
     c = cnt.cpu().numpy()
     ab = select_bytes(w, m, c, w.beam * w.b) + attend_bytes(w, m, c)
-    return {"us_per_layer_warm": round(us, 3), "build_ms": round(build_ms, 3), "mean_sel_count": float(c.mean()),
-            "algorithmic_bytes": int(ab), "achieved_GBps": round(ab / (us * 1e-6) / 1e9, 2),
+    return {"us_per_layer_cold": round(cold_us, 3), "us_per_layer_warm": round(us, 3), "build_ms": round(build_ms, 3),
+            "mean_sel_count": float(c.mean()),
+            "algorithmic_bytes": int(ab), "achieved_GBps_cold": round(ab / (cold_us * 1e-6) / 1e9, 2),
             "index_bytes": int(desc.bytes), "kv_bytes": int(2 * K.numel() * K.element_size()),
-            "timing": f"one layer replayed {per_graph} times per graph, {reps} graphs (cache-resident)"}
+            "timing": f"warm: one layer replayed {per_graph} times per graph, {reps} graphs (cache-resident); "
+                      f"cold: a graph of {R} x [512 MiB cache-evicting write, layer] minus a graph of {R} writes, "
+                      "median of 5"}
 
 
 def extra_train(lsa, synth, torch, np, dev, w, reps=3):
@@ -586,6 +652,12 @@ def main():
             if wdone >= args.warmup:
                 break
     torch.cuda.synchronize()
+    # every timed layer starts cold: a 512 MiB write (a fill kernel) evicts the
+    # L2 and last-level caches first
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush.fill_(1.0)
+    torch.cuda.synchronize()
+    del flush
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in blocks]
     log("timed", K_, "steps in", len(blocks), "launches over", NL, "distinct layers")
     torch.cuda.synchronize()
@@ -638,6 +710,7 @@ def main():
                  "mean_sel_count": float(np.mean([c.mean() for c in lay_counts])),
                  "index_bytes": int(desc.bytes), "kv_bytes": int(2 * K.numel() * K.element_size())}
 
+    prefill_rows = None
     # ---- secondary: last-chunk prefill on the same cache (4096 queries)
     if not args.no_prefill and w.mode == "decode" and w.n >= 4096:
         wp = synth.WORKLOADS.get("prefill_1m") if w.name == "decode_1m" else w.replace(m=4096, mode="chunk")
@@ -717,6 +790,9 @@ def main():
             "timing": "chunk step = one fused select_attend (node-major selection and attention): events around 5 "
                       "eager calls; graph: 5 replays of the captured step; two_calls: lsa_select then lsa_attend, "
                       "5 eager calls each"}
+        # 16 rows spread over the chunk for the oracle's prefill figure
+        ridx = torch.linspace(0, mp - 1, 16, device=dev).long()
+        prefill_rows = (Qp[ridx].clone(), ppos[ridx].clone())
         del Qp, psel, pcnt, pout, pws, psws, pfws
 
     if not args.no_extra:
@@ -732,7 +808,10 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("cpu baseline")
-        cpu = cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, args.cpu_seconds)
+        pre = None
+        if prefill_rows is not None:
+            pre = prefill_rows
+        cpu = cpu_baseline(w, K, V, W, Q, pos, index, desc, lsa, args.cpu_seconds, prefill=pre)
 
     # ---- secondary workloads on their own caches: decode at 10M tokens, a
     # training-shaped causal layer at 128k tokens
@@ -758,8 +837,11 @@ def main():
                    "L": w.L, "beam": w.beam, "k": w.k, "query_rows": m,
                    "step": "lsa_select_attend (select + attend, one launch), index resident",
                    "layers": NL,
-                   "timing": f"{NL} distinct decode layers (own K/V cache, index, query each) back to back in one "
-                             "HIP graph; time per layer",
+                   "timing": (f"{K_} steps = {nfull} replays of one HIP graph of the {NL} distinct decode layers "
+                              f"(own K/V cache, index and query each; {NL} x ~6 MB exceeds the 256 MB last-level "
+                              f"cache)" + (f" + one graph of layers 0..{rem - 1}" if rem else "") +
+                              ", after a 512 MiB cache-evicting write; time per layer")
+                             if use_graph else f"{K_} eager layer launches over {NL} distinct layers",
                    "indexer_arith": "f64 accumulate", "attention_arith": "f32 accumulate"},
         "roofline": roofline,
         "cpu_baseline": cpu,
