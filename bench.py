@@ -508,6 +508,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 10M decode and 128k training-layer figures")
     ap.add_argument("--layers", type=int, default=48,
                     help="distinct decode layers (each its own cache, index and query) run in sequence")
+    ap.add_argument("--extras", default="sinks,flat,insert,pca,decode10m,train",
+                    help="secondary figures to run (comma list of sinks, flat, insert, pca, decode10m, train)")
+    ap.add_argument("--calibrate-gather", action="store_true",
+                    help="first gather 1048576 random 256-byte rows of a 1 GiB tensor (index_select): "
+                         "256 MiB read at random and 256 MiB written, to scale counters of gather kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for hardware byte counters")
     args = ap.parse_args()
@@ -534,6 +539,14 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.calibrate_gather:
+        src = torch.ones((4 << 20, 64), dtype=torch.float32, device=dev)          # 4 Mi rows of 256 bytes
+        idx = torch.randperm(4 << 20, device=dev)[: 1 << 20]
+        for _ in range(3):
+            torch.index_select(src, 0, idx)
+        torch.cuda.synchronize()
+        del src, idx
+    extras = set(x for x in args.extras.split(",") if x)
     w = synth.WORKLOADS[args.workload]
     m = int(w.positions().shape[0])
     G = w.h_q // w.h_kv
@@ -796,14 +809,18 @@ def main():
         del Qp, psel, pcnt, pout, pws, psws, pfws
 
     if not args.no_extra:
-        log("sinks and window")
-        breakdown["sinks_window"] = local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc)
-        log("flat search")
-        breakdown["flat_search"] = flat_figures(lsa, torch, np, dev, w, layers[0], pos, desc)
-        log("insertion")
-        breakdown["index_insert"] = insert_figures(lsa, torch, np, dev, w, layers[0])
-        log("pca")
-        breakdown["pca_projection"] = pca_figures(lsa, torch, np, dev, w, layers[0])
+        if "sinks" in extras:
+            log("sinks and window")
+            breakdown["sinks_window"] = local_keys_figures(lsa, torch, np, dev, w, layers, pos, desc)
+        if "flat" in extras:
+            log("flat search")
+            breakdown["flat_search"] = flat_figures(lsa, torch, np, dev, w, layers[0], pos, desc)
+        if "insert" in extras:
+            log("insertion")
+            breakdown["index_insert"] = insert_figures(lsa, torch, np, dev, w, layers[0])
+        if "pca" in extras:
+            log("pca")
+            breakdown["pca_projection"] = pca_figures(lsa, torch, np, dev, w, layers[0])
 
     cpu = None
     if not args.no_cpu:
@@ -819,12 +836,14 @@ def main():
         del layers, L0, K, V, W, Q, index, fws, sws, aws, sel, cnt, cut, out, lse
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        log("decode_10m")
-        breakdown["decode_10m"] = extra_decode(lsa, synth, torch, np, dev, synth.WORKLOADS["decode_10m"])
-        torch.cuda.empty_cache()
-        log("train_128k")
-        breakdown["train_128k"] = extra_train(lsa, synth, torch, np, dev, synth.WORKLOADS["train_128k"])
-        torch.cuda.empty_cache()
+        if "decode10m" in extras:
+            log("decode_10m")
+            breakdown["decode_10m"] = extra_decode(lsa, synth, torch, np, dev, synth.WORKLOADS["decode_10m"])
+            torch.cuda.empty_cache()
+        if "train" in extras:
+            log("train_128k")
+            breakdown["train_128k"] = extra_train(lsa, synth, torch, np, dev, synth.WORKLOADS["train_128k"])
+            torch.cuda.empty_cache()
 
     res = {
         "metric": "µs/layer decode and queries/s last-chunk prefill at 1M/10M ctx; % HBM/MFMA peak",

@@ -15,9 +15,10 @@
 // columns per wave).  A column only sees the keys its row retrieved from that
 // node: the children whose leaves it took (a 64-bit mask from the selection's
 // finish), inside its retrieval range, and for the one leaf taken in part,
-// up to the last key taken.  Each column writes an unnormalised partial state
-// (output, base-2 max, sum); a merge kernel combines a group's states by
-// log-sum-exp.  Prefill, which computes in bulk, is where this pays (same
+// up to the last key taken.  Each column writes a partial state (its output
+// divided by its sum as 16-bit fixed point under a power-of-two scale of its
+// own, and the base-2 max and sum in fp32); a merge kernel combines a group's
+// states by log-sum-exp.  Prefill, which computes in bulk, is where this pays (same
 // page, section "The Accuracy-Efficiency Dilemma of Sparse Attention").
 #include <algorithm>
 
@@ -59,7 +60,8 @@ struct NmaArgs {
     int32_t *toff;              // [nbins + 1]: tiles before each bin
     int32_t *tbin;              // [tiles]: the bin of each tile
     u32x4_t *pinf;              // [pairs][2]: pair records in bin order (k_nma_pairs)
-    float *part;                // [groups][kNmaP][G][128 + 2]
+    int16_t *po;                // [groups][kNmaP][G][128]: o / l times 2^sh, rounded
+    floatx4_t *pml;             // [groups][kNmaP][G]: {m (base 2), l, 2^-sh, 0}
     float scale_log2;
     uint16_t *out;              // bf16 [m][h_q][128]
     float *lse;                 // [m][h_q] or NULL
@@ -425,16 +427,48 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
                 }
             }
         }
-        // partial states: unnormalised outputs, base-2 max and sum per column
+        // partial states.  A column's output o / l is stored as 16-bit
+        // integers after a scaling by 2^sh that brings its largest magnitude
+        // into [2^14, 2^15): an absolute error of at most 2^-16 of the
+        // power of two above that magnitude, whatever V holds.  A column with
+        // no key stores m = -inf, l = 0 and no output.
+        float amax[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) amax[cb] = fmaxf(amax[cb], fabsf(acc[cb][nb][x]));
+            amax[cb] = fmaxf(amax[cb], xor_lane_f<16>(amax[cb]));
+            amax[cb] = fmaxf(amax[cb], xor_lane_f<32>(amax[cb]));
+        }
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             const int col = 32 * w + 16 * cb + c16;
             if (col >= np * G) continue;
             const int32_t e = (int32_t)pi_s[pbuf][pcol[cb]][0].z;
-            float *pp = A.part + ((size_t)e * G + hh[cb]) * (kNmaD + 2);
+            const size_t slot = (size_t)e * G + hh[cb];
+            const float l = l_run[cb];
+            if (!(l > 0.0f)) {
+                if (q == 0) A.pml[slot] = floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
+                continue;
+            }
+            // l >= 1: the largest kept score contributes 2^(its lag behind m) >= 1
+            const float inv_l = 1.0f / l;
+            const int sh = 15 - __builtin_amdgcn_frexp_expf(amax[cb] * inv_l);
+            const float sc = __builtin_ldexpf(inv_l, sh);
+            int16_t *pp = A.po + slot * kNmaD + 4 * q;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<floatx4_t *>(pp + 16 * nb + 4 * q) = acc[cb][nb];
-            if (q == 0) { pp[kNmaD] = m_run[cb]; pp[kNmaD + 1] = l_run[cb]; }
+            for (int nb = 0; nb < 8; ++nb) {
+                // (saturating: a product rounded up to 2^15 stores 2^15 - 1)
+                const auto h01 = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(acc[cb][nb][0] * sc),
+                                                             (int)__builtin_rintf(acc[cb][nb][1] * sc));
+                const auto h23 = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(acc[cb][nb][2] * sc),
+                                                             (int)__builtin_rintf(acc[cb][nb][3] * sc));
+                *reinterpret_cast<uint2 *>(pp + 16 * nb) =
+                    uint2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+            }
+            if (q == 0) A.pml[slot] = floatx4_t{m_run[cb], l, __builtin_ldexpf(1.0f, -sh), 0.0f};
         }
         if (!has_next) break;
         // the next tile: its records into the other buffer; a new node is
@@ -461,42 +495,48 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
     }
 }
 
-// One workgroup per group: M = max m_j, l = sum l_j 2^(m_j - M),
-// o = sum o_j 2^(m_j - M) / l over the group's kept nodes j.
+// Merge: M = max m_j, l = sum l_j 2^(m_j - M), o = sum (o_j / l_j) l_j
+// 2^(m_j - M) / l over the group's kept nodes j.  Thread = (group, head,
+// 8-dim chunk): 16 threads a head, 256 / (16 G) groups a workgroup.
 __global__ __launch_bounds__(256) void k_nma_merge(NmaArgs A) {
-    __shared__ float ml_s[kNmaP][2][16];
-    const int64_t grp = blockIdx.x;
-    const int64_t i = A.row0 + grp / A.h_kv;
-    const int g = (int)(grp % A.h_kv);
-    const int G = A.G, P = A.keep[grp];
-    const float *pb = A.part + (size_t)grp * kNmaP * G * (kNmaD + 2);
-    for (int e = threadIdx.x; e < P * G; e += blockDim.x) {
-        const float *pp = pb + (size_t)e * (kNmaD + 2);
-        ml_s[e / G][0][e % G] = pp[kNmaD];
-        ml_s[e / G][1][e % G] = pp[kNmaD + 1];
-    }
-    __syncthreads();
-    for (int c4 = threadIdx.x; c4 < G * kNmaD / 4; c4 += blockDim.x) {
-        const int h = c4 / (kNmaD / 4), dd = 4 * (c4 % (kNmaD / 4));
-        float M = -INFINITY;
-        for (int j = 0; j < P; ++j) M = fmaxf(M, ml_s[j][0][h]);
-        float l = 0.0f;
-        floatx4_t o = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < P; ++j) {
-            const float mj = ml_s[j][0][h];
-            if (mj == -INFINITY) continue;
-            const float wgt = __builtin_amdgcn_exp2f(mj - M);
-            l += ml_s[j][1][h] * wgt;
-            const float *pp = pb + ((size_t)j * G + h) * (kNmaD + 2) + dd;
-            o += floatx4_t{pp[0], pp[1], pp[2], pp[3]} * wgt;
-        }
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
-        uint16_t *op = A.out + oh * kNmaD + dd;
+    const int G = A.G, per = 16 * G, gpw = 256 / per;
+    const int tid = threadIdx.x;
+    const int64_t grp = (int64_t)blockIdx.x * gpw + tid / per;
+    if (tid >= gpw * per || grp >= A.groups) return;
+    const int h = (tid % per) / 16, dd = 8 * (tid % 16);
+    const int P = A.keep[grp];
+    const floatx4_t *rec = A.pml + (size_t)grp * kNmaP * G + h;
+    const int16_t *po = A.po + ((size_t)grp * kNmaP * G + h) * kNmaD + dd;
+    typedef int16_t h8_t __attribute__((ext_vector_type(8)));
+    floatx4_t r[kNmaP];
+    h8_t v[kNmaP];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) op[x] = from_float<bf16_t>(o[x] * inv).bits;
-        if (dd == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    for (int j = 0; j < kNmaP; ++j) {
+        r[j] = j < P ? rec[(size_t)j * G] : floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
+        if (j < P && r[j][0] != -INFINITY) v[j] = *reinterpret_cast<const h8_t *>(po + (size_t)j * G * kNmaD);
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kNmaP; ++j) M = fmaxf(M, r[j][0]);
+    float l = 0.0f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kNmaP; ++j) {
+        if (r[j][0] == -INFINITY) continue;
+        const float wl = r[j][1] * __builtin_amdgcn_exp2f(r[j][0] - M);
+        l += wl;
+        const float wgt = wl * r[j][2];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[x] = fmaf((float)v[j][x], wgt, o[x]);
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const size_t oh = (size_t)(A.row0 + grp / A.h_kv) * A.h_q + (size_t)(grp % A.h_kv) * G + h;
+    uint32_t pk[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        pk[x] = (uint32_t)from_float<bf16_t>(o[2 * x] * inv).bits |
+                ((uint32_t)from_float<bf16_t>(o[2 * x + 1] * inv).bits << 16);
+    *reinterpret_cast<uint4 *>(A.out + oh * kNmaD + dd) = uint4{pk[0], pk[1], pk[2], pk[3]};
+    if (dd == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------- host side
@@ -524,7 +564,8 @@ NmaWs carve_nma_ws(char *base, int64_t groups, int G, int64_t nbins) {
     w.toff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
     w.tbin = (int32_t *)take(sizeof(int32_t) * nma_tiles_bound(groups, G, nbins));
     w.pinf = take(32 * (size_t)groups * kNmaP);
-    w.part = (float *)take(sizeof(float) * groups * kNmaP * G * (kNmaD + 2));
+    w.po = take(sizeof(int16_t) * groups * kNmaP * G * kNmaD);
+    w.pml = (float *)take(sizeof(floatx4_t) * groups * kNmaP * G);
     w.bytes = cur;
     return w;
 }
@@ -538,7 +579,8 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     A.pairs = B.pairs; A.noff = B.noff; A.keep = B.keep; A.amask = B.ws.amask; A.abound = B.ws.abound;
     A.nbins = (int64_t)B.h_kv * B.nodes_prev;
     A.T = kNmaCols / A.G;
-    A.toff = B.ws.toff; A.tbin = B.ws.tbin; A.pinf = (u32x4_t *)B.ws.pinf; A.part = B.ws.part;
+    A.toff = B.ws.toff; A.tbin = B.ws.tbin; A.pinf = (u32x4_t *)B.ws.pinf;
+    A.po = (int16_t *)B.ws.po; A.pml = (floatx4_t *)B.ws.pml;
     A.scale_log2 = B.scale * 1.4426950408889634f;
     A.out = (uint16_t *)B.out; A.lse = B.lse;
     // two resident workgroups per compute unit, each walking its range of tiles
@@ -550,7 +592,8 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     hipLaunchKernelGGL(k_nma_pairs, dim3((unsigned)std::min<int64_t>((B.groups * kNmaP + 255) / 256, 8192)),
                        dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(256), 0, st, A);
-    hipLaunchKernelGGL(k_nma_merge, dim3((unsigned)B.groups), dim3(256), 0, st, A);
+    const int64_t gpw = 256 / (16 * A.G);
+    hipLaunchKernelGGL(k_nma_merge, dim3((unsigned)((B.groups + gpw - 1) / gpw)), dim3(256), 0, st, A);
     return hipGetLastError();
 }
 
