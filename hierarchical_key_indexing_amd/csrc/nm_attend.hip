@@ -32,6 +32,9 @@ constexpr int kNmaP = 16;       // kept-node slots per group (the throughput pat
 constexpr int kNmaD = 128;      // head dimension of this path
 constexpr int kNmaKC = 64;      // keys staged per step
 constexpr int kNmaCols = 128;   // (pair, head) columns per tile: 32 per wave
+constexpr int kNmaMaxWg = 4096;  // attention workgroups at most
+constexpr int kNmaThreads = 256;
+constexpr int kNmaTd = 512;      // tile descriptors staged in LDS at a time// threads of the attention workgroup (four waves)
 constexpr int kKst = kNmaD + 8; // K tile row stride (bf16)
 constexpr int kVst = kNmaKC + 8;// V^T tile row stride (bf16)
 constexpr float kLazy = 8.0f;   // log2 headroom of the lazily moved running max
@@ -58,54 +61,92 @@ struct NmaArgs {
     int64_t nbins;
     int T;                      // pairs per tile (128 / G)
     int32_t *toff;              // [nbins + 1]: tiles before each bin
-    int32_t *tbin;              // [tiles]: the bin of each tile
+    int32_t *coff;              // [nbins + 1]: estimated cost before each bin
+    int32_t *wr;                // [nwg + 1]: first tile of each workgroup's share
+    int64_t nwg;                // attention workgroups (a multiple of 8)
+    int4 *tdesc;                // [tiles]: bin, first pair, pairs of each tile
     u32x4_t *pinf;              // [pairs][2]: pair records in bin order (k_nma_pairs)
-    int16_t *po;                // [groups][kNmaP][G][128]: o / l times 2^sh, rounded
-    floatx4_t *pml;             // [groups][kNmaP][G]: {m (base 2), l, 2^-sh, 0}
+    int16_t *po;                // [groups][kNmaP][G][128]: o / l in units of u, rounded
+    floatx4_t *pml;             // [groups][kNmaP][G]: {m (base 2), l, u, 0}
     float scale_log2;
     uint16_t *out;              // bf16 [m][h_q][128]
     float *lse;                 // [m][h_q] or NULL
 };
 
-// tiles per bin, exclusive scan (one workgroup; total at toff[nbins])
+// Estimated cost of one tile of bin e: the tile itself plus one unit per
+// step of 64 of the node's members.
+LSA_DEV int nma_tile_cost(const NmaArgs &A, int64_t e) {
+    const int g = (int)(e / A.nodes_prev);
+    const int64_t v = e % A.nodes_prev;
+    const int32_t *lof = A.leaf_off + (size_t)g * (A.nleaf + 1) + (size_t)v * A.b;
+    return 1 + (lof[A.b] - lof[0] + kNmaKC - 1) / kNmaKC;
+}
+
+// One workgroup: tiles per bin and their estimated cost (two units more a
+// bin, for staging its node), exclusive scans (totals at [nbins]); then the
+// tile list is cut into nwg shares of equal estimated cost, wr[r] the first
+// tile of share r.
 __global__ __launch_bounds__(256) void k_nma_scan(NmaArgs A) {
     __shared__ int scr[8];
-    int carry = 0;
+    int carry = 0, ccarry = 0;
     for (int64_t base = 0; base < A.nbins; base += 256 * 8) {
-        int v[8], s = 0;
+        int v[8], c[8], s = 0, cs = 0;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
             v[u] = e < A.nbins ? (A.noff[e + 1] - A.noff[e] + A.T - 1) / A.T : 0;
+            c[u] = v[u] > 0 ? v[u] * nma_tile_cost(A, e) + 2 : 0;
             s += v[u];
+            cs += c[u];
         }
-        int tot;
+        int tot, ctot;
         int run = carry + block_excl_scan(s, scr, &tot);
+        int crun = ccarry + block_excl_scan(cs, scr, &ctot);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
-            if (e < A.nbins) A.toff[e] = run;
+            if (e < A.nbins) { A.toff[e] = run; A.coff[e] = crun; }
             run += v[u];
+            crun += c[u];
         }
         carry += tot;
+        ccarry += ctot;
     }
-    if (threadIdx.x == 0) A.toff[A.nbins] = carry;
+    if (threadIdx.x == 0) { A.toff[A.nbins] = carry; A.coff[A.nbins] = ccarry; }
+    __syncthreads();
+    for (int64_t r = threadIdx.x; r <= A.nwg; r += blockDim.x) {
+        if (r == A.nwg) { A.wr[r] = carry; continue; }
+        const int64_t target = r * (int64_t)ccarry / A.nwg;
+        int64_t lo = 0, hi = A.nbins - 1;          // the last bin starting at or before target
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (A.coff[mid] <= target) lo = mid; else hi = mid - 1;
+        }
+        const int tiles = A.toff[lo + 1] - A.toff[lo];
+        const int64_t k = max<int64_t>(0, target - A.coff[lo] - 2) / nma_tile_cost(A, lo);
+        A.wr[r] = A.toff[lo] + (int32_t)min<int64_t>(k, tiles);
+    }
 }
 
+// Tile descriptors: the bin of each tile, its first pair and its pairs.
 __global__ __launch_bounds__(256) void k_nma_map(NmaArgs A) {
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.nbins; e += (int64_t)gridDim.x * blockDim.x)
-        for (int t = A.toff[e]; t < A.toff[e + 1]; ++t) A.tbin[t] = (int32_t)e;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.nbins; e += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t p0 = A.noff[e], p1 = A.noff[e + 1];
+        for (int t = A.toff[e]; t < A.toff[e + 1]; ++t) {
+            const int32_t pb = p0 + (t - A.toff[e]) * A.T;
+            A.tdesc[t] = int4{(int32_t)e, pb, min(A.T, p1 - pb), 0};
+        }
+    }
 }
 
-// Tiles [t0, t1) of workgroup `bid` of `nwg` (a multiple of 8): the tile
-// list, ordered by node, is cut into nwg contiguous ranges, and neighbouring
-// ranges run on one XCD (workgroup i runs on XCD i % 8), so the tiles of one
-// node that follow each other are served by that XCD's L2.
-LSA_DEV void nma_range(int64_t bid, int64_t nwg, int64_t total, int64_t &t0, int64_t &t1) {
-    const int64_t r = (bid % 8) * (nwg / 8) + bid / 8;
-    const int64_t per = (total + nwg - 1) / nwg;
-    t0 = min(total, r * per);
-    t1 = min(total, t0 + per);
+// Tiles [t0, t1) of workgroup `bid`: share r of the tile list, ordered by
+// node, where neighbouring shares run on one XCD (workgroup i runs on XCD
+// i % 8, nwg a multiple of 8), so the tiles of one node that follow each
+// other are served by that XCD's L2.
+LSA_DEV void nma_range(const NmaArgs &A, int64_t bid, int64_t &t0, int64_t &t1) {
+    const int64_t r = (bid % 8) * (A.nwg / 8) + bid / 8;
+    t0 = A.wr[r];
+    t1 = A.wr[r + 1];
 }
 
 // The child of the node whose leaf holds member position `at` (lof: the
@@ -210,39 +251,112 @@ LSA_DEV void nma_pair_masks(int np, const int32_t *ids, const int32_t *chs, cons
     }
 }
 
-// Tile t: its (head, node) bin, first pair and number of pairs.
-LSA_DEV void nma_tile_desc(const NmaArgs &A, int64_t t, int32_t &bin, int64_t &pb, int &np) {
-    bin = A.tbin[t];
-    pb = A.noff[bin] + (t - A.toff[bin]) * (int64_t)A.T;
-    np = (int)min<int64_t>(A.T, A.noff[bin + 1] - pb);
+// Sort the node's cnt staged members (and their children) by key id; the
+// padding entries after them stay in place.  Up to one member a thread:
+// each counts the smaller ids and moves to that rank.  Larger nodes: a
+// bitonic network over the power of two above `span`, padding (child 64)
+// sorting last.
+LSA_DEV void nma_sort_members(int cnt, int span, int32_t pad_id, int32_t *mid_s, int32_t *mch_s) {
+    const int tid = threadIdx.x;
+    if (cnt <= kNmaThreads) {
+        const int32_t my = tid < cnt ? mid_s[tid] : 0, mc = tid < cnt ? mch_s[tid] : 0;
+        int rank = 0;
+        if (tid < cnt) {
+            const int4 *m4 = reinterpret_cast<const int4 *>(mid_s);
+            for (int j = 0; j < cnt; j += 4) {
+                const int4 v = m4[j / 4];
+                rank += (v.x < my) + (j + 1 < cnt && v.y < my) + (j + 2 < cnt && v.z < my) + (j + 3 < cnt && v.w < my);
+            }
+        }
+        __syncthreads();
+        if (tid < cnt) { mid_s[rank] = my; mch_s[rank] = mc; }
+        __syncthreads();
+        return;
+    }
+    int N = kNmaKC;
+    while (N < span) N <<= 1;
+    for (int x = span + tid; x < N; x += kNmaThreads) { mid_s[x] = pad_id; mch_s[x] = 64; }
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < N; i += kNmaThreads) {
+                const int o = i ^ j;
+                if (o > i) {
+                    const int32_t ci = mch_s[i], co = mch_s[o];
+                    const int32_t ki = ci == 64 ? INT32_MAX : mid_s[i], ko = co == 64 ? INT32_MAX : mid_s[o];
+                    if ((ki > ko) == ((i & k) == 0)) {
+                        const int32_t t = mid_s[i];
+                        mid_s[i] = mid_s[o];
+                        mid_s[o] = t;
+                        mch_s[i] = co;
+                        mch_s[o] = ci;
+                    }
+                }
+            }
+            __syncthreads();
+        }
 }
 
 // Stage node `bin`: its leaf offsets, then (when they fit) its members and
-// their children, padded to whole steps; returns the member range.  Ends
-// with the members visible to the workgroup.
-LSA_DEV void nma_stage_node(const NmaArgs &A, int32_t bin, int32_t *lof_s, int32_t *mid_s, int32_t *mch_s,
-                            int32_t &lo, int32_t &hi, bool &fits) {
+// their children, padded to whole steps; returns the member range.  When
+// the first pair of the tile it is staged for (`frhi`: that pair's last
+// visible key) sees at least a whole step less than the node holds (causal
+// rows early in the sequence), the members are sorted by id, so that every
+// tile can stop after the last key its rows reach (`srt`).  Ends with the
+// members visible to the workgroup.
+LSA_DEV void nma_stage_node(const NmaArgs &A, int32_t bin, int32_t frhi, int32_t *lof_s, int32_t *mid_s,
+                            int32_t *mch_s, int32_t &lo, int32_t &hi, bool &fits, bool &srt, int *late_s) {
     const int tid = threadIdx.x, b = A.b;
     const int g = (int)(bin / A.nodes_prev);
     const int64_t v = bin % A.nodes_prev;
     if (tid <= b) lof_s[tid] = A.leaf_off[(size_t)g * (A.nleaf + 1) + (size_t)v * b + tid];
+    if (tid == 0) *late_s = 0;
     __syncthreads();
     lo = lof_s[0];
     hi = lof_s[b];
     const int span = (int)min<int64_t>((int64_t)(hi - lo + kNmaKC - 1) / kNmaKC * kNmaKC, (int64_t)kNmaIds + 1);
     fits = span <= kNmaIds;
+    srt = false;
     if (fits && hi > lo) {
         const int32_t *pm = A.perm + (size_t)g * A.n;
-        for (int x = tid; x < span; x += blockDim.x) {
+        for (int x = tid; x < span; x += kNmaThreads) {    // (span is a multiple of the wave: whole waves take part)
             const int64_t at = (int64_t)lo + x;
-            mid_s[x] = pm[at < hi ? at : hi - 1];
+            const int32_t id = pm[at < hi ? at : hi - 1];
+            mid_s[x] = id;
             mch_s[x] = at < hi ? nma_child(lof_s, b, at) : 64;
+            const uint64_t late = __ballot(at < hi && id > frhi);
+            if (lane_id() == 0 && late) atomicAdd(late_s, __popcll(late));
         }
+        __syncthreads();
+        srt = *late_s >= kNmaKC;
+        if (srt) nma_sort_members(hi - lo, span, pm[hi - 1], mid_s, mch_s);
     }
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
+// The end of the members a tile's pairs can see in a sorted node: past the
+// last id at or below the largest retrieval bound among the pairs (the same
+// in every wave).
+LSA_DEV int32_t nma_tile_end(const u32x4_t (*pi)[2], int np, const int32_t *mid_s, int32_t lo, int32_t hi) {
+    const int lane = lane_id();
+    int32_t r = INT32_MIN;
+    for (int p = lane; p < np; p += kWave) r = max(r, (int32_t)pi[p][1].x);
+    r = max(r, xor_lane_i<1>(r));
+    r = max(r, xor_lane_i<2>(r));
+    r = max(r, xor_lane_i<4>(r));
+    r = max(r, xor_lane_i<8>(r));
+    r = max(r, xor_lane_i<16>(r));
+    r = max(r, xor_lane_i<32>(r));
+    // count the sorted ids <= r (at most kNmaIds = 64 x 16): whole blocks of
+    // 16 by one ballot, then the members of the block the count ends in
+    const int cnt = hi - lo;
+    const int full = __popcll(__ballot(16 * lane + 15 < cnt && mid_s[16 * lane + 15] <= r));
+    const int base = 16 * full;
+    const int part = __popcll(__ballot(lane < 16 && base + lane < cnt && mid_s[base + lane] <= r));
+    return lo + base + part;
+}
+
+__global__ __launch_bounds__(kNmaThreads, 2) void k_nma_attend(NmaArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kNmaKC * kKst];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[kNmaD * kVst];
     __shared__ __attribute__((aligned(16))) int32_t mid_s[kNmaIds];    // the node's members (padded to whole steps)
@@ -252,22 +366,27 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
     __shared__ int32_t lof_s[65];
     __shared__ u32x4_t pi_s[2][kNmaCols][2];                           // pair records: this tile's, the next one's
     __shared__ uint64_t pch_s[kNmaCols];
+    __shared__ int late_s;
+    __shared__ int4 td_s[kNmaTd];                                      // tile descriptors tw .. tw + kNmaTd - 1
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int c16 = lane % 16, q = lane / 16;
     const int G = A.G, b = A.b;
     int64_t t0, t1;
-    nma_range(blockIdx.x, gridDim.x, A.toff[A.nbins], t0, t1);
+    nma_range(A, blockIdx.x, t0, t1);
     if (t0 >= t1) return;                         // (uniform in the workgroup)
 
+    // this workgroup's tile descriptors, kNmaTd at a time, in LDS
+    int64_t tw = t0;
+    for (int x = tid; x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
+    __syncthreads();
     // the first tile: its pair records, its node and its first step's rows
-    int32_t bin;
-    int64_t pb;
-    int np;
-    nma_tile_desc(A, t0, bin, pb, np);
+    int32_t bin = td_s[0].x;
+    int64_t pb = td_s[0].y;
+    int np = td_s[0].z;
     if (tid < np) { pi_s[0][tid][0] = A.pinf[2 * (pb + tid)]; pi_s[0][tid][1] = A.pinf[2 * (pb + tid) + 1]; }
     int32_t lo, hi;
-    bool fits;
-    nma_stage_node(A, bin, lof_s, mid_s, mch_s, lo, hi, fits);
+    bool fits, srt;
+    nma_stage_node(A, bin, (int32_t)A.pinf[2 * pb + 1].x, lof_s, mid_s, mch_s, lo, hi, fits, srt, &late_s);
     u32x4_t kr[4], vr[4];
     {
         const int g = (int)(bin / A.nodes_prev);
@@ -292,11 +411,18 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
         int32_t nbin = 0;
         int64_t npb = 0;
         int nnp = 0;
-        if (has_next) nma_tile_desc(A, t + 1, nbin, npb, nnp);
+        if (has_next) {
+            if (t + 1 - tw == kNmaTd) {           // the next window (every wave is past the last read)
+                tw = t + 1;
+                for (int x = tid; x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
+                __syncthreads();
+            }
+            const int4 d = td_s[t + 1 - tw];
+            nbin = d.x;
+            npb = d.y;
+            nnp = d.z;
+        }
         const bool next_same = has_next && nbin == bin && fits;
-        // the next tile's records, in flight during this tile
-        u32x4_t pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
-        if (has_next && tid < nnp) { pn0 = A.pinf[2 * (npb + tid)]; pn1 = A.pinf[2 * (npb + tid) + 1]; }
         // this lane's two columns (32 w + 16 cb + c16): (pair, head) and the
         // query fragments (zero past the tile)
         bf16x8_t qf[2][4];
@@ -315,6 +441,7 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
                 qf[cb][ks] = ok ? *reinterpret_cast<const bf16x8_t *>(Qr + 32 * ks + 8 * q) : bf16x8_t{};
         }
         const bool wave_on = 32 * w < np * G;     // (uniform in the wave)
+        const int32_t hi_t = srt ? nma_tile_end(pi_s[pbuf], np, mid_s, lo, hi) : hi;
         floatx4_t acc[2][8];
         float m_run[2], l_run[2];
 #pragma unroll
@@ -325,14 +452,14 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
             l_run[cb] = 0.0f;
         }
         int wb = 0;
-        for (int64_t c0 = lo; c0 < hi; c0 += kNmaKC, wb ^= 1) {
+        for (int64_t c0 = lo; c0 < hi_t; c0 += kNmaKC, wb ^= 1) {
             const int32_t *ids = fits ? mid_s + (c0 - lo) : win_s[wb];
             const int32_t *chs = fits ? mch_s + (c0 - lo) : wch_s[wb];
             __syncthreads();                      // the previous step's tiles are read
             nma_store_k(Ks, kr);
             nma_store_v(Vt, vr);
             nma_pair_masks(np, ids, chs, pi_s[pbuf], pch_s);
-            const bool more = c0 + kNmaKC < hi;
+            const bool more = c0 + kNmaKC < hi_t;
             if (more && !fits) nma_load_ids(pm, lof_s, b, c0 + kNmaKC, hi, win_s[wb ^ 1], wch_s[wb ^ 1]);
             __syncthreads();
             // rows in flight while this step is computed: the next step's, or
@@ -427,11 +554,14 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
                 }
             }
         }
+        // the next tile's records, in flight during the partial states
+        u32x4_t pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
+        if (has_next && tid < nnp) { pn0 = A.pinf[2 * (npb + tid)]; pn1 = A.pinf[2 * (npb + tid) + 1]; }
         // partial states.  A column's output o / l is stored as 16-bit
-        // integers after a scaling by 2^sh that brings its largest magnitude
-        // into [2^14, 2^15): an absolute error of at most 2^-16 of the
-        // power of two above that magnitude, whatever V holds.  A column with
-        // no key stores m = -inf, l = 0 and no output.
+        // integers in units of 2^ex / 32767, 2^ex the power of two above its
+        // largest magnitude: an absolute error of at most 2^ex / 65534,
+        // whatever V holds.  A column with no key stores m = -inf, l = 0 and
+        // no output.
         float amax[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
@@ -453,22 +583,21 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
                 if (q == 0) A.pml[slot] = floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
                 continue;
             }
-            // l >= 1: the largest kept score contributes 2^(its lag behind m) >= 1
+            // l >= 1: the largest kept score contributes 2^(its lag behind m) >= 1.
+            // (o / l) 2^-ex lies in (-1, 1); v_cvt_pknorm_i16_f32 stores it
+            // times 32767, rounded and clamped, two values an instruction.
             const float inv_l = 1.0f / l;
-            const int sh = 15 - __builtin_amdgcn_frexp_expf(amax[cb] * inv_l);
-            const float sc = __builtin_ldexpf(inv_l, sh);
+            const int ex = __builtin_amdgcn_frexp_expf(amax[cb] * inv_l);
+            const float sc = __builtin_ldexpf(inv_l, -ex);
             int16_t *pp = A.po + slot * kNmaD + 4 * q;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                // (saturating: a product rounded up to 2^15 stores 2^15 - 1)
-                const auto h01 = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(acc[cb][nb][0] * sc),
-                                                             (int)__builtin_rintf(acc[cb][nb][1] * sc));
-                const auto h23 = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(acc[cb][nb][2] * sc),
-                                                             (int)__builtin_rintf(acc[cb][nb][3] * sc));
+                const auto h01 = __builtin_amdgcn_cvt_pknorm_i16(acc[cb][nb][0] * sc, acc[cb][nb][1] * sc);
+                const auto h23 = __builtin_amdgcn_cvt_pknorm_i16(acc[cb][nb][2] * sc, acc[cb][nb][3] * sc);
                 *reinterpret_cast<uint2 *>(pp + 16 * nb) =
                     uint2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
             }
-            if (q == 0) A.pml[slot] = floatx4_t{m_run[cb], l, __builtin_ldexpf(1.0f, -sh), 0.0f};
+            if (q == 0) A.pml[slot] = floatx4_t{m_run[cb], l, __builtin_ldexpf(1.0f, ex) * (1.0f / 32767.0f), 0.0f};
         }
         if (!has_next) break;
         // the next tile: its records into the other buffer; a new node is
@@ -476,7 +605,8 @@ __global__ __launch_bounds__(256, 2) void k_nma_attend(NmaArgs A) {
         if (tid < nnp) { pi_s[pbuf ^ 1][tid][0] = pn0; pi_s[pbuf ^ 1][tid][1] = pn1; }
         __syncthreads();
         if (!next_same) {
-            nma_stage_node(A, nbin, lof_s, mid_s, mch_s, lo, hi, fits);
+            nma_stage_node(A, nbin, (int32_t)pi_s[pbuf ^ 1][0][1].x, lof_s, mid_s, mch_s, lo, hi, fits, srt,
+                           &late_s);
             const int gn = (int)(nbin / A.nodes_prev);
             const uint16_t *Kn = A.K + (size_t)gn * A.n * kNmaD, *Vn = A.V + (size_t)gn * A.n * kNmaD;
             if (!fits && hi > lo) {
@@ -562,7 +692,9 @@ NmaWs carve_nma_ws(char *base, int64_t groups, int G, int64_t nbins) {
     w.amask = (uint64_t *)take(sizeof(uint64_t) * groups * kNmaP);
     w.abound = (int32_t *)take(sizeof(int32_t) * groups * 2);
     w.toff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
-    w.tbin = (int32_t *)take(sizeof(int32_t) * nma_tiles_bound(groups, G, nbins));
+    w.coff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
+    w.wr = (int32_t *)take(sizeof(int32_t) * (kNmaMaxWg + 1));
+    w.tdesc = (int32_t *)take(sizeof(int4) * nma_tiles_bound(groups, G, nbins));
     w.pinf = take(32 * (size_t)groups * kNmaP);
     w.po = take(sizeof(int16_t) * groups * kNmaP * G * kNmaD);
     w.pml = (float *)take(sizeof(floatx4_t) * groups * kNmaP * G);
@@ -579,19 +711,21 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     A.pairs = B.pairs; A.noff = B.noff; A.keep = B.keep; A.amask = B.ws.amask; A.abound = B.ws.abound;
     A.nbins = (int64_t)B.h_kv * B.nodes_prev;
     A.T = kNmaCols / A.G;
-    A.toff = B.ws.toff; A.tbin = B.ws.tbin; A.pinf = (u32x4_t *)B.ws.pinf;
+    A.toff = B.ws.toff; A.coff = B.ws.coff; A.wr = B.ws.wr; A.tdesc = (int4 *)B.ws.tdesc; A.pinf = (u32x4_t *)B.ws.pinf;
     A.po = (int16_t *)B.ws.po; A.pml = (floatx4_t *)B.ws.pml;
     A.scale_log2 = B.scale * 1.4426950408889634f;
     A.out = (uint16_t *)B.out; A.lse = B.lse;
     // two resident workgroups per compute unit, each walking its range of tiles
     const int cus = std::max(device_cus(), 8);
-    const int64_t nwg = std::min<int64_t>(nma_tiles_bound(B.groups, A.G, A.nbins), (int64_t)(cus * 2 + 7) / 8 * 8);
+    const int64_t nwg = std::min<int64_t>({nma_tiles_bound(B.groups, A.G, A.nbins), (int64_t)(cus * 2 + 7) / 8 * 8,
+                                           (int64_t)kNmaMaxWg});
+    A.nwg = nwg;
     hipLaunchKernelGGL(k_nma_scan, dim3(1), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_map, dim3((unsigned)std::min<int64_t>((A.nbins + 255) / 256, 4096)), dim3(256), 0, st,
                        A);
     hipLaunchKernelGGL(k_nma_pairs, dim3((unsigned)std::min<int64_t>((B.groups * kNmaP + 255) / 256, 8192)),
                        dim3(256), 0, st, A);
-    hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(kNmaThreads), 0, st, A);
     const int64_t gpw = 256 / (16 * A.G);
     hipLaunchKernelGGL(k_nma_merge, dim3((unsigned)((B.groups + gpw - 1) / gpw)), dim3(256), 0, st, A);
     return hipGetLastError();
