@@ -82,20 +82,29 @@ LSA_DEV int nma_tile_cost(const NmaArgs &A, int64_t e) {
     return 1 + (lof[A.b] - lof[0] + kNmaKC - 1) / kNmaKC;
 }
 
-// One workgroup: tiles per bin and their estimated cost (two units more a
-// bin, for staging its node), exclusive scans (totals at [nbins]); then the
-// tile list is cut into nwg shares of equal estimated cost, wr[r] the first
-// tile of share r.
-__global__ __launch_bounds__(256) void k_nma_scan(NmaArgs A) {
-    __shared__ int scr[8];
+// Per bin, in parallel: its tiles and their estimated cost (two units more
+// a bin, for staging its node), into toff and coff before their scan.
+__global__ __launch_bounds__(256) void k_nma_count(NmaArgs A) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.nbins; e += (int64_t)gridDim.x * blockDim.x) {
+        const int v = (A.noff[e + 1] - A.noff[e] + A.T - 1) / A.T;
+        A.toff[e] = v;
+        A.coff[e] = v > 0 ? v * nma_tile_cost(A, e) + 2 : 0;
+    }
+}
+
+// One workgroup of 1024 threads, 16 bins a thread per round: exclusive
+// scans of toff and coff in place (totals at [nbins]).
+constexpr int kNmaScanT = 1024, kNmaScanV = 16;
+__global__ __launch_bounds__(kNmaScanT) void k_nma_scan(NmaArgs A) {
+    __shared__ int scr[kNmaScanT / kWave + 1];
     int carry = 0, ccarry = 0;
-    for (int64_t base = 0; base < A.nbins; base += 256 * 8) {
-        int v[8], c[8], s = 0, cs = 0;
+    for (int64_t base = 0; base < A.nbins; base += (int64_t)kNmaScanT * kNmaScanV) {
+        int v[kNmaScanV], c[kNmaScanV], s = 0, cs = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
-            v[u] = e < A.nbins ? (A.noff[e + 1] - A.noff[e] + A.T - 1) / A.T : 0;
-            c[u] = v[u] > 0 ? v[u] * nma_tile_cost(A, e) + 2 : 0;
+        for (int u = 0; u < kNmaScanV; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * kNmaScanV + u;
+            v[u] = e < A.nbins ? A.toff[e] : 0;
+            c[u] = e < A.nbins ? A.coff[e] : 0;
             s += v[u];
             cs += c[u];
         }
@@ -103,8 +112,8 @@ __global__ __launch_bounds__(256) void k_nma_scan(NmaArgs A) {
         int run = carry + block_excl_scan(s, scr, &tot);
         int crun = ccarry + block_excl_scan(cs, scr, &ctot);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
+        for (int u = 0; u < kNmaScanV; ++u) {
+            const int64_t e = base + (int64_t)threadIdx.x * kNmaScanV + u;
             if (e < A.nbins) { A.toff[e] = run; A.coff[e] = crun; }
             run += v[u];
             crun += c[u];
@@ -113,28 +122,31 @@ __global__ __launch_bounds__(256) void k_nma_scan(NmaArgs A) {
         ccarry += ctot;
     }
     if (threadIdx.x == 0) { A.toff[A.nbins] = carry; A.coff[A.nbins] = ccarry; }
-    __syncthreads();
-    for (int64_t r = threadIdx.x; r <= A.nwg; r += blockDim.x) {
-        if (r == A.nwg) { A.wr[r] = carry; continue; }
-        const int64_t target = r * (int64_t)ccarry / A.nwg;
-        int64_t lo = 0, hi = A.nbins - 1;          // the last bin starting at or before target
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) / 2;
-            if (A.coff[mid] <= target) lo = mid; else hi = mid - 1;
-        }
-        const int tiles = A.toff[lo + 1] - A.toff[lo];
-        const int64_t k = max<int64_t>(0, target - A.coff[lo] - 2) / nma_tile_cost(A, lo);
-        A.wr[r] = A.toff[lo] + (int32_t)min<int64_t>(k, tiles);
-    }
+    // the end of the last share; with no tile every share is empty
+    for (int64_t r = threadIdx.x; r <= A.nwg; r += blockDim.x)
+        if (r == A.nwg || ccarry == 0) A.wr[r] = r == A.nwg ? carry : 0;
 }
 
 // Tile descriptors: the bin of each tile, its first pair and its pairs.
+// The tile list is cut into nwg shares of equal estimated cost: share r
+// starts at cost floor(r C / nwg), C the total, and the bin whose cost range
+// holds that point writes wr[r], the first tile of the share.
 __global__ __launch_bounds__(256) void k_nma_map(NmaArgs A) {
+    const int64_t C = A.coff[A.nbins];
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.nbins; e += (int64_t)gridDim.x * blockDim.x) {
         const int32_t p0 = A.noff[e], p1 = A.noff[e + 1];
-        for (int t = A.toff[e]; t < A.toff[e + 1]; ++t) {
-            const int32_t pb = p0 + (t - A.toff[e]) * A.T;
-            A.tdesc[t] = int4{(int32_t)e, pb, min(A.T, p1 - pb), 0};
+        const int32_t tb = A.toff[e], tiles = A.toff[e + 1] - tb;
+        for (int t = 0; t < tiles; ++t) {
+            const int32_t pb = p0 + t * A.T;
+            A.tdesc[tb + t] = int4{(int32_t)e, pb, min(A.T, p1 - pb), 0};
+        }
+        const int64_t c0 = A.coff[e], c1 = A.coff[e + 1];
+        if (c1 == c0) continue;
+        const int64_t r0 = (c0 * A.nwg + C - 1) / C, r1 = min<int64_t>(A.nwg - 1, (c1 * A.nwg + C - 1) / C - 1);
+        const int pc = nma_tile_cost(A, e);
+        for (int64_t r = r0; r <= r1; ++r) {
+            const int64_t target = r * C / A.nwg;
+            A.wr[r] = tb + (int32_t)min<int64_t>(max<int64_t>(0, target - c0 - 2) / pc, tiles);
         }
     }
 }
@@ -638,25 +650,39 @@ __global__ __launch_bounds__(256) void k_nma_merge(NmaArgs A) {
     const floatx4_t *rec = A.pml + (size_t)grp * kNmaP * G + h;
     const int16_t *po = A.po + ((size_t)grp * kNmaP * G + h) * kNmaD + dd;
     typedef int16_t h8_t __attribute__((ext_vector_type(8)));
-    floatx4_t r[kNmaP];
-    h8_t v[kNmaP];
+    // the states' maxima and sums, then each output's weight l_j 2^(m_j - M)
+    // times the unit of its 16-bit values (0 for an empty state)
+    float mj[kNmaP], lj[kNmaP], uj[kNmaP];
 #pragma unroll
     for (int j = 0; j < kNmaP; ++j) {
-        r[j] = j < P ? rec[(size_t)j * G] : floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
-        if (j < P && r[j][0] != -INFINITY) v[j] = *reinterpret_cast<const h8_t *>(po + (size_t)j * G * kNmaD);
+        const floatx4_t r = j < P ? rec[(size_t)j * G] : floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
+        mj[j] = r[0];
+        lj[j] = r[1];
+        uj[j] = r[2];
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kNmaP; ++j) M = fmaxf(M, r[j][0]);
-    float l = 0.0f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kNmaP; ++j) M = fmaxf(M, mj[j]);
+    float l = 0.0f, wo[kNmaP];
 #pragma unroll
     for (int j = 0; j < kNmaP; ++j) {
-        if (r[j][0] == -INFINITY) continue;
-        const float wl = r[j][1] * __builtin_amdgcn_exp2f(r[j][0] - M);
+        const float wl = mj[j] == -INFINITY ? 0.0f : lj[j] * __builtin_amdgcn_exp2f(mj[j] - M);
         l += wl;
-        const float wgt = wl * r[j][2];
+        wo[j] = wl * uj[j];
+    }
+    // the outputs, eight states' loads in flight at a time
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int x = 0; x < 8; ++x) o[x] = fmaf((float)v[j][x], wgt, o[x]);
+    for (int j0 = 0; j0 < kNmaP; j0 += 8) {
+        h8_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (wo[j0 + j] != 0.0f) v[j] = *reinterpret_cast<const h8_t *>(po + (size_t)(j0 + j) * G * kNmaD);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (wo[j0 + j] != 0.0f)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) o[x] = fmaf((float)v[j][x], wo[j0 + j], o[x]);
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const size_t oh = (size_t)(A.row0 + grp / A.h_kv) * A.h_q + (size_t)(grp % A.h_kv) * G + h;
@@ -720,9 +746,10 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     const int64_t nwg = std::min<int64_t>({nma_tiles_bound(B.groups, A.G, A.nbins), (int64_t)(cus * 2 + 7) / 8 * 8,
                                            (int64_t)kNmaMaxWg});
     A.nwg = nwg;
-    hipLaunchKernelGGL(k_nma_scan, dim3(1), dim3(256), 0, st, A);
-    hipLaunchKernelGGL(k_nma_map, dim3((unsigned)std::min<int64_t>((A.nbins + 255) / 256, 4096)), dim3(256), 0, st,
-                       A);
+    const unsigned bin_blocks = (unsigned)std::min<int64_t>((A.nbins + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_nma_count, dim3(bin_blocks), dim3(256), 0, st, A);
+    hipLaunchKernelGGL(k_nma_scan, dim3(1), dim3(kNmaScanT), 0, st, A);
+    hipLaunchKernelGGL(k_nma_map, dim3(bin_blocks), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_pairs, dim3((unsigned)std::min<int64_t>((B.groups * kNmaP + 255) / 256, 8192)),
                        dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(kNmaThreads), 0, st, A);
