@@ -76,6 +76,77 @@ __global__ __launch_bounds__(256) void k_project(const T *__restrict__ K, const 
     }
 }
 
+// The same projection on the fp64 matrix cores (r = 64, d a multiple of 8,
+// d <= 256): a workgroup takes KB 16-key blocks, wave w the latent columns
+// 16 w .. 16 w + 15.  v_mfma_f64_16x16x4_f64 adds the four exact products of
+// dims 4 blk .. 4 blk + 3 in order, each addition rounded as a separate fma
+// would be, so the chain over blk ascending gives the same double sum bit for
+// bit.  The key tile is staged in LDS transposed ([dim][key], padded rows) as
+// floats.  NQ = d / 4 when fixed at compile time (the lane's weights, dims
+// 4 blk + l / 16 of its column, then sit in registers before the tile is
+// staged); NQ = 0 takes d at run time and loads a weight per block.
+constexpr int kPjMaxD = 256;
+LSA_DEV void load8(const bf16_t *src, size_t at, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(src + at);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u); }
+}
+LSA_DEV void load8(const float *src, size_t at, float (&v)[8]) {
+    const f4_t a = *reinterpret_cast<const f4_t *>(src + at), b = *reinterpret_cast<const f4_t *>(src + at + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T, int KB, int NQ>
+__global__ __launch_bounds__(256) void k_project_mfma(const T *__restrict__ K, const float *__restrict__ W,
+                                                      float *__restrict__ Z, int64_t n, int d) {
+    constexpr int r = 64, KT = 16 * KB, ST = KT + 1;
+    extern __shared__ float Kt[];                 // [d][ST]
+    const int g = blockIdx.y;
+    const int64_t key0 = (int64_t)blockIdx.x * KT;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int lr = lane % 16, lk = lane / 16;
+    const T *Kg = K + (size_t)g * n * d;
+    const float *wcol = W + (size_t)g * d * r + 16 * w + lr;
+    const int nq = NQ > 0 ? NQ : d / 4;
+    float wv[NQ > 0 ? NQ : 1];
+    if constexpr (NQ > 0) {
+#pragma unroll
+        for (int blk = 0; blk < NQ; ++blk) wv[blk] = wcol[(size_t)(4 * blk + lk) * r];
+    }
+    // the tile: key row kk, dims 8 x .. 8 x + 7 per 16-byte (bf16) or two
+    // 16-byte (fp32) loads, stored transposed
+    for (int idx = tid; idx < KT * (d / 8); idx += blockDim.x) {
+        const int kk = idx / (d / 8), x = idx % (d / 8);
+        const int64_t j = key0 + kk;
+        float v[8];
+        load8(Kg, j < n ? (size_t)j * d + 8 * x : 0, v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Kt[(8 * x + u) * ST + kk] = j < n ? v[u] : 0.0f;
+    }
+    __syncthreads();
+    d4_t acc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc[kb] = d4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll(NQ > 0 ? NQ : 1)
+    for (int blk = 0; blk < nq; ++blk) {
+        double b;
+        if constexpr (NQ > 0) b = (double)wv[blk];
+        else b = (double)wcol[(size_t)(4 * blk + lk) * r];
+        const float *krow = Kt + (4 * blk + lk) * ST + lr;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)krow[16 * kb], b, acc[kb], 0, 0, 0);
+    }
+    // element e of lane l: key 16 kb + l / 16 + 4 e, column 16 w + l % 16
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t j = key0 + 16 * kb + lk + 4 * e;
+            if (j < n) Z[((size_t)g * n + j) * r + 16 * w + lr] = (float)acc[kb][e];
+        }
+}
+
 // ---------------------------------------------------------------- level setup
 __global__ void k_iota(int32_t *perm, int64_t n, int h) {
     const int64_t tot = n * h;
@@ -550,15 +621,45 @@ static inline unsigned grid1(int64_t tot, int bs) {
     return (unsigned)g;
 }
 
+// The matrix-core projection: d = 128 with the weights in registers and
+// 128 keys a workgroup (66 KB of LDS: two workgroups a compute unit), other
+// d with 64 keys a workgroup.
+template <typename T, int KB, int NQ>
+static hipError_t launch_project_mfma(const T *K, int64_t n, int h, int d, const float *W, float *Z,
+                                      hipStream_t st) {
+    const size_t lds = sizeof(float) * (size_t)d * (16 * KB + 1);
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute((const void *)k_project_mfma<T, KB, NQ>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)((n + 16 * KB - 1) / (16 * KB)), (unsigned)h);
+    hipLaunchKernelGGL((k_project_mfma<T, KB, NQ>), grid, dim3(256), lds, st, K, W, Z, n, d);
+    return hipSuccess;
+}
+
+static hipError_t project_mfma(const void *K, int dtype, int64_t n, int h, int d, const float *W, float *Z,
+                               hipStream_t st) {
+    if (dtype == 0)
+        return d == 128 ? launch_project_mfma<float, 8, 32>((const float *)K, n, h, d, W, Z, st)
+                        : launch_project_mfma<float, 4, 0>((const float *)K, n, h, d, W, Z, st);
+    return d == 128 ? launch_project_mfma<bf16_t, 8, 32>((const bf16_t *)K, n, h, d, W, Z, st)
+                    : launch_project_mfma<bf16_t, 4, 0>((const bf16_t *)K, n, h, d, W, Z, st);
+}
+
 hipError_t build_index(const void *K, int dtype, int64_t n, int h, int d, const float *W, int r, int b, int L,
                        int iters, char *index, const int64_t *centroid_off, const int64_t *count_off,
                        int64_t leaf_off_off, int64_t perm_off, void *ws, hipStream_t st) {
     BuildWs w = carve_build_ws((char *)ws, n, h, r, b, L);
     const dim3 pg((unsigned)((n + 31) / 32), (unsigned)h);
-    if (dtype == 0)
+    if (r == 64 && d % 8 == 0 && d <= kPjMaxD) {
+        const hipError_t e = project_mfma(K, dtype, n, h, d, W, w.Z, st);
+        if (e != hipSuccess) return e;
+    } else if (dtype == 0) {
         hipLaunchKernelGGL(k_project<float>, pg, dim3(256), 0, st, (const float *)K, W, w.Z, n, d, r);
-    else
+    } else {
         hipLaunchKernelGGL(k_project<bf16_t>, pg, dim3(256), 0, st, (const bf16_t *)K, W, w.Z, n, d, r);
+    }
     hipLaunchKernelGGL(k_iota, dim3(grid1(n * h, 256)), dim3(256), 0, st, w.permA, n, h);
     hipLaunchKernelGGL(k_root_off, dim3(1), dim3(64), 0, st, w.offA, n, h);
     int32_t *prev_perm = w.permA, *prev_off = w.offA;

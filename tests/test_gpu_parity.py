@@ -159,6 +159,27 @@ def test_small_pipeline_matches_oracle(lsa, name, over):
         _check_attention(out3, lse3, o_ref[:1], lse_ref[:1], tol)
 
 
+# r = 64 builds take the projection on the fp64 matrix cores: fp32 keys with
+# d = 256 (its largest key tile, over 64 KB of LDS) and bf16 keys with
+# d = 136 (34 blocks of four dims), both with a ragged last tile of keys
+PROJ_CASES = [("proj_f32_d256", dict(n=1000, h_q=2, h_kv=2, d=256, dtype="f32", r=64, b=8, L=2, beam=2, k=100,
+                                     centres=50, m=3, mode="chunk")),
+              ("proj_bf16_d136", dict(n=777, h_q=3, h_kv=3, d=136, dtype="bf16", r=64, b=5, L=3, beam=2, k=50,
+                                      centres=40, m=2, mode="chunk"))]
+
+
+@pytest.mark.parametrize("name,over", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_projection_on_matrix_cores_matches_oracle(lsa, name, over):
+    """The index built through the matrix-core projection equals the
+    oracle's bit for bit (every centroid is a mean of projected keys)."""
+    dev = torch.device("cuda:0")
+    w = _wl("tiny_4k", **over).replace(name=name)
+    data = _inputs(w, dev)
+    say("projection", name)
+    index, desc, gix, oix = _build_both(lsa, w, data)
+    assert_index_equal(gix, oix)
+
+
 def _assert_exchange_zeroed(ws, groups, beam, G, d):
     """After a multi-workgroup call everything in its workspace but the trailing
     partial softmax states is zero again (counters and exchange buffers)."""
