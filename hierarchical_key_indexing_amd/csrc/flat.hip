@@ -70,6 +70,8 @@ struct FlatArgs {
     uint64_t *smp;              // [mb][h_kv][kSampleMax] sampled keys (0: not a candidate)
     uint64_t *thr;              // [mb][h_kv] threshold key T
     int32_t *lcnt, *lwt;        // [mb][h_kv] collected keys and their weight
+    int32_t *fail;              // [mb][h_kv] 1: the list does not decide the row (exact selection)
+    int2 *fl;                   // [h_kv][nleaf] first and last member of each leaf (0, 0: empty)
     uint64_t *lst;              // [mb][h_kv][kFlatList] collected keys
     int32_t *sel, *sel_count;   // the batch's rows
     float *sel_cutoff;
@@ -275,91 +277,239 @@ __global__ __launch_bounds__(256, 2) void k_flat_score(FlatArgs A) {
     }
 }
 
-// r = 64 and at least kFlatMfmaRows rows: the same outputs from the fp64
-// matrix cores.  Wave w takes rows 16 w .. 16 w + 15 of the tile (the
-// product's rows: u widened once) against the workgroup's leaves, 16 at a
-// time (the columns: lane (k, c) leaf c); the next 16 leaves' rows and member
-// ranges are loaded while a block is multiplied.  Lane (k, c) then owns rows
-// k + 4 e against leaf c.
+// r = 64 and at least kFlatMfmaRows rows: the scores from the fp64 matrix
+// cores, in three passes that write no full (row, leaf) table:
+//   MODE 1  the sample: leaves 0, S, 2S, ... (the sample index is the leaf
+//           space here), their keys to the sample and weights to the table;
+//   MODE 2  every leaf: the keys at or above the row's threshold T go to the
+//           row's list (through 32-key segments per row in LDS, one global
+//           reservation per row and workgroup), their weights to the table
+//           and to the row's list weight;
+//   MODE 3  every leaf, for the rows whose list does not decide them only:
+//           every score and weight to the table (the exact selection's input).
+// Wave w takes rows 16 w .. 16 w + 15 of the tile (the product's rows: u
+// widened once) against the workgroup's leaves, 16 at a time (the columns:
+// lane (k, c) leaf c).  A block's 16 leaf rows are staged once for the
+// workgroup in LDS, widened and in operand order, and the next block's are
+// loaded while it is multiplied.  Lane (k, c) then owns rows k + 4 e
+// against leaf c.
 constexpr int kFlatMfmaRows = 16;
+constexpr int kFlatSeg = 32;        // list keys per row staged in LDS by a collecting workgroup
 
+template <int MODE>
 __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
+    constexpr int SR = MODE == 2 ? kFlatRows : 1;
+    constexpr int LPW = MODE == 1 ? 64 : kFlatLeaves;        // leaves per workgroup
     __shared__ int32_t rlo_s[kFlatRows], rhi_s[kFlatRows];
-    const int64_t v0 = (int64_t)blockIdx.x * kFlatLeaves;
+    __shared__ uint64_t thr_s[SR];
+    __shared__ int cnt_s[SR], wsum_s[SR];
+    __shared__ uint64_t seg_s[SR][MODE == 2 ? kFlatSeg : 1];
+    __shared__ int fail_s[MODE == 3 ? kFlatRows : 1];
+    __shared__ int any_s;
+    // a step of two 16-leaf blocks, twice: their rows widened in operand
+    // order (dim 4 blk + k of leaf c of block h at [h][blk][k][c]) and member
+    // count, first offset, first and last member
+    __shared__ double bs[2][2][16][4][16];
+    __shared__ int4 meta_s[2][32];
+    const int64_t v0 = (int64_t)blockIdx.x * LPW;
     const int64_t i0 = (int64_t)blockIdx.y * kFlatRows;
     const int g = blockIdx.z;
+    const int tid = threadIdx.x;
     const int nr = (int)min<int64_t>(kFlatRows, A.mb - i0);
-    if ((int)threadIdx.x < nr) {
-        const AttnSet as = attn_set(A.q_pos[i0 + threadIdx.x], A.n, A.n_sink, A.window);
-        rlo_s[threadIdx.x] = as.rlo;
-        rhi_s[threadIdx.x] = as.rhi;
+    if (tid == 0) any_s = 0;
+    __syncthreads();
+    if (tid < nr) {
+        const AttnSet as = attn_set(A.q_pos[i0 + tid], A.n, A.n_sink, A.window);
+        rlo_s[tid] = as.rlo;
+        rhi_s[tid] = as.rhi;
+        const int64_t gi = (i0 + tid) * A.h_kv + g;
+        if constexpr (MODE == 2) { thr_s[tid] = A.thr[gi]; cnt_s[tid] = 0; wsum_s[tid] = 0; }
+        if constexpr (MODE == 3) {
+            fail_s[tid] = A.fail[gi];
+            if (fail_s[tid]) any_s = 1;
+        }
     }
     __syncthreads();
-    const int wv = threadIdx.x / kWave, lane = lane_id();
+    if (MODE == 3 && !any_s) return;                         // (uniform in the workgroup)
+    const int wv = tid / kWave, lane = lane_id();
     const int col = lane & 15, kk = lane >> 4;
     const int rb = 16 * wv;                                  // the wave's first row in the tile
-    if (rb >= nr) return;                                    // wave-local from here: no block barrier
+    const bool wave_on = rb < nr;                            // (uniform in the wave)
+    // the workgroup's leaf range; in the sample pass leaf x stands for leaf x S
+    const int64_t span = MODE == 1 ? (int64_t)A.ns : A.nleaf;
+    const int64_t vend = min<int64_t>(v0 + LPW, span);
     const float *Cg = A.C + (size_t)g * A.nleaf * 64;
-    const int32_t *cn = A.cnt + (size_t)g * A.nleaf;
     const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
     const int32_t *pm = A.perm + (size_t)g * A.n;
-    const size_t rs = (size_t)A.h_kv * A.nleaf;              // stride between rows
-    const size_t ss = (size_t)A.h_kv * kSampleMax;           // sample stride between rows
+    const int2 *fl = A.fl + (size_t)g * A.nleaf;
+    // staging: thread t loads dims 4 (t / 16) .. + 3 of leaf t % 16 of both
+    // blocks (a half-wave's stores: consecutive doubles), threads below 32
+    // also leaf t's member range (clamped leaves: in bounds)
+    const int sc_leaf = tid % 16, sq = tid / 16;
+    auto leaf_of = [&](int64_t x) -> int64_t {
+        const int64_t xc = min<int64_t>(x, span - 1);
+        return MODE == 1 ? xc * A.S : xc;
+    };
+    struct Stage { f4_t v[2]; int4 meta; };
+    auto stage_load = [&](Stage &st, int64_t vb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t v = leaf_of(vb + 16 * h + sc_leaf);
+            st.v[h] = *reinterpret_cast<const f4_t *>(Cg + (size_t)v * 64 + 4 * sq);
+        }
+        if (tid < 32) {
+            const int64_t vm = leaf_of(vb + tid);
+            const int2 f = fl[vm];
+            const int32_t a0 = lo[vm];
+            st.meta = int4{lo[vm + 1] - a0, a0, f.x, f.y};
+        }
+    };
+    auto stage_store = [&](int p, const Stage &st) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bs[p][h][sq][0][sc_leaf] = (double)st.v[h].x;
+            bs[p][h][sq][1][sc_leaf] = (double)st.v[h].y;
+            bs[p][h][sq][2][sc_leaf] = (double)st.v[h].z;
+            bs[p][h][sq][3][sc_leaf] = (double)st.v[h].w;
+        }
+        if (tid < 32) meta_s[p][tid] = st.meta;
+    };
     double ua[16];
-    {
+    int rlo[4], rhi[4], wacc[4] = {0, 0, 0, 0};
+    if (wave_on) {
         f4_t t[4];
         load_row_mfma(A.U + ((size_t)(i0 + min(rb + col, nr - 1)) * A.h_kv + g) * 64, kk, t);
         widen_row_mfma(t, ua);
-    }
-    int rlo[4], rhi[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int rr = min(rb + kk + 4 * e, nr - 1);
-        rlo[e] = rlo_s[rr];
-        rhi[e] = rhi_s[rr];
-    }
-    const int64_t vend = min<int64_t>(v0 + kFlatLeaves, A.nleaf);
-    // block 0's leaves (clamped ids: in bounds; leaves past the end are not written)
-    f4_t cur[4];
-    int64_t vc = min<int64_t>(v0 + col, A.nleaf - 1);
-    load_row_mfma(Cg + (size_t)vc * 64, kk, cur);
-    int c_cur = cn[vc], a0_cur = lo[vc], a1_cur = lo[vc + 1];
-#pragma unroll 1
-    for (int64_t vb = v0; vb < vend; vb += 16) {
-        const bool more = vb + 16 < vend;
-        f4_t nxt[4];
-        int c_nxt = 0, a0_nxt = 0, a1_nxt = 0;
-        if (more) {
-            const int64_t vn = min<int64_t>(vb + 16 + col, A.nleaf - 1);
-            load_row_mfma(Cg + (size_t)vn * 64, kk, nxt);
-            c_nxt = cn[vn]; a0_nxt = lo[vn]; a1_nxt = lo[vn + 1];
+        for (int e = 0; e < 4; ++e) {
+            const int rr = min(rb + kk + 4 * e, nr - 1);
+            rlo[e] = rlo_s[rr];
+            rhi[e] = rhi_s[rr];
         }
-        const int64_t v = vb + col;
-        const int c = c_cur, a0 = a0_cur, a1 = a1_cur;
-        const int32_t first = c > 0 ? pm[a0] : 0, last = c > 0 ? pm[a1 - 1] : 0;
-        const d4_t acc = mfma_dot64(ua, cur);
-        if (v < vend) {
-            const bool sampled = A.S > 0 && v % A.S == 0;
+    }
+    // the step of 32 leaves at vb, from buffer p
+    auto compute_step = [&](int64_t vb, int p) {
+        if (!wave_on) return;
+        // two independent chains (one a block), each over the dims in order
+        d4_t acc2[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+        for (int blk = 0; blk < 16; ++blk)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                acc2[h] = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[blk], bs[p][h][blk][kk][col], acc2[h], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const d4_t acc = acc2[h];
+            const int64_t x = vb + 16 * h + col, v = MODE == 1 ? x * A.S : x;
+            const int4 mt = meta_s[p][16 * h + col];         // member count, first offset, first, last
+            const int c = mt.x, a0 = mt.y;
+            const int32_t first = mt.z, last = mt.w;
+            if (x >= vend) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = rb + kk + 4 * e;
                 if (rr >= nr) continue;
-                const int eq = c > 0 ? members_in(pm + a0, a1 - a0, first, last, rlo[e], rhi[e]) : 0;
-                const uint32_t oq = eq > 0 ? orderable((float)acc[e]) : 0u;
-                const size_t o = ((size_t)(i0 + rr) * A.h_kv + g) * A.nleaf + v;
-                A.sc[o] = oq;
-                A.wt[o] = (uint16_t)min(eq, A.k);
-                if (sampled)
-                    A.smp[((size_t)(i0 + rr) * A.h_kv + g) * kSampleMax + v / A.S] =
-                        eq > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
+                if (MODE == 3 && !fail_s[rr]) continue;
+                const int64_t gi = (i0 + rr) * A.h_kv + g;
+                const size_t o = (size_t)gi * A.nleaf + v;
+                if constexpr (MODE == 2) {
+                    // the members in range are counted only for keys that
+                    // reach the threshold (a leaf whose range is cut costs a
+                    // search in memory)
+                    const uint64_t key = ((uint64_t)orderable((float)acc[e]) << 32) | (uint64_t)(~(uint32_t)v);
+                    if (c == 0 || key < thr_s[rr]) continue;
+                    const int eq = members_in(pm + a0, c, first, last, rlo[e], rhi[e]);
+                    if (eq > 0) {
+                        const int w = min(eq, A.k);
+                        A.wt[o] = (uint16_t)w;
+                        wacc[e] += w;
+                        const int pos = atomicAdd(&cnt_s[rr], 1);
+                        if (pos < kFlatSeg) {
+                            seg_s[rr][pos] = key;
+                        } else {
+                            const int gp = atomicAdd(A.lcnt + gi, 1);
+                            if (gp < kFlatList) A.lst[(size_t)gi * kFlatList + gp] = key;
+                        }
+                    }
+                } else {
+                    const int eq = c > 0 ? members_in(pm + a0, c, first, last, rlo[e], rhi[e]) : 0;
+                    const uint32_t oq = eq > 0 ? orderable((float)acc[e]) : 0u;
+                    if constexpr (MODE == 1) {
+                        A.wt[o] = (uint16_t)min(eq, A.k);
+                        A.smp[(size_t)gi * kSampleMax + x] =
+                            eq > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
+                    } else {
+                        A.sc[o] = oq;
+                        A.wt[o] = (uint16_t)min(eq, A.k);
+                    }
+                }
             }
         }
-        if (more) {
+    };
+    // steps two at a time: the loads of a step are issued two steps ahead
+    // and stored to LDS at the end of the step before it
+    Stage s0 = {}, s1 = {};
+    stage_load(s0, v0);
+    stage_store(0, s0);
+    __syncthreads();
+    if (v0 + 32 < vend) stage_load(s1, v0 + 32);
+#pragma unroll 1
+    for (int64_t vb = v0; vb < vend; vb += 64) {
+        if (vb + 64 < vend) stage_load(s0, vb + 64);
+        compute_step(vb, 0);
+        if (vb + 32 < vend) stage_store(1, s1);
+        __syncthreads();
+        if (vb + 32 >= vend) break;
+        if (vb + 96 < vend) stage_load(s1, vb + 96);
+        compute_step(vb + 32, 1);
+        if (vb + 64 < vend) stage_store(0, s0);
+        __syncthreads();
+    }
+    if constexpr (MODE == 2) {
+        if (wave_on) {
 #pragma unroll
-            for (int h = 0; h < 4; ++h) cur[h] = nxt[h];
-            c_cur = c_nxt; a0_cur = a0_nxt; a1_cur = a1_nxt;
+            for (int e = 0; e < 4; ++e)
+                if (wacc[e] > 0) atomicAdd(&wsum_s[rb + kk + 4 * e], wacc[e]);
+        }
+        // every row's segment into its list (one reservation) and its weight
+        __syncthreads();
+        if (tid < nr) {
+            const int64_t gi = (i0 + tid) * A.h_kv + g;
+            const int nseg = min(cnt_s[tid], kFlatSeg);
+            if (nseg > 0) {
+                const int base = atomicAdd(A.lcnt + gi, nseg);
+                for (int e = 0; e < nseg; ++e)
+                    if (base + e < kFlatList) A.lst[(size_t)gi * kFlatList + base + e] = seg_s[tid][e];
+            }
+            if (wsum_s[tid] > 0) atomicAdd(A.lwt + gi, wsum_s[tid]);
         }
     }
+}
+
+// Whether a row's list decides it: the list holds every key >= T, so it
+// holds the k-th retrieved key when it weighs >= k or holds every candidate
+// (T = 1), provided it did not overflow.
+LSA_DEV bool list_decides(const FlatArgs &A, int64_t gi) {
+    return A.lcnt[gi] <= kFlatList && (A.lwt[gi] >= A.k || A.thr[gi] == 1ull);
+}
+
+// Every leaf's first and last member (ascending lists), for the scoring's
+// retrieval-range counts.
+__global__ __launch_bounds__(256) void k_flat_bounds(FlatArgs A) {
+    const int64_t tot = (int64_t)A.h_kv * A.nleaf;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < tot; e += (int64_t)gridDim.x * blockDim.x) {
+        const int g = (int)(e / A.nleaf);
+        const int64_t v = e % A.nleaf;
+        const int32_t *lo = A.leaf_off + (size_t)g * (A.nleaf + 1);
+        const int32_t *pm = A.perm + (size_t)g * A.n;
+        const int32_t a0 = lo[v], a1 = lo[v + 1];
+        A.fl[e] = a1 > a0 ? int2{pm[a0], pm[a1 - 1]} : int2{0, 0};
+    }
+}
+
+__global__ __launch_bounds__(256) void k_flat_check(FlatArgs A) {
+    const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gi < A.mb * A.h_kv) A.fail[gi] = list_decides(A, gi) ? 0 : 1;
 }
 
 // ---------------------------------------------------------------- threshold
@@ -746,14 +896,12 @@ __global__ __launch_bounds__(256) void k_flat_finish(FlatArgs A) {
     const int64_t gi = blockIdx.x;                 // row * h_kv + KV head, within the batch
     const int tid = threadIdx.x;
     if (tid == 0) cut_s = -INFINITY;
-    const int nl0 = A.lcnt[gi], wl0 = A.lwt[gi];
-    const uint64_t T = A.thr[gi];
+    const int nl0 = A.lcnt[gi];
     uint64_t *glst = A.lst + (size_t)gi * kFlatList;
-    // the list holds every key >= T; it holds the k-th retrieved key when it
-    // weighs >= k, or when it holds every candidate (T = 1).  Otherwise the
-    // exact radix selection over every leaf builds it.
+    // the list decides the row (list_decides), or the exact radix selection
+    // over every leaf builds it
     int nl;
-    if (nl0 <= kFlatList && (wl0 >= A.k || T == 1ull)) {
+    if (list_decides(A, gi)) {
         for (int e = tid; e < nl0; e += blockDim.x) lst[e] = glst[e];
         nl = nl0;
         __syncthreads();
@@ -779,7 +927,8 @@ __global__ __launch_bounds__(256) void k_flat_finish(FlatArgs A) {
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct FlatWs {
-    float *U; double *Ud; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt; uint64_t *lst; size_t bytes;
+    float *U; double *Ud; uint32_t *sc; uint16_t *wt; uint64_t *smp, *thr; int32_t *lcnt, *lwt, *fail; uint64_t *lst;
+    int2 *fl; size_t bytes;
 };
 
 // (after the workspace's reserved prefix, which this path never writes)
@@ -788,6 +937,7 @@ FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
     FlatWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = a256(cur + n); return p; };
     const size_t groups = (size_t)mb * h_kv;
+    w.fl = (int2 *)take(sizeof(int2) * (size_t)h_kv * nleaf);     // first: the same place for every batch size
     w.U = (float *)take(sizeof(float) * groups * r);
     w.Ud = (double *)take(sizeof(double) * groups * r);
     w.sc = (uint32_t *)take(sizeof(uint32_t) * groups * nleaf);
@@ -796,6 +946,7 @@ FlatWs carve_flat_ws(char *base, int64_t mb, int h_kv, int r, int64_t nleaf) {
     w.thr = (uint64_t *)take(sizeof(uint64_t) * groups);
     w.lcnt = (int32_t *)take(sizeof(int32_t) * groups);
     w.lwt = (int32_t *)take(sizeof(int32_t) * groups);
+    w.fail = (int32_t *)take(sizeof(int32_t) * groups);
     w.lst = (uint64_t *)take(sizeof(uint64_t) * groups * kFlatList);
     w.bytes = cur;
     return w;
@@ -850,7 +1001,7 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
         A.W = W; A.k = k; A.n_sink = n_sink; A.window = window; A.row = row;
         A.U = w.U; A.Ud = w.Ud; A.sc = w.sc; A.wt = w.wt;
         A.S = S; A.ns = S > 0 ? (int)((nleaf + S - 1) / S) : 0;
-        A.smp = w.smp; A.thr = w.thr; A.lcnt = w.lcnt; A.lwt = w.lwt; A.lst = w.lst;
+        A.smp = w.smp; A.thr = w.thr; A.lcnt = w.lcnt; A.lwt = w.lwt; A.fail = w.fail; A.lst = w.lst; A.fl = w.fl;
         A.sel = sel + (size_t)i0 * h_kv * row;
         A.sel_count = sel_count + (size_t)i0 * h_kv;
         A.sel_cutoff = sel_cutoff ? sel_cutoff + (size_t)i0 * h_kv : nullptr;
@@ -859,11 +1010,28 @@ hipError_t select_flat(const void *Q, int dtype, int64_t m, int h_q, int d, cons
         else hipLaunchKernelGGL(k_flat_latent<bf16_t>, dim3((unsigned)nb, (unsigned)h_kv), dim3(256), 0, st, A);
         const dim3 sgrid((unsigned)((nleaf + kFlatLeaves - 1) / kFlatLeaves), (unsigned)((nb + kFlatRows - 1) / kFlatRows),
                          (unsigned)h_kv);
-        if (r == 64 && nb >= kFlatMfmaRows) hipLaunchKernelGGL(k_flat_score_mfma, sgrid, dim3(256), 0, st, A);
-        else if (r == 64) hipLaunchKernelGGL(k_flat_score<64>, sgrid, dim3(256), 0, st, A);
-        else hipLaunchKernelGGL(k_flat_score<0>, sgrid, dim3(256), 0, st, A);
-        hipLaunchKernelGGL(k_flat_threshold, dim3(groups), dim3(256), 0, st, A);
-        hipLaunchKernelGGL(k_flat_collect, dim3((unsigned)((nleaf + kCollect - 1) / kCollect), groups), dim3(256), 0, st, A);
+        if (r == 64 && nb >= kFlatMfmaRows) {
+            // threshold from the sample, the list from one scoring pass, the
+            // full table only for the rows the list does not decide
+            // every leaf's first and last member, once per call
+            if (i0 == 0)
+                hipLaunchKernelGGL(k_flat_bounds, dim3((unsigned)std::min<int64_t>((h_kv * nleaf + 255) / 256, 8192)),
+                                   dim3(256), 0, st, A);
+            if (S > 0) {
+                const dim3 pgrid((unsigned)((A.ns + 63) / 64), sgrid.y, sgrid.z);
+                hipLaunchKernelGGL(k_flat_score_mfma<1>, pgrid, dim3(256), 0, st, A);
+            }
+            hipLaunchKernelGGL(k_flat_threshold, dim3(groups), dim3(256), 0, st, A);
+            hipLaunchKernelGGL(k_flat_score_mfma<2>, sgrid, dim3(256), 0, st, A);
+            hipLaunchKernelGGL(k_flat_check, dim3((groups + 255) / 256), dim3(256), 0, st, A);
+            hipLaunchKernelGGL(k_flat_score_mfma<3>, sgrid, dim3(256), 0, st, A);
+        } else {
+            if (r == 64) hipLaunchKernelGGL(k_flat_score<64>, sgrid, dim3(256), 0, st, A);
+            else hipLaunchKernelGGL(k_flat_score<0>, sgrid, dim3(256), 0, st, A);
+            hipLaunchKernelGGL(k_flat_threshold, dim3(groups), dim3(256), 0, st, A);
+            hipLaunchKernelGGL(k_flat_collect, dim3((unsigned)((nleaf + kCollect - 1) / kCollect), groups), dim3(256),
+                               0, st, A);
+        }
         hipLaunchKernelGGL(k_flat_finish, dim3(groups), dim3(256), shm, st, A);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
