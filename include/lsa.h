@@ -403,21 +403,32 @@ int lsa_select_attend_workspace_bytes(int64_t m, int h_q, int d, const lsa_index
                                       int k, int n_sink, int window, int64_t *bytes);
 
 /*
- * lsa_select followed by lsa_attend on the same rows, in one launch when the
- * batch is small (the decode case: the beam workgroups of each (row, KV head)
- * pair also attend over the keys they retrieved and the last one merges the
- * partial softmax states), else as the two calls in sequence.  Arguments as
- * in lsa_select and lsa_attend; K and V are the cache the index was built
- * from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes bytes) must be
- * zero-filled before its first use; the one-launch form leaves the part it
- * polls zeroed and no other path writes it (see lsa_select), so ws serves any
- * number of calls of any sizes that fit it; calls sharing one ws must not run
- * concurrently.  In the one-launch form the workgroups of a
- * (row, KV head) pair split the attention evenly over the attention set
- * (retrieved keys, then sinks and window).
- * Outputs equal those of the two separate calls
- * (sel, sel_count and sel_cutoff bit for bit; out and lse within fp32
- * rounding of the accumulation order).
+ * lsa_select followed by lsa_attend on the same rows, in one of three forms:
+ *   - one launch when the batch is small (the decode case: the beam
+ *     workgroups of each (row, KV head) pair also attend over the keys they
+ *     retrieved, split evenly over the attention set, and the last one
+ *     merges the partial softmax states);
+ *   - node-major selection and attention for many rows (bf16, d = 128,
+ *     h_q/h_kv <= 16, n_sink = window = 0, the node-major selection's shapes,
+ *     and ws of lsa_select_attend_workspace_bytes): the rows are grouped by
+ *     the kept clusters they descend into ("Latent Sparse Attention Breaks
+ *     Through the Million-Token Context Bottleneck", section "How LSA
+ *     Sidesteps Per-Key Scoring with Hierarchical Clustering"), each
+ *     cluster's keys are staged once for a tile of (row, head) columns that
+ *     attend over the keys they retrieved from it, and the per-cluster
+ *     partial states (output / sum as 16-bit fixed point under a power-of-two
+ *     scale per column, maximum and sum in fp32) are merged by log-sum-exp;
+ *   - otherwise the two calls in sequence.
+ * Arguments as in lsa_select and lsa_attend; K and V are the cache the index
+ * was built from, [h_kv][n][d].  ws (lsa_select_attend_workspace_bytes
+ * bytes) must be zero-filled before its first use; the one-launch form
+ * leaves the part it polls zeroed and no other path writes it (see
+ * lsa_select), so ws serves any number of calls of any sizes that fit it;
+ * calls sharing one ws must not run concurrently.
+ * sel, sel_count and sel_cutoff equal those of lsa_select bit for bit; out
+ * and lse equal lsa_attend's within fp32 rounding of the accumulation order
+ * (plus, in the node-major form, at most 2^-16 of the power of two above
+ * each partial output's largest magnitude).
  * Limits: those of lsa_select and of lsa_attend.
  */
 int lsa_select_attend(const void *Q, const void *K, const void *V, int dtype, int64_t m, int h_q, int d,
