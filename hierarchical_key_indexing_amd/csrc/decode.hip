@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64], skip_s[64];
     __shared__ int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
-    __shared__ int keep_s, count_s, last_s;
+    __shared__ int keep_s, count_s, last_s, flag_s;
     __shared__ float m_run[16], l_run[16], alpha_s[16];
 
     constexpr bool kMfma = ATTEND && sizeof(T) == 2 && DC > 0 && DC % 32 == 0;
@@ -592,7 +592,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             A.sel_count[gi] = count + as.nloc;
             if (count < A.k && A.sel_cutoff) A.sel_cutoff[gi] = -INFINITY;
         }
-        __syncthreads();
+        // LDS only: no one in this workgroup reads the stores above (the
+        // published ids are polled), so they need not complete here
+        lds_barrier();
     }
 
     if constexpr (ATTEND) {
@@ -743,6 +745,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     }
     __syncthreads();
     if (!last_s) return;
+    // the group's timeout flag (every workgroup has arrived, so it is final),
+    // read now so that its round trip overlaps the merge
+    if (tid == 0) flag_s = __hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (ATTEND) {
         // each thread merges 4 consecutive outputs of one head: every load
         // (the P partial outputs and each partial's max and sum) is issued
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         // report it in the status word, which stays set until the host reads
         // it, and clear the group's flag so that no later launch reads it as
         // a published word
-        if (__hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        if (flag_s != 0) {
             __hip_atomic_fetch_or(A.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             publish(ctrl + 2, 0);
         }
