@@ -19,20 +19,24 @@
 // many eligible keys are retrieved before each of its leaves), so no
 // workgroup sorts more than 64 keys.  Workgroup p writes its own leaves' keys
 // at their retrieval offsets, and then attends over an even 1/P slice of the
-// retrieval order (matrix cores for bf16); the last workgroup of the group to
-// finish merges the P partial softmax states.
+// retrieval order (matrix cores for bf16).  Each workgroup then sends every
+// other one its partial softmax state for that workgroup's slice of the
+// outputs, and merges the P states of its own slice.
 //
 // Workgroups exchange data through the caller's workspace without barriers:
 // it starts zeroed, a writer publishes nonzero words with device-scope stores,
-// a reader polls each word it needs until it is nonzero (bounded; a flag of
-// the group records a timeout), and the last workgroup zeroes everything
-// again.  It also moves a timeout flag into the status word at the start of
-// the workspace, which the host reads (lsa_workspace_status, or after every
-// call in debug mode).  The grid is at most one workgroup per compute unit,
-// so every workgroup of a group is resident while the others wait on its
-// words.  No other path of the library writes the part of a workspace that
-// these workgroups poll (ws_reserved_bytes), so a stale word can only be one
-// this kernel left, and it leaves none.
+// and a reader polls each word it needs until it is nonzero (bounded).  Every
+// word is zeroed again before the launch ends: a partial-state word by its
+// one reader once read, the exchange words by all workgroups in slices once
+// their merge has received every partial state (a workgroup sends its states
+// only after its last exchange read).  A wait that gives up sets the status
+// word at the start of the workspace, which the host reads
+// (lsa_workspace_status, or after every call in debug mode); the workspace
+// must then be zero-filled again before its next use.  The grid is at most
+// one workgroup per compute unit, so every workgroup of a group is resident
+// while the others wait on its words.  No other path of the library writes
+// the part of a workspace that these workgroups poll (ws_reserved_bytes), so
+// a stale word can only be one this kernel left, and it leaves none.
 #include "common.h"
 #include "internal.h"
 #include "mfma_attn.h"
@@ -66,6 +70,7 @@ struct DecodeArgs {
     int beam, k;
     int n_sink, window;
     int row;              // entries per row of sel: k + n_sink + window
+    int nx;               // XCDs (accelerator complexes) the grid is spread over
     int32_t *sel, *sel_count;
     float *sel_cutoff;
     float scale_log2;
@@ -75,16 +80,33 @@ struct DecodeArgs {
     int32_t *status;      // the workspace's status word (kStatusWaitTimeout bit)
     // Exchange buffers: zero before a launch, published with device-scope
     // stores of nonzero values, polled by the readers, zeroed again at the end.
-    int32_t *ctrl;        // [groups][4]: -, arrivals, timeout flag, -
+    int32_t *ctrl;        // [groups][4]: -, -, a timeout flag seeded by the host (read and cleared by workgroup 0), -
     uint64_t *lists;      // [L-2][groups][P][P] top P child keys per workgroup (kEmpty: none)
     uint64_t *leaf_keys;  // [groups][P][64] sorted leaf keys (kEmpty: none)
     int32_t *leaf_pre;    // [groups][P][64] 1 + inclusive prefix of eligible counts
     int32_t *keys;        // [groups][k] 1 + key id at each retrieval position
-    float *part;          // [groups][P][part_stride(G, d)]: output, then G maxima, then G sums
+    uint32_t *recs;       // [groups][P writers][P readers][rec_stride]: partial states (done tokens without attention)
 };
 
-// floats per partial state, padded so every state starts 16-byte aligned
-LSA_HOST_DEV inline int part_stride(int G, int d) { return (G * d + 2 * G + 3) & ~3; }
+// Partial-state records.  The G * d outputs of a group are cut into P slices,
+// slice p = [slice_lo(p), slice_lo(p + 1)), merged by workgroup p.  Workgroup
+// q sends p one record: its unnormalised outputs of slice p (at most
+// slice_max words), then the maximum and the sum of each head the slice
+// touches (at most slice_heads heads), each word stored as the complement of
+// the float's bits, so that a published word is never zero.
+// (32-bit: T * p stays below 2^31 for every buffer sliced here)
+LSA_HOST_DEV inline int slice_lo(int T, int P, int p) { return (T * p) / P; }
+LSA_HOST_DEV inline int slice_max(int T, int P) { return (T + P - 1) / P; }
+LSA_HOST_DEV inline int slice_heads(int T, int P, int d) { return slice_max(T, P) / d + 2; }
+LSA_HOST_DEV inline int rec_stride(int T, int P, int d, bool attend) {
+    return attend ? (slice_max(T, P) + 2 * slice_heads(T, P, d) + 3) & ~3 : 4;
+}
+LSA_DEV uint32_t enc_word(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0xFFFFFFFFu) u = 0x7FC00000u;     // (a NaN; any other float's complement is nonzero)
+    return ~u;
+}
+LSA_DEV float dec_word(uint32_t w) { return __uint_as_float(~w); }
 
 // ---------------------------------------------------------------- helpers
 // For key x and the descending key lists a + q * stride (q = q0, q0 + dq, ...
@@ -180,8 +202,8 @@ LSA_DEV void load_rows(float *Cs, const float *__restrict__ src, int b, int r) {
 
 // Polls the words src[e] (e = threadIdx.x + blockDim.x * u < n) until each is
 // nonzero; every round issues all of the thread's outstanding loads at once.
-// Bounded: after kSpinLimit rounds `flag` records a timeout and words still
-// zero are returned as zero.
+// Bounded: after kSpinLimit rounds `flag` (this workgroup's, in LDS) records a
+// timeout and words still zero are returned as zero.
 template <int U, typename W>
 LSA_DEV void poll_nonzero(const W *src, int n, W (&out)[U], int32_t *flag) {
 #pragma unroll
@@ -198,7 +220,35 @@ LSA_DEV void poll_nonzero(const W *src, int n, W (&out)[U], int32_t *flag) {
         for (int u = 0; u < U; ++u) missing |= ((int)threadIdx.x + (int)blockDim.x * u < n) && out[u] == 0;
         if (!missing) break;
         if (spins >= kSpinLimit) {
-            __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = 1;
+            break;
+        }
+    }
+}
+
+// Polls the word pairs a[e], c[e] (e = t + nt * u < n; t in [0, nt)) until
+// both are nonzero; every round issues the loads of both arrays at once.
+// Bounded like poll_nonzero.
+template <int U>
+LSA_DEV void poll_pair(const uint64_t *a, const int32_t *c, int n, int t, int nt, uint64_t (&oa)[U],
+                       int32_t (&oc)[U], int32_t *flag) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) { oa[u] = 0; oc[u] = 0; }
+    for (int spins = 0;; ++spins) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = t + nt * u;
+            if (e < n) {
+                if (oa[u] == 0) oa[u] = __hip_atomic_load(a + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (oc[u] == 0) oc[u] = __hip_atomic_load(c + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        bool missing = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) missing |= (t + nt * u < n) && (oa[u] == 0 || oc[u] == 0);
+        if (!missing) break;
+        if (spins >= kSpinLimit) {
+            *flag = 1;
             break;
         }
     }
@@ -233,15 +283,24 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64], skip_s[64];
     __shared__ int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
-    __shared__ int keep_s, count_s, last_s, flag_s;
+    __shared__ int keep_s, count_s, flag_s;
     __shared__ float m_run[16], l_run[16], alpha_s[16];
 
     constexpr bool kMfma = ATTEND && sizeof(T) == 2 && DC > 0 && DC % 32 == 0;
     const int r = RC > 0 ? RC : A.r;
     const int d = DC > 0 ? DC : A.d;
     const int P = PC > 0 ? PC : A.beam;      // workgroups per group (= beam)
-    const int p = blockIdx.x;
-    const int gi = blockIdx.y;
+    const size_t groups = (size_t)A.m * A.h_kv;
+    // Workgroups are dispatched to the XCDs in turn (workgroup w to XCD
+    // w mod nx), so every group is given workgroups of one XCD: its
+    // exchanges then travel through one L2, and what one of its workgroups
+    // loads the others find there.  Correctness does not depend on it (every
+    // exchange is device-scope); workgroups past the last group leave at once.
+    const int xw = (int)blockIdx.x % A.nx, qw = (int)blockIdx.x / A.nx;
+    const int p = qw % P;
+    const size_t gsl = (size_t)xw + (size_t)A.nx * (size_t)(qw / P);
+    if (gsl >= groups) return;
+    const int gi = (int)gsl;
     const int64_t i = gi / A.h_kv;
     const int g = gi % A.h_kv;
     const int G = A.h_q / A.h_kv;
@@ -251,11 +310,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     const int wv = tid / kWave;
     const T *Q = (const T *)A.Q;
     int32_t *ctrl = A.ctrl + (size_t)gi * 4;
+    int32_t seeded = 0;
     const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     const int64_t nleaf = A.nodes[L];
     const int32_t *perm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
     const int32_t *leaf_off = (const int32_t *)(A.index + A.leaf_off_off) + (size_t)g * (nleaf + 1);
-    const size_t groups = (size_t)A.m * A.h_kv;
 
     // ---- prologue: level-1 rows and counts, W_g and the group's queries.
     // With r = 64, L >= 3 and b <= 4 P, wave w of workgroup p also owns
@@ -317,7 +376,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             g2s_scalar<16, T, float>(Ql, G * d, Q + ((size_t)i * A.h_q + (size_t)g * G) * d, G * d, G * d);
         }
         if (tid < b) ccnt[tid] = cnt_r;
-        if (tid == 0) { count_s = 0; last_s = 0; }
+        if (tid == 0) { count_s = 0; flag_s = 0; }
+        // the group's host-seeded timeout flag (read here, reported and
+        // cleared at the end by workgroup 0 alone)
+        if (p == 0 && tid == 0) seeded = __hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // (issued after the stores above, so no wait there covers them: they
         // land while the latent query is computed)
         // Unconditional loads (a wave that owns no node reads the start of
@@ -463,7 +525,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             uint64_t *m1 = lk + kMaxP * kMaxP;                // [nm][P]
             {
                 uint64_t w[kMaxP * kMaxP / 256];
-                poll_nonzero(src, nc, w, ctrl + 2);
+                poll_nonzero(src, nc, w, &flag_s);
 #pragma unroll
                 for (int u = 0; u < kMaxP * kMaxP / 256; ++u) {
                     const int e = tid + 256 * u;
@@ -505,12 +567,13 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     // ---- fill: every workgroup places its own leaves' keys
     {
         {
-            // keys and prefix counts of all P lists, polled as they are published
+            // keys and prefix counts of all P lists, polled as they are
+            // published (both arrays in every round)
             constexpr int U = kMaxP * 64 / 256;
             uint64_t tk[U];
             int32_t tp[U];
-            poll_nonzero(A.leaf_keys + (size_t)gi * P * 64, P * 64, tk, ctrl + 2);
-            poll_nonzero(A.leaf_pre + (size_t)gi * P * 64, P * 64, tp, ctrl + 2);
+            poll_pair(A.leaf_keys + (size_t)gi * P * 64, A.leaf_pre + (size_t)gi * P * 64, P * 64, tid, 256, tk, tp,
+                      &flag_s);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = tid + 256 * u;
@@ -520,7 +583,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 if (e < P * 64) { lk[e] = (tk[u] == kEmpty) ? 0ull : tk[u]; lp[e] = min(max(tp[u] - 1, 0), A.k); }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (wv == 0) {
             int tot = (lane < P) ? lp[lane * 64 + 63] : 0;
             tot = wave_sum_i(tot);
@@ -545,7 +608,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             wpart[wv][lane] = part;
         }
-        __syncthreads();
+        lds_barrier();
         const int count = count_s;
         int32_t *out = A.sel + (size_t)gi * A.row;
         if (wv == 0) {
@@ -569,7 +632,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (x != 0 && count == A.k && wex < A.k && wex + e >= A.k && A.sel_cutoff)
                 A.sel_cutoff[gi] = key_score(x);
         }
-        __syncthreads();
+        lds_barrier();
         // own key f (all threads): its lane j is the last with toff_s[j] <= f
         const int own = toff_s[64];
         const bool staged = v >= 0 && (clo[b] - clo[0]) <= kMemCap;
@@ -608,7 +671,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         const int cnt_all = count_s;
         const int tot = cnt_all + as.nloc;
         const int lo = (int)(((int64_t)tot * p) / P), hi = (int)(((int64_t)tot * (p + 1)) / P);
-        float *pp = A.part + ((size_t)gi * P + p) * part_stride(G, d);
+        // the combined unnormalised outputs [G][d] in LDS (oc), the maxima
+        // and sums in m_run, l_run, then sent to the readers below
+        float *oc = kMfma ? dyn + 4 * kWave * (DC / 4) + 128 : dyn;
         if constexpr (kMfma) {
             const uint16_t *Kg = (const uint16_t *)A.K + (size_t)g * A.n * DC;
             const uint16_t *Vg = (const uint16_t *)A.V + (size_t)g * A.n * DC;
@@ -624,7 +689,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 const int nsteps = (own + 4 * kMT - 1) / (4 * kMT);
                 for (int f0 = 0; f0 < nr; f0 += 8 * 256) {
                     int32_t w[8];
-                    poll_nonzero(A.keys + (size_t)gi * A.k + c0 + f0, nr - f0, w, ctrl + 2);
+                    poll_nonzero(A.keys + (size_t)gi * A.k + c0 + f0, nr - f0, w, &flag_s);
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
                         if (f0 + tid + 256 * u < nr) own_s[f0 + tid + 256 * u] = clamp_id(w[u] - 1, A.n);
@@ -645,11 +710,14 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             }
             wave_attn_stash<DC>(st, dyn);
             __syncthreads();
+            // the four waves' states combined into [G][DC] in LDS, then sent
+            // one output a lane, so that each store instruction writes whole
+            // lines of a record
             for (int e4 = tid; e4 < G * DC / 4; e4 += blockDim.x) {
                 const int h = e4 / (DC / 4), dd = 4 * (e4 % (DC / 4));
                 float M, Ls;
-                *reinterpret_cast<floatx4_t *>(pp + h * DC + dd) = wave_attn_combine4<DC>(dyn, h, dd, M, Ls);
-                if (dd == 0) { pp[G * DC + h] = M; pp[G * DC + G + h] = Ls; }
+                *reinterpret_cast<floatx4_t *>(oc + h * DC + dd) = wave_attn_combine4<DC>(dyn, h, dd, M, Ls);
+                if (dd == 0) { m_run[h] = M; l_run[h] = Ls; }
             }
         } else {
             const int dp = d + 1;
@@ -673,7 +741,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 const int nr = max(0, min(nk, cnt_all - f0));      // retrieved entries of the tile
                 {
                     int32_t w[1];
-                    poll_nonzero(A.keys + (size_t)gi * A.k + f0, nr, w, ctrl + 2);
+                    poll_nonzero(A.keys + (size_t)gi * A.k + f0, nr, w, &flag_s);
                     if (tid < nr) ids_s[tid] = clamp_id(w[0] - 1, A.n);
                     else if (tid < nk) ids_s[tid] = local_key(as, f0 + tid - cnt_all);
                 }
@@ -727,99 +795,119 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 if (q >= ne) break;
                 const int e = tid + q * blockDim.x;
                 if (e >= G * d) break;
-                pp[e] = acc[q];
+                oc[e] = acc[q];
             }
-            if (tid < G) { pp[G * d + tid] = m_run[tid]; pp[G * d + G + tid] = l_run[tid]; }
+        }
+        lds_barrier();
+        // records, one per reader r (wave r % 4 sends it): the outputs of
+        // slice r, then the maximum and the sum of each head it touches
+        const int NO = G * d, SM = slice_max(NO, P), RS = rec_stride(NO, P, d, true);
+        uint32_t *mine = A.recs + ((size_t)gi * P + p) * P * RS;
+        for (int r = wv; r < P; r += 4) {
+            const int lo_r = slice_lo(NO, P, r), hi_r = slice_lo(NO, P, r + 1), hl = lo_r / d;
+            const int nh = hi_r > lo_r ? (hi_r - 1) / d - hl + 1 : 0;
+            uint32_t *rec = mine + (size_t)r * RS;
+            for (int e = lo_r + lane; e < hi_r; e += kWave) publish(rec + (e - lo_r), enc_word(oc[e]));
+            if (lane < 2 * nh) publish(rec + SM + lane, enc_word((lane & 1) ? l_run[hl + lane / 2] : m_run[hl + lane / 2]));
         }
     }
 
-    // ---- arrival; the last workgroup merges and resets the group's counters
-    // (the partial state is written by every wave)
-    wave_stores_done();
-    __syncthreads();
-    if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const int old = __hip_atomic_fetch_add(ctrl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_s = (old == P - 1);
-        if (last_s) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    if (!last_s) return;
-    // the group's timeout flag (every workgroup has arrived, so it is final),
-    // read now so that its round trip overlaps the merge
-    if (tid == 0) flag_s = __hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- merge.  Workgroup p polls the P records of its slice (with
+    // attention) or the P done tokens (without); once it has them all, every
+    // workgroup of the group is past its last exchange read.
+    const int NO = G * d, RS = rec_stride(NO, P, d, ATTEND);
+    uint32_t *recs_g = A.recs + (size_t)gi * P * P * RS;     // [writer][reader][RS]
     if constexpr (ATTEND) {
-        // each thread merges 4 consecutive outputs of one head: every load
-        // (the P partial outputs and each partial's max and sum) is issued
-        // before the first use
-        const int stride = part_stride(G, d);
-        const float *pb = A.part + (size_t)gi * P * stride;
-        float *ml = dyn;                                   // [P][2G]: maxima, sums
-        for (int e = tid; e < P * 2 * G; e += blockDim.x) ml[e] = pb[(size_t)(e / (2 * G)) * stride + G * d + e % (2 * G)];
-        __syncthreads();
-        for (int c4 = tid; c4 < G * d / 4; c4 += blockDim.x) {
-            const int e = 4 * c4, h = e / d;
-            float4 o[kMaxP];
-            float mq[kMaxP], lq[kMaxP];
+        // the words of this slice, record q's word j at rv[q][j] (j < sp: output
+        // lo + j; then the maximum and the sum of each head of the slice),
+        // polled by all threads with every load of a round in flight, and
+        // cleared once read (each has this one reader)
+        const int SM = slice_max(NO, P);
+        const int lo = slice_lo(NO, P, p), hi = slice_lo(NO, P, p + 1), hlo = lo / d;
+        const int sp = hi - lo, nh = hi > lo ? (hi - 1) / d - hlo + 1 : 0, len = sp + 2 * nh;
+        float *rv = (kMfma ? dyn + 4 * kWave * (DC / 4) + 128 : dyn) + G * d;
+        const int nw = P * len;
+        constexpr int U = 8;
+        for (int f0 = 0; f0 < nw; f0 += U * (int)blockDim.x) {
+            uint32_t w[U], *src[U];
 #pragma unroll
-            for (int q = 0; q < kMaxP; ++q)
-                if (q < P) o[q] = *reinterpret_cast<const float4 *>(pb + (size_t)q * stride + e);
+            for (int u = 0; u < U; ++u) {
+                const int f = f0 + tid + u * (int)blockDim.x, fc = min(f, nw - 1);
+                const int q = fc / len, j = fc - q * len;
+                src[u] = recs_g + ((size_t)q * P + p) * RS + (j < sp ? j : SM + (j - sp));
+                w[u] = f < nw ? 0u : 1u;          // (words past the slice: nothing to wait for)
+            }
+            for (int spins = 0;; ++spins) {
+                bool missing = false;
 #pragma unroll
-            for (int q = 0; q < kMaxP; ++q) {
-                if (q < P) {
-                    mq[q] = ml[q * 2 * G + h];
-                    lq[q] = ml[q * 2 * G + G + h];
+                for (int u = 0; u < U; ++u)
+                    if (w[u] == 0) w[u] = __hip_atomic_load(src[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int u = 0; u < U; ++u) missing |= w[u] == 0;
+                if (!missing) break;
+                if (spins >= kSpinLimit) { flag_s = 1; break; }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int f = f0 + tid + u * (int)blockDim.x;
+                if (f < nw) {
+                    rv[f] = dec_word(w[u]);
+                    publish(src[u], 0u);
                 }
             }
+        }
+        lds_barrier();
+        for (int e = lo + tid; e < hi; e += blockDim.x) {
+            const int h = e / d, jm = sp + 2 * (h - hlo);
             float M = -INFINITY;
-#pragma unroll
-            for (int q = 0; q < kMaxP; ++q) if (q < P) M = fmaxf(M, mq[q]);
-            float l = 0.0f;
-            float4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < kMaxP; ++q) {
-                if (q < P && mq[q] > -INFINITY) {
-                    const float w = exp2f(mq[q] - M);
-                    l += lq[q] * w;
-                    acc.x += o[q].x * w; acc.y += o[q].y * w; acc.z += o[q].z * w; acc.w += o[q].w * w;
+            for (int q = 0; q < P; ++q) M = fmaxf(M, rv[q * len + jm]);
+            float l = 0.0f, acc = 0.0f;
+            for (int q = 0; q < P; ++q) {
+                const float mq = rv[q * len + jm];
+                if (mq > -INFINITY) {
+                    const float w = exp2f(mq - M);
+                    l += rv[q * len + jm + 1] * w;
+                    acc += rv[q * len + (e - lo)] * w;
                 }
             }
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
             const size_t oh = (size_t)i * A.h_q + (size_t)g * G + h;
-            T *op = (T *)A.out + oh * d + (e % d);
-            op[0] = from_float<T>(acc.x * inv); op[1] = from_float<T>(acc.y * inv);
-            op[2] = from_float<T>(acc.z * inv); op[3] = from_float<T>(acc.w * inv);
+            ((T *)A.out)[oh * d + (e % d)] = from_float<T>(l > 0.0f ? acc / l : 0.0f);
             if ((e % d) == 0 && A.lse) A.lse[oh] = (l > 0.0f) ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
-    }
-    // every workgroup has arrived and the merge has read the partial states,
-    // so no one reads the group's part of the workspace any more: leave all of
-    // it zeroed for the next launch (a launch of another shape lays its
-    // exchange buffers over this one's partial states)
-    __syncthreads();
-    if (ATTEND) {
-        const size_t np = (size_t)P * part_stride(G, d);
-        f4_t *pz = reinterpret_cast<f4_t *>(A.part + (size_t)gi * np);
-        for (size_t e = tid; e < np / 4; e += blockDim.x) pz[e] = f4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int e = tid; e < (L - 2) * P * P; e += blockDim.x)
-        publish(A.lists + ((size_t)(e / (P * P)) * groups + gi) * P * P + e % (P * P), (uint64_t)0);
-    for (int e = tid; e < P * 64; e += blockDim.x) {
-        publish(A.leaf_keys + (size_t)gi * P * 64 + e, (uint64_t)0);
-        publish(A.leaf_pre + (size_t)gi * P * 64 + e, 0);
-    }
-    if (ATTEND)
-        for (int e = tid; e < count_s; e += blockDim.x) publish(A.keys + (size_t)gi * A.k + e, 0);
-    if (tid == 0) {
-        // a bounded wait of this group gave up (its results may be wrong):
-        // report it in the status word, which stays set until the host reads
-        // it, and clear the group's flag so that no later launch reads it as
-        // a published word
-        if (flag_s != 0) {
-            __hip_atomic_fetch_or(A.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            publish(ctrl + 2, 0);
+    } else {
+        // done tokens: this workgroup's to every reader, then the P addressed to it
+        if (tid < P) {
+            publish(recs_g + ((size_t)p * P + tid) * RS, 1u);
+            const uint32_t *tok = recs_g + ((size_t)tid * P + p) * RS;     // writer tid's token to this workgroup
+            for (int spins = 0;; ++spins) {
+                if (__hip_atomic_load(tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+                if (spins >= kSpinLimit) { flag_s = 1; break; }
+            }
         }
-        publish(ctrl + 1, 0);
+    }
+    // every workgroup of the group is past its exchange reads: clear the
+    // exchange words, each workgroup one slice of every buffer
+    {
+        auto clear32 = [&](int32_t *base, int n) {
+            for (int e = slice_lo(n, P, p) + tid; e < slice_lo(n, P, p + 1); e += blockDim.x) publish(base + e, 0);
+        };
+        auto clear64 = [&](uint64_t *base, int n) {
+            for (int e = slice_lo(n, P, p) + tid; e < slice_lo(n, P, p + 1); e += blockDim.x) publish(base + e, (uint64_t)0);
+        };
+        for (int l = 0; l < L - 2; ++l) clear64(A.lists + ((size_t)l * groups + gi) * P * P, P * P);
+        clear64(A.leaf_keys + (size_t)gi * P * 64, P * 64);
+        clear32(A.leaf_pre + (size_t)gi * P * 64, P * 64);
+        if (ATTEND) clear32(A.keys + (size_t)gi * A.k, count_s);
+    }
+    if (!ATTEND && tid < P) publish(recs_g + ((size_t)tid * P + p) * RS, 0u);
+    lds_barrier();
+    if (tid == 0) {
+        // a bounded wait of this workgroup gave up (results may be wrong), or
+        // workgroup 0 found the group's seeded flag: report it in the status
+        // word, which stays set until the host reads it
+        if (flag_s != 0 || seeded != 0)
+            __hip_atomic_fetch_or(A.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seeded != 0) publish(ctrl + 2, 0);
     }
 }
 
@@ -827,11 +915,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodeWs {
-    int32_t *status, *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre, *keys; float *part; size_t bytes;
+    int32_t *status, *ctrl; uint64_t *lists, *leaf_keys; int32_t *leaf_pre, *keys; uint32_t *recs; size_t bytes;
 };
 
 // Workspace layout: the status word (kWsHeader bytes), then the exchange
-// buffers, then the partial softmax states.
+// buffers and the partial-state records, all polled.
 static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G, int d, int k) {
     size_t cur = 0;
     DecodeWs w{};
@@ -842,7 +930,7 @@ static DecodeWs carve_decode_ws(char *base, int64_t groups, int P, int L, int G,
     w.leaf_keys = (uint64_t *)take(sizeof(uint64_t) * (size_t)groups * P * 64);
     w.leaf_pre = (int32_t *)take(sizeof(int32_t) * (size_t)groups * P * 64);
     w.keys = (int32_t *)take(sizeof(int32_t) * (size_t)groups * k);
-    w.part = (float *)take(sizeof(float) * (size_t)groups * P * (size_t)part_stride(G, d));
+    w.recs = (uint32_t *)take(sizeof(uint32_t) * (size_t)groups * P * P * (size_t)rec_stride(G * d, P, d, true));
     w.bytes = cur;
     return w;
 }
@@ -860,21 +948,40 @@ int device_cus() {
     return c;
 }
 
+// XCDs of the current device (1 when the runtime cannot say): the decode grid
+// gives each group workgroups of one XCD.
+int device_xccs() {
+    static std::atomic<int> xcc[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    int c = xcc[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || c < 1) c = 1;
+        xcc[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+// Workgroups of the decode grid: nx XCDs x (groups per XCD, rounded up) x beam.
+static int64_t decode_grid(int64_t groups, int beam, int nx) { return (int64_t)nx * ((groups + nx - 1) / nx) * beam; }
+
 static bool fast_shape(int dtype, int d, int r) { return dtype == 1 && d == 128 && r == 64; }
 
-static size_t decode_dyn_bytes(int dtype, int G, int d, int r) {
+static size_t decode_dyn_bytes(int dtype, int G, int d, int r, int P) {
     // W (double in the fast shape), Q staging
     const size_t stage = (fast_shape(dtype, d, r) ? sizeof(double) : sizeof(float)) * (size_t)d * r +
                          sizeof(float) * (size_t)G * d;
+    // attention, then the combined outputs and the polled records of the merge
+    const size_t merge_words = (size_t)G * d + (size_t)P * rec_stride(G * d, P, d, true);
     size_t att;
     if (fast_shape(dtype, d, r))
-        att = std::max(sizeof(uint16_t) * 4 * (size_t)d * kVTS, sizeof(float) * (4 * (size_t)d * 16 + 128));
+        att = std::max(sizeof(uint16_t) * 4 * (size_t)d * kVTS, sizeof(float) * (4 * (size_t)d * 16 + 128 + merge_words));
     else
-        att = sizeof(float) * ((size_t)G * d + (size_t)kTKD * (d + 1) + (size_t)kTKD * d + (size_t)G * kTKD);
-    const size_t merge = sizeof(float) * (2 * kMaxP * 16 + 32);
+        att = sizeof(float) * std::max((size_t)G * d + (size_t)kTKD * (d + 1) + (size_t)kTKD * d + (size_t)G * kTKD,
+                                       merge_words);
     // fast shape: four waves' level-2 node blocks (64 rows at stride kCS)
     const size_t pre = fast_shape(dtype, d, r) ? sizeof(float) * 4 * 64 * (size_t)kCS : 0;
-    return std::max(std::max(stage, pre), std::max(att, merge));
+    return std::max(std::max(stage, pre), att);
 }
 
 constexpr size_t kStaticLds = 64 * 1024;      // upper bound of k_decode's static LDS
@@ -883,12 +990,12 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 bool decode_path_ok(int64_t m, int h_q, int h_kv, int d, int r, int b, int L, int beam, int k) {
     const int G = h_q / h_kv;
     if (L < 2 || b > 64 || r > 64 || beam > kMaxP || beam < 1 || G > 16 || d > 256 || d % 8 != 0) return false;
-    if (decode_dyn_bytes(0, G, d, r) + kStaticLds > kLdsPerCu) return false;
+    if (decode_dyn_bytes(0, G, d, r, beam) + kStaticLds > kLdsPerCu) return false;
     (void)k;
-    // every workgroup of a group must be resident at once (one per compute
-    // unit at this kernel's LDS size)
+    // every workgroup of a group must be resident at once: the whole grid,
+    // one workgroup per compute unit at this kernel's LDS size
     const int cus = device_cus();
-    return cus > 0 && m * h_kv * beam <= cus;
+    return cus > 0 && decode_grid(m * h_kv, beam, device_xccs()) <= cus;
 }
 
 int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int beam, int k) {
@@ -896,14 +1003,16 @@ int64_t decode_workspace_bytes(int64_t m, int h_q, int h_kv, int d, int L, int b
 }
 
 // An upper bound on the bytes from the start of a workspace that this path
-// polls (the status word and everything before the partial softmax states),
-// over every batch it accepts: groups * beam <= compute units, beam <= kMaxP,
-// L <= LSA_MAX_LEVELS, k <= 8192.
+// polls (all of its workspace), over every batch it accepts:
+// groups * beam <= compute units, beam <= kMaxP, L <= LSA_MAX_LEVELS,
+// k <= 8192, G * d <= 16 * 256.  A group's records take
+// beam * beam * rec_stride <= beam * (G * d + 2 G + 13 beam) words.
 int64_t decode_polled_bytes_bound() {
     const int64_t c = std::max(device_cus(), 1);
     const int64_t ctrl = sizeof(int32_t) * 4 * c, lists = sizeof(uint64_t) * (LSA_MAX_LEVELS - 2) * c * kMaxP;
     const int64_t leaf = (sizeof(uint64_t) + sizeof(int32_t)) * c * 64, keys = sizeof(int32_t) * c * 8192;
-    return kWsHeader + ctrl + lists + leaf + keys + 5 * 256;
+    const int64_t recs = sizeof(uint32_t) * c * (16 * 256 + 2 * 16 + 13 * kMaxP);
+    return kWsHeader + ctrl + lists + leaf + keys + recs + 6 * 256;
 }
 
 // The other paths place their buffers after this many bytes of a workspace,
@@ -976,12 +1085,13 @@ hipError_t decode(const void *Q, const void *K, const void *V, int dtype, int64_
     A.n_sink = n_sink; A.window = window; A.row = k + n_sink + window;
     A.sel = sel; A.sel_count = sel_count; A.sel_cutoff = sel_cutoff;
     A.scale_log2 = scale * 1.4426950408889634f; A.out = out; A.lse = lse;
+    A.nx = device_xccs();
     const int G = h_q / h_kv;
     DecodeWs w = carve_decode_ws((char *)ws, m * h_kv, beam, L, G, d, k);
     A.status = w.status; A.ctrl = w.ctrl; A.lists = w.lists; A.leaf_keys = w.leaf_keys; A.leaf_pre = w.leaf_pre; A.keys = w.keys;
-    A.part = w.part;
-    const size_t shm = decode_dyn_bytes(dtype, G, d, r);
-    const dim3 grid((unsigned)beam, (unsigned)(m * h_kv));
+    A.recs = w.recs;
+    const size_t shm = decode_dyn_bytes(dtype, G, d, r, beam);
+    const dim3 grid((unsigned)decode_grid(m * h_kv, beam, A.nx));
     if (fast_shape(dtype, d, r) && beam == 16) {
         return attend ? launch_decode<bf16_t, true, 64, 128, 16>(A, grid, shm, st)
                       : launch_decode<bf16_t, false, 64, 128, 16>(A, grid, shm, st);

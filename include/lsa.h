@@ -35,7 +35,8 @@
  *     workgroups (the multi-workgroup select of lsa_select and
  *     lsa_select_attend) bound every wait; a wait that gives up sets
  *     LSA_STATUS_WAIT_TIMEOUT in the status word of the call's workspace
- *     (its results may then be wrong), which lsa_workspace_status reads.
+ *     (its results may then be wrong, and the workspace must be zero-filled
+ *     again before its next use), which lsa_workspace_status reads.
  *   - Debug mode: with the environment variable LSA_DEBUG set to a value
  *     other than "0" when the library is first used, every entry point also
  *     checks on the host, before enqueueing, the index it reads (as
@@ -288,10 +289,11 @@ int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *
  * k + n_sink + window <= 2^24.
  *
  * Workspace: ws may be NULL.  When ws holds at least
- * lsa_select_workspace_bytes bytes (> 0), small batches (m * h_kv * beam up
- * to the number of compute units, L >= 2, beam <= 32) run on beam
- * workgroups per (row, KV head) that exchange their partial rankings through
- * ws (words published into zeroed memory and polled by the readers).  The
+ * lsa_select_workspace_bytes bytes (> 0), small batches run on beam
+ * workgroups per (row, KV head) group, all of one group on one XCD (L >= 2,
+ * beam <= 32, and XCDs * ceil(m * h_kv / XCDs) * beam at most the number of
+ * compute units), that exchange their partial rankings through ws (words
+ * published into zeroed memory and polled by the readers).  The
  * caller zero-fills ws once before its first use.  Those workgroups poll only
  * a prefix of ws that no other path of lsa_select, lsa_select_attend,
  * lsa_select_flat or lsa_attend writes (their buffers start after it), and

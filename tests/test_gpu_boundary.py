@@ -142,7 +142,7 @@ def test_gpu_index_export_import_round_trip(lsa):
 
 def test_wait_timeout_flag_reaches_the_status_word(lsa):
     """A group's timeout flag, set from the host before a normal one-launch
-    call (so no wait is forced), is moved by the call's last workgroup into
+    call (so no wait is forced), is reported by the group's workgroup 0 in
     the workspace's status word and cleared in place; lsa_workspace_status
     reads and clears the status word.  Results are unaffected."""
     dev = torch.device("cuda:0")
