@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
     __shared__ __attribute__((aligned(16))) uint64_t lk[kMaxP * 64];
     __shared__ int32_t lp[kMaxP * 64];
     __shared__ int32_t toff_s[65], a0_s[64], wex_s[64], wpart[4][64], skip_s[64];
-    __shared__ int32_t own_s[kOwnCap + 4 * kMT];
+    __shared__ __attribute__((aligned(16))) int32_t own_s[kOwnCap + 4 * kMT];
     __shared__ int32_t mem_s[kMemCap];
     __shared__ int keep_s, count_s, flag_s;
     __shared__ float m_run[16], l_run[16], alpha_s[16];
@@ -441,10 +441,27 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                 }
                 wave_sync();
                 uint64_t key = 0;
-                int e = 0;
                 if (lane < b && rcnt > 0) key = make_key(score_lds<RC>(u_s, Rs + lane * kCS, r), (uint32_t)(vw * b + lane));
-                wave_sort_desc(key, e);
-                if (lane < P) publish(A.lists + ((size_t)gi * P + rank) * P + lane, key ? key : kEmpty);
+                // the top P by rank (the number of larger keys, over all 64
+                // in this wave's slice of own_s; empty slots get distinct
+                // keys below every real one and stay empty)
+                uint64_t *wk = reinterpret_cast<uint64_t *>(own_s + wv * 192), *wt = wk + 64;
+                wk[lane] = key ? key : (uint64_t)(63 - lane);
+                wave_sync();
+                const uint64_t x = wk[lane];
+                int above = 0;
+#pragma unroll
+                for (int j = 0; j < 64; j += 2) {
+                    const uint4 kk = *reinterpret_cast<const uint4 *>(wk + j);
+                    above += ((((uint64_t)kk.y << 32) | kk.x) > x) ? 1 : 0;
+                    above += ((((uint64_t)kk.w << 32) | kk.z) > x) ? 1 : 0;
+                }
+                if (above < P) wt[above] = x;
+                wave_sync();
+                if (lane < P) {
+                    const uint64_t t = wt[lane];
+                    publish(A.lists + ((size_t)gi * P + rank) * P + lane, t >= (1ull << 32) ? t : kEmpty);
+                }
             }
         }
         if (wv == 0 && p >= keep && lane < P) publish(A.lists + ((size_t)gi * P + p) * P + lane, kEmpty);
@@ -485,6 +502,12 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
             if (mn <= kMemCap) g2s_flat<8>(mem_s, perm + clo[0], mn);
             __syncthreads();
         }
+        // wave 0 scores the node's children; then all four waves rank them
+        // (the rank of a key is the number of larger keys; empty slots get
+        // distinct keys below every real one and stay empty), in LDS that is
+        // free until the fill (own_s, wpart)
+        uint64_t *rk_key = reinterpret_cast<uint64_t *>(own_s), *rk_sk = rk_key + 64;
+        int32_t *rk_e = own_s + 256, *rk_se = own_s + 320;
         if (wv == 0) {
             uint64_t key = 0;
             int e = 0;
@@ -500,7 +523,26 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
                     if (e == 0) key = 0;
                 }
             }
-            wave_sort_desc(key, e);
+            rk_key[lane] = key ? key : (uint64_t)(63 - lane);
+            rk_e[lane] = e;
+        }
+        lds_barrier();
+        {
+            const uint64_t x = rk_key[lane];
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c += (rk_key[16 * wv + j] > x) ? 1 : 0;
+            wpart[wv][lane] = c;
+        }
+        lds_barrier();
+        if (wv == 0) {
+            const int rank = wpart[0][lane] + wpart[1][lane] + wpart[2][lane] + wpart[3][lane];
+            rk_sk[rank] = rk_key[lane];
+            rk_se[rank] = rk_e[lane];
+            wave_sync();
+            uint64_t key = rk_sk[lane];
+            const int e = rk_se[lane];
+            if (key < (1ull << 32)) key = 0;      // (an empty slot)
             if (!leaf) {
                 if (lane < P) publish(A.lists + (((size_t)(l - 2) * groups + gi) * P + p) * P + lane, key ? key : kEmpty);
             } else {
