@@ -402,18 +402,50 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs A) {
         qbar_s[t] = (double)(float)(s / (double)G);
     }
     lds_barrier();
-    for (int c = tid; c < r; c += blockDim.x) {
-        double s = 0.0;
-        if constexpr (DC > 0) {
-#pragma unroll 32
-            for (int t = 0; t < DC; ++t) {
-                if constexpr (kPreShape) s = fma(qbar_s[t], Wd[t * r + c], s);
-                else s = fma(qbar_s[t], (double)Wl[t * r + c], s);
-            }
-        } else {
-            for (int t = 0; t < d; ++t) s = fma(qbar_s[t], (double)Wl[t * r + c], s);
+    if constexpr (kPreShape) {
+        // u_c = fl32 of the sequential double sum over t of qbar_t W[t][c]
+        // (each product exact).  The four waves sum dims 32 w .. 32 w + 31
+        // and the terms' magnitudes; wave 0 adds the partials.  The sequential
+        // sum and this one both lie within 161 u A of the exact sum (u = 2^-53,
+        // A the sum of magnitudes), so with B = 256 u A (plus an underflow
+        // floor) covering that and the rounding of S +- B: when S - B and
+        // S + B round to the same float, so does the sequential sum; any
+        // other lane takes the sequential chain itself.
+        double *part = reinterpret_cast<double *>(Ql);       // [8][64] (the Q staging, read above)
+        double s = 0.0, a = 0.0;
+#pragma unroll
+        for (int t = 32 * wv; t < 32 * wv + 32; ++t) {
+            const double q = qbar_s[t], w = Wd[t * 64 + lane];
+            s = fma(q, w, s);
+            a = fma(fabs(q), fabs(w), a);
         }
-        u_s[c] = (double)(float)s;
+        part[wv * 64 + lane] = s;
+        part[(4 + wv) * 64 + lane] = a;
+        lds_barrier();
+        if (wv == 0) {
+            const double S = ((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane];
+            const double A2 = ((part[256 + lane] + part[320 + lane]) + part[384 + lane]) + part[448 + lane];
+            const double B = A2 * 0x1p-45 + 0x1p-1060;
+            const float lo = (float)(S - B), hi = (float)(S + B);
+            float v = lo;
+            if (__float_as_uint(lo) != __float_as_uint(hi)) {
+                double q = 0.0;
+                for (int t = 0; t < DC; ++t) q = fma(qbar_s[t], Wd[t * 64 + lane], q);
+                v = (float)q;
+            }
+            u_s[lane] = (double)v;
+        }
+    } else {
+        for (int c = tid; c < r; c += blockDim.x) {
+            double s = 0.0;
+            if constexpr (DC > 0) {
+#pragma unroll 32
+                for (int t = 0; t < DC; ++t) s = fma(qbar_s[t], (double)Wl[t * r + c], s);
+            } else {
+                for (int t = 0; t < d; ++t) s = fma(qbar_s[t], (double)Wl[t * r + c], s);
+            }
+            u_s[c] = (double)(float)s;
+        }
     }
     lds_barrier();
     // ---- level 1 (every workgroup of the group computes the same ranking)
