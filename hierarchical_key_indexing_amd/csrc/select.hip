@@ -233,6 +233,74 @@ LSA_DEV void fill_members(const int32_t *__restrict__ pm, int32_t *__restrict__ 
     }
 }
 
+// Positions of sel the block copy below covers (count <= kFlatCap).
+constexpr int kFlatCap = 2048;
+
+// The same copy with one retrieval position per lane: position f holds
+// member f - off of the last taken leaf whose offset off <= f.  Each taken
+// leaf marks its offset with its sorted position (KPT * thread + ii, which
+// increases with the offset) in `lead` (kFlatCap ints, LDS), a max scan
+// carries the marks forward, and dl[leaf] = a0 - off turns a position into
+// its member index.  Consecutive lanes then load and store consecutive
+// positions: 8 loads and 8 stores a thread for 2048 keys, where the copy by
+// leaves issues 4 x 8 mostly masked ones.  Needs count <= kFlatCap; lead and
+// dl (KPT * 256 ints) must not be in use by other threads on entry.
+template <int KPT>
+LSA_DEV void fill_members_flat(const int32_t *__restrict__ pm, int32_t *__restrict__ out, const int (&take)[KPT],
+                               const int (&a0v)[KPT], const int (&offv)[KPT], int count, int *lead, int *dl,
+                               int *scratch) {
+    constexpr int PER = kFlatCap / 256;
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+    int4 *l4 = reinterpret_cast<int4 *>(lead + PER * tid);
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) l4[j] = int4{-1, -1, -1, -1};
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < KPT; ++ii)
+        if (take[ii] > 0) { lead[offv[ii]] = KPT * tid + ii; dl[KPT * tid + ii] = a0v[ii] - offv[ii]; }
+    __syncthreads();
+    // running maximum over the thread's PER positions, then over the threads
+    // before it (lanes of its wave through shifts, earlier waves through LDS)
+    int v[PER];
+    {
+        int m = -1;
+#pragma unroll
+        for (int j = 0; j < PER / 4; ++j) {
+            const int4 q = l4[j];
+            m = max(m, q.x); v[4 * j] = m;
+            m = max(m, q.y); v[4 * j + 1] = m;
+            m = max(m, q.z); v[4 * j + 2] = m;
+            m = max(m, q.w); v[4 * j + 3] = m;
+        }
+        int incl = m;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl = max(incl, t);
+        }
+        if (lane == kWave - 1) scratch[wv] = incl;
+        int carry = __shfl_up(incl, 1);
+        if (lane == 0) carry = -1;
+        __syncthreads();
+        for (int q = 0; q < wv; ++q) carry = max(carry, scratch[q]);
+#pragma unroll
+        for (int j = 0; j < PER / 4; ++j)
+            l4[j] = int4{max(carry, v[4 * j]), max(carry, v[4 * j + 1]), max(carry, v[4 * j + 2]), max(carry, v[4 * j + 3])};
+    }
+    __syncthreads();
+    int32_t x[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int f = tid + 256 * j;
+        x[j] = (f < count) ? pm[dl[max(lead[f], 0)] + f] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int f = tid + 256 * j;
+        if (f < count) out[f] = x[j];
+    }
+}
+
 // u . row (64 floats) in double, ascending index; the row comes straight from
 // global memory in two halves (each half's 8 loads issued before its FMAs),
 // u from LDS.  Halves keep fewer registers live, so more waves stay resident.
@@ -834,7 +902,9 @@ __global__ __launch_bounds__(256) void k_nm_keep(NmArgs N) {
 // KPT = 4: 1024 candidate slots; KPT = 2: the 512 packed slots of b <= 32
 template <int KPT>
 __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
-    __shared__ __attribute__((aligned(16))) uint64_t sk[1024];
+    __shared__ __attribute__((aligned(16))) uint64_t sk[1024];   // the sort's, then the copy's position marks
+    __shared__ int dl_s[256 * KPT];
+    static_assert(sizeof(sk) >= kFlatCap * sizeof(int), "the position marks reuse the sort's array");
     __shared__ int scratch[8];
     __shared__ float cut_s;
     __shared__ unsigned long long msk_s[kFastP];
@@ -882,7 +952,8 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
             if (take[ii] < e4[ii]) { bnd_s[0] = slot; bnd_s[1] = pm[a0v[ii] + take[ii] - 1]; }
         }
     }
-    fill_members<KPT, 8>(pm, out, take, a0v, offv);
+    if (count <= kFlatCap) fill_members_flat<KPT>(pm, out, take, a0v, offv, count, reinterpret_cast<int *>(sk), dl_s, scratch);
+    else fill_members<KPT, 8>(pm, out, take, a0v, offv);
     const AttnSet as = attn_set(A.q_pos[i], A.n, A.n_sink, A.window);
     for (int t = tid; t < as.nloc; t += blockDim.x) out[count + t] = local_key(as, t);
     for (int t = count + as.nloc + tid; t < A.row; t += blockDim.x) out[t] = -1;
