@@ -607,6 +607,7 @@ __global__ __launch_bounds__(256) void k_nm_zero(NmArgs N, int64_t count) {
 
 constexpr int kNmChunk = 2048;      // pair entries per counting workgroup
 constexpr int kNmBins = 16384;      // (head, node) counters held in LDS (larger tables go straight to memory)
+constexpr int kNmSparse = 8192;     // from this many bins a fill workgroup reserves runs from its entries
 
 // the (head, node) bin of pair entry e, or -1 when the slot is empty
 LSA_DEV int64_t nm_bin(const NmArgs &N, int64_t e) {
@@ -641,24 +642,43 @@ __global__ __launch_bounds__(256) void k_nm_count(NmArgs N, int64_t nbins) {
 }
 
 // exclusive scan of ncnt[0..count) into noff and fptr, total at noff[count]
-__global__ __launch_bounds__(256) void k_nm_scan(NmArgs N, int64_t count) {
-    __shared__ int scr[8];
+constexpr int kNmScanT = 1024, kNmScanV = 16;   // threads, counts a thread (one round covers 16384 bins)
+__global__ __launch_bounds__(kNmScanT) void k_nm_scan(NmArgs N, int64_t count) {
+    __shared__ int scr[kNmScanT / kWave + 1];
+    const bool al = (((uintptr_t)N.ncnt | (uintptr_t)N.noff | (uintptr_t)N.fptr) & 15) == 0;
     int carry = 0;
-    for (int64_t base = 0; base < count; base += 256 * 8) {
-        int v[8], s = 0;
+    for (int64_t base = 0; base < count; base += (int64_t)kNmScanT * kNmScanV) {
+        const int64_t e0 = base + (int64_t)threadIdx.x * kNmScanV;
+        const bool whole = al && e0 + kNmScanV <= count;
+        int v[kNmScanV], s = 0;
+        if (whole) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
-            v[u] = e < count ? N.ncnt[e] : 0;
-            s += v[u];
+            for (int q = 0; q < kNmScanV / 4; ++q) {
+                const int4 x = *reinterpret_cast<const int4 *>(N.ncnt + e0 + 4 * q);
+                v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kNmScanV; ++u) v[u] = e0 + u < count ? N.ncnt[e0 + u] : 0;
         }
+#pragma unroll
+        for (int u = 0; u < kNmScanV; ++u) s += v[u];
         int tot;
         int run = carry + block_excl_scan(s, scr, &tot);
+        int o[kNmScanV];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * 8 + u;
-            if (e < count) { N.noff[e] = run; N.fptr[e] = run; }
-            run += v[u];
+        for (int u = 0; u < kNmScanV; ++u) { o[u] = run; run += v[u]; }
+        if (whole) {
+#pragma unroll
+            for (int q = 0; q < kNmScanV / 4; ++q) {
+                const int4 x = int4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+                *reinterpret_cast<int4 *>(N.noff + e0 + 4 * q) = x;
+                *reinterpret_cast<int4 *>(N.fptr + e0 + 4 * q) = x;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kNmScanV; ++u)
+                if (e0 + u < count) { N.noff[e0 + u] = o[u]; N.fptr[e0 + u] = o[u]; }
         }
         carry += tot;
     }
@@ -692,8 +712,21 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
         rk[u] = bin[u] >= 0 ? atomicAdd(&h_s[bin[u]], 1) : 0;
     }
     __syncthreads();
-    for (int u = threadIdx.x; u < nbins; u += blockDim.x)
-        if (h_s[u] > 0) h_s[u] = atomicAdd(N.fptr + u, h_s[u]);          // this workgroup's run
+    // this workgroup's run of each bin
+    if (nbins >= kNmSparse) {
+        // few entries per bin: reserved by the bin's first entry here, every
+        // reservation of a thread in flight together
+        int run[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) run[u] = (bin[u] >= 0 && rk[u] == 0) ? atomicAdd(N.fptr + bin[u], h_s[bin[u]]) : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (bin[u] >= 0 && rk[u] == 0) h_s[bin[u]] = run[u];
+    } else {
+        // many: one pass over the bins (consecutive bins a wave)
+        for (int u = threadIdx.x; u < nbins; u += blockDim.x)
+            if (h_s[u] > 0) h_s[u] = atomicAdd(N.fptr + u, h_s[u]);
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -1053,7 +1086,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
                                cnt);
             const size_t hb = cnt <= kNmBins ? (size_t)cnt * sizeof(int) : 0;
             hipLaunchKernelGGL(k_nm_count, dim3(cg), dim3(256), hb, st, N, cnt);
-            hipLaunchKernelGGL(k_nm_scan, dim3(1), dim3(256), 0, st, N, cnt);
+            hipLaunchKernelGGL(k_nm_scan, dim3(1), dim3(kNmScanT), 0, st, N, cnt);
             hipLaunchKernelGGL(k_nm_fill, dim3(cg), dim3(256), hb, st, N, cnt);
             const bool packed = A.b <= 32;
             hipLaunchKernelGGL(k_nm_score_mfma, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
