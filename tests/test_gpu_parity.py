@@ -672,7 +672,12 @@ NM_CASES = [("nm_b64_L2", dict(n=20000, h_q=16, h_kv=2, d=128, dtype="bf16", r=6
             ("nm_b16_L3", dict(n=30000, h_q=8, h_kv=4, d=64, dtype="f32", r=64, b=16, L=3, beam=16, k=700,
                                centres=900, m=500, mode="chunk")),
             ("nm_b32_L3_all", dict(n=6000, h_q=4, h_kv=1, d=128, dtype="bf16", r=64, b=32, L=3, beam=5, k=300,
-                                   centres=300, m=6000, mode="all"))]
+                                   centres=300, m=6000, mode="all")),
+            # about 5 keys a leaf and k = 3000: rows take more than 512 of the
+            # 1024 candidate leaves (the largest finish network) and more than
+            # 2048 keys (the copy by leaves)
+            ("nm_b64_L2_wide", dict(n=20000, h_q=8, h_kv=2, d=64, dtype="f32", r=64, b=64, L=2, beam=16, k=3000,
+                                    centres=1024, m=300, mode="chunk"))]
 
 
 @pytest.mark.parametrize("name,over", NM_CASES, ids=[c[0] for c in NM_CASES])
