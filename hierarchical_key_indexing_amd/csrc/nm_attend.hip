@@ -646,44 +646,39 @@ __global__ __launch_bounds__(256) void k_nma_merge(NmaArgs A) {
     const int64_t grp = (int64_t)blockIdx.x * gpw + tid / per;
     if (tid >= gpw * per || grp >= A.groups) return;
     const int h = (tid % per) / 16, dd = 8 * (tid % 16);
-    const int P = A.keep[grp];
     const floatx4_t *rec = A.pml + (size_t)grp * kNmaP * G + h;
     const int16_t *po = A.po + ((size_t)grp * kNmaP * G + h) * kNmaD + dd;
     typedef int16_t h8_t __attribute__((ext_vector_type(8)));
+    typedef float f3_t __attribute__((ext_vector_type(3)));
+    // the kept count and every slot's {m, l, unit} in one round (records of
+    // slots at or past the kept count are stale and masked below), then the
+    // kept states' outputs in the next, all sixteen loads in flight (slots
+    // past the count reload slot 0, unused)
+    const int P = A.keep[grp];
+    f3_t r[kNmaP];
+#pragma unroll
+    for (int j = 0; j < kNmaP; ++j) r[j] = *reinterpret_cast<const f3_t *>(rec + (size_t)j * G);
+    h8_t v[kNmaP];
+#pragma unroll
+    for (int j = 0; j < kNmaP; ++j) v[j] = *reinterpret_cast<const h8_t *>(po + (size_t)(j < P ? j : 0) * G * kNmaD);
     // the states' maxima and sums, then each output's weight l_j 2^(m_j - M)
     // times the unit of its 16-bit values (0 for an empty state)
-    float mj[kNmaP], lj[kNmaP], uj[kNmaP];
-#pragma unroll
-    for (int j = 0; j < kNmaP; ++j) {
-        const floatx4_t r = j < P ? rec[(size_t)j * G] : floatx4_t{-INFINITY, 0.0f, 0.0f, 0.0f};
-        mj[j] = r[0];
-        lj[j] = r[1];
-        uj[j] = r[2];
-    }
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kNmaP; ++j) M = fmaxf(M, mj[j]);
+    for (int j = 0; j < kNmaP; ++j) M = fmaxf(M, j < P ? r[j][0] : -INFINITY);
     float l = 0.0f, wo[kNmaP];
 #pragma unroll
     for (int j = 0; j < kNmaP; ++j) {
-        const float wl = mj[j] == -INFINITY ? 0.0f : lj[j] * __builtin_amdgcn_exp2f(mj[j] - M);
+        const float wl = (j >= P || r[j][0] == -INFINITY) ? 0.0f : r[j][1] * __builtin_amdgcn_exp2f(r[j][0] - M);
         l += wl;
-        wo[j] = wl * uj[j];
+        wo[j] = wl == 0.0f ? 0.0f : wl * r[j][2];      // (a stale record never reaches the product)
     }
-    // the outputs, eight states' loads in flight at a time
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j0 = 0; j0 < kNmaP; j0 += 8) {
-        h8_t v[8];
+    for (int j = 0; j < kNmaP; ++j)
+        if (wo[j] != 0.0f)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (wo[j0 + j] != 0.0f) v[j] = *reinterpret_cast<const h8_t *>(po + (size_t)(j0 + j) * G * kNmaD);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (wo[j0 + j] != 0.0f)
-#pragma unroll
-                for (int x = 0; x < 8; ++x) o[x] = fmaf((float)v[j][x], wo[j0 + j], o[x]);
-    }
+            for (int x = 0; x < 8; ++x) o[x] = fmaf((float)v[j][x], wo[j], o[x]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const size_t oh = (size_t)(A.row0 + grp / A.h_kv) * A.h_q + (size_t)(grp % A.h_kv) * G + h;
     uint32_t pk[4];
