@@ -97,26 +97,45 @@ __global__ __launch_bounds__(256) void k_nma_count(NmaArgs A) {
 constexpr int kNmaScanT = 1024, kNmaScanV = 16;
 __global__ __launch_bounds__(kNmaScanT) void k_nma_scan(NmaArgs A) {
     __shared__ int scr[kNmaScanT / kWave + 1];
+    const bool al = (((uintptr_t)A.toff | (uintptr_t)A.coff) & 15) == 0;
     int carry = 0, ccarry = 0;
     for (int64_t base = 0; base < A.nbins; base += (int64_t)kNmaScanT * kNmaScanV) {
+        const int64_t e0 = base + (int64_t)threadIdx.x * kNmaScanV;
+        const bool whole = al && e0 + kNmaScanV <= A.nbins;     // 16-byte loads and stores
         int v[kNmaScanV], c[kNmaScanV], s = 0, cs = 0;
+        if (whole) {
 #pragma unroll
-        for (int u = 0; u < kNmaScanV; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * kNmaScanV + u;
-            v[u] = e < A.nbins ? A.toff[e] : 0;
-            c[u] = e < A.nbins ? A.coff[e] : 0;
-            s += v[u];
-            cs += c[u];
+            for (int q4 = 0; q4 < kNmaScanV / 4; ++q4) {
+                const int4 x = *reinterpret_cast<const int4 *>(A.toff + e0 + 4 * q4);
+                const int4 y = *reinterpret_cast<const int4 *>(A.coff + e0 + 4 * q4);
+                v[4 * q4] = x.x; v[4 * q4 + 1] = x.y; v[4 * q4 + 2] = x.z; v[4 * q4 + 3] = x.w;
+                c[4 * q4] = y.x; c[4 * q4 + 1] = y.y; c[4 * q4 + 2] = y.z; c[4 * q4 + 3] = y.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kNmaScanV; ++u) {
+                v[u] = e0 + u < A.nbins ? A.toff[e0 + u] : 0;
+                c[u] = e0 + u < A.nbins ? A.coff[e0 + u] : 0;
+            }
         }
+#pragma unroll
+        for (int u = 0; u < kNmaScanV; ++u) { s += v[u]; cs += c[u]; }
         int tot, ctot;
         int run = carry + block_excl_scan(s, scr, &tot);
         int crun = ccarry + block_excl_scan(cs, scr, &ctot);
+        int ov[kNmaScanV], oc[kNmaScanV];
 #pragma unroll
-        for (int u = 0; u < kNmaScanV; ++u) {
-            const int64_t e = base + (int64_t)threadIdx.x * kNmaScanV + u;
-            if (e < A.nbins) { A.toff[e] = run; A.coff[e] = crun; }
-            run += v[u];
-            crun += c[u];
+        for (int u = 0; u < kNmaScanV; ++u) { ov[u] = run; oc[u] = crun; run += v[u]; crun += c[u]; }
+        if (whole) {
+#pragma unroll
+            for (int q4 = 0; q4 < kNmaScanV / 4; ++q4) {
+                *reinterpret_cast<int4 *>(A.toff + e0 + 4 * q4) = int4{ov[4 * q4], ov[4 * q4 + 1], ov[4 * q4 + 2], ov[4 * q4 + 3]};
+                *reinterpret_cast<int4 *>(A.coff + e0 + 4 * q4) = int4{oc[4 * q4], oc[4 * q4 + 1], oc[4 * q4 + 2], oc[4 * q4 + 3]};
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kNmaScanV; ++u)
+                if (e0 + u < A.nbins) { A.toff[e0 + u] = ov[u]; A.coff[e0 + u] = oc[u]; }
         }
         carry += tot;
         ccarry += ctot;
