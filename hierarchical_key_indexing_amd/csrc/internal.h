@@ -35,7 +35,7 @@ int64_t nm_workspace_bytes(int64_t m, int h_kv, int L, const int64_t *nodes);
 
 // node-major attention (nm_attend.hip), run after each batch of node-major
 // selection when select and attention are called together
-struct NmaWs { uint64_t *amask; int32_t *abound, *toff, *coff, *wr, *tdesc; char *pinf, *po; float *pml; size_t bytes; };
+struct NmaWs { int32_t *ppos, *toff, *coff, *wr, *tdesc; char *pinf, *po; float *pml; size_t bytes; };
 struct NmaBatch {
     const void *Q, *K, *V;
     const int32_t *q_pos;

@@ -56,8 +56,8 @@ struct NmaArgs {
     const int32_t *pairs;       // group * kNmaP + slot, grouped by (head, node) bin
     const int32_t *noff;        // [nbins + 1]: the bins' runs in pairs
     const int32_t *keep;        // [groups]
-    const uint64_t *amask;      // [groups][kNmaP]
-    const int32_t *abound;      // [groups][2]
+    uint16_t *out;              // bf16 [m][h_q][128]
+    float *lse;                 // [m][h_q] or NULL
     int64_t nbins;
     int T;                      // pairs per tile (128 / G)
     int32_t *toff;              // [nbins + 1]: tiles before each bin
@@ -65,12 +65,10 @@ struct NmaArgs {
     int32_t *wr;                // [nwg + 1]: first tile of each workgroup's share
     int64_t nwg;                // attention workgroups (a multiple of 8)
     int4 *tdesc;                // [tiles]: bin, first pair, pairs of each tile
-    u32x4_t *pinf;              // [pairs][2]: pair records in bin order (k_nma_pairs)
+    const u32x4_t *pinf;        // [pairs][2]: pair records in bin order (written by the selection's leaf finish)
     int16_t *po;                // [groups][kNmaP][G][128]: o / l in units of u, rounded
     floatx4_t *pml;             // [groups][kNmaP][G]: {m (base 2), l, u, 0}
     float scale_log2;
-    uint16_t *out;              // bf16 [m][h_q][128]
-    float *lse;                 // [m][h_q] or NULL
 };
 
 // Estimated cost of one tile of bin e: the tile itself plus one unit per
@@ -195,7 +193,7 @@ LSA_DEV int nma_child(const int32_t *lof, int b, int64_t at) {
 // repeats the last member so that every gather stays inside the cache).
 LSA_DEV void nma_load_ids(const int32_t *pm, const int32_t *lof_s, int b, int64_t t0, int64_t hi, int32_t *ids,
                           int32_t *cid) {
-    const int tid = threadIdx.x;
+    const int tid = opaque((int)threadIdx.x);
     if (tid < kNmaKC) {
         const int64_t at = t0 + tid;
         const bool in = at < hi;
@@ -248,25 +246,6 @@ LSA_DEV void nma_store_v(uint16_t *Vt, const u32x4_t (&vr)[4]) {
 
 constexpr int kNmaIds = 1024;   // members of a node staged in LDS (larger nodes: step by step)
 
-// Pair records, in bin order, 32 bytes each (two u32x4): taken-children mask
-// (low, high), entry (group * kNmaP + slot), retrieval range low; range
-// high, child of the leaf taken in part (-1: none), its last taken key, 0.
-// A tile reads its pairs' records in one coalesced load.
-__global__ __launch_bounds__(256) void k_nma_pairs(NmaArgs A) {
-    const int64_t npairs = A.noff[A.nbins];
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < npairs; p += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t e = A.pairs[p];
-        const int64_t grp = e / kNmaP;
-        const int j = e % kNmaP;
-        const AttnSet as = attn_set(A.q_pos[A.row0 + grp / A.h_kv], A.n, A.n_sink, A.window);
-        const uint64_t mask = A.amask[e];
-        const int32_t bs = A.abound[grp * 2];
-        const int32_t bc = (bs >= 0 && (bs >> 6) == j) ? (bs & 63) : -1;
-        A.pinf[2 * p] = u32x4_t{(uint32_t)mask, (uint32_t)(mask >> 32), (uint32_t)e, (uint32_t)as.rlo};
-        A.pinf[2 * p + 1] = u32x4_t{(uint32_t)as.rhi, (uint32_t)bc, (uint32_t)A.abound[grp * 2 + 1], 0u};
-    }
-}
-
 // The keys of the current step that each pair of the tile attends: one
 // ballot per pair (lane = key), wave w taking pairs w, w + 4, ...
 LSA_DEV void nma_pair_masks(int np, const int32_t *ids, const int32_t *chs, const u32x4_t (*pi)[2], uint64_t *pch) {
@@ -288,7 +267,7 @@ LSA_DEV void nma_pair_masks(int np, const int32_t *ids, const int32_t *chs, cons
 // bitonic network over the power of two above `span`, padding (child 64)
 // sorting last.
 LSA_DEV void nma_sort_members(int cnt, int span, int32_t pad_id, int32_t *mid_s, int32_t *mch_s) {
-    const int tid = threadIdx.x;
+    const int tid = opaque((int)threadIdx.x);
     if (cnt <= kNmaThreads) {
         const int32_t my = tid < cnt ? mid_s[tid] : 0, mc = tid < cnt ? mch_s[tid] : 0;
         int rank = 0;
@@ -337,7 +316,7 @@ LSA_DEV void nma_sort_members(int cnt, int span, int32_t pad_id, int32_t *mid_s,
 // members visible to the workgroup.
 LSA_DEV void nma_stage_node(const NmaArgs &A, int32_t bin, int32_t frhi, int32_t *lof_s, int32_t *mid_s,
                             int32_t *mch_s, int32_t &lo, int32_t &hi, bool &fits, bool &srt, int *late_s) {
-    const int tid = threadIdx.x, b = A.b;
+    const int tid = opaque((int)threadIdx.x), b = A.b;
     const int g = (int)(bin / A.nodes_prev);
     const int64_t v = bin % A.nodes_prev;
     if (tid <= b) lof_s[tid] = A.leaf_off[(size_t)g * (A.nleaf + 1) + (size_t)v * b + tid];
@@ -408,7 +387,7 @@ __global__ __launch_bounds__(kNmaThreads, 2) void k_nma_attend(NmaArgs A) {
 
     // this workgroup's tile descriptors, kNmaTd at a time, in LDS
     int64_t tw = t0;
-    for (int x = tid; x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
+    for (int x = opaque(tid); x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
     __syncthreads();
     // the first tile: its pair records, its node and its first step's rows
     int32_t bin = td_s[0].x;
@@ -445,7 +424,7 @@ __global__ __launch_bounds__(kNmaThreads, 2) void k_nma_attend(NmaArgs A) {
         if (has_next) {
             if (t + 1 - tw == kNmaTd) {           // the next window (every wave is past the last read)
                 tw = t + 1;
-                for (int x = tid; x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
+                for (int x = opaque(tid); x < kNmaTd && tw + x < t1; x += kNmaThreads) td_s[x] = A.tdesc[tw + x];
                 __syncthreads();
             }
             const int4 d = td_s[t + 1 - tw];
@@ -587,7 +566,8 @@ __global__ __launch_bounds__(kNmaThreads, 2) void k_nma_attend(NmaArgs A) {
         }
         // the next tile's records, in flight during the partial states
         u32x4_t pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
-        if (has_next && tid < nnp) { pn0 = A.pinf[2 * (npb + tid)]; pn1 = A.pinf[2 * (npb + tid) + 1]; }
+        const int tp = opaque(tid);
+        if (has_next && tp < nnp) { pn0 = A.pinf[2 * (npb + tp)]; pn1 = A.pinf[2 * (npb + tp) + 1]; }
         // partial states.  A column's output o / l is stored as 16-bit
         // integers in units of 2^ex / 32767, 2^ex the power of two above its
         // largest magnitude: an absolute error of at most 2^ex / 65534,
@@ -633,7 +613,7 @@ __global__ __launch_bounds__(kNmaThreads, 2) void k_nma_attend(NmaArgs A) {
         if (!has_next) break;
         // the next tile: its records into the other buffer; a new node is
         // staged (and its first step loaded) once every wave is past this one
-        if (tid < nnp) { pi_s[pbuf ^ 1][tid][0] = pn0; pi_s[pbuf ^ 1][tid][1] = pn1; }
+        if (tp < nnp) { pi_s[pbuf ^ 1][tp][0] = pn0; pi_s[pbuf ^ 1][tp][1] = pn1; }
         __syncthreads();
         if (!next_same) {
             nma_stage_node(A, nbin, (int32_t)pi_s[pbuf ^ 1][0][1].x, lof_s, mid_s, mch_s, lo, hi, fits, srt,
@@ -729,8 +709,7 @@ NmaWs carve_nma_ws(char *base, int64_t groups, int G, int64_t nbins) {
     size_t cur = 0;
     NmaWs w{};
     auto take = [&](size_t n) { char *p = base ? base + cur : nullptr; cur = nma_a256(cur + n); return p; };
-    w.amask = (uint64_t *)take(sizeof(uint64_t) * groups * kNmaP);
-    w.abound = (int32_t *)take(sizeof(int32_t) * groups * 2);
+    w.ppos = (int32_t *)take(sizeof(int32_t) * groups * kNmaP);
     w.toff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
     w.coff = (int32_t *)take(sizeof(int32_t) * (nbins + 1));
     w.wr = (int32_t *)take(sizeof(int32_t) * (kNmaMaxWg + 1));
@@ -748,7 +727,7 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     A.row0 = B.row0; A.groups = B.groups; A.h_q = B.h_q; A.h_kv = B.h_kv; A.G = B.h_q / B.h_kv;
     A.n = B.n; A.b = B.b; A.nodes_prev = B.nodes_prev; A.nleaf = B.nleaf;
     A.leaf_off = B.leaf_off; A.perm = B.perm; A.n_sink = B.n_sink; A.window = B.window;
-    A.pairs = B.pairs; A.noff = B.noff; A.keep = B.keep; A.amask = B.ws.amask; A.abound = B.ws.abound;
+    A.pairs = B.pairs; A.noff = B.noff; A.keep = B.keep;
     A.nbins = (int64_t)B.h_kv * B.nodes_prev;
     A.T = kNmaCols / A.G;
     A.toff = B.ws.toff; A.coff = B.ws.coff; A.wr = B.ws.wr; A.tdesc = (int4 *)B.ws.tdesc; A.pinf = (u32x4_t *)B.ws.pinf;
@@ -764,8 +743,6 @@ hipError_t nm_attend_batch(const NmaBatch &B, hipStream_t st) {
     hipLaunchKernelGGL(k_nma_count, dim3(bin_blocks), dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_scan, dim3(1), dim3(kNmaScanT), 0, st, A);
     hipLaunchKernelGGL(k_nma_map, dim3(bin_blocks), dim3(256), 0, st, A);
-    hipLaunchKernelGGL(k_nma_pairs, dim3((unsigned)std::min<int64_t>((B.groups * kNmaP + 255) / 256, 8192)),
-                       dim3(256), 0, st, A);
     hipLaunchKernelGGL(k_nma_attend, dim3((unsigned)nwg), dim3(kNmaThreads), 0, st, A);
     const int64_t gpw = 256 / (16 * A.G);
     hipLaunchKernelGGL(k_nma_merge, dim3((unsigned)((B.groups + gpw - 1) / gpw)), dim3(256), 0, st, A);

@@ -539,10 +539,11 @@ struct NmArgs {
     int32_t *ncnt, *noff, *fptr;   // [h_kv * nodes(level - 1) + 1]
     int32_t *pairs;                // [groups * kFastP]: group * kFastP + slot, grouped by node
     int32_t *pnode;                // [groups * kFastP]: the node of each entry of pairs
-    // taken leaves, for the node-major attention (NULL when none follows):
-    uint64_t *amask;               // [groups][kFastP]: bit c = child c of kept node j gave keys
-    int32_t *abound;               // [groups][2]: slot j * 64 + c of the leaf taken in part (-1: none)
-                                   // and the last key taken from it
+    // for the node-major attention (NULL when none follows):
+    int32_t *ppos;                 // [groups * kFastP]: where each leaf-level entry sits in pairs
+    uint4 *pinf;                   // [groups * kFastP][2]: the pair records, in the order of pairs: taken
+                                   // children mask (low, high), entry, retrieval range low; range high,
+                                   // child of the leaf taken in part (-1: none), its last taken key, 0
 };
 
 // kTopRows rows of one KV head per workgroup: W_g is staged once for them,
@@ -698,6 +699,7 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
                 const int32_t at = atomicAdd(N.fptr + bin, 1);
                 N.pairs[at] = (int32_t)(e0 + u);
                 N.pnode[at] = (int32_t)(bin % N.S.nodes[N.level - 1]);
+                if (N.ppos && N.level == N.S.L) N.ppos[e0 + u] = at;
             }
         }
         return;
@@ -734,6 +736,7 @@ __global__ __launch_bounds__(256) void k_nm_fill(NmArgs N, int64_t nbins) {
             const int32_t at = h_s[bin[u]] + rk[u];
             N.pairs[at] = (int32_t)(e0 + threadIdx.x + 256 * u);
             N.pnode[at] = (int32_t)(bin[u] % N.S.nodes[N.level - 1]);
+            if (N.ppos && N.level == N.S.L) N.ppos[e0 + threadIdx.x + 256 * u] = at;
         }
 }
 
@@ -949,6 +952,10 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     const int tid = threadIdx.x;
     if (tid == 0) { cut_s = -INFINITY; bnd_s[0] = -1; bnd_s[1] = 0; }
     if (tid < kFastP) msk_s[tid] = 0ull;
+    // (the attention's: the kept count and where this group's slots sit in
+    // pairs, loaded early)
+    const int keepv = N.pinf ? N.keep[grp] : 0;
+    const int32_t pos = (N.pinf && tid < kFastP) ? N.ppos[grp * kFastP + tid] : 0;
     uint64_t k4[KPT];
     nm_load_keys<KPT>(N, grp, k4, KPT == 2);
     block_sort_desc<KPT>(k4, sk);
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
         if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
         off += e4[ii];
     }
-    if (N.amask) {
+    if (N.pinf) {
         // the taken leaves per kept node, and the one leaf (if any) whose
         // eligible members are taken only in part: its last taken key
 #pragma unroll
@@ -995,9 +1002,13 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
         A.sel_count[(size_t)i * A.h_kv + g] = count + as.nloc;
         if (A.sel_cutoff) A.sel_cutoff[(size_t)i * A.h_kv + g] = cut_s;
     }
-    if (N.amask) {
-        if (tid < kFastP) N.amask[grp * kFastP + tid] = msk_s[tid];
-        if (tid < 2) N.abound[grp * 2 + tid] = bnd_s[tid];
+    if (N.pinf && tid < keepv) {
+        // the attention's record of kept slot tid, at its place in pairs
+        const uint64_t mask = msk_s[tid];
+        const int32_t bs = bnd_s[0];
+        const int32_t bc = (bs >= 0 && (bs >> 6) == tid) ? (bs & 63) : -1;
+        N.pinf[2 * pos] = uint4{(uint32_t)mask, (uint32_t)(mask >> 32), (uint32_t)(grp * kFastP + tid), (uint32_t)as.rlo};
+        N.pinf[2 * pos + 1] = uint4{(uint32_t)as.rhi, (uint32_t)bc, (uint32_t)bnd_s[1], 0u};
     }
 }
 
@@ -1072,8 +1083,8 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         NmaWs aw{};
         if (att) {
             aw = carve_nma_ws((char *)ws + w.bytes, groups, G, (int64_t)A.h_kv * A.nodes[A.L - 1]);
-            N.amask = aw.amask;
-            N.abound = aw.abound;
+            N.ppos = aw.ppos;
+            N.pinf = (uint4 *)aw.pinf;
         }
         const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
         if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
@@ -1098,7 +1109,7 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
         if (e != hipSuccess) return e;
         if (att) {
             // the leaf level's pairs (grouped by kept level-(L-1) node) and the
-            // finish's taken-leaf masks drive the attention of this batch
+            // records the finish wrote for them drive the attention of this batch
             NmaBatch B{};
             B.Q = A.Q; B.K = att->K; B.V = att->V; B.q_pos = A.q_pos; B.row0 = r0; B.groups = groups;
             B.h_q = A.h_q; B.h_kv = A.h_kv; B.n = A.n; B.b = A.b;
