@@ -86,16 +86,6 @@ __global__ __launch_bounds__(256) void k_project(const T *__restrict__ K, const 
 // 4 blk + l / 16 of its column, then sit in registers before the tile is
 // staged); NQ = 0 takes d at run time and loads a weight per block.
 constexpr int kPjMaxD = 256;
-LSA_DEV void load8(const bf16_t *src, size_t at, float (&v)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(src + at);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u); }
-}
-LSA_DEV void load8(const float *src, size_t at, float (&v)[8]) {
-    const f4_t a = *reinterpret_cast<const f4_t *>(src + at), b = *reinterpret_cast<const f4_t *>(src + at + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
 template <typename T, int KB, int NQ>
 __global__ __launch_bounds__(256) void k_project_mfma(const T *__restrict__ K, const float *__restrict__ W,
                                                       float *__restrict__ Z, int64_t n, int d) {

@@ -202,13 +202,16 @@ LSA_DEV void sort_half_cleaners(uint64_t &key, int &pay, int lane) {
     sort_cx<S, S>(key, pay, lane);
     if constexpr (S > 1) sort_half_cleaners<S / 2>(key, pay, lane);
 }
-template <int SIZE>
+template <int SIZE, int TOP = kWave>
 LSA_DEV void sort_phase(uint64_t &key, int &pay, int lane) {
     sort_cx<SIZE - 1, SIZE / 2>(key, pay, lane);
     if constexpr (SIZE >= 4) sort_half_cleaners<SIZE / 4>(key, pay, lane);
-    if constexpr (SIZE < kWave) sort_phase<SIZE * 2>(key, pay, lane);
+    if constexpr (SIZE < TOP) sort_phase<SIZE * 2, TOP>(key, pay, lane);
 }
 LSA_DEV void wave_sort_desc(uint64_t &key, int &pay) { sort_phase<2>(key, pay, lane_id()); }
+// The same network stopped at blocks of 32 lanes: lanes 0..31 and 32..63
+// are two independent sorts.
+LSA_DEV void half_wave_sort_desc(uint64_t &key, int &pay) { sort_phase<2, 32>(key, pay, lane_id()); }
 
 // Bitonic sort, descending, of the 256 * KPT 64-bit keys of a 256-thread
 // block, KPT (1, 2 or 4) per thread: thread t holds elements KPT t ..
@@ -563,6 +566,18 @@ LSA_DEV void in_range(const AttnSet &s, const int32_t *mem, int len, int &first,
     const int z = (mem[len - 1] <= s.rhi) ? len : count_le(mem, len, s.rhi);
     first = a;
     cnt = max(0, z - a);
+}
+
+// Eight consecutive elements (16-byte aligned) widened to float.
+LSA_DEV void load8(const bf16_t *src, size_t at, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(src + at);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u); }
+}
+LSA_DEV void load8(const float *src, size_t at, float (&v)[8]) {
+    const f4_t a = *reinterpret_cast<const f4_t *>(src + at), b = *reinterpret_cast<const f4_t *>(src + at + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 // fp64 MFMA: v_mfma_f64_16x16x4_f64 accumulates D[i][j] += A[i][k] * B[k][j]

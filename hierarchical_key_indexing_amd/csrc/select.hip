@@ -601,6 +601,188 @@ __global__ __launch_bounds__(256) void k_nm_top(NmArgs N) {
     }
 }
 
+// The same step on the fp64 matrix cores (d a multiple of 8, 64 rows of one
+// KV head per workgroup).  qbar is staged in LDS transposed ([dim][row]);
+// wave w forms latent columns 16 w .. 16 w + 15 of the four 16-row blocks as
+// v_mfma_f64_16x16x4_f64 chains over dims 4 blk + k (blk ascending), which is
+// fast_latent's sequential double sum bit for bit.  Then wave w scores rows
+// 16 w .. 16 w + 15 against the root's children (16 children a product, the
+// same chains over the 64 latent dims as score_row64), and ranks each of its
+// rows with one wave sort.  u and the kept nodes equal k_nm_top's.  NQ = d / 4
+// when fixed at compile time (the lane's W_g column in registers), else 0.
+constexpr int kTopMRows = 64;
+constexpr int kTopUS = kFastR + 4;    // u row stride in LDS (16-byte rows)
+constexpr int kTopSS = kFastR + 1;    // score row stride in LDS
+
+size_t nm_top_mfma_lds(int d) {
+    const size_t q = (size_t)d * (kTopMRows + 1), us = (size_t)kTopMRows * (kTopUS + kTopSS);
+    return sizeof(float) * (q > us ? q : us);
+}
+
+template <typename T, int NQ>
+__global__ __launch_bounds__(256) void k_nm_top_mfma(NmArgs N) {
+    constexpr int R = kFastR, RB = kTopMRows, ST = RB + 1;
+    extern __shared__ __attribute__((aligned(16))) float tsm[];
+    float *qt = tsm;                          // [d][ST], then u rows and scores:
+    float *u_s = tsm;                         // [RB][kTopUS]
+    float *sc_s = tsm + RB * kTopUS;          // [RB][kTopSS]
+    const SelectArgs &A = N.S;
+    const int g = blockIdx.y;
+    const int64_t rb = (int64_t)blockIdx.x * RB;                      // first row, relative to the batch
+    const int nr = (int)min<int64_t>(RB, N.groups / A.h_kv - rb);
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave, lr = lane % 16, lk = lane / 16;
+    const int G = A.h_q / A.h_kv, d = A.d, nq = NQ > 0 ? NQ : d / 4;
+    const T *Q = (const T *)A.Q;
+    const float *wcol = A.W + (size_t)g * d * R + 16 * w + lr;
+    const float *C1 = (const float *)(A.index + A.centroid_off[1]) + (size_t)g * A.nodes[1] * R;
+    const int32_t *cn1 = (const int32_t *)(A.index + A.count_off[1]) + (size_t)g * A.nodes[1];
+    const int cnt1 = lane < A.b ? cn1[lane] : 0;
+    // qbar of row rr, dims 8 x .. 8 x + 7: the G heads summed in double in
+    // head order, divided by G, rounded once
+    if constexpr (NQ > 0) {
+        // (d = 4 NQ: the thread's SL chunks loaded together, two heads a round)
+        constexpr int XC = NQ / 2, SL = RB * XC / 256;
+        static_assert(RB * XC % 256 == 0, "whole chunks per thread");
+        double s[SL][8];
+        size_t at[SL];
+        bool ok[SL];
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+            const int idx = tid + 256 * sl, rr = idx / XC, x = idx % XC;
+            ok[sl] = rr < nr;
+            at[sl] = ok[sl] ? ((size_t)(N.row0 + rb + rr) * A.h_q + (size_t)g * G) * d + 8 * x : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s[sl][u] = 0.0;
+        }
+        for (int h = 0; h < G; h += 2) {
+            const int h1 = h + 1 < G ? h + 1 : h;
+            float v[SL][8], v1[SL][8];
+#pragma unroll
+            for (int sl = 0; sl < SL; ++sl) {
+                load8(Q, at[sl] + (size_t)h * d, v[sl]);
+                load8(Q, at[sl] + (size_t)h1 * d, v1[sl]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s[sl][u] = s[sl][u] + (double)v[sl][u];
+            if (h1 != h) {
+#pragma unroll
+                for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) s[sl][u] = s[sl][u] + (double)v1[sl][u];
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+            const int idx = tid + 256 * sl, rr = idx / XC, x = idx % XC;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) qt[(8 * x + u) * ST + rr] = ok[sl] ? (float)(s[sl][u] / (double)G) : 0.0f;
+        }
+    } else {
+        for (int idx = tid; idx < RB * (d / 8); idx += blockDim.x) {
+            const int rr = idx / (d / 8), x = idx % (d / 8);
+            double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+            if (rr < nr) {
+                const size_t at = ((size_t)(N.row0 + rb + rr) * A.h_q + (size_t)g * G) * d + 8 * x;
+                for (int h = 0; h < G; ++h) {
+                    float v[8];
+                    load8(Q, at + (size_t)h * d, v);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) s[u] = s[u] + (double)v[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) qt[(8 * x + u) * ST + rr] = (float)(s[u] / (double)G);
+        }
+    }
+    // the lane's W_g column (dims 4 blk + l / 16), in flight across the barrier
+    float wv[NQ > 0 ? NQ : 1];
+    if constexpr (NQ > 0) {
+#pragma unroll
+        for (int blk = 0; blk < NQ; ++blk) wv[blk] = wcol[(size_t)(4 * blk + lk) * R];
+    }
+    __syncthreads();
+    d4_t acc[RB / 16];
+#pragma unroll
+    for (int kb = 0; kb < RB / 16; ++kb) acc[kb] = d4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll(NQ > 0 ? NQ : 1)
+    for (int blk = 0; blk < nq; ++blk) {
+        double bw;
+        if constexpr (NQ > 0) bw = (double)wv[blk];
+        else bw = (double)wcol[(size_t)(4 * blk + lk) * R];
+        const float *qrow = qt + (4 * blk + lk) * ST + lr;
+#pragma unroll
+        for (int kb = 0; kb < RB / 16; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qrow[16 * kb], bw, acc[kb], 0, 0, 0);
+    }
+    __syncthreads();                     // qt read by every wave: its space now takes u
+    // element e of lane l: row 16 kb + l / 16 + 4 e, latent column 16 w + l % 16
+#pragma unroll
+    for (int kb = 0; kb < RB / 16; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 16 * kb + lk + 4 * e;
+            const float uv = (float)acc[kb][e];
+            u_s[rr * kTopUS + 16 * w + lr] = uv;
+            if (rr < nr) N.U[((rb + rr) * A.h_kv + g) * R + 16 * w + lr] = uv;
+        }
+    // level 1: rows 16 w .. 16 w + 15 (this wave's) x children 16 cb .. 16 cb + 15
+    const int cbn = (A.b + 15) / 16;
+    f4_t crow[4][4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+        if (cb < cbn) load_row_mfma(C1 + (size_t)min(16 * cb + lr, A.b - 1) * R, lk, crow[cb]);
+    __syncthreads();                     // every wave's u rows in LDS
+    double ua[16];
+    {
+        f4_t v[4];
+        load_row_mfma(u_s + (16 * w + lr) * kTopUS, lk, v);
+        widen_row_mfma(v, ua);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        if (cb >= cbn) continue;
+        const d4_t sc = mfma_dot64(ua, crow[cb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc_s[(16 * w + lk + 4 * e) * kTopSS + 16 * cb + lr] = (float)sc[e];
+    }
+    wave_sync();                         // the wave ranks only its own rows
+    if (A.b <= 32) {
+        // two rows a sort: row 16 w + q in lanes 0..31, row 16 w + q + 1 in 32..63
+        const int c = lane & 31, hi = lane >> 5;
+        const int cnt1h = __shfl(cnt1, c);
+        for (int q = 0; q < 16; q += 2) {
+            const int rr = 16 * w + q + hi;
+            if (16 * w + q >= nr) break;
+            uint64_t key = (c < A.b && cnt1h > 0 && rr < nr) ? make_key(sc_s[rr * kTopSS + c], (uint32_t)c) : 0ull;
+            int pay = 0;
+            const uint64_t nzm = __ballot(key != 0);
+            const int nz = __popcll(hi ? (nzm >> 32) : (nzm & 0xffffffffull));
+            half_wave_sort_desc(key, pay);
+            const int keep = min(A.beam, nz);
+            if (rr < nr) {
+                const int64_t grp = (rb + rr) * A.h_kv + g;
+                if (c < kFastP) N.kept[grp * kFastP + c] = c < keep ? (int32_t)key_id(key) : 0;
+                if (c == 0) N.keep[grp] = keep;
+            }
+        }
+    } else {
+        for (int q = 0; q < 16; ++q) {
+            const int rr = 16 * w + q;
+            if (rr >= nr) break;
+            const int64_t grp = (rb + rr) * A.h_kv + g;
+            uint64_t key = (lane < A.b && cnt1 > 0) ? make_key(sc_s[rr * kTopSS + lane], (uint32_t)lane) : 0ull;
+            int pay = 0;
+            const int nz = __popcll(__ballot(key != 0));
+            wave_sort_desc(key, pay);
+            const int keep = min(A.beam, nz);
+            if (lane < kFastP) N.kept[grp * kFastP + lane] = lane < keep ? (int32_t)key_id(key) : 0;
+            if (lane == 0) N.keep[grp] = keep;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_nm_zero(NmArgs N, int64_t count) {
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x)
         N.ncnt[e] = 0;
@@ -940,6 +1122,7 @@ template <int KPT>
 __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     __shared__ __attribute__((aligned(16))) uint64_t sk[1024];   // the sort's, then the copy's position marks
     __shared__ int dl_s[256 * KPT];
+    __shared__ int eli_s[kFastP * 64], lof_s[kFastP * 64];
     static_assert(sizeof(sk) >= kFlatCap * sizeof(int), "the position marks reuse the sort's array");
     __shared__ int scratch[8];
     __shared__ float cut_s;
@@ -958,14 +1141,34 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     const int32_t pos = (N.pinf && tid < kFastP) ? N.ppos[grp * kFastP + tid] : 0;
     uint64_t k4[KPT];
     nm_load_keys<KPT>(N, grp, k4, KPT == 2);
+    {
+        // the eligible counts and first members of the thread's slots, loaded
+        // with the keys and kept in LDS by slot for the sorted keys to find
+        const int32_t *eli = N.eli + (size_t)grp * (kFastP * 64);
+        const int32_t *lof = N.lof + (size_t)grp * (kFastP * 64);
+        const int keep = N.keep[grp], per = KPT == 2 ? 32 : 64;
+        int ev[KPT], lv[KPT];
+#pragma unroll
+        for (int ii = 0; ii < KPT; ++ii) {
+            const int e = KPT * tid + ii, sl = nm_slot(e, KPT == 2);
+            const bool in = e < kFastP * per && e / per < keep;
+            ev[ii] = in ? eli[sl] : 0;
+            lv[ii] = in ? lof[sl] : 0;
+        }
+#pragma unroll
+        for (int ii = 0; ii < KPT; ++ii) {
+            const int sl = nm_slot(KPT * tid + ii, KPT == 2);
+            eli_s[sl] = ev[ii];
+            lof_s[sl] = lv[ii];
+        }
+    }
     block_sort_desc<KPT>(k4, sk);
-    const int32_t *eli = N.eli + (size_t)grp * (kFastP * 64);
-    const int32_t *lof = N.lof + (size_t)grp * (kFastP * 64);
+    lds_barrier();                      // eli_s and lof_s written by every thread
     const int32_t *pm = (const int32_t *)(A.index + A.perm_off) + (size_t)g * A.n;
     int e4[KPT], tot = 0;
 #pragma unroll
     for (int ii = 0; ii < KPT; ++ii) {
-        e4[ii] = (k4[ii] != 0) ? eli[(int)(k4[ii] & 1023u)] : 0;
+        e4[ii] = (k4[ii] != 0) ? eli_s[(int)(k4[ii] & 1023u)] : 0;
         tot += e4[ii];
     }
     int total;
@@ -977,7 +1180,7 @@ __global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
     for (int ii = 0; ii < KPT; ++ii) {
         offv[ii] = off;
         take[ii] = (e4[ii] > 0 && off < count) ? min(e4[ii], count - off) : 0;
-        a0v[ii] = take[ii] > 0 ? lof[(int)(k4[ii] & 1023u)] : 0;
+        a0v[ii] = take[ii] > 0 ? lof_s[(int)(k4[ii] & 1023u)] : 0;
         if (take[ii] > 0 && count == A.k && off + e4[ii] >= A.k) cut_s = key_score(k4[ii]);
         off += e4[ii];
     }
@@ -1072,6 +1275,15 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
     const int G = att ? A.h_q / A.h_kv : 0;
     const int64_t mb = nm_batch_rows(A.m, A.h_kv, A.L, A.nodes, ws_bytes, G);
     if (mb < 1) return hipErrorInvalidValue;
+    // the matrix-core top step takes 16-byte loads of 8-element query chunks
+    const bool top_mfma = A.d % 8 == 0 && ((uintptr_t)A.Q & 15) == 0;
+    if (top_mfma && nm_top_mfma_lds(A.d) > 65536) {
+        const size_t lds = nm_top_mfma_lds(A.d);
+        const hipError_t e = dtype == 0
+            ? hipFuncSetAttribute((const void *)k_nm_top_mfma<float, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+            : hipFuncSetAttribute((const void *)k_nm_top_mfma<bf16_t, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     for (int64_t r0 = 0; r0 < A.m; r0 += mb) {
         const int64_t nb = std::min(mb, A.m - r0);
         const int64_t groups = nb * A.h_kv;
@@ -1086,9 +1298,18 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
             N.ppos = aw.ppos;
             N.pinf = (uint4 *)aw.pinf;
         }
-        const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
-        if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
-        else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
+        if (top_mfma) {
+            const dim3 tg((unsigned)((nb + kTopMRows - 1) / kTopMRows), (unsigned)A.h_kv);
+            const size_t lds = nm_top_mfma_lds(A.d);
+            if (dtype == 0 && A.d == 128) hipLaunchKernelGGL((k_nm_top_mfma<float, 32>), tg, dim3(256), lds, st, N);
+            else if (dtype == 0) hipLaunchKernelGGL((k_nm_top_mfma<float, 0>), tg, dim3(256), lds, st, N);
+            else if (A.d == 128) hipLaunchKernelGGL((k_nm_top_mfma<bf16_t, 32>), tg, dim3(256), lds, st, N);
+            else hipLaunchKernelGGL((k_nm_top_mfma<bf16_t, 0>), tg, dim3(256), lds, st, N);
+        } else {
+            const dim3 tg((unsigned)((nb + kTopRows - 1) / kTopRows), (unsigned)A.h_kv);
+            if (dtype == 0) hipLaunchKernelGGL(k_nm_top<float>, tg, dim3(256), 0, st, N);
+            else hipLaunchKernelGGL(k_nm_top<bf16_t>, tg, dim3(256), 0, st, N);
+        }
         for (int l = 2; l <= A.L; ++l) {
             N.level = l;
             const int64_t cnt = (int64_t)A.h_kv * A.nodes[l - 1];
