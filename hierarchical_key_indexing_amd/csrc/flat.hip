@@ -375,7 +375,8 @@ __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
         if (tid < 32) meta_s[p][tid] = st.meta;
     };
     double ua[16];
-    int rlo[4], rhi[4], wacc[4] = {0, 0, 0, 0};
+    int rlo[4], rhi[4];
+    uint64_t thr[4] = {0ull, 0ull, 0ull, 0ull};
     if (wave_on) {
         f4_t t[4];
         load_row_mfma(A.U + ((size_t)(i0 + min(rb + col, nr - 1)) * A.h_kv + g) * 64, kk, t);
@@ -385,6 +386,7 @@ __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
             const int rr = min(rb + kk + 4 * e, nr - 1);
             rlo[e] = rlo_s[rr];
             rhi[e] = rhi_s[rr];
+            if constexpr (MODE == 2) thr[e] = thr_s[rr];
         }
     }
     // the step of 32 leaves at vb, from buffer p
@@ -397,6 +399,54 @@ __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 acc2[h] = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[blk], bs[p][h][blk][kk][col], acc2[h], 0, 0, 0);
+        if constexpr (MODE == 2) {
+            // which of the lane's eight keys reach their row's threshold (a
+            // bit each), then rounds that take one hit per lane, every lane
+            // with a hit together: a round per hit of the busiest lane rather
+            // than a branch per (block, element) with any hit in the wave
+            uint32_t ok[8];
+            uint32_t hits = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t x = vb + 16 * h + col;
+                const int c = meta_s[p][16 * h + col].x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ok[4 * h + e] = orderable((float)acc2[h][e]);
+                    const uint64_t key = ((uint64_t)ok[4 * h + e] << 32) | (uint64_t)(~(uint32_t)x);
+                    if (x < vend && rb + kk + 4 * e < nr && c > 0 && key >= thr[e]) hits |= 1u << (4 * h + e);
+                }
+            }
+            while (__ballot(hits != 0)) {
+                if (hits != 0) {
+                    const int bi = __builtin_ctz(hits);
+                    hits &= hits - 1;
+                    const int h = bi >> 2, e = bi & 3;
+                    uint32_t o32 = ok[0];
+#pragma unroll
+                    for (int t = 1; t < 8; ++t) o32 = bi == t ? ok[t] : o32;
+                    const int rr = rb + kk + 4 * e;
+                    const int64_t x = vb + 16 * h + col;
+                    const int4 mt = meta_s[p][16 * h + col];     // member count, first offset, first, last
+                    const int eq = members_in(pm + mt.y, mt.x, mt.z, mt.w, rlo_s[rr], rhi_s[rr]);
+                    if (eq > 0) {
+                        const int64_t gi = (i0 + rr) * A.h_kv + g;
+                        const int w = min(eq, A.k);
+                        A.wt[(size_t)gi * A.nleaf + x] = (uint16_t)w;
+                        atomicAdd(&wsum_s[rr], w);
+                        const uint64_t key = ((uint64_t)o32 << 32) | (uint64_t)(~(uint32_t)x);
+                        const int pos = atomicAdd(&cnt_s[rr], 1);
+                        if (pos < kFlatSeg) {
+                            seg_s[rr][pos] = key;
+                        } else {
+                            const int gp = atomicAdd(A.lcnt + gi, 1);
+                            if (gp < kFlatList) A.lst[(size_t)gi * kFlatList + gp] = key;
+                        }
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const d4_t acc = acc2[h];
@@ -412,36 +462,15 @@ __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
                 if (MODE == 3 && !fail_s[rr]) continue;
                 const int64_t gi = (i0 + rr) * A.h_kv + g;
                 const size_t o = (size_t)gi * A.nleaf + v;
-                if constexpr (MODE == 2) {
-                    // the members in range are counted only for keys that
-                    // reach the threshold (a leaf whose range is cut costs a
-                    // search in memory)
-                    const uint64_t key = ((uint64_t)orderable((float)acc[e]) << 32) | (uint64_t)(~(uint32_t)v);
-                    if (c == 0 || key < thr_s[rr]) continue;
-                    const int eq = members_in(pm + a0, c, first, last, rlo[e], rhi[e]);
-                    if (eq > 0) {
-                        const int w = min(eq, A.k);
-                        A.wt[o] = (uint16_t)w;
-                        wacc[e] += w;
-                        const int pos = atomicAdd(&cnt_s[rr], 1);
-                        if (pos < kFlatSeg) {
-                            seg_s[rr][pos] = key;
-                        } else {
-                            const int gp = atomicAdd(A.lcnt + gi, 1);
-                            if (gp < kFlatList) A.lst[(size_t)gi * kFlatList + gp] = key;
-                        }
-                    }
+                const int eq = c > 0 ? members_in(pm + a0, c, first, last, rlo[e], rhi[e]) : 0;
+                const uint32_t oq = eq > 0 ? orderable((float)acc[e]) : 0u;
+                if constexpr (MODE == 1) {
+                    A.wt[o] = (uint16_t)min(eq, A.k);
+                    A.smp[(size_t)gi * kSampleMax + x] =
+                        eq > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
                 } else {
-                    const int eq = c > 0 ? members_in(pm + a0, c, first, last, rlo[e], rhi[e]) : 0;
-                    const uint32_t oq = eq > 0 ? orderable((float)acc[e]) : 0u;
-                    if constexpr (MODE == 1) {
-                        A.wt[o] = (uint16_t)min(eq, A.k);
-                        A.smp[(size_t)gi * kSampleMax + x] =
-                            eq > 0 ? ((uint64_t)oq << 32) | (uint64_t)(~(uint32_t)v) : 0ull;
-                    } else {
-                        A.sc[o] = oq;
-                        A.wt[o] = (uint16_t)min(eq, A.k);
-                    }
+                    A.sc[o] = oq;
+                    A.wt[o] = (uint16_t)min(eq, A.k);
                 }
             }
         }
@@ -466,11 +495,6 @@ __global__ __launch_bounds__(256) void k_flat_score_mfma(FlatArgs A) {
         __syncthreads();
     }
     if constexpr (MODE == 2) {
-        if (wave_on) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (wacc[e] > 0) atomicAdd(&wsum_s[rb + kk + 4 * e], wacc[e]);
-        }
         // every row's segment into its list (one reservation) and its weight
         __syncthreads();
         if (tid < nr) {
