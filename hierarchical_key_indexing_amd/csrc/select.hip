@@ -521,8 +521,8 @@ __global__ __launch_bounds__(256, 5) void k_select_fast(SelectArgs A) {
 //                kept node; with b <= 32 the first 32 of them, the packed
 //                slots of nm_slot), at the leaf level with eligible counts
 //                and first members;
-//   k_nm_keep    internal levels, per (row, KV head): the top `beam` by a
-//                weighted radix selection and a one-wave sort;
+//   k_nm_keep_w  internal levels, per (row, KV head): the top `beam` by a
+//                wave radix selection and a one-wave sort;
 //   k_nm_finish  leaf level, per (row, KV head): block sort (1024 slots, or
 //                the 512 packed ones) and fill.
 
@@ -1092,29 +1092,80 @@ LSA_DEV void nm_load_keys(const NmArgs &N, int64_t grp, uint64_t (&k)[KPT], bool
     }
 }
 
-__global__ __launch_bounds__(256) void k_nm_keep(NmArgs N) {
-    __shared__ int hist_s[256], sel_s[4], ncol_s;
-    __shared__ uint64_t col_s[kFastP];
-    const int64_t grp = blockIdx.x;
-    const int P = N.S.beam;
-    uint64_t k4[4];
-    nm_load_keys<4>(N, grp, k4, N.S.b <= 32);
-    const int one[4] = {1, 1, 1, 1};
-    const uint64_t thr = block_radix_select(k4, one, P, hist_s, sel_s);
-    if (threadIdx.x == 0) ncol_s = 0;
-    __syncthreads();
+// Internal levels: the top `beam` of each group's candidates, one wave per
+// group (four groups a workgroup, no workgroup barrier).  The candidates sit
+// KPL a lane (KPL = 8: the 512 packed slots of b <= 32; 16: all 1024); a wave
+// radix selection takes eight bits a round from the top and stops once the
+// digit holding the boundary is taken whole (as block_radix_select), then a
+// one-wave sort orders the kept keys.
+template <int KPL>
+__global__ __launch_bounds__(256) void k_nm_keep_w(NmArgs N) {
+    __shared__ __attribute__((aligned(16))) int hist_s[4][256];
+    __shared__ uint64_t col_s[4][kWave];
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int64_t grp = (int64_t)blockIdx.x * 4 + wv;
+    if (grp >= N.groups) return;                            // (uniform in the wave)
+    constexpr bool packed = KPL == 8;
+    constexpr int per = packed ? 32 : 64, tot = kFastP * per;
+    const int keep = N.keep[grp];
+    uint64_t k[KPL];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-        if (k4[ii] != 0 && k4[ii] >= thr) col_s[atomicAdd(&ncol_s, 1)] = k4[ii];
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        const int lane = lane_id(), nk = ncol_s;
-        uint64_t key = lane < nk ? col_s[lane] : 0ull;
-        int pay = 0;
-        wave_sort_desc(key, pay);
-        if (lane < kFastP) N.kept[grp * kFastP + lane] = lane < nk ? (int32_t)slot_key_id(key) : 0;
-        if (lane == 0) N.keep[grp] = nk;
+    for (int ii = 0; ii < KPL; ++ii) {
+        const int e = lane + kWave * ii;
+        k[ii] = e / per < keep ? N.keys[(size_t)grp * (kFastP * 64) + nm_slot(e, packed)] : 0ull;
     }
+    static_assert(KPL * kWave == tot, "a lane per 1/64 of the slots");
+    int *hist = hist_s[wv];
+    int want = N.S.beam;
+    uint64_t prefix = 0, mask = 0;
+    bool none = false;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        wave_sync();                                        // the last round's reads done
+        *reinterpret_cast<int4 *>(hist + 4 * lane) = int4{0, 0, 0, 0};
+        wave_sync();
+#pragma unroll
+        for (int ii = 0; ii < KPL; ++ii)
+            if (k[ii] != 0 && (k[ii] & mask) == prefix) atomicAdd(&hist[(int)((k[ii] >> shift) & 255u)], 1);
+        wave_sync();
+        // lane l holds digits 255 - 4 l - j (j = 0..3): the count of the
+        // larger digits is an exclusive scan in lane order
+        const int4 hq = *reinterpret_cast<const int4 *>(hist + 252 - 4 * lane);
+        const int h[4] = {hq.w, hq.z, hq.y, hq.x};
+        const int lsum = h[0] + h[1] + h[2] + h[3];
+        const int incl = wave_incl_scan_add(lsum);
+        int before = incl - lsum, dg = -1, rest = 0, hv = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (h[j] > 0 && before < want && before + h[j] >= want) { dg = 255 - 4 * lane - j; rest = want - before; hv = h[j]; }
+            before += h[j];
+        }
+        const uint64_t fm = __ballot(dg >= 0);
+        if (fm == 0) { none = true; break; }                // all keys together weigh less than want
+        const int fl = __builtin_ctzll(fm);
+        dg = __builtin_amdgcn_readlane(dg, fl);
+        want = __builtin_amdgcn_readlane(rest, fl);
+        hv = __builtin_amdgcn_readlane(hv, fl);
+        prefix |= (uint64_t)dg << shift;
+        mask |= (uint64_t)255 << shift;
+        if (hv == want) break;                              // the whole digit is taken
+    }
+    const uint64_t thr = none ? 0ull : prefix;
+    // the kept keys (min(beam, nonzero) of them) gathered and sorted
+    int mine = 0;
+#pragma unroll
+    for (int ii = 0; ii < KPL; ++ii) mine += (k[ii] != 0 && k[ii] >= thr) ? 1 : 0;
+    const int incl = wave_incl_scan_add(mine);
+    int at = incl - mine;
+    const int nk = __builtin_amdgcn_readlane(incl, kWave - 1);
+#pragma unroll
+    for (int ii = 0; ii < KPL; ++ii)
+        if (k[ii] != 0 && k[ii] >= thr) col_s[wv][at++] = k[ii];
+    wave_sync();
+    uint64_t key = lane < nk ? col_s[wv][lane] : 0ull;
+    int pay = 0;
+    wave_sort_desc(key, pay);
+    if (lane < kFastP) N.kept[grp * kFastP + lane] = lane < nk ? (int32_t)slot_key_id(key) : 0;
+    if (lane == 0) N.keep[grp] = nk;
 }
 
 // KPT = 4: 1024 candidate slots; KPT = 2: the 512 packed slots of b <= 32
@@ -1322,7 +1373,8 @@ static hipError_t select_nm(const SelectArgs &A, int dtype, void *ws, int64_t ws
             hipLaunchKernelGGL(k_nm_fill, dim3(cg), dim3(256), hb, st, N, cnt);
             const bool packed = A.b <= 32;
             hipLaunchKernelGGL(k_nm_score_mfma, dim3((unsigned)((groups * kFastP + 63) / 64)), dim3(256), 0, st, N);
-            if (l < A.L) hipLaunchKernelGGL(k_nm_keep, dim3((unsigned)groups), dim3(256), 0, st, N);
+            if (l < A.L && packed) hipLaunchKernelGGL(k_nm_keep_w<8>, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, st, N);
+            else if (l < A.L) hipLaunchKernelGGL(k_nm_keep_w<16>, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, st, N);
             else if (packed) hipLaunchKernelGGL(k_nm_finish<2>, dim3((unsigned)groups), dim3(256), 0, st, N);
             else hipLaunchKernelGGL(k_nm_finish<4>, dim3((unsigned)groups), dim3(256), 0, st, N);
         }
