@@ -246,8 +246,18 @@ __global__ __launch_bounds__(256) void k_ins_small(InsArgs A) {
         const float *Wg = A.W + (size_t)g * d * r;
         const int nw = d * r;
         if ((nw & 3) == 0) {
+            // eight 16-byte loads a thread in flight before their stores
             const f4_t *w4 = reinterpret_cast<const f4_t *>(Wg);
-            for (int e = tid; e < nw / 4; e += blockDim.x) reinterpret_cast<f4_t *>(Wsm)[e] = w4[e];
+            f4_t *s4 = reinterpret_cast<f4_t *>(Wsm);
+            const int n4 = nw / 4;
+            for (int e0 = tid; e0 < n4; e0 += 8 * (int)blockDim.x) {
+                f4_t t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = w4[min(e0 + u * (int)blockDim.x, n4 - 1)];   // (clamped: in bounds)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (e0 + u * (int)blockDim.x < n4) s4[e0 + u * (int)blockDim.x] = t[u];
+            }
         } else {
             for (int e = tid; e < nw; e += blockDim.x) Wsm[e] = Wg[e];
         }
