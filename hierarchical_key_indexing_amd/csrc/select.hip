@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(256) void k_nm_keep_w(NmArgs N) {
 
 // KPT = 4: 1024 candidate slots; KPT = 2: the 512 packed slots of b <= 32
 template <int KPT>
-__global__ __launch_bounds__(256) void k_nm_finish(NmArgs N) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void k_nm_finish(NmArgs N) {
     __shared__ __attribute__((aligned(16))) uint64_t sk[1024];   // the sort's, then the copy's position marks
     __shared__ int dl_s[256 * KPT];
     __shared__ int eli_s[kFastP * 64], lof_s[kFastP * 64];
