@@ -1290,7 +1290,7 @@ static NmWs carve_nm_ws(char *base, int64_t groups, int h_kv, int64_t max_nodes)
     return w;
 }
 
-constexpr int64_t kNmRows = 16384;  // rows per batch the workspace query sizes for
+constexpr int64_t kNmRows = 32768;  // rows per batch the workspace query sizes for
 
 // the node-major path applies to the throughput kernel's shapes
 bool nm_shape_ok(int r, int b, int L, int beam, int d, const int64_t *nodes) {

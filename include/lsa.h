@@ -236,7 +236,7 @@ int lsa_index_insert(const void *K_new, int dtype, int64_t m, int d, const float
  * Bytes of device workspace that let lsa_select run its multi-workgroup
  * paths for this batch (*bytes): the decode kernel for small batches; for
  * larger ones with r = 64, b <= 64, beam <= 16, L >= 2 and leaf ids below
- * 2^22, the node-major path, sized for batches of up to 16384 rows; 0 when
+ * 2^22, the node-major path, sized for batches of up to 32768 rows; 0 when
  * neither applies (then every (row, KV head) pair runs in one workgroup).
  */
 int lsa_select_workspace_bytes(int64_t m, int h_q, int d, const lsa_index_desc *desc, int beam, int k,
