@@ -45,7 +45,7 @@ constexpr int kFlatLeaves = 1024;   // leaves per scoring workgroup
 constexpr int kFlatRows = 64;       // rows per scoring workgroup
 constexpr int kFlatList = 16384;    // keys collected per (row, KV head) in LDS
 constexpr int kFlatBins = 2048;     // radix digits of up to 11 bits
-constexpr int64_t kFlatBatch = 256; // rows per batch the workspace query sizes for
+constexpr int64_t kFlatBatch = 512; // rows per batch the workspace query sizes for
 constexpr int kSampleMax = 1024;    // sampled keys per (row, KV head)
 constexpr int kCollect = 4096;      // leaves per collecting workgroup
 

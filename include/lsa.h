@@ -313,7 +313,7 @@ int lsa_select(const void *Q, int dtype, int64_t m, int h_q, int d, const int32_
 
 /*
  * Bytes of device workspace lsa_select_flat needs to run m rows in batches of
- * up to 256 rows (*bytes).  Any workspace of at least the one-row size works;
+ * up to 512 rows (*bytes).  Any workspace of at least the one-row size works;
  * a smaller one runs the rows in smaller batches.
  */
 int lsa_select_flat_workspace_bytes(int64_t m, int h_q, const lsa_index_desc *desc, int64_t *bytes);
