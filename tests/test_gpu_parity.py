@@ -677,7 +677,15 @@ NM_CASES = [("nm_b64_L2", dict(n=20000, h_q=16, h_kv=2, d=128, dtype="bf16", r=6
             # 1024 candidate leaves (the largest finish network) and more than
             # 2048 keys (the copy by leaves)
             ("nm_b64_L2_wide", dict(n=20000, h_q=8, h_kv=2, d=64, dtype="f32", r=64, b=64, L=2, beam=16, k=3000,
-                                    centres=1024, m=300, mode="chunk"))]
+                                    centres=1024, m=300, mode="chunk")),
+            # b = 24: two rows a level-1 sort with lanes past b masked, 384
+            # packed candidates per internal level
+            ("nm_b24_L3", dict(n=15000, h_q=12, h_kv=3, d=72, dtype="bf16", r=64, b=24, L=3, beam=16, k=400,
+                               centres=600, m=333, mode="chunk")),
+            # d = 100 (not a multiple of 8: the vector-ALU top step) and b = 4:
+            # internal levels with fewer candidates than the beam
+            ("nm_b4_L3_d100", dict(n=3000, h_q=4, h_kv=2, d=100, dtype="f32", r=64, b=4, L=3, beam=16, k=200,
+                                   centres=64, m=257, mode="chunk"))]
 
 
 @pytest.mark.parametrize("name,over", NM_CASES, ids=[c[0] for c in NM_CASES])
