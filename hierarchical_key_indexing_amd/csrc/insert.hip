@@ -81,12 +81,40 @@ LSA_DEV void ins_child_row(const float *C, int64_t child, int r, float (&row)[64
     }
 }
 
+// The key's latent in registers: 16-byte LDS reads of the row every lane
+// shares (the row 16-byte aligned), issued together, so the distance chains
+// below wait on no LDS read.
+LSA_DEV void ins_load_z(const float *z, float (&zr)[64]) {
+    const f4_t *z4 = reinterpret_cast<const f4_t *>(z);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+        const f4_t t = z4[x];
+        zr[4 * x] = t.x; zr[4 * x + 1] = t.y; zr[4 * x + 2] = t.z; zr[4 * x + 3] = t.w;
+    }
+}
+
+// Squared distance in double, dimensions ascending, each difference and
+// square rounded once (the build's assignment distance).
+LSA_DEV double ins_sq_dist(const float (&z)[64], const float (&cs)[64], int r) {
+#pragma clang fp contract(off)
+    double dist = 0.0;
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+        if (x < r) {
+            const double diff = (double)z[x] - (double)cs[x];
+            const double sq = diff * diff;
+            dist = dist + sq;
+        }
+    }
+    return dist;
+}
+
 // The wave's nearest child: lane c holds child c's row (`ok`: a non-empty
 // child); squared distance in double, ties to the smaller child.
-LSA_DEV int ins_nearest(const float *z, const float (&row)[64], int r, bool ok) {
+LSA_DEV int ins_nearest(const float (&z)[64], const float (&row)[64], int r, bool ok) {
     const int lane = lane_id();
     // distances are >= 0, so their bit patterns order like the values
-    uint64_t key = ok ? (uint64_t)__double_as_longlong(sq_dist(z, row, r)) : ~0ull;
+    uint64_t key = ok ? (uint64_t)__double_as_longlong(ins_sq_dist(z, row, r)) : ~0ull;
     int best = lane;
 #pragma unroll
     for (int s = 1; s < kWave; s <<= 1) {
@@ -107,8 +135,8 @@ LSA_DEV int ins_nearest(const float *z, const float (&row)[64], int r, bool ok) 
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
-    __shared__ float z_s[4][64];
-    __shared__ float k_s[4][256];
+    __shared__ __attribute__((aligned(16))) float z_s[4][64];
+    __shared__ __attribute__((aligned(16))) float k_s[4][256];
     const int g = blockIdx.y, wv = threadIdx.x / kWave, lane = lane_id();
     const int64_t j = (int64_t)blockIdx.x * 4 + wv;
     if (j >= A.m) return;                                   // whole waves only
@@ -146,6 +174,8 @@ __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
         A.Z[((size_t)g * A.m + j) * r + lane] = (float)acc;
     }
     wave_sync();
+    float zr[64];
+    ins_load_z(z_s[wv], zr);
     int64_t u = 0;
     for (int l = 1; l <= A.L; ++l) {
         const float *C = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
@@ -156,7 +186,7 @@ __global__ __launch_bounds__(256) void k_ins_descend(InsArgs A) {
             ins_child_row(C, child, r, row);
             cnt = cn[child];
         }
-        u = u * b + ins_nearest(z_s[wv], row, r, lane < b && cnt > 0);
+        u = u * b + ins_nearest(zr, row, r, lane < b && cnt > 0);
         if (lane == 0) A.path[((size_t)g * A.m + j) * A.L + (l - 1)] = (int32_t)u;
     }
 }
@@ -228,8 +258,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_ins_small(InsArgs A) {
 #pragma clang fp contract(off)
     extern __shared__ __attribute__((aligned(16))) float dsm[];     // W_g [d][r], then a row tile per wave
-    __shared__ float k_s[4][256];
-    __shared__ float zl[kInsSmall][64];
+    __shared__ __attribute__((aligned(16))) float k_s[4][256];
+    __shared__ __attribute__((aligned(16))) float zl[kInsSmall][64];
     __shared__ int32_t path_s[kInsSmall][LSA_MAX_LEVELS];
     __shared__ uint64_t ks[LSA_MAX_LEVELS][kInsSmall];
     __shared__ int32_t seg_s[LSA_MAX_LEVELS][kInsSmall + 1];
@@ -277,10 +307,34 @@ __global__ __launch_bounds__(256) void k_ins_small(InsArgs A) {
         // in double over i ascending (each product exact), rounded once
         if (lane < r) {
             double acc = 0.0;
-            for (int i = 0; i < d; ++i) acc = fma((double)k_s[wv][i], (double)Wsm[i * r + lane], acc);
+            if (d % 16 == 0) {
+                // 16 dims a round: the key's four 16-byte LDS reads (every
+                // lane the same address) and the column's 16 reads issued
+                // before the round's FMAs, the next round's during them
+                const f4_t *k4 = reinterpret_cast<const f4_t *>(k_s[wv]);
+                for (int i0 = 0; i0 < d; i0 += 16) {
+                    f4_t kv[4];
+                    float wc[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) kv[q] = k4[i0 / 4 + q];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) wc[u] = Wsm[(i0 + u) * r + lane];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc = fma((double)kv[q].x, (double)wc[4 * q], acc);
+                        acc = fma((double)kv[q].y, (double)wc[4 * q + 1], acc);
+                        acc = fma((double)kv[q].z, (double)wc[4 * q + 2], acc);
+                        acc = fma((double)kv[q].w, (double)wc[4 * q + 3], acc);
+                    }
+                }
+            } else {
+                for (int i = 0; i < d; ++i) acc = fma((double)k_s[wv][i], (double)Wsm[i * r + lane], acc);
+            }
             zl[j][lane] = (float)acc;
         }
         wave_sync();
+        float zr[64];
+        ins_load_z(zl[j], zr);
         int64_t u = 0;
         for (int l = 1; l <= L; ++l) {
             const float *C = (const float *)(A.index + A.centroid_off[l]) + (size_t)g * A.nodes[l] * r;
@@ -318,7 +372,7 @@ __global__ __launch_bounds__(256) void k_ins_small(InsArgs A) {
                 ins_child_row(C, child, r, row);
                 cnt = cn[child];
             }
-            u = u * b + ins_nearest(zl[j], row, r, lane < b && cnt > 0);
+            u = u * b + ins_nearest(zr, row, r, lane < b && cnt > 0);
             if (lane == 0) path_s[j][l - 1] = (int32_t)u;
         }
     }
